@@ -1,0 +1,296 @@
+"""CPU oracle for hybrid compressed attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the GPU library
+(``long_context_attention_18_amd``) and never imports it. Inputs reach both
+sides from the seeded generators in ``long_context_attention_18_amd.synth``,
+which hold none of the method's arithmetic.
+
+The arithmetic lives in ``lca_oracle.c`` (plain scalar fp64 C); this module
+only marshals numpy arrays through ctypes and composes the per-step functions
+into a layer, in the order the pages describe the method ("DeepSeek-V4: a
+million-token context that agents can actually use", CSA and HCA paragraphs,
+Figures 3 and 4): compress every m tokens into one entry, score the
+compressed blocks with the lightning indexer (CSA), keep the top-k (CSA) or
+all blocks (HCA), add the sliding window of recent tokens, attend with one
+softmax.
+
+Parity unpinned (no numeric statement on the pages separates these readings
+from alternatives): RoPE base and pairing, per-channel gates, RoPE applied to
+each token before pooling, the indexer key stream, the indexer weighting
+form, the FP4 scale rule.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+_LIB = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+HEAD_DIM = 128
+NOPE_DIM = 64
+ROPE_DIM = 64
+IDX_DIM = 64
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.lcao_exp_det.restype = ctypes.c_double
+        L.lcao_exp_det.argtypes = [ctypes.c_double]
+        L.lcao_exp_consts.argtypes = [_f64p]
+        L.lcao_fp8_encode.restype = ctypes.c_uint8
+        L.lcao_fp8_encode.argtypes = [ctypes.c_double]
+        L.lcao_fp8_decode.restype = ctypes.c_double
+        L.lcao_fp8_decode.argtypes = [ctypes.c_uint8]
+        L.lcao_bf16_encode.restype = ctypes.c_uint16
+        L.lcao_bf16_encode.argtypes = [ctypes.c_double]
+        L.lcao_bf16_decode.restype = ctypes.c_float
+        L.lcao_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.lcao_fp4_encode.restype = ctypes.c_uint8
+        L.lcao_fp4_encode.argtypes = [ctypes.c_double]
+        L.lcao_fp4_decode.restype = ctypes.c_double
+        L.lcao_fp4_decode.argtypes = [ctypes.c_uint8]
+        L.lcao_mxfp4_quant.argtypes = [_f64p, ctypes.c_int, _u8p, _u8p]
+        L.lcao_rope_inv_freq.argtypes = [_f64p]
+        L.lcao_rope_rotate.argtypes = [_f64p, ctypes.c_int64]
+        L.lcao_pool.argtypes = [ctypes.c_int, ctypes.c_int, _f64p, _f64p, _f64p, _f64p, _f64p]
+        L.lcao_entry_encode.argtypes = [_f64p, _u8p, _f32p, _u16p]
+        L.lcao_entry_decode.argtypes = [_u8p, ctypes.c_float, _u16p, _f64p]
+        L.lcao_compress.argtypes = [ctypes.c_int, _u16p, _u16p, _u16p, _u16p, ctypes.c_int64, ctypes.c_int64,
+                                    _f32p, _f32p, ctypes.c_int64, ctypes.c_int64, _u8p, _f32p, _u16p, _u8p, _u8p]
+        L.lcao_window_entries.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int64, _u8p, _f32p, _u16p]
+        L.lcao_index_scores.argtypes = [ctypes.c_int, _u16p, _f32p, _u8p, _u8p, ctypes.c_int64, _f32p]
+        L.lcao_topk.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, _i32p]
+        L.lcao_attend.argtypes = [ctypes.c_int, _u16p, ctypes.c_int64, _f64p, ctypes.c_int64, _u16p, _f64p, _f64p]
+        _LIB = L
+    return _LIB
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- scalars
+def exp_det(x: float) -> float:
+    return lib().lcao_exp_det(float(x))
+
+
+def exp_consts():
+    out = np.zeros(17, np.float64)
+    lib().lcao_exp_consts(_p(out, _f64p))
+    return out
+
+
+def fp8_encode(v: float) -> int:
+    return lib().lcao_fp8_encode(float(v))
+
+
+def fp8_decode(c: int) -> float:
+    return lib().lcao_fp8_decode(int(c))
+
+
+def bf16_encode(v: float) -> int:
+    return lib().lcao_bf16_encode(float(v))
+
+
+def bf16_decode(b: int) -> float:
+    return lib().lcao_bf16_decode(int(b))
+
+
+def fp4_encode(v: float) -> int:
+    return lib().lcao_fp4_encode(float(v))
+
+
+def fp4_decode(c: int) -> float:
+    return lib().lcao_fp4_decode(int(c))
+
+
+# ---------------------------------------------------------------- vectors
+def mxfp4_quant(x):
+    x = _c(x, np.float64)
+    n = x.shape[-1]
+    assert n % 32 == 0
+    codes = np.zeros(n, np.uint8)
+    scales = np.zeros(n // 32, np.uint8)
+    lib().lcao_mxfp4_quant(_p(x, _f64p), n, _p(codes, _u8p), _p(scales, _u8p))
+    return codes, scales
+
+
+def rope_inv_freq():
+    out = np.zeros(ROPE_DIM // 2, np.float64)
+    lib().lcao_rope_inv_freq(_p(out, _f64p))
+    return out
+
+
+def rope_rotate(x, pos: int):
+    x = np.array(x, dtype=np.float64, copy=True)
+    assert x.shape == (HEAD_DIM,)
+    lib().lcao_rope_rotate(_p(x, _f64p), int(pos))
+    return x
+
+
+def pool(gate, bias, val):
+    gate = _c(gate, np.float64)
+    bias = _c(bias, np.float64)
+    val = _c(val, np.float64)
+    m, C = gate.shape
+    out = np.zeros(C, np.float64)
+    w = np.zeros((m, C), np.float64)
+    lib().lcao_pool(m, C, _p(gate, _f64p), _p(bias, _f64p), _p(val, _f64p), _p(out, _f64p), _p(w, _f64p))
+    return out, w
+
+
+def entry_encode(x):
+    x = _c(x, np.float64)
+    nope = np.zeros(NOPE_DIM, np.uint8)
+    scale = np.zeros(1, np.float32)
+    rope = np.zeros(ROPE_DIM, np.uint16)
+    lib().lcao_entry_encode(_p(x, _f64p), _p(nope, _u8p), _p(scale, _f32p), _p(rope, _u16p))
+    return nope, scale[0], rope
+
+
+def entry_decode(nope, scale, rope):
+    nope = _c(nope, np.uint8)
+    rope = _c(rope, np.uint16)
+    out = np.zeros(HEAD_DIM, np.float64)
+    lib().lcao_entry_decode(_p(nope, _u8p), float(scale), _p(rope, _u16p), _p(out, _f64p))
+    return out
+
+
+def entries_decode(nope, scale, rope):
+    """Dequantise many entries: nope [n][64] u8, scale [n] f32, rope [n][64] u16 -> [n][128] f64."""
+    n = nope.shape[0]
+    out = np.zeros((n, HEAD_DIM), np.float64)
+    for i in range(n):
+        out[i] = entry_decode(nope[i], scale[i], rope[i])
+    return out
+
+
+# ---------------------------------------------------------------- layer steps
+def compress(m, kv, gate, ik, ig, tok0, bias, idx_bias, j_begin, j_end):
+    """Entries of blocks [j_begin, j_end) of one sequence.
+
+    kv, gate: [n_tok][128] BF16 bits (uint16) for positions tok0..; ik, ig:
+    [n_tok][64] (CSA) or None (HCA). bias [m][128] f32, idx_bias [m][64] f32.
+    """
+    kv = _c(kv, np.uint16)
+    gate = _c(gate, np.uint16)
+    n_tok = kv.shape[0]
+    nb = max(0, j_end - j_begin)
+    out = {
+        "nope": np.zeros((nb, NOPE_DIM), np.uint8),
+        "scale": np.zeros(nb, np.float32),
+        "rope": np.zeros((nb, ROPE_DIM), np.uint16),
+    }
+    csa = ik is not None
+    if csa:
+        ik = _c(ik, np.uint16)
+        ig = _c(ig, np.uint16)
+        out["idx_codes"] = np.zeros((nb, IDX_DIM), np.uint8)
+        out["idx_scales"] = np.zeros((nb, 2), np.uint8)
+        idx_bias = _c(idx_bias, np.float32)
+    bias = _c(bias, np.float32)
+    if nb == 0:
+        return out
+    lib().lcao_compress(
+        int(m), _p(kv, _u16p), _p(gate, _u16p), _p(ik, _u16p) if csa else None, _p(ig, _u16p) if csa else None,
+        int(tok0), int(n_tok), _p(bias, _f32p), _p(idx_bias, _f32p) if csa else None, int(j_begin), int(j_end),
+        _p(out["nope"], _u8p), _p(out["scale"], _f32p), _p(out["rope"], _u16p),
+        _p(out["idx_codes"], _u8p) if csa else None, _p(out["idx_scales"], _u8p) if csa else None)
+    return out
+
+
+def window_entries(kv, tok0):
+    kv = _c(kv, np.uint16)
+    n = kv.shape[0]
+    out = {"nope": np.zeros((n, NOPE_DIM), np.uint8), "scale": np.zeros(n, np.float32),
+           "rope": np.zeros((n, ROPE_DIM), np.uint16)}
+    if n:
+        lib().lcao_window_entries(_p(kv, _u16p), int(tok0), int(n), _p(out["nope"], _u8p),
+                                  _p(out["scale"], _f32p), _p(out["rope"], _u16p))
+    return out
+
+
+def index_scores(qI, w, idx_codes, idx_scales):
+    """qI [H_I][64] BF16 bits, w [H_I] f32, keys [n][64] codes + [n][2] scale bytes -> [n] f32."""
+    qI = _c(qI, np.uint16)
+    w = _c(w, np.float32)
+    idx_codes = _c(idx_codes, np.uint8)
+    idx_scales = _c(idx_scales, np.uint8)
+    n = idx_codes.shape[0]
+    out = np.zeros(n, np.float32)
+    lib().lcao_index_scores(int(qI.shape[0]), _p(qI, _u16p), _p(w, _f32p), _p(idx_codes, _u8p),
+                            _p(idx_scales, _u8p), int(n), _p(out, _f32p))
+    return out
+
+
+def topk(scores, k):
+    scores = _c(scores, np.float32)
+    out = np.zeros(k, np.int32)
+    lib().lcao_topk(_p(scores, _f32p), int(scores.shape[0]), int(k), _p(out, _i32p))
+    return out
+
+
+def attend(q, t, keys):
+    """q [H][128] BF16 bits at position t, keys [n][128] f64 -> (out bf16 bits, out f64, lse f64)."""
+    q = _c(q, np.uint16)
+    keys = _c(keys, np.float64)
+    H = q.shape[0]
+    ob = np.zeros((H, HEAD_DIM), np.uint16)
+    of = np.zeros((H, HEAD_DIM), np.float64)
+    lse = np.zeros(H, np.float64)
+    lib().lcao_attend(int(H), _p(q, _u16p), int(t), _p(keys, _f64p), int(keys.shape[0]), _p(ob, _u16p),
+                      _p(of, _f64p), _p(lse, _f64p))
+    return ob, of, lse
+
+
+# ---------------------------------------------------------------- one query of one layer
+def n_visible(t: int, m: int) -> int:
+    """Blocks visible to a query at position t: those whose last token is <= t."""
+    return (t + 1) // m
+
+
+def layer_query(kind, m, k, W, t, q, qI, w, d1, d3, win, win_pos0=0):
+    """One query of one layer over caches that already hold position t.
+
+    d1: dict nope/scale/rope for blocks 0..; d3: dict idx_codes/idx_scales
+    (CSA) or None; win: per-token entries for positions win_pos0.. (dict).
+    Returns dict(topk, out_bf16, out_f64, lse).
+    """
+    N = n_visible(t, m)
+    res = {}
+    if kind == "csa":
+        scores = index_scores(qI, w, d3["idx_codes"][:N], d3["idx_scales"][:N])
+        sel = topk(scores, k)
+        res["topk"] = sel
+        res["scores"] = scores
+        comp = sel[sel >= 0]
+    else:
+        comp = np.arange(N)
+    s0 = max(0, t - W + 1)
+    ws = np.arange(s0, t + 1) - win_pos0
+    assert ws.min() >= 0
+    keys_c = entries_decode(d1["nope"][comp], d1["scale"][comp], d1["rope"][comp]) if len(comp) else \
+        np.zeros((0, HEAD_DIM))
+    keys_w = entries_decode(win["nope"][ws], win["scale"][ws], win["rope"][ws])
+    keys = np.concatenate([keys_c, keys_w], axis=0)
+    ob, of, lse = attend(q, t, keys)
+    res.update(out_bf16=ob, out_f64=of, lse=lse, n_comp=len(comp))
+    return res
