@@ -1,0 +1,213 @@
+/*
+ * lca.h -- C ABI of liblca.so: hybrid compressed long-context attention
+ * (CSA / HCA compressed KV cache + sliding window) on AMD gfx950 (MI355X).
+ *
+ * The method is the one the pages describe in "DeepSeek-V4: a million-token
+ * context that agents can actually use" (molayo1419.me rendering of the
+ * Hugging Face blog): CSA paragraph and Figure 3 (KV entries compressed 4x by
+ * softmax-gated pooling with a learned positional bias; an FP4 lightning
+ * indexer, a ReLU-scored multi-head dot product, picks the top-k compressed
+ * blocks per query; a sliding-window branch covers the recent uncompressed
+ * tokens), HCA paragraph and Figure 4 (128x compression, no selection, dense
+ * attention over the compressed stream plus the same window), and the
+ * storage paragraph (FP8 KV entries, BF16 RoPE dims, FP4 indexer). The cache
+ * layout -- a compressed cache, a separate sliding-window state and a
+ * separately managed uncompressed tail -- follows the KV-cache section of
+ * velog.io "DeepSeek V4 논문 정리".
+ *
+ * Conventions for every entry point:
+ *  - All pointers named *_dev are device pointers; the caller owns every
+ *    byte (allocate, keep alive until the stream is done, free). The library
+ *    never allocates, frees or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *    the call returns at once. Kernel faults surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are checked on the host before anything is launched; a bad
+ *    argument returns a negative status and launches nothing.
+ *  - BF16 tensors are passed as uint16_t bit patterns; every tensor is dense
+ *    row-major with the shape written next to it; B = batch of the cache.
+ *  - Every sequence of a cache holds the same number of tokens (`len`).
+ *  - A cache (and a workspace) is not thread-safe; distinct caches are
+ *    independent.
+ *
+ * Entry (196 bytes, one per compressed block and one per window token):
+ *   64 "nope" dims as FP8 E4M3FN codes + one fp32 scale, 64 RoPE dims BF16.
+ * Indexer key (34 bytes, CSA): 64 dims as FP4 E2M1 (two per byte, element
+ *   2i in the low nibble) + two E8M0 scale bytes (one per 32 dims).
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lca_status;
+#define LCA_OK 0
+#define LCA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define LCA_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define LCA_ERR_UNSUPPORTED (-3) /* a descriptor value this library does not implement */
+#define LCA_ERR_CAPACITY (-4)    /* the cache or the window state is too small for the call */
+#define LCA_ERR_ORDER (-5)       /* compress / append called out of order */
+#define LCA_ERR_WORKSPACE (-6)   /* workspace missing or smaller than lca_workspace_bytes() */
+#define LCA_ERR_LAUNCH (-7)      /* the HIP runtime rejected a launch */
+
+#define LCA_KIND_CSA 0
+#define LCA_KIND_HCA 1
+
+#define LCA_HEAD_DIM 128 /* shared KV head: 64 nope + 64 RoPE dims */
+#define LCA_NOPE_DIM 64
+#define LCA_ROPE_DIM 64
+#define LCA_IDX_DIM 64   /* lightning-indexer head dim */
+
+/* One attention layer. Supported: kind CSA or HCA; 1 <= m <= 128;
+ * 1 <= n_heads <= 64; 1 <= window <= 4096; CSA: 1 <= idx_heads <= 8 and
+ * 1 <= topk <= 2048 (both ignored for HCA). */
+typedef struct lca_layer_desc {
+  int32_t kind;      /* LCA_KIND_CSA or LCA_KIND_HCA */
+  int32_t m;         /* tokens pooled into one entry (CSA 4, HCA 128 on the pages) */
+  int32_t n_heads;   /* query heads, dim 128, all sharing the one KV head */
+  int32_t window;    /* W: sliding-window length in tokens, the query included */
+  int32_t idx_heads; /* CSA: lightning-indexer query heads, dim 64 */
+  int32_t topk;      /* CSA: compressed blocks kept per query */
+} lca_layer_desc;
+
+/* A bound cache. Fill it with lca_cache_bind(); the library updates `len`
+ * and `pending`; every other field is read-only for the caller. */
+typedef struct lca_cache {
+  lca_layer_desc desc;
+  int32_t batch;      /* B */
+  int32_t ring;       /* R: window-state slots per sequence (token s lives in slot s mod R) */
+  int64_t max_ctx;    /* token capacity per sequence */
+  int64_t max_blocks; /* max_ctx / m */
+  int64_t len;        /* tokens appended so far (same for every sequence) */
+  int64_t pending;    /* tokens compressed but not yet appended (0 or T) */
+  /* compressed cache (D1): [B][max_blocks][64] u8, [B][max_blocks] f32, [B][max_blocks][64] bf16 */
+  uint8_t* blk_codes_dev;
+  float* blk_scale_dev;
+  uint16_t* blk_rope_dev;
+  /* CSA indexer keys (D3): [B][max_blocks][32] u8 (FP4 pairs), [B][max_blocks][2] u8 (E8M0); NULL for HCA */
+  uint8_t* idx_codes_dev;
+  uint8_t* idx_scale_dev;
+  /* sliding-window state (D2): [B][R][64] u8, [B][R] f32, [B][R][64] bf16 */
+  uint8_t* win_codes_dev;
+  float* win_scale_dev;
+  uint16_t* win_rope_dev;
+  /* uncompressed tail: [B][m][tail_width] bf16, token p in slot p mod m;
+   * tail_width = 128 (kv) + 128 (gate) [+ 64 (ik) + 64 (ig) for CSA] */
+  uint16_t* tail_dev;
+  int32_t tail_width;
+  int32_t reserved0;
+  /* RoPE frequencies 10000^(-2i/64), i < 32, computed on the host at bind */
+  double rope_inv_freq[32];
+} lca_cache;
+
+/* Bytes of device memory lca_cache_bind() carves for one layer:
+ * D1 (196 B/block) + D3 (34 B/block, CSA) + D2 (196 B/slot) + tail, each
+ * array 256-byte aligned. max_blocks = max_ctx / m. Returns 0 for an
+ * invalid descriptor or size. */
+size_t lca_cache_bytes(const lca_layer_desc* desc, int32_t batch, int64_t max_ctx, int32_t ring);
+
+/* Carve `base_dev` (>= lca_cache_bytes() bytes, 256-byte aligned) into the
+ * arrays above, zero them on `stream`, set len = pending = 0 and fill the
+ * RoPE frequencies. ring >= window; to let Tq queries attend in one call
+ * (chunked prefill), ring >= Tq + window - 1. */
+lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* base_dev, size_t bytes,
+                          int32_t batch, int64_t max_ctx, int32_t ring, void* stream);
+
+/* Scratch one call of lca_csa_indexer_topk / lca_csa_sparse_attn /
+ * lca_hca_dense_attn needs for up to max_tq queries per sequence at up to
+ * max_ctx tokens. Nothing in it survives a call (every call initialises what
+ * it reads), so a workspace may be shared by caches of the same or smaller
+ * shape; calls sharing one workspace must not overlap in time.
+ * lca_workspace_init() zero-fills it (optional; useful for reproducible
+ * memory dumps). */
+size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx);
+lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
+
+/* CSA compressor (CSA paragraph and Figure 3: every m = 4 tokens pooled into
+ * one entry by softmax-gated pooling with a learned positional bias).
+ * Consumes the tail plus T new tokens at positions len .. len+T-1 and writes
+ * the D1 entry and the D3 indexer key of every block that these tokens
+ * complete. Per block j and channel c:
+ *   a_i = softmax_i(gate[jm+i][c] + bias[i][c]),  y_c = sum_i a_i * key_i[c]
+ * where key_i is the token's kv with dims 64..127 RoPE-rotated at the
+ * token's own position; the indexer key pools ik with ig and idx_bias the
+ * same way (no RoPE) and is stored as MX-FP4.
+ *   kv_dev, gate_dev: [B][T][128] bf16; ik_dev, ig_dev: [B][T][64] bf16;
+ *   bias_dev: [m][128] f32; idx_bias_dev: [m][64] f32.
+ * Must be followed by lca_swa_tail_append() with the same tokens before the
+ * next compress (LCA_ERR_ORDER otherwise); len + T <= max_ctx. */
+lca_status lca_csa_compress(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                            const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                            const float* idx_bias_dev, int32_t T, void* stream);
+
+/* HCA compressor (HCA paragraph and Figure 4: the same pooling at m = 128,
+ * no indexer key). Arguments as lca_csa_compress without ik/ig/idx_bias. */
+lca_status lca_hca_compress(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                            const float* bias_dev, int32_t T, void* stream);
+
+/* Sliding-window state and uncompressed tail (Figure 3's sliding-window
+ * branch; the KV-cache section's separate window state and separately
+ * managed tail). Writes the window entry of each of the T tokens (its kv,
+ * dims 64..127 RoPE-rotated at its position, FP8/BF16-encoded with its own
+ * scale) into slot s mod R (only the last R tokens of a long call survive),
+ * keeps the BF16 inputs of the tokens of the not yet complete block in the
+ * tail, and advances len by T. Same input layout as the compressor; ik/ig
+ * are NULL for HCA. Requires the preceding compress of exactly these T
+ * tokens. */
+lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                               const uint16_t* ik_dev, const uint16_t* ig_dev, int32_t T, void* stream);
+
+/* CSA lightning indexer + per-query top-k (CSA paragraph: FP4, ReLU-scored
+ * multi-head dot product; the top-k compressed blocks per query). The
+ * queries are the last Tq appended tokens, positions len-Tq .. len-1; query
+ * t sees blocks j < (t+1)/m (the block's last token at or before t). Per
+ * visible block:
+ *   s_h = fp32( <MXFP4(qI_h), key_j> ),  score_j = sum_h w_h * max(s_h, 0)
+ * (a chain of fmaf over h = 0..idx_heads-1 from +0). topk_dev receives the
+ * min(k, visible) blocks with the largest (score, -j), in ascending j,
+ * padded with -1.
+ *   qI_dev: [B][Tq][idx_heads][64] bf16; w_dev: [B][Tq][idx_heads] f32;
+ *   topk_dev: [B][Tq][k] int32. */
+lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, int32_t Tq,
+                                int32_t* topk_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* The two method steps of lca_csa_indexer_topk as separate calls (same
+ * arguments; the scores travel in the workspace, so both calls must get the
+ * same cache state, Tq and workspace, in this order, with nothing else using
+ * the workspace in between):
+ *  lca_csa_index_score: the lightning-indexer scores of every visible block
+ *    of the Tq queries (an HBM stream over the FP4 keys);
+ *  lca_csa_topk_select: the per-query top-k of those scores into topk_dev. */
+lca_status lca_csa_index_score(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, int32_t Tq,
+                               void* ws_dev, size_t ws_bytes, void* stream);
+lca_status lca_csa_topk_select(lca_cache* cache, int32_t Tq, int32_t* topk_dev, void* ws_dev, size_t ws_bytes,
+                               void* stream);
+
+/* CSA sparse attention (Figure 3): per query t and head h, one softmax over
+ * the multiset {D1 entries selected by topk} + {window entries of positions
+ * max(0, t-W+1) .. t}; K = V = the dequantised 128-dim entry; logits
+ * RoPE(q_h, t) . x / sqrt(128). Entries of -1 in topk are skipped.
+ *   q_dev: [B][Tq][n_heads][128] bf16 (not rotated); topk_dev: [B][Tq][k];
+ *   out_dev: [B][Tq][n_heads][128] bf16; lse_dev: [B][Tq][n_heads] f32
+ *   (natural-log log-sum-exp of the logits) or NULL. */
+lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
+                               uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* HCA dense attention (HCA paragraph and Figure 4): as lca_csa_sparse_attn
+ * over every visible D1 entry j < (t+1)/m plus the window. */
+lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev,
+                              float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* lca_status_str(lca_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCA_H */

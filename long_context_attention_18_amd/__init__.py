@@ -1,0 +1,260 @@
+"""Python binding of liblca.so (include/lca.h): hybrid compressed long-context
+attention -- CSA / HCA compressed KV cache with a sliding window -- on AMD
+gfx950 (MI355X).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels. Functions carry the C entry points' names and arguments; device
+buffers may be passed as torch tensors (their data_ptr() is used) or as raw
+integer addresses. A non-zero status raises ``LcaError``. There is no CPU
+fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblca.so")
+
+LCA_KIND_CSA = 0
+LCA_KIND_HCA = 1
+
+_STATUS = {0: "LCA_OK", -1: "LCA_ERR_NULL", -2: "LCA_ERR_SHAPE", -3: "LCA_ERR_UNSUPPORTED", -4: "LCA_ERR_CAPACITY",
+           -5: "LCA_ERR_ORDER", -6: "LCA_ERR_WORKSPACE", -7: "LCA_ERR_LAUNCH"}
+
+
+class LcaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({lib().lca_status_str(status).decode()})")
+
+
+class lca_layer_desc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("m", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("idx_heads", ctypes.c_int32), ("topk", ctypes.c_int32)]
+
+
+class lca_cache(ctypes.Structure):
+    _fields_ = [("desc", lca_layer_desc), ("batch", ctypes.c_int32), ("ring", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int64), ("max_blocks", ctypes.c_int64), ("len", ctypes.c_int64),
+                ("pending", ctypes.c_int64),
+                ("blk_codes_dev", ctypes.c_void_p), ("blk_scale_dev", ctypes.c_void_p),
+                ("blk_rope_dev", ctypes.c_void_p), ("idx_codes_dev", ctypes.c_void_p),
+                ("idx_scale_dev", ctypes.c_void_p), ("win_codes_dev", ctypes.c_void_p),
+                ("win_scale_dev", ctypes.c_void_p), ("win_rope_dev", ctypes.c_void_p),
+                ("tail_dev", ctypes.c_void_p), ("tail_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("rope_inv_freq", ctypes.c_double * 32)]
+
+
+_LIB = None
+_VP = ctypes.c_void_p
+_DP = ctypes.POINTER(lca_layer_desc)
+_CP = ctypes.POINTER(lca_cache)
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "lca_cache_bytes": (_SZ, [_DP, _I32, _I64, _I32]),
+    "lca_cache_bind": (_I32, [_DP, _CP, _VP, _SZ, _I32, _I64, _I32, _VP]),
+    "lca_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I64]),
+    "lca_workspace_init": (_I32, [_VP, _SZ, _VP]),
+    "lca_csa_compress": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
+    "lca_hca_compress": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP]),
+    "lca_swa_tail_append": (_I32, [_CP, _VP, _VP, _VP, _VP, _I32, _VP]),
+    "lca_csa_indexer_topk": (_I32, [_CP, _VP, _VP, _I32, _VP, _VP, _SZ, _VP]),
+    "lca_csa_index_score": (_I32, [_CP, _VP, _VP, _I32, _VP, _SZ, _VP]),
+    "lca_csa_topk_select": (_I32, [_CP, _I32, _VP, _VP, _SZ, _VP]),
+    "lca_csa_sparse_attn": (_I32, [_CP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_hca_dense_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_status_str": (ctypes.c_char_p, [_I32]),
+}
+
+
+def lib():
+    """Load the in-tree liblca.so. Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python -m long_context_attention_18_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _ptr(x):
+    """Device address of a torch tensor (or an int / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != 0:
+        raise LcaError(fn, status)
+
+
+def make_desc(kind: str, m: int, n_heads: int, window: int = 128, idx_heads: int = 0, topk: int = 0):
+    return lca_layer_desc(LCA_KIND_CSA if kind == "csa" else LCA_KIND_HCA, m, n_heads, window, idx_heads, topk)
+
+
+# ----------------------------------------------------------------- entry points
+def lca_cache_bytes(desc, batch, max_ctx, ring):
+    return lib().lca_cache_bytes(ctypes.byref(desc), batch, max_ctx, ring)
+
+
+def lca_cache_bind(desc, cache, base, nbytes, batch, max_ctx, ring, stream=None):
+    _check("lca_cache_bind", lib().lca_cache_bind(ctypes.byref(desc), ctypes.byref(cache), _ptr(base), nbytes,
+                                                   batch, max_ctx, ring, _stream(stream)))
+
+
+def lca_workspace_bytes(desc, batch, max_tq, max_ctx):
+    return lib().lca_workspace_bytes(ctypes.byref(desc), batch, max_tq, max_ctx)
+
+
+def lca_workspace_init(ws, nbytes, stream=None):
+    _check("lca_workspace_init", lib().lca_workspace_init(_ptr(ws), nbytes, _stream(stream)))
+
+
+def lca_csa_compress(cache, kv, gate, ik, ig, bias, idx_bias, T, stream=None):
+    _check("lca_csa_compress", lib().lca_csa_compress(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(ik), _ptr(ig),
+                                                       _ptr(bias), _ptr(idx_bias), T, _stream(stream)))
+
+
+def lca_hca_compress(cache, kv, gate, bias, T, stream=None):
+    _check("lca_hca_compress", lib().lca_hca_compress(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(bias), T,
+                                                       _stream(stream)))
+
+
+def lca_swa_tail_append(cache, kv, gate, ik, ig, T, stream=None):
+    _check("lca_swa_tail_append", lib().lca_swa_tail_append(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(ik),
+                                                             _ptr(ig), T, _stream(stream)))
+
+
+def lca_csa_indexer_topk(cache, qI, w, Tq, topk, ws, ws_bytes, stream=None):
+    _check("lca_csa_indexer_topk", lib().lca_csa_indexer_topk(ctypes.byref(cache), _ptr(qI), _ptr(w), Tq, _ptr(topk),
+                                                               _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_csa_index_score(cache, qI, w, Tq, ws, ws_bytes, stream=None):
+    _check("lca_csa_index_score", lib().lca_csa_index_score(ctypes.byref(cache), _ptr(qI), _ptr(w), Tq, _ptr(ws),
+                                                             ws_bytes, _stream(stream)))
+
+
+def lca_csa_topk_select(cache, Tq, topk, ws, ws_bytes, stream=None):
+    _check("lca_csa_topk_select", lib().lca_csa_topk_select(ctypes.byref(cache), Tq, _ptr(topk), _ptr(ws), ws_bytes,
+                                                             _stream(stream)))
+
+
+def lca_csa_sparse_attn(cache, q, topk, Tq, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_csa_sparse_attn", lib().lca_csa_sparse_attn(ctypes.byref(cache), _ptr(q), _ptr(topk), Tq, _ptr(out),
+                                                             _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_hca_dense_attn(cache, q, Tq, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_hca_dense_attn", lib().lca_hca_dense_attn(ctypes.byref(cache), _ptr(q), Tq, _ptr(out), _ptr(lse),
+                                                           _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_status_str(status):
+    return lib().lca_status_str(status).decode()
+
+
+# ----------------------------------------------------------------- device-memory plumbing
+class DeviceLayer:
+    """One layer's cache and workspace in torch-allocated device memory.
+
+    Owns the buffers (torch uint8 tensors) and the bound lca_cache struct;
+    the methods forward to the entry points above with this layer's cache.
+    """
+
+    def __init__(self, desc, batch, max_ctx, ring, max_tq=1, device="cuda", stream=None):
+        import torch
+        self.desc = desc
+        self.batch, self.max_ctx, self.ring, self.max_tq = batch, max_ctx, ring, max_tq
+        nbytes = lca_cache_bytes(desc, batch, max_ctx, ring)
+        if nbytes == 0:
+            raise LcaError("lca_cache_bytes", -2)
+        self.cache_bytes = nbytes
+        self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = (self.mem.data_ptr() + 255) // 256 * 256
+        self.cache = lca_cache()
+        lca_cache_bind(desc, self.cache, base, nbytes, batch, max_ctx, ring, stream)
+        self.ws_bytes = lca_workspace_bytes(desc, batch, max_tq, max_ctx)
+        self.ws_mem = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
+        self.ws = (self.ws_mem.data_ptr() + 255) // 256 * 256
+        lca_workspace_init(self.ws, self.ws_bytes, stream)
+
+    @property
+    def len(self):
+        return self.cache.len
+
+    @property
+    def csa(self):
+        return self.desc.kind == LCA_KIND_CSA
+
+    def compress(self, kv, gate, bias, ik=None, ig=None, idx_bias=None, stream=None):
+        T = kv.shape[1]
+        if self.csa:
+            lca_csa_compress(self.cache, kv, gate, ik, ig, bias, idx_bias, T, stream)
+        else:
+            lca_hca_compress(self.cache, kv, gate, bias, T, stream)
+
+    def append(self, kv, gate, ik=None, ig=None, stream=None):
+        lca_swa_tail_append(self.cache, kv, gate, ik, ig, kv.shape[1], stream)
+
+    def indexer_topk(self, qI, w, topk, stream=None):
+        lca_csa_indexer_topk(self.cache, qI, w, qI.shape[1], topk, self.ws, self.ws_bytes, stream)
+
+    def index_score(self, qI, w, stream=None):
+        lca_csa_index_score(self.cache, qI, w, qI.shape[1], self.ws, self.ws_bytes, stream)
+
+    def topk_select(self, Tq, topk, stream=None):
+        lca_csa_topk_select(self.cache, Tq, topk, self.ws, self.ws_bytes, stream)
+
+    def sparse_attn(self, q, topk, out, lse=None, stream=None):
+        lca_csa_sparse_attn(self.cache, q, topk, q.shape[1], out, lse, self.ws, self.ws_bytes, stream)
+
+    def dense_attn(self, q, out, lse=None, stream=None):
+        lca_hca_dense_attn(self.cache, q, q.shape[1], out, lse, self.ws, self.ws_bytes, stream)
+
+    def views(self):
+        """Typed torch views of the cache arrays (for checks)."""
+        import torch
+        c = self.cache
+        B, NB, R = self.batch, c.max_blocks, self.ring
+        base = self.mem.data_ptr()
+
+        def view(addr, n, dtype, shape):
+            off = addr - base
+            esz = torch.tensor([], dtype=dtype).element_size()
+            return self.mem[off:off + n * esz].view(dtype).view(*shape)
+
+        v = {
+            "blk_codes": view(c.blk_codes_dev, B * NB * 64, torch.uint8, (B, NB, 64)),
+            "blk_scale": view(c.blk_scale_dev, B * NB, torch.float32, (B, NB)),
+            "blk_rope": view(c.blk_rope_dev, B * NB * 64, torch.int16, (B, NB, 64)),
+            "win_codes": view(c.win_codes_dev, B * R * 64, torch.uint8, (B, R, 64)),
+            "win_scale": view(c.win_scale_dev, B * R, torch.float32, (B, R)),
+            "win_rope": view(c.win_rope_dev, B * R * 64, torch.int16, (B, R, 64)),
+        }
+        if self.csa:
+            v["idx_codes"] = view(c.idx_codes_dev, B * NB * 32, torch.uint8, (B, NB, 32))
+            v["idx_scale"] = view(c.idx_scale_dev, B * NB * 2, torch.uint8, (B, NB, 2))
+        return v

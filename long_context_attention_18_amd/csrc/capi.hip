@@ -1,0 +1,382 @@
+// capi.hip -- the extern "C" boundary of liblca.so (declared in include/lca.h).
+//
+// Host-side only: argument checks, cache carving, workspace layout, and the
+// kernel launches. Every check happens before the first launch of a call, so
+// a rejected call enqueues nothing.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/lca.h"
+#include "kernels.h"
+
+using namespace lca;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool desc_ok(const lca_layer_desc* d) {
+  if (!d) return false;
+  if (d->kind != LCA_KIND_CSA && d->kind != LCA_KIND_HCA) return false;
+  if (d->m < 1 || d->m > 128) return false;
+  if (d->n_heads < 1 || d->n_heads > 64) return false;
+  if (d->window < 1 || d->window > 4096) return false;
+  if (d->kind == LCA_KIND_CSA) {
+    if (d->idx_heads < 1 || d->idx_heads > 8) return false;
+    if (d->topk < 1 || d->topk > 2048) return false;
+  }
+  return true;
+}
+
+int32_t tail_width(const lca_layer_desc* d) { return d->kind == LCA_KIND_CSA ? 384 : 256; }
+
+struct Layout {
+  size_t blk_codes, blk_scale, blk_rope, idx_codes, idx_scale, win_codes, win_scale, win_rope, tail, total;
+};
+
+Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring) {
+  Layout L{};
+  const size_t nb = (size_t)B * (size_t)(max_ctx / d->m);
+  const size_t nw = (size_t)B * (size_t)ring;
+  size_t off = 0;
+  L.blk_codes = off; off = align_up(off + nb * 64);
+  L.blk_scale = off; off = align_up(off + nb * 4);
+  L.blk_rope = off; off = align_up(off + nb * 128);
+  if (d->kind == LCA_KIND_CSA) {
+    L.idx_codes = off; off = align_up(off + nb * 32);
+    L.idx_scale = off; off = align_up(off + nb * 2);
+  }
+  L.win_codes = off; off = align_up(off + nw * 64);
+  L.win_scale = off; off = align_up(off + nw * 4);
+  L.win_rope = off; off = align_up(off + nw * 128);
+  L.tail = off; off = align_up(off + (size_t)B * d->m * tail_width(d) * 2);
+  L.total = off;
+  return L;
+}
+
+bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring) {
+  if (B < 1 || B > 65535) return false;
+  if (max_ctx < d->m || max_ctx > ((int64_t)1 << 32)) return false;
+  if (max_ctx / d->m > (int64_t)2048 * kScoreChunk) return false;  // score chunks per query fit the scan's LDS
+  if (ring < d->window || ring > (1 << 24)) return false;
+  return true;
+}
+
+// Workspace: indexer (keys, thresholds, candidates, counters) then attention partials.
+struct WsLayout {
+  size_t keys, thr, cand, cnt, part, total;
+  int32_t G;
+};
+
+int32_t score_chunks(int64_t max_blocks) { return (int32_t)((max_blocks + kScoreChunk - 1) / kScoreChunk); }
+
+WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t max_ctx) {
+  WsLayout W{};
+  const int64_t max_blocks = max_ctx / d->m;
+  const size_t nq = (size_t)B * (size_t)max_tq;
+  size_t off = 0;
+  W.G = score_chunks(max_blocks);
+  W.cnt = off; off = align_up(off + nq * 4);  // counters first: lca_workspace_init clears them
+  if (d->kind == LCA_KIND_CSA) {
+    W.keys = off; off = align_up(off + nq * (size_t)max_blocks * 4);
+    W.thr = off; off = align_up(off + nq * (size_t)W.G * 4);
+    W.cand = off; off = align_up(off + nq * (size_t)kCandCap * 8);
+  }
+  // split-K partials: splits are used only while B*Tq < kAttnTargetWGs, and then
+  // B*Tq*splits < 2*kAttnTargetWGs (see attn_splits)
+  W.part = off; off = align_up(off + (size_t)2 * kAttnTargetWGs * d->n_heads * kPartStride * 4);
+  W.total = off;
+  return W;
+}
+
+void attn_splits(int64_t n_keys, int32_t nq, int32_t* splits, int32_t* per_split) {
+  int64_t max_chunks = (n_keys + kAttnKeys - 1) / kAttnKeys;
+  int64_t s = 1;
+  if (nq < kAttnTargetWGs) s = (kAttnTargetWGs + nq - 1) / nq;
+  if (s > max_chunks) s = max_chunks;
+  if (s < 1) s = 1;
+  int64_t per = (n_keys + s - 1) / s;
+  per = (per + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
+  s = (n_keys + per - 1) / per;
+  *splits = (int32_t)s;
+  *per_split = (int32_t)per;
+}
+
+lca_status launch_status(hipError_t e) { return e == hipSuccess ? LCA_OK : LCA_ERR_LAUNCH; }
+
+bool cache_ok(const lca_cache* c) {
+  return c && desc_ok(&c->desc) && c->blk_codes_dev && c->win_codes_dev && c->tail_dev;
+}
+
+IngestArgs ingest_args(lca_cache* c, const uint16_t* kv, const uint16_t* gate, const uint16_t* ik,
+                       const uint16_t* ig, int32_t T) {
+  IngestArgs a{};
+  a.kv = kv;
+  a.gate = gate;
+  a.ik = ik;
+  a.ig = ig;
+  a.blk_codes = c->blk_codes_dev;
+  a.blk_scale = c->blk_scale_dev;
+  a.blk_rope = c->blk_rope_dev;
+  a.idx_codes = c->idx_codes_dev;
+  a.idx_scale = c->idx_scale_dev;
+  a.win_codes = c->win_codes_dev;
+  a.win_scale = c->win_scale_dev;
+  a.win_rope = c->win_rope_dev;
+  a.tail = c->tail_dev;
+  a.len = c->len;
+  a.max_blocks = c->max_blocks;
+  a.T = T;
+  a.m = c->desc.m;
+  a.ring = c->ring;
+  a.tail_width = c->tail_width;
+  a.B = c->batch;
+  std::memcpy(a.inv_freq, c->rope_inv_freq, sizeof(a.inv_freq));
+  return a;
+}
+
+lca_status compress_impl(lca_cache* c, bool csa, const uint16_t* kv, const uint16_t* gate, const uint16_t* ik,
+                         const uint16_t* ig, const float* bias, const float* idx_bias, int32_t T, void* stream) {
+  if (!cache_ok(c) || !kv || !gate || !bias) return LCA_ERR_NULL;
+  if (csa != (c->desc.kind == LCA_KIND_CSA)) return LCA_ERR_UNSUPPORTED;
+  if (csa && (!ik || !ig || !idx_bias || !c->idx_codes_dev || !c->idx_scale_dev)) return LCA_ERR_NULL;
+  if (T < 1) return LCA_ERR_SHAPE;
+  if (c->pending != 0) return LCA_ERR_ORDER;
+  if (c->len + T > c->max_ctx) return LCA_ERR_CAPACITY;
+  IngestArgs a = ingest_args(c, kv, gate, ik, ig, T);
+  a.bias = bias;
+  a.idx_bias = idx_bias;
+  const int64_t m = c->desc.m;
+  a.first = c->len / m;
+  const int64_t n_blocks = (c->len + T) / m - c->len / m;
+  hipError_t e = launch_compress(a, csa, n_blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return LCA_ERR_LAUNCH;
+  c->pending = T;
+  return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lca_status_str(lca_status s) {
+  switch (s) {
+    case LCA_OK: return "ok";
+    case LCA_ERR_NULL: return "null pointer";
+    case LCA_ERR_SHAPE: return "size out of range";
+    case LCA_ERR_UNSUPPORTED: return "unsupported descriptor";
+    case LCA_ERR_CAPACITY: return "cache or window state too small";
+    case LCA_ERR_ORDER: return "compress / append out of order";
+    case LCA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t lca_cache_bytes(const lca_layer_desc* desc, int32_t batch, int64_t max_ctx, int32_t ring) {
+  if (!desc_ok(desc) || !sizes_ok(desc, batch, max_ctx, ring)) return 0;
+  return layout(desc, batch, max_ctx, ring).total;
+}
+
+lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* base_dev, size_t bytes, int32_t batch,
+                          int64_t max_ctx, int32_t ring, void* stream) {
+  if (!desc || !cache || !base_dev) return LCA_ERR_NULL;
+  if (!desc_ok(desc)) return LCA_ERR_UNSUPPORTED;
+  if (!sizes_ok(desc, batch, max_ctx, ring)) return LCA_ERR_SHAPE;
+  if (((uintptr_t)base_dev) % kAlign != 0) return LCA_ERR_SHAPE;
+  Layout L = layout(desc, batch, max_ctx, ring);
+  if (bytes < L.total) return LCA_ERR_CAPACITY;
+  std::memset(cache, 0, sizeof(*cache));
+  cache->desc = *desc;
+  if (desc->kind == LCA_KIND_HCA) {
+    cache->desc.idx_heads = 0;
+    cache->desc.topk = 0;
+  }
+  cache->batch = batch;
+  cache->ring = ring;
+  cache->max_ctx = max_ctx;
+  cache->max_blocks = max_ctx / desc->m;
+  char* base = (char*)base_dev;
+  cache->blk_codes_dev = (uint8_t*)(base + L.blk_codes);
+  cache->blk_scale_dev = (float*)(base + L.blk_scale);
+  cache->blk_rope_dev = (uint16_t*)(base + L.blk_rope);
+  if (desc->kind == LCA_KIND_CSA) {
+    cache->idx_codes_dev = (uint8_t*)(base + L.idx_codes);
+    cache->idx_scale_dev = (uint8_t*)(base + L.idx_scale);
+  }
+  cache->win_codes_dev = (uint8_t*)(base + L.win_codes);
+  cache->win_scale_dev = (float*)(base + L.win_scale);
+  cache->win_rope_dev = (uint16_t*)(base + L.win_rope);
+  cache->tail_dev = (uint16_t*)(base + L.tail);
+  cache->tail_width = tail_width(desc);
+  for (int i = 0; i < 32; ++i) cache->rope_inv_freq[i] = std::pow(10000.0, -(double)(2 * i) / 64.0);
+  return launch_status(launch_fill_zero(base_dev, L.total, (hipStream_t)stream));
+}
+
+size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx) {
+  if (!desc_ok(desc) || batch < 1 || max_tq < 1 || max_ctx < desc->m) return 0;
+  return ws_layout(desc, batch, max_tq, max_ctx).total;
+}
+
+lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream) {
+  if (!ws_dev) return LCA_ERR_NULL;
+  if (((uintptr_t)ws_dev) % kAlign != 0 || bytes % 16 != 0) return LCA_ERR_SHAPE;
+  return launch_status(launch_fill_zero(ws_dev, bytes, (hipStream_t)stream));
+}
+
+lca_status lca_csa_compress(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                            const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                            const float* idx_bias_dev, int32_t T, void* stream) {
+  return compress_impl(cache, true, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, stream);
+}
+
+lca_status lca_hca_compress(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                            const float* bias_dev, int32_t T, void* stream) {
+  return compress_impl(cache, false, kv_dev, gate_dev, nullptr, nullptr, bias_dev, nullptr, T, stream);
+}
+
+lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                               const uint16_t* ik_dev, const uint16_t* ig_dev, int32_t T, void* stream) {
+  if (!cache_ok(cache) || !kv_dev || !gate_dev) return LCA_ERR_NULL;
+  const bool csa = cache->desc.kind == LCA_KIND_CSA;
+  if (csa && (!ik_dev || !ig_dev)) return LCA_ERR_NULL;
+  if (T < 1) return LCA_ERR_SHAPE;
+  if (cache->pending != T) return LCA_ERR_ORDER;
+  if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
+  IngestArgs a = ingest_args(cache, kv_dev, gate_dev, csa ? ik_dev : nullptr, csa ? ig_dev : nullptr, T);
+  const int64_t end = cache->len + T;
+  const int64_t win_first = (end - cache->ring > cache->len) ? end - cache->ring : cache->len;
+  a.first = win_first;
+  a.n_win = (int32_t)(end - win_first);
+  int64_t tail_first = (end / cache->desc.m) * cache->desc.m;
+  if (tail_first < cache->len) tail_first = cache->len;
+  const int32_t n_tail = (int32_t)(end - tail_first);
+  hipError_t e = launch_append(a, csa, n_tail, (hipStream_t)stream);
+  if (e != hipSuccess) return LCA_ERR_LAUNCH;
+  cache->len = end;
+  cache->pending = 0;
+  return LCA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, bool need_q, int32_t Tq,
+                      int32_t* topk_dev, bool need_topk, void* ws_dev, size_t ws_bytes, ScoreArgs* out) {
+  if (!cache_ok(cache)) return LCA_ERR_NULL;
+  if (need_q && (!qI_dev || !w_dev)) return LCA_ERR_NULL;
+  if (need_topk && !topk_dev) return LCA_ERR_NULL;
+  if (cache->desc.kind != LCA_KIND_CSA || !cache->idx_codes_dev) return LCA_ERR_UNSUPPORTED;
+  if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (!ws_dev) return LCA_ERR_WORKSPACE;
+  WsLayout W = ws_layout(&cache->desc, cache->batch, Tq, cache->max_ctx);
+  if (ws_bytes < W.total) return LCA_ERR_WORKSPACE;
+  ScoreArgs a{};
+  char* ws = (char*)ws_dev;
+  a.qI = qI_dev;
+  a.w = w_dev;
+  a.idx_codes = cache->idx_codes_dev;
+  a.idx_scale = cache->idx_scale_dev;
+  a.keys = (uint32_t*)(ws + W.keys);
+  a.thr = (uint32_t*)(ws + W.thr);
+  a.cand = (uint64_t*)(ws + W.cand);
+  a.cand_cnt = (uint32_t*)(ws + W.cnt);
+  a.topk = topk_dev;
+  a.len = cache->len;
+  a.max_blocks = cache->max_blocks;
+  a.Tq = Tq;
+  a.HI = cache->desc.idx_heads;
+  a.k = cache->desc.topk;
+  a.m = cache->desc.m;
+  a.G = W.G;
+  *out = a;
+  return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_csa_index_score(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, int32_t Tq,
+                               void* ws_dev, size_t ws_bytes, void* stream) {
+  ScoreArgs a;
+  lca_status st = score_args(cache, qI_dev, w_dev, true, Tq, nullptr, false, ws_dev, ws_bytes, &a);
+  if (st != LCA_OK) return st;
+  return launch_status(launch_index_score(a, cache->batch, (hipStream_t)stream));
+}
+
+lca_status lca_csa_topk_select(lca_cache* cache, int32_t Tq, int32_t* topk_dev, void* ws_dev, size_t ws_bytes,
+                               void* stream) {
+  ScoreArgs a;
+  lca_status st = score_args(cache, nullptr, nullptr, false, Tq, topk_dev, true, ws_dev, ws_bytes, &a);
+  if (st != LCA_OK) return st;
+  return launch_status(launch_topk_select(a, cache->batch, (hipStream_t)stream));
+}
+
+lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, int32_t Tq,
+                                int32_t* topk_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  ScoreArgs a;
+  lca_status st = score_args(cache, qI_dev, w_dev, true, Tq, topk_dev, true, ws_dev, ws_bytes, &a);
+  if (st != LCA_OK) return st;
+  hipError_t e = launch_index_score(a, cache->batch, (hipStream_t)stream);
+  if (e != hipSuccess) return LCA_ERR_LAUNCH;
+  return launch_status(launch_topk_select(a, cache->batch, (hipStream_t)stream));
+}
+
+static lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev,
+                                 int32_t Tq, uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes,
+                                 void* stream) {
+  if (!cache_ok(cache) || !q_dev || !out_dev) return LCA_ERR_NULL;
+  if (!dense && !topk_dev) return LCA_ERR_NULL;
+  if (dense != (cache->desc.kind == LCA_KIND_HCA)) return LCA_ERR_UNSUPPORTED;
+  if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if ((int64_t)Tq + cache->desc.window - 1 > cache->ring) return LCA_ERR_CAPACITY;
+  AttnArgs a{};
+  a.q = q_dev;
+  a.topk = dense ? nullptr : topk_dev;
+  a.blk_codes = cache->blk_codes_dev;
+  a.blk_scale = cache->blk_scale_dev;
+  a.blk_rope = cache->blk_rope_dev;
+  a.win_codes = cache->win_codes_dev;
+  a.win_scale = cache->win_scale_dev;
+  a.win_rope = cache->win_rope_dev;
+  a.out = out_dev;
+  a.lse = lse_dev;
+  a.len = cache->len;
+  a.max_blocks = cache->max_blocks;
+  a.Tq = Tq;
+  a.H = cache->desc.n_heads;
+  a.k = dense ? 0 : cache->desc.topk;
+  a.m = cache->desc.m;
+  a.W = cache->desc.window;
+  a.ring = cache->ring;
+  a.dense = dense ? 1 : 0;
+  std::memcpy(a.inv_freq, cache->rope_inv_freq, sizeof(a.inv_freq));
+  const int64_t n_first = dense ? cache->len / cache->desc.m : (int64_t)cache->desc.topk;
+  const int32_t nq = cache->batch * Tq;
+  attn_splits(n_first + cache->desc.window, nq, &a.splits, &a.keys_per_split);
+  if (a.splits > 1) {
+    if (!ws_dev) return LCA_ERR_WORKSPACE;
+    WsLayout W = ws_layout(&cache->desc, cache->batch, Tq, cache->max_ctx);
+    if (ws_bytes < W.total) return LCA_ERR_WORKSPACE;
+    a.part = (float*)((char*)ws_dev + W.part);
+  }
+  return launch_status(launch_attention(a, cache->batch, (hipStream_t)stream));
+}
+
+lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
+                               uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return attention_impl(cache, false, q_dev, topk_dev, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+}
+
+lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev,
+                              float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return attention_impl(cache, true, q_dev, nullptr, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+}
+
+}  // extern "C"

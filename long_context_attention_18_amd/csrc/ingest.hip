@@ -1,0 +1,202 @@
+// ingest.hip -- KV compressor and sliding-window / tail append for gfx950.
+//
+// Compressor: the CSA paragraph and Figure 3 of "DeepSeek-V4: a
+// million-token context that agents can actually use" (softmax-gated
+// pooling with a learned positional bias, every 4 tokens into one entry),
+// the HCA paragraph and Figure 4 (the same at 128x). Window / tail: Figure
+// 3's sliding-window branch and the KV-cache section of velog.io
+// "DeepSeek V4 논문 정리" (separate window state, separately managed
+// uncompressed tail).
+//
+// One 64-lane wave per compressed block (or per window token). Lane c owns
+// channel c of the 64 "nope" dims, channel 64+c of the RoPE dims and, for
+// CSA, channel c of the indexer stream. The pooling is fp64 with the
+// library's own exp so that the FP8 / FP4 codes are reproducible bit for bit;
+// this is a few thousand flops per block, far off any roofline (decode
+// writes at most one block per m tokens).
+#include "dev_formats.h"
+#include "kernels.h"
+
+namespace lca {
+
+namespace {
+
+constexpr int kTailKv = 0, kTailGate = 128, kTailIk = 256, kTailIg = 320;
+
+// BF16 input row of token p (absolute position) of sequence b: from the tail
+// if the token was appended by an earlier call, else from this call's input.
+__device__ __forceinline__ const uint16_t* token_row(const IngestArgs& a, int b, int64_t p, const uint16_t* in,
+                                                     int width, int tail_off) {
+  if (p < a.len) return a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width + tail_off;
+  return in + ((size_t)b * a.T + (size_t)(p - a.len)) * width;
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double half_wave_max(double v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// RoPE-rotated value of channel 64+c of token p (pair (2i, 2i+1), i = c/2):
+//   even: x0 cos - x1 sin;  odd: x0 sin + x1 cos;  angle p * inv_freq[i]; fp64.
+__device__ __forceinline__ double rope_channel(const uint16_t* kv_row, int c, int64_t p, const double* inv_freq) {
+  int i = c >> 1;
+  double x0 = (double)bf16_to_f32(kv_row[kNope + 2 * i]);
+  double x1 = (double)bf16_to_f32(kv_row[kNope + 2 * i + 1]);
+  double phi = (double)p * inv_freq[i];
+  double sn, cs;
+  sincos(phi, &sn, &cs);
+  return (c & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
+}
+
+// Write one 196-byte entry from the lane's nope value xn (dim c) and RoPE
+// value xr (dim 64+c): scale = fp32(amax / 448), code = E4M3FN(x / scale).
+__device__ __forceinline__ void write_entry(double xn, double xr, int c, uint8_t* codes, float* scale,
+                                            uint16_t* rope) {
+  double amax = wave_max(fabs(xn));
+  float s = (float)(amax / 448.0);
+  bool zero = (amax == 0.0) || (s == 0.0f);
+  uint32_t code = zero ? 0u : fp8_e4m3_encode(xn / (double)s);
+  codes[c] = (uint8_t)code;
+  rope[c] = bf16_encode(xr);
+  if (c == 0) *scale = zero ? 0.0f : s;
+}
+
+template <bool CSA>
+__global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
+  const int c = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t j = a.first + blockIdx.x;
+  const int m = a.m;
+  const int64_t p0 = j * m;
+
+  // pass 1: per-channel max of gate + bias over the block's m positions
+  double mu_n = -INFINITY, mu_r = -INFINITY, mu_i = -INFINITY;
+  for (int i = 0; i < m; ++i) {
+    const int64_t p = p0 + i;
+    const uint16_t* g = token_row(a, b, p, a.gate, kHeadDim, kTailGate);
+    mu_n = fmax(mu_n, (double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]);
+    mu_r = fmax(mu_r, (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]);
+    if (CSA) {
+      const uint16_t* gi = token_row(a, b, p, a.ig, kIdxDim, kTailIg);
+      mu_i = fmax(mu_i, (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]);
+    }
+  }
+  // pass 2: softmax denominators, summed in ascending position order
+  double S_n = 0.0, S_r = 0.0, S_i = 0.0;
+  for (int i = 0; i < m; ++i) {
+    const int64_t p = p0 + i;
+    const uint16_t* g = token_row(a, b, p, a.gate, kHeadDim, kTailGate);
+    S_n = S_n + pool_exp(((double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]) - mu_n);
+    S_r = S_r + pool_exp(((double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]) - mu_r);
+    if (CSA) {
+      const uint16_t* gi = token_row(a, b, p, a.ig, kIdxDim, kTailIg);
+      S_i = S_i + pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i);
+    }
+  }
+  // pass 3: weighted sum, one fma per position in ascending order
+  double y_n = 0.0, y_r = 0.0, y_i = 0.0;
+  for (int i = 0; i < m; ++i) {
+    const int64_t p = p0 + i;
+    const uint16_t* g = token_row(a, b, p, a.gate, kHeadDim, kTailGate);
+    const uint16_t* kv = token_row(a, b, p, a.kv, kHeadDim, kTailKv);
+    double w_n = pool_exp(((double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]) - mu_n) / S_n;
+    double w_r = pool_exp(((double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]) - mu_r) / S_r;
+    y_n = fma(w_n, (double)bf16_to_f32(kv[c]), y_n);
+    y_r = fma(w_r, rope_channel(kv, c, p, a.inv_freq), y_r);
+    if (CSA) {
+      const uint16_t* gi = token_row(a, b, p, a.ig, kIdxDim, kTailIg);
+      const uint16_t* ki = token_row(a, b, p, a.ik, kIdxDim, kTailIk);
+      double w_i = pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i) / S_i;
+      y_i = fma(w_i, (double)bf16_to_f32(ki[c]), y_i);
+    }
+  }
+
+  const size_t e = (size_t)b * a.max_blocks + (size_t)j;
+  write_entry(y_n, y_r, c, a.blk_codes + e * kNope, a.blk_scale + e, a.blk_rope + e * kRope);
+
+  if (CSA) {
+    // MX-FP4 indexer key: lanes 0..31 form scale block 0, lanes 32..63 block 1
+    double amax = half_wave_max(fabs(y_i));
+    int E = (amax == 0.0) ? -127 : mx_block_exp(amax);
+    uint32_t code = (amax == 0.0) ? 0u : fp4_e2m1_encode(ldexp(y_i, -E));
+    uint32_t hi = __shfl_down(code, 1, 64);
+    if ((c & 1) == 0) a.idx_codes[e * 32 + (c >> 1)] = (uint8_t)(code | (hi << 4));
+    if ((c & 31) == 0) a.idx_scale[e * 2 + (c >> 5)] = (uint8_t)((amax == 0.0) ? 0 : E + 127);
+  }
+}
+
+template <bool CSA>
+__global__ __launch_bounds__(64) void append_kernel(IngestArgs a) {
+  const int c = threadIdx.x;
+  const int b = blockIdx.y;
+  if ((int)blockIdx.x < a.n_win) {
+    // window entry of token s: its own kv, RoPE'd at s, its own FP8 scale
+    const int64_t s = a.first + blockIdx.x;
+    const uint16_t* kv = a.kv + ((size_t)b * a.T + (size_t)(s - a.len)) * kHeadDim;
+    double xn = (double)bf16_to_f32(kv[c]);
+    double xr = rope_channel(kv, c, s, a.inv_freq);
+    const size_t e = (size_t)b * a.ring + (size_t)(s % a.ring);
+    write_entry(xn, xr, c, a.win_codes + e * kNope, a.win_scale + e, a.win_rope + e * kRope);
+    return;
+  }
+  // tail: tokens of the block that is still incomplete after this call
+  const int64_t end = a.len + a.T;
+  int64_t tail_first = (end / a.m) * a.m;
+  if (tail_first < a.len) tail_first = a.len;
+  const int64_t p = tail_first + (blockIdx.x - a.n_win);
+  const size_t r = (size_t)b * a.T + (size_t)(p - a.len);
+  uint16_t* dst = a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width;
+  dst[kTailKv + c] = a.kv[r * kHeadDim + c];
+  dst[kTailKv + 64 + c] = a.kv[r * kHeadDim + 64 + c];
+  dst[kTailGate + c] = a.gate[r * kHeadDim + c];
+  dst[kTailGate + 64 + c] = a.gate[r * kHeadDim + 64 + c];
+  if (CSA) {
+    dst[kTailIk + c] = a.ik[r * kIdxDim + c];
+    dst[kTailIg + c] = a.ig[r * kIdxDim + c];
+  }
+}
+
+__global__ void fill_zero_kernel(uint4* p, size_t n16) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace
+
+hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  dim3 grid((unsigned)n_blocks, (unsigned)a.B);
+  if (csa) hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const IngestArgs& a, bool csa, int32_t n_tail, hipStream_t s) {
+  int64_t n = (int64_t)a.n_win + n_tail;
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)n, (unsigned)a.B);
+  if (csa) hipLaunchKernelGGL(append_kernel<true>, grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(append_kernel<false>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel rather than
+// a runtime memset, so the work can sit inside a captured graph.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)p, n16);
+  return hipGetLastError();
+}
+
+}  // namespace lca

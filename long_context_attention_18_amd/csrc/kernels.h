@@ -1,0 +1,107 @@
+// kernels.h -- internal launch interface between the C ABI (capi.hip) and
+// the gfx950 kernels. Not installed; the public interface is include/lca.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lca {
+
+constexpr int kHeadDim = 128;
+constexpr int kNope = 64;
+constexpr int kRope = 64;
+constexpr int kIdxDim = 64;
+
+// ---- indexer / top-k tiling --------------------------------------------
+constexpr int kScoreWaves = 4;                        // waves per score workgroup
+constexpr int kScoreIters = 16;                       // 32-block tiles per wave
+constexpr int kScoreChunk = kScoreWaves * kScoreIters * 32;  // blocks per workgroup (2048)
+constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
+constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
+constexpr int kCandCap = 8192;                        // candidates kept per query for the LDS select
+
+// ---- attention tiling ----------------------------------------------------
+constexpr int kAttnKeys = 64;                         // keys staged per iteration
+constexpr int kAttnTargetWGs = 512;                   // split-K target for small query counts
+constexpr int kPartStride = kHeadDim + 2;             // O[128], m, l per (query, split, head)
+
+struct IngestArgs {
+  const uint16_t* kv;      // [B][T][128]
+  const uint16_t* gate;    // [B][T][128]
+  const uint16_t* ik;      // [B][T][64]   (CSA) or null
+  const uint16_t* ig;      // [B][T][64]   (CSA) or null
+  const float* bias;       // [m][128]
+  const float* idx_bias;   // [m][64]     (CSA) or null
+  uint8_t* blk_codes;      // [B][max_blocks][64]
+  float* blk_scale;        // [B][max_blocks]
+  uint16_t* blk_rope;      // [B][max_blocks][64]
+  uint8_t* idx_codes;      // [B][max_blocks][32]
+  uint8_t* idx_scale;      // [B][max_blocks][2]
+  uint8_t* win_codes;      // [B][R][64]
+  float* win_scale;        // [B][R]
+  uint16_t* win_rope;      // [B][R][64]
+  uint16_t* tail;          // [B][m][tail_width]
+  int64_t len;             // tokens already appended before this call
+  int64_t max_blocks;
+  int64_t first;           // first block (compress) / first window token (append)
+  int32_t T;
+  int32_t m;
+  int32_t ring;
+  int32_t tail_width;
+  int32_t n_win;           // append: window tokens written
+  int32_t B;
+  double inv_freq[32];
+};
+
+struct ScoreArgs {
+  const uint16_t* qI;      // [B][Tq][HI][64]
+  const float* w;          // [B][Tq][HI]
+  const uint8_t* idx_codes;
+  const uint8_t* idx_scale;
+  uint32_t* keys;          // ws [B*Tq][max_blocks]
+  uint32_t* thr;           // ws [B*Tq][G]
+  uint64_t* cand;          // ws [B*Tq][kCandCap]
+  uint32_t* cand_cnt;      // ws [B*Tq]
+  int32_t* topk;           // [B][Tq][k]
+  int64_t len;
+  int64_t max_blocks;
+  int32_t Tq;
+  int32_t HI;
+  int32_t k;
+  int32_t m;
+  int32_t G;               // score chunks per query (stride of thr)
+};
+
+struct AttnArgs {
+  const uint16_t* q;       // [B][Tq][H][128]
+  const int32_t* topk;     // [B][Tq][k] (CSA) or null (HCA)
+  const uint8_t* blk_codes;
+  const float* blk_scale;
+  const uint16_t* blk_rope;
+  const uint8_t* win_codes;
+  const float* win_scale;
+  const uint16_t* win_rope;
+  uint16_t* out;           // [B][Tq][H][128]
+  float* lse;              // [B][Tq][H] or null
+  float* part;             // ws [B*Tq][S][H][kPartStride]
+  int64_t len;
+  int64_t max_blocks;
+  int32_t Tq;
+  int32_t H;
+  int32_t k;               // CSA: top-k slots; HCA: 0
+  int32_t m;
+  int32_t W;
+  int32_t ring;
+  int32_t splits;          // S
+  int32_t keys_per_split;  // multiple of kAttnKeys
+  int32_t dense;           // 1 = HCA (every visible block), 0 = CSA (topk list)
+  double inv_freq[32];
+};
+
+hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s);
+hipError_t launch_append(const IngestArgs& a, bool csa, int32_t n_tail, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s);
+hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s);
+
+}  // namespace lca

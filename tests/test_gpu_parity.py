@@ -1,0 +1,111 @@
+"""GPU parity: liblca.so through its C ABI against the CPU oracle, on seeded
+inputs of the workloads' shapes at sizes the oracle finishes in seconds
+(several score tiles, ragged tails, chunked ingestion, decode and chunked
+prefill). Pages: "DeepSeek-V4: a million-token context that agents can
+actually use", CSA/HCA paragraphs and Figures 3-4.
+"""
+import numpy as np
+import pytest
+
+from long_context_attention_18_amd import configs
+
+pytestmark = pytest.mark.gpu
+
+try:
+    from gpu_harness import LayerRun, check_queries, compare_cache
+except ImportError:  # run from the repository root
+    from tests.gpu_harness import LayerRun, check_queries, compare_cache
+
+
+def _ingest(run, chunks):
+    for T in chunks:
+        run.ingest(T)
+
+
+def _decode(run, n_steps, oracle_upto):
+    oc = [run.oracle_caches(b, oracle_upto) for b in range(run.B)]
+    worst = None
+    for _ in range(n_steps):
+        run.ingest(1)
+        qin, topk, out, lse = run.run_queries(1)
+        w = check_queries(run, oc, qin, topk, out, lse, [run.len - 1])
+        worst = w if worst is None else {k: max(worst[k], w[k]) for k in w}
+    return worst, oc
+
+
+def test_csa_small_decode_config0_shape():
+    """CSA m=4, B=1, 4096-token context ingested in ragged chunks, 16 decode queries (H=8, H_I=4, k=64)."""
+    layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
+    run = LayerRun(layer, B=1, max_ctx=4096 + 16, ring=128, sigma=0.02 * 1024 ** 0.5, hidden=1024)
+    _ingest(run, [1000, 7, 2, 3087])
+    assert run.len == 4096
+    worst, oc = _decode(run, 16, 4096 + 16)
+    rep = compare_cache(run, oc)
+    print("csa c0-shape worst", worst, rep)
+
+
+def test_hca_decode_ragged_tail():
+    """HCA m=128, B=2, context not a multiple of 128 (a live tail), H=64."""
+    layer = configs.Layer("hca", 128, n_heads=64, window=128)
+    run = LayerRun(layer, B=2, max_ctx=8192, ring=128)
+    _ingest(run, [4096, 3000, 33])
+    worst, oc = _decode(run, 4, run.len + 4)
+    compare_cache(run, oc)
+    print("hca worst", worst)
+
+
+def test_csa_decode_many_score_tiles():
+    """CSA with 3 score workgroups per query (N > 4096 blocks), B=2, H=64, H_I=8, k=256."""
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=256)
+    run = LayerRun(layer, B=2, max_ctx=20000, ring=128)
+    _ingest(run, [8192, 8192, 1999])
+    worst, oc = _decode(run, 3, run.len + 3)
+    compare_cache(run, oc)
+    print("csa multi-tile worst", worst)
+
+
+def test_dense_causal_identity_m1_gpu():
+    """m=1, k >= #blocks, window >= context: the layer is dense causal attention (each token twice)."""
+    layer = configs.Layer("csa", 1, n_heads=16, window=64, idx_heads=2, topk=64)
+    run = LayerRun(layer, B=1, max_ctx=64, ring=64)
+    _ingest(run, [40])
+    worst, oc = _decode(run, 5, 45)
+    print("m=1 worst", worst)
+
+
+def test_window_only_before_first_hca_block():
+    """HCA with t < 127: no visible block, textbook sliding-window attention."""
+    layer = configs.Layer("hca", 128, n_heads=16, window=32)
+    run = LayerRun(layer, B=1, max_ctx=256, ring=32)
+    _ingest(run, [90])
+    _decode(run, 3, 93)
+
+
+def test_csa_chunked_prefill_queries():
+    """Chunked prefill: Tq = 512 queries per call, causal block visibility, ring >= Tq + W - 1."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=64)
+    Tq = 512
+    run = LayerRun(layer, B=1, max_ctx=2048, ring=Tq + 127, max_tq=Tq, sigma=1.0)
+    oc = None
+    for c in range(4):
+        run.ingest(Tq)
+        qin, topk, out, lse = run.run_queries(Tq)
+        if oc is None or c == 3:
+            oc = [run.oracle_caches(b, 2048) for b in range(run.B)]
+        pos = list(range(run.len - Tq, run.len))
+        check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 7)) + [Tq - 1])
+    compare_cache(run, oc)
+
+
+def test_ingest_chunking_invariance():
+    """The same token stream ingested token by token, in 7s, or at once: identical cache bytes."""
+    layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
+    views = []
+    for chunks in ([1] * 130, [7] * 18 + [4], [130]):
+        run = LayerRun(layer, B=2, max_ctx=256, ring=128)
+        _ingest(run, chunks)
+        v = run.dev.views()
+        views.append({k: t.cpu().numpy().copy() for k, t in v.items()})
+    for k in views[0]:
+        assert np.array_equal(views[0][k], views[1][k]), k
+        assert np.array_equal(views[0][k], views[2][k]), k
