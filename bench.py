@@ -1,0 +1,417 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the hybrid compressed attention hot path on one MI355X.
+
+One step = one new token for each of the B sequences through every layer of
+the workload: compress the block the token completes (if any), append the
+token to the window state / tail, lightning-indexer scores and top-k (CSA
+layers), sparse (CSA) or dense (HCA) attention with the window under one
+softmax. All inputs of all steps are in HBM before the timed region. HIP
+events on the launch stream bracket the whole timed region and, in every
+step, the dominant kernel (the indexer's score stream over the FP4 keys), so
+its average duration is measured live on the stream it runs on. The steps are
+launched directly, behind a GPU spin that lasts until the host has enqueued
+the whole timed region ("prequeued"), so no step waits on the host.
+
+Prints one JSON line. `value` is whole-job decode throughput in query
+tokens/s (B tokens per step / step time). `roofline` is the dominant
+kernel's algorithmic bytes per launch (34 B per visible indexer key, plus the
+queries) over its measured duration, against MI355X's 8 TB/s.
+`cpu_baseline` times the plain C oracle on a bounded sample of the same
+workload (sequence 0, the first few timed decode queries) and doubles as a
+full-size parity check of those queries (top-k exact, attention within
+tolerance).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload csa_decode_1m|hca_decode_64k|stack8_decode_256k|csa_decode_small]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tok/s + HBM GB/s (% of peak), CSA/HCA layer at 1M ctx, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD_BY_NAME = {"csa_decode_small": 0, "hca_decode_64k": 1, "csa_decode_1m": 2, "stack8_decode_256k": 4}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="csa_decode_1m", choices=sorted(WORKLOAD_BY_NAME))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--oracle-queries", type=int, default=4, help="decode queries in the CPU-baseline sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 256 MiB device copy first (reference kernel for HBM counters)")
+    p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """HIP events through the HIP runtime torch already loaded (torch's own Event refuses graph capture
+    on ROCm). external=True records event nodes when the stream is being captured."""
+
+    def __init__(self):
+        import ctypes
+        import torch
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecordWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        # hipEventDisableSystemFence: no system-scope cache flush at the event, which would stretch the
+        # bracketed kernel's measured time
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+        return ev
+
+    def record(self, ev, external):
+        import torch
+        rc = self.hip.hipEventRecordWithFlags(ev, torch.cuda.current_stream().cuda_stream, 1 if external else 0)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecordWithFlags: {rc}")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return ms.value
+
+
+class Layer:
+    """One layer of the workload on the device: cache, workspace, per-step inputs and outputs."""
+
+    def __init__(self, wl, li, layer, n_steps, threads):
+        import numpy as np
+        import torch
+        import long_context_attention_18_amd as lca
+        from long_context_attention_18_amd import synth
+        self.np, self.torch, self.lca, self.synth = np, torch, lca, synth
+        self.wl, self.li, self.layer = wl, li, layer
+        self.B = wl.batch
+        self.csa = layer.csa
+        self.threads = threads
+        self.desc = lca.make_desc(layer.kind, layer.m, layer.n_heads, layer.window, layer.idx_heads, layer.topk)
+        self.max_ctx = wl.context + n_steps + layer.m
+        self.dev = lca.DeviceLayer(self.desc, self.B, self.max_ctx, layer.window, max_tq=1)
+        self.streams = [synth.TokenStream(wl.wid, li, b, self.csa, wl.sigma) for b in range(self.B)]
+        self.bias = synth.biases(wl.wid, li, layer.m, self.csa)
+        self.bias_dev = {k: torch.from_numpy(v).cuda() for k, v in self.bias.items()}
+
+    def _tokens_all(self, pos0, n):
+        """[B][n][w] token arrays for all sequences, generated in parallel threads."""
+        np = self.np
+        sub = max(4096, (n // max(1, self.threads // self.B) + 4095) // 4096 * 4096)
+        jobs = []
+        with cf.ThreadPoolExecutor(self.threads) as ex:
+            for b in range(self.B):
+                for p in range(pos0, pos0 + n, sub):
+                    jobs.append((b, p, ex.submit(self.streams[b].tokens, p, min(sub, pos0 + n - p))))
+            parts = {}
+            for b, p, f in jobs:
+                parts[(b, p)] = f.result()
+        keys = parts[(0, pos0)].keys()
+        out = {}
+        for k in keys:
+            out[k] = np.stack([np.concatenate([parts[(b, p)][k] for p in range(pos0, pos0 + n, sub)])
+                               for b in range(self.B)])
+        return out
+
+    def _upload(self, a):
+        np, torch = self.np, self.torch
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def prefill(self, chunk):
+        torch = self.torch
+        ctx = self.wl.context
+        for pos in range(0, ctx, chunk):
+            T = min(chunk, ctx - pos)
+            tok = {k: self._upload(v) for k, v in self._tokens_all(pos, T).items()}
+            self.dev.compress(tok["kv"], tok["gate"], self.bias_dev["bias"], tok.get("ik"), tok.get("ig"),
+                              self.bias_dev.get("idx_bias"))
+            self.dev.append(tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"))
+            torch.cuda.synchronize()
+
+    def make_step_inputs(self, n_steps):
+        """Per-step inputs, [S][B][1][...] on the device; per-step outputs."""
+        np, torch, synth = self.np, self.torch, self.synth
+        ctx = self.wl.context
+        tok = self._tokens_all(ctx, n_steps)  # [B][S][w]
+        self.step_tok = {k: self._upload(np.ascontiguousarray(v.transpose(1, 0, 2))[:, :, None, :])
+                         for k, v in tok.items()}
+        L = self.layer
+        proj = synth.QueryProjector(self.wl.wid, self.li, self.wl.hidden, L.n_heads, L.idx_heads)
+        pos = list(range(ctx, ctx + n_steps))
+        per = [proj.queries(b, pos) for b in range(self.B)]
+        qin = {k: np.stack([p[k] for p in per], axis=1)[:, :, None] for k in per[0]}  # [S][B][1][...]
+        self.step_q_host = qin
+        self.step_q = {k: self._upload(v) for k, v in qin.items()}
+        self.out = torch.empty((self.B, 1, L.n_heads, 128), dtype=torch.int16, device="cuda")
+        if self.csa:
+            self.topk = torch.empty((self.B, 1, L.topk), dtype=torch.int32, device="cuda")
+        self.kept = {}
+
+    def keep_outputs(self, steps):
+        """Give these steps their own output buffers (checked against the oracle afterwards)."""
+        torch = self.torch
+        for s in steps:
+            self.kept[s] = {"out": torch.empty_like(self.out)}
+            if self.csa:
+                self.kept[s]["topk"] = torch.empty_like(self.topk)
+
+    def step(self, s, ev_score=None, rec=None):
+        t = {k: v[s] for k, v in self.step_tok.items()}
+        q = {k: v[s] for k, v in self.step_q.items()}
+        out = self.kept[s]["out"] if s in self.kept else self.out
+        self.dev.compress(t["kv"], t["gate"], self.bias_dev["bias"], t.get("ik"), t.get("ig"),
+                          self.bias_dev.get("idx_bias"))
+        self.dev.append(t["kv"], t["gate"], t.get("ik"), t.get("ig"))
+        if self.csa:
+            topk = self.kept[s]["topk"] if s in self.kept else self.topk
+            if ev_score is not None:
+                rec(ev_score[0])
+            self.dev.index_score(q["qI"], q["w"])
+            if ev_score is not None:
+                rec(ev_score[1])
+            self.dev.topk_select(1, topk)
+            self.dev.sparse_attn(q["q"], topk, out)
+        else:
+            if ev_score is not None:
+                rec(ev_score[0])
+            self.dev.dense_attn(q["q"], out)
+            if ev_score is not None:
+                rec(ev_score[1])
+
+
+def score_bytes(layer, B, t):
+    """Algorithmic bytes of one score launch: 34 B per visible indexer key, plus qI and w."""
+    n = (t + 1) // layer.m
+    return B * (n * 34 + layer.idx_heads * (64 * 2 + 4))
+
+
+def attn_bytes(layer, B, t):
+    n = (t + 1) // layer.m
+    w = min(layer.window, t + 1)
+    return B * ((n + w) * 196 + layer.n_heads * 128 * 2 * 2)
+
+
+def src_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if taken on the current source."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("src_sha") != src:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def oracle_sample(layers, wl, first_step, n_queries, threads):
+    """Oracle on sequence 0 of the first layer: cache build (not timed as decode), then n decode queries timed."""
+    import numpy as np
+    import oracle as O
+    L = layers[0]
+    lay = L.layer
+    t_last = wl.context + first_step + n_queries - 1
+    upto = t_last + 1
+    t0 = time.perf_counter()
+    st = L.streams[0]
+    sub = 65536
+    with cf.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda p: st.tokens(p, min(sub, upto - p)), range(0, upto, sub)))
+    tok = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+    nb = upto // lay.m
+    bl = max(1, (nb + threads - 1) // threads)
+
+    def comp(j0):
+        j1 = min(nb, j0 + bl)
+        return O.compress(lay.m, tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"), 0, L.bias["bias"],
+                          L.bias.get("idx_bias"), j0, j1)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        cparts = list(ex.map(comp, range(0, nb, bl)))
+    d1 = {k: np.concatenate([p[k] for p in cparts]) for k in cparts[0]}
+    lo = max(0, wl.context + first_step - lay.window - 1)
+    win = O.window_entries(tok["kv"][lo:upto], lo)
+    build_s = time.perf_counter() - t0
+    results = []
+    t0 = time.perf_counter()
+    for i in range(n_queries):
+        s = first_step + i
+        t = wl.context + s
+        qh = {k: v[s, 0, 0] for k, v in L.step_q_host.items()}
+        r = O.layer_query(lay.kind, lay.m, lay.topk, lay.window, t, qh["q"], qh.get("qI"), qh.get("w"), d1,
+                          d1 if lay.csa else None, win, win_pos0=lo)
+        results.append((s, t, r))
+    dec_s = time.perf_counter() - t0
+    return results, dec_s, build_s, nb
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the hot path on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import long_context_attention_18_amd as lca
+    from long_context_attention_18_amd import configs, synth
+
+    lca.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = configs.WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
+    K, W = args.steps, args.warmup
+    S = W + K
+    log(f"workload {wl.name}: {wl.note}; warmup {W}, steps {K}")
+
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    t0 = time.perf_counter()
+    layers = [Layer(wl, li, layer, S, args.threads) for li, layer in enumerate(wl.layers)]
+    chunk = max(4096, min(65536, (1 << 26) // (wl.batch * 768)))
+    for L in layers:
+        L.prefill(chunk)
+        L.make_step_inputs(S)
+    n_check = 0 if args.no_cpu_baseline else max(1, args.oracle_queries)
+    layers[0].keep_outputs(range(W, W + n_check))
+    torch.cuda.synchronize()
+    log(f"caches filled to {wl.context} tokens x {wl.batch} seqs x {len(layers)} layer(s) in "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    dom = next((L for L in layers if L.csa), layers[0])
+    dom_kernel = "score_kernel" if dom.csa else "attn_kernel"
+    hev = HipEvents()
+    mode = "prequeued"
+    rec = lambda e: hev.record(e, False)
+    ev_begin, ev_end = hev.create(), hev.create()
+    ev_dom = [(hev.create(), hev.create()) for _ in range(K)]
+
+    def run_steps(steps, timed):
+        for i, s in enumerate(steps):
+            for L in layers:
+                L.step(s, ev_dom[i] if (timed and L is dom) else None, rec)
+
+    torch.cuda.synchronize()
+    if True:
+        run_steps(range(W), False)
+        torch.cuda.synchronize()
+        # keep the GPU busy while the host enqueues the whole timed region, so no step waits on the host
+        torch.cuda._sleep(int(5.0e5 * max(20, K)))
+        h0 = time.perf_counter()
+        rec(ev_begin)
+        run_steps(range(W, S), True)
+        rec(ev_end)
+        enq_ms = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - h0) * 1e3
+        log(f"host enqueue of the timed region: {enq_ms:.2f} ms")
+
+    total_ms = hev.elapsed_ms(ev_begin, ev_end)
+    ms_per_step = total_ms / K
+    dom_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in ev_dom])
+    value = wl.batch * K / (total_ms / 1e3)
+    log(f"timed {K} steps: {total_ms:.3f} ms on the GPU clock ({host_ms:.3f} ms host incl. spin); "
+        f"{ms_per_step * 1e3:.2f} us/step; {dom_kernel} {dom_us.mean():.2f} us avg "
+        f"(min {dom_us.min():.2f}, max {dom_us.max():.2f})")
+
+    # algorithmic bytes
+    t_steps = [wl.context + s for s in range(W, S)]
+    step_bytes = sum(configs.decode_step_bytes(L.layer, t + 1) * wl.batch for L in layers for t in t_steps) / K
+    if dom.csa:
+        dom_bytes = float(np.mean([score_bytes(dom.layer, wl.batch, t) for t in t_steps]))
+        src = src_sha(os.path.join(ROOT, "long_context_attention_18_amd", "csrc", "indexer.hip"))
+    else:
+        dom_bytes = float(np.mean([attn_bytes(dom.layer, wl.batch, t) for t in t_steps]))
+        src = src_sha(os.path.join(ROOT, "long_context_attention_18_amd", "csrc", "attention.hip"))
+    dom_avg_us = float(dom_us.mean())
+    achieved = dom_bytes / (dom_avg_us * 1e-6) / 1e9
+    traffic = load_traffic(dom_kernel, wl.name, src)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context,
+                   "layers": ",".join(l.kind.upper() for l in wl.layers),
+                   "n_heads": wl.layers[0].n_heads, "window": wl.layers[0].window,
+                   "topk": max((l.topk for l in wl.layers), default=0),
+                   "idx_heads": max((l.idx_heads for l in wl.layers), default=0), "launch": mode},
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_avg_us, 3)},
+        "step_hbm": {"algorithmic_bytes": int(step_bytes),
+                     "gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+
+    if n_check:
+        log("oracle sample (sequence 0) ...")
+        res, dec_s, build_s, nb = oracle_sample(layers, wl, W, n_check, args.threads)
+        L = layers[0]
+        parity = {"queries": len(res), "topk_exact": True, "max_rel_l2": 0.0, "max_abs": 0.0}
+        for s, t, r in res:
+            out = L.kept[s]["out"][0, 0].cpu().numpy().view(np.uint16)
+            g = synth.bf16_to_f32(out).astype(np.float64)
+            ref = r["out_f64"]
+            parity["max_rel_l2"] = max(parity["max_rel_l2"], float(np.linalg.norm(g - ref) / np.linalg.norm(ref)))
+            parity["max_abs"] = max(parity["max_abs"], float(np.abs(g - ref).max()))
+            if L.csa:
+                tk = L.kept[s]["topk"][0, 0].cpu().numpy()
+                parity["topk_exact"] &= bool(np.array_equal(tk, r["topk"]))
+        parity["ok"] = parity["topk_exact"] and parity["max_rel_l2"] <= 1e-2 and parity["max_abs"] <= 2e-2
+        result["cpu_baseline"] = {
+            "value": round(len(res) / dec_s, 4), "unit": "query-tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(res)} decode queries of sequence 0 of layer 0 at context {wl.context}-"
+                      f"{wl.context + len(res) - 1} ({nb} compressed blocks) through the plain C oracle "
+                      f"(scores, top-k, attention), single thread, {dec_s:.2f} s; its cache build for that "
+                      f"sequence ({build_s:.1f} s on {args.threads} threads) is not counted"}
+        result["parity_sample"] = parity
+        log(f"oracle: {dec_s:.2f} s for {len(res)} queries; parity {parity}")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

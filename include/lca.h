@@ -128,6 +128,15 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx);
 lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
 
+/* Where the indexer leaves its scores (CSA): after lca_csa_index_score (or
+ * lca_csa_indexer_topk) with this Tq on a cache of this shape, the workspace
+ * holds at this byte offset, for query q = b*Tq + i, a row of max_ctx/m
+ * uint32 keys, valid for the visible blocks j < (t+1)/m. key =
+ * bits(score) ^ (score < 0 ? 0xFFFFFFFF : 0x80000000), so keys order like the
+ * scores. Written only when some query sees more than topk blocks. Returns 0
+ * for HCA or invalid arguments. */
+size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t Tq, int64_t max_ctx);
+
 /* CSA compressor (CSA paragraph and Figure 3: every m = 4 tokens pooled into
  * one entry by softmax-gated pooling with a learned positional bias).
  * Consumes the tail plus T new tokens at positions len .. len+T-1 and writes

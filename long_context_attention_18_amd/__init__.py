@@ -59,6 +59,7 @@ _SIGNATURES = {
     "lca_cache_bind": (_I32, [_DP, _CP, _VP, _SZ, _I32, _I64, _I32, _VP]),
     "lca_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I64]),
     "lca_workspace_init": (_I32, [_VP, _SZ, _VP]),
+    "lca_workspace_scores_offset": (_SZ, [_DP, _I32, _I32, _I64]),
     "lca_csa_compress": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "lca_hca_compress": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP]),
     "lca_swa_tail_append": (_I32, [_CP, _VP, _VP, _VP, _VP, _I32, _VP]),
@@ -130,6 +131,10 @@ def lca_workspace_bytes(desc, batch, max_tq, max_ctx):
 
 def lca_workspace_init(ws, nbytes, stream=None):
     _check("lca_workspace_init", lib().lca_workspace_init(_ptr(ws), nbytes, _stream(stream)))
+
+
+def lca_workspace_scores_offset(desc, batch, Tq, max_ctx):
+    return lib().lca_workspace_scores_offset(ctypes.byref(desc), batch, Tq, max_ctx)
 
 
 def lca_csa_compress(cache, kv, gate, ik, ig, bias, idx_bias, T, stream=None):
@@ -233,6 +238,18 @@ class DeviceLayer:
 
     def dense_attn(self, q, out, lse=None, stream=None):
         lca_hca_dense_attn(self.cache, q, q.shape[1], out, lse, self.ws, self.ws_bytes, stream)
+
+    def index_scores(self, Tq):
+        """fp32 scores the last index_score / indexer_topk call left in the workspace: [B][Tq][max_blocks]."""
+        import torch
+        off = lca_workspace_scores_offset(self.desc, self.batch, Tq, self.max_ctx)
+        nb = self.cache.max_blocks
+        base = self.ws - self.ws_mem.data_ptr() + off
+        keys = self.ws_mem[base:base + self.batch * Tq * nb * 4].view(torch.int32).view(self.batch, Tq, nb)
+        k = keys.cpu().numpy().view("uint32")
+        import numpy as np
+        bits = np.where(k & 0x80000000, k ^ 0x80000000, ~k).astype(np.uint32)
+        return bits.view(np.float32)
 
     def views(self):
         """Typed torch views of the cache arrays (for checks)."""

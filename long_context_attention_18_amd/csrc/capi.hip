@@ -67,7 +67,7 @@ bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
 // Workspace: indexer (keys, thresholds, candidates, counters) then attention partials.
 struct WsLayout {
   size_t keys, thr, cand, cnt, part, total;
-  int32_t G;
+  int32_t G, G2;
 };
 
 int32_t score_chunks(int64_t max_blocks) { return (int32_t)((max_blocks + kScoreChunk - 1) / kScoreChunk); }
@@ -78,11 +78,12 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   const size_t nq = (size_t)B * (size_t)max_tq;
   size_t off = 0;
   W.G = score_chunks(max_blocks);
-  W.cnt = off; off = align_up(off + nq * 4);  // counters first: lca_workspace_init clears them
+  W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
+    W.cnt = off; off = align_up(off + nq * (size_t)W.G2 * 4);
     W.keys = off; off = align_up(off + nq * (size_t)max_blocks * 4);
     W.thr = off; off = align_up(off + nq * (size_t)W.G * 4);
-    W.cand = off; off = align_up(off + nq * (size_t)kCandCap * 8);
+    W.cand = off; off = align_up(off + nq * (size_t)max_blocks * 8);
   }
   // split-K partials: splits are used only while B*Tq < kAttnTargetWGs, and then
   // B*Tq*splits < 2*kAttnTargetWGs (see attn_splits)
@@ -215,6 +216,11 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
   return launch_status(launch_fill_zero(base_dev, L.total, (hipStream_t)stream));
 }
 
+size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t Tq, int64_t max_ctx) {
+  if (!desc_ok(desc) || desc->kind != LCA_KIND_CSA || batch < 1 || Tq < 1 || max_ctx < desc->m) return 0;
+  return ws_layout(desc, batch, Tq, max_ctx).keys;
+}
+
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx) {
   if (!desc_ok(desc) || batch < 1 || max_tq < 1 || max_ctx < desc->m) return 0;
   return ws_layout(desc, batch, max_tq, max_ctx).total;
@@ -284,7 +290,7 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.keys = (uint32_t*)(ws + W.keys);
   a.thr = (uint32_t*)(ws + W.thr);
   a.cand = (uint64_t*)(ws + W.cand);
-  a.cand_cnt = (uint32_t*)(ws + W.cnt);
+  a.seg_cnt = (uint32_t*)(ws + W.cnt);
   a.topk = topk_dev;
   a.len = cache->len;
   a.max_blocks = cache->max_blocks;
@@ -293,6 +299,7 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.k = cache->desc.topk;
   a.m = cache->desc.m;
   a.G = W.G;
+  a.G2 = W.G2;
   *out = a;
   return LCA_OK;
 }

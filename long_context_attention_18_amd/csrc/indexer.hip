@@ -21,7 +21,15 @@
 // adds two scaled exact terms, and one correctly rounded fp32 addition of two
 // exact terms is the fp32 rounding of the exact dot product. The keys stream
 // straight from HBM into the B operand (34 B per block, 16-B loads, fully
-// coalesced), so the kernel is a pure HBM stream. The head combine is done in
+// coalesced), so the kernel is a pure HBM stream. That argument needs the two
+// terms J_b * 2^(S_b - 256) (J_b < 2^13 in magnitude, S_b = sum of the two
+// E8M0 bytes of half b) to fit fp32's 24 bits together: measured on MI355X,
+// the instruction is not round-to-nearest once they do not. So every block
+// whose bytes give |S_0 - S_1| > 10, or a term outside fp32's normal range,
+// is flagged (a ballot over the wave) and rescored exactly in fp64 from the
+// codes -- the same sums in the same order as the definition. With real data
+// the flag never fires; it keeps the top-k exact for any input.
+// The head combine is done in
 // the MFMA output layout: lanes of row-group 0/2 hold heads 0..3, row-group
 // 1/3 heads 4..7, and one cross-lane move continues the fmaf chain.
 // Each workgroup also histograms the top 12 bits of the ordered score key in
@@ -30,11 +38,14 @@
 //
 // Kernel 2 (scan): L = the r-th largest T_c, r = ceil(G/2) chunks, k' =
 // ceil(k/r): at least r*k' >= k scores are >= L, so every winner is >= L.
-// Scores >= L are appended to a per-query candidate list (a few times k).
+// Each workgroup compacts its scores >= L, in index order, into its own
+// segment (wave ballots + one LDS prefix scan: no global atomics).
 //
 // Kernel 3 (select): radix select over the 64-bit keys (score_key << 32 |
-// ~j) of the candidates in LDS (or over all N scores if the list overflowed),
-// then a bitonic sort of the winners' indices. Exact for any input.
+// ~j) of the candidates gathered into LDS in index order (or over all N
+// scores when there are too many), then an order-preserving compaction of
+// the winners, so the output is ascending without a sort. Exact for any
+// input.
 #include "dev_formats.h"
 #include "kernels.h"
 
@@ -51,6 +62,35 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 __device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
+
+// twice the E2M1 value of a code: magnitudes {0, 1, 2, 3, 4, 6, 8, 12}, bit 3 the sign
+__device__ __forceinline__ int e2m1_x2(uint32_t c) {
+  int m = (int)(c & 7u);
+  int v = m < 4 ? m : (m < 6 ? 2 * m - 4 : 4 * m - 16);
+  return (c & 8u) ? -v : v;
+}
+
+// Exact score of one block from its FP4 codes: per head, the two 32-element
+// halves as integer dot products J_b of doubled values, the value
+// J_0 * 2^(S_0 - 256) + J_1 * 2^(S_1 - 256) summed in fp64 and rounded once to
+// fp32, then the ReLU-weighted fmaf chain over heads.
+__device__ __forceinline__ float exact_block_score(const uint8_t* kc, int ks0, int ks1, const uint32_t* qcode /* [8][8] */,
+                                                   const int* qscale /* [8][2] */, const float* w, int HI) {
+  float acc = 0.0f;
+  for (int h = 0; h < HI; ++h) {
+    int J[2] = {0, 0};
+    for (int c = 0; c < 64; ++c) {
+      const int kq = e2m1_x2((kc[c >> 1] >> (4 * (c & 1))) & 15u);
+      J[c >> 5] += e2m1_x2((qcode[h * 8 + (c >> 3)] >> (4 * (c & 7))) & 15u) * kq;
+    }
+    double D = 0.0;
+    D = D + ldexp((double)J[0], qscale[h * 2 + 0] + ks0 - 256);
+    D = D + ldexp((double)J[1], qscale[h * 2 + 1] + ks1 - 256);
+    float sh = (float)D;
+    acc = fmaf(w[h], sh > 0.0f ? sh : 0.0f, acc);
+  }
+  return acc == 0.0f ? 0.0f : acc;
+}
 
 __device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int tq) {
   int64_t t = a.len - a.Tq + tq;
@@ -77,87 +117,207 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return off + incl - v;
 }
 
+// FP4 E2M1 code of v (fp32), ties to even, saturating at +-6. The query
+// values x * 2^-E it is used on are exact in fp32 (a BF16 value times a power
+// of two inside fp32's range), so this makes the same decisions as the fp64
+// encoder.
+__device__ __forceinline__ uint32_t fp4_e2m1_encode_f32(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = fabsf(v);
+  if (a >= 6.0f) return sign | 7u;
+  int e = (a < 1.0f) ? 0 : ilogbf(a);
+  float r = rintf(ldexpf(a, 1 - e));  // 2..4 for a >= 1, 0..2 below
+  uint32_t ri = (uint32_t)r;
+  if (ri >= 4) { ri >>= 1; e += 1; }
+  if (ri == 0) return sign;
+  if (ri < 2) return sign | 1u;
+  if (e > 2) return sign | 7u;
+  return sign | ((uint32_t)(e + 1) << 1) | (ri - 2);
+}
+
+__device__ __forceinline__ float from_partner(float x, int odd_row) {
+  // value of lane l ^ 16 (v_permlane16_swap: odd rows of the first operand <-> even rows of the second)
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(odd_row ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t from_partner_u(uint32_t x, int odd_row) {
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return odd_row ? r[0] : r[1];
+}
+
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t thr_s;
+  __shared__ uint32_t qcode_s[8 * 8];  // quantised query: [head][8 words of 8 codes]
+  __shared__ int qscale_s[8 * 2];      // its E8M0 bytes: [head][half]
+  __shared__ int guard_s[6];           // block-scale bounds inside which the MFMA sum is exact
+  __shared__ uint32_t flag_blk[kScoreChunk];  // blocks to rescore exactly (offset in chunk)
+  __shared__ uint32_t flag_key[kScoreChunk];  // the key the MFMA path stored for them
+  __shared__ uint32_t n_flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int64_t N = visible_blocks(a, tq);
-  const int64_t j_begin = (int64_t)blockIdx.x * kScoreChunk;
-  // this call's candidate counter starts at zero (the scan kernel runs after this one)
-  if (blockIdx.x == 0 && tid == 0) a.cand_cnt[q] = 0;
+  const int N = (int)visible_blocks(a, tq);
+  const int j_begin = blockIdx.x * kScoreChunk;
   if (j_begin >= N) return;
   for (int i = tid; i < kHistBins; i += 256) hist[i] = 0;
-  if (tid == 0) thr_s = 0;
+  if (tid == 0) {
+    thr_s = 0;
+    n_flag = 0;
+  }
+  const float* wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
 
-  // ---- A operand: MXFP4 query. Lane: row r = lane%16 = (p, h) = (r/8, r%8), K-group g = lane/16.
-  const int r = lane & 15, g = lane >> 4, p = r >> 3, h = r & 7, half = g & 1;
-  uint32_t av[4] = {0u, 0u, 0u, 0u};
-  int sa = 127;
-  if ((g >> 1) == p && h < a.HI) {
-    const uint16_t* src = a.qI + (((size_t)b * a.Tq + tq) * a.HI + h) * kIdxDim + half * 32;
-    double amax = 0.0;
-    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)bf16_to_f32(src[i])));
-    if (amax == 0.0) {
-      sa = 0;
-    } else {
-      int E = mx_block_exp(amax);
-      sa = E + 127;
-      for (int i = 0; i < 32; ++i) {
-        uint32_t code = fp4_e2m1_encode(ldexp((double)bf16_to_f32(src[i]), -E));
-        av[i >> 3] |= code << (4 * (i & 7));
+  // ---- MX-FP4 query, once per workgroup (wave 0): lane -> head lane/8, eight dims 8*(lane%8)..
+  if (wave == 0) {
+    const int h = lane >> 3, part = lane & 7;
+    uint32_t word = 0, sbyte = 0;
+    if (h < a.HI) {
+      const uint16_t* src = a.qI + (((size_t)b * a.Tq + tq) * a.HI + h) * kIdxDim + part * 8;
+      const uint4 raw = *reinterpret_cast<const uint4*>(src);
+      float x[8];
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[2 * u] = __uint_as_float(rw[u] << 16);
+        x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      if (amax > 0.0f) {
+        int E = ilogbf(amax) - 2;
+        E = E < -127 ? -127 : (E > 127 ? 127 : E);
+        sbyte = (uint32_t)(E + 127);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= fp4_e2m1_encode_f32(ldexpf(x[i], -E)) << (4 * i);
       }
     }
-  }
-  const v8i A = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
-  // head weights of the four output rows this lane holds: rows 4g+i = (p' = g/2, h' = 4(g%2)+i)
-  float wv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int hh = 4 * (g & 1) + i;
-    wv[i] = hh < a.HI ? a.w[((size_t)b * a.Tq + tq) * a.HI + hh] : 0.0f;
+    if (h < 8) {
+      qcode_s[h * 8 + part] = word;
+      if ((part & 3) == 0) qscale_s[h * 2 + (part >> 2)] = (int)sbyte;
+    }
   }
   __syncthreads();
+  if (tid == 0) {
+    // exactness bounds over the live heads: |S0 - S1| <= 10 and 130 <= S_b <= 370, S_b = qs_b + ks_b
+    int dlo = -100000, dhi = 100000, k0lo = -100000, k0hi = 100000, k1lo = -100000, k1hi = 100000;
+    for (int h = 0; h < a.HI; ++h) {
+      const int q0 = qscale_s[2 * h], q1 = qscale_s[2 * h + 1], dq = q0 - q1;
+      dlo = max(dlo, -10 - dq);
+      dhi = min(dhi, 10 - dq);
+      k0lo = max(k0lo, 130 - q0);
+      k0hi = min(k0hi, 370 - q0);
+      k1lo = max(k1lo, 130 - q1);
+      k1hi = min(k1hi, 370 - q1);
+    }
+    guard_s[0] = dlo; guard_s[1] = dhi; guard_s[2] = k0lo; guard_s[3] = k0hi; guard_s[4] = k1lo; guard_s[5] = k1hi;
+  }
+  // ---- two A operands. Lane: row r = lane%16, K-group g = lane/16; row r holds (p, h) = (r/8, r%8)
+  // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only.
+  const int r = lane & 15, g = lane >> 4, p = r >> 3, odd = g & 1;
+  const int hA = r & 7, hB = (hA + 4) & 7;
+  uint32_t aA[4] = {0u, 0u, 0u, 0u}, aB[4] = {0u, 0u, 0u, 0u};
+  int sA = 127, sB = 127;
+  if ((g >> 1) == p) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      aA[u] = qcode_s[hA * 8 + odd * 4 + u];
+      aB[u] = qcode_s[hB * 8 + odd * 4 + u];
+    }
+    sA = qscale_s[hA * 2 + odd];
+    sB = qscale_s[hB * 2 + odd];
+  }
+  const v8i A0 = {(int)aA[0], (int)aA[1], (int)aA[2], (int)aA[3], 0, 0, 0, 0};
+  const v8i A1 = {(int)aB[0], (int)aB[1], (int)aB[2], (int)aB[3], 0, 0, 0, 0};
+  float wlo[4], whi[4];  // head weights 0..3 and 4..7 (0 for heads >= H_I)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wlo[i] = i < a.HI ? wq[i] : 0.0f;
+    whi[i] = i + 4 < a.HI ? wq[i + 4] : 0.0f;
+  }
+  __syncthreads();
+  const int dlo = guard_s[0], dhi = guard_s[1], k0lo = guard_s[2], k0hi = guard_s[3], k1lo = guard_s[4],
+            k1hi = guard_s[5];
 
   const size_t kbase = (size_t)b * a.max_blocks;
   uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
   const uint8_t* codes = a.idx_codes + kbase * 32;
   const uint8_t* scl = a.idx_scale + kbase * 2;
+  // all of this wave's key loads first (16 tiles x 16 B + 1 scale byte per lane in flight), then the MFMAs.
+  // Unconditional loads (address clamped to the last visible block, always in bounds) issue back to back.
+  const int wave_j0 = j_begin + wave * kScoreIters * 32;
+  const int n2 = 2 * (lane & 15) + (g >> 1);  // block of this lane inside a 32-block tile
+  uint4 bvs[kScoreIters];
+  int sbs[kScoreIters];
+#pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
-    const int64_t j0 = j_begin + ((int64_t)wave * kScoreIters + it) * 32;
-    if (j0 >= N) break;
-    // B operand: column n = lane%16 -> blocks j0+2n, j0+2n+1; K-group g -> (block 2n + g/2, half g%2)
-    const int64_t jb = j0 + 2 * (lane & 15) + (g >> 1);
-    uint4 bv = make_uint4(0u, 0u, 0u, 0u);
-    int sb = 0;
-    if (jb < N) {
-      bv = *reinterpret_cast<const uint4*>(codes + jb * 32 + half * 16);
-      sb = scl[jb * 2 + half];
-    }
-    const v8i Bv = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bv, acc, 4, 4, 0, sa, 0, sb);
-    // lane holds C[4g+i][lane%16]: block jb (p' = g/2), heads 4(g%2)+i
+    int jb = wave_j0 + it * 32 + n2;
+    jb = jb < N ? jb : N - 1;
+    bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + odd * 16);
+    sbs[it] = scl[(size_t)jb * 2 + odd];
+  }
+#pragma unroll
+  for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+    const int tA = 2 * pr, tB = 2 * pr + 1;
+    const bool liveA = wave_j0 + tA * 32 + n2 < N, liveB = wave_j0 + tB * 32 + n2 < N;
+    const uint4 bA = liveA ? bvs[tA] : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 bB = liveB ? bvs[tB] : make_uint4(0u, 0u, 0u, 0u);
+    const int sbA = liveA ? sbs[tA] : 0, sbB = liveB ? sbs[tB] : 0;
+    const v8i BA = {(int)bA.x, (int)bA.y, (int)bA.z, (int)bA.w, 0, 0, 0, 0};
+    const v8i BB = {(int)bB.x, (int)bB.y, (int)bB.z, (int)bB.w, 0, 0, 0, 0};
+    v4f accA = {0.0f, 0.0f, 0.0f, 0.0f}, accB = {0.0f, 0.0f, 0.0f, 0.0f};
+    accA = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, BA, accA, 4, 4, 0, sA, 0, sbA);
+    accB = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, BB, accB, 4, 4, 0, sB, 0, sbB);
+    // rows 4g..4g+3 of this lane: tile A gives heads 0..3 on even g, 4..7 on odd g; tile B the reverse.
+    // Heads 0..3 first (fmaf chain from +0), then the partner lane (g^1) continues with heads 4..7.
     float e = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e = fmaf(wv[i], relu(acc[i]), e);
-    float s = __shfl_up(e, 16, 64);  // heads 0..3 of the same block, from row-group g-1
+    for (int i = 0; i < 4; ++i) e = fmaf(wlo[i], relu(odd ? accB[i] : accA[i]), e);
+    float s = from_partner(e, odd);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(wv[i], relu(acc[i]), s);
-    if ((g & 1) && jb < N) {
+    for (int i = 0; i < 4; ++i) s = fmaf(whi[i], relu(odd ? accA[i] : accB[i]), s);
+    // this lane now holds the final score of block jb: tile A if g is odd, tile B if even
+    const int jb = wave_j0 + (odd ? tA : tB) * 32 + n2;
+    const uint32_t other = from_partner_u((uint32_t)sbA | ((uint32_t)sbB << 8), odd);
+    const int own = odd ? sbA : sbB;
+    const int oth = odd ? (int)(other & 0xFFu) : (int)(other >> 8);
+    const int ks0 = odd ? oth : own, ks1 = odd ? own : oth;
+    const int dk = ks0 - ks1;
+    const bool bad = dk < dlo || dk > dhi || ks0 < k0lo || ks0 > k0hi || ks1 < k1lo || ks1 > k1hi;
+    if (jb < N) {
       if (s == 0.0f) s = 0.0f;
-      uint32_t key = order_key(s);
+      const uint32_t key = order_key(s);
       keys[jb] = key;
       atomicAdd(&hist[key >> 20], 1u);
+      if (bad) {
+        const uint32_t f = atomicAdd(&n_flag, 1u);
+        flag_blk[f] = (uint32_t)(jb - j_begin);
+        flag_key[f] = key;
+      }
+    }
+  }
+  __syncthreads();
+  // exact rescoring of the flagged blocks (none with real data), fixing the histogram and the stored key
+  for (uint32_t f = tid; f < n_flag; f += 256) {
+    const int jb = j_begin + (int)flag_blk[f];
+    const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
+                                       qcode_s, qscale_s, wq, a.HI);
+    const uint32_t key = order_key(ex);
+    if (key != flag_key[f]) {
+      atomicSub(&hist[flag_key[f] >> 20], 1u);
+      atomicAdd(&hist[key >> 20], 1u);
+      keys[jb] = key;
     }
   }
   __syncthreads();
 
   // ---- chunk lower bound: lowest key of the histogram bin holding the k'-th largest score
-  const int64_t G_q = (N + kScoreChunk - 1) / kScoreChunk;
-  const int64_t rr = (G_q + 1) / 2;
+  const int G_q = (N + kScoreChunk - 1) / kScoreChunk;
+  const int rr = (G_q + 1) / 2;
   const uint32_t kp = (uint32_t)((a.k + rr - 1) / rr);
   const int top = kHistBins - 16 * tid;  // this thread's bins: [top-16, top), scanned downwards
   uint32_t cnt = 0;
@@ -179,9 +339,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }
 
 __global__ __launch_bounds__(256) void scan_kernel(ScoreArgs a) {
+  constexpr int kPer = kScanPerWG / 256;  // keys per thread: j = start + u*256 + tid
   __shared__ uint32_t sthr[2048];
   __shared__ uint32_t L_s;
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint32_t cnt_s[kPer * 4];    // candidates per (u, wave), then their exclusive offsets
+  __shared__ uint32_t total_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int tq = q % a.Tq;
   const int64_t N = visible_blocks(a, tq);
@@ -206,32 +369,55 @@ __global__ __launch_bounds__(256) void scan_kernel(ScoreArgs a) {
   const uint32_t L = L_s;
   const int64_t end = (start + kScanPerWG < N) ? start + kScanPerWG : N;
   const uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
-  uint64_t* cand = a.cand + (size_t)q * kCandCap;
-  for (int64_t base = start; base < end; base += 256) {
-    const int64_t j = base + tid;
-    uint32_t key = 0;
-    bool pred = false;
-    if (j < end) {
-      key = keys[j];
-      pred = key >= L;
-    }
-    uint64_t mask = __ballot(pred);
-    if (mask == 0) continue;
-    uint32_t n = (uint32_t)__popcll(mask);
-    uint32_t pos = 0;
-    if (lane == 0) pos = atomicAdd(&a.cand_cnt[q], n);
-    pos = __shfl(pos, 0, 64);
-    uint32_t rank = (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-    if (pred && pos + rank < (uint32_t)kCandCap)
-      cand[pos + rank] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+  uint32_t kv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t j = start + (int64_t)u * 256 + tid;
+    kv[u] = j < end ? keys[j] : 0u;
   }
+  // candidates (key >= L) keep index order: (u, wave, lane) order is ascending j
+  uint64_t masks[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t j = start + (int64_t)u * 256 + tid;
+    masks[u] = __ballot(j < end && kv[u] >= L);
+    if (lane == 0) cnt_s[u * 4 + wave] = (uint32_t)__popcll(masks[u]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scan of the kPer*4 counts in (u, wave) order; two per lane
+    uint32_t c0 = cnt_s[2 * lane], c1 = cnt_s[2 * lane + 1];
+    uint32_t incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    uint32_t excl = incl - c0 - c1;
+    cnt_s[2 * lane] = excl;
+    cnt_s[2 * lane + 1] = excl + c0;
+    if (lane == 63) total_s = incl;
+  }
+  __syncthreads();
+  uint64_t* seg = a.cand + (size_t)q * a.max_blocks + start;  // this workgroup's segment
+  const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if ((masks[u] >> lane) & 1ull) {
+      const uint32_t pos = cnt_s[u * 4 + wave] + (uint32_t)__popcll(masks[u] & lt);
+      const uint32_t j = (uint32_t)(start + (int64_t)u * 256 + tid);
+      seg[pos] = ((uint64_t)kv[u] << 32) | (uint64_t)(0xFFFFFFFFu - j);
+    }
+  }
+  if (tid == 0) a.seg_cnt[(size_t)q * a.G2 + blockIdx.x] = total_s;
 }
 
 __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   __shared__ uint64_t cs[kCandCap];
-  __shared__ int32_t list[2048];
+  __shared__ uint32_t seg_off[2049];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sel_digit, sel_above, sel_count, n_win;
+  __shared__ uint32_t wsum[8];
+  __shared__ uint32_t sel_digit, sel_above, sel_count;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.x;
   const int tq = q % a.Tq;
@@ -241,23 +427,37 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
     for (int i = tid; i < a.k; i += 512) out[i] = (i < N) ? i : -1;
     return;
   }
-  const uint32_t total = a.cand_cnt[q];
+  // segment offsets of the scan's ordered candidate lists
+  const int G2_q = (int)((N + kScanPerWG - 1) / kScanPerWG);
+  if (tid == 0) {
+    uint32_t acc = 0;
+    for (int g = 0; g < G2_q; ++g) {
+      seg_off[g] = acc;
+      acc += a.seg_cnt[(size_t)q * a.G2 + g];
+    }
+    seg_off[G2_q] = acc;
+  }
+  __syncthreads();
+  const uint32_t total = seg_off[G2_q];
   const bool fast = total <= (uint32_t)kCandCap;
   const int64_t n = fast ? (int64_t)total : N;
   const uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
   if (fast) {
-    const uint64_t* cand = a.cand + (size_t)q * kCandCap;
-    for (int64_t i = tid; i < n; i += 512) cs[i] = cand[i];
+    const uint64_t* cand = a.cand + (size_t)q * a.max_blocks;
+    for (int g = 0; g < G2_q; ++g) {
+      const uint32_t c = seg_off[g + 1] - seg_off[g];
+      for (uint32_t i = tid; i < c; i += 512) cs[seg_off[g] + i] = cand[(size_t)g * kScanPerWG + i];
+    }
   }
-  if (tid == 0) n_win = 0;
   __syncthreads();
+  // element i in index order: the ordered candidates, or (slow path) every visible block
   auto elem = [&](int64_t i) -> uint64_t {
     if (fast) return cs[i];
     return ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
   };
 
-  // radix select of the k-th largest 64-bit key, 8 bits at a time, stopping
-  // as soon as the bin that holds it is taken whole
+  // radix select of the k-th largest 64-bit key (score key, then lower index first),
+  // 8 bits at a time, stopping as soon as the bin that holds it is taken whole
   uint64_t prefix = 0, mask = 0;
   uint32_t need = (uint32_t)a.k;  // N > k here
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -299,36 +499,29 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
     mask |= (uint64_t)0xFF << shift;
     if (sel_count == need) break;
   }
-  // winners: every element whose determined bits are >= the selected prefix
-  for (int64_t i = tid; i < n; i += 512) {
-    uint64_t e = elem(i);
+  // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run
+  const int64_t per = (n + 511) / 512;
+  const int64_t i0 = (int64_t)tid * per;
+  const int64_t i1 = (i0 + per < n) ? i0 + per : n;
+  uint32_t mine = 0;
+  for (int64_t i = i0; i < i1; ++i) mine += ((elem(i) & mask) >= prefix) ? 1u : 0u;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - mine;
+  for (int w = 0; w < wave; ++w) pos += wsum[w];
+  for (int64_t i = i0; i < i1; ++i) {
+    const uint64_t e = elem(i);
     if ((e & mask) >= prefix) {
-      uint32_t s = atomicAdd(&n_win, 1u);
-      if (s < 2048u) list[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
+      if (pos < (uint32_t)a.k) out[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
+      ++pos;
     }
   }
-  __syncthreads();
-  const int kk = a.k;
-  int n2 = 1;
-  while (n2 < kk) n2 <<= 1;
-  for (int i = kk + tid; i < n2; i += 512) list[i] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += 512) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool asc = (lo & size) == 0;
-        int32_t x = list[lo], y = list[hi];
-        if ((x > y) == asc) {
-          list[lo] = y;
-          list[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < kk; i += 512) out[i] = list[i];
 }
 
 }  // namespace

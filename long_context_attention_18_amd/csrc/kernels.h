@@ -17,7 +17,7 @@ constexpr int kScoreIters = 16;                       // 32-block tiles per wave
 constexpr int kScoreChunk = kScoreWaves * kScoreIters * 32;  // blocks per workgroup (2048)
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
-constexpr int kCandCap = 8192;                        // candidates kept per query for the LDS select
+constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
 
 // ---- attention tiling ----------------------------------------------------
 constexpr int kAttnKeys = 64;                         // keys staged per iteration
@@ -59,8 +59,8 @@ struct ScoreArgs {
   const uint8_t* idx_scale;
   uint32_t* keys;          // ws [B*Tq][max_blocks]
   uint32_t* thr;           // ws [B*Tq][G]
-  uint64_t* cand;          // ws [B*Tq][kCandCap]
-  uint32_t* cand_cnt;      // ws [B*Tq]
+  uint64_t* cand;          // ws [B*Tq][max_blocks]: ordered candidates, one segment per scan workgroup
+  uint32_t* seg_cnt;       // ws [B*Tq][G2]: candidates per segment
   int32_t* topk;           // [B][Tq][k]
   int64_t len;
   int64_t max_blocks;
@@ -69,6 +69,7 @@ struct ScoreArgs {
   int32_t k;
   int32_t m;
   int32_t G;               // score chunks per query (stride of thr)
+  int32_t G2;              // scan segments per query (stride of seg_cnt)
 };
 
 struct AttnArgs {

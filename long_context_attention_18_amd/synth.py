@@ -32,9 +32,12 @@ T_KV, T_GATE, T_IK, T_IG, T_HID, T_WQ, T_WQI, T_WW, T_BIAS, T_IBIAS = range(10)
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bfloat16 bit patterns, round to nearest even (storage conversion)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rnd = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + rnd) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = (u >> 16) & 1          # new array; u (a view of x) is not modified
+    r += 0x7FFF
+    r += u                     # no uint32 overflow for finite inputs
+    r >>= 16
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0

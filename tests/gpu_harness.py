@@ -53,8 +53,10 @@ def bf16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 class LayerRun:
     """One layer of B sequences: seeded inputs, device cache, oracle mirror."""
 
-    def __init__(self, layer, B, max_ctx, ring, max_tq=1, workload=90, layer_id=0, sigma=1.28, hidden=512):
+    def __init__(self, layer, B, max_ctx, ring, max_tq=1, workload=90, layer_id=0, sigma=1.28, hidden=512,
+                 transform=None, qtransform=None):
         import long_context_attention_18_amd as lca
+        self.transform, self.qtransform = transform, qtransform
         self.layer, self.B = layer, B
         self.csa = layer.csa
         self.m = layer.m
@@ -66,8 +68,13 @@ class LayerRun:
         self.proj = synth.QueryProjector(workload, layer_id, hidden, layer.n_heads, layer.idx_heads)
         self.len = 0
 
+    def tokens(self, b, pos0, n):
+        tok = self.streams[b].tokens(pos0, n)
+        return self.transform(tok, pos0) if self.transform else tok
+
     def ingest(self, T):
-        tok = synth.token_batch(self.streams, self.len, T)
+        parts = [self.tokens(b, self.len, T) for b in range(self.B)]
+        tok = {k: np.stack([p[k] for p in parts]) for k in parts[0]}
         d = {k: to_dev(v) for k, v in tok.items()}
         if self.csa:
             self.dev.compress(d["kv"], d["gate"], self.bias_dev["bias"], d["ik"], d["ig"], self.bias_dev["idx_bias"])
@@ -80,7 +87,8 @@ class LayerRun:
     def queries(self, positions):
         """Per-sequence query inputs at absolute positions -> stacked arrays [B][n][...]."""
         per = [self.proj.queries(b, positions) for b in range(self.B)]
-        return {k: np.stack([p[k] for p in per]) for k in per[0]}
+        out = {k: np.stack([p[k] for p in per]) for k in per[0]}
+        return self.qtransform(out) if self.qtransform else out
 
     def run_queries(self, Tq):
         """Queries at the last Tq positions -> (q inputs, topk or None, out bf16, lse)."""
@@ -91,9 +99,13 @@ class LayerRun:
         out = torch.empty((self.B, Tq, H, 128), dtype=torch.int16, device="cuda")
         lse = torch.empty((self.B, Tq, H), dtype=torch.float32, device="cuda")
         topk = None
+        self.last_scores = None
         if self.csa:
             topk = torch.full((self.B, Tq, self.layer.topk), -7, dtype=torch.int32, device="cuda")
             self.dev.indexer_topk(to_dev(qin["qI"]), to_dev(qin["w"]), topk)
+            torch.cuda.synchronize()
+            if self.len // self.m > self.layer.topk:
+                self.last_scores = self.dev.index_scores(Tq)
             self.dev.sparse_attn(to_dev(qin["q"]), topk, out, lse)
         else:
             self.dev.dense_attn(to_dev(qin["q"]), out, lse)
@@ -102,7 +114,7 @@ class LayerRun:
 
     # ---------------------------------------------------------------- oracle side
     def oracle_caches(self, b, upto):
-        tok = self.streams[b].tokens(0, upto)
+        tok = self.tokens(b, 0, upto)
         d1 = O.compress(self.m, tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"), 0, self.bias["bias"],
                         self.bias.get("idx_bias"), 0, upto // self.m)
         win = O.window_entries(tok["kv"], 0)
@@ -153,7 +165,7 @@ def attn_error(got_bf16: np.ndarray, ref_f64: np.ndarray):
 
 def check_queries(run: LayerRun, oracle_by_seq, qin, topk, out, lse, positions, sample=None):
     """Oracle layer_query for each (seq, query) and the comparison bar."""
-    worst = {"rel": 0.0, "abs": 0.0, "lse": 0.0}
+    worst = {"rel": 0.0, "abs": 0.0, "lse": 0.0, "scores_checked": 0}
     idx = range(len(positions)) if sample is None else sample
     for b in range(run.B):
         d1, win = oracle_by_seq[b]
@@ -162,6 +174,13 @@ def check_queries(run: LayerRun, oracle_by_seq, qin, topk, out, lse, positions, 
             r = O.layer_query(run.layer.kind, run.m, run.layer.topk, run.layer.window, t, qin["q"][b, i],
                               qin.get("qI", [None] * run.B)[b][i] if run.csa else None,
                               qin["w"][b, i] if run.csa else None, d1, d1 if run.csa else None, win)
+            if run.csa and run.last_scores is not None:
+                n = len(r["scores"])
+                gs = run.last_scores[b, i, :n]
+                bad = np.nonzero(gs.view(np.uint32) != r["scores"].view(np.uint32))[0]
+                assert bad.size == 0, f"seq {b} t={t}: {bad.size} scores differ, e.g. block {bad[:4]} " \
+                                      f"gpu {gs[bad[:4]]} oracle {r['scores'][bad[:4]]}"
+                worst["scores_checked"] += n
             if run.csa:
                 assert np.array_equal(topk[b, i], r["topk"]), \
                     f"seq {b} query t={t}: top-k differs: gpu-only {sorted(set(topk[b, i]) - set(r['topk']))[:8]} " \

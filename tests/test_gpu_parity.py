@@ -7,7 +7,7 @@ actually use", CSA/HCA paragraphs and Figures 3-4.
 import numpy as np
 import pytest
 
-from long_context_attention_18_amd import configs
+from long_context_attention_18_amd import configs, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +109,33 @@ def test_ingest_chunking_invariance():
     for k in views[0]:
         assert np.array_equal(views[0][k], views[1][k]), k
         assert np.array_equal(views[0][k], views[2][k]), k
+
+
+def test_indexer_exact_on_wide_scale_gaps():
+    """Indexer keys whose 32-dim halves differ by ~2^20 in size, keys with an all-zero half, and a
+    query head with a tiny half: every score and the top-k still equal the oracle's bit for bit
+    (the scaled MFMA alone is not exact there; the flagged fp64 rescoring is)."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=128)
+
+    def transform(tok, pos0):
+        f = synth.bf16_to_f32(tok["ik"]).copy()
+        blk = (pos0 + np.arange(f.shape[0])) // 4
+        f[blk % 3 == 0, 32:] *= np.float32(2.0 ** -20)
+        f[blk % 7 == 1, :32] = 0.0
+        f[blk % 11 == 5, :32] *= np.float32(2.0 ** -13)
+        out = dict(tok)
+        out["ik"] = synth.bf16_bits(f)
+        return out
+
+    def qtransform(qin):
+        f = synth.bf16_to_f32(qin["qI"]).copy()
+        f[:, :, 3, 32:] *= np.float32(2.0 ** -25)
+        out = dict(qin)
+        out["qI"] = synth.bf16_bits(f)
+        return out
+
+    run = LayerRun(layer, B=2, max_ctx=6000, ring=128, transform=transform, qtransform=qtransform)
+    _ingest(run, [5000])
+    worst, oc = _decode(run, 3, 5003)
+    assert worst["scores_checked"] > 0
+    compare_cache(run, oc)
