@@ -120,11 +120,13 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
 
 /* Scratch one call of lca_csa_indexer_topk / lca_csa_sparse_attn /
  * lca_hca_dense_attn needs for up to max_tq queries per sequence at up to
- * max_ctx tokens. Nothing in it survives a call (every call initialises what
- * it reads), so a workspace may be shared by caches of the same or smaller
- * shape; calls sharing one workspace must not overlap in time.
- * lca_workspace_init() zero-fills it (optional; useful for reproducible
- * memory dumps). */
+ * max_ctx tokens. For CSA it begins with one 16 KiB histogram per query that
+ * must be zero when an indexer call starts: zero the workspace once with
+ * lca_workspace_init() before its first use; every completed
+ * lca_csa_indexer_topk (or lca_csa_topk_select) leaves it zero again.
+ * Everything else in it is rewritten by each call. A workspace may be shared
+ * by caches of the same or smaller shape; calls sharing one workspace must
+ * not overlap in time. */
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx);
 lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
 
@@ -188,7 +190,8 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
 /* The two method steps of lca_csa_indexer_topk as separate calls (same
  * arguments; the scores travel in the workspace, so both calls must get the
  * same cache state, Tq and workspace, in this order, with nothing else using
- * the workspace in between):
+ * the workspace in between; an lca_csa_index_score without its
+ * lca_csa_topk_select leaves the workspace histograms dirty):
  *  lca_csa_index_score: the lightning-indexer scores of every visible block
  *    of the Tq queries (an HBM stream over the FP4 keys);
  *  lca_csa_topk_select: the per-query top-k of those scores into topk_dev. */

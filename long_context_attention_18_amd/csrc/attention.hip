@@ -89,9 +89,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           float x0 = bf16_to_f32((uint16_t)(w & 0xFFFFu));
           float x1 = bf16_to_f32((uint16_t)(w >> 16));
           const int pi = (d0 - kNope) / 2 + u;
-          double sn, cs;
-          sincos((double)t * a.inv_freq[pi], &sn, &cs);
-          float c = (float)cs, s = (float)sn;
+          // angle t * f reduced to [-pi, pi] in fp64 with 2*pi as a double plus its remainder (error
+          // about 1e-10 rad at a million positions), then fp32 sin/cos: the rotated query is rounded to
+          // bf16, far coarser than either step
+          const double phi = (double)t * a.inv_freq[pi];
+          const double n = rint(phi * 0.15915494309189535);
+          const double r = (phi - n * 6.28318530717958623) - n * 2.4492935982947064e-16;
+          float s, c;
+          sincosf((float)r, &s, &c);
           v[2 * u] = f32_to_bf16(x0 * c - x1 * s);
           v[2 * u + 1] = f32_to_bf16(x0 * s + x1 * c);
         }
@@ -272,18 +277,29 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // Joint softmax across splits: M = max m_s, L = sum l_s e^(m_s - M),
 // out = sum O_s e^(m_s - M) / L, lse = M + log L.
 __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
+  __shared__ float ms[kMaxSplits], ls[kMaxSplits];
   const int q = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const float* base = a.part + ((size_t)q * a.splits * a.H + h) * kPartStride;
   const size_t sstride = (size_t)a.H * kPartStride;
+  for (int s = d; s < a.splits; s += 128) {
+    ms[s] = base[s * sstride + kHeadDim];
+    ls[s] = base[s * sstride + kHeadDim + 1];
+  }
+  // all of this thread's partial outputs in flight at once
+  float o[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) o[s] = s < a.splits ? base[s * sstride + d] : 0.0f;
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, base[s * sstride + kHeadDim]);
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ms[s]);
   float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = base[s * sstride + kHeadDim];
-    if (ms == -INFINITY) continue;
-    const float f = __expf(ms - M);
-    L += base[s * sstride + kHeadDim + 1] * f;
-    acc += base[s * sstride + d] * f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < a.splits && ms[s] != -INFINITY) {
+      const float f = __expf(ms[s] - M);
+      L += ls[s] * f;
+      acc += o[s] * f;
+    }
   }
   const int b = q / a.Tq, tq = q % a.Tq;
   a.out[(((size_t)b * a.Tq + tq) * a.H + h) * kHeadDim + d] = f32_to_bf16(acc / L);

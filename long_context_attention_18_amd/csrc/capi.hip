@@ -66,23 +66,22 @@ bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
 
 // Workspace: indexer (keys, thresholds, candidates, counters) then attention partials.
 struct WsLayout {
-  size_t keys, thr, cand, cnt, part, total;
-  int32_t G, G2;
+  size_t keys, ghist, cand, cnt, part, total;
+  int32_t G2;
 };
-
-int32_t score_chunks(int64_t max_blocks) { return (int32_t)((max_blocks + kScoreChunk - 1) / kScoreChunk); }
 
 WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t max_ctx) {
   WsLayout W{};
   const int64_t max_blocks = max_ctx / d->m;
   const size_t nq = (size_t)B * (size_t)max_tq;
   size_t off = 0;
-  W.G = score_chunks(max_blocks);
   W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
+    // the per-query histograms first: they must be zero when a call starts (lca_workspace_init, then
+    // every select leaves them zero), and a smaller-Tq call keeps them at the same place
+    W.ghist = off; off = align_up(off + (size_t)B * max_tq * kHistBins * 4);
     W.cnt = off; off = align_up(off + nq * (size_t)W.G2 * 4);
     W.keys = off; off = align_up(off + nq * (size_t)max_blocks * 4);
-    W.thr = off; off = align_up(off + nq * (size_t)W.G * 4);
     W.cand = off; off = align_up(off + nq * (size_t)max_blocks * 8);
   }
   // split-K partials: splits are used only while B*Tq < kAttnTargetWGs, and then
@@ -97,6 +96,7 @@ void attn_splits(int64_t n_keys, int32_t nq, int32_t* splits, int32_t* per_split
   int64_t s = 1;
   if (nq < kAttnTargetWGs) s = (kAttnTargetWGs + nq - 1) / nq;
   if (s > max_chunks) s = max_chunks;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   int64_t per = (n_keys + s - 1) / s;
   per = (per + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
@@ -288,7 +288,7 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.idx_codes = cache->idx_codes_dev;
   a.idx_scale = cache->idx_scale_dev;
   a.keys = (uint32_t*)(ws + W.keys);
-  a.thr = (uint32_t*)(ws + W.thr);
+  a.ghist = (uint32_t*)(ws + W.ghist);
   a.cand = (uint64_t*)(ws + W.cand);
   a.seg_cnt = (uint32_t*)(ws + W.cnt);
   a.topk = topk_dev;
@@ -298,7 +298,6 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.HI = cache->desc.idx_heads;
   a.k = cache->desc.topk;
   a.m = cache->desc.m;
-  a.G = W.G;
   a.G2 = W.G2;
   *out = a;
   return LCA_OK;

@@ -32,14 +32,15 @@
 // The head combine is done in
 // the MFMA output layout: lanes of row-group 0/2 hold heads 0..3, row-group
 // 1/3 heads 4..7, and one cross-lane move continues the fmaf chain.
-// Each workgroup also histograms the top 12 bits of the ordered score key in
-// LDS and emits a lower bound T_c below which fewer than k' of its scores lie
-// ("at least k' scores of this chunk are >= T_c").
+// Each workgroup also counts, per bin of the top 12 bits of the ordered
+// score key, its scores from its maximum down to a quarter of it, and adds
+// those ~17 bins to a per-query global histogram.
 //
-// Kernel 2 (scan): L = the r-th largest T_c, r = ceil(G/2) chunks, k' =
-// ceil(k/r): at least r*k' >= k scores are >= L, so every winner is >= L.
-// Each workgroup compacts its scores >= L, in index order, into its own
-// segment (wave ballots + one LDS prefix scan: no global atomics).
+// Kernel 2 (scan): L = the bottom of the highest bin at which the global
+// histogram, summed from the top, reaches k. A bin's count can only be short
+// (a chunk leaves out scores below its own cut), so at least k scores are >=
+// L and every winner is >= L. Each workgroup compacts its scores >= L, in
+// index order, into its own segment (wave ballots + one LDS prefix scan).
 //
 // Kernel 3 (select): radix select over the 64-bit keys (score_key << 32 |
 // ~j) of the candidates gathered into LDS in index order (or over all N
@@ -117,22 +118,14 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return off + incl - v;
 }
 
-// FP4 E2M1 code of v (fp32), ties to even, saturating at +-6. The query
-// values x * 2^-E it is used on are exact in fp32 (a BF16 value times a power
-// of two inside fp32's range), so this makes the same decisions as the fp64
-// encoder.
-__device__ __forceinline__ uint32_t fp4_e2m1_encode_f32(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+// FP4 E2M1 code of v (fp32) by comparisons: the magnitude code counts the round-to-nearest-even
+// decision points a passes (0.25 and 1.25, 2.5, 5 are ties that stay down; 0.75, 1.75, 3.5 ties that go up).
+__device__ __forceinline__ uint32_t fp4_e2m1_code_cmp(float v) {
   const float a = fabsf(v);
-  if (a >= 6.0f) return sign | 7u;
-  int e = (a < 1.0f) ? 0 : ilogbf(a);
-  float r = rintf(ldexpf(a, 1 - e));  // 2..4 for a >= 1, 0..2 below
-  uint32_t ri = (uint32_t)r;
-  if (ri >= 4) { ri >>= 1; e += 1; }
-  if (ri == 0) return sign;
-  if (ri < 2) return sign | 1u;
-  if (e > 2) return sign | 7u;
-  return sign | ((uint32_t)(e + 1) << 1) | (ri - 2);
+  uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  // saturating: every a > 5 is code 7 (6.0). The query values x * 2^-E are exact in fp32 (a BF16 value
+  // times a power of two), so this makes the fp64 encoder's decisions.
+  return ((__float_as_uint(v) >> 28) & 8u) | m;
 }
 
 __device__ __forceinline__ float from_partner(float x, int odd_row) {
@@ -148,36 +141,57 @@ __device__ __forceinline__ uint32_t from_partner_u(uint32_t x, int odd_row) {
 
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t thr_s;
-  __shared__ uint32_t qcode_s[8 * 8];  // quantised query: [head][8 words of 8 codes]
-  __shared__ int qscale_s[8 * 2];      // its E8M0 bytes: [head][half]
-  __shared__ int guard_s[6];           // block-scale bounds inside which the MFMA sum is exact
+  __shared__ uint32_t qcode_s[1][8 * 8];  // quantised query [head][8 words of 8 codes]
+  __shared__ int qscale_s[1][8 * 2];      // its E8M0 bytes [head][half]
+  __shared__ int guard_s[6];              // block-scale bounds inside which the MFMA sum is exact
   __shared__ uint32_t flag_blk[kScoreChunk];  // blocks to rescore exactly (offset in chunk)
-  __shared__ uint32_t flag_key[kScoreChunk];  // the key the MFMA path stored for them
   __shared__ uint32_t n_flag;
+  __shared__ uint32_t wmax_s[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
   const int N = (int)visible_blocks(a, tq);
   const int j_begin = blockIdx.x * kScoreChunk;
   if (j_begin >= N) return;
-  for (int i = tid; i < kHistBins; i += 256) hist[i] = 0;
-  if (tid == 0) {
-    thr_s = 0;
-    n_flag = 0;
-  }
   const float* wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
 
-  // ---- MX-FP4 query, once per workgroup (wave 0): lane -> head lane/8, eight dims 8*(lane%8)..
+  // ---- loads, smallest first (vector loads return in order): the query slice this lane quantises
+  // (lane -> head lane/8, dims 8*(lane%8)..+8), the head weights, then the keys.
+  const int qh = lane >> 3, qpart = lane & 7;
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+  if (qh < a.HI) qraw = *reinterpret_cast<const uint4*>(a.qI + (((size_t)b * a.Tq + tq) * a.HI + qh) * kIdxDim + qpart * 8);
+  float wlo[4], whi[4];  // head weights 0..3 and 4..7 (0 for heads >= H_I)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wlo[i] = i < a.HI ? wq[i] : 0.0f;
+    whi[i] = i + 4 < a.HI ? wq[i + 4] : 0.0f;
+  }
+  const size_t kbase = (size_t)b * a.max_blocks;
+  uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
+  const uint8_t* codes = a.idx_codes + kbase * 32;
+  const uint8_t* scl = a.idx_scale + kbase * 2;
+  const int wave_j0 = j_begin + wave * kScoreIters * 32;
+  const int n2 = 2 * (lane & 15) + ((lane >> 4) >> 1);  // block of this lane inside a 32-block tile
+  // All of this wave's key loads (kScoreIters tiles x 16 B + 1 scale byte per lane), unconditional with
+  // the address clamped to the last visible block (always in bounds), so they issue back to back.
+  uint4 bvs[kScoreIters];
+  int sbs[kScoreIters];
+#pragma unroll
+  for (int it = 0; it < kScoreIters; ++it) {
+    int jb = wave_j0 + it * 32 + n2;
+    jb = jb < N ? jb : N - 1;
+    bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + ((lane >> 4) & 1) * 16);
+    sbs[it] = scl[(size_t)jb * 2 + ((lane >> 4) & 1)];
+  }
+  for (int i = tid; i < kHistBins; i += 256) hist[i] = 0;
+  if (tid == 0) n_flag = 0;
+
+  // ---- MX-FP4 query and the exactness bounds, once per workgroup by wave 0
   if (wave == 0) {
-    const int h = lane >> 3, part = lane & 7;
     uint32_t word = 0, sbyte = 0;
-    if (h < a.HI) {
-      const uint16_t* src = a.qI + (((size_t)b * a.Tq + tq) * a.HI + h) * kIdxDim + part * 8;
-      const uint4 raw = *reinterpret_cast<const uint4*>(src);
+    if (qh < a.HI) {
       float x[8];
-      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+      const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         x[2 * u] = __uint_as_float(rw[u] << 16);
@@ -193,29 +207,31 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         E = E < -127 ? -127 : (E > 127 ? 127 : E);
         sbyte = (uint32_t)(E + 127);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) word |= fp4_e2m1_encode_f32(ldexpf(x[i], -E)) << (4 * i);
+        for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
       }
     }
-    if (h < 8) {
-      qcode_s[h * 8 + part] = word;
-      if ((part & 3) == 0) qscale_s[h * 2 + (part >> 2)] = (int)sbyte;
+    qcode_s[0][qh * 8 + qpart] = word;
+    if ((qpart & 3) == 0) qscale_s[0][qh * 2 + (qpart >> 2)] = (int)sbyte;
+    // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
+    // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
+    const int q0 = __shfl((int)sbyte, (lane & 7) * 8, 64), q1 = __shfl((int)sbyte, (lane & 7) * 8 + 4, 64);
+    const bool live = (lane & 7) < a.HI;
+    int g0 = live ? -10 - (q0 - q1) : -100000, g1 = live ? 10 - (q0 - q1) : 100000;
+    int g2 = live ? 130 - q0 : -100000, g3 = live ? 370 - q0 : 100000;
+    int g4 = live ? 130 - q1 : -100000, g5 = live ? 370 - q1 : 100000;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      g0 = max(g0, __shfl_xor(g0, o, 64)); g1 = min(g1, __shfl_xor(g1, o, 64));
+      g2 = max(g2, __shfl_xor(g2, o, 64)); g3 = min(g3, __shfl_xor(g3, o, 64));
+      g4 = max(g4, __shfl_xor(g4, o, 64)); g5 = min(g5, __shfl_xor(g5, o, 64));
+    }
+    if (lane == 0) {
+      guard_s[0] = g0; guard_s[1] = g1; guard_s[2] = g2; guard_s[3] = g3; guard_s[4] = g4; guard_s[5] = g5;
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    // exactness bounds over the live heads: |S0 - S1| <= 10 and 130 <= S_b <= 370, S_b = qs_b + ks_b
-    int dlo = -100000, dhi = 100000, k0lo = -100000, k0hi = 100000, k1lo = -100000, k1hi = 100000;
-    for (int h = 0; h < a.HI; ++h) {
-      const int q0 = qscale_s[2 * h], q1 = qscale_s[2 * h + 1], dq = q0 - q1;
-      dlo = max(dlo, -10 - dq);
-      dhi = min(dhi, 10 - dq);
-      k0lo = max(k0lo, 130 - q0);
-      k0hi = min(k0hi, 370 - q0);
-      k1lo = max(k1lo, 130 - q1);
-      k1hi = min(k1hi, 370 - q1);
-    }
-    guard_s[0] = dlo; guard_s[1] = dhi; guard_s[2] = k0lo; guard_s[3] = k0hi; guard_s[4] = k1lo; guard_s[5] = k1hi;
-  }
+  __syncthreads();  // quantised query, bounds, zeroed histogram and n_flag visible
+  const int dlo = guard_s[0], dhi = guard_s[1], k0lo = guard_s[2], k0hi = guard_s[3], k1lo = guard_s[4],
+            k1hi = guard_s[5];
   // ---- two A operands. Lane: row r = lane%16, K-group g = lane/16; row r holds (p, h) = (r/8, r%8)
   // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only.
   const int r = lane & 15, g = lane >> 4, p = r >> 3, odd = g & 1;
@@ -225,41 +241,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   if ((g >> 1) == p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      aA[u] = qcode_s[hA * 8 + odd * 4 + u];
-      aB[u] = qcode_s[hB * 8 + odd * 4 + u];
+      aA[u] = qcode_s[0][hA * 8 + odd * 4 + u];
+      aB[u] = qcode_s[0][hB * 8 + odd * 4 + u];
     }
-    sA = qscale_s[hA * 2 + odd];
-    sB = qscale_s[hB * 2 + odd];
+    sA = qscale_s[0][hA * 2 + odd];
+    sB = qscale_s[0][hB * 2 + odd];
   }
   const v8i A0 = {(int)aA[0], (int)aA[1], (int)aA[2], (int)aA[3], 0, 0, 0, 0};
   const v8i A1 = {(int)aB[0], (int)aB[1], (int)aB[2], (int)aB[3], 0, 0, 0, 0};
-  float wlo[4], whi[4];  // head weights 0..3 and 4..7 (0 for heads >= H_I)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wlo[i] = i < a.HI ? wq[i] : 0.0f;
-    whi[i] = i + 4 < a.HI ? wq[i + 4] : 0.0f;
-  }
-  __syncthreads();
-  const int dlo = guard_s[0], dhi = guard_s[1], k0lo = guard_s[2], k0hi = guard_s[3], k1lo = guard_s[4],
-            k1hi = guard_s[5];
 
-  const size_t kbase = (size_t)b * a.max_blocks;
-  uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
-  const uint8_t* codes = a.idx_codes + kbase * 32;
-  const uint8_t* scl = a.idx_scale + kbase * 2;
-  // all of this wave's key loads first (16 tiles x 16 B + 1 scale byte per lane in flight), then the MFMAs.
-  // Unconditional loads (address clamped to the last visible block, always in bounds) issue back to back.
-  const int wave_j0 = j_begin + wave * kScoreIters * 32;
-  const int n2 = 2 * (lane & 15) + (g >> 1);  // block of this lane inside a 32-block tile
-  uint4 bvs[kScoreIters];
-  int sbs[kScoreIters];
-#pragma unroll
-  for (int it = 0; it < kScoreIters; ++it) {
-    int jb = wave_j0 + it * 32 + n2;
-    jb = jb < N ? jb : N - 1;
-    bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + odd * 16);
-    sbs[it] = scl[(size_t)jb * 2 + odd];
-  }
+  uint32_t lane_keys[kScoreIters / 2];  // this lane's final key per tile pair (0 = no block)
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) {
     const int tA = 2 * pr, tB = 2 * pr + 1;
@@ -288,59 +279,61 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int ks0 = odd ? oth : own, ks1 = odd ? own : oth;
     const int dk = ks0 - ks1;
     const bool bad = dk < dlo || dk > dhi || ks0 < k0lo || ks0 > k0hi || ks1 < k1lo || ks1 > k1hi;
+    uint32_t key = 0;
     if (jb < N) {
       if (s == 0.0f) s = 0.0f;
-      const uint32_t key = order_key(s);
+      key = order_key(s);
       keys[jb] = key;
-      atomicAdd(&hist[key >> 20], 1u);
-      if (bad) {
-        const uint32_t f = atomicAdd(&n_flag, 1u);
-        flag_blk[f] = (uint32_t)(jb - j_begin);
-        flag_key[f] = key;
-      }
+      if (bad) flag_blk[atomicAdd(&n_flag, 1u)] = (uint32_t)(jb - j_begin);
     }
+    lane_keys[pr] = key;
   }
   __syncthreads();
-  // exact rescoring of the flagged blocks (none with real data), fixing the histogram and the stored key
-  for (uint32_t f = tid; f < n_flag; f += 256) {
+  // exact rescoring of the flagged blocks (none with real data); the reload below picks the new keys up
+  const uint32_t nf = n_flag;
+  for (uint32_t f = tid; f < nf; f += 256) {
     const int jb = j_begin + (int)flag_blk[f];
     const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
-                                       qcode_s, qscale_s, wq, a.HI);
-    const uint32_t key = order_key(ex);
-    if (key != flag_key[f]) {
-      atomicSub(&hist[flag_key[f] >> 20], 1u);
-      atomicAdd(&hist[key >> 20], 1u);
-      keys[jb] = key;
+                                       qcode_s[0], qscale_s[0], wq, a.HI);
+    keys[jb] = order_key(ex);
+  }
+  if (nf != 0) {
+    __syncthreads();
+    __threadfence_block();
+#pragma unroll
+    for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+      const int jb = wave_j0 + ((odd ? 2 * pr : 2 * pr + 1)) * 32 + n2;
+      if (jb < N) lane_keys[pr] = keys[jb];
     }
   }
+  // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
+  // and the 16 bins below it (down to a quarter of the max). Counts in a bin only ever undercount, so
+  // the bin where the global count from the top reaches k is a lower bound of the k-th largest key.
+  uint32_t m = 0;
+#pragma unroll
+  for (int pr = 0; pr < kScoreIters / 2; ++pr) m = max(m, lane_keys[pr]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if (lane == 0) wmax_s[wave] = m;
   __syncthreads();
-
-  // ---- chunk lower bound: lowest key of the histogram bin holding the k'-th largest score
-  const int G_q = (N + kScoreChunk - 1) / kScoreChunk;
-  const int rr = (G_q + 1) / 2;
-  const uint32_t kp = (uint32_t)((a.k + rr - 1) / rr);
-  const int top = kHistBins - 16 * tid;  // this thread's bins: [top-16, top), scanned downwards
-  uint32_t cnt = 0;
-  for (int i = 1; i <= 16; ++i) cnt += hist[top - i];
-  uint32_t total;
-  uint32_t excl = block_excl_scan(cnt, wsum, &total);
-  if (total >= kp && excl < kp && excl + cnt >= kp) {
-    uint32_t c = excl;
-    for (int i = 1; i <= 16; ++i) {
-      c += hist[top - i];
-      if (c >= kp) {
-        thr_s = (uint32_t)(top - i) << 20;
-        break;
-      }
-    }
+  const uint32_t kmax = max(max(wmax_s[0], wmax_s[1]), max(wmax_s[2], wmax_s[3]));
+  const int top_bin = (int)(kmax >> 20);
+  const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
+#pragma unroll
+  for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+    const uint32_t key = lane_keys[pr];
+    if (key != 0 && (int)(key >> 20) >= low_bin) atomicAdd(&hist[key >> 20], 1u);
   }
   __syncthreads();
-  if (tid == 0) a.thr[(size_t)q * a.G + blockIdx.x] = thr_s;
+  if (tid <= top_bin - low_bin) {
+    const uint32_t c = hist[low_bin + tid];
+    if (c) atomicAdd(&a.ghist[(size_t)q * kHistBins + low_bin + tid], c);
+  }
 }
 
 __global__ __launch_bounds__(256) void scan_kernel(ScoreArgs a) {
   constexpr int kPer = kScanPerWG / 256;  // keys per thread: j = start + u*256 + tid
-  __shared__ uint32_t sthr[2048];
+  __shared__ uint32_t wsum[4];
   __shared__ uint32_t L_s;
   __shared__ uint32_t cnt_s[kPer * 4];    // candidates per (u, wave), then their exclusive offsets
   __shared__ uint32_t total_s;
@@ -351,30 +344,43 @@ __global__ __launch_bounds__(256) void scan_kernel(ScoreArgs a) {
   if (N <= a.k) return;  // the select kernel takes every visible block
   const int64_t start = (int64_t)blockIdx.x * kScanPerWG;
   if (start >= N) return;
-  const int G_q = (int)((N + kScoreChunk - 1) / kScoreChunk);
-  const int rr = (G_q + 1) / 2;
-  if (tid == 0) L_s = 0;
-  for (int i = tid; i < G_q; i += 256) sthr[i] = a.thr[(size_t)q * a.G + i];
-  __syncthreads();
-  for (int i = tid; i < G_q; i += 256) {
-    uint32_t v = sthr[i];
-    int rank = 0;
-    for (int j = 0; j < G_q; ++j) {
-      uint32_t u = sthr[j];
-      rank += (u > v) || (u == v && j < i);
-    }
-    if (rank == rr - 1) L_s = v;
-  }
-  __syncthreads();
-  const uint32_t L = L_s;
+  // this workgroup's keys first (they do not depend on the threshold), then the chunk bounds
   const int64_t end = (start + kScanPerWG < N) ? start + kScanPerWG : N;
   const uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
   uint32_t kv[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int64_t j = start + (int64_t)u * 256 + tid;
-    kv[u] = j < end ? keys[j] : 0u;
+    kv[u] = keys[j < end ? j : end - 1];
   }
+  // L = the lowest key of the highest bin at which the query's global histogram, counted from the top,
+  // reaches k (every winner is >= L; no such bin: L = 0, every block a candidate)
+  if (tid == 0) L_s = 0;
+  {
+    const int top = kHistBins - 16 * tid;
+    uint32_t hv[16];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 1; i <= 16; ++i) {
+      hv[i - 1] = a.ghist[(size_t)q * kHistBins + top - i];
+      cnt += hv[i - 1];
+    }
+    uint32_t tot;
+    const uint32_t excl = block_excl_scan(cnt, wsum, &tot);
+    const uint32_t kk = (uint32_t)a.k;
+    if (excl < kk && excl + cnt >= kk) {
+      uint32_t c = excl;
+      for (int i = 1; i <= 16; ++i) {
+        c += hv[i - 1];
+        if (c >= kk) {
+          L_s = (uint32_t)(top - i) << 20;
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t L = L_s;
   // candidates (key >= L) keep index order: (u, wave, lane) order is ascending j
   uint64_t masks[kPer];
 #pragma unroll
@@ -414,39 +420,81 @@ __global__ __launch_bounds__(256) void scan_kernel(ScoreArgs a) {
 
 __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   __shared__ uint64_t cs[kCandCap];
-  __shared__ uint32_t seg_off[2049];
+  __shared__ uint32_t seg_off[2049];  // G2_q <= 512 segments
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wsum[8];
   __shared__ uint32_t sel_digit, sel_above, sel_count;
+  __shared__ uint64_t red_lo[8], red_hi[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.x;
   const int tq = q % a.Tq;
   const int64_t N = visible_blocks(a, tq);
   int32_t* out = a.topk + (size_t)q * a.k;
+  // the scan kernel is done with this query's global histogram: clear it for the next call
+  for (int i = tid; i < kHistBins; i += 512) a.ghist[(size_t)q * kHistBins + i] = 0u;
   if (N <= a.k) {
     for (int i = tid; i < a.k; i += 512) out[i] = (i < N) ? i : -1;
     return;
   }
-  // segment offsets of the scan's ordered candidate lists
+  // One round of loads: every segment's count and, speculatively, its first kSpec slots (always in
+  // bounds: a segment has room for kScanPerWG candidates); only a fuller segment needs a second round.
   const int G2_q = (int)((N + kScanPerWG - 1) / kScanPerWG);
-  if (tid == 0) {
-    uint32_t acc = 0;
-    for (int g = 0; g < G2_q; ++g) {
-      seg_off[g] = acc;
-      acc += a.seg_cnt[(size_t)q * a.G2 + g];
-    }
-    seg_off[G2_q] = acc;
+  constexpr int kSpec = 256;
+  const uint64_t* cand = a.cand + (size_t)q * a.max_blocks;
+  const int lanes_per_seg = G2_q <= 32 ? 16 : (G2_q <= 64 ? 8 : 0);  // speculation only for few segments
+  uint64_t spec[16];
+  const int my_seg = lanes_per_seg ? tid / lanes_per_seg : 0;
+  const int my_sub = lanes_per_seg ? tid % lanes_per_seg : 0;
+  const int per_lane = lanes_per_seg ? kSpec / lanes_per_seg : 0;
+  if (lanes_per_seg && my_seg < G2_q) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r < per_lane) spec[r] = cand[(size_t)my_seg * kScanPerWG + my_sub + r * lanes_per_seg];
   }
-  __syncthreads();
+  for (int g0 = 0; g0 < G2_q; g0 += 512) {
+    const int gi = g0 + tid;
+    const uint32_t c = gi < G2_q ? a.seg_cnt[(size_t)q * a.G2 + gi] : 0u;
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t base = g0 == 0 ? 0u : seg_off[g0];
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    if (gi < G2_q) seg_off[gi] = base + incl - c;
+    if (tid == 511) seg_off[g0 + 512 < G2_q ? g0 + 512 : G2_q] = base + incl;
+    __syncthreads();
+  }
   const uint32_t total = seg_off[G2_q];
   const bool fast = total <= (uint32_t)kCandCap;
   const int64_t n = fast ? (int64_t)total : N;
   const uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
   if (fast) {
-    const uint64_t* cand = a.cand + (size_t)q * a.max_blocks;
-    for (int g = 0; g < G2_q; ++g) {
-      const uint32_t c = seg_off[g + 1] - seg_off[g];
-      for (uint32_t i = tid; i < c; i += 512) cs[seg_off[g] + i] = cand[(size_t)g * kScanPerWG + i];
+    uint32_t covered = 0;  // slots per segment already placed from the speculative loads
+    if (lanes_per_seg) {
+      covered = kSpec;
+      if (my_seg < G2_q) {
+        const uint32_t c = seg_off[my_seg + 1] - seg_off[my_seg];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = my_sub + r * lanes_per_seg;
+          if (r < per_lane && i < c) cs[seg_off[my_seg] + i] = spec[r];
+        }
+      }
+    }
+    // the rest (segments beyond the speculated slots): flat gather, segment found by binary search
+    for (uint32_t i = tid; i < total; i += 512) {
+      int lo = 0, hi = G2_q - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg_off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      const uint32_t off = i - seg_off[lo];
+      if (off >= covered) cs[i] = cand[(size_t)lo * kScanPerWG + off];
     }
   }
   __syncthreads();
@@ -456,16 +504,46 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
     return ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
   };
 
-  // radix select of the k-th largest 64-bit key (score key, then lower index first),
-  // 8 bits at a time, stopping as soon as the bin that holds it is taken whole
-  uint64_t prefix = 0, mask = 0;
+  // radix select of the k-th largest 64-bit key (score key, then lower index first), 8 bits at a time
+  // from the highest bit in which the elements differ, stopping as soon as the bin that holds it is
+  // taken whole
+  {
+    uint64_t lo = ~0ull, hi = 0;
+    for (int64_t i = tid; i < n; i += 512) {
+      const uint64_t e = elem(i);
+      lo = e < lo ? e : lo;
+      hi = e > hi ? e : hi;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    if (lane == 0) {
+      red_lo[wave] = lo;
+      red_hi[wave] = hi;
+    }
+  }
+  __syncthreads();
+  uint64_t glo = red_lo[0], ghi = red_hi[0];
+  for (int w = 1; w < 8; ++w) {
+    glo = red_lo[w] < glo ? red_lo[w] : glo;
+    ghi = red_hi[w] > ghi ? red_hi[w] : ghi;
+  }
+  const uint64_t diff = glo ^ ghi;                 // nonzero: keys are unique and n > k >= 1
+  const int hb = 63 - __clzll((long long)diff);    // highest differing bit
+  const uint64_t common = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+  uint64_t prefix = glo & common, mask = common;
   uint32_t need = (uint32_t)a.k;  // N > k here
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int shift = hb - 7; shift > -8; shift -= 8) {
+    const int sh = shift < 0 ? 0 : shift;           // the last digit may be narrower than 8 bits
+    const uint64_t dmask = shift < 0 ? ((1ull << (shift + 8)) - 1ull) : 255ull;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int64_t i = tid; i < n; i += 512) {
       uint64_t e = elem(i);
-      if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)(e >> shift) & 255u], 1u);
+      if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -495,8 +573,8 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
     __syncthreads();
     const uint32_t d = sel_digit;
     need -= sel_above;
-    prefix |= (uint64_t)d << shift;
-    mask |= (uint64_t)0xFF << shift;
+    prefix |= (uint64_t)d << sh;
+    mask |= dmask << sh;
     if (sel_count == need) break;
   }
   // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run

@@ -23,6 +23,7 @@ constexpr int kCandCap = 8192;                        // candidates the select k
 constexpr int kAttnKeys = 64;                         // keys staged per iteration
 constexpr int kAttnTargetWGs = 512;                   // split-K target for small query counts
 constexpr int kPartStride = kHeadDim + 2;             // O[128], m, l per (query, split, head)
+constexpr int kMaxSplits = 32;                        // split-K limit (the merge holds one value per split)
 
 struct IngestArgs {
   const uint16_t* kv;      // [B][T][128]
@@ -58,7 +59,7 @@ struct ScoreArgs {
   const uint8_t* idx_codes;
   const uint8_t* idx_scale;
   uint32_t* keys;          // ws [B*Tq][max_blocks]
-  uint32_t* thr;           // ws [B*Tq][G]
+  uint32_t* ghist;         // ws [B*Tq][kHistBins]: per-query global histogram, zero between calls
   uint64_t* cand;          // ws [B*Tq][max_blocks]: ordered candidates, one segment per scan workgroup
   uint32_t* seg_cnt;       // ws [B*Tq][G2]: candidates per segment
   int32_t* topk;           // [B][Tq][k]
@@ -68,7 +69,6 @@ struct ScoreArgs {
   int32_t HI;
   int32_t k;
   int32_t m;
-  int32_t G;               // score chunks per query (stride of thr)
   int32_t G2;              // scan segments per query (stride of seg_cnt)
 };
 
