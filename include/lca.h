@@ -120,8 +120,8 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
 
 /* Scratch one call of lca_csa_indexer_topk / lca_csa_sparse_attn /
  * lca_hca_dense_attn needs for up to max_tq queries per sequence at up to
- * max_ctx tokens. For CSA it begins with one 16 KiB histogram per query that
- * must be zero when an indexer call starts: zero the workspace once with
+ * max_ctx tokens. For CSA it holds, per query, a 16 KiB histogram that must
+ * be zero when an indexer call starts: zero the workspace once with
  * lca_workspace_init() before its first use; every completed
  * lca_csa_indexer_topk (or lca_csa_topk_select) leaves it zero again.
  * Everything else in it is rewritten by each call. A workspace may be shared
@@ -131,13 +131,13 @@ size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t ma
 lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
 
 /* Where the indexer leaves its scores (CSA): after lca_csa_index_score (or
- * lca_csa_indexer_topk) with this Tq on a cache of this shape, the workspace
- * holds at this byte offset, for query q = b*Tq + i, a row of max_ctx/m
- * uint32 keys, valid for the visible blocks j < (t+1)/m. key =
- * bits(score) ^ (score < 0 ? 0xFFFFFFFF : 0x80000000), so keys order like the
- * scores. Written only when some query sees more than topk blocks. Returns 0
- * for HCA or invalid arguments. */
-size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t Tq, int64_t max_ctx);
+ * lca_csa_indexer_topk) on a cache of this shape, the workspace holds at this
+ * byte offset the row of max_ctx/m uint32 keys of query `query` (= b*Tq + i),
+ * valid for its visible blocks j < (t+1)/m: key = bits(score) ^ (score < 0 ?
+ * 0xFFFFFFFF : 0x80000000), so keys order like the scores. Written only when
+ * some query of the call sees more than topk blocks. Returns 0 for HCA or
+ * invalid arguments. */
+size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t query, int64_t max_ctx);
 
 /* CSA compressor (CSA paragraph and Figure 3: every m = 4 tokens pooled into
  * one entry by softmax-gated pooling with a learned positional bias).

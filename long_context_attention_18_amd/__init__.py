@@ -133,8 +133,8 @@ def lca_workspace_init(ws, nbytes, stream=None):
     _check("lca_workspace_init", lib().lca_workspace_init(_ptr(ws), nbytes, _stream(stream)))
 
 
-def lca_workspace_scores_offset(desc, batch, Tq, max_ctx):
-    return lib().lca_workspace_scores_offset(ctypes.byref(desc), batch, Tq, max_ctx)
+def lca_workspace_scores_offset(desc, batch, query, max_ctx):
+    return lib().lca_workspace_scores_offset(ctypes.byref(desc), batch, query, max_ctx)
 
 
 def lca_csa_compress(cache, kv, gate, ik, ig, bias, idx_bias, T, stream=None):
@@ -241,13 +241,15 @@ class DeviceLayer:
 
     def index_scores(self, Tq):
         """fp32 scores the last index_score / indexer_topk call left in the workspace: [B][Tq][max_blocks]."""
-        import torch
-        off = lca_workspace_scores_offset(self.desc, self.batch, Tq, self.max_ctx)
-        nb = self.cache.max_blocks
-        base = self.ws - self.ws_mem.data_ptr() + off
-        keys = self.ws_mem[base:base + self.batch * Tq * nb * 4].view(torch.int32).view(self.batch, Tq, nb)
-        k = keys.cpu().numpy().view("uint32")
         import numpy as np
+        nb = self.cache.max_blocks
+        rows = []
+        for qi in range(self.batch * Tq):
+            off = lca_workspace_scores_offset(self.desc, self.batch, qi, self.max_ctx)
+            base = self.ws - self.ws_mem.data_ptr() + off
+            rows.append(self.ws_mem[base:base + nb * 4])
+        import torch
+        k = torch.stack(rows).cpu().numpy().view(np.uint32).reshape(self.batch, Tq, nb)
         bits = np.where(k & 0x80000000, k ^ 0x80000000, ~k).astype(np.uint32)
         return bits.view(np.float32)
 

@@ -64,9 +64,11 @@ bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
   return true;
 }
 
-// Workspace: indexer (keys, thresholds, candidates, counters) then attention partials.
+// Workspace: the attention split-K partials first (fixed size), then, for CSA, one block per query
+// (histogram, scan segment counts, score keys, candidates). Nothing's place depends on a call's Tq,
+// so the per-query histograms that must be zero between calls stay put.
 struct WsLayout {
-  size_t keys, ghist, cand, cnt, part, total;
+  size_t part, qbase, qstride, off_seg, off_keys, off_cand, total;
   int32_t G2;
 };
 
@@ -74,19 +76,20 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   WsLayout W{};
   const int64_t max_blocks = max_ctx / d->m;
   const size_t nq = (size_t)B * (size_t)max_tq;
-  size_t off = 0;
-  W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
-  if (d->kind == LCA_KIND_CSA) {
-    // the per-query histograms first: they must be zero when a call starts (lca_workspace_init, then
-    // every select leaves them zero), and a smaller-Tq call keeps them at the same place
-    W.ghist = off; off = align_up(off + (size_t)B * max_tq * kHistBins * 4);
-    W.cnt = off; off = align_up(off + nq * (size_t)W.G2 * 4);
-    W.keys = off; off = align_up(off + nq * (size_t)max_blocks * 4);
-    W.cand = off; off = align_up(off + nq * (size_t)max_blocks * 8);
-  }
   // split-K partials: splits are used only while B*Tq < kAttnTargetWGs, and then
   // B*Tq*splits < 2*kAttnTargetWGs (see attn_splits)
-  W.part = off; off = align_up(off + (size_t)2 * kAttnTargetWGs * d->n_heads * kPartStride * 4);
+  W.part = 0;
+  size_t off = align_up((size_t)2 * kAttnTargetWGs * d->n_heads * kPartStride * 4);
+  W.qbase = off;
+  W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
+  if (d->kind == LCA_KIND_CSA) {
+    size_t q = align_up((size_t)kHistBins * 4);
+    W.off_seg = q; q = align_up(q + (size_t)W.G2 * 4);
+    W.off_keys = q; q = align_up(q + (size_t)max_blocks * 4);
+    W.off_cand = q; q = align_up(q + (size_t)max_blocks * 8);
+    W.qstride = q;
+    off += nq * q;
+  }
   W.total = off;
   return W;
 }
@@ -216,9 +219,10 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
   return launch_status(launch_fill_zero(base_dev, L.total, (hipStream_t)stream));
 }
 
-size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t Tq, int64_t max_ctx) {
-  if (!desc_ok(desc) || desc->kind != LCA_KIND_CSA || batch < 1 || Tq < 1 || max_ctx < desc->m) return 0;
-  return ws_layout(desc, batch, Tq, max_ctx).keys;
+size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t query, int64_t max_ctx) {
+  if (!desc_ok(desc) || desc->kind != LCA_KIND_CSA || batch < 1 || query < 0 || max_ctx < desc->m) return 0;
+  WsLayout W = ws_layout(desc, batch, 1, max_ctx);
+  return W.qbase + (size_t)query * W.qstride + W.off_keys;
 }
 
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx) {
@@ -287,10 +291,11 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.w = w_dev;
   a.idx_codes = cache->idx_codes_dev;
   a.idx_scale = cache->idx_scale_dev;
-  a.keys = (uint32_t*)(ws + W.keys);
-  a.ghist = (uint32_t*)(ws + W.ghist);
-  a.cand = (uint64_t*)(ws + W.cand);
-  a.seg_cnt = (uint32_t*)(ws + W.cnt);
+  a.qbase = (uint8_t*)(ws + W.qbase);
+  a.qstride = W.qstride;
+  a.off_seg = W.off_seg;
+  a.off_keys = W.off_keys;
+  a.off_cand = W.off_cand;
   a.topk = topk_dev;
   a.len = cache->len;
   a.max_blocks = cache->max_blocks;

@@ -42,9 +42,10 @@
 // L and every winner is >= L. Each workgroup compacts its scores >= L, in
 // index order, into its own segment (wave ballots + one LDS prefix scan).
 //
-// Kernel 3 (select): radix select over the 64-bit keys (score_key << 32 |
-// ~j) of the candidates gathered into LDS in index order (or over all N
-// scores when there are too many), then an order-preserving compaction of
+// The last scan workgroup of each query (device-scope fence + counter)
+// then runs the selection: radix select over the 64-bit keys (score_key <<
+// 32 | ~j) of the candidates gathered into LDS in index order (or over all
+// N scores when there are too many), then an order-preserving compaction of
 // the winners, so the output is ascending without a sort. Exact for any
 // input.
 #include "dev_formats.h"
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     whi[i] = i + 4 < a.HI ? wq[i + 4] : 0.0f;
   }
   const size_t kbase = (size_t)b * a.max_blocks;
-  uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
+  uint32_t* keys = q_keys(a, q);
   const uint8_t* codes = a.idx_codes + kbase * 32;
   const uint8_t* scl = a.idx_scale + kbase * 2;
   const int wave_j0 = j_begin + wave * kScoreIters * 32;
@@ -327,120 +328,39 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __syncthreads();
   if (tid <= top_bin - low_bin) {
     const uint32_t c = hist[low_bin + tid];
-    if (c) atomicAdd(&a.ghist[(size_t)q * kHistBins + low_bin + tid], c);
+    if (c) atomicAdd(&q_hist(a, q)[low_bin + tid], c);
   }
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(ScoreArgs a) {
-  constexpr int kPer = kScanPerWG / 256;  // keys per thread: j = start + u*256 + tid
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t L_s;
-  __shared__ uint32_t cnt_s[kPer * 4];    // candidates per (u, wave), then their exclusive offsets
-  __shared__ uint32_t total_s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = blockIdx.y;
-  const int tq = q % a.Tq;
-  const int64_t N = visible_blocks(a, tq);
-  if (N <= a.k) return;  // the select kernel takes every visible block
-  const int64_t start = (int64_t)blockIdx.x * kScanPerWG;
-  if (start >= N) return;
-  // this workgroup's keys first (they do not depend on the threshold), then the chunk bounds
-  const int64_t end = (start + kScanPerWG < N) ? start + kScanPerWG : N;
-  const uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
-  uint32_t kv[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int64_t j = start + (int64_t)u * 256 + tid;
-    kv[u] = keys[j < end ? j : end - 1];
-  }
-  // L = the lowest key of the highest bin at which the query's global histogram, counted from the top,
-  // reaches k (every winner is >= L; no such bin: L = 0, every block a candidate)
-  if (tid == 0) L_s = 0;
-  {
-    const int top = kHistBins - 16 * tid;
-    uint32_t hv[16];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 1; i <= 16; ++i) {
-      hv[i - 1] = a.ghist[(size_t)q * kHistBins + top - i];
-      cnt += hv[i - 1];
-    }
-    uint32_t tot;
-    const uint32_t excl = block_excl_scan(cnt, wsum, &tot);
-    const uint32_t kk = (uint32_t)a.k;
-    if (excl < kk && excl + cnt >= kk) {
-      uint32_t c = excl;
-      for (int i = 1; i <= 16; ++i) {
-        c += hv[i - 1];
-        if (c >= kk) {
-          L_s = (uint32_t)(top - i) << 20;
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t L = L_s;
-  // candidates (key >= L) keep index order: (u, wave, lane) order is ascending j
-  uint64_t masks[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int64_t j = start + (int64_t)u * 256 + tid;
-    masks[u] = __ballot(j < end && kv[u] >= L);
-    if (lane == 0) cnt_s[u * 4 + wave] = (uint32_t)__popcll(masks[u]);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // exclusive scan of the kPer*4 counts in (u, wave) order; two per lane
-    uint32_t c0 = cnt_s[2 * lane], c1 = cnt_s[2 * lane + 1];
-    uint32_t incl = c0 + c1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    uint32_t excl = incl - c0 - c1;
-    cnt_s[2 * lane] = excl;
-    cnt_s[2 * lane + 1] = excl + c0;
-    if (lane == 63) total_s = incl;
-  }
-  __syncthreads();
-  uint64_t* seg = a.cand + (size_t)q * a.max_blocks + start;  // this workgroup's segment
-  const uint64_t lt = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if ((masks[u] >> lane) & 1ull) {
-      const uint32_t pos = cnt_s[u * 4 + wave] + (uint32_t)__popcll(masks[u] & lt);
-      const uint32_t j = (uint32_t)(start + (int64_t)u * 256 + tid);
-      seg[pos] = ((uint64_t)kv[u] << 32) | (uint64_t)(0xFFFFFFFFu - j);
-    }
-  }
-  if (tid == 0) a.seg_cnt[(size_t)q * a.G2 + blockIdx.x] = total_s;
-}
+// ---- the selection (last scan workgroup of a query): radix select of the k-th largest 64-bit key
+// over the ordered candidates, then the winners in index order. 512 threads.
+struct SelectLds {
+  uint64_t cs[kCandCap];
+  uint32_t seg_off[2049];  // G2_q <= 512 segments
+  uint32_t hist[256];
+  uint32_t wsum[8];
+  uint32_t sel_digit, sel_above, sel_count;
+  uint64_t red_lo[8], red_hi[8];
+};
 
-__global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
-  __shared__ uint64_t cs[kCandCap];
-  __shared__ uint32_t seg_off[2049];  // G2_q <= 512 segments
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[8];
-  __shared__ uint32_t sel_digit, sel_above, sel_count;
-  __shared__ uint64_t red_lo[8], red_hi[8];
+__device__ void select_query(const ScoreArgs& a, int q, int64_t N, SelectLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = blockIdx.x;
-  const int tq = q % a.Tq;
-  const int64_t N = visible_blocks(a, tq);
   int32_t* out = a.topk + (size_t)q * a.k;
-  // the scan kernel is done with this query's global histogram: clear it for the next call
-  for (int i = tid; i < kHistBins; i += 512) a.ghist[(size_t)q * kHistBins + i] = 0u;
-  if (N <= a.k) {
-    for (int i = tid; i < a.k; i += 512) out[i] = (i < N) ? i : -1;
-    return;
-  }
+  uint64_t* cs = S.cs;
+  uint32_t* seg_off = S.seg_off;
+  uint32_t* hist = S.hist;
+  uint32_t* wsum = S.wsum;
+  uint32_t& sel_digit = S.sel_digit;
+  uint32_t& sel_above = S.sel_above;
+  uint32_t& sel_count = S.sel_count;
+  uint64_t* red_lo = S.red_lo;
+  uint64_t* red_hi = S.red_hi;
+
   // One round of loads: every segment's count and, speculatively, its first kSpec slots (always in
   // bounds: a segment has room for kScanPerWG candidates); only a fuller segment needs a second round.
   const int G2_q = (int)((N + kScanPerWG - 1) / kScanPerWG);
   constexpr int kSpec = 256;
-  const uint64_t* cand = a.cand + (size_t)q * a.max_blocks;
+  const uint64_t* cand = q_cand(a, q);
   const int lanes_per_seg = G2_q <= 32 ? 16 : (G2_q <= 64 ? 8 : 0);  // speculation only for few segments
   uint64_t spec[16];
   const int my_seg = lanes_per_seg ? tid / lanes_per_seg : 0;
@@ -453,7 +373,7 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   }
   for (int g0 = 0; g0 < G2_q; g0 += 512) {
     const int gi = g0 + tid;
-    const uint32_t c = gi < G2_q ? a.seg_cnt[(size_t)q * a.G2 + gi] : 0u;
+    const uint32_t c = gi < G2_q ? q_seg(a, q)[gi] : 0u;
     uint32_t incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -471,7 +391,7 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   const uint32_t total = seg_off[G2_q];
   const bool fast = total <= (uint32_t)kCandCap;
   const int64_t n = fast ? (int64_t)total : N;
-  const uint32_t* keys = a.keys + (size_t)q * a.max_blocks;
+  const uint32_t* keys = q_keys(a, q);
   if (fast) {
     uint32_t covered = 0;  // slots per segment already placed from the speculative loads
     if (lanes_per_seg) {
@@ -602,6 +522,115 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   }
 }
 
+// Candidate scan: every key >= L (the bound the query's global histogram gives) is written, in index
+// order, to this workgroup's segment of the candidate row; the segment's count goes to seg. A query with
+// at most k visible blocks gets its whole list (and its histogram cleared) here.
+__global__ __launch_bounds__(512) void scan_kernel(ScoreArgs a) {
+  constexpr int kPer = kScanPerWG / 512;  // keys per thread: j = start + u*512 + tid
+  __shared__ uint32_t wsum[8];
+  __shared__ uint32_t L_s;
+  __shared__ uint32_t cnt_s[kPer * 8];    // candidates per (u, wave), then their exclusive offsets
+  __shared__ uint32_t total_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = blockIdx.y;
+  const int tq = q % a.Tq;
+  const int64_t N = visible_blocks(a, tq);
+  if (N <= a.k) {
+    // every visible block is selected; one workgroup writes the list and clears the histogram
+    if (blockIdx.x == 0) {
+      int32_t* out = a.topk + (size_t)q * a.k;
+      for (int i = tid; i < a.k; i += 512) out[i] = (i < N) ? i : -1;
+      for (int i = tid; i < kHistBins; i += 512) q_hist(a, q)[i] = 0u;
+    }
+    return;
+  }
+  const int64_t start = (int64_t)blockIdx.x * kScanPerWG;
+  if (start >= N) return;
+  // this workgroup's keys first (they do not depend on the threshold), then the chunk bounds
+  const int64_t end = (start + kScanPerWG < N) ? start + kScanPerWG : N;
+  const uint32_t* keys = q_keys(a, q);
+  uint32_t kv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t j = start + (int64_t)u * 512 + tid;
+    kv[u] = keys[j < end ? j : end - 1];
+  }
+  // L = the lowest key of the highest bin at which the query's global histogram, counted from the top,
+  // reaches k (every winner is >= L; no such bin: L = 0, every block a candidate)
+  if (tid == 0) L_s = 0;
+  {
+    const int top = kHistBins - 8 * tid;
+    uint32_t hv[8];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 1; i <= 8; ++i) {
+      hv[i - 1] = q_hist(a, q)[top - i];
+      cnt += hv[i - 1];
+    }
+    uint32_t tot;
+    const uint32_t excl = block_excl_scan(cnt, wsum, &tot);
+    const uint32_t kk = (uint32_t)a.k;
+    if (excl < kk && excl + cnt >= kk) {
+      uint32_t c = excl;
+      for (int i = 1; i <= 8; ++i) {
+        c += hv[i - 1];
+        if (c >= kk) {
+          L_s = (uint32_t)(top - i) << 20;
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t L = L_s;
+  // candidates (key >= L) keep index order: (u, wave, lane) order is ascending j
+  uint64_t masks[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t j = start + (int64_t)u * 512 + tid;
+    masks[u] = __ballot(j < end && kv[u] >= L);
+    if (lane == 0) cnt_s[u * 8 + wave] = (uint32_t)__popcll(masks[u]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scan of the kPer*8 counts in (u, wave) order; two per lane
+    uint32_t c0 = cnt_s[2 * lane], c1 = cnt_s[2 * lane + 1];
+    uint32_t incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    uint32_t excl = incl - c0 - c1;
+    cnt_s[2 * lane] = excl;
+    cnt_s[2 * lane + 1] = excl + c0;
+    if (lane == 63) total_s = incl;
+  }
+  __syncthreads();
+  uint64_t* seg = q_cand(a, q) + start;  // this workgroup's segment
+  const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if ((masks[u] >> lane) & 1ull) {
+      const uint32_t pos = cnt_s[u * 8 + wave] + (uint32_t)__popcll(masks[u] & lt);
+      const uint32_t j = (uint32_t)(start + (int64_t)u * 512 + tid);
+      seg[pos] = ((uint64_t)kv[u] << 32) | (uint64_t)(0xFFFFFFFFu - j);
+    }
+  }
+  if (tid == 0) q_seg(a, q)[blockIdx.x] = total_s;
+}
+
+// Selection: one workgroup per query gathers the ordered candidates and radix-selects the k largest.
+// Every scan workgroup has read the histogram by now, so it is cleared here for the next call.
+__global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
+  __shared__ SelectLds S;
+  const int q = blockIdx.x;
+  const int64_t N = visible_blocks(a, q % a.Tq);
+  if (N <= a.k) return;
+  for (int i = threadIdx.x; i < kHistBins; i += 512) q_hist(a, q)[i] = 0u;
+  select_query(a, q, N, S);
+}
+
 }  // namespace
 
 hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
@@ -616,10 +645,9 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
 hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s) {
   const int64_t N_last = a.len / a.m;
   const unsigned nq = (unsigned)(B * a.Tq);
-  if (N_last > a.k) {
-    unsigned g2 = (unsigned)((N_last + kScanPerWG - 1) / kScanPerWG);
-    hipLaunchKernelGGL(scan_kernel, dim3(g2, nq), dim3(256), 0, s, a);
-  }
+  unsigned g2 = (unsigned)((N_last + kScanPerWG - 1) / kScanPerWG);
+  if (g2 < 1) g2 = 1;
+  hipLaunchKernelGGL(scan_kernel, dim3(g2, nq), dim3(512), 0, s, a);
   hipLaunchKernelGGL(select_kernel, dim3(nq), dim3(512), 0, s, a);
   return hipGetLastError();
 }

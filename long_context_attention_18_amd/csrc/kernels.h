@@ -53,15 +53,17 @@ struct IngestArgs {
   double inv_freq[32];
 };
 
+// The indexer's workspace is one block per query (so its place does not depend on how many queries
+// a call has): [histogram kHistBins u32][seg_cnt G2 u32][keys max_blocks u32]
+// [candidates max_blocks u64], each part 256-byte aligned, qstride bytes per query.
 struct ScoreArgs {
   const uint16_t* qI;      // [B][Tq][HI][64]
   const float* w;          // [B][Tq][HI]
   const uint8_t* idx_codes;
   const uint8_t* idx_scale;
-  uint32_t* keys;          // ws [B*Tq][max_blocks]
-  uint32_t* ghist;         // ws [B*Tq][kHistBins]: per-query global histogram, zero between calls
-  uint64_t* cand;          // ws [B*Tq][max_blocks]: ordered candidates, one segment per scan workgroup
-  uint32_t* seg_cnt;       // ws [B*Tq][G2]: candidates per segment
+  uint8_t* qbase;          // ws: per-query blocks
+  uint64_t qstride;
+  uint64_t off_seg, off_keys, off_cand;
   int32_t* topk;           // [B][Tq][k]
   int64_t len;
   int64_t max_blocks;
@@ -69,8 +71,13 @@ struct ScoreArgs {
   int32_t HI;
   int32_t k;
   int32_t m;
-  int32_t G2;              // scan segments per query (stride of seg_cnt)
+  int32_t G2;              // scan segments per query
 };
+
+__device__ __forceinline__ uint32_t* q_hist(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride); }
+__device__ __forceinline__ uint32_t* q_seg(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_seg); }
+__device__ __forceinline__ uint32_t* q_keys(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_keys); }
+__device__ __forceinline__ uint64_t* q_cand(const ScoreArgs& a, int q) { return (uint64_t*)(a.qbase + (size_t)q * a.qstride + a.off_cand); }
 
 struct AttnArgs {
   const uint16_t* q;       // [B][Tq][H][128]
