@@ -194,8 +194,7 @@ class Layer:
             self.dev.index_score(q["qI"], q["w"])
             if ev_score is not None:
                 rec(ev_score[1])
-            self.dev.topk_select(1, topk)
-            self.dev.sparse_attn(q["q"], topk, out)
+            self.dev.topk_attn(q["q"], out, None, topk)
         else:
             if ev_score is not None:
                 rec(ev_score[0])

@@ -118,12 +118,13 @@ size_t lca_cache_bytes(const lca_layer_desc* desc, int32_t batch, int64_t max_ct
 lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* base_dev, size_t bytes,
                           int32_t batch, int64_t max_ctx, int32_t ring, void* stream);
 
-/* Scratch one call of lca_csa_indexer_topk / lca_csa_sparse_attn /
- * lca_hca_dense_attn needs for up to max_tq queries per sequence at up to
+/* Scratch one call of lca_csa_indexer_topk / lca_csa_attend /
+ * lca_csa_sparse_attn / lca_hca_dense_attn needs for up to max_tq queries per sequence at up to
  * max_ctx tokens. For CSA it holds, per query, a 16 KiB histogram that must
  * be zero when an indexer call starts: zero the workspace once with
  * lca_workspace_init() before its first use; every completed
- * lca_csa_indexer_topk (or lca_csa_topk_select) leaves it zero again.
+ * lca_csa_indexer_topk, lca_csa_topk_select, lca_csa_attend or
+ * lca_csa_topk_attn leaves it zero again.
  * Everything else in it is rewritten by each call. A workspace may be shared
  * by caches of the same or smaller shape; calls sharing one workspace must
  * not overlap in time. */
@@ -214,6 +215,27 @@ lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const in
  * over every visible D1 entry j < (t+1)/m plus the window. */
 lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev,
                               float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* The CSA query path with the selection and the attention in one launch
+ * (CSA paragraph: top-k compressed blocks per query; Figure 3: their
+ * attention joined with the sliding-window branch under one softmax).
+ * Results are those of lca_csa_indexer_topk followed by lca_csa_sparse_attn
+ * on the same arguments: the same top-k lists bit for bit, attention outputs
+ * equal up to fp32 summation order.
+ *  lca_csa_attend: indexer scores, top-k and attention of the Tq queries
+ *    (three kernels: score, candidate scan, selection + attention).
+ *  lca_csa_topk_attn: the same after a separate lca_csa_index_score with the
+ *    same cache state, Tq and workspace.
+ * topk_dev ([B][Tq][k] int32) may be NULL when the lists are not wanted.
+ * Every workgroup of the last kernel selects its query's list itself (one
+ * per 16 heads): meant for decode-sized Tq; large Tq (chunked prefill) is
+ * cheaper through the separate calls. Workspace and histogram rules as for
+ * lca_csa_indexer_topk; ring >= Tq + window - 1. */
+lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev,
+                          int32_t Tq, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream);
+lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev,
+                             uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* lca_status_str(lca_status status);

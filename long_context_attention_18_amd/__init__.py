@@ -68,6 +68,8 @@ _SIGNATURES = {
     "lca_csa_topk_select": (_I32, [_CP, _I32, _VP, _VP, _SZ, _VP]),
     "lca_csa_sparse_attn": (_I32, [_CP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "lca_hca_dense_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_csa_attend": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -177,6 +179,16 @@ def lca_hca_dense_attn(cache, q, Tq, out, lse, ws, ws_bytes, stream=None):
                                                            _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def lca_csa_attend(cache, qI, w, q, Tq, topk, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_csa_attend", lib().lca_csa_attend(ctypes.byref(cache), _ptr(qI), _ptr(w), _ptr(q), Tq, _ptr(topk),
+                                                   _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_csa_topk_attn(cache, q, Tq, topk, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_csa_topk_attn", lib().lca_csa_topk_attn(ctypes.byref(cache), _ptr(q), Tq, _ptr(topk), _ptr(out),
+                                                         _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def lca_status_str(status):
     return lib().lca_status_str(status).decode()
 
@@ -238,6 +250,12 @@ class DeviceLayer:
 
     def dense_attn(self, q, out, lse=None, stream=None):
         lca_hca_dense_attn(self.cache, q, q.shape[1], out, lse, self.ws, self.ws_bytes, stream)
+
+    def attend(self, qI, w, q, out, lse=None, topk=None, stream=None):
+        lca_csa_attend(self.cache, qI, w, q, q.shape[1], topk, out, lse, self.ws, self.ws_bytes, stream)
+
+    def topk_attn(self, q, out, lse=None, topk=None, stream=None):
+        lca_csa_topk_attn(self.cache, q, q.shape[1], topk, out, lse, self.ws, self.ws_bytes, stream)
 
     def index_scores(self, Tq):
         """fp32 scores the last index_score / indexer_topk call left in the workspace: [B][Tq][max_blocks]."""

@@ -1,0 +1,443 @@
+// attend.hip -- one-launch attention for a few queries (decode), for gfx950.
+//
+// Figure 3 of "DeepSeek-V4: a million-token context that agents can actually
+// use" (CSA: the selected compressed blocks plus a sliding-window branch) and
+// Figure 4 / the HCA paragraph (every compressed block plus the window), with
+// one softmax over all of a query's keys:
+//   logit = RoPE(q_h, t) . x / sqrt(128),  K = V = the dequantised entry.
+//
+// A workgroup owns one query and 16 of its heads, and walks ALL the query's
+// keys, so no split-K partials and no merge launch are needed: the 8 waves
+// take 32-key chunks in turn, each keeps an online softmax for the 16 heads,
+// and the 8 wave states are merged in LDS at the end. With few queries the
+// step is latency-bound, and this keeps it to one launch. Each wave takes a
+// contiguous range of the key slots and issues the gathers of up to kRound
+// chunks at once (random reads: one memory latency per round).
+//
+// Modes: LIST (the caller's top-k list), DENSE (HCA: every visible block) and
+// SELECT (CSA: the workgroup first runs the exact top-k selection of its
+// query from the scan's candidates, select.h, into LDS -- the 4 head-group
+// workgroups of a query do it side by side, which costs no extra time in a
+// latency-bound step -- then attends over the result).
+//
+// Key slots: the window first, then the compressed entries (the softmax does
+// not depend on the order).
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16; lane l = 16 g + r):
+//   S^T = K . Q^T   A = 16 keys x 32 dims, straight from the gathered entry
+//                   (lane: key r, dims 8g..8g+7 of the K-step); B = Q^T
+//                   (lane: head r, same dims); out lane: head r, keys 4g+v.
+//   O^T = V^T . P^T A = V^T (lane: dim r of the tile, 8 keys) from a per-wave
+//                   LDS transpose; B = P^T (lane: head r, keys 8g..8g+7).
+// Within a 32-key chunk, MFMA K index 8g + 2v + tt is key 4g+v of 16-key tile
+// tt, so each lane's B operand for P^T is exactly the 8 logits it holds. The
+// FP8 codes and BF16 RoPE dims are exact in bf16; the fp32 scale multiplies
+// the nope logits and is folded into P for the nope output dims.
+#include "dev_formats.h"
+#include "kernels.h"
+#include "select.h"
+
+namespace lca {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 8;
+constexpr int kChunk = 32;     // keys per wave step: two 16-key tiles
+constexpr int kVtStride = 40;  // bf16 per V^T row (32 keys + 8 pad; 80 B keeps 16-B reads aligned)
+constexpr int kRound = 4;      // chunks a wave gathers at once (VGPR budget)
+
+struct AttendLds {
+  union {
+    SelectLds sel;  // selection
+    struct {
+      uint16_t vt[kWaves][kHeadDim * kVtStride];  // per-wave V^T of its current chunk
+      float scl[kWaves][2][16];                   // per-wave key scales of the chunk's two tiles
+    } b;
+    struct {
+      float o[kWaves][16][kHeadDim + 4];  // row stride 132 floats: conflict-free 16-B accesses
+      float m[kWaves][16], l[kWaves][16];
+    } c;
+  } u;
+  int32_t list[kMaxTopk];  // compressed entries to attend (block indices)
+  float cos_t[32], sin_t[32];
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// value held by lane l ^ 16 / l ^ 32 (VALU lane swaps)
+__device__ __forceinline__ float xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+}
+
+// 8 E4M3FN codes (little-endian bytes) -> 8 bf16: v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts
+// two codes exactly (every E4M3FN value is a bf16 value; checked for all 256 codes on MI355X)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 c) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true));
+  return o;
+}
+
+// two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed low first
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// Load through a global-address-space pointer (a global_load, counted by vmcnt only).
+template <typename T>
+__device__ __forceinline__ T ldg(const void* p) {
+  typedef const __attribute__((address_space(1))) T global_t;
+  return *(global_t*)p;
+}
+
+// One 32-key chunk's raw gathered data, as lane (r, g) holds it: key r of tiles 0 and 1.
+struct Raw {
+  u32x2 c0[2], c1[2];  // FP8 codes, dims 8g..8g+7 and 32+8g..32+8g+7
+  u32x4 r0[2], r1[2];  // BF16 RoPE dims 64+8g.. and 96+8g..
+  float sc[2];
+};
+
+struct Keys {
+  // base arrays and sizes held by value: read through a pointer to the kernel arguments they become
+  // vector loads that every gather would wait for
+  const uint8_t *win_codes, *blk_codes;
+  const uint16_t *win_rope, *blk_rope;
+  const float *win_scale, *blk_scale;
+  uint32_t ring;
+  const int32_t* list;
+  size_t win_row, blk_row;  // b * ring, b * max_blocks
+  uint32_t win_base;        // ring slot of the first window position
+  int n_win, n_list;
+  bool use_list;
+  // Entry of key slot `slot` (< n_win + n_list): window position t - n_win + 1 + slot, or the
+  // compressed block list[slot - n_win] (dense: slot - n_win). Branch-free, so the loads that
+  // follow stay in straight-line code and the compiler can wait for them one chunk at a time.
+  __device__ __forceinline__ size_t entry(int slot, bool* in_win) const {
+    *in_win = slot < n_win;
+    const int li = *in_win ? 0 : slot - n_win;
+    const int64_t j = use_list ? (int64_t)list[li] : (int64_t)li;
+    uint32_t ws = win_base + (uint32_t)slot;
+    ws = ws >= ring ? ws - ring : ws;
+    return *in_win ? win_row + ws : blk_row + (size_t)j;
+  }
+  // lane (r, g): key r of the chunk's two tiles; slots at or beyond `end` read slot 0 (masked later)
+  __device__ __forceinline__ void load(int chunk_slot, int end, int r, int g, Raw& R) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      int slot = chunk_slot + tt * 16 + r;
+      slot = slot < end ? slot : 0;
+      bool w;
+      const size_t e = entry(slot, &w);
+      const uint8_t* codes = (w ? win_codes : blk_codes) + e * kNope;
+      const uint16_t* rope = (w ? win_rope : blk_rope) + e * kRope;
+      const float* scl = (w ? win_scale : blk_scale) + e;
+      R.c0[tt] = ldg<u32x2>(codes + 8 * g);
+      R.c1[tt] = ldg<u32x2>(codes + 32 + 8 * g);
+      R.r0[tt] = ldg<u32x4>(rope + 8 * g);
+      R.r1[tt] = ldg<u32x4>(rope + 32 + 8 * g);
+      R.sc[tt] = ldg<float>(scl);
+    }
+  }
+};
+
+// One 32-key chunk of one wave: S^T = K . Q^T for the two 16-key tiles, the online softmax of head r,
+// V^T into the wave's LDS buffer, O^T += V^T . P^T. Lane (r, g): head r; keys 4g+v of each tile.
+// Logits stay unscaled (S = q.x); the 1/sqrt(128) and log2(e) factors go into one multiply before
+// exp2. The running max m is raised only when a chunk's max exceeds it by more than kLazy (log2
+// units), and only then is O rescaled (once per wave, for the heads that moved): the softmax does
+// not depend on the reference point, and P stays below 2^kLazy. Slots at or beyond `end` are empty.
+__device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int end, const bf16x8 (&qb)[4], float* scl,
+                                             uint16_t* vt, int kpos, int r, int g, float& m_run, float& l_run,
+                                             v4f (&O)[8]) {
+  constexpr float kC = 0.12751743074640293f;  // log2(e) / sqrt(128)
+  constexpr float kLazy = 8.0f;
+  u32x4 kn0[2], kn1[2];
+  float Sv[2][4];
+  v4f sc4[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    kn0[tt] = fp8x8_to_bf16(cur.c0[tt]);
+    kn1[tt] = fp8x8_to_bf16(cur.c1[tt]);
+    v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+    an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kn0[tt]), qb[0], an, 0, 0, 0);
+    an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kn1[tt]), qb[1], an, 0, 0, 0);
+    ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.r0[tt]), qb[2], ar, 0, 0, 0);
+    ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.r1[tt]), qb[3], ar, 0, 0, 0);
+    if (g == 0) scl[tt * 16 + r] = cur.sc[tt];
+    sc4[tt] = *reinterpret_cast<const v4f*>(scl + tt * 16 + 4 * g);
+    const int slot0 = chunk_slot + tt * 16 + 4 * g;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Sv[tt][v] = (slot0 + v < end) ? an[v] * sc4[tt][v] + ar[v] : -INFINITY;
+  }
+  // online softmax of head r (its keys are spread over the 4 lane groups)
+  float mx = fmaxf(fmaxf(fmaxf(Sv[0][0], Sv[0][1]), fmaxf(Sv[0][2], Sv[0][3])),
+                   fmaxf(fmaxf(Sv[1][0], Sv[1][1]), fmaxf(Sv[1][2], Sv[1][3])));
+  mx = fmaxf(mx, xor16(mx));
+  mx = fmaxf(mx, xor32(mx));
+  const bool raise = mx * kC > m_run * kC + kLazy;  // also true for the first finite max (m_run = -inf)
+  if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
+    const float m_new = raise ? mx : m_run;
+    const float alpha = raise ? __builtin_amdgcn_exp2f((m_run - m_new) * kC) : 1.0f;  // 0 from -inf
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+  float rs = 0.0f;
+  u32x4 pr, pn;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float p0 = __builtin_amdgcn_exp2f((Sv[0][v] - m_use) * kC);
+    const float p1 = __builtin_amdgcn_exp2f((Sv[1][v] - m_use) * kC);
+    rs += p0 + p1;
+    pr[v] = pack_bf16(p0, p1);
+    pn[v] = pack_bf16(p0 * sc4[0][v], p1 * sc4[1][v]);
+  }
+  rs += xor16(rs);
+  rs += xor32(rs);
+  l_run += rs;
+
+  // V^T of the chunk into this wave's LDS buffer: per dim, the pair (tile 0, tile 1) of key r
+  {
+    const u32x4 grp[4][2] = {{kn0[0], kn0[1]}, {kn1[0], kn1[1]}, {cur.r0[0], cur.r0[1]}, {cur.r1[0], cur.r1[1]}};
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int dim0 = 32 * G + 8 * g;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // low (u even) or high (u odd) halves of the two tiles' words: v_perm_b32 byte select
+        const uint32_t pair = __builtin_amdgcn_perm(grp[G][1][u >> 1], grp[G][0][u >> 1],
+                                                    (u & 1) ? 0x07060302u : 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vt + (dim0 + u) * kVtStride + kpos) = pair;
+      }
+    }
+  }
+  // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P)
+  const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const u32x4 va = *reinterpret_cast<const u32x4*>(vt + (dt * 16 + r) * kVtStride + 8 * g);
+    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0,
+                                                     0);
+  }
+}
+
+// NR chunks of one wave: every gather issued first, then the chunks in order (straight-line code).
+template <int NR>
+__device__ __forceinline__ void attend_round(const Keys K, int slot0, int end, const bf16x8 (&qb)[4], float* scl,
+                                             uint16_t* vt, int kpos, int r, int g, float& m_run, float& l_run,
+                                             v4f (&O)[8]) {
+  Raw buf[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) K.load(slot0 + u * kChunk, end, r, g, buf[u]);
+#pragma unroll
+  for (int u = 0; u < NR; ++u)
+    attend_chunk(buf[u], slot0 + u * kChunk, end, qb, scl, vt, kpos, r, g, m_run, l_run, O);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
+  __shared__ AttendLds S;
+  const AttnArgs& a = args.t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int hg = blockIdx.x, q = blockIdx.y;
+  const int b = q / a.Tq, tq = q % a.Tq;
+  const int64_t t = a.len - a.Tq + tq;
+  const int64_t N = (t + 1) / a.m;
+  const bool do_select = MODE == kAttendSelect && N > a.k;
+
+  Keys K;
+  K.win_codes = a.win_codes;
+  K.blk_codes = a.blk_codes;
+  K.win_rope = a.win_rope;
+  K.blk_rope = a.blk_rope;
+  K.win_scale = a.win_scale;
+  K.blk_scale = a.blk_scale;
+  K.ring = (uint32_t)a.ring;
+  K.list = S.list;
+  K.win_row = (size_t)b * a.ring;
+  K.blk_row = (size_t)b * a.max_blocks;
+  K.n_win = (int)((int64_t)a.W < t + 1 ? (int64_t)a.W : t + 1);
+  K.win_base = (uint32_t)((t - K.n_win + 1) % a.ring);
+  if (MODE == kAttendDense) {
+    K.n_list = (int)N;
+    K.use_list = false;
+  } else if (MODE == kAttendList) {
+    K.n_list = a.k;
+    K.use_list = true;
+  } else {
+    K.n_list = (int)(N < a.k ? N : (int64_t)a.k);
+    K.use_list = do_select;
+  }
+  // RoPE angles of position t: reduced to [-pi, pi] in fp64 (2 pi as a double plus its remainder),
+  // then fp32 sin / cos; the rotated query is rounded to bf16, far coarser than either step
+  if (tid < 32) {
+    const double phi = (double)t * a.inv_freq[tid];
+    const double n = rint(phi * 0.15915494309189535);
+    const double rr = (phi - n * 6.28318530717958623) - n * 2.4492935982947064e-16;
+    float sn, cs;
+    sincosf((float)rr, &sn, &cs);
+    S.cos_t[tid] = cs;
+    S.sin_t[tid] = sn;
+  }
+  // query rows (head hg*16 + r, dims 32 ks + 8 g ..), loaded now, rotated after the barrier
+  const int head = hg * 16 + r;
+  const bool head_ok = head < a.H;
+  u32x4 qraw[4];
+  {
+    const uint16_t* qp = a.q + (((size_t)b * a.Tq + tq) * a.H + (head_ok ? head : 0)) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qraw[ks] = head_ok ? *reinterpret_cast<const u32x4*>(qp + ks * 32 + 8 * g) : (u32x4){0u, 0u, 0u, 0u};
+  }
+  if (MODE == kAttendList) {
+    // the caller's list, valid entries (0 <= j < N) only, in order
+    const int32_t* lp = a.topk + ((size_t)b * a.Tq + tq) * a.k;
+    uint32_t* wsum = S.u.sel.wsum;
+    int n = 0;
+    for (int base = 0; base < a.k; base += 512) {
+      const int i = base + tid;
+      const int32_t j = i < a.k ? lp[i] : -1;
+      const bool ok = j >= 0 && (int64_t)j < N;
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+      __syncthreads();
+      int pos = n + (int)__popcll(m & ((1ull << lane) - 1ull));
+      int tot = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = (int)wsum[w];
+        if (w < wave) pos += c;
+        tot += c;
+      }
+      if (ok) S.list[pos] = j;
+      n += tot;
+      __syncthreads();
+    }
+    K.n_list = n;
+  }
+  if (do_select) {
+    const ScoreArgs& sa = args.s;
+    if (hg == 0)  // every scan workgroup has read this query's histogram: clear it for the next call
+      for (int i = tid; i < kHistBins; i += 512) q_hist(sa, q)[i] = 0u;
+    select_query(sa, q, N, S.u.sel, S.list);
+  }
+  __syncthreads();
+  if (do_select && hg == 0 && args.s.topk) {
+    int32_t* o = args.s.topk + (size_t)q * a.k;
+    for (int i = tid; i < a.k; i += 512) o[i] = S.list[i];
+  }
+
+  // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3)
+  bf16x8 qb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 v = qraw[ks];
+    if (ks >= 2) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pi = 16 * (ks - 2) + 4 * g + u;
+        const float c = S.cos_t[pi], s = S.sin_t[pi];
+        const float x0 = bf16_to_f32((uint16_t)(v[u] & 0xFFFFu));
+        const float x1 = bf16_to_f32((uint16_t)(v[u] >> 16));
+        v[u] = (uint32_t)f32_to_bf16(x0 * c - x1 * s) | ((uint32_t)f32_to_bf16(x0 * s + x1 * c) << 16);
+      }
+    }
+    qb[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  v4f O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  uint16_t* vt = S.u.b.vt[wave];
+  float* scl = &S.u.b.scl[wave][0][0];
+  const int kpos = 8 * (r >> 2) + 2 * (r & 3);  // MFMA K index of key r of tile 0 (tile 1: +1)
+
+  // wave w: key slots [w * per, (w + 1) * per), in rounds of up to kRound chunks
+  const int n_keys = K.n_win + K.n_list;
+  const int per = ((n_keys + kWaves * 16 - 1) / (kWaves * 16)) * 16;
+  const int w_begin = wave * per;
+  const int w_end = min(w_begin + per, n_keys);
+  const int w_chunks = (per + kChunk - 1) / kChunk;  // the same for every wave
+  for (int c = 0; c < w_chunks; c += kRound) {
+    const int slot0 = w_begin + c * kChunk;
+    switch (min(kRound, w_chunks - c)) {
+      case 1: attend_round<1>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
+      case 2: attend_round<2>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
+      case 3: attend_round<3>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
+      default: attend_round<kRound>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
+    }
+  }
+
+  // ---- merge the 8 wave states: lane (r, g) holds head r, dims dt*16 + 4g + v
+  __syncthreads();
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&S.u.c.o[wave][r][dt * 16 + 4 * g]) = O[dt];
+  if (g == 0) {
+    S.u.c.m[wave][r] = m_run;
+    S.u.c.l[wave][r] = l_run;
+  }
+  __syncthreads();
+  {
+    const int h = tid >> 5, d0 = (tid & 31) * 4;
+    // wave states in raw logit units (q . x): weight 2^((m_w - M) log2(e) / sqrt(128))
+    constexpr float kC = 0.12751743074640293f;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.u.c.m[w][h]);
+    float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = S.u.c.m[w][h];
+      if (mw == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f((mw - M) * kC);
+      L += S.u.c.l[w][h] * f;
+      const v4f ov = *reinterpret_cast<const v4f*>(&S.u.c.o[w][h][d0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += ov[i] * f;
+    }
+    const int hh = hg * 16 + h;
+    if (hh < a.H) {
+      const float inv = 1.0f / L;
+      const size_t row = ((size_t)b * a.Tq + tq) * a.H + hh;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
+      *reinterpret_cast<uint2*>(a.out + row * kHeadDim + d0) = pk;
+      if (a.lse && d0 == 0) a.lse[row] = M * 0.08838834764831845f + __logf(L);  // natural-log units
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t s) {
+  const unsigned nq = (unsigned)(B * args.t.Tq);
+  const unsigned hgs = (unsigned)((args.t.H + 15) / 16);
+  if (mode == kAttendSelect) hipLaunchKernelGGL(attend_kernel<kAttendSelect>, dim3(hgs, nq), dim3(512), 0, s, args);
+  else if (mode == kAttendDense) hipLaunchKernelGGL(attend_kernel<kAttendDense>, dim3(hgs, nq), dim3(512), 0, s, args);
+  else hipLaunchKernelGGL(attend_kernel<kAttendList>, dim3(hgs, nq), dim3(512), 0, s, args);
+  return hipGetLastError();
+}
+
+}  // namespace lca

@@ -338,11 +338,13 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
   return launch_status(launch_topk_select(a, cache->batch, (hipStream_t)stream));
 }
 
-static lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev,
-                                 int32_t Tq, uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+lca_status attn_args(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
+                     uint16_t* out_dev, float* lse_dev, AttnArgs* out) {
   if (!cache_ok(cache) || !q_dev || !out_dev) return LCA_ERR_NULL;
-  if (!dense && !topk_dev) return LCA_ERR_NULL;
   if (dense != (cache->desc.kind == LCA_KIND_HCA)) return LCA_ERR_UNSUPPORTED;
   if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
   if (cache->pending != 0) return LCA_ERR_ORDER;
@@ -368,8 +370,27 @@ static lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q
   a.ring = cache->ring;
   a.dense = dense ? 1 : 0;
   std::memcpy(a.inv_freq, cache->rope_inv_freq, sizeof(a.inv_freq));
-  const int64_t n_first = dense ? cache->len / cache->desc.m : (int64_t)cache->desc.topk;
+  *out = a;
+  return LCA_OK;
+}
+
+// Few queries: one launch, a workgroup per (query, 16 heads) over all keys. Many queries: one
+// workgroup per query and all heads, split over the keys only while there are too few queries
+// to fill the chip (then merged).
+lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev,
+                          int32_t Tq, uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes,
+                          void* stream) {
+  if (!dense && !topk_dev) return LCA_ERR_NULL;
+  AttnArgs a;
+  lca_status st = attn_args(cache, dense, q_dev, topk_dev, Tq, out_dev, lse_dev, &a);
+  if (st != LCA_OK) return st;
   const int32_t nq = cache->batch * Tq;
+  if (nq < kAttnTargetWGs) {
+    AttendArgs args{};
+    args.t = a;
+    return launch_status(launch_attend(args, cache->batch, dense ? kAttendDense : kAttendList, (hipStream_t)stream));
+  }
+  const int64_t n_first = dense ? cache->len / cache->desc.m : (int64_t)cache->desc.topk;
   attn_splits(n_first + cache->desc.window, nq, &a.splits, &a.keys_per_split);
   if (a.splits > 1) {
     if (!ws_dev) return LCA_ERR_WORKSPACE;
@@ -380,6 +401,28 @@ static lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q
   return launch_status(launch_attention(a, cache->batch, (hipStream_t)stream));
 }
 
+lca_status topk_attn_impl(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, bool score,
+                          const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                          void* ws_dev, size_t ws_bytes, void* stream) {
+  AttendArgs args{};
+  lca_status st = score_args(cache, qI_dev, w_dev, score, Tq, topk_dev, false, ws_dev, ws_bytes, &args.s);
+  if (st != LCA_OK) return st;
+  st = attn_args(cache, false, q_dev, nullptr, Tq, out_dev, lse_dev, &args.t);
+  if (st != LCA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (score) {
+    hipError_t e = launch_index_score(args.s, cache->batch, s);
+    if (e != hipSuccess) return LCA_ERR_LAUNCH;
+  }
+  hipError_t e = launch_topk_select(args.s, cache->batch, s, false);
+  if (e != hipSuccess) return LCA_ERR_LAUNCH;
+  return launch_status(launch_attend(args, cache->batch, kAttendSelect, s));
+}
+
+}  // namespace
+
+extern "C" {
+
 lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
                                uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   return attention_impl(cache, false, q_dev, topk_dev, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
@@ -388,6 +431,19 @@ lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const in
 lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev,
                               float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   return attention_impl(cache, true, q_dev, nullptr, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+}
+
+lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev,
+                             uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return topk_attn_impl(cache, nullptr, nullptr, false, q_dev, Tq, topk_dev, out_dev, lse_dev, ws_dev, ws_bytes,
+                        stream);
+}
+
+lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev,
+                          int32_t Tq, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream) {
+  return topk_attn_impl(cache, qI_dev, w_dev, true, q_dev, Tq, topk_dev, out_dev, lse_dev, ws_dev, ws_bytes,
+                        stream);
 }
 
 }  // extern "C"

@@ -117,16 +117,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // Exact E4M3FN -> bfloat16 bit pattern (every E4M3FN value is a bf16 value;
-// NaN codes are never stored).
+// NaN codes are never stored). Branch-free: the 7 magnitude bits placed at
+// fp32's exponent/mantissa boundary (E at bit 23, M at bit 20) read as
+// 2^(E-127) * (1 + M/8), or M * 2^-129 for E = 0 (an fp32 subnormal); times
+// 2^120 that is the E4M3 value, 2^(E-7) * (1 + M/8) or M * 2^-9, exactly.
 __device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 8;
-  uint32_t E = (c >> 3) & 15u, M = c & 7u;
-  if (E == 0) {
-    // M * 2^-9: exact in fp32, then the top half of its bits
-    float f = (float)M * 0x1p-9f;
-    return (uint16_t)(s | (__float_as_uint(f) >> 16));
-  }
-  return (uint16_t)(s | ((E + 120u) << 7) | (M << 4));
+  const float f = __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
+  return (uint16_t)(((c & 0x80u) << 8) | (__float_as_uint(f) >> 16));
 }
 
 }  // namespace lca

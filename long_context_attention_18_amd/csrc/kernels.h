@@ -105,11 +105,22 @@ struct AttnArgs {
   double inv_freq[32];
 };
 
+// One-launch attention for a few queries (attend.hip): the query's compressed entries come from the
+// caller's top-k list, from every visible block (HCA), or from the top-k selection run in the same
+// workgroup over the scan's candidates.
+constexpr int kMaxTopk = 2048;
+constexpr int kAttendList = 0, kAttendDense = 1, kAttendSelect = 2;
+struct AttendArgs {
+  ScoreArgs s;  // selection inputs (kAttendSelect)
+  AttnArgs t;
+};
+
 hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s);
 hipError_t launch_append(const IngestArgs& a, bool csa, int32_t n_tail, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s);
-hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s);
+hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool with_select = true);
+hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s);
 
 }  // namespace lca

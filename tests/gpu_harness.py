@@ -90,8 +90,11 @@ class LayerRun:
         out = {k: np.stack([p[k] for p in per]) for k in per[0]}
         return self.qtransform(out) if self.qtransform else out
 
-    def run_queries(self, Tq):
-        """Queries at the last Tq positions -> (q inputs, topk or None, out bf16, lse)."""
+    def run_queries(self, Tq, fused=False):
+        """Queries at the last Tq positions -> (q inputs, topk or None, out bf16, lse).
+
+        fused: the CSA path through lca_csa_attend (selection and attention in one launch)
+        instead of lca_csa_indexer_topk + lca_csa_sparse_attn."""
         import torch
         pos = list(range(self.len - Tq, self.len))
         qin = self.queries(pos)
@@ -102,11 +105,15 @@ class LayerRun:
         self.last_scores = None
         if self.csa:
             topk = torch.full((self.B, Tq, self.layer.topk), -7, dtype=torch.int32, device="cuda")
-            self.dev.indexer_topk(to_dev(qin["qI"]), to_dev(qin["w"]), topk)
+            if fused:
+                self.dev.attend(to_dev(qin["qI"]), to_dev(qin["w"]), to_dev(qin["q"]), out, lse, topk)
+            else:
+                self.dev.indexer_topk(to_dev(qin["qI"]), to_dev(qin["w"]), topk)
             torch.cuda.synchronize()
             if self.len // self.m > self.layer.topk:
                 self.last_scores = self.dev.index_scores(Tq)
-            self.dev.sparse_attn(to_dev(qin["q"]), topk, out, lse)
+            if not fused:
+                self.dev.sparse_attn(to_dev(qin["q"]), topk, out, lse)
         else:
             self.dev.dense_attn(to_dev(qin["q"]), out, lse)
         torch.cuda.synchronize()

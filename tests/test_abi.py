@@ -98,6 +98,8 @@ def test_bad_arguments_are_rejected_before_any_launch():
     assert L.lca_csa_indexer_topk(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, None) == -1
     assert L.lca_csa_sparse_attn(ctypes.byref(cache), 1, 1, 1, 1, None, 1, 1, None) == -1
     assert L.lca_hca_dense_attn(ctypes.byref(cache), 1, 1, 1, None, 1, 1, None) == -1
+    assert L.lca_csa_attend(ctypes.byref(cache), 1, 1, 1, 1, None, 1, None, 1, 1, None) == -1
+    assert L.lca_csa_topk_attn(ctypes.byref(cache), 1, 1, None, 1, None, 1, 1, None) == -1
     assert L.lca_workspace_init(None, 256, None) == -1
 
 
@@ -135,10 +137,17 @@ def test_order_capacity_and_kind_checks():
     # workspace missing / too small
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, None, 0, None) == -6
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, P, 16, None) == -6
+    assert L.lca_csa_attend(ctypes.byref(c), P, P, P, 1, None, P, None, None, 0, None) == -6
     # window state too small for Tq queries at once
     assert L.lca_csa_sparse_attn(ctypes.byref(c), P, P, 2, P, None, P, 1 << 30, None) == -4
+    assert L.lca_csa_attend(ctypes.byref(c), P, P, P, 2, None, P, None, P, 1 << 30, None) == -4
+    assert L.lca_csa_topk_attn(ctypes.byref(c), P, 2, None, P, None, P, 1 << 30, None) == -4
+    # the fused query path needs q and out; the top-k list output is optional
+    assert L.lca_csa_attend(ctypes.byref(c), P, P, None, 1, None, P, None, P, 1 << 30, None) == -1
+    assert L.lca_csa_topk_attn(ctypes.byref(c), P, 1, None, None, None, P, 1 << 30, None) == -1
     h = _fake_bound_cache("hca")
     assert L.lca_csa_compress(ctypes.byref(h), P, P, P, P, P, P, 1, None) == -3
+    assert L.lca_csa_attend(ctypes.byref(h), P, P, P, 1, None, P, None, P, 1 << 30, None) == -3
 
 
 def test_workspace_bytes_grows_with_queries():

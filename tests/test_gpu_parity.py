@@ -22,12 +22,12 @@ def _ingest(run, chunks):
         run.ingest(T)
 
 
-def _decode(run, n_steps, oracle_upto):
+def _decode(run, n_steps, oracle_upto, fused=False):
     oc = [run.oracle_caches(b, oracle_upto) for b in range(run.B)]
     worst = None
     for _ in range(n_steps):
         run.ingest(1)
-        qin, topk, out, lse = run.run_queries(1)
+        qin, topk, out, lse = run.run_queries(1, fused=fused)
         w = check_queries(run, oc, qin, topk, out, lse, [run.len - 1])
         worst = w if worst is None else {k: max(worst[k], w[k]) for k in w}
     return worst, oc
@@ -139,3 +139,69 @@ def test_indexer_exact_on_wide_scale_gaps():
     worst, oc = _decode(run, 3, 5003)
     assert worst["scores_checked"] > 0
     compare_cache(run, oc)
+
+
+def test_csa_calls_with_changing_query_counts():
+    """One workspace serves indexer calls of 48, 1, 17 and 1 queries in turn (each query sees more than k
+    blocks): every call starts from the histograms the previous one cleared, whatever its query count."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=64)
+    run = LayerRun(layer, B=2, max_ctx=3072, ring=48 + 127, max_tq=48)
+    _ingest(run, [2048])
+    oc = [run.oracle_caches(b, 3072) for b in range(run.B)]
+    for Tq in (48, 1, 17, 1):
+        run.ingest(Tq)
+        qin, topk, out, lse = run.run_queries(Tq)
+        check_queries(run, oc, qin, topk, out, lse, list(range(run.len - Tq, run.len)))
+
+
+def test_fused_attend_many_score_tiles():
+    """lca_csa_attend (selection + attention in one launch) on the multi-tile CSA case: top-k lists and
+    scores bit-exact, attention within the bar."""
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=256)
+    run = LayerRun(layer, B=2, max_ctx=20000, ring=128)
+    _ingest(run, [8192, 8192, 1999])
+    worst, oc = _decode(run, 3, run.len + 3, fused=True)
+    assert worst["scores_checked"] > 0
+    print("fused multi-tile worst", worst)
+
+
+def test_fused_attend_short_context_and_small_heads():
+    """lca_csa_attend with fewer visible blocks than k (no selection) and H = 8 (half a head group)."""
+    layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
+    run = LayerRun(layer, B=1, max_ctx=512, ring=128, sigma=0.02 * 1024 ** 0.5, hidden=1024)
+    _ingest(run, [200])
+    _decode(run, 60, 260, fused=True)  # crosses from N <= k to N > k
+
+
+def test_fused_matches_separate_calls():
+    """Same state, same queries: lca_csa_attend and lca_csa_indexer_topk + lca_csa_sparse_attn give the same
+    top-k lists, and outputs equal up to fp32 summation order; lca_csa_topk_attn without a list output
+    gives the fused outputs bit for bit."""
+    import torch
+    try:
+        from gpu_harness import to_dev, attn_error
+    except ImportError:
+        from tests.gpu_harness import to_dev, attn_error
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=512)
+    run = LayerRun(layer, B=3, max_ctx=12000, ring=128)
+    _ingest(run, [11000])
+    qin = run.queries([run.len - 1])
+    qI, w, q = to_dev(qin["qI"]), to_dev(qin["w"]), to_dev(qin["q"])
+    shape = (run.B, 1, layer.n_heads, 128)
+    out_s = torch.empty(shape, dtype=torch.int16, device="cuda")
+    out_f = torch.empty(shape, dtype=torch.int16, device="cuda")
+    out_t = torch.empty(shape, dtype=torch.int16, device="cuda")
+    tk_s = torch.full((run.B, 1, layer.topk), -7, dtype=torch.int32, device="cuda")
+    tk_f = torch.full((run.B, 1, layer.topk), -7, dtype=torch.int32, device="cuda")
+    run.dev.indexer_topk(qI, w, tk_s)
+    run.dev.sparse_attn(q, tk_s, out_s)
+    run.dev.attend(qI, w, q, out_f, None, tk_f)
+    run.dev.index_score(qI, w)
+    run.dev.topk_attn(q, out_t)
+    torch.cuda.synchronize()
+    assert torch.equal(tk_s, tk_f)
+    assert torch.equal(out_f, out_t)
+    a = out_f.cpu().numpy().view(np.uint16)
+    ref = synth.bf16_to_f32(out_s.cpu().numpy().view(np.uint16)).astype(np.float64)
+    rel, mab = attn_error(a, ref)
+    assert rel < 4e-3 and mab < 1e-2, (rel, mab)
