@@ -53,6 +53,8 @@ def parse_args():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 256 MiB device copy first (reference kernel for HBM counters)")
     p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    p.add_argument("--no-step-events", action="store_true",
+                   help="time the region without the per-step events around the dominant kernel (no roofline)")
     return p.parse_args()
 
 
@@ -320,7 +322,7 @@ def main():
     def run_steps(steps, timed):
         for i, s in enumerate(steps):
             for L in layers:
-                L.step(s, ev_dom[i] if (timed and L is dom) else None, rec)
+                L.step(s, ev_dom[i] if (timed and L is dom and not args.no_step_events) else None, rec)
 
     torch.cuda.synchronize()
     if True:
@@ -339,6 +341,9 @@ def main():
 
     total_ms = hev.elapsed_ms(ev_begin, ev_end)
     ms_per_step = total_ms / K
+    if args.no_step_events:
+        log(f"timed {K} steps without per-step events: {total_ms:.3f} ms; {ms_per_step * 1e3:.2f} us/step")
+        return 0
     dom_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in ev_dom])
     value = wl.batch * K / (total_ms / 1e3)
     log(f"timed {K} steps: {total_ms:.3f} ms on the GPU clock ({host_ms:.3f} ms host incl. spin); "

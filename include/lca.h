@@ -127,7 +127,8 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
  * lca_csa_topk_attn leaves it zero again.
  * Everything else in it is rewritten by each call. A workspace may be shared
  * by caches of the same or smaller shape; calls sharing one workspace must
- * not overlap in time. */
+ * not overlap in time. HCA layers need none (0 bytes): lca_csa_sparse_attn
+ * and lca_hca_dense_attn accept ws_dev = NULL. */
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx);
 lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
 

@@ -18,11 +18,11 @@
 // S_rope) and folded into P for the nope output dims (O_nope = (P*scale).C),
 // so no dequantised copy is rounded. The rotated query is rounded to bf16.
 //
-// Grid: (splits, queries). A workgroup (4 waves, 16 heads each) walks its
-// share of the key list 64 keys at a time: gathers the entries into LDS
-// (key-major for Q.K^T, dim-major for P.V), keeps a running max / sum per
-// head (online softmax), and either writes the normalised output (one
-// split) or its partial (max, sum, O) for merge_kernel.
+// This kernel serves calls with many queries (chunked prefill); calls with
+// fewer than 512 go to attend.hip. Grid: one workgroup per query (4 waves,
+// 16 heads each) walks the key list 64 keys at a time: gathers the entries
+// into LDS (key-major for Q.K^T, dim-major for P.V), keeps a running max /
+// sum per head (online softmax) and writes the normalised output.
 #include "dev_formats.h"
 #include "kernels.h"
 
@@ -60,15 +60,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, col = lane & 15;
-  const int q = blockIdx.y, split = blockIdx.x;
+  const int q = blockIdx.x;
   const int b = q / a.Tq, tq = q % a.Tq;
   const int64_t t = a.len - a.Tq + tq;
   const int64_t N = (t + 1) / a.m;
   const int64_t n_first = a.dense ? N : (int64_t)a.k;  // key slots before the window
   const int64_t total = n_first + a.W;
-  const int64_t s_begin = (int64_t)split * a.keys_per_split;
-  int64_t s_end = s_begin + a.keys_per_split;
-  if (s_end > total) s_end = total;
+  const int64_t s_begin = 0, s_end = total;
 
   // ---- rotated query, as A operands: row = head (wave*16 + col), K-group kg, 4 K-steps of 32 dims
   const int head = wave * 16 + col;
@@ -256,62 +254,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int h = wave * 16 + 4 * kg + i;
     if (h >= a.H) continue;
-    if (a.splits == 1) {
-      const float inv = 1.0f / l_run[i];
-      uint16_t* o = a.out + (((size_t)b * a.Tq + tq) * a.H + h) * kHeadDim;
+    const float inv = 1.0f / l_run[i];
+    uint16_t* o = a.out + (((size_t)b * a.Tq + tq) * a.H + h) * kHeadDim;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) o[nt * 16 + col] = f32_to_bf16(O[nt][i] * inv);
-      if (a.lse && col == 0) a.lse[((size_t)b * a.Tq + tq) * a.H + h] = m_run[i] + __logf(l_run[i]);
-    } else {
-      float* pp = a.part + (((size_t)q * a.splits + split) * a.H + h) * kPartStride;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) pp[nt * 16 + col] = O[nt][i];
-      if (col == 0) {
-        pp[kHeadDim] = m_run[i];
-        pp[kHeadDim + 1] = l_run[i];
-      }
-    }
+    for (int nt = 0; nt < 8; ++nt) o[nt * 16 + col] = f32_to_bf16(O[nt][i] * inv);
+    if (a.lse && col == 0) a.lse[((size_t)b * a.Tq + tq) * a.H + h] = m_run[i] + __logf(l_run[i]);
   }
-}
-
-// Joint softmax across splits: M = max m_s, L = sum l_s e^(m_s - M),
-// out = sum O_s e^(m_s - M) / L, lse = M + log L.
-__global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
-  __shared__ float ms[kMaxSplits], ls[kMaxSplits];
-  const int q = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  const float* base = a.part + ((size_t)q * a.splits * a.H + h) * kPartStride;
-  const size_t sstride = (size_t)a.H * kPartStride;
-  for (int s = d; s < a.splits; s += 128) {
-    ms[s] = base[s * sstride + kHeadDim];
-    ls[s] = base[s * sstride + kHeadDim + 1];
-  }
-  // all of this thread's partial outputs in flight at once
-  float o[kMaxSplits];
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) o[s] = s < a.splits ? base[s * sstride + d] : 0.0f;
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ms[s]);
-  float L = 0.0f, acc = 0.0f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < a.splits && ms[s] != -INFINITY) {
-      const float f = __expf(ms[s] - M);
-      L += ls[s] * f;
-      acc += o[s] * f;
-    }
-  }
-  const int b = q / a.Tq, tq = q % a.Tq;
-  a.out[(((size_t)b * a.Tq + tq) * a.H + h) * kHeadDim + d] = f32_to_bf16(acc / L);
-  if (a.lse && d == 0) a.lse[((size_t)b * a.Tq + tq) * a.H + h] = M + __logf(L);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s) {
   const unsigned nq = (unsigned)(B * a.Tq);
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)a.splits, nq), dim3(256), 0, s, a);
-  if (a.splits > 1) hipLaunchKernelGGL(merge_kernel, dim3(nq, (unsigned)a.H), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(attn_kernel, dim3(nq), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -64,11 +64,11 @@ bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
   return true;
 }
 
-// Workspace: the attention split-K partials first (fixed size), then, for CSA, one block per query
-// (histogram, scan segment counts, score keys, candidates). Nothing's place depends on a call's Tq,
-// so the per-query histograms that must be zero between calls stay put.
+// Workspace (CSA only): one block per query (histogram, scan segment counts, score keys,
+// candidates). Nothing's place depends on a call's Tq, so the per-query histograms that must be
+// zero between calls stay put.
 struct WsLayout {
-  size_t part, qbase, qstride, off_seg, off_keys, off_cand, total;
+  size_t qbase, qstride, off_seg, off_keys, off_cand, total;
   int32_t G2;
 };
 
@@ -76,10 +76,7 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   WsLayout W{};
   const int64_t max_blocks = max_ctx / d->m;
   const size_t nq = (size_t)B * (size_t)max_tq;
-  // split-K partials: splits are used only while B*Tq < kAttnTargetWGs, and then
-  // B*Tq*splits < 2*kAttnTargetWGs (see attn_splits)
-  W.part = 0;
-  size_t off = align_up((size_t)2 * kAttnTargetWGs * d->n_heads * kPartStride * 4);
+  size_t off = 0;
   W.qbase = off;
   W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
@@ -92,20 +89,6 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   }
   W.total = off;
   return W;
-}
-
-void attn_splits(int64_t n_keys, int32_t nq, int32_t* splits, int32_t* per_split) {
-  int64_t max_chunks = (n_keys + kAttnKeys - 1) / kAttnKeys;
-  int64_t s = 1;
-  if (nq < kAttnTargetWGs) s = (kAttnTargetWGs + nq - 1) / nq;
-  if (s > max_chunks) s = max_chunks;
-  if (s > kMaxSplits) s = kMaxSplits;
-  if (s < 1) s = 1;
-  int64_t per = (n_keys + s - 1) / s;
-  per = (per + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
-  s = (n_keys + per - 1) / per;
-  *splits = (int32_t)s;
-  *per_split = (int32_t)per;
 }
 
 lca_status launch_status(hipError_t e) { return e == hipSuccess ? LCA_OK : LCA_ERR_LAUNCH; }
@@ -374,9 +357,8 @@ lca_status attn_args(lca_cache* cache, bool dense, const uint16_t* q_dev, const 
   return LCA_OK;
 }
 
-// Few queries: one launch, a workgroup per (query, 16 heads) over all keys. Many queries: one
-// workgroup per query and all heads, split over the keys only while there are too few queries
-// to fill the chip (then merged).
+// Few queries: a workgroup per (query, 16 heads) over all keys (attend.hip). Many queries: a
+// workgroup per query and all heads (attention.hip).
 lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev,
                           int32_t Tq, uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes,
                           void* stream) {
@@ -385,20 +367,13 @@ lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, c
   lca_status st = attn_args(cache, dense, q_dev, topk_dev, Tq, out_dev, lse_dev, &a);
   if (st != LCA_OK) return st;
   const int32_t nq = cache->batch * Tq;
-  if (nq < kAttnTargetWGs) {
+  hipStream_t s = (hipStream_t)stream;
+  if (nq <= kAttendMaxQueries) {
     AttendArgs args{};
     args.t = a;
-    return launch_status(launch_attend(args, cache->batch, dense ? kAttendDense : kAttendList, (hipStream_t)stream));
+    return launch_status(launch_attend(args, cache->batch, dense ? kAttendDense : kAttendList, s));
   }
-  const int64_t n_first = dense ? cache->len / cache->desc.m : (int64_t)cache->desc.topk;
-  attn_splits(n_first + cache->desc.window, nq, &a.splits, &a.keys_per_split);
-  if (a.splits > 1) {
-    if (!ws_dev) return LCA_ERR_WORKSPACE;
-    WsLayout W = ws_layout(&cache->desc, cache->batch, Tq, cache->max_ctx);
-    if (ws_bytes < W.total) return LCA_ERR_WORKSPACE;
-    a.part = (float*)((char*)ws_dev + W.part);
-  }
-  return launch_status(launch_attention(a, cache->batch, (hipStream_t)stream));
+  return launch_status(launch_attention(a, cache->batch, s));
 }
 
 lca_status topk_attn_impl(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, bool score,

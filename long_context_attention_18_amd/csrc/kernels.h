@@ -20,10 +20,8 @@ constexpr int kScanPerWG = 8192;                      // keys per candidate-scan
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
 
 // ---- attention tiling ----------------------------------------------------
-constexpr int kAttnKeys = 64;                         // keys staged per iteration
-constexpr int kAttnTargetWGs = 512;                   // split-K target for small query counts
-constexpr int kPartStride = kHeadDim + 2;             // O[128], m, l per (query, split, head)
-constexpr int kMaxSplits = 32;                        // split-K limit (the merge holds one value per split)
+constexpr int kAttnKeys = 64;                         // keys staged per iteration (many-query kernel)
+constexpr int kAttendMaxQueries = 511;                // up to this many queries per call: attend.hip
 
 struct IngestArgs {
   const uint16_t* kv;      // [B][T][128]
@@ -90,7 +88,6 @@ struct AttnArgs {
   const uint16_t* win_rope;
   uint16_t* out;           // [B][Tq][H][128]
   float* lse;              // [B][Tq][H] or null
-  float* part;             // ws [B*Tq][S][H][kPartStride]
   int64_t len;
   int64_t max_blocks;
   int32_t Tq;
@@ -99,8 +96,6 @@ struct AttnArgs {
   int32_t m;
   int32_t W;
   int32_t ring;
-  int32_t splits;          // S
-  int32_t keys_per_split;  // multiple of kAttnKeys
   int32_t dense;           // 1 = HCA (every visible block), 0 = CSA (topk list)
   double inv_freq[32];
 };
