@@ -21,8 +21,15 @@ workload (sequence 0, the first few timed decode queries) and doubles as a
 full-size parity check of those queries (top-k exact, attention within
 tolerance).
 
+With --workload csa_prefill_128k it times the chunked prefill instead: one
+pass of 131072 tokens in chunks of 8192 (compress, append, indexer scores and
+top-k of the chunk's 8192 queries, sparse attention), after an untimed pass
+of two chunks; `value` is prefill tokens/s and `roofline` the score kernel's
+MXFP4 FLOPs against the MFMA peak.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload csa_decode_1m|hca_decode_64k|stack8_decode_256k|csa_decode_small]
+                       [--workload csa_decode_1m|hca_decode_64k|stack8_decode_256k|csa_decode_small|
+                                   csa_prefill_128k]
 """
 from __future__ import annotations
 
@@ -39,7 +46,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode query-tok/s + HBM GB/s (% of peak), CSA/HCA layer at 1M ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-WORKLOAD_BY_NAME = {"csa_decode_small": 0, "hca_decode_64k": 1, "csa_decode_1m": 2, "stack8_decode_256k": 4}
+WORKLOAD_BY_NAME = {"csa_decode_small": 0, "hca_decode_64k": 1, "csa_decode_1m": 2, "csa_prefill_128k": 3,
+                    "stack8_decode_256k": 4}
+PREFILL_METRIC = "chunked-prefill tok/s (CSA layer, 131072 tokens, chunk 8192), 1 GPU"
+MXFP4_PEAK_TFLOPS = 10100.0
 
 
 def parse_args():
@@ -273,6 +283,136 @@ def oracle_sample(layers, wl, first_step, n_queries, threads):
     return results, dec_s, build_s, nb
 
 
+def prefill_bench(args, wl):
+    """Chunked prefill of one CSA layer: the whole pass timed, per-chunk events around the score kernel."""
+    import numpy as np
+    import torch
+    import long_context_attention_18_amd as lca
+    from long_context_attention_18_amd import configs, synth
+    layer = wl.layers[0]
+    C = wl.prefill_chunk
+    total = configs.PREFILL_TOKENS[wl.wid]
+    n_chunks = total // C
+    H, HI, k = layer.n_heads, layer.idx_heads, layer.topk
+    desc = lca.make_desc(layer.kind, layer.m, H, layer.window, HI, k)
+    dev = lca.DeviceLayer(desc, 1, total + layer.m, C + layer.window - 1, max_tq=C)
+    stream_in = synth.TokenStream(wl.wid, 0, 0, True, wl.sigma)
+    bias = synth.biases(wl.wid, 0, layer.m, True)
+    bias_dev = {key: torch.from_numpy(v).cuda() for key, v in bias.items()}
+
+    def up(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t0 = time.perf_counter()
+
+    def make(c):
+        tok = stream_in.tokens(c * C, C)
+        qin = synth.direct_queries(wl.wid, 0, 0, c * C, C, H, HI, wl.sigma)
+        return tok, qin
+
+    with cf.ThreadPoolExecutor(min(args.threads, n_chunks)) as ex:
+        host = list(ex.map(make, range(n_chunks)))
+    inputs = [({key: up(v[None]) for key, v in tok.items()}, {key: up(v[None]) for key, v in qin.items()})
+              for tok, qin in host]
+    topk = [torch.empty((1, C, k), dtype=torch.int32, device="cuda") for _ in range(2)]
+    out = [torch.empty((1, C, H, 128), dtype=torch.int16, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    log(f"inputs of {total} tokens on the device in {time.perf_counter() - t0:.1f} s")
+    hev = HipEvents()
+    rec = lambda e: hev.record(e, False)
+    ev = [(hev.create(), hev.create()) for _ in range(n_chunks)]
+    ev_begin, ev_end = hev.create(), hev.create()
+    last = n_chunks - 1
+
+    def chunk(c, timed):
+        tok, qin = inputs[c]
+        slot = 0 if c == 0 else (1 if c == last else None)
+        tk = topk[slot] if slot is not None else topk[1]
+        o = out[slot] if slot is not None else out[1]
+        dev.compress(tok["kv"], tok["gate"], bias_dev["bias"], tok["ik"], tok["ig"], bias_dev["idx_bias"])
+        dev.append(tok["kv"], tok["gate"], tok["ik"], tok["ig"])
+        if timed:
+            rec(ev[c][0])
+        dev.index_score(qin["qI"], qin["w"])
+        if timed:
+            rec(ev[c][1])
+        dev.topk_select(C, tk)
+        dev.sparse_attn(qin["q"], tk, o)
+
+    for c in range(2):
+        chunk(c, False)
+    torch.cuda.synchronize()
+    dev.reset()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e7))
+    rec(ev_begin)
+    for c in range(n_chunks):
+        chunk(c, True)
+    rec(ev_end)
+    torch.cuda.synchronize()
+    total_ms = hev.elapsed_ms(ev_begin, ev_end)
+    sc_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in ev])
+    # MXFP4 MACs of the score kernel: every visible block of every query, H_I heads x 64 dims
+    flops = []
+    for c in range(n_chunks):
+        t = np.arange(c * C, (c + 1) * C)
+        n = (t + 1) // layer.m
+        flops.append(float(np.sum(np.where(n > k, n, 0))) * HI * 64 * 2)  # no scores while N <= k
+    sel = [c for c in range(n_chunks) if flops[c] > 0]
+    achieved = float(np.sum([flops[c] for c in sel]) / np.sum([sc_us[c] * 1e-6 for c in sel]) / 1e12)
+    log(f"timed prefill of {total} tokens: {total_ms:.2f} ms; score kernel {sc_us[sel].mean():.1f} us avg per "
+        f"chunk ({achieved:.1f} TFLOP/s MXFP4)")
+    result = {
+        "metric": PREFILL_METRIC, "value": round(total / (total_ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": n_chunks, "warmup": 2, "ms_per_step": round(total_ms / n_chunks, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4+bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": total, "chunk": C, "n_heads": H, "window": layer.window,
+                   "topk": k, "idx_heads": HI},
+        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(achieved, 2),
+                     "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 5),
+                     "traffic": None, "avg_launch_us": round(float(sc_us[sel].mean()), 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        log("oracle sample ...")
+        tok_all = stream_in.tokens(0, total)
+        d1 = O.compress(layer.m, tok_all["kv"], tok_all["gate"], tok_all["ik"], tok_all["ig"], 0, bias["bias"],
+                        bias["idx_bias"], 0, total // layer.m)
+        win = O.window_entries(tok_all["kv"], 0)
+        parity = {"queries": 0, "topk_exact": True, "max_rel_l2": 0.0, "max_abs": 0.0}
+        t_or = 0.0
+        for c, slot in ((0, 0), (last, 1)):
+            tk_h = topk[slot][0].cpu().numpy()
+            o_h = out[slot][0].cpu().numpy().view(np.uint16)
+            _, qin = host[c]
+            for i in (C // 2, C - 1):
+                t = c * C + i
+                s0 = time.perf_counter()
+                r = O.layer_query("csa", layer.m, k, layer.window, t, qin["q"][i], qin["qI"][i], qin["w"][i], d1,
+                                  d1, win)
+                t_or += time.perf_counter() - s0
+                g = synth.bf16_to_f32(o_h[i]).astype(np.float64)
+                ref = r["out_f64"]
+                parity["queries"] += 1
+                parity["topk_exact"] &= bool(np.array_equal(tk_h[i], r["topk"]))
+                parity["max_rel_l2"] = max(parity["max_rel_l2"], float(np.linalg.norm(g - ref) / np.linalg.norm(ref)))
+                parity["max_abs"] = max(parity["max_abs"], float(np.abs(g - ref).max()))
+        parity["ok"] = parity["topk_exact"] and parity["max_rel_l2"] <= 1e-2 and parity["max_abs"] <= 2e-2
+        result["cpu_baseline"] = {
+            "value": round(parity["queries"] / t_or, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{parity['queries']} prefill queries (positions {C // 2}, {C - 1}, {last * C + C // 2}, "
+                      f"{total - 1}) through the plain C oracle (scores, top-k, attention), single thread, "
+                      f"{t_or:.2f} s; its cache build is not counted"}
+        result["parity_sample"] = parity
+        log(f"oracle: {t_or:.2f} s; parity {parity}")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -288,6 +428,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     wl = configs.WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
+    if wl.prefill_chunk:
+        log(f"workload {wl.name}: {wl.note}")
+        return prefill_bench(args, wl)
     K, W = args.steps, args.warmup
     S = W + K
     log(f"workload {wl.name}: {wl.note}; warmup {W}, steps {K}")

@@ -185,7 +185,7 @@ lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const u
  * min(k, visible) blocks with the largest (score, -j), in ascending j,
  * padded with -1.
  *   qI_dev: [B][Tq][idx_heads][64] bf16; w_dev: [B][Tq][idx_heads] f32;
- *   topk_dev: [B][Tq][k] int32. */
+ *   topk_dev: [B][Tq][k] int32. B * Tq <= 65535 (else LCA_ERR_SHAPE). */
 lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, int32_t Tq,
                                 int32_t* topk_dev, void* ws_dev, size_t ws_bytes, void* stream);
 

@@ -218,6 +218,12 @@ class DeviceLayer:
         self.ws = (self.ws_mem.data_ptr() + 255) // 256 * 256
         lca_workspace_init(self.ws, self.ws_bytes, stream)
 
+    def reset(self, stream=None):
+        """Empty the cache (rebind: zeroed, len = 0) and re-zero the workspace."""
+        base = (self.mem.data_ptr() + 255) // 256 * 256
+        lca_cache_bind(self.desc, self.cache, base, self.cache_bytes, self.batch, self.max_ctx, self.ring, stream)
+        lca_workspace_init(self.ws, self.ws_bytes, stream)
+
     @property
     def len(self):
         return self.cache.len

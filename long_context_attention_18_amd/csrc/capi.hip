@@ -264,6 +264,7 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   if (need_topk && !topk_dev) return LCA_ERR_NULL;
   if (cache->desc.kind != LCA_KIND_CSA || !cache->idx_codes_dev) return LCA_ERR_UNSUPPORTED;
   if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
+  if ((int64_t)cache->batch * Tq > kMaxGridY) return LCA_ERR_SHAPE;  // queries index grid.y
   if (cache->pending != 0) return LCA_ERR_ORDER;
   if (!ws_dev) return LCA_ERR_WORKSPACE;
   WsLayout W = ws_layout(&cache->desc, cache->batch, Tq, cache->max_ctx);

@@ -22,6 +22,7 @@ constexpr int kCandCap = 8192;                        // candidates the select k
 // ---- attention tiling ----------------------------------------------------
 constexpr int kAttnKeys = 64;                         // keys staged per iteration (many-query kernel)
 constexpr int kAttendMaxQueries = 511;                // up to this many queries per call: attend.hip
+constexpr int64_t kMaxGridY = 65535;                  // launch limit of grid.y (indexer grids: one row per query)
 
 struct IngestArgs {
   const uint16_t* kv;      // [B][T][128]
