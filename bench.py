@@ -196,18 +196,15 @@ class Layer:
         t = {k: v[s] for k, v in self.step_tok.items()}
         q = {k: v[s] for k, v in self.step_q.items()}
         out = self.kept[s]["out"] if s in self.kept else self.out
-        self.dev.compress(t["kv"], t["gate"], self.bias_dev["bias"], t.get("ik"), t.get("ig"),
-                          self.bias_dev.get("idx_bias"))
-        self.dev.append(t["kv"], t["gate"], t.get("ik"), t.get("ig"))
         if self.csa:
+            # the whole CSA step in one call; it records the events around its score launch
             topk = self.kept[s]["topk"] if s in self.kept else self.topk
-            if ev_score is not None:
-                rec(ev_score[0])
-            self.dev.index_score(q["qI"], q["w"])
-            if ev_score is not None:
-                rec(ev_score[1])
-            self.dev.topk_attn(q["q"], out, None, topk)
+            self.dev.step(t["kv"], t["gate"], t["ik"], t["ig"], self.bias_dev["bias"], self.bias_dev["idx_bias"],
+                          q["qI"], q["w"], q["q"], out, None, topk,
+                          score_events=(ev_score if ev_score is not None else (None, None)))
         else:
+            self.dev.compress(t["kv"], t["gate"], self.bias_dev["bias"])
+            self.dev.append(t["kv"], t["gate"])
             if ev_score is not None:
                 rec(ev_score[0])
             self.dev.dense_attn(q["q"], out)

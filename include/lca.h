@@ -193,7 +193,8 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
  * arguments; the scores travel in the workspace, so both calls must get the
  * same cache state, Tq and workspace, in this order, with nothing else using
  * the workspace in between; an lca_csa_index_score without its
- * lca_csa_topk_select leaves the workspace histograms dirty):
+ * lca_csa_topk_select leaves the workspace histograms counting it: the next
+ * selection is then slower, still exact, and clears them):
  *  lca_csa_index_score: the lightning-indexer scores of every visible block
  *    of the Tq queries (an HBM stream over the FP4 keys);
  *  lca_csa_topk_select: the per-query top-k of those scores into topk_dev. */
@@ -237,6 +238,24 @@ lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float*
                           size_t ws_bytes, void* stream);
 lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev,
                              uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* One decode step of a CSA layer in one call: the T new tokens of every
+ * sequence go in (lca_csa_compress + lca_swa_tail_append: the blocks they
+ * complete are pooled into D1/D3, their window entries and tail copies are
+ * written) and their T queries attend (lca_csa_attend): same results, bit for
+ * bit in the cache and the top-k lists. Three launches (four when a block
+ * completes): compress, score, candidate scan with the append in the same
+ * launch, selection + attention. For decode-sized calls: B * T <= 511
+ * (else LCA_ERR_SHAPE); ring >= T + window - 1. Inputs as for the compressor
+ * and lca_csa_attend; topk_dev and lse_dev may be NULL. score_ev_begin /
+ * score_ev_end, when not NULL, are hipEvent_t the call records on `stream`
+ * around the indexer score kernel (for timing it). Checks everything before
+ * launching: a rejected call leaves the cache unchanged. */
+lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
+                        const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
+                        const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
+                        void* score_ev_begin, void* score_ev_end);
 
 /* Human-readable name of a status code (static storage). */
 const char* lca_status_str(lca_status status);

@@ -70,6 +70,8 @@ _SIGNATURES = {
     "lca_hca_dense_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_attend": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
+                            _VP, _VP]),
     "lca_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -81,6 +83,9 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                                "(or python -m long_context_attention_18_amd._build)")
+        # torch first: its libamdhip64 carries the soname liblca.so asks for, so both share one HIP runtime
+        # (and torch's streams and events are valid in the library)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             f = getattr(L, name)
@@ -189,6 +194,14 @@ def lca_csa_topk_attn(cache, q, Tq, topk, out, lse, ws, ws_bytes, stream=None):
                                                          _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def lca_csa_step(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, ws, ws_bytes, stream=None,
+                 score_events=(None, None)):
+    _check("lca_csa_step", lib().lca_csa_step(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(ik), _ptr(ig),
+                                               _ptr(bias), _ptr(idx_bias), T, _ptr(qI), _ptr(w), _ptr(q), _ptr(topk),
+                                               _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream),
+                                               score_events[0], score_events[1]))
+
+
 def lca_status_str(status):
     return lib().lca_status_str(status).decode()
 
@@ -262,6 +275,12 @@ class DeviceLayer:
 
     def topk_attn(self, q, out, lse=None, topk=None, stream=None):
         lca_csa_topk_attn(self.cache, q, q.shape[1], topk, out, lse, self.ws, self.ws_bytes, stream)
+
+    def step(self, kv, gate, ik, ig, bias, idx_bias, qI, w, q, out, lse=None, topk=None, stream=None,
+             score_events=(None, None)):
+        """One decode step (CSA): T = kv.shape[1] tokens in, their queries attend."""
+        lca_csa_step(self.cache, kv, gate, ik, ig, bias, idx_bias, kv.shape[1], qI, w, q, topk, out, lse, self.ws,
+                     self.ws_bytes, stream, score_events)
 
     def index_scores(self, Tq):
         """fp32 scores the last index_score / indexer_topk call left in the workspace: [B][Tq][max_blocks]."""

@@ -125,6 +125,7 @@ struct Keys {
   const int32_t* list;
   size_t win_row, blk_row;  // b * ring, b * max_blocks
   uint32_t win_base;        // ring slot of the first window position
+  int64_t j_max;            // last visible block (0 when none)
   int n_win, n_list;
   bool use_list;
   // Entry of key slot `slot` (< n_win + n_list): window position t - n_win + 1 + slot, or the
@@ -133,7 +134,8 @@ struct Keys {
   __device__ __forceinline__ size_t entry(int slot, bool* in_win) const {
     *in_win = slot < n_win;
     const int li = *in_win ? 0 : slot - n_win;
-    const int64_t j = use_list ? (int64_t)list[li] : (int64_t)li;
+    int64_t j = use_list ? (int64_t)list[li] : (int64_t)li;
+    j = j < 0 ? 0 : (j > j_max ? j_max : j);  // list entries are valid by construction; never read outside
     uint32_t ws = win_base + (uint32_t)slot;
     ws = ws >= ring ? ws - ring : ws;
     return *in_win ? win_row + ws : blk_row + (size_t)j;
@@ -279,6 +281,7 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   K.blk_row = (size_t)b * a.max_blocks;
   K.n_win = (int)((int64_t)a.W < t + 1 ? (int64_t)a.W : t + 1);
   K.win_base = (uint32_t)((t - K.n_win + 1) % a.ring);
+  K.j_max = N > 0 ? N - 1 : 0;
   if (MODE == kAttendDense) {
     K.n_list = (int)N;
     K.use_list = false;
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
     const ScoreArgs& sa = args.s;
     if (hg == 0)  // every scan workgroup has read this query's histogram: clear it for the next call
       for (int i = tid; i < kHistBins; i += 512) q_hist(sa, q)[i] = 0u;
-    select_query(sa, q, N, S.u.sel, S.list);
+    K.n_list = (int)select_query(sa, q, N, S.u.sel, S.list);
   }
   __syncthreads();
   if (do_select && hg == 0 && args.s.topk) {

@@ -415,6 +415,55 @@ lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq
                         stream);
 }
 
+lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
+                        const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
+                        const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
+                        void* score_ev_begin, void* score_ev_end) {
+  // every check first, so a rejected call leaves the cache as it was
+  if (!cache_ok(cache) || !kv_dev || !gate_dev || !ik_dev || !ig_dev || !bias_dev || !idx_bias_dev)
+    return LCA_ERR_NULL;
+  if (cache->desc.kind != LCA_KIND_CSA || !cache->idx_codes_dev) return LCA_ERR_UNSUPPORTED;
+  if (T < 1 || (int64_t)cache->batch * T > kAttendMaxQueries) return LCA_ERR_SHAPE;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
+  lca_cache after = *cache;  // the cache once the T tokens are in: what the query kernels see
+  after.len = cache->len + T;
+  AttendArgs args{};
+  lca_status st = score_args(&after, qI_dev, w_dev, true, T, topk_dev, false, ws_dev, ws_bytes, &args.s);
+  if (st != LCA_OK) return st;
+  st = attn_args(&after, false, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
+  if (st != LCA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t m = cache->desc.m;
+  // compress the blocks the T tokens complete (their keys are scored below)
+  const int64_t n_blocks = (cache->len + T) / m - cache->len / m;
+  if (n_blocks > 0) {
+    IngestArgs ca = ingest_args(cache, kv_dev, gate_dev, ik_dev, ig_dev, T);
+    ca.bias = bias_dev;
+    ca.idx_bias = idx_bias_dev;
+    ca.first = cache->len / m;
+    if (launch_compress(ca, true, n_blocks, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  }
+  if (score_ev_begin && hipEventRecord((hipEvent_t)score_ev_begin, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (score_ev_end && hipEventRecord((hipEvent_t)score_ev_end, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  // the append (window entries, tail) rides in the candidate-scan launch
+  IngestArgs app = ingest_args(cache, kv_dev, gate_dev, ik_dev, ig_dev, T);
+  const int64_t end = cache->len + T;
+  const int64_t win_first = (end - cache->ring > cache->len) ? end - cache->ring : cache->len;
+  app.first = win_first;
+  app.n_win = (int32_t)(end - win_first);
+  int64_t tail_first = (end / m) * m;
+  if (tail_first < cache->len) tail_first = cache->len;
+  const int32_t units = app.n_win + (int32_t)(end - tail_first);
+  if (launch_topk_select(args.s, cache->batch, s, false, &app, units) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (launch_attend(args, cache->batch, kAttendSelect, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  cache->len = end;
+  cache->pending = 0;
+  return LCA_OK;
+}
+
 lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev,
                           int32_t Tq, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev, void* ws_dev,
                           size_t ws_bytes, void* stream) {

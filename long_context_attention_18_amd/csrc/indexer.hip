@@ -48,6 +48,7 @@
 // ~j) and writes the winners by an order-preserving compaction, so the
 // output is ascending without a sort. Exact for any input.
 #include "dev_formats.h"
+#include "ingest.h"
 #include "kernels.h"
 #include "select.h"
 
@@ -335,7 +336,20 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // Candidate scan: every key >= L (the bound the query's global histogram gives) is written, in index
 // order, to this workgroup's segment of the candidate row; the segment's count goes to seg. A query with
 // at most k visible blocks gets its whole list (and its histogram cleared) here.
-__global__ __launch_bounds__(512) void scan_kernel(ScoreArgs a) {
+// APPEND: the launch has one more row of workgroups (blockIdx.y == B*Tq) that writes a decode step's
+// window entries and tail copies (the append), one workgroup per sequence, one unit per wave. The
+// score kernel before it reads neither the window ring nor the tail, and the attention after it
+// needs the new window entries: this launch is a free slot for that work.
+template <bool APPEND>
+__global__ __launch_bounds__(512) void scan_kernel(ScanArgs args) {
+  const ScoreArgs& a = args.a;
+  if (APPEND && (int)blockIdx.y == (int)gridDim.y - 1) {
+    const int b = blockIdx.x;
+    if (b < args.app.B)
+      for (int unit = (int)(threadIdx.x >> 6); unit < args.app_units; unit += 8)
+        append_unit<true>(args.app, b, unit, threadIdx.x & 63);
+    return;
+  }
   constexpr int kPer = kScanPerWG / 512;  // keys per thread: j = start + u*512 + tid
   __shared__ uint32_t wsum[8];
   __shared__ uint32_t L_s;
@@ -440,7 +454,9 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   const int64_t N = visible_blocks(a, q % a.Tq);
   if (N <= a.k) return;
   for (int i = threadIdx.x; i < kHistBins; i += 512) q_hist(a, q)[i] = 0u;
-  select_query(a, q, N, S, a.topk + (size_t)q * a.k);
+  int32_t* out = a.topk + (size_t)q * a.k;
+  const uint32_t n = select_query(a, q, N, S, out);
+  for (int i = (int)n + (int)threadIdx.x; i < a.k; i += 512) out[i] = -1;  // only if fewer than k were found
 }
 
 }  // namespace
@@ -454,12 +470,22 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool with_select) {
+hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool with_select,
+                              const IngestArgs* app, int32_t app_units) {
   const int64_t N_last = a.len / a.m;
   const unsigned nq = (unsigned)(B * a.Tq);
   unsigned g2 = (unsigned)((N_last + kScanPerWG - 1) / kScanPerWG);
   if (g2 < 1) g2 = 1;
-  hipLaunchKernelGGL(scan_kernel, dim3(g2, nq), dim3(512), 0, s, a);
+  ScanArgs args{};
+  args.a = a;
+  if (app && app_units > 0) {
+    args.app = *app;
+    args.app_units = app_units;
+    const unsigned gx = g2 > (unsigned)B ? g2 : (unsigned)B;
+    hipLaunchKernelGGL(scan_kernel<true>, dim3(gx, nq + 1), dim3(512), 0, s, args);
+  } else {
+    hipLaunchKernelGGL(scan_kernel<false>, dim3(g2, nq), dim3(512), 0, s, args);
+  }
   if (with_select) hipLaunchKernelGGL(select_kernel, dim3(nq), dim3(512), 0, s, a);
   return hipGetLastError();
 }

@@ -1,0 +1,93 @@
+// ingest.h -- per-token window entries and tail copies (the append step), shared by the append
+// kernel and the candidate scan, which does a decode step's append in the same launch.
+//
+// Figure 3's sliding-window branch of "DeepSeek-V4: a million-token context that agents can
+// actually use" and the KV-cache section of velog.io "DeepSeek V4 논문 정리" (separate window
+// state, separately managed uncompressed tail).
+#pragma once
+#include "dev_formats.h"
+#include "kernels.h"
+
+namespace lca {
+
+constexpr int kTailKv = 0, kTailGate = 128, kTailIk = 256, kTailIg = 320;
+
+// BF16 input row of token p (absolute position) of sequence b: from the tail
+// if the token was appended by an earlier call, else from this call's input.
+__device__ __forceinline__ const uint16_t* token_row(const IngestArgs& a, int b, int64_t p, const uint16_t* in,
+                                                     int width, int tail_off) {
+  if (p < a.len) return a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width + tail_off;
+  return in + ((size_t)b * a.T + (size_t)(p - a.len)) * width;
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double half_wave_max(double v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// RoPE-rotated value of channel 64+c of token p (pair (2i, 2i+1), i = c/2):
+//   even: x0 cos - x1 sin;  odd: x0 sin + x1 cos;  angle p * inv_freq[i]; fp64.
+__device__ __forceinline__ double rope_channel(const uint16_t* kv_row, int c, int64_t p, const double* inv_freq) {
+  int i = c >> 1;
+  double x0 = (double)bf16_to_f32(kv_row[kNope + 2 * i]);
+  double x1 = (double)bf16_to_f32(kv_row[kNope + 2 * i + 1]);
+  double phi = (double)p * inv_freq[i];
+  double sn, cs;
+  sincos(phi, &sn, &cs);
+  return (c & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
+}
+
+// Write one 196-byte entry from the lane's nope value xn (dim c) and RoPE
+// value xr (dim 64+c): scale = fp32(amax / 448), code = E4M3FN(x / scale).
+__device__ __forceinline__ void write_entry(double xn, double xr, int c, uint8_t* codes, float* scale,
+                                            uint16_t* rope) {
+  double amax = wave_max(fabs(xn));
+  float s = (float)(amax / 448.0);
+  bool zero = (amax == 0.0) || (s == 0.0f);
+  uint32_t code = zero ? 0u : fp8_e4m3_encode(xn / (double)s);
+  codes[c] = (uint8_t)code;
+  rope[c] = bf16_encode(xr);
+  if (c == 0) *scale = zero ? 0.0f : s;
+}
+
+// One unit of the append of sequence b, on the 64 lanes of a wave (lane c): unit < n_win writes the
+// window entry of token a.first + unit (its kv, RoPE'd at its position, its own FP8 scale) into ring
+// slot s mod R; the following units copy the BF16 inputs of the tokens of the block that is still
+// incomplete after this call into the tail.
+template <bool CSA>
+__device__ __forceinline__ void append_unit(const IngestArgs& a, int b, int unit, int c) {
+  if (unit < a.n_win) {
+    // window entry of token s: its own kv, RoPE'd at s, its own FP8 scale
+    const int64_t s = a.first + unit;
+    const uint16_t* kv = a.kv + ((size_t)b * a.T + (size_t)(s - a.len)) * kHeadDim;
+    double xn = (double)bf16_to_f32(kv[c]);
+    double xr = rope_channel(kv, c, s, a.inv_freq);
+    const size_t e = (size_t)b * a.ring + (size_t)(s % a.ring);
+    write_entry(xn, xr, c, a.win_codes + e * kNope, a.win_scale + e, a.win_rope + e * kRope);
+    return;
+  }
+  // tail: tokens of the block that is still incomplete after this call
+  const int64_t end = a.len + a.T;
+  int64_t tail_first = (end / a.m) * a.m;
+  if (tail_first < a.len) tail_first = a.len;
+  const int64_t p = tail_first + (unit - a.n_win);
+  const size_t r = (size_t)b * a.T + (size_t)(p - a.len);
+  uint16_t* dst = a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width;
+  dst[kTailKv + c] = a.kv[r * kHeadDim + c];
+  dst[kTailKv + 64 + c] = a.kv[r * kHeadDim + 64 + c];
+  dst[kTailGate + c] = a.gate[r * kHeadDim + c];
+  dst[kTailGate + 64 + c] = a.gate[r * kHeadDim + 64 + c];
+  if (CSA) {
+    dst[kTailIk + c] = a.ik[r * kIdxDim + c];
+    dst[kTailIg + c] = a.ig[r * kIdxDim + c];
+  }
+}
+
+}  // namespace lca

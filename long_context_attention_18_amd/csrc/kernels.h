@@ -115,7 +115,13 @@ hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipS
 hipError_t launch_append(const IngestArgs& a, bool csa, int32_t n_tail, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s);
-hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool with_select = true);
+struct ScanArgs {
+  ScoreArgs a;
+  IngestArgs app;     // a decode step's append, done by the scan launch (app_units > 0)
+  int32_t app_units;  // window entries + tail copies per sequence
+};
+hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool with_select = true,
+                              const IngestArgs* app = nullptr, int32_t app_units = 0);
 hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s);
 

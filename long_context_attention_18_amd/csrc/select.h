@@ -25,7 +25,10 @@ struct SelectLds {
   uint64_t red_lo[8], red_hi[8];
 };
 
-__device__ inline void select_query(const ScoreArgs& a, int q, int64_t N, SelectLds& S, int32_t* out) {
+// Returns the number of winners written (min(k, N) whenever N > k). The candidate lower bound is only
+// a hint: with fewer than k candidates (a histogram left dirty by a score call without its selection)
+// the selection takes the path over every visible block and stays exact.
+__device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, SelectLds& S, int32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t* cs = S.cs;
   uint32_t* seg_off = S.seg_off;
@@ -70,7 +73,7 @@ __device__ inline void select_query(const ScoreArgs& a, int q, int64_t N, Select
     __syncthreads();
   }
   const uint32_t total = seg_off[G2_q];
-  const bool fast = total <= (uint32_t)kCandCap;
+  const bool fast = total >= (uint32_t)a.k && total <= (uint32_t)kCandCap;
   const int64_t n = fast ? (int64_t)total : N;
   const uint32_t* keys = q_keys(a, q);
   if (fast) {
@@ -105,78 +108,83 @@ __device__ inline void select_query(const ScoreArgs& a, int q, int64_t N, Select
     return ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
   };
 
-  // radix select of the k-th largest 64-bit key (score key, then lower index first), 8 bits at a time
-  // from the highest bit in which the elements differ, stopping as soon as the bin that holds it is
-  // taken whole
-  {
-    uint64_t lo = ~0ull, hi = 0;
-    for (int64_t i = tid; i < n; i += 512) {
-      const uint64_t e = elem(i);
-      lo = e < lo ? e : lo;
-      hi = e > hi ? e : hi;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
-      lo = l2 < lo ? l2 : lo;
-      hi = h2 > hi ? h2 : hi;
-    }
-    if (lane == 0) {
-      red_lo[wave] = lo;
-      red_hi[wave] = hi;
-    }
-  }
-  __syncthreads();
-  uint64_t glo = red_lo[0], ghi = red_hi[0];
-  for (int w = 1; w < 8; ++w) {
-    glo = red_lo[w] < glo ? red_lo[w] : glo;
-    ghi = red_hi[w] > ghi ? red_hi[w] : ghi;
-  }
-  const uint64_t diff = glo ^ ghi;                 // nonzero: keys are unique and n > k >= 1
-  const int hb = 63 - __clzll((long long)diff);    // highest differing bit
-  const uint64_t common = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
-  uint64_t prefix = glo & common, mask = common;
-  uint32_t need = (uint32_t)a.k;  // N > k here
-  for (int shift = hb - 7; shift > -8; shift -= 8) {
-    const int sh = shift < 0 ? 0 : shift;           // the last digit may be narrower than 8 bits
-    const uint64_t dmask = shift < 0 ? ((1ull << (shift + 8)) - 1ull) : 255ull;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += 512) {
-      uint64_t e = elem(i);
-      if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane covers bins 255-4*lane .. 252-4*lane (descending)
-      uint32_t c4 = 0;
-      for (int i = 0; i < 4; ++i) c4 += hist[255 - 4 * lane - i];
-      uint32_t incl = c4;
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
+  // every element a winner (n == k): no selection
+  uint64_t prefix = 0, mask = 0;
+  if (n > (int64_t)a.k) {
+    // radix select of the k-th largest 64-bit key (score key, then lower index first), 8 bits at a time
+    // from the highest bit in which the elements differ, stopping as soon as the bin that holds it is
+    // taken whole
+    {
+      uint64_t lo = ~0ull, hi = 0;
+      for (int64_t i = tid; i < n; i += 512) {
+        const uint64_t e = elem(i);
+        lo = e < lo ? e : lo;
+        hi = e > hi ? e : hi;
       }
-      uint32_t excl = incl - c4;
-      if (excl < need && incl >= need) {
-        uint32_t c = excl;
-        for (int i = 0; i < 4; ++i) {
-          uint32_t d = 255 - 4 * lane - i;
-          if (c + hist[d] >= need) {
-            sel_digit = d;
-            sel_above = c;
-            sel_count = hist[d];
-            break;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+      }
+      if (lane == 0) {
+        red_lo[wave] = lo;
+        red_hi[wave] = hi;
+      }
+    }
+    __syncthreads();
+    uint64_t glo = red_lo[0], ghi = red_hi[0];
+    for (int w = 1; w < 8; ++w) {
+      glo = red_lo[w] < glo ? red_lo[w] : glo;
+      ghi = red_hi[w] > ghi ? red_hi[w] : ghi;
+    }
+    const uint64_t diff = glo ^ ghi;                 // nonzero: keys are unique and n > k >= 1
+    const int hb = 63 - __clzll((long long)diff);    // highest differing bit
+    const uint64_t common = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+    prefix = glo & common;
+    mask = common;
+    uint32_t need = (uint32_t)a.k;  // N > k here
+    for (int shift = hb - 7; shift > -8; shift -= 8) {
+      const int sh = shift < 0 ? 0 : shift;           // the last digit may be narrower than 8 bits
+      const uint64_t dmask = shift < 0 ? ((1ull << (shift + 8)) - 1ull) : 255ull;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int64_t i = tid; i < n; i += 512) {
+        uint64_t e = elem(i);
+        if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane covers bins 255-4*lane .. 252-4*lane (descending)
+        uint32_t c4 = 0;
+        for (int i = 0; i < 4; ++i) c4 += hist[255 - 4 * lane - i];
+        uint32_t incl = c4;
+        for (int o = 1; o < 64; o <<= 1) {
+          uint32_t t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        uint32_t excl = incl - c4;
+        if (excl < need && incl >= need) {
+          uint32_t c = excl;
+          for (int i = 0; i < 4; ++i) {
+            uint32_t d = 255 - 4 * lane - i;
+            if (c + hist[d] >= need) {
+              sel_digit = d;
+              sel_above = c;
+              sel_count = hist[d];
+              break;
+            }
+            c += hist[d];
           }
-          c += hist[d];
         }
       }
+      __syncthreads();
+      const uint32_t d = sel_digit;
+      need -= sel_above;
+      prefix |= (uint64_t)d << sh;
+      mask |= dmask << sh;
+      if (sel_count == need) break;
     }
-    __syncthreads();
-    const uint32_t d = sel_digit;
-    need -= sel_above;
-    prefix |= (uint64_t)d << sh;
-    mask |= dmask << sh;
-    if (sel_count == need) break;
   }
   // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run
   const int64_t per = (n + 511) / 512;
@@ -192,8 +200,11 @@ __device__ inline void select_query(const ScoreArgs& a, int q, int64_t N, Select
   }
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  uint32_t pos = incl - mine;
-  for (int w = 0; w < wave; ++w) pos += wsum[w];
+  uint32_t pos = incl - mine, n_win = 0;
+  for (int w = 0; w < 8; ++w) {
+    if (w < wave) pos += wsum[w];
+    n_win += wsum[w];
+  }
   for (int64_t i = i0; i < i1; ++i) {
     const uint64_t e = elem(i);
     if ((e & mask) >= prefix) {
@@ -201,6 +212,7 @@ __device__ inline void select_query(const ScoreArgs& a, int q, int64_t N, Select
       ++pos;
     }
   }
+  return n_win < (uint32_t)a.k ? n_win : (uint32_t)a.k;
 }
 
 }  // namespace lca

@@ -119,6 +119,24 @@ class LayerRun:
         torch.cuda.synchronize()
         return qin, (from_dev(topk) if topk is not None else None), from_dev(out, np.uint16), from_dev(lse)
 
+    def step(self, T=1):
+        """T new tokens per sequence and their queries through lca_csa_step (one call)."""
+        import torch
+        parts = [self.tokens(b, self.len, T) for b in range(self.B)]
+        tok = {k: to_dev(np.stack([p[k] for p in parts])) for k in parts[0]}
+        pos = list(range(self.len, self.len + T))
+        qin = self.queries(pos)
+        H = self.layer.n_heads
+        out = torch.empty((self.B, T, H, 128), dtype=torch.int16, device="cuda")
+        lse = torch.empty((self.B, T, H), dtype=torch.float32, device="cuda")
+        topk = torch.full((self.B, T, self.layer.topk), -7, dtype=torch.int32, device="cuda")
+        self.dev.step(tok["kv"], tok["gate"], tok["ik"], tok["ig"], self.bias_dev["bias"], self.bias_dev["idx_bias"],
+                      to_dev(qin["qI"]), to_dev(qin["w"]), to_dev(qin["q"]), out, lse, topk)
+        torch.cuda.synchronize()
+        self.len += T
+        self.last_scores = self.dev.index_scores(T) if self.len // self.m > self.layer.topk else None
+        return qin, from_dev(topk), from_dev(out, np.uint16), from_dev(lse)
+
     # ---------------------------------------------------------------- oracle side
     def oracle_caches(self, b, upto):
         tok = self.tokens(b, 0, upto)

@@ -100,6 +100,8 @@ def test_bad_arguments_are_rejected_before_any_launch():
     assert L.lca_hca_dense_attn(ctypes.byref(cache), 1, 1, 1, None, 1, 1, None) == -1
     assert L.lca_csa_attend(ctypes.byref(cache), 1, 1, 1, 1, None, 1, None, 1, 1, None) == -1
     assert L.lca_csa_topk_attn(ctypes.byref(cache), 1, 1, None, 1, None, 1, 1, None) == -1
+    assert L.lca_csa_step(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, 1, None, 1, 1, None, None,
+                          None) == -1
     assert L.lca_workspace_init(None, 256, None) == -1
 
 
@@ -134,6 +136,14 @@ def test_order_capacity_and_kind_checks():
     # queries beyond what was appended
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, P, 1 << 30, None) == -2
     c.len = 100
+    # one-call step: decode-sized only (B*T <= 511), rejected calls leave the cache as it was
+    c.len = 0
+    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 512, P, P, P, None, P, None, P, 1 << 30, None, None,
+                          None) == -2
+    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, None, 0, None, None,
+                          None) == -6
+    assert c.len == 0 and c.pending == 0
+    c.len = 100
     # workspace missing / too small
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, None, 0, None) == -6
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, P, 16, None) == -6
@@ -148,6 +158,8 @@ def test_order_capacity_and_kind_checks():
     h = _fake_bound_cache("hca")
     assert L.lca_csa_compress(ctypes.byref(h), P, P, P, P, P, P, 1, None) == -3
     assert L.lca_csa_attend(ctypes.byref(h), P, P, P, 1, None, P, None, P, 1 << 30, None) == -3
+    assert L.lca_csa_step(ctypes.byref(h), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, 1 << 30, None, None,
+                          None) == -3
 
 
 def test_workspace_bytes_grows_with_queries():

@@ -205,3 +205,74 @@ def test_fused_matches_separate_calls():
     ref = synth.bf16_to_f32(out_s.cpu().numpy().view(np.uint16)).astype(np.float64)
     rel, mab = attn_error(a, ref)
     assert rel < 4e-3 and mab < 1e-2, (rel, mab)
+
+
+def test_csa_step_one_call_decode():
+    """lca_csa_step (compress + append + indexer + top-k + attention in one call) for 9 decode steps across
+    block boundaries: against the oracle, and bit for bit against the separate calls on a twin cache
+    (cache bytes, top-k lists, outputs, LSE)."""
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=256)
+    a = LayerRun(layer, B=3, max_ctx=6000, ring=128)
+    b = LayerRun(layer, B=3, max_ctx=6000, ring=128)
+    for run in (a, b):
+        _ingest(run, [5001])
+    oc = [a.oracle_caches(i, 5010) for i in range(a.B)]
+    for _ in range(9):
+        qa, tka, oa, la = a.step(1)
+        b.ingest(1)
+        qb, tkb, ob, lb = b.run_queries(1, fused=True)
+        check_queries(a, oc, qa, tka, oa, la, [a.len - 1])
+        assert np.array_equal(tka, tkb)
+        assert np.array_equal(oa, ob)
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    va, vb = a.dev.views(), b.dev.views()
+    for k in va:
+        assert np.array_equal(va[k].cpu().numpy(), vb[k].cpu().numpy()), k
+    compare_cache(a, oc)
+
+
+def test_csa_step_short_context():
+    """lca_csa_step from an empty cache: window-only queries, then N <= k, then selection (k = 16)."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=32, idx_heads=4, topk=16)
+    run = LayerRun(layer, B=2, max_ctx=256, ring=32)
+    oc = [run.oracle_caches(i, 140) for i in range(run.B)]
+    for _ in range(140):
+        qin, tk, out, lse = run.step(1)
+        check_queries(run, oc, qin, tk, out, lse, [run.len - 1])
+    compare_cache(run, oc)
+
+
+def test_selection_exact_after_repeated_score_calls():
+    """Contract misuse that must stay safe and exact: lca_csa_index_score called three times without its
+    selection (the per-query histograms count every call, so the scan's candidate bound is too high and
+    fewer than k candidates pass). The selection falls back to all visible blocks: top-k lists still
+    equal the oracle's, through lca_csa_topk_select and through lca_csa_topk_attn."""
+    import torch
+    try:
+        from gpu_harness import to_dev, from_dev
+    except ImportError:
+        from tests.gpu_harness import to_dev, from_dev
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=256)
+    run = LayerRun(layer, B=2, max_ctx=12000, ring=128)
+    _ingest(run, [11000])
+    oc = [run.oracle_caches(b, 11000) for b in range(run.B)]
+    qin = run.queries([run.len - 1])
+    qI, w, q = to_dev(qin["qI"]), to_dev(qin["w"]), to_dev(qin["q"])
+    H = layer.n_heads
+    for via_attn in (False, True):
+        for _ in range(3):
+            run.dev.index_score(qI, w)
+        topk = torch.full((run.B, 1, layer.topk), -7, dtype=torch.int32, device="cuda")
+        out = torch.empty((run.B, 1, H, 128), dtype=torch.int16, device="cuda")
+        lse = torch.empty((run.B, 1, H), dtype=torch.float32, device="cuda")
+        if via_attn:
+            run.dev.topk_attn(q, out, lse, topk)
+        else:
+            run.dev.topk_select(1, topk)
+            run.dev.sparse_attn(q, topk, out, lse)
+        torch.cuda.synchronize()
+        run.last_scores = None
+        check_queries(run, oc, qin, from_dev(topk), from_dev(out, np.uint16), from_dev(lse), [run.len - 1])
+    # the selections cleared the histograms: a normal call is exact again
+    qa, tk, out, lse = run.run_queries(1, fused=True)
+    check_queries(run, oc, qa, tk, out, lse, [run.len - 1])
