@@ -183,6 +183,21 @@ class Layer:
         if self.csa:
             self.topk = torch.empty((self.B, 1, L.topk), dtype=torch.int32, device="cuda")
         self.kept = {}
+        # per-step device addresses, resolved once: the timed loop then costs one library call per step
+        # on the host (tensor slicing per step would make the host, not the GPU, set the pace)
+        names = ("kv", "gate", "ik", "ig") if self.csa else ("kv", "gate")
+        self.step_ptrs = [tuple(self.step_tok[k][s].data_ptr() for k in names) +
+                          tuple(self.step_q[k][s].data_ptr() for k in (("qI", "w", "q") if self.csa else ("q",)))
+                          for s in range(n_steps)]
+        self._bind_step()
+
+    def _bind_step(self):
+        """Pre-bound fast path of step(): the library function and the per-layer constant arguments."""
+        lca, torch = self.lca, self.torch
+        self._lib = lca.lib()
+        self._stream = torch.cuda.current_stream().cuda_stream
+        self._cache_ref = lca.ctypes.byref(self.dev.cache)
+        self._bias = (self.bias_dev["bias"].data_ptr(), self.bias_dev["idx_bias"].data_ptr() if self.csa else None)
 
     def keep_outputs(self, steps):
         """Give these steps their own output buffers (checked against the oracle afterwards)."""
@@ -193,23 +208,33 @@ class Layer:
                 self.kept[s]["topk"] = torch.empty_like(self.topk)
 
     def step(self, s, ev_score=None, rec=None):
-        t = {k: v[s] for k, v in self.step_tok.items()}
-        q = {k: v[s] for k, v in self.step_q.items()}
-        out = self.kept[s]["out"] if s in self.kept else self.out
         if self.csa:
-            # the whole CSA step in one call; it records the events around its score launch
-            topk = self.kept[s]["topk"] if s in self.kept else self.topk
-            self.dev.step(t["kv"], t["gate"], t["ik"], t["ig"], self.bias_dev["bias"], self.bias_dev["idx_bias"],
-                          q["qI"], q["w"], q["q"], out, None, topk,
-                          score_events=(ev_score if ev_score is not None else (None, None)))
-        else:
-            self.dev.compress(t["kv"], t["gate"], self.bias_dev["bias"])
-            self.dev.append(t["kv"], t["gate"])
+            # the whole CSA step in one library call; it records the events around its score launch
+            kv, gate, ik, ig, qI, w, q = self.step_ptrs[s]
+            kept = self.kept.get(s)
+            out = (kept["out"] if kept else self.out).data_ptr()
+            topk = (kept["topk"] if kept else self.topk).data_ptr()
+            ev0, ev1 = ev_score if ev_score is not None else (None, None)
+            rc = self._lib.lca_csa_step(self._cache_ref, kv, gate, ik, ig, self._bias[0], self._bias[1], 1, qI, w, q,
+                                        topk, out, None, self.dev.ws, self.dev.ws_bytes, self._stream, ev0, ev1)
+            if rc != 0:
+                raise self.lca.LcaError("lca_csa_step", rc)
+            return
+        # HCA: compress (the library launches nothing unless a block completes), append, dense attention
+        kv, gate, q = self.step_ptrs[s]
+        kept = self.kept.get(s)
+        out = (kept["out"] if kept else self.out).data_ptr()
+        L, c, st = self._lib, self._cache_ref, self._stream
+        rc = L.lca_hca_compress(c, kv, gate, self._bias[0], 1, st) or L.lca_swa_tail_append(c, kv, gate, None, None,
+                                                                                           1, st)
+        if rc == 0:
             if ev_score is not None:
                 rec(ev_score[0])
-            self.dev.dense_attn(q["q"], out)
+            rc = L.lca_hca_dense_attn(c, q, 1, out, None, self.dev.ws, self.dev.ws_bytes, st)
             if ev_score is not None:
                 rec(ev_score[1])
+        if rc != 0:
+            raise self.lca.LcaError("HCA step", rc)
 
 
 def score_bytes(layer, B, t):

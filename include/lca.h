@@ -103,17 +103,19 @@ typedef struct lca_cache {
   int32_t reserved0;
   /* RoPE frequencies 10000^(-2i/64), i < 32, computed on the host at bind */
   double rope_inv_freq[32];
+  /* their device copy (256 B at the end of the cache memory), what the kernels read */
+  double* rope_inv_freq_dev;
 } lca_cache;
 
 /* Bytes of device memory lca_cache_bind() carves for one layer:
- * D1 (196 B/block) + D3 (34 B/block, CSA) + D2 (196 B/slot) + tail, each
- * array 256-byte aligned. max_blocks = max_ctx / m. Returns 0 for an
+ * D1 (196 B/block) + D3 (34 B/block, CSA) + D2 (196 B/slot) + tail + the
+ * 256-B RoPE frequency table, each array 256-byte aligned. max_blocks = max_ctx / m. Returns 0 for an
  * invalid descriptor or size. */
 size_t lca_cache_bytes(const lca_layer_desc* desc, int32_t batch, int64_t max_ctx, int32_t ring);
 
 /* Carve `base_dev` (>= lca_cache_bytes() bytes, 256-byte aligned) into the
  * arrays above, zero them on `stream`, set len = pending = 0 and fill the
- * RoPE frequencies. ring >= window; to let Tq queries attend in one call
+ * RoPE frequencies (host array, and its device copy, written on `stream`). ring >= window; to let Tq queries attend in one call
  * (chunked prefill), ring >= Tq + window - 1. */
 lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* base_dev, size_t bytes,
                           int32_t batch, int64_t max_ctx, int32_t ring, void* stream);

@@ -43,7 +43,7 @@ class lca_cache(ctypes.Structure):
                 ("idx_scale_dev", ctypes.c_void_p), ("win_codes_dev", ctypes.c_void_p),
                 ("win_scale_dev", ctypes.c_void_p), ("win_rope_dev", ctypes.c_void_p),
                 ("tail_dev", ctypes.c_void_p), ("tail_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
-                ("rope_inv_freq", ctypes.c_double * 32)]
+                ("rope_inv_freq", ctypes.c_double * 32), ("rope_inv_freq_dev", ctypes.c_void_p)]
 
 
 _LIB = None

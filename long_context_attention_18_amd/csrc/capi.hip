@@ -33,7 +33,7 @@ bool desc_ok(const lca_layer_desc* d) {
 int32_t tail_width(const lca_layer_desc* d) { return d->kind == LCA_KIND_CSA ? 384 : 256; }
 
 struct Layout {
-  size_t blk_codes, blk_scale, blk_rope, idx_codes, idx_scale, win_codes, win_scale, win_rope, tail, total;
+  size_t blk_codes, blk_scale, blk_rope, idx_codes, idx_scale, win_codes, win_scale, win_rope, tail, inv_freq, total;
 };
 
 Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring) {
@@ -52,6 +52,7 @@ Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
   L.win_scale = off; off = align_up(off + nw * 4);
   L.win_rope = off; off = align_up(off + nw * 128);
   L.tail = off; off = align_up(off + (size_t)B * d->m * tail_width(d) * 2);
+  L.inv_freq = off; off = align_up(off + 32 * sizeof(double));
   L.total = off;
   return L;
 }
@@ -120,7 +121,7 @@ IngestArgs ingest_args(lca_cache* c, const uint16_t* kv, const uint16_t* gate, c
   a.ring = c->ring;
   a.tail_width = c->tail_width;
   a.B = c->batch;
-  std::memcpy(a.inv_freq, c->rope_inv_freq, sizeof(a.inv_freq));
+  a.inv_freq = c->rope_inv_freq_dev;
   return a;
 }
 
@@ -199,7 +200,11 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
   cache->tail_dev = (uint16_t*)(base + L.tail);
   cache->tail_width = tail_width(desc);
   for (int i = 0; i < 32; ++i) cache->rope_inv_freq[i] = std::pow(10000.0, -(double)(2 * i) / 64.0);
-  return launch_status(launch_fill_zero(base_dev, L.total, (hipStream_t)stream));
+  cache->rope_inv_freq_dev = (double*)(base + L.inv_freq);
+  if (launch_fill_zero(base_dev, L.total, (hipStream_t)stream) != hipSuccess) return LCA_ERR_LAUNCH;
+  // the kernels read the frequencies from this device copy (kept out of every launch's arguments)
+  return launch_status(hipMemcpyAsync(cache->rope_inv_freq_dev, cache->rope_inv_freq, 32 * sizeof(double),
+                                      hipMemcpyHostToDevice, (hipStream_t)stream));
 }
 
 size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t query, int64_t max_ctx) {
@@ -288,6 +293,11 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.k = cache->desc.topk;
   a.m = cache->desc.m;
   a.G2 = W.G2;
+  {
+    const int64_t g1 = (a.len / a.m + kScoreChunk - 1) / kScoreChunk;  // score chunks of the last query
+    int64_t cm = 2 * (((int64_t)a.k + (g1 > 0 ? g1 : 1) - 1) / (g1 > 0 ? g1 : 1));
+    a.cmin = (int32_t)(cm < 16 ? 16 : (cm > kScoreChunk ? kScoreChunk : cm));
+  }
   *out = a;
   return LCA_OK;
 }
@@ -353,7 +363,7 @@ lca_status attn_args(lca_cache* cache, bool dense, const uint16_t* q_dev, const 
   a.W = cache->desc.window;
   a.ring = cache->ring;
   a.dense = dense ? 1 : 0;
-  std::memcpy(a.inv_freq, cache->rope_inv_freq, sizeof(a.inv_freq));
+  a.inv_freq = cache->rope_inv_freq_dev;
   *out = a;
   return LCA_OK;
 }

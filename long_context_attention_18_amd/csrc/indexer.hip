@@ -149,6 +149,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ uint32_t flag_blk[kScoreChunk];  // blocks to rescore exactly (offset in chunk)
   __shared__ uint32_t n_flag;
   __shared__ uint32_t wmax_s[4];
+  __shared__ uint32_t range_s;
+  __shared__ int lo_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
@@ -309,8 +311,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     }
   }
   // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
-  // and the 16 bins below it (down to a quarter of the max). Counts in a bin only ever undercount, so
-  // the bin where the global count from the top reaches k is a lower bound of the k-th largest key.
+  // and the 16 bins below it (down to a quarter of the max), or, when those hold fewer than cmin of the
+  // chunk's keys, every bin down to where the chunk's count from the top reaches cmin. Counts in a bin
+  // only ever undercount, so the bin where the global count from the top reaches k is a lower bound of
+  // the k-th largest key; cmin (twice a chunk's share of k) keeps that bound tight when the scores
+  // bunch up, e.g. all <= 0 (every indexer weight negative): the max is then 0 and the keys of negative
+  // scores lie far below its bin.
   uint32_t m = 0;
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) m = max(m, lane_keys[pr]);
@@ -327,9 +333,46 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     if (key != 0 && (int)(key >> 20) >= low_bin) atomicAdd(&hist[key >> 20], 1u);
   }
   __syncthreads();
-  if (tid <= top_bin - low_bin) {
-    const uint32_t c = hist[low_bin + tid];
-    if (c) atomicAdd(&q_hist(a, q)[low_bin + tid], c);
+  if (wave == 0) {
+    uint32_t v = (lane <= top_bin - low_bin) ? hist[low_bin + lane] : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
+    if (lane == 0) range_s = v;
+  }
+  __syncthreads();
+  int lo = low_bin;
+  if (range_s < (uint32_t)a.cmin && low_bin > 0) {
+    // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
+#pragma unroll
+    for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+      const uint32_t key = lane_keys[pr];
+      if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&hist[key >> 20], 1u);
+    }
+    if (tid == 0) lo_s = 0;
+    __syncthreads();
+    const int hi_b = kHistBins - 16 * tid;  // this thread: bins [hi_b - 16, hi_b), threads in descending order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 1; i <= 16; ++i) cnt += hist[hi_b - i];
+    uint32_t tot;
+    const uint32_t excl = block_excl_scan(cnt, wmax_s, &tot);
+    const uint32_t cm = (uint32_t)a.cmin;
+    if (excl < cm && excl + cnt >= cm) {
+      uint32_t c = excl;
+      for (int i = 1; i <= 16; ++i) {
+        c += hist[hi_b - i];
+        if (c >= cm) {
+          lo_s = hi_b - i;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    lo = lo_s;
+  }
+  for (int i = lo + tid; i <= top_bin; i += 256) {
+    const uint32_t c = hist[i];
+    if (c) atomicAdd(&q_hist(a, q)[i], c);
   }
 }
 

@@ -49,7 +49,7 @@ struct IngestArgs {
   int32_t tail_width;
   int32_t n_win;           // append: window tokens written
   int32_t B;
-  double inv_freq[32];
+  const double* inv_freq;  // [32], device copy of the cache's RoPE frequencies
 };
 
 // The indexer's workspace is one block per query (so its place does not depend on how many queries
@@ -71,6 +71,7 @@ struct ScoreArgs {
   int32_t k;
   int32_t m;
   int32_t G2;              // scan segments per query
+  int32_t cmin;            // keys each score chunk counts into the histogram at least (twice its share of k)
 };
 
 __device__ __forceinline__ uint32_t* q_hist(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride); }
@@ -98,7 +99,7 @@ struct AttnArgs {
   int32_t W;
   int32_t ring;
   int32_t dense;           // 1 = HCA (every visible block), 0 = CSA (topk list)
-  double inv_freq[32];
+  const double* inv_freq;  // [32], device copy of the cache's RoPE frequencies
 };
 
 // One-launch attention for a few queries (attend.hip): the query's compressed entries come from the

@@ -276,3 +276,24 @@ def test_selection_exact_after_repeated_score_calls():
     # the selections cleared the histograms: a normal call is exact again
     qa, tk, out, lse = run.run_queries(1, fused=True)
     check_queries(run, oc, qa, tk, out, lse, [run.len - 1])
+
+
+def test_indexer_all_weights_negative():
+    """Every indexer weight negative: all scores <= 0, the top-k are the zero and least negative scores,
+    whose keys sit far below the chunk maxima's bins. The score chunks then count down to cmin keys
+    (the tight-bound path); scores and top-k must still equal the oracle bit for bit, through the
+    separate calls and through lca_csa_step."""
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=256)
+
+    def qtransform(qin):
+        out = dict(qin)
+        out["w"] = -np.abs(qin["w"])
+        return out
+
+    run = LayerRun(layer, B=2, max_ctx=20000, ring=128, qtransform=qtransform)
+    _ingest(run, [8192, 8192, 1999])
+    worst, oc = _decode(run, 3, run.len + 6)
+    assert worst["scores_checked"] > 0
+    for _ in range(3):
+        qin, tk, out, lse = run.step(1)
+        check_queries(run, oc, qin, tk, out, lse, [run.len - 1])
