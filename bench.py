@@ -249,6 +249,11 @@ def attn_bytes(layer, B, t):
     return B * ((n + w) * 196 + layer.n_heads * 128 * 2 * 2)
 
 
+def total_spin_ms_estimate(K, n_layers):
+    """Lower estimate of the pre-region spin in ms (6e5 * max(20, K) * n_layers cycles at <= 2.4 GHz)."""
+    return 6.0e5 * max(20, K) * n_layers / 2.4e9 * 1e3
+
+
 def src_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -494,7 +499,8 @@ def main():
         run_steps(range(W), False)
         torch.cuda.synchronize()
         # keep the GPU busy while the host enqueues the whole timed region, so no step waits on the host
-        torch.cuda._sleep(int(5.0e5 * max(20, K)))
+        # (about 0.25 ms of spin per step and layer: several times the host's enqueue cost)
+        torch.cuda._sleep(int(6.0e5 * max(20, K) * len(layers)))
         h0 = time.perf_counter()
         rec(ev_begin)
         run_steps(range(W, S), True)
@@ -503,6 +509,8 @@ def main():
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - h0) * 1e3
         log(f"host enqueue of the timed region: {enq_ms:.2f} ms")
+        if enq_ms > total_spin_ms_estimate(K, len(layers)):
+            log("warning: the host enqueue outlasted the spin; the GPU may have waited on the host")
 
     total_ms = hev.elapsed_ms(ev_begin, ev_end)
     ms_per_step = total_ms / K
