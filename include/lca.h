@@ -122,15 +122,15 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
 
 /* Scratch one call of lca_csa_indexer_topk / lca_csa_attend /
  * lca_csa_sparse_attn / lca_hca_dense_attn needs for up to max_tq queries per sequence at up to
- * max_ctx tokens. For CSA it holds, per query, a 16 KiB histogram that must
- * be zero when an indexer call starts: zero the workspace once with
- * lca_workspace_init() before its first use; every completed
- * lca_csa_indexer_topk, lca_csa_topk_select, lca_csa_attend or
- * lca_csa_topk_attn leaves it zero again.
- * Everything else in it is rewritten by each call. A workspace may be shared
- * by caches of the same or smaller shape; calls sharing one workspace must
- * not overlap in time. HCA layers need none (0 bytes): lca_csa_sparse_attn
- * and lca_hca_dense_attn accept ws_dev = NULL. */
+ * max_ctx tokens. It holds counters of the attention's key splits and, for
+ * CSA, a 16 KiB histogram per query, all of which must be zero when a call
+ * starts: zero the workspace once with lca_workspace_init() before its first
+ * use; every completed call leaves them zero again (an lca_csa_index_score
+ * without its selection excepted, see below). Everything else in it is
+ * rewritten by each call. A workspace may be shared by caches of the same or
+ * smaller shape; calls sharing one workspace must not overlap in time.
+ * lca_csa_sparse_attn and lca_hca_dense_attn also accept ws_dev = NULL (they
+ * then use fewer, longer workgroups for few queries). */
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx);
 lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
 

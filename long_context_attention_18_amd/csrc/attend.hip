@@ -6,10 +6,12 @@
 // one softmax over all of a query's keys:
 //   logit = RoPE(q_h, t) . x / sqrt(128),  K = V = the dequantised entry.
 //
-// A workgroup owns one query and 16 of its heads, and walks ALL the query's
-// keys, so no split-K partials and no merge launch are needed: the 8 waves
-// take 32-key chunks in turn, each keeps an online softmax for the 16 heads,
-// and the 8 wave states are merged in LDS at the end. With few queries the
+// A workgroup owns one query, 16 of its heads and a share of its keys (all
+// of them, or one of up to 4 key splits when the call has few queries): its
+// 8 waves take contiguous ranges of 32-key chunks, each keeps an online
+// softmax for the 16 heads, and the 8 wave states are merged in LDS. With
+// splits, each workgroup writes a partial and the last of a (query, group)
+// to finish merges them, in the same launch. With few queries the
 // step is latency-bound, and this keeps it to one launch. Each wave takes a
 // contiguous range of the key slots and issues the gathers of up to kRound
 // chunks at once (random reads: one memory latency per round).
@@ -66,6 +68,7 @@ struct AttendLds {
     } c;
   } u;
   int32_t list[kMaxTopk];  // compressed entries to attend (block indices)
+  int last;                // this workgroup merges the splits
   float cos_t[32], sin_t[32];
 };
 
@@ -262,7 +265,8 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   const AttnArgs& a = args.t;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int hg = blockIdx.x, q = blockIdx.y;
+  const int hgs = (a.H + 15) / 16;
+  const int hg = blockIdx.x % hgs, split = blockIdx.x / hgs, q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
   const int64_t t = a.len - a.Tq + tq;
   const int64_t N = (t + 1) / a.m;
@@ -340,12 +344,12 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   }
   if (do_select) {
     const ScoreArgs& sa = args.s;
-    if (hg == 0)  // every scan workgroup has read this query's histogram: clear it for the next call
+    if (hg == 0 && split == 0)  // every scan workgroup has read this query's histogram: clear it for the next call
       for (int i = tid; i < kHistBins; i += 512) q_hist(sa, q)[i] = 0u;
     K.n_list = (int)select_query(sa, q, N, S.u.sel, S.list);
   }
   __syncthreads();
-  if (do_select && hg == 0 && args.s.topk) {
+  if (do_select && hg == 0 && split == 0 && args.s.topk) {
     int32_t* o = args.s.topk + (size_t)q * a.k;
     for (int i = tid; i < a.k; i += 512) o[i] = S.list[i];
   }
@@ -376,11 +380,16 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   float* scl = &S.u.b.scl[wave][0][0];
   const int kpos = 8 * (r >> 2) + 2 * (r & 3);  // MFMA K index of key r of tile 0 (tile 1: +1)
 
-  // wave w: key slots [w * per, (w + 1) * per), in rounds of up to kRound chunks
+  // this workgroup: key slots [s_begin, s_end) of its split; wave w: [s_begin + w * per, + per), in rounds
+  // of up to kRound chunks
   const int n_keys = K.n_win + K.n_list;
-  const int per = ((n_keys + kWaves * 16 - 1) / (kWaves * 16)) * 16;
-  const int w_begin = wave * per;
-  const int w_end = min(w_begin + per, n_keys);
+  const int splits = args.splits;
+  const int per_split = ((n_keys + splits * 16 - 1) / (splits * 16)) * 16;
+  const int s_begin = split * per_split;
+  const int s_end = min(s_begin + per_split, n_keys);
+  const int per = ((per_split + kWaves * 16 - 1) / (kWaves * 16)) * 16;
+  const int w_begin = s_begin + wave * per;
+  const int w_end = min(w_begin + per, s_end);
   const int w_chunks = (per + kChunk - 1) / kChunk;  // the same for every wave
   for (int c = 0; c < w_chunks; c += kRound) {
     const int slot0 = w_begin + c * kChunk;
@@ -419,6 +428,40 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += ov[i] * f;
     }
+    if (splits > 1) {
+      // this split's partial; the last split of the (query, group) to finish merges all of them
+      AttendPartial* mine = args.part + ((size_t)q * hgs + hg) * splits + split;
+      *reinterpret_cast<v4f*>(&mine->o[h][d0]) = (v4f){acc[0], acc[1], acc[2], acc[3]};
+      if (d0 == 0) {
+        mine->m[h] = M;
+        mine->l[h] = L;
+      }
+      uint32_t* cnt = args.cnt + (size_t)q * hgs + hg;
+      __syncthreads();
+      if (tid == 0)
+        S.last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(splits - 1);
+      __syncthreads();
+      if (!S.last) return;
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *cnt = 0u;  // every split has counted: ready for the next call
+      }
+      __syncthreads();
+      const AttendPartial* all = args.part + ((size_t)q * hgs + hg) * splits;
+      M = -INFINITY;
+      for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, all[sp].m[h]);
+      L = 0.0f;
+      acc[0] = acc[1] = acc[2] = acc[3] = 0.0f;
+      for (int sp = 0; sp < splits; ++sp) {
+        const float ms = all[sp].m[h];
+        if (ms == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f((ms - M) * kC);
+        L += all[sp].l[h] * f;
+        const v4f ov = *reinterpret_cast<const v4f*>(&all[sp].o[h][d0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += ov[i] * f;
+      }
+    }
     const int hh = hg * 16 + h;
     if (hh < a.H) {
       const float inv = 1.0f / L;
@@ -436,10 +479,10 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
 
 hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t s) {
   const unsigned nq = (unsigned)(B * args.t.Tq);
-  const unsigned hgs = (unsigned)((args.t.H + 15) / 16);
-  if (mode == kAttendSelect) hipLaunchKernelGGL(attend_kernel<kAttendSelect>, dim3(hgs, nq), dim3(512), 0, s, args);
-  else if (mode == kAttendDense) hipLaunchKernelGGL(attend_kernel<kAttendDense>, dim3(hgs, nq), dim3(512), 0, s, args);
-  else hipLaunchKernelGGL(attend_kernel<kAttendList>, dim3(hgs, nq), dim3(512), 0, s, args);
+  const unsigned gx = (unsigned)((args.t.H + 15) / 16 * args.splits);
+  if (mode == kAttendSelect) hipLaunchKernelGGL(attend_kernel<kAttendSelect>, dim3(gx, nq), dim3(512), 0, s, args);
+  else if (mode == kAttendDense) hipLaunchKernelGGL(attend_kernel<kAttendDense>, dim3(gx, nq), dim3(512), 0, s, args);
+  else hipLaunchKernelGGL(attend_kernel<kAttendList>, dim3(gx, nq), dim3(512), 0, s, args);
   return hipGetLastError();
 }
 

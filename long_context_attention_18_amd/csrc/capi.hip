@@ -65,11 +65,12 @@ bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
   return true;
 }
 
-// Workspace (CSA only): one block per query (histogram, scan segment counts, score keys,
-// candidates). Nothing's place depends on a call's Tq, so the per-query histograms that must be
-// zero between calls stay put.
+// Workspace: the one-launch attention's (query, head group) counters first (fixed size and place: they
+// must be zero between calls), then, for CSA, one block per query (histogram, scan segment counts,
+// score keys, candidates), then the attention's split partials. The counters' and the per-query
+// blocks' places do not depend on a call's Tq, so what must be zero between calls stays put.
 struct WsLayout {
-  size_t qbase, qstride, off_seg, off_keys, off_cand, total;
+  size_t cnt, qbase, qstride, off_seg, off_keys, off_cand, part, total;
   int32_t G2;
 };
 
@@ -77,7 +78,8 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   WsLayout W{};
   const int64_t max_blocks = max_ctx / d->m;
   const size_t nq = (size_t)B * (size_t)max_tq;
-  size_t off = 0;
+  W.cnt = 0;
+  size_t off = kAttendCounterBytes;
   W.qbase = off;
   W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
@@ -88,8 +90,28 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
     W.qstride = q;
     off += nq * q;
   }
-  W.total = off;
+  W.part = align_up(off);
+  const size_t nq_att = nq < (size_t)kAttendMaxQueries ? nq : (size_t)kAttendMaxQueries;
+  const size_t groups = (size_t)(d->n_heads + 15) / 16;
+  W.total = align_up(W.part + nq_att * groups * kAttendMaxSplits * sizeof(AttendPartial));
   return W;
+}
+
+// Key splits of the one-launch attention for nq queries: about kAttendTargetWGs workgroups per call
+int32_t attend_splits(int32_t nq, int32_t H) {
+  const int64_t groups = (H + 15) / 16;
+  int64_t s = (kAttendTargetWGs + nq * groups - 1) / (nq * groups);
+  return (int32_t)(s < 1 ? 1 : (s > kAttendMaxSplits ? kAttendMaxSplits : s));
+}
+
+void attend_workspace(AttendArgs* args, const lca_cache* c, int32_t Tq, void* ws_dev, size_t ws_bytes) {
+  args->splits = 1;
+  if (!ws_dev) return;
+  WsLayout W = ws_layout(&c->desc, c->batch, Tq, c->max_ctx);
+  if (ws_bytes < W.total) return;
+  args->splits = attend_splits(c->batch * Tq, c->desc.n_heads);
+  args->part = (AttendPartial*)((char*)ws_dev + W.part);
+  args->cnt = (uint32_t*)((char*)ws_dev + W.cnt);
 }
 
 lca_status launch_status(hipError_t e) { return e == hipSuccess ? LCA_OK : LCA_ERR_LAUNCH; }
@@ -382,6 +404,7 @@ lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, c
   if (nq <= kAttendMaxQueries) {
     AttendArgs args{};
     args.t = a;
+    attend_workspace(&args, cache, Tq, ws_dev, ws_bytes);
     return launch_status(launch_attend(args, cache->batch, dense ? kAttendDense : kAttendList, s));
   }
   return launch_status(launch_attention(a, cache->batch, s));
@@ -395,6 +418,7 @@ lca_status topk_attn_impl(lca_cache* cache, const uint16_t* qI_dev, const float*
   if (st != LCA_OK) return st;
   st = attn_args(cache, false, q_dev, nullptr, Tq, out_dev, lse_dev, &args.t);
   if (st != LCA_OK) return st;
+  attend_workspace(&args, cache, Tq, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
   if (score) {
     hipError_t e = launch_index_score(args.s, cache->batch, s);
@@ -444,6 +468,7 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
   if (st != LCA_OK) return st;
   st = attn_args(&after, false, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
   if (st != LCA_OK) return st;
+  attend_workspace(&args, &after, T, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
   const int64_t m = cache->desc.m;
   // compress the blocks the T tokens complete (their keys are scored below)

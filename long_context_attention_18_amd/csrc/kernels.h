@@ -107,9 +107,23 @@ struct AttnArgs {
 // workgroup over the scan's candidates.
 constexpr int kMaxTopk = 2048;
 constexpr int kAttendList = 0, kAttendDense = 1, kAttendSelect = 2;
+// Key splits of the one-launch attention: a (query, 16-head group) may be spread over up to
+// kAttendMaxSplits workgroups, each over its share of the keys; each writes a partial (running max,
+// sum and unnormalised O of its 16 heads) and the last to finish (a per-(query, group) counter,
+// release / acquire at agent scope) merges them.
+constexpr int kAttendMaxSplits = 4;
+constexpr int kAttendTargetWGs = 64;  // splits are chosen to give a call about this many workgroups
+struct AttendPartial {
+  float m[16], l[16];
+  float o[16][kHeadDim];
+};
+constexpr size_t kAttendCounterBytes = 8192;  // (query, group) counters: 511 queries x 4 groups x 4 B, padded
 struct AttendArgs {
   ScoreArgs s;  // selection inputs (kAttendSelect)
   AttnArgs t;
+  AttendPartial* part;  // [B*Tq][groups][splits] (splits > 1)
+  uint32_t* cnt;        // [B*Tq][groups], zero between calls (splits > 1)
+  int32_t splits;
 };
 
 hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s);

@@ -16,29 +16,43 @@
 
 namespace lca {
 
+constexpr int kRadixBits = 11;  // digit width of the radix select: 2048 LDS bins, two passes in the common case
+constexpr int kRadixBins = 1 << kRadixBits;
+
 struct SelectLds {
   uint64_t cs[kCandCap];
-  uint32_t seg_off[2049];  // G2_q <= 512 segments
-  uint32_t hist[256];
+  uint32_t seg_off[2049];  // G2_q <= 2048 segments
+  uint32_t hist[kRadixBins];
   uint32_t wsum[8];
-  uint32_t sel_digit, sel_above, sel_count;
+  uint32_t sel_digit, sel_above, sel_count, flat_needed;
   uint64_t red_lo[8], red_hi[8];
 };
 
+// exclusive prefix sum over the 512 threads of the workgroup (thread order); every thread calls it
+__device__ __forceinline__ uint32_t excl_scan_512(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int w = 0; w < wave; ++w) off += wsum[w];
+  return off + incl - v;
+}
+
 // Returns the number of winners written (min(k, N) whenever N > k). The candidate lower bound is only
 // a hint: with fewer than k candidates (a histogram left dirty by a score call without its selection)
-// the selection takes the path over every visible block and stays exact.
+// or more than fit in LDS, the selection takes the path over every visible block and stays exact.
 __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, SelectLds& S, int32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t* cs = S.cs;
   uint32_t* seg_off = S.seg_off;
   uint32_t* hist = S.hist;
   uint32_t* wsum = S.wsum;
-  uint32_t& sel_digit = S.sel_digit;
-  uint32_t& sel_above = S.sel_above;
-  uint32_t& sel_count = S.sel_count;
-  uint64_t* red_lo = S.red_lo;
-  uint64_t* red_hi = S.red_hi;
 
   // One round of loads: every segment's count and, speculatively, its first kSpec slots (always in
   // bounds: a segment has room for kScanPerWG candidates); only a fuller segment needs a second round.
@@ -46,6 +60,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   constexpr int kSpec = 256;
   const uint64_t* cand = q_cand(a, q);
   const int lanes_per_seg = G2_q <= 32 ? 16 : (G2_q <= 64 ? 8 : 0);  // speculation only for few segments
+  const uint32_t covered = lanes_per_seg ? kSpec : 0u;  // slots per segment the speculative loads place
   uint64_t spec[16];
   const int my_seg = lanes_per_seg ? tid / lanes_per_seg : 0;
   const int my_sub = lanes_per_seg ? tid % lanes_per_seg : 0;
@@ -55,6 +70,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
     for (int r = 0; r < 16; ++r)
       if (r < per_lane) spec[r] = cand[(size_t)my_seg * kScanPerWG + my_sub + r * lanes_per_seg];
   }
+  if (tid == 0) S.flat_needed = 0u;
   for (int g0 = 0; g0 < G2_q; g0 += 512) {
     const int gi = g0 + tid;
     const uint32_t c = gi < G2_q ? q_seg(a, q)[gi] : 0u;
@@ -70,120 +86,123 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
     for (int w = 0; w < wave; ++w) base += wsum[w];
     if (gi < G2_q) seg_off[gi] = base + incl - c;
     if (tid == 511) seg_off[g0 + 512 < G2_q ? g0 + 512 : G2_q] = base + incl;
+    if (c > covered) S.flat_needed = 1u;
     __syncthreads();
   }
   const uint32_t total = seg_off[G2_q];
   const bool fast = total >= (uint32_t)a.k && total <= (uint32_t)kCandCap;
   const int64_t n = fast ? (int64_t)total : N;
   const uint32_t* keys = q_keys(a, q);
-  if (fast) {
-    uint32_t covered = 0;  // slots per segment already placed from the speculative loads
-    if (lanes_per_seg) {
-      covered = kSpec;
-      if (my_seg < G2_q) {
-        const uint32_t c = seg_off[my_seg + 1] - seg_off[my_seg];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t i = my_sub + r * lanes_per_seg;
-          if (r < per_lane && i < c) cs[seg_off[my_seg] + i] = spec[r];
-        }
-      }
-    }
-    // the rest (segments beyond the speculated slots): flat gather, segment found by binary search
-    for (uint32_t i = tid; i < total; i += 512) {
-      int lo = 0, hi = G2_q - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seg_off[mid] <= i) lo = mid;
-        else hi = mid - 1;
-      }
-      const uint32_t off = i - seg_off[lo];
-      if (off >= covered) cs[i] = cand[(size_t)lo * kScanPerWG + off];
-    }
-  }
-  __syncthreads();
   // element i in index order: the ordered candidates, or (slow path) every visible block
   auto elem = [&](int64_t i) -> uint64_t {
     if (fast) return cs[i];
     return ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
   };
+  // gather into LDS (fast path), keeping each thread's smallest and largest element
+  uint64_t lo = ~0ull, hi = 0;
+  if (fast) {
+    if (lanes_per_seg && my_seg < G2_q) {
+      const uint32_t c = seg_off[my_seg + 1] - seg_off[my_seg];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t i = my_sub + r * lanes_per_seg;
+        if (r < per_lane && i < c) {
+          cs[seg_off[my_seg] + i] = spec[r];
+          lo = spec[r] < lo ? spec[r] : lo;
+          hi = spec[r] > hi ? spec[r] : hi;
+        }
+      }
+    }
+    if (S.flat_needed) {
+      // segments longer than the speculated slots: flat gather, segment found by binary search
+      for (uint32_t i = tid; i < total; i += 512) {
+        int l = 0, h = G2_q - 1;
+        while (l < h) {
+          const int mid = (l + h + 1) >> 1;
+          if (seg_off[mid] <= i) l = mid;
+          else h = mid - 1;
+        }
+        const uint32_t off = i - seg_off[l];
+        if (off >= covered) {
+          const uint64_t e = cand[(size_t)l * kScanPerWG + off];
+          cs[i] = e;
+          lo = e < lo ? e : lo;
+          hi = e > hi ? e : hi;
+        }
+      }
+    }
+  } else {
+    for (int64_t i = tid; i < n; i += 512) {
+      const uint64_t e = elem(i);
+      lo = e < lo ? e : lo;
+      hi = e > hi ? e : hi;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
+  }
+  if (lane == 0) {
+    S.red_lo[wave] = lo;
+    S.red_hi[wave] = hi;
+  }
+  __syncthreads();
 
   // every element a winner (n == k): no selection
   uint64_t prefix = 0, mask = 0;
   if (n > (int64_t)a.k) {
-    // radix select of the k-th largest 64-bit key (score key, then lower index first), 8 bits at a time
-    // from the highest bit in which the elements differ, stopping as soon as the bin that holds it is
-    // taken whole
-    {
-      uint64_t lo = ~0ull, hi = 0;
-      for (int64_t i = tid; i < n; i += 512) {
-        const uint64_t e = elem(i);
-        lo = e < lo ? e : lo;
-        hi = e > hi ? e : hi;
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
-        lo = l2 < lo ? l2 : lo;
-        hi = h2 > hi ? h2 : hi;
-      }
-      if (lane == 0) {
-        red_lo[wave] = lo;
-        red_hi[wave] = hi;
-      }
-    }
-    __syncthreads();
-    uint64_t glo = red_lo[0], ghi = red_hi[0];
+    uint64_t glo = S.red_lo[0], ghi = S.red_hi[0];
     for (int w = 1; w < 8; ++w) {
-      glo = red_lo[w] < glo ? red_lo[w] : glo;
-      ghi = red_hi[w] > ghi ? red_hi[w] : ghi;
+      glo = S.red_lo[w] < glo ? S.red_lo[w] : glo;
+      ghi = S.red_hi[w] > ghi ? S.red_hi[w] : ghi;
     }
-    const uint64_t diff = glo ^ ghi;                 // nonzero: keys are unique and n > k >= 1
-    const int hb = 63 - __clzll((long long)diff);    // highest differing bit
+    // radix select of the k-th largest 64-bit key (score key, then lower index first), kRadixBits at a
+    // time from the highest bit in which the elements differ (keys are unique and n > k >= 1, so some
+    // bit differs), stopping as soon as the bin that holds it is taken whole
+    const int hb = 63 - __clzll((long long)(glo ^ ghi));
     const uint64_t common = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
     prefix = glo & common;
     mask = common;
-    uint32_t need = (uint32_t)a.k;  // N > k here
-    for (int shift = hb - 7; shift > -8; shift -= 8) {
-      const int sh = shift < 0 ? 0 : shift;           // the last digit may be narrower than 8 bits
-      const uint64_t dmask = shift < 0 ? ((1ull << (shift + 8)) - 1ull) : 255ull;
-      if (tid < 256) hist[tid] = 0;
+    uint32_t need = (uint32_t)a.k;
+    for (int shift = hb - (kRadixBits - 1); shift > -kRadixBits; shift -= kRadixBits) {
+      const int sh = shift < 0 ? 0 : shift;  // the last digit may be narrower
+      const uint64_t dmask = shift < 0 ? ((1ull << (shift + kRadixBits)) - 1ull) : (uint64_t)(kRadixBins - 1);
+      for (int i = tid; i < kRadixBins; i += 512) hist[i] = 0u;
       __syncthreads();
       for (int64_t i = tid; i < n; i += 512) {
-        uint64_t e = elem(i);
+        const uint64_t e = elem(i);
         if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
       }
       __syncthreads();
-      if (wave == 0) {
-        // lane covers bins 255-4*lane .. 252-4*lane (descending)
-        uint32_t c4 = 0;
-        for (int i = 0; i < 4; ++i) c4 += hist[255 - 4 * lane - i];
-        uint32_t incl = c4;
-        for (int o = 1; o < 64; o <<= 1) {
-          uint32_t t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
-        }
-        uint32_t excl = incl - c4;
-        if (excl < need && incl >= need) {
-          uint32_t c = excl;
-          for (int i = 0; i < 4; ++i) {
-            uint32_t d = 255 - 4 * lane - i;
-            if (c + hist[d] >= need) {
-              sel_digit = d;
-              sel_above = c;
-              sel_count = hist[d];
-              break;
-            }
-            c += hist[d];
+      // counts from the top: thread t holds bins 2047-4t .. 2044-4t
+      uint32_t h4[4], c4 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h4[j] = hist[kRadixBins - 1 - 4 * tid - j];
+        c4 += h4[j];
+      }
+      const uint32_t excl = excl_scan_512(c4, wsum);
+      if (excl < need && excl + c4 >= need) {
+        uint32_t c = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (c + h4[j] >= need) {
+            S.sel_digit = (uint32_t)(kRadixBins - 1 - 4 * tid - j);
+            S.sel_above = c;
+            S.sel_count = h4[j];
+            break;
           }
+          c += h4[j];
         }
       }
       __syncthreads();
-      const uint32_t d = sel_digit;
-      need -= sel_above;
+      const uint32_t d = S.sel_digit;
+      need -= S.sel_above;
       prefix |= (uint64_t)d << sh;
       mask |= dmask << sh;
-      if (sel_count == need) break;
+      if (S.sel_count == need) break;
     }
   }
   // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run
@@ -192,19 +211,9 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   const int64_t i1 = (i0 + per < n) ? i0 + per : n;
   uint32_t mine = 0;
   for (int64_t i = i0; i < i1; ++i) mine += ((elem(i) & mask) >= prefix) ? 1u : 0u;
-  uint32_t incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t pos = incl - mine, n_win = 0;
-  for (int w = 0; w < 8; ++w) {
-    if (w < wave) pos += wsum[w];
-    n_win += wsum[w];
-  }
+  uint32_t pos = excl_scan_512(mine, wsum);
+  uint32_t n_win = 0;
+  for (int w = 0; w < 8; ++w) n_win += wsum[w];
   for (int64_t i = i0; i < i1; ++i) {
     const uint64_t e = elem(i);
     if ((e & mask) >= prefix) {
