@@ -91,16 +91,21 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
     off += nq * q;
   }
   W.part = align_up(off);
-  const size_t nq_att = nq < (size_t)kAttendMaxQueries ? nq : (size_t)kAttendMaxQueries;
-  const size_t groups = (size_t)(d->n_heads + 15) / 16;
-  W.total = align_up(W.part + nq_att * groups * kAttendMaxSplits * sizeof(AttendPartial));
+  // partials exist only with splits, and then (query, group, split) triples number <= kAttendMaxWGs
+  W.total = align_up(W.part + (size_t)kAttendMaxWGs * sizeof(AttendPartial));
   return W;
 }
 
-// Key splits of the one-launch attention for nq queries: about kAttendTargetWGs workgroups per call
-int32_t attend_splits(int32_t nq, int32_t H) {
+// Key splits of the one-launch attention: none for up to 768 keys, else about one 32-key chunk per
+// wave (8 waves per workgroup), within kAttendMaxWGs workgroups per call. n_keys: the most keys a query of the call attends.
+int32_t attend_splits(int32_t nq, int32_t H, int64_t n_keys) {
   const int64_t groups = (H + 15) / 16;
-  int64_t s = (kAttendTargetWGs + nq * groups - 1) / (nq * groups);
+  const int64_t chunks = (n_keys + 31) / 32;
+  // up to 3 chunks per wave the partials, the fence and the merge cost more than the split saves
+  if (chunks <= 3 * 8) return 1;
+  int64_t s = (chunks + 7) / 8;
+  const int64_t cap = kAttendMaxWGs / (nq * groups);
+  if (s > cap) s = cap;
   return (int32_t)(s < 1 ? 1 : (s > kAttendMaxSplits ? kAttendMaxSplits : s));
 }
 
@@ -109,7 +114,10 @@ void attend_workspace(AttendArgs* args, const lca_cache* c, int32_t Tq, void* ws
   if (!ws_dev) return;
   WsLayout W = ws_layout(&c->desc, c->batch, Tq, c->max_ctx);
   if (ws_bytes < W.total) return;
-  args->splits = attend_splits(c->batch * Tq, c->desc.n_heads);
+  const int64_t N_last = c->len / c->desc.m;  // visible blocks of the last query (the most)
+  const int64_t n_list = c->desc.kind == LCA_KIND_CSA ? (N_last < c->desc.topk ? N_last : c->desc.topk) : N_last;
+  const int64_t n_win = c->len < c->desc.window ? c->len : c->desc.window;
+  args->splits = attend_splits(c->batch * Tq, c->desc.n_heads, n_list + n_win);
   args->part = (AttendPartial*)((char*)ws_dev + W.part);
   args->cnt = (uint32_t*)((char*)ws_dev + W.cnt);
 }

@@ -108,11 +108,11 @@ struct AttnArgs {
 constexpr int kMaxTopk = 2048;
 constexpr int kAttendList = 0, kAttendDense = 1, kAttendSelect = 2;
 // Key splits of the one-launch attention: a (query, 16-head group) may be spread over up to
-// kAttendMaxSplits workgroups, each over its share of the keys; each writes a partial (running max,
+// kAttendMaxSplits workgroups (about one 32-key chunk per wave), each over its share of the keys; each writes a partial (running max,
 // sum and unnormalised O of its 16 heads) and the last to finish (a per-(query, group) counter,
 // release / acquire at agent scope) merges them.
-constexpr int kAttendMaxSplits = 4;
-constexpr int kAttendTargetWGs = 64;  // splits are chosen to give a call about this many workgroups
+constexpr int kAttendMaxSplits = 8;
+constexpr int kAttendMaxWGs = 256;  // with splits, a call stays within one workgroup per CU (LDS allows one)
 struct AttendPartial {
   float m[16], l[16];
   float o[16][kHeadDim];

@@ -297,3 +297,28 @@ def test_indexer_all_weights_negative():
     for _ in range(3):
         qin, tk, out, lse = run.step(1)
         check_queries(run, oc, qin, tk, out, lse, [run.len - 1])
+
+
+def test_attention_key_splits_csa():
+    """k = 1024 with more visible blocks than k: 1152 keys per query, so the one-launch attention spreads
+    each (query, head group) over 5 key splits merged by the last to finish. Through lca_csa_step and
+    through the separate calls: against the oracle."""
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=1024)
+    run = LayerRun(layer, B=2, max_ctx=9000, ring=128)
+    _ingest(run, [8200])
+    worst, oc = _decode(run, 2, 8210, fused=True)
+    for _ in range(2):
+        qin, tk, out, lse = run.step(1)
+        check_queries(run, oc, qin, tk, out, lse, [run.len - 1])
+    qin, tk, out, lse = run.run_queries(1)
+    check_queries(run, oc, qin, tk, out, lse, [run.len - 1])
+    print("csa split worst", worst)
+
+
+def test_attention_key_splits_hca():
+    """HCA with 832 keys per query (704 blocks + the window): dense attention over 4 key splits."""
+    layer = configs.Layer("hca", 128, n_heads=64, window=128)
+    run = LayerRun(layer, B=2, max_ctx=90200, ring=128)
+    _ingest(run, [65536, 24575])
+    worst, oc = _decode(run, 3, run.len + 3)
+    print("hca split worst", worst)
