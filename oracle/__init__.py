@@ -270,20 +270,26 @@ def n_visible(t: int, m: int) -> int:
 def layer_query(kind, m, k, W, t, q, qI, w, d1, d3, win, win_pos0=0):
     """One query of one layer over caches that already hold position t.
 
+    kind: "csa", "hca", or "swa" -- the window-only layer that the layer
+    interleave paragraph of the pages gives the final MTP block of V4-Pro's
+    stack (the sliding window and nothing else: no compressed branch; m, k,
+    d1 and d3 are then unused).
     d1: dict nope/scale/rope for blocks 0..; d3: dict idx_codes/idx_scales
     (CSA) or None; win: per-token entries for positions win_pos0.. (dict).
     Returns dict(topk, out_bf16, out_f64, lse).
     """
-    N = n_visible(t, m)
     res = {}
-    if kind == "csa":
+    if kind == "swa":
+        comp = np.arange(0)
+    elif kind == "csa":
+        N = n_visible(t, m)
         scores = index_scores(qI, w, d3["idx_codes"][:N], d3["idx_scales"][:N])
         sel = topk(scores, k)
         res["topk"] = sel
         res["scores"] = scores
         comp = sel[sel >= 0]
     else:
-        comp = np.arange(N)
+        comp = np.arange(n_visible(t, m))
     s0 = max(0, t - W + 1)
     ws = np.arange(s0, t + 1) - win_pos0
     assert ws.min() >= 0

@@ -318,6 +318,31 @@ def test_window_only_before_first_block(oracle):
         assert np.abs(r["out_f64"] - ref).max() < 1e-12
 
 
+def test_window_only_layer_is_sliding_window_attention(oracle):
+    """The window-only layer (the final MTP block of the layer interleave paragraph) at any position:
+    textbook softmax attention over the last W tokens' entries, nothing else; the window's storage
+    offset (win_pos0) does not change the result."""
+    L, W = 300, 128
+    tok = _tokens(L, False, 8)
+    win = oracle.window_entries(tok["kv"], 0)
+    rng = np.random.default_rng(21)
+    for t in (0, 1, W - 1, W, L - 1):
+        q = synth.bf16_bits((rng.standard_normal((4, 128)) * 1.3).astype(np.float32))
+        r = oracle.layer_query("swa", 1, 0, W, t, q, None, None, None, None, win)
+        assert r["n_comp"] == 0 and "topk" not in r
+        s0 = max(0, t - W + 1)
+        keys = oracle.entries_decode(win["nope"][s0:t + 1], win["scale"][s0:t + 1], win["rope"][s0:t + 1])
+        assert keys.shape[0] == min(W, t + 1)
+        qt = np.stack([oracle.rope_rotate(synth.bf16_to_f32(q[h]).astype(np.float64), t) for h in range(4)])
+        ref, rlse = _textbook(qt, keys)
+        assert np.abs(r["out_f64"] - ref).max() < 1e-12
+        assert np.abs(r["lse"] - rlse).max() < 1e-12
+        if s0 > 0:
+            part = {k: v[s0 - 1:] for k, v in win.items()}
+            r2 = oracle.layer_query("swa", 1, 0, W, t, q, None, None, None, None, part, win_pos0=s0 - 1)
+            assert np.array_equal(r2["out_bf16"], r["out_bf16"])
+
+
 def test_hca_is_csa_with_unbounded_k(oracle):
     """HCA = dense over every visible block: equal to CSA selection with k >= #blocks."""
     L = 3 * 128 + 50
