@@ -27,9 +27,13 @@ top-k of the chunk's 8192 queries, sparse attention), after an untimed pass
 of two chunks; `value` is prefill tokens/s and `roofline` the score kernel's
 MXFP4 FLOPs against the MFMA peak.
 
+With --workload v4pro61_mtp_decode_1m the step runs V4-Pro's whole layer
+schedule (61 layers: two HCA, then CSA and HCA alternating, plus the
+window-only MTP block) over B=4 sequences at 1M context.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload csa_decode_1m|hca_decode_64k|stack8_decode_256k|csa_decode_small|
-                                   csa_prefill_128k]
+                                   csa_prefill_128k|v4pro61_mtp_decode_1m]
 """
 from __future__ import annotations
 
@@ -47,7 +51,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode query-tok/s + HBM GB/s (% of peak), CSA/HCA layer at 1M ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD_BY_NAME = {"csa_decode_small": 0, "hca_decode_64k": 1, "csa_decode_1m": 2, "csa_prefill_128k": 3,
-                    "stack8_decode_256k": 4}
+                    "stack8_decode_256k": 4, "v4pro61_mtp_decode_1m": 5}
 PREFILL_METRIC = "chunked-prefill tok/s (CSA layer, 131072 tokens, chunk 8192), 1 GPU"
 MXFP4_PEAK_TFLOPS = 10100.0
 
@@ -120,13 +124,15 @@ class Layer:
         self.np, self.torch, self.lca, self.synth = np, torch, lca, synth
         self.wl, self.li, self.layer = wl, li, layer
         self.B = wl.batch
-        self.csa = layer.csa
+        self.csa, self.swa = layer.csa, layer.swa
         self.threads = threads
         self.desc = lca.make_desc(layer.kind, layer.m, layer.n_heads, layer.window, layer.idx_heads, layer.topk)
         self.max_ctx = wl.context + n_steps + layer.m
         self.dev = lca.DeviceLayer(self.desc, self.B, self.max_ctx, layer.window, max_tq=1)
-        self.streams = [synth.TokenStream(wl.wid, li, b, self.csa, wl.sigma) for b in range(self.B)]
-        self.bias = synth.biases(wl.wid, li, layer.m, self.csa)
+        from long_context_attention_18_amd import configs
+        self.stream_li = configs.stream_layer_id(wl, li)
+        self.streams = [synth.TokenStream(wl.wid, self.stream_li, b, self.csa, wl.sigma) for b in range(self.B)]
+        self.bias = {} if self.swa else synth.biases(wl.wid, li, layer.m, self.csa)
         self.bias_dev = {k: torch.from_numpy(v).cuda() for k, v in self.bias.items()}
 
     def _tokens_all(self, pos0, n):
@@ -154,24 +160,26 @@ class Layer:
             a = a.view(np.int16)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    def prefill(self, chunk):
-        torch = self.torch
-        ctx = self.wl.context
-        for pos in range(0, ctx, chunk):
-            T = min(chunk, ctx - pos)
-            tok = {k: self._upload(v) for k, v in self._tokens_all(pos, T).items()}
-            self.dev.compress(tok["kv"], tok["gate"], self.bias_dev["bias"], tok.get("ik"), tok.get("ig"),
-                              self.bias_dev.get("idx_bias"))
-            self.dev.append(tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"))
-            torch.cuda.synchronize()
+    def ingest(self, tok):
+        """T tokens of every sequence ([B][T][...] device tensors) into the cache."""
+        if self.swa:
+            self.dev.append(tok["kv"], None)
+            return
+        self.dev.compress(tok["kv"], tok["gate"], self.bias_dev["bias"], tok.get("ik"), tok.get("ig"),
+                          self.bias_dev.get("idx_bias"))
+        self.dev.append(tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"))
 
-    def make_step_inputs(self, n_steps):
+    def step_tokens(self, n_steps):
+        """The decode steps' tokens, [S][B][1][...] on the device."""
+        np = self.np
+        tok = self._tokens_all(self.wl.context, n_steps)  # [B][S][w]
+        return {k: self._upload(np.ascontiguousarray(v.transpose(1, 0, 2))[:, :, None, :]) for k, v in tok.items()}
+
+    def make_step_inputs(self, n_steps, step_tok):
         """Per-step inputs, [S][B][1][...] on the device; per-step outputs."""
         np, torch, synth = self.np, self.torch, self.synth
         ctx = self.wl.context
-        tok = self._tokens_all(ctx, n_steps)  # [B][S][w]
-        self.step_tok = {k: self._upload(np.ascontiguousarray(v.transpose(1, 0, 2))[:, :, None, :])
-                         for k, v in tok.items()}
+        self.step_tok = step_tok
         L = self.layer
         proj = synth.QueryProjector(self.wl.wid, self.li, self.wl.hidden, L.n_heads, L.idx_heads)
         pos = list(range(ctx, ctx + n_steps))
@@ -185,7 +193,7 @@ class Layer:
         self.kept = {}
         # per-step device addresses, resolved once: the timed loop then costs one library call per step
         # on the host (tensor slicing per step would make the host, not the GPU, set the pace)
-        names = ("kv", "gate", "ik", "ig") if self.csa else ("kv", "gate")
+        names = ("kv", "gate", "ik", "ig") if self.csa else (("kv",) if self.swa else ("kv", "gate"))
         self.step_ptrs = [tuple(self.step_tok[k][s].data_ptr() for k in names) +
                           tuple(self.step_q[k][s].data_ptr() for k in (("qI", "w", "q") if self.csa else ("q",)))
                           for s in range(n_steps)]
@@ -197,7 +205,8 @@ class Layer:
         self._lib = lca.lib()
         self._stream = torch.cuda.current_stream().cuda_stream
         self._cache_ref = lca.ctypes.byref(self.dev.cache)
-        self._bias = (self.bias_dev["bias"].data_ptr(), self.bias_dev["idx_bias"].data_ptr() if self.csa else None)
+        self._bias = (None, None) if self.swa else \
+            (self.bias_dev["bias"].data_ptr(), self.bias_dev["idx_bias"].data_ptr() if self.csa else None)
 
     def keep_outputs(self, steps):
         """Give these steps their own output buffers (checked against the oracle afterwards)."""
@@ -220,11 +229,19 @@ class Layer:
             if rc != 0:
                 raise self.lca.LcaError("lca_csa_step", rc)
             return
-        # HCA: compress (the library launches nothing unless a block completes), append, dense attention
-        kv, gate, q = self.step_ptrs[s]
         kept = self.kept.get(s)
         out = (kept["out"] if kept else self.out).data_ptr()
         L, c, st = self._lib, self._cache_ref, self._stream
+        if self.swa:
+            # window-only layer: append (the token's window entry), attention over the window
+            kv, q = self.step_ptrs[s]
+            rc = L.lca_swa_tail_append(c, kv, None, None, None, 1, st) or \
+                L.lca_swa_attn(c, q, 1, out, None, self.dev.ws, self.dev.ws_bytes, st)
+            if rc != 0:
+                raise self.lca.LcaError("window-only step", rc)
+            return
+        # HCA: compress (the library launches nothing unless a block completes), append, dense attention
+        kv, gate, q = self.step_ptrs[s]
         rc = L.lca_hca_compress(c, kv, gate, self._bias[0], 1, st) or L.lca_swa_tail_append(c, kv, gate, None, None,
                                                                                            1, st)
         if rc == 0:
@@ -235,6 +252,48 @@ class Layer:
                 rec(ev_score[1])
         if rc != 0:
             raise self.lca.LcaError("HCA step", rc)
+
+
+def fill_caches(layers, wl, chunk):
+    """Every layer's cache filled to the workload's context and its decode-step inputs made; layers that
+    share a token stream get each chunk generated and uploaded once."""
+    import torch
+    groups = {}
+    for L in layers:
+        groups.setdefault((L.stream_li, L.csa), []).append(L)
+    ctx = wl.context
+    t0 = time.perf_counter()
+    for g, Ls in enumerate(groups.values()):
+        for pos in range(0, ctx, chunk):
+            T = min(chunk, ctx - pos)
+            tok = {k: Ls[0]._upload(v) for k, v in Ls[0]._tokens_all(pos, T).items()}
+            for L in Ls:
+                L.ingest(tok)
+            torch.cuda.synchronize()
+            del tok
+            if len(groups) < len(layers) and (pos // chunk) % 16 == 15:
+                log(f"stream {g + 1}/{len(groups)}: {pos + T} tokens into {len(Ls)} layer(s), "
+                    f"{time.perf_counter() - t0:.0f} s")
+    return groups
+
+
+def layers_label(layer_list):
+    """The layer kinds in order, runs of a repeated pair written once with a count."""
+    kinds = [l.kind.upper() for l in layer_list]
+    if len(kinds) <= 8:
+        return ",".join(kinds)
+    i, parts = 0, []
+    while i < len(kinds):
+        n = 1
+        while i + 2 * (n + 1) <= len(kinds) and kinds[i:i + 2] == kinds[i + 2 * n:i + 2 * n + 2]:
+            n += 1
+        if n > 1 and kinds[i] != kinds[i + 1] and (i == 0 or kinds[i - 1] != kinds[i]):
+            parts.append(f"({kinds[i]},{kinds[i + 1]})x{n}")
+            i += 2 * n
+        else:
+            parts.append(kinds[i])
+            i += 1
+    return ",".join(parts) + f" [{len(kinds)} layers]"
 
 
 def score_bytes(layer, B, t):
@@ -283,7 +342,7 @@ def oracle_sample(layers, wl, first_step, n_queries, threads):
     with cf.ThreadPoolExecutor(threads) as ex:
         parts = list(ex.map(lambda p: st.tokens(p, min(sub, upto - p)), range(0, upto, sub)))
     tok = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
-    nb = upto // lay.m
+    nb = lay.blocks(upto)
     bl = max(1, (nb + threads - 1) // threads)
 
     def comp(j0):
@@ -291,9 +350,11 @@ def oracle_sample(layers, wl, first_step, n_queries, threads):
         return O.compress(lay.m, tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"), 0, L.bias["bias"],
                           L.bias.get("idx_bias"), j0, j1)
 
-    with cf.ThreadPoolExecutor(threads) as ex:
-        cparts = list(ex.map(comp, range(0, nb, bl)))
-    d1 = {k: np.concatenate([p[k] for p in cparts]) for k in cparts[0]}
+    d1 = None
+    if nb:
+        with cf.ThreadPoolExecutor(threads) as ex:
+            cparts = list(ex.map(comp, range(0, nb, bl)))
+        d1 = {k: np.concatenate([p[k] for p in cparts]) for k in cparts[0]}
     lo = max(0, wl.context + first_step - lay.window - 1)
     win = O.window_entries(tok["kv"][lo:upto], lo)
     build_s = time.perf_counter() - t0
@@ -472,9 +533,11 @@ def main():
     t0 = time.perf_counter()
     layers = [Layer(wl, li, layer, S, args.threads) for li, layer in enumerate(wl.layers)]
     chunk = max(4096, min(65536, (1 << 26) // (wl.batch * 768)))
-    for L in layers:
-        L.prefill(chunk)
-        L.make_step_inputs(S)
+    groups = fill_caches(layers, wl, chunk)
+    for Ls in groups.values():
+        step_tok = Ls[0].step_tokens(S)
+        for L in Ls:
+            L.make_step_inputs(S, step_tok)
     n_check = 0 if args.no_cpu_baseline else max(1, args.oracle_queries)
     layers[0].keep_outputs(range(W, W + n_check))
     torch.cuda.synchronize()
@@ -496,8 +559,13 @@ def main():
 
     torch.cuda.synchronize()
     if True:
+        h0 = time.perf_counter()
         run_steps(range(W), False)
+        warm_host_us = (time.perf_counter() - h0) * 1e6 / max(1, W)
         torch.cuda.synchronize()
+        # the host's own enqueue cost per step (warm-up, no spin ahead of it): the GPU never waits on the
+        # host as long as this stays below the GPU's time per step
+        log(f"host enqueue per step in the warm-up: {warm_host_us:.1f} us")
         # keep the GPU busy while the host enqueues the whole timed region, so no step waits on the host
         # (about 0.25 ms of spin per step and layer: several times the host's enqueue cost)
         torch.cuda._sleep(int(6.0e5 * max(20, K) * len(layers)))
@@ -509,11 +577,17 @@ def main():
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - h0) * 1e3
         log(f"host enqueue of the timed region: {enq_ms:.2f} ms")
+        # a long region fills the device queue: the host then blocks until the spin ends and enqueues
+        # the rest while the GPU runs, which costs nothing as long as it enqueues faster than the GPU runs
         if enq_ms > total_spin_ms_estimate(K, len(layers)):
-            log("warning: the host enqueue outlasted the spin; the GPU may have waited on the host")
+            log("the host enqueue outlasted the spin (device queue full); the GPU keeps the pace as long "
+                "as the warm-up's host time per step stays below the GPU's")
 
     total_ms = hev.elapsed_ms(ev_begin, ev_end)
     ms_per_step = total_ms / K
+    if warm_host_us > 0.9 * ms_per_step * 1e3:
+        log(f"warning: host enqueue per step ({warm_host_us:.0f} us) is close to or above the GPU's "
+            f"({ms_per_step * 1e3:.0f} us): the GPU may have waited on the host")
     if args.no_step_events:
         log(f"timed {K} steps without per-step events: {total_ms:.3f} ms; {ms_per_step * 1e3:.2f} us/step")
         return 0
@@ -550,7 +624,7 @@ def main():
         "dtype": "mxfp4+bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context,
-                   "layers": ",".join(l.kind.upper() for l in wl.layers),
+                   "layers": layers_label(wl.layers),
                    "n_heads": wl.layers[0].n_heads, "window": wl.layers[0].window,
                    "topk": max((l.topk for l in wl.layers), default=0),
                    "idx_heads": max((l.idx_heads for l in wl.layers), default=0), "launch": mode},
@@ -579,9 +653,10 @@ def main():
         parity["ok"] = parity["topk_exact"] and parity["max_rel_l2"] <= 1e-2 and parity["max_abs"] <= 2e-2
         result["cpu_baseline"] = {
             "value": round(len(res) / dec_s, 4), "unit": "query-tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(res)} decode queries of sequence 0 of layer 0 at context {wl.context}-"
-                      f"{wl.context + len(res) - 1} ({nb} compressed blocks) through the plain C oracle "
-                      f"(scores, top-k, attention), single thread, {dec_s:.2f} s; its cache build for that "
+            "sample": f"{len(res)} decode queries of sequence 0 of layer 0 ({L.layer.kind.upper()}) at context "
+                      f"{wl.context}-{wl.context + len(res) - 1} ({nb} compressed blocks) through the plain C "
+                      f"oracle ({'scores, top-k, ' if L.csa else ''}attention), single thread, {dec_s:.2f} s; "
+                      f"its cache build for that "
                       f"sequence ({build_s:.1f} s on {args.threads} threads) is not counted"}
         result["parity_sample"] = parity
         log(f"oracle: {dec_s:.2f} s for {len(res)} queries; parity {parity}")

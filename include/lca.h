@@ -57,17 +57,22 @@ typedef int32_t lca_status;
 
 #define LCA_KIND_CSA 0
 #define LCA_KIND_HCA 1
+/* Window-only layer: the sliding window and nothing else (the layer
+ * interleave paragraph: the final MTP block of V4-Pro's stack runs only the
+ * sliding window). Its cache holds the window state alone. */
+#define LCA_KIND_SWA 2
 
 #define LCA_HEAD_DIM 128 /* shared KV head: 64 nope + 64 RoPE dims */
 #define LCA_NOPE_DIM 64
 #define LCA_ROPE_DIM 64
 #define LCA_IDX_DIM 64   /* lightning-indexer head dim */
 
-/* One attention layer. Supported: kind CSA or HCA; 1 <= m <= 128;
- * 1 <= n_heads <= 64; 1 <= window <= 4096; CSA: 1 <= idx_heads <= 8 and
- * 1 <= topk <= 2048 (both ignored for HCA). */
+/* One attention layer. Supported: kind CSA, HCA or SWA; 1 <= n_heads <= 64;
+ * 1 <= window <= 4096; CSA and HCA: 1 <= m <= 128; CSA: 1 <= idx_heads <= 8
+ * and 1 <= topk <= 2048 (both ignored for HCA and SWA; m ignored for SWA:
+ * the bound cache stores m = 1, idx_heads = topk = 0). */
 typedef struct lca_layer_desc {
-  int32_t kind;      /* LCA_KIND_CSA or LCA_KIND_HCA */
+  int32_t kind;      /* LCA_KIND_CSA, LCA_KIND_HCA or LCA_KIND_SWA */
   int32_t m;         /* tokens pooled into one entry (CSA 4, HCA 128 on the pages) */
   int32_t n_heads;   /* query heads, dim 128, all sharing the one KV head */
   int32_t window;    /* W: sliding-window length in tokens, the query included */
@@ -82,10 +87,11 @@ typedef struct lca_cache {
   int32_t batch;      /* B */
   int32_t ring;       /* R: window-state slots per sequence (token s lives in slot s mod R) */
   int64_t max_ctx;    /* token capacity per sequence */
-  int64_t max_blocks; /* max_ctx / m */
+  int64_t max_blocks; /* max_ctx / m (0 for SWA) */
   int64_t len;        /* tokens appended so far (same for every sequence) */
   int64_t pending;    /* tokens compressed but not yet appended (0 or T) */
-  /* compressed cache (D1): [B][max_blocks][64] u8, [B][max_blocks] f32, [B][max_blocks][64] bf16 */
+  /* compressed cache (D1): [B][max_blocks][64] u8, [B][max_blocks] f32, [B][max_blocks][64] bf16;
+   * NULL for SWA */
   uint8_t* blk_codes_dev;
   float* blk_scale_dev;
   uint16_t* blk_rope_dev;
@@ -97,7 +103,7 @@ typedef struct lca_cache {
   float* win_scale_dev;
   uint16_t* win_rope_dev;
   /* uncompressed tail: [B][m][tail_width] bf16, token p in slot p mod m;
-   * tail_width = 128 (kv) + 128 (gate) [+ 64 (ik) + 64 (ig) for CSA] */
+   * tail_width = 128 (kv) + 128 (gate) [+ 64 (ik) + 64 (ig) for CSA]; NULL and 0 for SWA */
   uint16_t* tail_dev;
   int32_t tail_width;
   int32_t reserved0;
@@ -109,8 +115,8 @@ typedef struct lca_cache {
 
 /* Bytes of device memory lca_cache_bind() carves for one layer:
  * D1 (196 B/block) + D3 (34 B/block, CSA) + D2 (196 B/slot) + tail + the
- * 256-B RoPE frequency table, each array 256-byte aligned. max_blocks = max_ctx / m. Returns 0 for an
- * invalid descriptor or size. */
+ * 256-B RoPE frequency table, each array 256-byte aligned. max_blocks = max_ctx / m; SWA: D2 and the
+ * table only. Returns 0 for an invalid descriptor or size. */
 size_t lca_cache_bytes(const lca_layer_desc* desc, int32_t batch, int64_t max_ctx, int32_t ring);
 
 /* Carve `base_dev` (>= lca_cache_bytes() bytes, 256-byte aligned) into the
@@ -173,7 +179,8 @@ lca_status lca_hca_compress(lca_cache* cache, const uint16_t* kv_dev, const uint
  * keeps the BF16 inputs of the tokens of the not yet complete block in the
  * tail, and advances len by T. Same input layout as the compressor; ik/ig
  * are NULL for HCA. Requires the preceding compress of exactly these T
- * tokens. */
+ * tokens. SWA: no compressor and no tail; only kv is read (gate, ik, ig may
+ * be NULL) and no compress precedes. */
 lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
                                const uint16_t* ik_dev, const uint16_t* ig_dev, int32_t T, void* stream);
 
@@ -219,6 +226,14 @@ lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const in
  * over every visible D1 entry j < (t+1)/m plus the window. */
 lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev,
                               float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Window-only attention of an SWA cache (layer interleave paragraph: the
+ * final MTP block runs only the sliding window): per query t and head h, one
+ * softmax over the window entries of positions max(0, t-W+1) .. t; logits,
+ * K = V and outputs as lca_csa_sparse_attn. ws_dev may be NULL (W <= 768
+ * never splits a query's keys). */
+lca_status lca_swa_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev, float* lse_dev,
+                        void* ws_dev, size_t ws_bytes, void* stream);
 
 /* The CSA query path with the selection and the attention in one launch
  * (CSA paragraph: top-k compressed blocks per query; Figure 3: their

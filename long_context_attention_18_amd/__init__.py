@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(HERE, "liblca.so")
 
 LCA_KIND_CSA = 0
 LCA_KIND_HCA = 1
+LCA_KIND_SWA = 2
+_KINDS = {"csa": LCA_KIND_CSA, "hca": LCA_KIND_HCA, "swa": LCA_KIND_SWA}
 
 _STATUS = {0: "LCA_OK", -1: "LCA_ERR_NULL", -2: "LCA_ERR_SHAPE", -3: "LCA_ERR_UNSUPPORTED", -4: "LCA_ERR_CAPACITY",
            -5: "LCA_ERR_ORDER", -6: "LCA_ERR_WORKSPACE", -7: "LCA_ERR_LAUNCH"}
@@ -68,6 +70,7 @@ _SIGNATURES = {
     "lca_csa_topk_select": (_I32, [_CP, _I32, _VP, _VP, _SZ, _VP]),
     "lca_csa_sparse_attn": (_I32, [_CP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "lca_hca_dense_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_swa_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_attend": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
@@ -119,7 +122,8 @@ def _check(fn, status):
 
 
 def make_desc(kind: str, m: int, n_heads: int, window: int = 128, idx_heads: int = 0, topk: int = 0):
-    return lca_layer_desc(LCA_KIND_CSA if kind == "csa" else LCA_KIND_HCA, m, n_heads, window, idx_heads, topk)
+    """kind: "csa", "hca" or "swa" (window-only; m is then ignored)."""
+    return lca_layer_desc(_KINDS[kind], m, n_heads, window, idx_heads, topk)
 
 
 # ----------------------------------------------------------------- entry points
@@ -184,6 +188,11 @@ def lca_hca_dense_attn(cache, q, Tq, out, lse, ws, ws_bytes, stream=None):
                                                            _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def lca_swa_attn(cache, q, Tq, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_swa_attn", lib().lca_swa_attn(ctypes.byref(cache), _ptr(q), Tq, _ptr(out), _ptr(lse), _ptr(ws),
+                                               ws_bytes, _stream(stream)))
+
+
 def lca_csa_attend(cache, qI, w, q, Tq, topk, out, lse, ws, ws_bytes, stream=None):
     _check("lca_csa_attend", lib().lca_csa_attend(ctypes.byref(cache), _ptr(qI), _ptr(w), _ptr(q), Tq, _ptr(topk),
                                                    _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
@@ -245,8 +254,14 @@ class DeviceLayer:
     def csa(self):
         return self.desc.kind == LCA_KIND_CSA
 
+    @property
+    def swa(self):
+        return self.desc.kind == LCA_KIND_SWA
+
     def compress(self, kv, gate, bias, ik=None, ig=None, idx_bias=None, stream=None):
         T = kv.shape[1]
+        if self.swa:
+            raise ValueError("a window-only layer has no compressor: call append() alone")
         if self.csa:
             lca_csa_compress(self.cache, kv, gate, ik, ig, bias, idx_bias, T, stream)
         else:
@@ -269,6 +284,9 @@ class DeviceLayer:
 
     def dense_attn(self, q, out, lse=None, stream=None):
         lca_hca_dense_attn(self.cache, q, q.shape[1], out, lse, self.ws, self.ws_bytes, stream)
+
+    def swa_attn(self, q, out, lse=None, stream=None):
+        lca_swa_attn(self.cache, q, q.shape[1], out, lse, self.ws, self.ws_bytes, stream)
 
     def attend(self, qI, w, q, out, lse=None, topk=None, stream=None):
         lca_csa_attend(self.cache, qI, w, q, q.shape[1], topk, out, lse, self.ws, self.ws_bytes, stream)
@@ -309,13 +327,14 @@ class DeviceLayer:
             return self.mem[off:off + n * esz].view(dtype).view(*shape)
 
         v = {
-            "blk_codes": view(c.blk_codes_dev, B * NB * 64, torch.uint8, (B, NB, 64)),
-            "blk_scale": view(c.blk_scale_dev, B * NB, torch.float32, (B, NB)),
-            "blk_rope": view(c.blk_rope_dev, B * NB * 64, torch.int16, (B, NB, 64)),
             "win_codes": view(c.win_codes_dev, B * R * 64, torch.uint8, (B, R, 64)),
             "win_scale": view(c.win_scale_dev, B * R, torch.float32, (B, R)),
             "win_rope": view(c.win_rope_dev, B * R * 64, torch.int16, (B, R, 64)),
         }
+        if not self.swa:
+            v["blk_codes"] = view(c.blk_codes_dev, B * NB * 64, torch.uint8, (B, NB, 64))
+            v["blk_scale"] = view(c.blk_scale_dev, B * NB, torch.float32, (B, NB))
+            v["blk_rope"] = view(c.blk_rope_dev, B * NB * 64, torch.int16, (B, NB, 64))
         if self.csa:
             v["idx_codes"] = view(c.idx_codes_dev, B * NB * 32, torch.uint8, (B, NB, 32))
             v["idx_scale"] = view(c.idx_scale_dev, B * NB * 2, torch.uint8, (B, NB, 2))

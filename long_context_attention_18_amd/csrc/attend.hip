@@ -269,7 +269,8 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   const int hg = blockIdx.x % hgs, split = blockIdx.x / hgs, q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
   const int64_t t = a.len - a.Tq + tq;
-  const int64_t N = (t + 1) / a.m;
+  // visible blocks; max_blocks bounds them (0 for the window-only layer, which has no compressed stream)
+  const int64_t N = min((t + 1) / a.m, a.max_blocks);
   const bool do_select = MODE == kAttendSelect && N > a.k;
 
   Keys K;

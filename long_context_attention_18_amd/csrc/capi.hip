@@ -19,8 +19,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool desc_ok(const lca_layer_desc* d) {
   if (!d) return false;
-  if (d->kind != LCA_KIND_CSA && d->kind != LCA_KIND_HCA) return false;
-  if (d->m < 1 || d->m > 128) return false;
+  if (d->kind != LCA_KIND_CSA && d->kind != LCA_KIND_HCA && d->kind != LCA_KIND_SWA) return false;
+  if (d->kind != LCA_KIND_SWA && (d->m < 1 || d->m > 128)) return false;
   if (d->n_heads < 1 || d->n_heads > 64) return false;
   if (d->window < 1 || d->window > 4096) return false;
   if (d->kind == LCA_KIND_CSA) {
@@ -30,7 +30,15 @@ bool desc_ok(const lca_layer_desc* d) {
   return true;
 }
 
-int32_t tail_width(const lca_layer_desc* d) { return d->kind == LCA_KIND_CSA ? 384 : 256; }
+int32_t tail_width(const lca_layer_desc* d) {
+  return d->kind == LCA_KIND_CSA ? 384 : (d->kind == LCA_KIND_HCA ? 256 : 0);
+}
+
+// tokens per compressed entry; the window-only layer has no compressed stream (no blocks at any m)
+int64_t pool_m(const lca_layer_desc* d) { return d->kind == LCA_KIND_SWA ? 1 : d->m; }
+int64_t n_blocks_max(const lca_layer_desc* d, int64_t max_ctx) {
+  return d->kind == LCA_KIND_SWA ? 0 : max_ctx / d->m;
+}
 
 struct Layout {
   size_t blk_codes, blk_scale, blk_rope, idx_codes, idx_scale, win_codes, win_scale, win_rope, tail, inv_freq, total;
@@ -38,7 +46,7 @@ struct Layout {
 
 Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring) {
   Layout L{};
-  const size_t nb = (size_t)B * (size_t)(max_ctx / d->m);
+  const size_t nb = (size_t)B * (size_t)n_blocks_max(d, max_ctx);
   const size_t nw = (size_t)B * (size_t)ring;
   size_t off = 0;
   L.blk_codes = off; off = align_up(off + nb * 64);
@@ -51,7 +59,7 @@ Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
   L.win_codes = off; off = align_up(off + nw * 64);
   L.win_scale = off; off = align_up(off + nw * 4);
   L.win_rope = off; off = align_up(off + nw * 128);
-  L.tail = off; off = align_up(off + (size_t)B * d->m * tail_width(d) * 2);
+  L.tail = off; off = align_up(off + (size_t)B * pool_m(d) * tail_width(d) * 2);
   L.inv_freq = off; off = align_up(off + 32 * sizeof(double));
   L.total = off;
   return L;
@@ -59,8 +67,8 @@ Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
 
 bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring) {
   if (B < 1 || B > 65535) return false;
-  if (max_ctx < d->m || max_ctx > ((int64_t)1 << 32)) return false;
-  if (max_ctx / d->m > (int64_t)2048 * kScoreChunk) return false;  // score chunks per query fit the scan's LDS
+  if (max_ctx < pool_m(d) || max_ctx > ((int64_t)1 << 32)) return false;
+  if (n_blocks_max(d, max_ctx) > (int64_t)2048 * kScoreChunk) return false;  // score chunks per query fit the scan's LDS
   if (ring < d->window || ring > (1 << 24)) return false;
   return true;
 }
@@ -76,7 +84,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t max_ctx) {
   WsLayout W{};
-  const int64_t max_blocks = max_ctx / d->m;
+  const int64_t max_blocks = n_blocks_max(d, max_ctx);
   const size_t nq = (size_t)B * (size_t)max_tq;
   W.cnt = 0;
   size_t off = kAttendCounterBytes;
@@ -114,7 +122,7 @@ void attend_workspace(AttendArgs* args, const lca_cache* c, int32_t Tq, void* ws
   if (!ws_dev) return;
   WsLayout W = ws_layout(&c->desc, c->batch, Tq, c->max_ctx);
   if (ws_bytes < W.total) return;
-  const int64_t N_last = c->len / c->desc.m;  // visible blocks of the last query (the most)
+  const int64_t N_last = c->max_blocks > 0 ? c->len / c->desc.m : 0;  // visible blocks of the last query (the most)
   const int64_t n_list = c->desc.kind == LCA_KIND_CSA ? (N_last < c->desc.topk ? N_last : c->desc.topk) : N_last;
   const int64_t n_win = c->len < c->desc.window ? c->len : c->desc.window;
   args->splits = attend_splits(c->batch * Tq, c->desc.n_heads, n_list + n_win);
@@ -125,7 +133,9 @@ void attend_workspace(AttendArgs* args, const lca_cache* c, int32_t Tq, void* ws
 lca_status launch_status(hipError_t e) { return e == hipSuccess ? LCA_OK : LCA_ERR_LAUNCH; }
 
 bool cache_ok(const lca_cache* c) {
-  return c && desc_ok(&c->desc) && c->blk_codes_dev && c->win_codes_dev && c->tail_dev;
+  if (!c || !desc_ok(&c->desc) || !c->win_codes_dev || !c->win_scale_dev || !c->win_rope_dev) return false;
+  if (c->desc.kind == LCA_KIND_SWA) return c->max_blocks == 0 && c->desc.m == 1;
+  return c->blk_codes_dev && c->tail_dev;
 }
 
 IngestArgs ingest_args(lca_cache* c, const uint16_t* kv, const uint16_t* gate, const uint16_t* ik,
@@ -158,7 +168,7 @@ IngestArgs ingest_args(lca_cache* c, const uint16_t* kv, const uint16_t* gate, c
 lca_status compress_impl(lca_cache* c, bool csa, const uint16_t* kv, const uint16_t* gate, const uint16_t* ik,
                          const uint16_t* ig, const float* bias, const float* idx_bias, int32_t T, void* stream) {
   if (!cache_ok(c) || !kv || !gate || !bias) return LCA_ERR_NULL;
-  if (csa != (c->desc.kind == LCA_KIND_CSA)) return LCA_ERR_UNSUPPORTED;
+  if (csa ? c->desc.kind != LCA_KIND_CSA : c->desc.kind != LCA_KIND_HCA) return LCA_ERR_UNSUPPORTED;
   if (csa && (!ik || !ig || !idx_bias || !c->idx_codes_dev || !c->idx_scale_dev)) return LCA_ERR_NULL;
   if (T < 1) return LCA_ERR_SHAPE;
   if (c->pending != 0) return LCA_ERR_ORDER;
@@ -208,18 +218,23 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
   if (bytes < L.total) return LCA_ERR_CAPACITY;
   std::memset(cache, 0, sizeof(*cache));
   cache->desc = *desc;
-  if (desc->kind == LCA_KIND_HCA) {
+  if (desc->kind != LCA_KIND_CSA) {
     cache->desc.idx_heads = 0;
     cache->desc.topk = 0;
   }
+  const bool swa = desc->kind == LCA_KIND_SWA;
+  if (swa) cache->desc.m = 1;
   cache->batch = batch;
   cache->ring = ring;
   cache->max_ctx = max_ctx;
-  cache->max_blocks = max_ctx / desc->m;
+  cache->max_blocks = n_blocks_max(desc, max_ctx);
   char* base = (char*)base_dev;
-  cache->blk_codes_dev = (uint8_t*)(base + L.blk_codes);
-  cache->blk_scale_dev = (float*)(base + L.blk_scale);
-  cache->blk_rope_dev = (uint16_t*)(base + L.blk_rope);
+  if (!swa) {
+    cache->blk_codes_dev = (uint8_t*)(base + L.blk_codes);
+    cache->blk_scale_dev = (float*)(base + L.blk_scale);
+    cache->blk_rope_dev = (uint16_t*)(base + L.blk_rope);
+    cache->tail_dev = (uint16_t*)(base + L.tail);
+  }
   if (desc->kind == LCA_KIND_CSA) {
     cache->idx_codes_dev = (uint8_t*)(base + L.idx_codes);
     cache->idx_scale_dev = (uint8_t*)(base + L.idx_scale);
@@ -227,7 +242,6 @@ lca_status lca_cache_bind(const lca_layer_desc* desc, lca_cache* cache, void* ba
   cache->win_codes_dev = (uint8_t*)(base + L.win_codes);
   cache->win_scale_dev = (float*)(base + L.win_scale);
   cache->win_rope_dev = (uint16_t*)(base + L.win_rope);
-  cache->tail_dev = (uint16_t*)(base + L.tail);
   cache->tail_width = tail_width(desc);
   for (int i = 0; i < 32; ++i) cache->rope_inv_freq[i] = std::pow(10000.0, -(double)(2 * i) / 64.0);
   cache->rope_inv_freq_dev = (double*)(base + L.inv_freq);
@@ -244,7 +258,7 @@ size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, in
 }
 
 size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t max_tq, int64_t max_ctx) {
-  if (!desc_ok(desc) || batch < 1 || max_tq < 1 || max_ctx < desc->m) return 0;
+  if (!desc_ok(desc) || batch < 1 || max_tq < 1 || max_ctx < pool_m(desc)) return 0;
   return ws_layout(desc, batch, max_tq, max_ctx).total;
 }
 
@@ -267,11 +281,12 @@ lca_status lca_hca_compress(lca_cache* cache, const uint16_t* kv_dev, const uint
 
 lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
                                const uint16_t* ik_dev, const uint16_t* ig_dev, int32_t T, void* stream) {
-  if (!cache_ok(cache) || !kv_dev || !gate_dev) return LCA_ERR_NULL;
-  const bool csa = cache->desc.kind == LCA_KIND_CSA;
+  if (!cache_ok(cache) || !kv_dev) return LCA_ERR_NULL;
+  const bool csa = cache->desc.kind == LCA_KIND_CSA, swa = cache->desc.kind == LCA_KIND_SWA;
+  if (!swa && !gate_dev) return LCA_ERR_NULL;
   if (csa && (!ik_dev || !ig_dev)) return LCA_ERR_NULL;
   if (T < 1) return LCA_ERR_SHAPE;
-  if (cache->pending != T) return LCA_ERR_ORDER;
+  if (cache->pending != (swa ? 0 : T)) return LCA_ERR_ORDER;  // the window-only layer has no compressor
   if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
   IngestArgs a = ingest_args(cache, kv_dev, gate_dev, csa ? ik_dev : nullptr, csa ? ig_dev : nullptr, T);
   const int64_t end = cache->len + T;
@@ -280,7 +295,7 @@ lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const u
   a.n_win = (int32_t)(end - win_first);
   int64_t tail_first = (end / cache->desc.m) * cache->desc.m;
   if (tail_first < cache->len) tail_first = cache->len;
-  const int32_t n_tail = (int32_t)(end - tail_first);
+  const int32_t n_tail = swa ? 0 : (int32_t)(end - tail_first);
   hipError_t e = launch_append(a, csa, n_tail, (hipStream_t)stream);
   if (e != hipSuccess) return LCA_ERR_LAUNCH;
   cache->len = end;
@@ -366,19 +381,23 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
 
 namespace {
 
-lca_status attn_args(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
+// kind: the layer kind the entry point serves; dense = every visible block (HCA) or none (SWA: no blocks)
+lca_status attn_args(lca_cache* cache, int32_t kind, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
                      uint16_t* out_dev, float* lse_dev, AttnArgs* out) {
   if (!cache_ok(cache) || !q_dev || !out_dev) return LCA_ERR_NULL;
-  if (dense != (cache->desc.kind == LCA_KIND_HCA)) return LCA_ERR_UNSUPPORTED;
+  if (cache->desc.kind != kind) return LCA_ERR_UNSUPPORTED;
+  const bool dense = kind != LCA_KIND_CSA;
   if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
   if (cache->pending != 0) return LCA_ERR_ORDER;
   if ((int64_t)Tq + cache->desc.window - 1 > cache->ring) return LCA_ERR_CAPACITY;
   AttnArgs a{};
   a.q = q_dev;
   a.topk = dense ? nullptr : topk_dev;
-  a.blk_codes = cache->blk_codes_dev;
-  a.blk_scale = cache->blk_scale_dev;
-  a.blk_rope = cache->blk_rope_dev;
+  // SWA: max_blocks = 0, so no query sees a block; the block arrays alias the window's, never read
+  const bool swa = kind == LCA_KIND_SWA;
+  a.blk_codes = swa ? cache->win_codes_dev : cache->blk_codes_dev;
+  a.blk_scale = swa ? cache->win_scale_dev : cache->blk_scale_dev;
+  a.blk_rope = swa ? cache->win_rope_dev : cache->blk_rope_dev;
   a.win_codes = cache->win_codes_dev;
   a.win_scale = cache->win_scale_dev;
   a.win_rope = cache->win_rope_dev;
@@ -400,12 +419,13 @@ lca_status attn_args(lca_cache* cache, bool dense, const uint16_t* q_dev, const 
 
 // Few queries: a workgroup per (query, 16 heads) over all keys (attend.hip). Many queries: a
 // workgroup per query and all heads (attention.hip).
-lca_status attention_impl(lca_cache* cache, bool dense, const uint16_t* q_dev, const int32_t* topk_dev,
+lca_status attention_impl(lca_cache* cache, int32_t kind, const uint16_t* q_dev, const int32_t* topk_dev,
                           int32_t Tq, uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes,
                           void* stream) {
+  const bool dense = kind != LCA_KIND_CSA;
   if (!dense && !topk_dev) return LCA_ERR_NULL;
   AttnArgs a;
-  lca_status st = attn_args(cache, dense, q_dev, topk_dev, Tq, out_dev, lse_dev, &a);
+  lca_status st = attn_args(cache, kind, q_dev, topk_dev, Tq, out_dev, lse_dev, &a);
   if (st != LCA_OK) return st;
   const int32_t nq = cache->batch * Tq;
   hipStream_t s = (hipStream_t)stream;
@@ -424,7 +444,7 @@ lca_status topk_attn_impl(lca_cache* cache, const uint16_t* qI_dev, const float*
   AttendArgs args{};
   lca_status st = score_args(cache, qI_dev, w_dev, score, Tq, topk_dev, false, ws_dev, ws_bytes, &args.s);
   if (st != LCA_OK) return st;
-  st = attn_args(cache, false, q_dev, nullptr, Tq, out_dev, lse_dev, &args.t);
+  st = attn_args(cache, LCA_KIND_CSA, q_dev, nullptr, Tq, out_dev, lse_dev, &args.t);
   if (st != LCA_OK) return st;
   attend_workspace(&args, cache, Tq, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
@@ -443,12 +463,17 @@ extern "C" {
 
 lca_status lca_csa_sparse_attn(lca_cache* cache, const uint16_t* q_dev, const int32_t* topk_dev, int32_t Tq,
                                uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
-  return attention_impl(cache, false, q_dev, topk_dev, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+  return attention_impl(cache, LCA_KIND_CSA, q_dev, topk_dev, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
 }
 
 lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev,
                               float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
-  return attention_impl(cache, true, q_dev, nullptr, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+  return attention_impl(cache, LCA_KIND_HCA, q_dev, nullptr, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+}
+
+lca_status lca_swa_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev, float* lse_dev,
+                        void* ws_dev, size_t ws_bytes, void* stream) {
+  return attention_impl(cache, LCA_KIND_SWA, q_dev, nullptr, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
 }
 
 lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev,
@@ -474,7 +499,7 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
   AttendArgs args{};
   lca_status st = score_args(&after, qI_dev, w_dev, true, T, topk_dev, false, ws_dev, ws_bytes, &args.s);
   if (st != LCA_OK) return st;
-  st = attn_args(&after, false, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
+  st = attn_args(&after, LCA_KIND_CSA, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
   if (st != LCA_OK) return st;
   attend_workspace(&args, &after, T, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;

@@ -59,11 +59,12 @@ class LayerRun:
         self.transform, self.qtransform = transform, qtransform
         self.layer, self.B = layer, B
         self.csa = layer.csa
+        self.swa = layer.kind == "swa"
         self.m = layer.m
         self.desc = lca.make_desc(layer.kind, layer.m, layer.n_heads, layer.window, layer.idx_heads, layer.topk)
         self.dev = lca.DeviceLayer(self.desc, B, max_ctx, ring, max_tq=max_tq)
         self.streams = [synth.TokenStream(workload, layer_id, b, self.csa, sigma) for b in range(B)]
-        self.bias = synth.biases(workload, layer_id, layer.m, self.csa)
+        self.bias = {} if self.swa else synth.biases(workload, layer_id, layer.m, self.csa)
         self.bias_dev = {k: to_dev(v) for k, v in self.bias.items()}
         self.proj = synth.QueryProjector(workload, layer_id, hidden, layer.n_heads, layer.idx_heads)
         self.len = 0
@@ -76,7 +77,9 @@ class LayerRun:
         parts = [self.tokens(b, self.len, T) for b in range(self.B)]
         tok = {k: np.stack([p[k] for p in parts]) for k in parts[0]}
         d = {k: to_dev(v) for k, v in tok.items()}
-        if self.csa:
+        if self.swa:
+            self.dev.append(d["kv"], None)
+        elif self.csa:
             self.dev.compress(d["kv"], d["gate"], self.bias_dev["bias"], d["ik"], d["ig"], self.bias_dev["idx_bias"])
             self.dev.append(d["kv"], d["gate"], d["ik"], d["ig"])
         else:
@@ -114,6 +117,8 @@ class LayerRun:
                 self.last_scores = self.dev.index_scores(Tq)
             if not fused:
                 self.dev.sparse_attn(to_dev(qin["q"]), topk, out, lse)
+        elif self.swa:
+            self.dev.swa_attn(to_dev(qin["q"]), out, lse)
         else:
             self.dev.dense_attn(to_dev(qin["q"]), out, lse)
         torch.cuda.synchronize()
@@ -140,33 +145,43 @@ class LayerRun:
     # ---------------------------------------------------------------- oracle side
     def oracle_caches(self, b, upto):
         tok = self.tokens(b, 0, upto)
+        if self.swa:
+            return None, O.window_entries(tok["kv"], 0)
         d1 = O.compress(self.m, tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"), 0, self.bias["bias"],
                         self.bias.get("idx_bias"), 0, upto // self.m)
         win = O.window_entries(tok["kv"], 0)
         return d1, win
 
 
+def _compare_blocks(run, v, b, d1, nb, report):
+    """Compressed entries (and CSA indexer keys) of sequence b: bit-exact, RoPE dims within 1 ulp."""
+    codes = from_dev(v["blk_codes"][b, :nb])
+    scale = from_dev(v["blk_scale"][b, :nb])
+    rope = from_dev(v["blk_rope"][b, :nb], np.uint16)
+    assert np.array_equal(codes, d1["nope"][:nb]), f"seq {b}: FP8 codes differ at {np.argwhere(codes != d1['nope'][:nb])[:5]}"
+    assert np.array_equal(scale.view(np.uint32), d1["scale"][:nb].view(np.uint32)), f"seq {b}: scales differ"
+    ud = bf16_ulp_diff(rope, d1["rope"][:nb])
+    assert ud.max(initial=0) <= 1, f"seq {b}: RoPE dims differ by {ud.max()} ulp"
+    report["rope_ulp1"] += int((ud > 0).sum())
+    report["rope_total"] += ud.size
+    if run.csa:
+        ic = unpack_nibbles(from_dev(v["idx_codes"][b, :nb]))
+        isc = from_dev(v["idx_scale"][b, :nb])
+        assert np.array_equal(ic, d1["idx_codes"][:nb]), f"seq {b}: FP4 codes differ at {np.argwhere(ic != d1['idx_codes'][:nb])[:5]}"
+        assert np.array_equal(isc, d1["idx_scales"][:nb]), f"seq {b}: E8M0 bytes differ"
+
+
 def compare_cache(run: LayerRun, oracle_by_seq, check_window=True):
     """Bit-exact block entries / indexer keys; window slots for the last R positions."""
     v = run.dev.views()
-    nb = run.len // run.m
+    nb = 0 if run.swa else run.len // run.m
     report = {"rope_ulp1": 0, "rope_total": 0}
     for b in range(run.B):
         d1, win = oracle_by_seq[b]
-        codes = from_dev(v["blk_codes"][b, :nb])
-        scale = from_dev(v["blk_scale"][b, :nb])
-        rope = from_dev(v["blk_rope"][b, :nb], np.uint16)
-        assert np.array_equal(codes, d1["nope"][:nb]), f"seq {b}: FP8 codes differ at {np.argwhere(codes != d1['nope'][:nb])[:5]}"
-        assert np.array_equal(scale.view(np.uint32), d1["scale"][:nb].view(np.uint32)), f"seq {b}: scales differ"
-        ud = bf16_ulp_diff(rope, d1["rope"][:nb])
-        assert ud.max(initial=0) <= 1, f"seq {b}: RoPE dims differ by {ud.max()} ulp"
-        report["rope_ulp1"] += int((ud > 0).sum())
-        report["rope_total"] += ud.size
-        if run.csa:
-            ic = unpack_nibbles(from_dev(v["idx_codes"][b, :nb]))
-            isc = from_dev(v["idx_scale"][b, :nb])
-            assert np.array_equal(ic, d1["idx_codes"][:nb]), f"seq {b}: FP4 codes differ at {np.argwhere(ic != d1['idx_codes'][:nb])[:5]}"
-            assert np.array_equal(isc, d1["idx_scales"][:nb]), f"seq {b}: E8M0 bytes differ"
+        if run.swa:
+            assert "blk_codes" not in v
+        else:
+            _compare_blocks(run, v, b, d1, nb, report)
         if check_window:
             R = run.dev.ring
             lo = max(0, run.len - R)

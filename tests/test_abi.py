@@ -169,3 +169,55 @@ def test_workspace_bytes_grows_with_queries():
     b = lca.lca_workspace_bytes(d, 4, 16, 1 << 20)
     assert 0 < a < b
     assert a >= 4 * (1 << 18) * 4  # one fp32 score key per visible block
+
+
+def test_window_only_layer_sizes_and_checks():
+    """The window-only kind (the final MTP block of the layer interleave paragraph): its cache is the
+    window state and the RoPE table alone; compressor and indexer entry points reject it."""
+    B, R, ctx = 4, 128, 1 << 20
+    d = lca.make_desc("swa", 0, 64, 128)
+    assert lca.lca_cache_bytes(d, B, ctx, R) == _align(B * R * 64) + _align(B * R * 4) + _align(B * R * 128) + 256
+    assert lca.lca_cache_bytes(lca.make_desc("swa", 77, 64, 128), B, ctx, R) == lca.lca_cache_bytes(d, B, ctx, R)
+    assert lca.lca_cache_bytes(lca.make_desc("swa", 0, 64, 128), B, ctx, 64) == 0  # ring < window
+    assert lca.lca_workspace_bytes(d, B, 1, ctx) > 0
+    L = lca.lib()
+    c = lca.lca_cache()
+    c.desc = lca.make_desc("swa", 1, 8, 128)
+    c.batch, c.ring, c.max_ctx, c.max_blocks = 1, 128, 4096, 0
+    c.win_codes_dev = c.win_scale_dev = c.win_rope_dev = 0x100000
+    P = 0x200000
+    assert L.lca_hca_compress(ctypes.byref(c), P, P, P, 1, None) == -3
+    assert L.lca_csa_compress(ctypes.byref(c), P, P, P, P, P, P, 1, None) == -3
+    assert L.lca_hca_dense_attn(ctypes.byref(c), P, 1, P, None, P, 1 << 30, None) == -3
+    assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, P, 1 << 30, None) in (-2, -3)
+    assert L.lca_swa_attn(ctypes.byref(c), P, 1, P, None, None, 0, None) == -2      # nothing appended yet
+    assert L.lca_swa_tail_append(ctypes.byref(c), None, None, None, None, 1, None) == -1
+    assert L.lca_swa_tail_append(ctypes.byref(c), P, None, None, None, 4097, None) == -4
+    c.len = 10
+    assert L.lca_swa_attn(ctypes.byref(c), P, 2, P, None, None, 0, None) == -4      # ring < Tq + W - 1
+    assert L.lca_swa_attn(ctypes.byref(c), None, 1, P, None, None, 0, None) == -1
+    c.max_blocks = 4096  # a window-only cache never has blocks
+    assert L.lca_swa_attn(ctypes.byref(c), P, 1, P, None, None, 0, None) == -1
+    h = _fake_bound_cache("hca")
+    h.len = 10
+    assert L.lca_swa_attn(ctypes.byref(h), P, 1, P, None, P, 1 << 30, None) == -3
+
+
+def test_v4pro_layer_schedule():
+    """The layer interleave paragraph: V4-Pro has 61 layers, layers 0-1 HCA, layers 2-60 alternating CSA
+    and HCA, and a final MTP block that runs only the sliding window."""
+    k = configs.v4pro_schedule(61, mtp=True)
+    assert len(k) == 62 and k[:2] == ("hca", "hca") and k[-1] == "swa"
+    body = k[2:61]
+    assert all(a != b for a, b in zip(body, body[1:]))          # strictly alternating
+    assert k.count("csa") == 30 and k.count("hca") == 31 and k.count("swa") == 1
+    assert configs.v4pro_schedule(8, mtp=False) == tuple(l.kind for l in configs.WORKLOADS[4].layers)
+    wl = configs.WORKLOADS[5]
+    assert tuple(l.kind for l in wl.layers) == k
+    # one decode step's algorithmic bytes: 30 CSA + 31 HCA + 1 window-only layer at 1M context
+    t1 = wl.context + 1
+    by_kind = {l.kind: configs.decode_step_bytes(l, t1) for l in wl.layers}
+    assert sum(configs.decode_step_bytes(l, t1) for l in wl.layers) == \
+        30 * by_kind["csa"] + 31 * by_kind["hca"] + by_kind["swa"]
+    assert by_kind["swa"] == 128 * 196 + 64 * 128 * 2 * 2 + 128 * 2 + 196
+    assert configs.kv_bytes_per_seq(wl.layers[-1], 1 << 20) == 128 * 196

@@ -322,3 +322,40 @@ def test_attention_key_splits_hca():
     _ingest(run, [65536, 24575])
     worst, oc = _decode(run, 3, run.len + 3)
     print("hca split worst", worst)
+
+
+def test_window_only_layer_decode():
+    """The window-only layer (the final MTP block): window entries bit-exact in the ring, decode queries
+    from the very first token on (t < W) and beyond the first window, B=3, H=64."""
+    layer = configs.Layer("swa", 1, n_heads=64, window=128)
+    run = LayerRun(layer, B=3, max_ctx=1200, ring=128, layer_id=61)
+    oc = [run.oracle_caches(b, 1200) for b in range(run.B)]
+    for _ in range(3):   # t = 0, 1, 2: fewer window tokens than W
+        run.ingest(1)
+        qin, topk, out, lse = run.run_queries(1)
+        assert topk is None
+        check_queries(run, oc, qin, topk, out, lse, [run.len - 1])
+    _ingest(run, [700, 5, 300])
+    worst, _ = _decode(run, 4, 1200)
+    compare_cache(run, oc)
+    print("swa decode worst", worst)
+
+
+def test_window_only_layer_many_queries_and_long_window():
+    """Window-only queries in one call: Tq = 100 (one-launch attention), Tq = 300 with B = 2 (600 queries:
+    the many-query kernel), and a 1024-token window with 16 heads (key splits)."""
+    layer = configs.Layer("swa", 1, n_heads=32, window=128)
+    run = LayerRun(layer, B=2, max_ctx=1400, ring=300 + 127, max_tq=300, layer_id=61)
+    oc = [run.oracle_caches(b, 1400) for b in range(run.B)]
+    for Tq in (100, 300):
+        run.ingest(Tq)
+        qin, topk, out, lse = run.run_queries(Tq)
+        pos = list(range(run.len - Tq, run.len))
+        check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 9)) + [Tq - 1])
+    compare_cache(run, oc)
+    layer = configs.Layer("swa", 1, n_heads=16, window=1024)
+    run = LayerRun(layer, B=2, max_ctx=3000, ring=1024, layer_id=61)
+    _ingest(run, [1500])
+    worst, oc = _decode(run, 3, 1503)
+    compare_cache(run, oc)
+    print("swa long-window worst", worst)
