@@ -27,6 +27,13 @@ top-k of the chunk's 8192 queries, sparse attention), after an untimed pass
 of two chunks; `value` is prefill tokens/s and `roofline` the score kernel's
 MXFP4 FLOPs against the MFMA peak.
 
+With --workload csa_snapshot_1m it times the persistence path on the
+csa_decode_1m caches: K snapshots of one sequence's state (compressed
+entries, indexer keys, window, tail: 60 MB) into a device buffer and K
+restores of it into another sequence; `value` is state bytes moved per second
+(each byte read once and written once) and `roofline` the copy kernel's HBM
+bytes against 8 TB/s.
+
 With --workload v4pro61_mtp_decode_1m the step runs V4-Pro's whole layer
 schedule (61 layers: two HCA, then CSA and HCA alternating, plus the
 window-only MTP block) over B=4 sequences at 1M context.
@@ -51,7 +58,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode query-tok/s + HBM GB/s (% of peak), CSA/HCA layer at 1M ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD_BY_NAME = {"csa_decode_small": 0, "hca_decode_64k": 1, "csa_decode_1m": 2, "csa_prefill_128k": 3,
-                    "stack8_decode_256k": 4, "v4pro61_mtp_decode_1m": 5}
+                    "stack8_decode_256k": 4, "v4pro61_mtp_decode_1m": 5, "csa_snapshot_1m": 2}
+PERSIST_METRIC = "snapshot + restore GB/s of one 1M-token CSA sequence's compressed state, 1 GPU"
 PREFILL_METRIC = "chunked-prefill tok/s (CSA layer, 131072 tokens, chunk 8192), 1 GPU"
 MXFP4_PEAK_TFLOPS = 10100.0
 
@@ -501,6 +509,65 @@ def prefill_bench(args, wl):
     return 0
 
 
+def persist_bench(args, wl):
+    """Snapshot / restore of one sequence of the csa_decode_1m caches, each launch bracketed by events."""
+    import numpy as np
+    import torch
+    import long_context_attention_18_amd as lca
+    K = args.steps
+    layers = [Layer(wl, 0, wl.layers[0], 1, args.threads)]
+    t0 = time.perf_counter()
+    fill_caches(layers, wl, max(4096, min(65536, (1 << 26) // (wl.batch * 768))))
+    L = layers[0]
+    log(f"cache filled to {wl.context} tokens x {wl.batch} seqs in {time.perf_counter() - t0:.1f} s")
+    snap, info = L.dev.snapshot(0)
+    state = int(info.bytes) - lca.LCA_SNAPSHOT_HEADER
+    hev = HipEvents()
+    rec = lambda e: hev.record(e, False)
+    ev = [(hev.create(), hev.create(), hev.create()) for _ in range(K)]
+    c, st, lib = ctypes_ref(L.dev.cache), torch.cuda.current_stream().cuda_stream, lca.lib()
+    ptr, nbytes = snap.data_ptr(), int(info.bytes)
+    info_ref = ctypes_ref(info)
+    for i in range(max(1, args.warmup)):
+        lib.lca_cache_snapshot(c, i % wl.batch, ptr, nbytes, info_ref, st)
+        lib.lca_cache_restore(c, (i + 1) % wl.batch, ptr, nbytes, info_ref, st)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e7))
+    for i in range(K):
+        rec(ev[i][0])
+        rc = lib.lca_cache_snapshot(c, i % wl.batch, ptr, nbytes, info_ref, st)
+        rec(ev[i][1])
+        rc = rc or lib.lca_cache_restore(c, (i + 1) % wl.batch, ptr, nbytes, info_ref, st)
+        rec(ev[i][2])
+        if rc != 0:
+            raise lca.LcaError("snapshot / restore", rc)
+    torch.cuda.synchronize()
+    snap_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b, _ in ev])
+    rest_us = np.array([hev.elapsed_ms(b, c2) * 1e3 for _, b, c2 in ev])
+    per_pair_us = float(snap_us.mean() + rest_us.mean())
+    value = 2 * state / (per_pair_us * 1e-6) / 1e9
+    achieved = 2 * state / (snap_us.mean() * 1e-6) / 1e9
+    log(f"state {state / 1e6:.1f} MB; snapshot {snap_us.mean():.1f} us, restore {rest_us.mean():.1f} us")
+    result = {
+        "metric": PERSIST_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(per_pair_us / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "csa_snapshot_1m", "batch": wl.batch, "context": wl.context,
+                   "state_bytes": state, "blocks": int(info.n_blocks)},
+        "roofline": {"bound": "hbm", "kernel": "copy_runs_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": 2 * state, "avg_launch_us": round(float(snap_us.mean()), 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def ctypes_ref(x):
+    import ctypes
+    return ctypes.byref(x)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -516,6 +583,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     wl = configs.WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
+    if args.workload == "csa_snapshot_1m":
+        log(f"workload {args.workload}: snapshot / restore of {wl.name}'s sequences")
+        return persist_bench(args, wl)
     if wl.prefill_chunk:
         log(f"workload {wl.name}: {wl.note}")
         return prefill_bench(args, wl)

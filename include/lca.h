@@ -274,6 +274,65 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
                         uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
                         void* score_ev_begin, void* score_ev_end);
 
+/* ---- persistence: snapshot and restore of one sequence's state ----------
+ * The KV-cache section of velog.io "DeepSeek V4 논문 정리" keeps compressed KV
+ * on disk for requests that share a prefix. A snapshot is a contiguous
+ * buffer holding one sequence's whole state at its current length: its
+ * compressed entries (D1), indexer keys (D3, CSA), window entries in
+ * position order and uncompressed tail rows, behind a 256-byte header that
+ * starts with a copy of lca_snapshot_info. The buffer is device memory; the
+ * caller moves it to host memory or disk and back as plain bytes. Restoring
+ * it into a cache gives that cache exactly the state (bit for bit in every
+ * entry a later call reads) of one that ingested the same tokens, so a shared
+ * prefix is compressed once and restored into any number of sequences, which
+ * then continue with their own tokens. */
+#define LCA_SNAPSHOT_MAGIC 0x5341434Cu /* "LCAS" */
+#define LCA_SNAPSHOT_VERSION 1u
+#define LCA_SNAPSHOT_HEADER 256
+
+typedef struct lca_snapshot_info {
+  uint32_t magic;     /* LCA_SNAPSHOT_MAGIC */
+  uint32_t version;   /* LCA_SNAPSHOT_VERSION */
+  int32_t kind;       /* layer kind of the cache it came from */
+  int32_t m;          /* its m (1 for SWA) */
+  int32_t tail_width; /* its tail row width in BF16 values (0 for SWA) */
+  int32_t reserved;
+  int64_t len;        /* tokens of the sequence */
+  int64_t n_blocks;   /* compressed entries 0 .. n_blocks-1 (len / m; 0 for SWA) */
+  int64_t n_win;      /* window entries of positions len-n_win .. len-1 (min(len, ring)) */
+  int64_t n_tail;     /* tail rows of positions len-n_tail .. len-1 (len mod m; 0 for SWA) */
+  /* byte offsets in the buffer, each 256-aligned: D1 codes [n_blocks][64] u8, D1 scales [n_blocks] f32,
+   * D1 RoPE [n_blocks][64] bf16, D3 codes [n_blocks][32] u8, D3 scales [n_blocks][2] u8, window codes
+   * [n_win][64] u8, window scales [n_win] f32, window RoPE [n_win][64] bf16, tail [n_tail][tail_width]
+   * bf16, end; sections a kind does not have are empty */
+  uint64_t off[10];
+  uint64_t bytes;     /* total bytes of the snapshot (= off[9]) */
+} lca_snapshot_info;
+
+/* Layout of a snapshot of any sequence of `cache` at its current length:
+ * fills *info (bytes included) without touching the device. LCA_ERR_ORDER
+ * while a compress waits for its append. */
+lca_status lca_snapshot_layout(const lca_cache* cache, lca_snapshot_info* info);
+
+/* Copies sequence `seq` (0 <= seq < B) of `cache` into dst_dev (>= info->bytes
+ * device bytes, 256-byte aligned) on `stream` -- the header included -- and
+ * fills *info as lca_snapshot_layout does. The cache is not changed. */
+lca_status lca_cache_snapshot(const lca_cache* cache, int32_t seq, void* dst_dev, size_t bytes,
+                              lca_snapshot_info* info, void* stream);
+
+/* Restores the snapshot in src_dev (described by *info, the header the
+ * snapshot wrote or the info its lca_cache_snapshot returned) into sequence
+ * `seq` of `cache`, or into every sequence when seq = -1. The cache must have
+ * the snapshot's kind, m and tail width, room for its length and a window
+ * the snapshot covers (n_win >= min(len, window)); every sequence of a cache
+ * holds the same number of tokens, so seq = -1 needs len = 0 or
+ * len = info->len and seq >= 0 needs len = info->len (or batch = 1); the
+ * cache's len becomes info->len. Rejected headers (magic, version, sizes,
+ * offsets that do not match the layout) return LCA_ERR_UNSUPPORTED or
+ * LCA_ERR_SHAPE and change nothing. */
+lca_status lca_cache_restore(lca_cache* cache, int32_t seq, const void* src_dev, size_t bytes,
+                             const lca_snapshot_info* info, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* lca_status_str(lca_status status);
 

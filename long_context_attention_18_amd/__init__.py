@@ -48,6 +48,15 @@ class lca_cache(ctypes.Structure):
                 ("rope_inv_freq", ctypes.c_double * 32), ("rope_inv_freq_dev", ctypes.c_void_p)]
 
 
+class lca_snapshot_info(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("kind", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("tail_width", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("len", ctypes.c_int64), ("n_blocks", ctypes.c_int64), ("n_win", ctypes.c_int64),
+                ("n_tail", ctypes.c_int64), ("off", ctypes.c_uint64 * 10), ("bytes", ctypes.c_uint64)]
+
+
+LCA_SNAPSHOT_HEADER = 256
+
 _LIB = None
 _VP = ctypes.c_void_p
 _DP = ctypes.POINTER(lca_layer_desc)
@@ -55,6 +64,7 @@ _CP = ctypes.POINTER(lca_cache)
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
+_SP = ctypes.POINTER(lca_snapshot_info)
 
 _SIGNATURES = {
     "lca_cache_bytes": (_SZ, [_DP, _I32, _I64, _I32]),
@@ -75,6 +85,9 @@ _SIGNATURES = {
     "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
                             _VP, _VP]),
+    "lca_snapshot_layout": (_I32, [_CP, _SP]),
+    "lca_cache_snapshot": (_I32, [_CP, _I32, _VP, _SZ, _SP, _VP]),
+    "lca_cache_restore": (_I32, [_CP, _I32, _VP, _SZ, _SP, _VP]),
     "lca_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -211,6 +224,24 @@ def lca_csa_step(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out
                                                score_events[0], score_events[1]))
 
 
+def lca_snapshot_layout(cache):
+    info = lca_snapshot_info()
+    _check("lca_snapshot_layout", lib().lca_snapshot_layout(ctypes.byref(cache), ctypes.byref(info)))
+    return info
+
+
+def lca_cache_snapshot(cache, seq, dst, nbytes, stream=None):
+    info = lca_snapshot_info()
+    _check("lca_cache_snapshot", lib().lca_cache_snapshot(ctypes.byref(cache), seq, _ptr(dst), nbytes,
+                                                           ctypes.byref(info), _stream(stream)))
+    return info
+
+
+def lca_cache_restore(cache, seq, src, nbytes, info, stream=None):
+    _check("lca_cache_restore", lib().lca_cache_restore(ctypes.byref(cache), seq, _ptr(src), nbytes,
+                                                         ctypes.byref(info), _stream(stream)))
+
+
 def lca_status_str(status):
     return lib().lca_status_str(status).decode()
 
@@ -300,6 +331,23 @@ class DeviceLayer:
         lca_csa_step(self.cache, kv, gate, ik, ig, bias, idx_bias, kv.shape[1], qI, w, q, topk, out, lse, self.ws,
                      self.ws_bytes, stream, score_events)
 
+    # ---- persistence: snapshots are device buffers; files hold their bytes as they are
+    def snapshot(self, seq=0, stream=None):
+        """Sequence `seq`'s state -> (uint8 device tensor whose first 256-aligned byte starts the
+        snapshot, its lca_snapshot_info)."""
+        import torch
+        info = lca_snapshot_layout(self.cache)
+        buf = torch.empty(info.bytes + 256, dtype=torch.uint8, device=self.mem.device)
+        off = (-buf.data_ptr()) % 256
+        view = buf[off:off + info.bytes]
+        info = lca_cache_snapshot(self.cache, seq, view.data_ptr(), info.bytes, stream)
+        return view, info
+
+    def restore(self, snap, info, seq=-1, stream=None):
+        """Restore a snapshot (device tensor from snapshot() or load_snapshot()) into sequence `seq`
+        (-1: every sequence)."""
+        lca_cache_restore(self.cache, seq, snap.data_ptr(), snap.numel(), info, stream)
+
     def index_scores(self, Tq):
         """fp32 scores the last index_score / indexer_topk call left in the workspace: [B][Tq][max_blocks]."""
         import numpy as np
@@ -339,3 +387,28 @@ class DeviceLayer:
             v["idx_codes"] = view(c.idx_codes_dev, B * NB * 32, torch.uint8, (B, NB, 32))
             v["idx_scale"] = view(c.idx_scale_dev, B * NB * 2, torch.uint8, (B, NB, 2))
         return v
+
+
+# ----------------------------------------------------------------- snapshot files
+def save_snapshot(path, snap):
+    """Write a snapshot's bytes (header included) to `path`."""
+    import torch
+    torch.cuda.synchronize()
+    snap.cpu().numpy().tofile(path)
+
+
+def load_snapshot(path, device="cuda"):
+    """Read a snapshot file -> (device tensor, 256-byte aligned, lca_snapshot_info from its header)."""
+    import numpy as np
+    import torch
+    raw = np.fromfile(path, dtype=np.uint8)
+    if raw.size < LCA_SNAPSHOT_HEADER:
+        raise ValueError(f"{path}: {raw.size} bytes, shorter than a snapshot header")
+    info = lca_snapshot_info.from_buffer_copy(raw[:ctypes.sizeof(lca_snapshot_info)].tobytes())
+    if info.bytes != raw.size:
+        raise ValueError(f"{path}: header says {info.bytes} bytes, file has {raw.size}")
+    buf = torch.empty(raw.size + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    view = buf[off:off + raw.size]
+    view.copy_(torch.from_numpy(raw))
+    return view, info

@@ -3,6 +3,7 @@
 // Host-side only: argument checks, cache carving, workspace layout, and the
 // kernel launches. Every check happens before the first launch of a call, so
 // a rejected call enqueues nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -537,6 +538,163 @@ lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float*
                           size_t ws_bytes, void* stream) {
   return topk_attn_impl(cache, qI_dev, w_dev, true, q_dev, Tq, topk_dev, out_dev, lse_dev, ws_dev, ws_bytes,
                         stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- persistence
+namespace {
+
+constexpr int kSections = 9;
+
+void snapshot_layout(int32_t kind, int32_t m, int32_t tw, int64_t len, int64_t n_win, lca_snapshot_info* I,
+                     size_t* sizes = nullptr) {
+  std::memset(I, 0, sizeof(*I));
+  I->magic = LCA_SNAPSHOT_MAGIC;
+  I->version = LCA_SNAPSHOT_VERSION;
+  I->kind = kind;
+  I->m = m;
+  I->tail_width = tw;
+  I->len = len;
+  I->n_blocks = kind == LCA_KIND_SWA ? 0 : len / m;
+  I->n_win = n_win;
+  I->n_tail = kind == LCA_KIND_SWA ? 0 : len % m;
+  const size_t nb = (size_t)I->n_blocks, nw = (size_t)n_win, nt = (size_t)I->n_tail;
+  const bool csa = kind == LCA_KIND_CSA;
+  const size_t sz[kSections] = {nb * 64, nb * 4, nb * 128, csa ? nb * 32 : 0, csa ? nb * 2 : 0,
+                                nw * 64, nw * 4, nw * 128, nt * (size_t)tw * 2};
+  size_t off = LCA_SNAPSHOT_HEADER;
+  for (int i = 0; i < kSections; ++i) {
+    I->off[i] = off;
+    off = align_up(off + sz[i]);
+    if (sizes) sizes[i] = sz[i];
+  }
+  I->off[kSections] = off;
+  I->bytes = off;
+}
+
+void add_run(CopyArgs& a, const void* src, void* dst, uint64_t bytes, uint64_t src_stride, uint64_t dst_stride) {
+  if (bytes == 0) return;
+  if (a.n_runs >= kMaxCopyRuns) {  // at most 21 runs by construction; the launcher refuses an overflow
+    a.n_runs = kMaxCopyRuns + 1;
+    return;
+  }
+  CopyRun& r = a.run[a.n_runs++];
+  r.src = (const uint8_t*)src;
+  r.dst = (uint8_t*)dst;
+  r.bytes = bytes;
+  r.src_stride = src_stride;
+  r.dst_stride = dst_stride;
+}
+
+// positions p0 .. p0+n-1 (n <= R) of a ring of R slots: at most two runs of consecutive slots
+int ring_runs(int64_t p0, int64_t n, int32_t R, int64_t pos[2], int64_t cnt[2]) {
+  if (n <= 0) return 0;
+  const int64_t first = std::min<int64_t>(n, R - p0 % R);
+  pos[0] = p0;
+  cnt[0] = first;
+  if (first == n) return 1;
+  pos[1] = p0 + first;
+  cnt[1] = n - first;
+  return 2;
+}
+
+// The runs between sequence b0 of the cache and a snapshot buffer laid out as I. to_snapshot: cache ->
+// buffer; else buffer -> cache, repeated for every grid row (cache strides, the same buffer). Window
+// positions len-nw .. len-1 (nw <= ring) sit at buffer index pos - (len - I.n_win).
+void state_runs(const lca_cache* c, int32_t b0, const lca_snapshot_info& I, int64_t nw, uint8_t* buf,
+                bool to_snapshot, CopyArgs& a) {
+  const size_t mb = (size_t)c->max_blocks, R = (size_t)c->ring, nb = (size_t)I.n_blocks;
+  const size_t tw2 = (size_t)c->tail_width * 2;
+  auto pair = [&](void* cache_p, uint64_t off, uint64_t bytes, uint64_t stride) {
+    if (to_snapshot) add_run(a, cache_p, buf + off, bytes, 0, 0);
+    else add_run(a, buf + off, cache_p, bytes, 0, stride);
+  };
+  if (c->desc.kind != LCA_KIND_SWA) {
+    pair(c->blk_codes_dev + (size_t)b0 * mb * 64, I.off[0], nb * 64, mb * 64);
+    pair(c->blk_scale_dev + (size_t)b0 * mb, I.off[1], nb * 4, mb * 4);
+    pair(c->blk_rope_dev + (size_t)b0 * mb * 64, I.off[2], nb * 128, mb * 128);
+    pair(c->tail_dev + (size_t)b0 * c->desc.m * c->tail_width, I.off[8], (size_t)I.n_tail * tw2,
+         (size_t)c->desc.m * tw2);
+  }
+  if (c->desc.kind == LCA_KIND_CSA) {
+    pair(c->idx_codes_dev + (size_t)b0 * mb * 32, I.off[3], nb * 32, mb * 32);
+    pair(c->idx_scale_dev + (size_t)b0 * mb * 2, I.off[4], nb * 2, mb * 2);
+  }
+  int64_t pos[2], cnt[2];
+  const int n = ring_runs(I.len - nw, nw, c->ring, pos, cnt);
+  for (int i = 0; i < n; ++i) {
+    const size_t slot = (size_t)b0 * R + (size_t)(pos[i] % c->ring);
+    const uint64_t idx = (uint64_t)(pos[i] - (I.len - I.n_win));
+    pair(c->win_codes_dev + slot * 64, I.off[5] + idx * 64, (uint64_t)cnt[i] * 64, R * 64);
+    pair(c->win_scale_dev + slot, I.off[6] + idx * 4, (uint64_t)cnt[i] * 4, R * 4);
+    pair(c->win_rope_dev + slot * 64, I.off[7] + idx * 128, (uint64_t)cnt[i] * 128, R * 128);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_snapshot_layout(const lca_cache* cache, lca_snapshot_info* info) {
+  if (!cache_ok(cache) || !info) return LCA_ERR_NULL;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  snapshot_layout(cache->desc.kind, cache->desc.m, cache->tail_width, cache->len,
+                  std::min<int64_t>(cache->len, cache->ring), info);
+  return LCA_OK;
+}
+
+lca_status lca_cache_snapshot(const lca_cache* cache, int32_t seq, void* dst_dev, size_t bytes,
+                              lca_snapshot_info* info, void* stream) {
+  if (!cache_ok(cache) || !dst_dev || !info) return LCA_ERR_NULL;
+  if (seq < 0 || seq >= cache->batch) return LCA_ERR_SHAPE;
+  if (((uintptr_t)dst_dev) % kAlign != 0) return LCA_ERR_SHAPE;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  lca_snapshot_info I;
+  size_t sz[kSections];
+  snapshot_layout(cache->desc.kind, cache->desc.m, cache->tail_width, cache->len,
+                  std::min<int64_t>(cache->len, cache->ring), &I, sz);
+  if (bytes < I.bytes) return LCA_ERR_CAPACITY;
+  CopyArgs a{};
+  state_runs(cache, seq, I, I.n_win, (uint8_t*)dst_dev, true, a);
+  // zeros in the alignment gaps, so a snapshot's bytes depend on the state alone
+  for (int i = 0; i < kSections; ++i)
+    add_run(a, nullptr, (uint8_t*)dst_dev + I.off[i] + sz[i], I.off[i + 1] - I.off[i] - sz[i], 0, 0);
+  static_assert(sizeof(lca_snapshot_info) <= sizeof(a.header), "header words hold the info");
+  std::memcpy(a.header, &I, sizeof(I));
+  a.header_dst = (uint8_t*)dst_dev;
+  if (launch_copy_runs(a, 1, (hipStream_t)stream) != hipSuccess) return LCA_ERR_LAUNCH;
+  *info = I;
+  return LCA_OK;
+}
+
+lca_status lca_cache_restore(lca_cache* cache, int32_t seq, const void* src_dev, size_t bytes,
+                             const lca_snapshot_info* info, void* stream) {
+  if (!cache_ok(cache) || !src_dev || !info) return LCA_ERR_NULL;
+  if (info->magic != LCA_SNAPSHOT_MAGIC || info->version != LCA_SNAPSHOT_VERSION) return LCA_ERR_UNSUPPORTED;
+  if (info->kind != cache->desc.kind || info->m != cache->desc.m || info->tail_width != cache->tail_width)
+    return LCA_ERR_UNSUPPORTED;
+  if (seq < -1 || seq >= cache->batch) return LCA_ERR_SHAPE;
+  if (((uintptr_t)src_dev) % kAlign != 0) return LCA_ERR_SHAPE;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (info->len < 0 || info->n_win < 0 || info->n_win > info->len) return LCA_ERR_SHAPE;
+  if (info->len > cache->max_ctx) return LCA_ERR_CAPACITY;
+  // the window attention reads must all be in the snapshot
+  if (info->n_win < std::min<int64_t>(info->len, cache->desc.window)) return LCA_ERR_SHAPE;
+  lca_snapshot_info E;
+  snapshot_layout(info->kind, info->m, info->tail_width, info->len, info->n_win, &E);
+  if (E.n_blocks != info->n_blocks || E.n_tail != info->n_tail || E.bytes != info->bytes ||
+      std::memcmp(E.off, info->off, sizeof(E.off)) != 0)
+    return LCA_ERR_SHAPE;
+  if (bytes < info->bytes) return LCA_ERR_CAPACITY;
+  // every sequence of a cache holds the same number of tokens
+  if (seq >= 0 && cache->batch > 1 && cache->len != info->len) return LCA_ERR_SHAPE;
+  CopyArgs a{};
+  const int64_t nw = std::min<int64_t>(info->n_win, cache->ring);
+  state_runs(cache, seq < 0 ? 0 : seq, E, nw, (uint8_t*)const_cast<void*>(src_dev), false, a);
+  if (launch_copy_runs(a, seq < 0 ? cache->batch : 1, (hipStream_t)stream) != hipSuccess) return LCA_ERR_LAUNCH;
+  cache->len = info->len;
+  return LCA_OK;
 }
 
 }  // extern "C"

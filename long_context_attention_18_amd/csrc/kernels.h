@@ -126,6 +126,27 @@ struct AttendArgs {
   int32_t splits;
 };
 
+// Contiguous runs copied between a cache and a snapshot buffer (persist.hip): run i moves `bytes`
+// from src + y * src_stride to dst + y * dst_stride for every grid row y < n_dst (src = null: writes
+// zeros); the launcher sets `unit` (16, 4 or 1 bytes) from the addresses' alignment. Workgroup (0, 0)
+// also writes the kCopyHeaderWords header words to header_dst when it is not null.
+constexpr int kMaxCopyRuns = 24;
+constexpr int kCopyHeaderWords = 64;
+struct CopyRun {
+  const uint8_t* src;
+  uint8_t* dst;
+  uint64_t bytes;
+  uint64_t src_stride, dst_stride;
+  int32_t unit;
+};
+struct CopyArgs {
+  CopyRun run[kMaxCopyRuns];
+  int32_t n_runs;
+  uint8_t* header_dst;
+  uint32_t header[kCopyHeaderWords];
+};
+hipError_t launch_copy_runs(CopyArgs& a, int32_t n_dst, hipStream_t s);
+
 hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s);
 hipError_t launch_append(const IngestArgs& a, bool csa, int32_t n_tail, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

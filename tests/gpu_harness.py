@@ -54,7 +54,9 @@ class LayerRun:
     """One layer of B sequences: seeded inputs, device cache, oracle mirror."""
 
     def __init__(self, layer, B, max_ctx, ring, max_tq=1, workload=90, layer_id=0, sigma=1.28, hidden=512,
-                 transform=None, qtransform=None):
+                 transform=None, qtransform=None, seq_ids=None, token_fn=None):
+        """seq_ids: the seeded sequence each local sequence draws its tokens and queries from (default:
+        its own index); token_fn(b, pos0, n): replaces the seeded token streams (e.g. a shared prefix)."""
         import long_context_attention_18_amd as lca
         self.transform, self.qtransform = transform, qtransform
         self.layer, self.B = layer, B
@@ -63,14 +65,16 @@ class LayerRun:
         self.m = layer.m
         self.desc = lca.make_desc(layer.kind, layer.m, layer.n_heads, layer.window, layer.idx_heads, layer.topk)
         self.dev = lca.DeviceLayer(self.desc, B, max_ctx, ring, max_tq=max_tq)
-        self.streams = [synth.TokenStream(workload, layer_id, b, self.csa, sigma) for b in range(B)]
+        self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
+        self.token_fn = token_fn
+        self.streams = [synth.TokenStream(workload, layer_id, sid, self.csa, sigma) for sid in self.seq_ids]
         self.bias = {} if self.swa else synth.biases(workload, layer_id, layer.m, self.csa)
         self.bias_dev = {k: to_dev(v) for k, v in self.bias.items()}
         self.proj = synth.QueryProjector(workload, layer_id, hidden, layer.n_heads, layer.idx_heads)
         self.len = 0
 
     def tokens(self, b, pos0, n):
-        tok = self.streams[b].tokens(pos0, n)
+        tok = self.token_fn(b, pos0, n) if self.token_fn else self.streams[b].tokens(pos0, n)
         return self.transform(tok, pos0) if self.transform else tok
 
     def ingest(self, T):
@@ -89,7 +93,7 @@ class LayerRun:
 
     def queries(self, positions):
         """Per-sequence query inputs at absolute positions -> stacked arrays [B][n][...]."""
-        per = [self.proj.queries(b, positions) for b in range(self.B)]
+        per = [self.proj.queries(sid, positions) for sid in self.seq_ids]
         out = {k: np.stack([p[k] for p in per]) for k in per[0]}
         return self.qtransform(out) if self.qtransform else out
 
@@ -171,8 +175,9 @@ def _compare_blocks(run, v, b, d1, nb, report):
         assert np.array_equal(isc, d1["idx_scales"][:nb]), f"seq {b}: E8M0 bytes differ"
 
 
-def compare_cache(run: LayerRun, oracle_by_seq, check_window=True):
-    """Bit-exact block entries / indexer keys; window slots for the last R positions."""
+def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positions=None):
+    """Bit-exact block entries / indexer keys; window slots for the last R positions (or the last
+    window_positions of them)."""
     v = run.dev.views()
     nb = 0 if run.swa else run.len // run.m
     report = {"rope_ulp1": 0, "rope_total": 0}
@@ -184,7 +189,7 @@ def compare_cache(run: LayerRun, oracle_by_seq, check_window=True):
             _compare_blocks(run, v, b, d1, nb, report)
         if check_window:
             R = run.dev.ring
-            lo = max(0, run.len - R)
+            lo = max(0, run.len - (R if window_positions is None else min(R, window_positions)))
             pos = np.arange(lo, run.len)
             slots = pos % R
             wc = from_dev(v["win_codes"][b])[slots]

@@ -221,3 +221,81 @@ def test_v4pro_layer_schedule():
         30 * by_kind["csa"] + 31 * by_kind["hca"] + by_kind["swa"]
     assert by_kind["swa"] == 128 * 196 + 64 * 128 * 2 * 2 + 128 * 2 + 196
     assert configs.kv_bytes_per_seq(wl.layers[-1], 1 << 20) == 128 * 196
+
+
+def _snap_closed_form(kind, m, tw, L, nw):
+    nb = 0 if kind == "swa" else L // m
+    nt = 0 if kind == "swa" else L % m
+    sizes = [nb * 64, nb * 4, nb * 128, nb * 32 if kind == "csa" else 0, nb * 2 if kind == "csa" else 0,
+             nw * 64, nw * 4, nw * 128, nt * tw * 2]
+    off, offs = 256, []
+    for z in sizes:
+        offs.append(off)
+        off = _align(off + z)
+    return nb, nt, offs + [off]
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "swa"])
+def test_snapshot_layout_closed_form(kind):
+    """One sequence's snapshot: 196 B per compressed entry (+34 B per CSA indexer key), 196 B per window
+    entry, the tail rows, behind a 256-B header; every section 256-aligned."""
+    c = _fake_bound_cache("csa" if kind == "csa" else "hca")
+    if kind == "swa":
+        c.desc = lca.make_desc("swa", 1, 8, 128)
+        c.max_blocks, c.tail_width = 0, 0
+        c.blk_codes_dev = c.blk_scale_dev = c.blk_rope_dev = c.tail_dev = None
+    for L in (0, 3, 127, 128, 1000, 4095):
+        c.len = L
+        info = lca.lca_snapshot_layout(c)
+        nw = min(L, c.ring)
+        nb, nt, offs = _snap_closed_form(kind, c.desc.m, c.tail_width, L, nw)
+        assert (info.magic, info.version) == (0x5341434C, 1)
+        assert (info.len, info.n_blocks, info.n_win, info.n_tail) == (L, nb, nw, nt)
+        assert list(info.off) == offs and info.bytes == offs[-1]
+        payload = nb * (196 + (34 if kind == "csa" else 0)) + nw * 196 + nt * c.tail_width * 2
+        assert payload <= info.bytes - 256 < payload + 9 * 256
+    c.pending = 5
+    with pytest.raises(lca.LcaError):
+        lca.lca_snapshot_layout(c)
+
+
+def test_restore_rejects_bad_headers_and_shapes():
+    L = lca.lib()
+    c = _fake_bound_cache("csa")          # B = 1, max_ctx 4096, ring 128, window 128
+    c.len = 1000
+    good = lca.lca_snapshot_layout(c)
+    P, big = 0x200000, 1 << 30
+
+    def restore(info, seq=0, cache=c, nbytes=big, src=P):
+        return L.lca_cache_restore(ctypes.byref(cache), seq, src, nbytes, ctypes.byref(info), None)
+
+    def mod(**kw):
+        i = lca.lca_snapshot_info.from_buffer_copy(bytes(good))
+        for k, v in kw.items():
+            setattr(i, k, v)
+        return i
+
+    assert restore(mod(magic=0)) == -3 and restore(mod(version=2)) == -3
+    assert restore(mod(kind=1)) == -3 and restore(mod(m=8)) == -3 and restore(mod(tail_width=256)) == -3
+    assert restore(good, seq=1) == -2 and restore(good, seq=-2) == -2
+    assert restore(good, src=P + 8) == -2
+    assert restore(good, nbytes=good.bytes - 1) == -4
+    assert restore(mod(len=5000)) in (-2, -4)                   # beyond max_ctx (and layout no longer matches)
+    assert restore(mod(n_win=100)) == -2                        # window of the last 128 positions not covered
+    bad = mod()
+    bad.off[3] += 256
+    assert restore(bad) == -2                                   # offsets that do not match the layout
+    assert restore(mod(n_blocks=249)) == -2
+    assert L.lca_cache_restore(ctypes.byref(c), 0, None, big, ctypes.byref(good), None) == -1
+    h = _fake_bound_cache("hca")
+    assert restore(good, cache=h) == -3                         # a CSA snapshot into an HCA cache
+    c.pending = 1
+    assert restore(good) == -5
+    c.pending = 0
+    # every sequence holds the same number of tokens: one sequence of a B = 2 cache only at equal length
+    c.batch = 2
+    c.len = 999
+    assert restore(good, seq=1) == -2
+    assert c.len == 999
+    assert L.lca_cache_snapshot(ctypes.byref(c), 2, P, big, ctypes.byref(lca.lca_snapshot_info()), None) == -2
+    assert L.lca_cache_snapshot(ctypes.byref(c), 0, P, 16, ctypes.byref(lca.lca_snapshot_info()), None) == -4
