@@ -26,7 +26,9 @@
  *    argument returns a negative status and launches nothing.
  *  - BF16 tensors are passed as uint16_t bit patterns; every tensor is dense
  *    row-major with the shape written next to it; B = batch of the cache.
- *  - Every sequence of a cache holds the same number of tokens (`len`).
+ *  - Every sequence of a cache holds the same number of tokens (`len`),
+ *    except through the ragged calls (lca_ragged_*), where the caller
+ *    passes each sequence's length with every call.
  *  - A cache (and a workspace) is not thread-safe; distinct caches are
  *    independent.
  *
@@ -106,7 +108,7 @@ typedef struct lca_cache {
    * tail_width = 128 (kv) + 128 (gate) [+ 64 (ik) + 64 (ig) for CSA]; NULL and 0 for SWA */
   uint16_t* tail_dev;
   int32_t tail_width;
-  int32_t reserved0;
+  int32_t ragged;     /* 1 once a ragged call (lca_ragged_*) used the cache: it then tracks no len */
   /* RoPE frequencies 10000^(-2i/64), i < 32, computed on the host at bind */
   double rope_inv_freq[32];
   /* their device copy (256 B at the end of the cache memory), what the kernels read */
@@ -327,11 +329,61 @@ lca_status lca_cache_snapshot(const lca_cache* cache, int32_t seq, void* dst_dev
  * the snapshot covers (n_win >= min(len, window)); every sequence of a cache
  * holds the same number of tokens, so seq = -1 needs len = 0 or
  * len = info->len and seq >= 0 needs len = info->len (or batch = 1); the
- * cache's len becomes info->len. Rejected headers (magic, version, sizes,
+ * cache's len becomes info->len. A ragged cache takes any sequence at any
+ * length and keeps len = 0 (the caller's len[seq] becomes info->len). Rejected headers (magic, version, sizes,
  * offsets that do not match the layout) return LCA_ERR_UNSUPPORTED or
  * LCA_ERR_SHAPE and change nothing. */
 lca_status lca_cache_restore(lca_cache* cache, int32_t seq, const void* src_dev, size_t bytes,
                              const lca_snapshot_info* info, void* stream);
+
+/* ---- ragged batches (continuous batching) ---------------------------------
+ * Sequences of one cache at different lengths, each adding its own number
+ * of tokens per call. As serving engines do, the caller tracks the lengths:
+ * every ragged call gets len[b] (tokens sequence b holds before the call)
+ * and T[b] (tokens it adds, 0 <= T[b] <= T_max; 0 leaves the sequence
+ * untouched), both on the host (checks, launch sizes) and on the device (the
+ * kernels), with equal contents; afterwards the caller adds T[b] to len[b].
+ * Inputs, queries and outputs keep the [B][T_max][...] layout with sequence
+ * b's rows 0 .. T[b]-1 in use; other rows are neither read nor written. The
+ * first ragged call marks the cache ragged (it must be empty then); from
+ * then on its len stays 0, the uniform calls reject it (LCA_ERR_ORDER), and
+ * lca_ragged_snapshot takes a sequence's length from the caller. Restoring a
+ * snapshot into a sequence of a ragged cache works at any length (the
+ * caller's len[b] becomes the snapshot's len). Results per sequence are
+ * those of a uniform cache holding that sequence alone (CSA paragraph,
+ * Figures 3 and 4 of "DeepSeek-V4: a million-token context that agents can
+ * actually use"). */
+
+/* The compressor and the window / tail append for the T[b] new tokens of
+ * every sequence (lca_csa_compress / lca_hca_compress followed by
+ * lca_swa_tail_append, per sequence); no queries. Any T_max (chunked
+ * prefill of newly admitted sequences). Inputs as for the uniform calls;
+ * gate, ik, ig, bias, idx_bias may be NULL where the layer kind has no use
+ * for them. */
+lca_status lca_ragged_ingest(lca_cache* cache, int32_t T_max, const int64_t* len_host, const int32_t* T_host,
+                             const int64_t* len_dev, const int32_t* T_dev, const uint16_t* kv_dev,
+                             const uint16_t* gate_dev, const uint16_t* ik_dev, const uint16_t* ig_dev,
+                             const float* bias_dev, const float* idx_bias_dev, void* stream);
+
+/* One continuous-batching step of any layer kind: lca_ragged_ingest, then
+ * the queries of the new tokens (positions len[b] .. len[b]+T[b]-1) attend:
+ * CSA as lca_csa_step (indexer scores, top-k, sparse + window attention),
+ * HCA as lca_hca_dense_attn, SWA as lca_swa_attn. qI, w and topk are CSA's
+ * (topk and lse may be NULL); B * T_max <= 511 (else LCA_ERR_SHAPE);
+ * ring >= T_max + window - 1; the workspace (sized for max_tq >= T_max) is
+ * required for CSA, optional otherwise. */
+lca_status lca_ragged_step(lca_cache* cache, int32_t T_max, const int64_t* len_host, const int32_t* T_host,
+                           const int64_t* len_dev, const int32_t* T_dev, const uint16_t* kv_dev,
+                           const uint16_t* gate_dev, const uint16_t* ik_dev, const uint16_t* ig_dev,
+                           const float* bias_dev, const float* idx_bias_dev, const uint16_t* qI_dev,
+                           const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev,
+                           float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* lca_cache_snapshot for a sequence of a ragged cache that holds `len`
+ * tokens (the caller's len[seq]). With dst_dev = NULL it only fills *info
+ * (the layout, for sizing the buffer). */
+lca_status lca_ragged_snapshot(const lca_cache* cache, int32_t seq, int64_t len, void* dst_dev, size_t bytes,
+                               lca_snapshot_info* info, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* lca_status_str(lca_status status);

@@ -44,7 +44,7 @@ class lca_cache(ctypes.Structure):
                 ("blk_rope_dev", ctypes.c_void_p), ("idx_codes_dev", ctypes.c_void_p),
                 ("idx_scale_dev", ctypes.c_void_p), ("win_codes_dev", ctypes.c_void_p),
                 ("win_scale_dev", ctypes.c_void_p), ("win_rope_dev", ctypes.c_void_p),
-                ("tail_dev", ctypes.c_void_p), ("tail_width", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("tail_dev", ctypes.c_void_p), ("tail_width", ctypes.c_int32), ("ragged", ctypes.c_int32),
                 ("rope_inv_freq", ctypes.c_double * 32), ("rope_inv_freq_dev", ctypes.c_void_p)]
 
 
@@ -88,6 +88,10 @@ _SIGNATURES = {
     "lca_snapshot_layout": (_I32, [_CP, _SP]),
     "lca_cache_snapshot": (_I32, [_CP, _I32, _VP, _SZ, _SP, _VP]),
     "lca_cache_restore": (_I32, [_CP, _I32, _VP, _SZ, _SP, _VP]),
+    "lca_ragged_ingest": (_I32, [_CP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "lca_ragged_step": (_I32, [_CP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                               _VP, _VP, _VP, _SZ, _VP]),
+    "lca_ragged_snapshot": (_I32, [_CP, _I32, _I64, _VP, _SZ, _SP, _VP]),
     "lca_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -242,6 +246,29 @@ def lca_cache_restore(cache, seq, src, nbytes, info, stream=None):
                                                          ctypes.byref(info), _stream(stream)))
 
 
+def lca_ragged_ingest(cache, T_max, len_host, T_host, len_dev, T_dev, kv, gate, ik, ig, bias, idx_bias,
+                      stream=None):
+    """len_host / T_host: numpy int64 / int32 arrays [B] (the same values as len_dev / T_dev)."""
+    _check("lca_ragged_ingest", lib().lca_ragged_ingest(
+        ctypes.byref(cache), T_max, len_host.ctypes.data, T_host.ctypes.data, _ptr(len_dev), _ptr(T_dev), _ptr(kv),
+        _ptr(gate), _ptr(ik), _ptr(ig), _ptr(bias), _ptr(idx_bias), _stream(stream)))
+
+
+def lca_ragged_step(cache, T_max, len_host, T_host, len_dev, T_dev, kv, gate, ik, ig, bias, idx_bias, qI, w, q, topk,
+                    out, lse, ws, ws_bytes, stream=None):
+    _check("lca_ragged_step", lib().lca_ragged_step(
+        ctypes.byref(cache), T_max, len_host.ctypes.data, T_host.ctypes.data, _ptr(len_dev), _ptr(T_dev), _ptr(kv),
+        _ptr(gate), _ptr(ik), _ptr(ig), _ptr(bias), _ptr(idx_bias), _ptr(qI), _ptr(w), _ptr(q), _ptr(topk),
+        _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_ragged_snapshot(cache, seq, length, dst, nbytes, stream=None):
+    info = lca_snapshot_info()
+    _check("lca_ragged_snapshot", lib().lca_ragged_snapshot(ctypes.byref(cache), seq, length, _ptr(dst), nbytes,
+                                                             ctypes.byref(info), _stream(stream)))
+    return info
+
+
 def lca_status_str(status):
     return lib().lca_status_str(status).decode()
 
@@ -347,6 +374,42 @@ class DeviceLayer:
         """Restore a snapshot (device tensor from snapshot() or load_snapshot()) into sequence `seq`
         (-1: every sequence)."""
         lca_cache_restore(self.cache, seq, snap.data_ptr(), snap.numel(), info, stream)
+
+    # ---- ragged batches: the caller's per-sequence lengths travel with every call
+    def _ragged_arrays(self, lens, T):
+        import numpy as np
+        import torch
+        lh = np.ascontiguousarray(lens, dtype=np.int64)
+        th = np.ascontiguousarray(T, dtype=np.int32)
+        assert lh.shape == (self.batch,) and th.shape == (self.batch,)
+        ld = torch.from_numpy(lh).to(self.mem.device)
+        td = torch.from_numpy(th).to(self.mem.device)
+        return lh, th, ld, td
+
+    def ragged_ingest(self, lens, T, kv, gate=None, bias=None, ik=None, ig=None, idx_bias=None, stream=None):
+        """Sequence b (holding lens[b] tokens) adds the T[b] tokens in rows 0..T[b]-1 of kv[b] etc."""
+        lh, th, ld, td = self._ragged_arrays(lens, T)
+        lca_ragged_ingest(self.cache, kv.shape[1], lh, th, ld, td, kv, gate, ik, ig, bias, idx_bias, stream)
+        import torch
+        torch.cuda.current_stream().synchronize()  # the device copies of the arrays live until here
+
+    def ragged_step(self, lens, T, kv, q, out, gate=None, bias=None, ik=None, ig=None, idx_bias=None, qI=None, w=None,
+                    topk=None, lse=None, stream=None):
+        """One continuous-batching step: sequence b adds T[b] tokens and their queries attend."""
+        lh, th, ld, td = self._ragged_arrays(lens, T)
+        lca_ragged_step(self.cache, kv.shape[1], lh, th, ld, td, kv, gate, ik, ig, bias, idx_bias, qI, w, q, topk,
+                        out, lse, self.ws, self.ws_bytes, stream)
+        import torch
+        torch.cuda.current_stream().synchronize()
+
+    def ragged_snapshot(self, seq, length, stream=None):
+        import torch
+        info = lca_ragged_snapshot(self.cache, seq, length, None, 0)
+        buf = torch.empty(info.bytes + 256, dtype=torch.uint8, device=self.mem.device)
+        off = (-buf.data_ptr()) % 256
+        view = buf[off:off + info.bytes]
+        info = lca_ragged_snapshot(self.cache, seq, length, view.data_ptr(), info.bytes, stream)
+        return view, info
 
     def index_scores(self, Tq):
         """fp32 scores the last index_score / indexer_topk call left in the workspace: [B][Tq][max_blocks]."""

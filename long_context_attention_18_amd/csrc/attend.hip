@@ -268,7 +268,8 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   const int hgs = (a.H + 15) / 16;
   const int hg = blockIdx.x % hgs, split = blockIdx.x / hgs, q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int64_t t = a.len - a.Tq + tq;
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  if (t < 0) return;  // ragged batch: no query in this row
   // visible blocks; max_blocks bounds them (0 for the window-only layer, which has no compressed stream)
   const int64_t N = min((t + 1) / a.m, a.max_blocks);
   const bool do_select = MODE == kAttendSelect && N > a.k;

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int kg = lane >> 4, col = lane & 15;
   const int q = blockIdx.x;
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int64_t t = a.len - a.Tq + tq;
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  if (t < 0) return;  // ragged batch: no query in this row
   const int64_t N = min((t + 1) / a.m, a.max_blocks);  // 0 for the window-only layer
   const int64_t n_first = a.dense ? N : (int64_t)a.k;  // key slots before the window
   const int64_t total = n_first + a.W;

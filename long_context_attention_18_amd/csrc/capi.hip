@@ -172,7 +172,7 @@ lca_status compress_impl(lca_cache* c, bool csa, const uint16_t* kv, const uint1
   if (csa ? c->desc.kind != LCA_KIND_CSA : c->desc.kind != LCA_KIND_HCA) return LCA_ERR_UNSUPPORTED;
   if (csa && (!ik || !ig || !idx_bias || !c->idx_codes_dev || !c->idx_scale_dev)) return LCA_ERR_NULL;
   if (T < 1) return LCA_ERR_SHAPE;
-  if (c->pending != 0) return LCA_ERR_ORDER;
+  if (c->pending != 0 || c->ragged) return LCA_ERR_ORDER;
   if (c->len + T > c->max_ctx) return LCA_ERR_CAPACITY;
   IngestArgs a = ingest_args(c, kv, gate, ik, ig, T);
   a.bias = bias;
@@ -287,7 +287,7 @@ lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const u
   if (!swa && !gate_dev) return LCA_ERR_NULL;
   if (csa && (!ik_dev || !ig_dev)) return LCA_ERR_NULL;
   if (T < 1) return LCA_ERR_SHAPE;
-  if (cache->pending != (swa ? 0 : T)) return LCA_ERR_ORDER;  // the window-only layer has no compressor
+  if (cache->ragged || cache->pending != (swa ? 0 : T)) return LCA_ERR_ORDER;  // the window-only layer has no compressor
   if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
   IngestArgs a = ingest_args(cache, kv_dev, gate_dev, csa ? ik_dev : nullptr, csa ? ig_dev : nullptr, T);
   const int64_t end = cache->len + T;
@@ -316,7 +316,7 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   if (cache->desc.kind != LCA_KIND_CSA || !cache->idx_codes_dev) return LCA_ERR_UNSUPPORTED;
   if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
   if ((int64_t)cache->batch * Tq > kMaxGridY) return LCA_ERR_SHAPE;  // queries index grid.y
-  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (cache->pending != 0 || cache->ragged) return LCA_ERR_ORDER;
   if (!ws_dev) return LCA_ERR_WORKSPACE;
   WsLayout W = ws_layout(&cache->desc, cache->batch, Tq, cache->max_ctx);
   if (ws_bytes < W.total) return LCA_ERR_WORKSPACE;
@@ -389,7 +389,7 @@ lca_status attn_args(lca_cache* cache, int32_t kind, const uint16_t* q_dev, cons
   if (cache->desc.kind != kind) return LCA_ERR_UNSUPPORTED;
   const bool dense = kind != LCA_KIND_CSA;
   if (Tq < 1 || Tq > cache->len) return LCA_ERR_SHAPE;
-  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (cache->pending != 0 || cache->ragged) return LCA_ERR_ORDER;
   if ((int64_t)Tq + cache->desc.window - 1 > cache->ring) return LCA_ERR_CAPACITY;
   AttnArgs a{};
   a.q = q_dev;
@@ -493,7 +493,7 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
     return LCA_ERR_NULL;
   if (cache->desc.kind != LCA_KIND_CSA || !cache->idx_codes_dev) return LCA_ERR_UNSUPPORTED;
   if (T < 1 || (int64_t)cache->batch * T > kAttendMaxQueries) return LCA_ERR_SHAPE;
-  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (cache->pending != 0 || cache->ragged) return LCA_ERR_ORDER;
   if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
   lca_cache after = *cache;  // the cache once the T tokens are in: what the query kernels see
   after.len = cache->len + T;
@@ -638,22 +638,26 @@ extern "C" {
 
 lca_status lca_snapshot_layout(const lca_cache* cache, lca_snapshot_info* info) {
   if (!cache_ok(cache) || !info) return LCA_ERR_NULL;
-  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (cache->pending != 0 || cache->ragged) return LCA_ERR_ORDER;
   snapshot_layout(cache->desc.kind, cache->desc.m, cache->tail_width, cache->len,
                   std::min<int64_t>(cache->len, cache->ring), info);
   return LCA_OK;
 }
 
-lca_status lca_cache_snapshot(const lca_cache* cache, int32_t seq, void* dst_dev, size_t bytes,
-                              lca_snapshot_info* info, void* stream) {
-  if (!cache_ok(cache) || !dst_dev || !info) return LCA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+lca_status snapshot_impl(const lca_cache* cache, int32_t seq, int64_t len, void* dst_dev, size_t bytes,
+                         lca_snapshot_info* info, void* stream) {
   if (seq < 0 || seq >= cache->batch) return LCA_ERR_SHAPE;
   if (((uintptr_t)dst_dev) % kAlign != 0) return LCA_ERR_SHAPE;
   if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (len < 0 || len > cache->max_ctx) return LCA_ERR_SHAPE;
   lca_snapshot_info I;
   size_t sz[kSections];
-  snapshot_layout(cache->desc.kind, cache->desc.m, cache->tail_width, cache->len,
-                  std::min<int64_t>(cache->len, cache->ring), &I, sz);
+  snapshot_layout(cache->desc.kind, cache->desc.m, cache->tail_width, len, std::min<int64_t>(len, cache->ring), &I,
+                  sz);
   if (bytes < I.bytes) return LCA_ERR_CAPACITY;
   CopyArgs a{};
   state_runs(cache, seq, I, I.n_win, (uint8_t*)dst_dev, true, a);
@@ -666,6 +670,29 @@ lca_status lca_cache_snapshot(const lca_cache* cache, int32_t seq, void* dst_dev
   if (launch_copy_runs(a, 1, (hipStream_t)stream) != hipSuccess) return LCA_ERR_LAUNCH;
   *info = I;
   return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_cache_snapshot(const lca_cache* cache, int32_t seq, void* dst_dev, size_t bytes,
+                              lca_snapshot_info* info, void* stream) {
+  if (!cache_ok(cache) || !dst_dev || !info) return LCA_ERR_NULL;
+  if (cache->ragged) return LCA_ERR_ORDER;
+  return snapshot_impl(cache, seq, cache->len, dst_dev, bytes, info, stream);
+}
+
+lca_status lca_ragged_snapshot(const lca_cache* cache, int32_t seq, int64_t len, void* dst_dev, size_t bytes,
+                               lca_snapshot_info* info, void* stream) {
+  if (!cache_ok(cache) || !info) return LCA_ERR_NULL;
+  if (!dst_dev) {  // layout only
+    if (len < 0 || len > cache->max_ctx) return LCA_ERR_SHAPE;
+    snapshot_layout(cache->desc.kind, cache->desc.m, cache->tail_width, len, std::min<int64_t>(len, cache->ring),
+                    info);
+    return LCA_OK;
+  }
+  return snapshot_impl(cache, seq, len, dst_dev, bytes, info, stream);
 }
 
 lca_status lca_cache_restore(lca_cache* cache, int32_t seq, const void* src_dev, size_t bytes,
@@ -687,14 +714,139 @@ lca_status lca_cache_restore(lca_cache* cache, int32_t seq, const void* src_dev,
       std::memcmp(E.off, info->off, sizeof(E.off)) != 0)
     return LCA_ERR_SHAPE;
   if (bytes < info->bytes) return LCA_ERR_CAPACITY;
-  // every sequence of a cache holds the same number of tokens
-  if (seq >= 0 && cache->batch > 1 && cache->len != info->len) return LCA_ERR_SHAPE;
+  // every sequence of a uniform cache holds the same number of tokens
+  if (!cache->ragged && seq >= 0 && cache->batch > 1 && cache->len != info->len) return LCA_ERR_SHAPE;
   CopyArgs a{};
   const int64_t nw = std::min<int64_t>(info->n_win, cache->ring);
   state_runs(cache, seq < 0 ? 0 : seq, E, nw, (uint8_t*)const_cast<void*>(src_dev), false, a);
   if (launch_copy_runs(a, seq < 0 ? cache->batch : 1, (hipStream_t)stream) != hipSuccess) return LCA_ERR_LAUNCH;
-  cache->len = info->len;
+  if (!cache->ragged) cache->len = info->len;
   return LCA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- ragged batches
+namespace {
+
+// The per-sequence arrays of a ragged call, checked on the host; max_end = the most tokens any
+// sequence holds after the call (sizes the launches, whose workgroups beyond a sequence's own
+// work return at once).
+struct Ragged {
+  const int64_t* len_dev;
+  const int32_t* T_dev;
+  int32_t T_max;
+  int64_t max_end;
+  int64_t blocks;  // most blocks one sequence completes
+  int32_t units;   // most append units (window entries + tail rows) of one sequence
+};
+
+lca_status ragged_check(lca_cache* c, int32_t T_max, const int64_t* len_h, const int32_t* T_h,
+                        const int64_t* len_d, const int32_t* T_d, Ragged* r) {
+  if (!cache_ok(c) || !len_h || !T_h || !len_d || !T_d) return LCA_ERR_NULL;
+  if (T_max < 1 || T_max > (1 << 24)) return LCA_ERR_SHAPE;
+  if (c->pending != 0) return LCA_ERR_ORDER;
+  if (!c->ragged && c->len != 0) return LCA_ERR_ORDER;  // a cache turns ragged while empty
+  const int64_t m = c->desc.m;
+  *r = Ragged{len_d, T_d, T_max, 0, 0, 0};
+  for (int32_t b = 0; b < c->batch; ++b) {
+    const int64_t len = len_h[b];
+    const int32_t T = T_h[b];
+    if (len < 0 || T < 0 || T > T_max) return LCA_ERR_SHAPE;
+    if (len + T > c->max_ctx) return LCA_ERR_CAPACITY;
+    const int64_t end = len + T;
+    r->max_end = std::max(r->max_end, end);
+    if (c->desc.kind != LCA_KIND_SWA) r->blocks = std::max(r->blocks, end / m - len / m);
+    const int64_t win_first = std::max(len, end - (int64_t)c->ring);
+    const int64_t tail_first = std::max(len, c->desc.kind == LCA_KIND_SWA ? end : (end / m) * m);
+    r->units = std::max<int32_t>(r->units, (int32_t)((end - win_first) + (end - tail_first)));
+  }
+  return LCA_OK;
+}
+
+lca_status ragged_ingest_impl(lca_cache* c, const Ragged& r, const uint16_t* kv, const uint16_t* gate,
+                              const uint16_t* ik, const uint16_t* ig, const float* bias, const float* idx_bias,
+                              bool with_append, IngestArgs* app_out, hipStream_t s) {
+  const int32_t kind = c->desc.kind;
+  if (!kv) return LCA_ERR_NULL;
+  if (kind != LCA_KIND_SWA && (!gate || !bias)) return LCA_ERR_NULL;
+  if (kind == LCA_KIND_CSA && (!ik || !ig || !idx_bias)) return LCA_ERR_NULL;
+  const bool csa = kind == LCA_KIND_CSA;
+  IngestArgs a = ingest_args(c, kv, gate, csa ? ik : nullptr, csa ? ig : nullptr, r.T_max);
+  a.len = 0;
+  a.seq_len = r.len_dev;
+  a.seq_T = r.T_dev;
+  a.bias = bias;
+  a.idx_bias = csa ? idx_bias : nullptr;
+  if (r.blocks > 0 && launch_compress(a, csa, r.blocks, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  a.first = 0;
+  a.n_win = 0;  // per sequence in the kernel
+  if (app_out) *app_out = a;
+  if (with_append && launch_append(a, csa, r.units, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_ragged_ingest(lca_cache* cache, int32_t T_max, const int64_t* len_host, const int32_t* T_host,
+                             const int64_t* len_dev, const int32_t* T_dev, const uint16_t* kv_dev,
+                             const uint16_t* gate_dev, const uint16_t* ik_dev, const uint16_t* ig_dev,
+                             const float* bias_dev, const float* idx_bias_dev, void* stream) {
+  Ragged r;
+  lca_status st = ragged_check(cache, T_max, len_host, T_host, len_dev, T_dev, &r);
+  if (st != LCA_OK) return st;
+  st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, true, nullptr,
+                          (hipStream_t)stream);
+  if (st == LCA_OK) cache->ragged = 1;
+  return st;
+}
+
+lca_status lca_ragged_step(lca_cache* cache, int32_t T_max, const int64_t* len_host, const int32_t* T_host,
+                           const int64_t* len_dev, const int32_t* T_dev, const uint16_t* kv_dev,
+                           const uint16_t* gate_dev, const uint16_t* ik_dev, const uint16_t* ig_dev,
+                           const float* bias_dev, const float* idx_bias_dev, const uint16_t* qI_dev,
+                           const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev,
+                           float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  Ragged r;
+  lca_status st = ragged_check(cache, T_max, len_host, T_host, len_dev, T_dev, &r);
+  if (st != LCA_OK) return st;
+  if ((int64_t)cache->batch * T_max > kAttendMaxQueries) return LCA_ERR_SHAPE;
+  if (!kv_dev || !q_dev || !out_dev) return LCA_ERR_NULL;
+  const int32_t kind = cache->desc.kind;
+  // the queries' view: the cache after the call, sized by the longest sequence (the argument builders
+  // check shapes against it; the kernels take each sequence's own length from len_dev / T_dev)
+  lca_cache after = *cache;
+  after.ragged = 0;
+  after.len = std::max<int64_t>(r.max_end, T_max);
+  AttendArgs args{};
+  if (kind == LCA_KIND_CSA) {
+    st = score_args(&after, qI_dev, w_dev, true, T_max, topk_dev, false, ws_dev, ws_bytes, &args.s);
+    if (st != LCA_OK) return st;
+    args.s.seq_len = len_dev;
+    args.s.seq_T = T_dev;
+  }
+  st = attn_args(&after, kind, q_dev, nullptr, T_max, out_dev, lse_dev, &args.t);
+  if (st != LCA_OK) return st;
+  args.t.seq_len = len_dev;
+  args.t.seq_T = T_dev;
+  attend_workspace(&args, &after, T_max, ws_dev, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == LCA_KIND_CSA) {
+    // compress; score; candidate scan with the append in the same launch; selection + attention
+    IngestArgs app;
+    st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, false, &app, s);
+    if (st != LCA_OK) return st;
+    cache->ragged = 1;
+    if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (launch_topk_select(args.s, cache->batch, s, false, &app, r.units) != hipSuccess) return LCA_ERR_LAUNCH;
+    return launch_status(launch_attend(args, cache->batch, kAttendSelect, s));
+  }
+  st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, nullptr, nullptr, bias_dev, nullptr, true, nullptr, s);
+  if (st != LCA_OK) return st;
+  cache->ragged = 1;
+  return launch_status(launch_attend(args, cache->batch, kAttendDense, s));
 }
 
 }  // extern "C"

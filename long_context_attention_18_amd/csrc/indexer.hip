@@ -95,9 +95,10 @@ __device__ __forceinline__ float exact_block_score(const uint8_t* kc, int ks0, i
   return acc == 0.0f ? 0.0f : acc;
 }
 
-__device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int tq) {
-  int64_t t = a.len - a.Tq + tq;
-  return (t + 1) / a.m;
+// blocks visible to query row tq of sequence b (0 for a row without a query)
+__device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int b, int tq) {
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  return t < 0 ? 0 : (t + 1) / a.m;
 }
 
 // exclusive prefix sum of `v` over the 256 threads of a workgroup; *total gets the sum
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int N = (int)visible_blocks(a, tq);
+  const int N = (int)visible_blocks(a, b, tq);
   const int j_begin = blockIdx.x * kScoreChunk;
   if (j_begin >= N) return;
   const float* wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
@@ -401,7 +402,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs args) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int tq = q % a.Tq;
-  const int64_t N = visible_blocks(a, tq);
+  if (query_t(a.seq_len, a.seq_T, a.len, a.Tq, q / a.Tq, tq) < 0) return;  // ragged: no query in this row
+  const int64_t N = visible_blocks(a, q / a.Tq, tq);
   if (N <= a.k) {
     // every visible block is selected; one workgroup writes the list and clears the histogram
     if (blockIdx.x == 0) {
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs args) {
 __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   __shared__ SelectLds S;
   const int q = blockIdx.x;
-  const int64_t N = visible_blocks(a, q % a.Tq);
+  const int64_t N = visible_blocks(a, q / a.Tq, q % a.Tq);
   if (N <= a.k) return;
   for (int i = threadIdx.x; i < kHistBins; i += 512) q_hist(a, q)[i] = 0u;
   int32_t* out = a.topk + (size_t)q * a.k;

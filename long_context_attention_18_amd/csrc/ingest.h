@@ -12,12 +12,12 @@ namespace lca {
 
 constexpr int kTailKv = 0, kTailGate = 128, kTailIk = 256, kTailIg = 320;
 
-// BF16 input row of token p (absolute position) of sequence b: from the tail
-// if the token was appended by an earlier call, else from this call's input.
-__device__ __forceinline__ const uint16_t* token_row(const IngestArgs& a, int b, int64_t p, const uint16_t* in,
-                                                     int width, int tail_off) {
-  if (p < a.len) return a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width + tail_off;
-  return in + ((size_t)b * a.T + (size_t)(p - a.len)) * width;
+// BF16 input row of token p (absolute position) of sequence b, which held len tokens before this call:
+// from the tail if an earlier call appended it, else from this call's input (row stride a.T).
+__device__ __forceinline__ const uint16_t* token_row(const IngestArgs& a, int b, int64_t len, int64_t p,
+                                                     const uint16_t* in, int width, int tail_off) {
+  if (p < len) return a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width + tail_off;
+  return in + ((size_t)b * a.T + (size_t)(p - len)) * width;
 }
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -63,10 +63,21 @@ __device__ __forceinline__ void write_entry(double xn, double xr, int c, uint8_t
 // incomplete after this call into the tail.
 template <bool CSA>
 __device__ __forceinline__ void append_unit(const IngestArgs& a, int b, int unit, int c) {
-  if (unit < a.n_win) {
+  int64_t len = a.len, first = a.first, end = a.len + a.T;
+  int32_t n_win = a.n_win;
+  if (a.seq_len) {  // ragged batch: this sequence's own window tokens and tail rows; units beyond them idle
+    len = a.seq_len[b];
+    end = len + a.seq_T[b];
+    first = end - a.ring > len ? end - a.ring : len;
+    n_win = (int32_t)(end - first);
+    int64_t tail_first = (end / a.m) * a.m;
+    if (tail_first < len) tail_first = len;
+    if (unit >= n_win + (int32_t)(end - tail_first)) return;
+  }
+  if (unit < n_win) {
     // window entry of token s: its own kv, RoPE'd at s, its own FP8 scale
-    const int64_t s = a.first + unit;
-    const uint16_t* kv = a.kv + ((size_t)b * a.T + (size_t)(s - a.len)) * kHeadDim;
+    const int64_t s = first + unit;
+    const uint16_t* kv = a.kv + ((size_t)b * a.T + (size_t)(s - len)) * kHeadDim;
     double xn = (double)bf16_to_f32(kv[c]);
     double xr = rope_channel(kv, c, s, a.inv_freq);
     const size_t e = (size_t)b * a.ring + (size_t)(s % a.ring);
@@ -74,11 +85,10 @@ __device__ __forceinline__ void append_unit(const IngestArgs& a, int b, int unit
     return;
   }
   // tail: tokens of the block that is still incomplete after this call
-  const int64_t end = a.len + a.T;
   int64_t tail_first = (end / a.m) * a.m;
-  if (tail_first < a.len) tail_first = a.len;
-  const int64_t p = tail_first + (unit - a.n_win);
-  const size_t r = (size_t)b * a.T + (size_t)(p - a.len);
+  if (tail_first < len) tail_first = len;
+  const int64_t p = tail_first + (unit - n_win);
+  const size_t r = (size_t)b * a.T + (size_t)(p - len);
   uint16_t* dst = a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width;
   dst[kTailKv + c] = a.kv[r * kHeadDim + c];
   dst[kTailKv + 64 + c] = a.kv[r * kHeadDim + 64 + c];

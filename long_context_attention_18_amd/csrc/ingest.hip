@@ -26,19 +26,22 @@ template <bool CSA>
 __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
   const int c = threadIdx.x;
   const int b = blockIdx.y;
-  const int64_t j = a.first + blockIdx.x;
   const int m = a.m;
+  const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
+  const int64_t j = (a.seq_len ? len / m : a.first) + blockIdx.x;
+  // ragged batch: the blocks this sequence's own tokens complete (the grid covers the most of any)
+  if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;
   const int64_t p0 = j * m;
 
   // pass 1: per-channel max of gate + bias over the block's m positions
   double mu_n = -INFINITY, mu_r = -INFINITY, mu_i = -INFINITY;
   for (int i = 0; i < m; ++i) {
     const int64_t p = p0 + i;
-    const uint16_t* g = token_row(a, b, p, a.gate, kHeadDim, kTailGate);
+    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
     mu_n = fmax(mu_n, (double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]);
     mu_r = fmax(mu_r, (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]);
     if (CSA) {
-      const uint16_t* gi = token_row(a, b, p, a.ig, kIdxDim, kTailIg);
+      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
       mu_i = fmax(mu_i, (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]);
     }
   }
@@ -46,11 +49,11 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
   double S_n = 0.0, S_r = 0.0, S_i = 0.0;
   for (int i = 0; i < m; ++i) {
     const int64_t p = p0 + i;
-    const uint16_t* g = token_row(a, b, p, a.gate, kHeadDim, kTailGate);
+    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
     S_n = S_n + pool_exp(((double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]) - mu_n);
     S_r = S_r + pool_exp(((double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]) - mu_r);
     if (CSA) {
-      const uint16_t* gi = token_row(a, b, p, a.ig, kIdxDim, kTailIg);
+      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
       S_i = S_i + pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i);
     }
   }
@@ -58,15 +61,15 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
   double y_n = 0.0, y_r = 0.0, y_i = 0.0;
   for (int i = 0; i < m; ++i) {
     const int64_t p = p0 + i;
-    const uint16_t* g = token_row(a, b, p, a.gate, kHeadDim, kTailGate);
-    const uint16_t* kv = token_row(a, b, p, a.kv, kHeadDim, kTailKv);
+    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
+    const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
     double w_n = pool_exp(((double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]) - mu_n) / S_n;
     double w_r = pool_exp(((double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]) - mu_r) / S_r;
     y_n = fma(w_n, (double)bf16_to_f32(kv[c]), y_n);
     y_r = fma(w_r, rope_channel(kv, c, p, a.inv_freq), y_r);
     if (CSA) {
-      const uint16_t* gi = token_row(a, b, p, a.ig, kIdxDim, kTailIg);
-      const uint16_t* ki = token_row(a, b, p, a.ik, kIdxDim, kTailIk);
+      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
+      const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
       double w_i = pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i) / S_i;
       y_i = fma(w_i, (double)bf16_to_f32(ki[c]), y_i);
     }

@@ -50,6 +50,10 @@ struct IngestArgs {
   int32_t n_win;           // append: window tokens written
   int32_t B;
   const double* inv_freq;  // [32], device copy of the cache's RoPE frequencies
+  // ragged batches: sequence b holds seq_len[b] tokens before the call and adds seq_T[b] <= T of them
+  // (rows 0..seq_T[b]-1 of its inputs); null: every sequence holds len and adds T
+  const int64_t* seq_len;
+  const int32_t* seq_T;
 };
 
 // The indexer's workspace is one block per query (so its place does not depend on how many queries
@@ -72,7 +76,18 @@ struct ScoreArgs {
   int32_t m;
   int32_t G2;              // scan segments per query
   int32_t cmin;            // keys each score chunk counts into the histogram at least (twice its share of k)
+  // ragged batches (see IngestArgs): the queries of sequence b are its seq_T[b] new tokens, positions
+  // seq_len[b] + i for rows i < seq_T[b]; null: positions len - Tq + i
+  const int64_t* seq_len;
+  const int32_t* seq_T;
 };
+
+// Position of query row tq of sequence b, or -1 when the row holds no query (ragged batches)
+__device__ __forceinline__ int64_t query_t(const int64_t* seq_len, const int32_t* seq_T, int64_t len, int32_t Tq,
+                                           int b, int tq) {
+  if (seq_len) return tq < seq_T[b] ? seq_len[b] + tq : -1;
+  return len - Tq + tq;
+}
 
 __device__ __forceinline__ uint32_t* q_hist(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride); }
 __device__ __forceinline__ uint32_t* q_seg(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_seg); }
@@ -100,6 +115,8 @@ struct AttnArgs {
   int32_t ring;
   int32_t dense;           // 1 = HCA (every visible block), 0 = CSA (topk list)
   const double* inv_freq;  // [32], device copy of the cache's RoPE frequencies
+  const int64_t* seq_len;  // ragged batches, as in ScoreArgs
+  const int32_t* seq_T;
 };
 
 // One-launch attention for a few queries (attend.hip): the query's compressed entries come from the

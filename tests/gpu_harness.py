@@ -175,13 +175,14 @@ def _compare_blocks(run, v, b, d1, nb, report):
         assert np.array_equal(isc, d1["idx_scales"][:nb]), f"seq {b}: E8M0 bytes differ"
 
 
-def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positions=None):
+def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positions=None, lens=None):
     """Bit-exact block entries / indexer keys; window slots for the last R positions (or the last
-    window_positions of them)."""
+    window_positions of them). lens: each sequence's own length (ragged batches; default run.len)."""
     v = run.dev.views()
-    nb = 0 if run.swa else run.len // run.m
     report = {"rope_ulp1": 0, "rope_total": 0}
     for b in range(run.B):
+        L = run.len if lens is None else int(lens[b])
+        nb = 0 if run.swa else L // run.m
         d1, win = oracle_by_seq[b]
         if run.swa:
             assert "blk_codes" not in v
@@ -189,15 +190,15 @@ def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positi
             _compare_blocks(run, v, b, d1, nb, report)
         if check_window:
             R = run.dev.ring
-            lo = max(0, run.len - (R if window_positions is None else min(R, window_positions)))
-            pos = np.arange(lo, run.len)
+            lo = max(0, L - (R if window_positions is None else min(R, window_positions)))
+            pos = np.arange(lo, L)
             slots = pos % R
             wc = from_dev(v["win_codes"][b])[slots]
             ws = from_dev(v["win_scale"][b])[slots]
             wr = from_dev(v["win_rope"][b], np.uint16)[slots]
-            assert np.array_equal(wc, win["nope"][lo:run.len]), f"seq {b}: window FP8 codes differ"
-            assert np.array_equal(ws.view(np.uint32), win["scale"][lo:run.len].view(np.uint32))
-            assert bf16_ulp_diff(wr, win["rope"][lo:run.len]).max(initial=0) <= 1
+            assert np.array_equal(wc, win["nope"][lo:L]), f"seq {b}: window FP8 codes differ"
+            assert np.array_equal(ws.view(np.uint32), win["scale"][lo:L].view(np.uint32))
+            assert bf16_ulp_diff(wr, win["rope"][lo:L]).max(initial=0) <= 1
     return report
 
 

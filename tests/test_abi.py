@@ -299,3 +299,50 @@ def test_restore_rejects_bad_headers_and_shapes():
     assert c.len == 999
     assert L.lca_cache_snapshot(ctypes.byref(c), 2, P, big, ctypes.byref(lca.lca_snapshot_info()), None) == -2
     assert L.lca_cache_snapshot(ctypes.byref(c), 0, P, 16, ctypes.byref(lca.lca_snapshot_info()), None) == -4
+
+
+def test_ragged_calls_checks():
+    """Ragged batches: per-sequence lengths and token counts checked on the host before any launch;
+    a cache turns ragged only while empty and then refuses the uniform calls."""
+    import numpy as np
+    L = lca.lib()
+    c = _fake_bound_cache("csa")     # B = 1, max_ctx 4096, ring 128
+    c.batch = 3
+    P, big = 0x200000, 1 << 30
+    lens = np.array([0, 5, 4000], np.int64)
+    Ts = np.array([1, 0, 2], np.int32)
+
+    def ingest(lh, th, T_max=2, cache=c, dev=P):
+        return L.lca_ragged_ingest(ctypes.byref(cache), T_max, lh.ctypes.data, th.ctypes.data, dev, dev, P, P, P, P,
+                                   P, P, None)
+
+    def step(lh, th, T_max=2, ws=P, wsb=big, q=P):
+        return L.lca_ragged_step(ctypes.byref(c), T_max, lh.ctypes.data, th.ctypes.data, P, P, P, P, P, P, P, P, P, P,
+                                 q, None, P, None, ws, wsb, None)
+
+    assert ingest(lens, Ts, dev=None) == -1
+    assert ingest(lens, np.array([1, 0, 3], np.int32)) == -2                       # T[b] > T_max
+    assert ingest(lens, np.array([-1, 0, 0], np.int32)) == -2
+    assert ingest(np.array([0, -5, 0], np.int64), Ts) == -2
+    assert ingest(np.array([0, 5, 4095], np.int64), Ts) == -4                      # beyond max_ctx
+    assert ingest(lens, Ts, T_max=0) == -2
+    assert step(lens, Ts, T_max=171) == -2                                         # B * T_max > 511
+    assert step(lens, Ts, q=None) == -1
+    assert step(lens, Ts, ws=None, wsb=0) == -6                                    # CSA needs the workspace
+    assert step(lens, Ts, T_max=2) in (-4,)                                        # ring 128 < T_max + W - 1
+    c.len = 10
+    assert ingest(lens, Ts) == -5                                                  # not empty and not ragged
+    c.len = 0
+    c.ragged = 1                                                                   # as after a ragged call
+    assert L.lca_csa_compress(ctypes.byref(c), P, P, P, P, P, P, 1, None) == -5
+    assert L.lca_swa_tail_append(ctypes.byref(c), P, P, P, P, 1, None) == -5
+    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, big, None, None,
+                          None) == -5
+    info = lca.lca_snapshot_info()
+    assert L.lca_snapshot_layout(ctypes.byref(c), ctypes.byref(info)) == -5
+    assert L.lca_cache_snapshot(ctypes.byref(c), 0, P, big, ctypes.byref(info), None) == -5
+    # the ragged snapshot takes the sequence's length from the caller; NULL buffer = layout only
+    assert L.lca_ragged_snapshot(ctypes.byref(c), 0, 1001, None, 0, ctypes.byref(info), None) == 0
+    assert (info.len, info.n_blocks, info.n_win, info.n_tail) == (1001, 250, 128, 1)
+    assert L.lca_ragged_snapshot(ctypes.byref(c), 0, 5000, None, 0, ctypes.byref(info), None) == -2
+    assert L.lca_ragged_snapshot(ctypes.byref(c), 3, 10, P, big, ctypes.byref(info), None) == -2
