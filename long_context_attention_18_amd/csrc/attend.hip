@@ -431,37 +431,52 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
       for (int i = 0; i < 4; ++i) acc[i] += ov[i] * f;
     }
     if (splits > 1) {
-      // this split's partial; the last split of the (query, group) to finish merges all of them
+      // This split's partial; the last split of the (query, group) to finish merges all of them. The
+      // workgroups sit on different XCDs, whose L2s are not coherent with each other: the partials are
+      // written and read with agent-scope atomic stores and loads, which go to memory, so no L2
+      // writeback or invalidate is needed (an agent-scope release / acquire fence does both, for every
+      // dirty line of the L2, at several microseconds). Each thread waits for its own stores to
+      // complete before the workgroup counts itself in.
       AttendPartial* mine = args.part + ((size_t)q * hgs + hg) * splits + split;
-      *reinterpret_cast<v4f*>(&mine->o[h][d0]) = (v4f){acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __hip_atomic_store(&mine->o[h][d0 + i], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d0 == 0) {
-        mine->m[h] = M;
-        mine->l[h] = L;
+        __hip_atomic_store(&mine->m[h], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&mine->l[h], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       uint32_t* cnt = args.cnt + (size_t)q * hgs + hg;
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
       __syncthreads();
       if (tid == 0)
-        S.last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(splits - 1);
+        S.last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(splits - 1);
       __syncthreads();
       if (!S.last) return;
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        *cnt = 0u;  // every split has counted: ready for the next call
-      }
-      __syncthreads();
+      if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
       const AttendPartial* all = args.part + ((size_t)q * hgs + hg) * splits;
+      auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+      // every split's (m, l, o slice) loaded at once, unconditionally (a load behind a branch would make
+      // the compiler wait for all outstanding loads there: one memory round trip per split)
+      float mv[kAttendMaxSplits], lv[kAttendMaxSplits], ov[kAttendMaxSplits][4];
+#pragma unroll
+      for (int u = 0; u < kAttendMaxSplits; ++u) {
+        const int sp = min(u, splits - 1);
+        mv[u] = ld(&all[sp].m[h]);
+        lv[u] = ld(&all[sp].l[h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[u][i] = ld(&all[sp].o[h][d0 + i]);
+      }
       M = -INFINITY;
-      for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, all[sp].m[h]);
+#pragma unroll
+      for (int u = 0; u < kAttendMaxSplits; ++u) M = fmaxf(M, mv[u]);  // duplicates of the last split change nothing
       L = 0.0f;
       acc[0] = acc[1] = acc[2] = acc[3] = 0.0f;
-      for (int sp = 0; sp < splits; ++sp) {
-        const float ms = all[sp].m[h];
-        if (ms == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f((ms - M) * kC);
-        L += all[sp].l[h] * f;
-        const v4f ov = *reinterpret_cast<const v4f*>(&all[sp].o[h][d0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += ov[i] * f;
+      for (int u = 0; u < kAttendMaxSplits; ++u) {
+        // an empty split (m = -inf, l = 0, o = 0) weighs 0, and so does a duplicate
+        const float f = u < splits ? __builtin_amdgcn_exp2f((mv[u] - M) * kC) : 0.0f;
+        L += lv[u] * f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += ov[u][i] * f;
       }
     }
     const int hh = hg * 16 + h;
