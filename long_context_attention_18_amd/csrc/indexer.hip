@@ -142,22 +142,23 @@ __device__ __forceinline__ uint32_t from_partner_u(uint32_t x, int odd_row) {
   return odd_row ? r[0] : r[1];
 }
 
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t qcode_s[1][8 * 8];  // quantised query [head][8 words of 8 codes]
-  __shared__ int qscale_s[1][8 * 2];      // its E8M0 bytes [head][half]
-  __shared__ int guard_s[6];              // block-scale bounds inside which the MFMA sum is exact
-  __shared__ uint32_t flag_blk[kScoreChunk];  // blocks to rescore exactly (offset in chunk)
-  __shared__ uint32_t n_flag;
-  __shared__ uint32_t wmax_s[4];
-  __shared__ uint32_t range_s;
-  __shared__ int lo_s;
+// LDS of one score workgroup
+struct ScoreLds {
+  uint32_t hist[kHistBins];
+  uint32_t qcode[8 * 8];  // quantised query [head][8 words of 8 codes] (for the exact rescoring)
+  int qscale[8 * 2];      // its E8M0 bytes [head][half]
+  uint32_t flag_blk[kScoreWaves][kScoreIters * 32];  // per wave: blocks to rescore exactly (offset in chunk)
+  uint32_t n_flag[kScoreWaves];
+  uint32_t wmax[kScoreWaves];
+  uint32_t range;
+  int lo;
+};
+
+// One score workgroup's chunk: kScoreChunk blocks from j_begin. FULL: the whole chunk is visible, so
+// every key load is one base address plus a constant offset and no block needs a bounds test.
+template <bool FULL>
+__device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = blockIdx.y;
-  const int b = q / a.Tq, tq = q % a.Tq;
-  const int N = (int)visible_blocks(a, b, tq);
-  const int j_begin = blockIdx.x * kScoreChunk;
-  if (j_begin >= N) return;
   const float* wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
 
   // ---- loads, smallest first (vector loads return in order): the query slice this lane quantises
@@ -177,48 +178,64 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const uint8_t* scl = a.idx_scale + kbase * 2;
   const int wave_j0 = j_begin + wave * kScoreIters * 32;
   const int n2 = 2 * (lane & 15) + ((lane >> 4) >> 1);  // block of this lane inside a 32-block tile
-  // All of this wave's key loads (kScoreIters tiles x 16 B + 1 scale byte per lane), unconditional with
-  // the address clamped to the last visible block (always in bounds), so they issue back to back.
+  const int half = (lane >> 4) & 1;                      // which 16 bytes of its block's codes
+  // All of this wave's key loads (kScoreIters tiles x 16 B + 1 scale byte per lane), issued back to
+  // back: one base address plus constant offsets for a full chunk, else each address clamped to the
+  // last visible block (always in bounds).
   uint4 bvs[kScoreIters];
   int sbs[kScoreIters];
+  if (FULL) {
+    const uint8_t* cb = codes + (size_t)(wave_j0 + n2) * 32 + half * 16;
+    const uint8_t* sb = scl + (size_t)(wave_j0 + n2) * 2 + half;
 #pragma unroll
-  for (int it = 0; it < kScoreIters; ++it) {
-    int jb = wave_j0 + it * 32 + n2;
-    jb = jb < N ? jb : N - 1;
-    bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + ((lane >> 4) & 1) * 16);
-    sbs[it] = scl[(size_t)jb * 2 + ((lane >> 4) & 1)];
-  }
-  for (int i = tid; i < kHistBins; i += 256) hist[i] = 0;
-  if (tid == 0) n_flag = 0;
-
-  // ---- MX-FP4 query and the exactness bounds, once per workgroup by wave 0
-  if (wave == 0) {
-    uint32_t word = 0, sbyte = 0;
-    if (qh < a.HI) {
-      float x[8];
-      const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[2 * u] = __uint_as_float(rw[u] << 16);
-        x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-      if (amax > 0.0f) {
-        int E = ilogbf(amax) - 2;
-        E = E < -127 ? -127 : (E > 127 ? 127 : E);
-        sbyte = (uint32_t)(E + 127);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
-      }
+    for (int it = 0; it < kScoreIters; ++it) {
+      bvs[it] = *reinterpret_cast<const uint4*>(cb + it * 32 * 32);
+      sbs[it] = sb[it * 32 * 2];
     }
-    qcode_s[0][qh * 8 + qpart] = word;
-    if ((qpart & 3) == 0) qscale_s[0][qh * 2 + (qpart >> 2)] = (int)sbyte;
-    // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
-    // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
+  } else {
+#pragma unroll
+    for (int it = 0; it < kScoreIters; ++it) {
+      int jb = wave_j0 + it * 32 + n2;
+      jb = jb < N ? jb : N - 1;
+      bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + half * 16);
+      sbs[it] = scl[(size_t)jb * 2 + half];
+    }
+  }
+  for (int i = tid; i < kHistBins; i += 256) S.hist[i] = 0;  // used after the barrier that follows the loop
+  if (lane == 0) S.n_flag[wave] = 0;                          // this wave's own list: program order suffices
+
+  // ---- MX-FP4 query and the exactness bounds, computed by every wave for itself (no barrier: the
+  // values move between lanes by shuffles)
+  uint32_t word = 0, sbyte = 0;
+  if (qh < a.HI) {
+    float x[8];
+    const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[2 * u] = __uint_as_float(rw[u] << 16);
+      x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    if (amax > 0.0f) {
+      int E = ilogbf(amax) - 2;
+      E = E < -127 ? -127 : (E > 127 ? 127 : E);
+      sbyte = (uint32_t)(E + 127);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
+    }
+  }
+  if (wave == 0) {  // an LDS copy for the exact rescoring, read after the loop's barrier
+    S.qcode[qh * 8 + qpart] = word;
+    if ((qpart & 3) == 0) S.qscale[qh * 2 + (qpart >> 2)] = (int)sbyte;
+  }
+  // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
+  // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
+  int dlo, dhi, k0lo, k0hi, k1lo, k1hi;
+  {
     const int q0 = __shfl((int)sbyte, (lane & 7) * 8, 64), q1 = __shfl((int)sbyte, (lane & 7) * 8 + 4, 64);
     const bool live = (lane & 7) < a.HI;
     int g0 = live ? -10 - (q0 - q1) : -100000, g1 = live ? 10 - (q0 - q1) : 100000;
@@ -230,27 +247,25 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       g2 = max(g2, __shfl_xor(g2, o, 64)); g3 = min(g3, __shfl_xor(g3, o, 64));
       g4 = max(g4, __shfl_xor(g4, o, 64)); g5 = min(g5, __shfl_xor(g5, o, 64));
     }
-    if (lane == 0) {
-      guard_s[0] = g0; guard_s[1] = g1; guard_s[2] = g2; guard_s[3] = g3; guard_s[4] = g4; guard_s[5] = g5;
-    }
+    dlo = g0; dhi = g1; k0lo = g2; k0hi = g3; k1lo = g4; k1hi = g5;
   }
-  __syncthreads();  // quantised query, bounds, zeroed histogram and n_flag visible
-  const int dlo = guard_s[0], dhi = guard_s[1], k0lo = guard_s[2], k0hi = guard_s[3], k1lo = guard_s[4],
-            k1hi = guard_s[5];
   // ---- two A operands. Lane: row r = lane%16, K-group g = lane/16; row r holds (p, h) = (r/8, r%8)
-  // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only.
+  // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only: the
+  // words of head h's dims 32*(g%2) .. +32, held by lanes 8h + 4*(g%2) + u after the quantisation.
   const int r = lane & 15, g = lane >> 4, p = r >> 3, odd = g & 1;
   const int hA = r & 7, hB = (hA + 4) & 7;
-  uint32_t aA[4] = {0u, 0u, 0u, 0u}, aB[4] = {0u, 0u, 0u, 0u};
-  int sA = 127, sB = 127;
-  if ((g >> 1) == p) {
+  const bool own_group = (g >> 1) == p;
+  uint32_t aA[4], aB[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      aA[u] = qcode_s[0][hA * 8 + odd * 4 + u];
-      aB[u] = qcode_s[0][hB * 8 + odd * 4 + u];
-    }
-    sA = qscale_s[0][hA * 2 + odd];
-    sB = qscale_s[0][hB * 2 + odd];
+  for (int u = 0; u < 4; ++u) {
+    aA[u] = (uint32_t)__shfl((int)word, hA * 8 + odd * 4 + u, 64);
+    aB[u] = (uint32_t)__shfl((int)word, hB * 8 + odd * 4 + u, 64);
+  }
+  int sA = __shfl((int)sbyte, hA * 8 + odd * 4, 64), sB = __shfl((int)sbyte, hB * 8 + odd * 4, 64);
+  if (!own_group) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) aA[u] = aB[u] = 0u;
+    sA = sB = 127;
   }
   const v8i A0 = {(int)aA[0], (int)aA[1], (int)aA[2], (int)aA[3], 0, 0, 0, 0};
   const v8i A1 = {(int)aB[0], (int)aB[1], (int)aB[2], (int)aB[3], 0, 0, 0, 0};
@@ -259,7 +274,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) {
     const int tA = 2 * pr, tB = 2 * pr + 1;
-    const bool liveA = wave_j0 + tA * 32 + n2 < N, liveB = wave_j0 + tB * 32 + n2 < N;
+    const bool liveA = FULL || wave_j0 + tA * 32 + n2 < N, liveB = FULL || wave_j0 + tB * 32 + n2 < N;
     const uint4 bA = liveA ? bvs[tA] : make_uint4(0u, 0u, 0u, 0u);
     const uint4 bB = liveB ? bvs[tB] : make_uint4(0u, 0u, 0u, 0u);
     const int sbA = liveA ? sbs[tA] : 0, sbB = liveB ? sbs[tB] : 0;
@@ -273,9 +288,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     float e = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) e = fmaf(wlo[i], relu(odd ? accB[i] : accA[i]), e);
-    float s = from_partner(e, odd);
+    float sc = from_partner(e, odd);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(whi[i], relu(odd ? accA[i] : accB[i]), s);
+    for (int i = 0; i < 4; ++i) sc = fmaf(whi[i], relu(odd ? accA[i] : accB[i]), sc);
     // this lane now holds the final score of block jb: tile A if g is odd, tile B if even
     const int jb = wave_j0 + (odd ? tA : tB) * 32 + n2;
     const uint32_t other = from_partner_u((uint32_t)sbA | ((uint32_t)sbB << 8), odd);
@@ -285,22 +300,26 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int dk = ks0 - ks1;
     const bool bad = dk < dlo || dk > dhi || ks0 < k0lo || ks0 > k0hi || ks1 < k1lo || ks1 > k1hi;
     uint32_t key = 0;
-    if (jb < N) {
-      if (s == 0.0f) s = 0.0f;
-      key = order_key(s);
+    if (FULL || jb < N) {
+      if (sc == 0.0f) sc = 0.0f;
+      key = order_key(sc);
       keys[jb] = key;
-      if (bad) flag_blk[atomicAdd(&n_flag, 1u)] = (uint32_t)(jb - j_begin);
+      if (bad) S.flag_blk[wave][atomicAdd(&S.n_flag[wave], 1u)] = (uint32_t)(jb - j_begin);
     }
     lane_keys[pr] = key;
   }
   __syncthreads();
   // exact rescoring of the flagged blocks (none with real data); the reload below picks the new keys up
-  const uint32_t nf = n_flag;
-  for (uint32_t f = tid; f < nf; f += 256) {
-    const int jb = j_begin + (int)flag_blk[f];
-    const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
-                                       qcode_s[0], qscale_s[0], wq, a.HI);
-    keys[jb] = order_key(ex);
+  uint32_t nf = 0;
+  for (int w = 0; w < kScoreWaves; ++w) {
+    const uint32_t n = S.n_flag[w];
+    for (uint32_t f = tid; f < n; f += 256) {
+      const int jb = j_begin + (int)S.flag_blk[w][f];
+      const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
+                                         S.qcode, S.qscale, wq, a.HI);
+      keys[jb] = order_key(ex);
+    }
+    nf += n;
   }
   if (nf != 0) {
     __syncthreads();
@@ -308,7 +327,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int pr = 0; pr < kScoreIters / 2; ++pr) {
       const int jb = wave_j0 + ((odd ? 2 * pr : 2 * pr + 1)) * 32 + n2;
-      if (jb < N) lane_keys[pr] = keys[jb];
+      if (FULL || jb < N) lane_keys[pr] = keys[jb];
     }
   }
   // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
@@ -323,58 +342,69 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   for (int pr = 0; pr < kScoreIters / 2; ++pr) m = max(m, lane_keys[pr]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-  if (lane == 0) wmax_s[wave] = m;
+  if (lane == 0) S.wmax[wave] = m;
   __syncthreads();
-  const uint32_t kmax = max(max(wmax_s[0], wmax_s[1]), max(wmax_s[2], wmax_s[3]));
+  const uint32_t kmax = max(max(S.wmax[0], S.wmax[1]), max(S.wmax[2], S.wmax[3]));
   const int top_bin = (int)(kmax >> 20);
   const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) {
     const uint32_t key = lane_keys[pr];
-    if (key != 0 && (int)(key >> 20) >= low_bin) atomicAdd(&hist[key >> 20], 1u);
+    if (key != 0 && (int)(key >> 20) >= low_bin) atomicAdd(&S.hist[key >> 20], 1u);
   }
   __syncthreads();
   if (wave == 0) {
-    uint32_t v = (lane <= top_bin - low_bin) ? hist[low_bin + lane] : 0u;
+    uint32_t v = (lane <= top_bin - low_bin) ? S.hist[low_bin + lane] : 0u;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-    if (lane == 0) range_s = v;
+    if (lane == 0) S.range = v;
   }
   __syncthreads();
   int lo = low_bin;
-  if (range_s < (uint32_t)a.cmin && low_bin > 0) {
+  if (S.range < (uint32_t)a.cmin && low_bin > 0) {
     // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
 #pragma unroll
     for (int pr = 0; pr < kScoreIters / 2; ++pr) {
       const uint32_t key = lane_keys[pr];
-      if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&hist[key >> 20], 1u);
+      if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&S.hist[key >> 20], 1u);
     }
-    if (tid == 0) lo_s = 0;
+    if (tid == 0) S.lo = 0;
     __syncthreads();
     const int hi_b = kHistBins - 16 * tid;  // this thread: bins [hi_b - 16, hi_b), threads in descending order
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 1; i <= 16; ++i) cnt += hist[hi_b - i];
+    for (int i = 1; i <= 16; ++i) cnt += S.hist[hi_b - i];
     uint32_t tot;
-    const uint32_t excl = block_excl_scan(cnt, wmax_s, &tot);
+    const uint32_t excl = block_excl_scan(cnt, S.wmax, &tot);
     const uint32_t cm = (uint32_t)a.cmin;
     if (excl < cm && excl + cnt >= cm) {
       uint32_t c = excl;
       for (int i = 1; i <= 16; ++i) {
-        c += hist[hi_b - i];
+        c += S.hist[hi_b - i];
         if (c >= cm) {
-          lo_s = hi_b - i;
+          S.lo = hi_b - i;
           break;
         }
       }
     }
     __syncthreads();
-    lo = lo_s;
+    lo = S.lo;
   }
   for (int i = lo + tid; i <= top_bin; i += 256) {
-    const uint32_t c = hist[i];
+    const uint32_t c = S.hist[i];
     if (c) atomicAdd(&q_hist(a, q)[i], c);
   }
+}
+
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  __shared__ ScoreLds S;
+  const int q = blockIdx.y;
+  const int b = q / a.Tq, tq = q % a.Tq;
+  const int N = (int)visible_blocks(a, b, tq);
+  const int j_begin = blockIdx.x * kScoreChunk;
+  if (j_begin >= N) return;
+  if (j_begin + kScoreChunk <= N) score_chunk<true>(a, S, q, b, tq, N, j_begin);
+  else score_chunk<false>(a, S, q, b, tq, N, j_begin);
 }
 
 // Candidate scan: every key >= L (the bound the query's global histogram gives) is written, in index
