@@ -104,12 +104,7 @@ __device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int b, int
 // exclusive prefix sum of `v` over the 256 threads of a workgroup; *total gets the sum
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint32_t off = 0, tot = 0;
@@ -145,8 +140,9 @@ __device__ __forceinline__ uint32_t from_partner_u(uint32_t x, int odd_row) {
 // LDS of one score workgroup
 struct ScoreLds {
   uint32_t hist[kHistBins];
-  uint32_t qcode[8 * 8];  // quantised query [head][8 words of 8 codes] (for the exact rescoring)
+  uint32_t qcode[8 * 8];  // quantised query [head][8 words of 8 codes]
   int qscale[8 * 2];      // its E8M0 bytes [head][half]
+  int guard[6];           // block-scale bounds inside which the MFMA sum is exact
   uint32_t flag_blk[kScoreWaves][kScoreIters * 32];  // per wave: blocks to rescore exactly (offset in chunk)
   uint32_t n_flag[kScoreWaves];
   uint32_t wmax[kScoreWaves];
@@ -191,6 +187,9 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     for (int it = 0; it < kScoreIters; ++it) {
       bvs[it] = *reinterpret_cast<const uint4*>(cb + it * 32 * 32);
       sbs[it] = sb[it * 32 * 2];
+      // keep the tiles' loads in order: loads return in order, so the first tile pair can start as
+      // soon as its own data is in (a reordered issue would make it wait for most of the chunk)
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
@@ -199,43 +198,42 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
       jb = jb < N ? jb : N - 1;
       bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + half * 16);
       sbs[it] = scl[(size_t)jb * 2 + half];
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  for (int i = tid; i < kHistBins; i += 256) S.hist[i] = 0;  // used after the barrier that follows the loop
-  if (lane == 0) S.n_flag[wave] = 0;                          // this wave's own list: program order suffices
+  for (int i = tid; i < kHistBins; i += 256) S.hist[i] = 0;
+  if (lane == 0) S.n_flag[wave] = 0;
 
-  // ---- MX-FP4 query and the exactness bounds, computed by every wave for itself (no barrier: the
-  // values move between lanes by shuffles)
-  uint32_t word = 0, sbyte = 0;
-  if (qh < a.HI) {
-    float x[8];
-    const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+  // ---- MX-FP4 query and the exactness bounds, once per workgroup by wave 0 (every wave quantising it
+  // for itself avoids the barrier but costs more: the 2 waves per SIMD compete for the VALU while the
+  // keys stream in)
+  if (wave == 0) {
+    uint32_t word = 0, sbyte = 0;
+    if (qh < a.HI) {
+      float x[8];
+      const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[2 * u] = __uint_as_float(rw[u] << 16);
-      x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
+      for (int u = 0; u < 4; ++u) {
+        x[2 * u] = __uint_as_float(rw[u] << 16);
+        x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      if (amax > 0.0f) {
+        int E = ilogbf(amax) - 2;
+        E = E < -127 ? -127 : (E > 127 ? 127 : E);
+        sbyte = (uint32_t)(E + 127);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
+      }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    if (amax > 0.0f) {
-      int E = ilogbf(amax) - 2;
-      E = E < -127 ? -127 : (E > 127 ? 127 : E);
-      sbyte = (uint32_t)(E + 127);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
-    }
-  }
-  if (wave == 0) {  // an LDS copy for the exact rescoring, read after the loop's barrier
     S.qcode[qh * 8 + qpart] = word;
     if ((qpart & 3) == 0) S.qscale[qh * 2 + (qpart >> 2)] = (int)sbyte;
-  }
-  // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
-  // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
-  int dlo, dhi, k0lo, k0hi, k1lo, k1hi;
-  {
+    // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
+    // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
     const int q0 = __shfl((int)sbyte, (lane & 7) * 8, 64), q1 = __shfl((int)sbyte, (lane & 7) * 8 + 4, 64);
     const bool live = (lane & 7) < a.HI;
     int g0 = live ? -10 - (q0 - q1) : -100000, g1 = live ? 10 - (q0 - q1) : 100000;
@@ -247,25 +245,27 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
       g2 = max(g2, __shfl_xor(g2, o, 64)); g3 = min(g3, __shfl_xor(g3, o, 64));
       g4 = max(g4, __shfl_xor(g4, o, 64)); g5 = min(g5, __shfl_xor(g5, o, 64));
     }
-    dlo = g0; dhi = g1; k0lo = g2; k0hi = g3; k1lo = g4; k1hi = g5;
+    if (lane == 0) {
+      S.guard[0] = g0; S.guard[1] = g1; S.guard[2] = g2; S.guard[3] = g3; S.guard[4] = g4; S.guard[5] = g5;
+    }
   }
+  __syncthreads();  // quantised query and bounds visible
+  const int dlo = S.guard[0], dhi = S.guard[1], k0lo = S.guard[2], k0hi = S.guard[3], k1lo = S.guard[4],
+            k1hi = S.guard[5];
   // ---- two A operands. Lane: row r = lane%16, K-group g = lane/16; row r holds (p, h) = (r/8, r%8)
-  // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only: the
-  // words of head h's dims 32*(g%2) .. +32, held by lanes 8h + 4*(g%2) + u after the quantisation.
+  // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only.
   const int r = lane & 15, g = lane >> 4, p = r >> 3, odd = g & 1;
   const int hA = r & 7, hB = (hA + 4) & 7;
-  const bool own_group = (g >> 1) == p;
-  uint32_t aA[4], aB[4];
+  uint32_t aA[4] = {0u, 0u, 0u, 0u}, aB[4] = {0u, 0u, 0u, 0u};
+  int sA = 127, sB = 127;
+  if ((g >> 1) == p) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    aA[u] = (uint32_t)__shfl((int)word, hA * 8 + odd * 4 + u, 64);
-    aB[u] = (uint32_t)__shfl((int)word, hB * 8 + odd * 4 + u, 64);
-  }
-  int sA = __shfl((int)sbyte, hA * 8 + odd * 4, 64), sB = __shfl((int)sbyte, hB * 8 + odd * 4, 64);
-  if (!own_group) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) aA[u] = aB[u] = 0u;
-    sA = sB = 127;
+    for (int u = 0; u < 4; ++u) {
+      aA[u] = S.qcode[hA * 8 + odd * 4 + u];
+      aB[u] = S.qcode[hB * 8 + odd * 4 + u];
+    }
+    sA = S.qscale[hA * 2 + odd];
+    sB = S.qscale[hB * 2 + odd];
   }
   const v8i A0 = {(int)aA[0], (int)aA[1], (int)aA[2], (int)aA[3], 0, 0, 0, 0};
   const v8i A1 = {(int)aB[0], (int)aB[1], (int)aB[2], (int)aB[3], 0, 0, 0, 0};
@@ -496,12 +496,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs args) {
   if (wave == 0) {
     // exclusive scan of the kPer*8 counts in (u, wave) order; two per lane
     uint32_t c0 = cnt_s[2 * lane], c1 = cnt_s[2 * lane + 1];
-    uint32_t incl = c0 + c1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const uint32_t incl = wave_incl_scan(c0 + c1);
     uint32_t excl = incl - c0 - c1;
     cnt_s[2 * lane] = excl;
     cnt_s[2 * lane + 1] = excl + c0;

@@ -82,6 +82,19 @@ struct ScoreArgs {
   const int32_t* seq_T;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row broadcasts (GFX9
+// data-parallel primitives: one VALU add each, no LDS round trip): lanes shifted in from outside a
+// 16-lane row contribute 0, and rows 1-3 then take the running totals of the rows before them.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // Position of query row tq of sequence b, or -1 when the row holds no query (ragged batches)
 __device__ __forceinline__ int64_t query_t(const int64_t* seq_len, const int32_t* seq_T, int64_t len, int32_t Tq,
                                            int b, int tq) {

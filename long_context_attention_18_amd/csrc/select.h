@@ -8,15 +8,17 @@
 // Input: the candidates the scan left in index order, one segment per scan
 // workgroup (every key >= a lower bound of the k-th key), or, when there are
 // more than fit in LDS, every visible block's key. Radix select finds the
-// k-th largest 64-bit key, 8 bits at a time from the highest bit in which the
-// elements differ; an order-preserving compaction then writes the winners in
-// ascending block index to `out` (global or LDS), without a sort.
+// k-th largest 64-bit key, 11 bits at a time from the highest bit in which the
+// elements differ, until the bin that holds it is taken whole or holds at most
+// 64 elements, which one wave then ranks directly; an order-preserving
+// compaction writes the winners in ascending block index to `out` (global or
+// LDS), without a sort.
 #pragma once
 #include "kernels.h"
 
 namespace lca {
 
-constexpr int kRadixBits = 11;  // digit width of the radix select: 2048 LDS bins, two passes in the common case
+constexpr int kRadixBits = 11;  // digit width of the radix select: 2048 LDS bins
 constexpr int kRadixBins = 1 << kRadixBits;
 
 struct SelectLds {
@@ -26,17 +28,15 @@ struct SelectLds {
   uint32_t wsum[8];
   uint32_t sel_digit, sel_above, sel_count, flat_needed;
   uint64_t red_lo[8], red_hi[8];
+  uint64_t small[64];  // a boundary bin of at most 64 elements, ranked directly
+  uint32_t small_n;
+  uint64_t sel_thresh;
 };
 
 // exclusive prefix sum over the 512 threads of the workgroup (thread order); every thread calls it
 __device__ __forceinline__ uint32_t excl_scan_512(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint32_t off = 0;
@@ -74,12 +74,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   for (int g0 = 0; g0 < G2_q; g0 += 512) {
     const int gi = g0 + tid;
     const uint32_t c = gi < G2_q ? q_seg(a, q)[gi] : 0u;
-    uint32_t incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const uint32_t incl = wave_incl_scan(c);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     uint32_t base = g0 == 0 ? 0u : seg_off[g0];
@@ -203,6 +198,28 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
       prefix |= (uint64_t)d << sh;
       mask |= dmask << sh;
       if (S.sel_count == need) break;
+      if (S.sel_count <= 64) {
+        // a small boundary bin: gather its elements and find the need-th largest by direct ranking
+        // (keys are unique, so exactly one element has need-1 larger ones) instead of another pass
+        if (tid == 0) S.small_n = 0u;
+        __syncthreads();
+        for (int64_t i = tid; i < n; i += 512) {
+          const uint64_t e = elem(i);
+          if ((e & mask) == prefix) S.small[atomicAdd(&S.small_n, 1u)] = e;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const uint32_t c = S.sel_count;
+          const uint64_t mine = lane < (int)c ? S.small[lane] : 0ull;
+          uint32_t rank = 0;
+          for (uint32_t m = 0; m < c; ++m) rank += S.small[m] > mine ? 1u : 0u;
+          if (lane < (int)c && rank == need - 1) S.sel_thresh = mine;
+        }
+        __syncthreads();
+        prefix = S.sel_thresh;  // the winners are exactly the elements >= the need-th largest of the bin
+        mask = ~0ull;
+        break;
+      }
     }
   }
   // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run
