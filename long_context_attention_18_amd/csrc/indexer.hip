@@ -101,7 +101,7 @@ __device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int b, int
   return t < 0 ? 0 : (t + 1) / a.m;
 }
 
-// exclusive prefix sum of `v` over the 256 threads of a workgroup; *total gets the sum
+// exclusive prefix sum of `v` over the threads of a workgroup; *total gets the sum
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
@@ -201,7 +201,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  for (int i = tid; i < kHistBins; i += 256) S.hist[i] = 0;
+  for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
   if (lane == 0) S.n_flag[wave] = 0;
 
   // ---- MX-FP4 query and the exactness bounds, once per workgroup by wave 0 (every wave quantising it
@@ -313,7 +313,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   uint32_t nf = 0;
   for (int w = 0; w < kScoreWaves; ++w) {
     const uint32_t n = S.n_flag[w];
-    for (uint32_t f = tid; f < n; f += 256) {
+    for (uint32_t f = tid; f < n; f += kScoreThreads) {
       const int jb = j_begin + (int)S.flag_blk[w][f];
       const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
                                          S.qcode, S.qscale, wq, a.HI);
@@ -344,7 +344,9 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
   if (lane == 0) S.wmax[wave] = m;
   __syncthreads();
-  const uint32_t kmax = max(max(S.wmax[0], S.wmax[1]), max(S.wmax[2], S.wmax[3]));
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int w = 0; w < kScoreWaves; ++w) kmax = max(kmax, S.wmax[w]);
   const int top_bin = (int)(kmax >> 20);
   const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
 #pragma unroll
@@ -370,16 +372,17 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     }
     if (tid == 0) S.lo = 0;
     __syncthreads();
-    const int hi_b = kHistBins - 16 * tid;  // this thread: bins [hi_b - 16, hi_b), threads in descending order
+    constexpr int kPerT = kHistBins / kScoreThreads;  // bins per thread
+    const int hi_b = kHistBins - kPerT * tid;  // this thread: bins [hi_b - kPerT, hi_b), threads in descending order
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 1; i <= 16; ++i) cnt += S.hist[hi_b - i];
+    for (int i = 1; i <= kPerT; ++i) cnt += S.hist[hi_b - i];
     uint32_t tot;
     const uint32_t excl = block_excl_scan(cnt, S.wmax, &tot);
     const uint32_t cm = (uint32_t)a.cmin;
     if (excl < cm && excl + cnt >= cm) {
       uint32_t c = excl;
-      for (int i = 1; i <= 16; ++i) {
+      for (int i = 1; i <= kPerT; ++i) {
         c += S.hist[hi_b - i];
         if (c >= cm) {
           S.lo = hi_b - i;
@@ -390,13 +393,13 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     __syncthreads();
     lo = S.lo;
   }
-  for (int i = lo + tid; i <= top_bin; i += 256) {
+  for (int i = lo + tid; i <= top_bin; i += kScoreThreads) {
     const uint32_t c = S.hist[i];
     if (c) atomicAdd(&q_hist(a, q)[i], c);
   }
 }
 
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   __shared__ ScoreLds S;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
@@ -536,7 +539,7 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
   if (N_last <= a.k) return hipSuccess;  // every visible block is selected; no scores needed
   const unsigned nq = (unsigned)(B * a.Tq);
   unsigned g1 = (unsigned)((N_last + kScoreChunk - 1) / kScoreChunk);
-  hipLaunchKernelGGL(score_kernel, dim3(g1, nq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(score_kernel, dim3(g1, nq), dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
 }
 

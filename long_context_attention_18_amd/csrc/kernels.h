@@ -12,9 +12,10 @@ constexpr int kRope = 64;
 constexpr int kIdxDim = 64;
 
 // ---- indexer / top-k tiling --------------------------------------------
-constexpr int kScoreWaves = 4;                        // waves per score workgroup
-constexpr int kScoreIters = 16;                       // 32-block tiles per wave
+constexpr int kScoreWaves = 8;                        // waves per score workgroup
+constexpr int kScoreIters = 8;                        // 32-block tiles per wave
 constexpr int kScoreChunk = kScoreWaves * kScoreIters * 32;  // blocks per workgroup (2048)
+constexpr int kScoreThreads = kScoreWaves * 64;
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
