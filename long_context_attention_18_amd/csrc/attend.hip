@@ -35,6 +35,7 @@
 // tt, so each lane's B operand for P^T is exactly the 8 logits it holds. The
 // FP8 codes and BF16 RoPE dims are exact in bf16; the fp32 scale multiplies
 // the nope logits and is folded into P for the nope output dims.
+#include "attn_common.h"
 #include "dev_formats.h"
 #include "kernels.h"
 #include "select.h"
@@ -42,13 +43,6 @@
 namespace lca {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kChunk = 32;     // keys per wave step: two 16-key tiles
@@ -71,45 +65,6 @@ struct AttendLds {
   int last;                // this workgroup merges the splits
   float cos_t[32], sin_t[32];
 };
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// value held by lane l ^ 16 / l ^ 32 (VALU lane swaps)
-__device__ __forceinline__ float xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
-}
-
-// 8 E4M3FN codes (little-endian bytes) -> 8 bf16: v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts
-// two codes exactly (every E4M3FN value is a bf16 value; checked for all 256 codes on MI355X)
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 c) {
-  u32x4 o;
-  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false));
-  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true));
-  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false));
-  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true));
-  return o;
-}
-
-// two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed low first
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-// Load through a global-address-space pointer (a global_load, counted by vmcnt only).
-template <typename T>
-__device__ __forceinline__ T ldg(const void* p) {
-  typedef const __attribute__((address_space(1))) T global_t;
-  return *(global_t*)p;
-}
 
 // One 32-key chunk's raw gathered data, as lane (r, g) holds it: key r of tiles 0 and 1.
 struct Raw {
@@ -172,7 +127,7 @@ struct Keys {
 __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int end, const bf16x8 (&qb)[4], float* scl,
                                              uint16_t* vt, int kpos, int r, int g, float& m_run, float& l_run,
                                              v4f (&O)[8]) {
-  constexpr float kC = 0.12751743074640293f;  // log2(e) / sqrt(128)
+  constexpr float kC = kLog2eRsqrtD;
   constexpr float kLazy = 8.0f;
   u32x4 kn0[2], kn1[2];
   float Sv[2][4];
@@ -301,11 +256,8 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   // RoPE angles of position t: reduced to [-pi, pi] in fp64 (2 pi as a double plus its remainder),
   // then fp32 sin / cos; the rotated query is rounded to bf16, far coarser than either step
   if (tid < 32) {
-    const double phi = (double)t * a.inv_freq[tid];
-    const double n = rint(phi * 0.15915494309189535);
-    const double rr = (phi - n * 6.28318530717958623) - n * 2.4492935982947064e-16;
     float sn, cs;
-    sincosf((float)rr, &sn, &cs);
+    rope_angle(t, a.inv_freq[tid], &sn, &cs);
     S.cos_t[tid] = cs;
     S.sin_t[tid] = sn;
   }
@@ -415,7 +367,7 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   {
     const int h = tid >> 5, d0 = (tid & 31) * 4;
     // wave states in raw logit units (q . x): weight 2^((m_w - M) log2(e) / sqrt(128))
-    constexpr float kC = 0.12751743074640293f;
+    constexpr float kC = kLog2eRsqrtD;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.u.c.m[w][h]);

@@ -1,28 +1,24 @@
-// attention.hip -- CSA sparse / HCA dense attention with the sliding-window
-// branch under one softmax, for gfx950.
+// attention.hip -- CSA sparse / HCA dense / window-only attention with the sliding-window branch
+// under one softmax, for calls with many queries (chunked prefill), on gfx950.
 //
-// Figure 3 of "DeepSeek-V4: a million-token context that agents can actually
-// use" (CSA: the selected compressed blocks plus a sliding-window branch over
-// the recent uncompressed tokens) and Figure 4 / the HCA paragraph (every
-// compressed block, densely, plus the same window). Per query t and head h:
+// Figure 3 of "DeepSeek-V4: a million-token context that agents can actually use" (CSA: the selected
+// compressed blocks plus a sliding-window branch over the recent uncompressed tokens) and Figure 4 /
+// the HCA paragraph (every compressed block, densely, plus the same window). Per query t and head h:
 //   keys  = {D1 entries: top-k list (CSA) or all j < (t+1)/m (HCA)}
 //           + {window entries of positions max(0, t-W+1) .. t}
 //   logit = RoPE(q_h, t) . x / sqrt(128),  K = V = the dequantised entry
 //   out   = softmax over ALL keys (one normalisation) . x
 //
-// All query heads share the one KV head, so per query this is a
-// [H x 128] x [128 x keys] product followed by [H x keys] x [keys x 128]:
-// both run on v_mfma_f32_16x16x32_bf16 with heads as the M dimension. The
-// FP8 codes and the BF16 RoPE dims are exact in bf16; the per-entry fp32
-// scale is applied to the nope part of the logits (S = S_nope*scale +
-// S_rope) and folded into P for the nope output dims (O_nope = (P*scale).C),
-// so no dequantised copy is rounded. The rotated query is rounded to bf16.
-//
-// This kernel serves calls with many queries (chunked prefill); calls with
-// fewer than 512 go to attend.hip. Grid: one workgroup per query (4 waves,
-// 16 heads each) walks the key list 64 keys at a time: gathers the entries
-// into LDS (key-major for Q.K^T, dim-major for P.V), keeps a running max /
-// sum per head (online softmax) and writes the normalised output.
+// All query heads share the one KV head. One workgroup per query, one wave per 16 heads. The keys go
+// 32 at a time through LDS, gathered, converted and transposed once for all heads: every thread
+// brings in 8 dims of two keys (key r of the two 16-key tiles), writes them key-major for S^T = K.Q^T
+// (keys as the MFMA's M dimension) and, as pairs (tile 0, tile 1) of one dim, dim-major for
+// O^T = V^T.P^T. The S^T accumulator is exactly the B operand of that product when MFMA K index
+// 8g + 2v + t is key 4g+v of tile t, so P never leaves registers. The FP8 codes and the BF16 RoPE dims
+// are exact in bf16; the per-entry fp32 scale multiplies the nope logits and is folded into P for the
+// nope output dims. The next chunk's gathers are issued before the current chunk is computed, into
+// the second of two LDS buffers, one barrier per chunk. Calls with up to 511 queries use attend.hip.
+#include "attn_common.h"
 #include "dev_formats.h"
 #include "kernels.h"
 
@@ -30,236 +26,254 @@ namespace lca {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+constexpr int kMWaves = 4;       // one wave per 16-head group
+constexpr int kMThreads = kMWaves * 64;
+constexpr int kMChunk = 32;      // keys per step: two 16-key tiles
+constexpr int kKdStride = 136;   // bf16 per key-major row (128 + 8 pad)
+constexpr int kMVtStride = 40;   // bf16 per dim-major row (32 keys + 8 pad; 80 B keeps 16-B reads aligned)
 
-constexpr int KC = kAttnKeys;   // 64 keys per iteration
-constexpr int KD_STRIDE = 136;  // bf16 per Kd row (128 + 8 pad)
-constexpr int VT_STRIDE = 72;   // bf16 per Vt row (64 + 8 pad)
-constexpr int P_STRIDE = 72;
+struct ManyLds {
+  uint16_t kd[2][kMChunk * kKdStride];    // key-major chunk (two buffers)
+  uint16_t vt[2][kHeadDim * kMVtStride];  // dim-major chunk, keys in MFMA K order
+  float scl[2][kMChunk];                  // the keys' FP8 scales (>= 0); -1 marks a slot without a key
+  int32_t list[kMaxTopk];                 // CSA: the query's top-k row
+  float cos_t[32], sin_t[32];
+};
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// The gather of one thread for one chunk: part pp = tid / 16 (dims 8pp .. 8pp+7; pp < 8 the FP8 nope
+// codes, pp >= 8 the BF16 RoPE dims), key r = tid % 16 of both tiles.
+struct Fetch {
+  u32x2 code[2];
+  u32x4 rope[2];
+  float scale[2];
+  bool valid[2];
+};
+
+struct Query {
+  const uint8_t *blk_codes, *win_codes;
+  const uint16_t *blk_rope, *win_rope;
+  const float *blk_scale, *win_scale;
+  size_t blk_row, win_row;  // b * max_blocks, b * ring
+  int64_t t, N;
+  int32_t n_first, total, W, ring;
+  bool dense;
+};
+
+// entry of key slot `slot`: slots [0, n_first) the top-k row or the dense blocks, then the window of
+// positions t-W+1 .. t; branch-free, with an in-bounds entry for slots that hold no key
+__device__ __forceinline__ void slot_entry(const Query& Q, const int32_t* list, int slot, size_t* e, bool* win,
+                                           bool* valid) {
+  const bool in_first = slot < Q.n_first;
+  const int ls = in_first ? slot : 0;
+  const int64_t j = Q.dense ? (int64_t)ls : (int64_t)list[ls];
+  const int64_t s = Q.t - Q.W + 1 + (slot - Q.n_first);
+  const bool ok_blk = j >= 0 && j < Q.N;
+  const bool ok_win = s >= 0;
+  *valid = slot < Q.total && (in_first ? ok_blk : ok_win);
+  *win = !in_first;
+  const int64_t jc = ok_blk ? j : 0;
+  const int64_t sc = ok_win ? s : 0;
+  *e = in_first ? Q.blk_row + (size_t)jc : Q.win_row + (size_t)(sc % Q.ring);
 }
 
-__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
-  u32x4 v = *reinterpret_cast<const u32x4*>(p);
-  return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int chunk0, int pp, int r, Fetch& F) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    size_t e;
+    bool w, ok;
+    slot_entry(Q, list, chunk0 + tt * 16 + r, &e, &w, &ok);
+    F.valid[tt] = ok;
+    if (pp < 8) {
+      F.code[tt] = ldg<u32x2>((w ? Q.win_codes : Q.blk_codes) + e * kNope + 8 * pp);
+      F.scale[tt] = ldg<float>((w ? Q.win_scale : Q.blk_scale) + e);
+    } else {
+      F.rope[tt] = ldg<u32x4>((w ? Q.win_rope : Q.blk_rope) + e * kRope + 8 * (pp - 8));
+    }
+  }
 }
 
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kd[KC * KD_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * VT_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Pn[4 * 16 * P_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Pr[4 * 16 * P_STRIDE];
-  __shared__ float kscale[KC];
-  __shared__ int kvalid[KC];
+// the fetched dims into the chunk buffers: key-major rows and (tile 0, tile 1) pairs of dim-major rows
+__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, uint16_t* vt, float* scl) {
+  u32x4 v[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    v[tt] = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
+    if (!F.valid[tt]) v[tt] = zero;
+    *reinterpret_cast<u32x4*>(kd + (tt * 16 + r) * kKdStride + 8 * pp) = v[tt];
+  }
+  const int kpos = 8 * (r >> 2) + 2 * (r & 3);  // MFMA K index of key r of tile 0 (tile 1: +1)
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t pair = __builtin_amdgcn_perm(v[1][u >> 1], v[0][u >> 1], (u & 1) ? 0x07060302u : 0x05040100u);
+    *reinterpret_cast<uint32_t*>(vt + (8 * pp + u) * kMVtStride + kpos) = pair;
+  }
+  if (pp == 0) {
+    scl[r] = F.valid[0] ? F.scale[0] : -1.0f;
+    scl[16 + r] = F.valid[1] ? F.scale[1] : -1.0f;
+  }
+}
 
+__global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
+  __shared__ ManyLds S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kg = lane >> 4, col = lane & 15;
+  const int r = lane & 15, g = lane >> 4;
   const int q = blockIdx.x;
   const int b = q / a.Tq, tq = q % a.Tq;
   const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
   if (t < 0) return;  // ragged batch: no query in this row
-  const int64_t N = min((t + 1) / a.m, a.max_blocks);  // 0 for the window-only layer
-  const int64_t n_first = a.dense ? N : (int64_t)a.k;  // key slots before the window
-  const int64_t total = n_first + a.W;
-  const int64_t s_begin = 0, s_end = total;
 
-  // ---- rotated query, as A operands: row = head (wave*16 + col), K-group kg, 4 K-steps of 32 dims
-  const int head = wave * 16 + col;
+  Query Q;
+  Q.blk_codes = a.blk_codes;
+  Q.win_codes = a.win_codes;
+  Q.blk_rope = a.blk_rope;
+  Q.win_rope = a.win_rope;
+  Q.blk_scale = a.blk_scale;
+  Q.win_scale = a.win_scale;
+  Q.blk_row = (size_t)b * a.max_blocks;
+  Q.win_row = (size_t)b * a.ring;
+  Q.t = t;
+  Q.N = min((t + 1) / a.m, a.max_blocks);  // 0 for the window-only layer
+  Q.dense = a.dense != 0;
+  Q.n_first = Q.dense ? (int32_t)Q.N : a.k;
+  Q.total = Q.n_first + a.W;
+  Q.W = a.W;
+  Q.ring = a.ring;
+
+  // RoPE angles of position t, the top-k row (CSA), the query rows (head 16 * wave + r, dims 32 ks + 8 g)
+  if (tid < 32) {
+    float sn, cs;
+    rope_angle(t, a.inv_freq[tid], &sn, &cs);
+    S.cos_t[tid] = cs;
+    S.sin_t[tid] = sn;
+  }
+  if (!Q.dense) {
+    const int32_t* row = a.topk + ((size_t)b * a.Tq + tq) * a.k;
+    for (int i = tid; i < a.k; i += kMThreads) S.list[i] = row[i];
+  }
+  const int head = wave * 16 + r;
   const bool head_ok = head < a.H;
-  bf16x8 qa[4];
+  u32x4 qraw[4];
   {
     const uint16_t* qp = a.q + (((size_t)b * a.Tq + tq) * a.H + (head_ok ? head : 0)) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = ks * 32 + 8 * kg;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (head_ok) raw = *reinterpret_cast<const u32x4*>(qp + d0);
-      if (ks >= 2 && head_ok) {
-        uint16_t v[8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          uint32_t w = raw[u];
-          float x0 = bf16_to_f32((uint16_t)(w & 0xFFFFu));
-          float x1 = bf16_to_f32((uint16_t)(w >> 16));
-          const int pi = (d0 - kNope) / 2 + u;
-          // angle t * f reduced to [-pi, pi] in fp64 with 2*pi as a double plus its remainder (error
-          // about 1e-10 rad at a million positions), then fp32 sin/cos: the rotated query is rounded to
-          // bf16, far coarser than either step
-          const double phi = (double)t * a.inv_freq[pi];
-          const double n = rint(phi * 0.15915494309189535);
-          const double r = (phi - n * 6.28318530717958623) - n * 2.4492935982947064e-16;
-          float s, c;
-          sincosf((float)r, &s, &c);
-          v[2 * u] = f32_to_bf16(x0 * c - x1 * s);
-          v[2 * u + 1] = f32_to_bf16(x0 * s + x1 * c);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) raw[u] = (uint32_t)v[2 * u] | ((uint32_t)v[2 * u + 1] << 16);
-      }
-      qa[ks] = __builtin_bit_cast(bf16x8, raw);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      qraw[ks] = head_ok ? ldg<u32x4>(qp + ks * 32 + 8 * g) : zero;
     }
   }
+  __syncthreads();  // angles and the top-k row in LDS
 
-  const float inv_sqrt_d = 0.08838834764831845f;  // 1/sqrt(128)
-  float m_run[4], l_run[4];
-  v4f O[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.0f;
-  }
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) O[nt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  // chunk 0 into buffer 0 (the gathers need the top-k row)
+  const int pp = tid >> 4, rr = tid & 15;
+  Fetch F;
+  fetch(Q, S.list, 0, pp, rr, F);
 
-  const size_t blk_base = (size_t)b * a.max_blocks;
-  const size_t win_base = (size_t)b * a.ring;
-  uint16_t* Pn_w = Pn + wave * 16 * P_STRIDE;
-  uint16_t* Pr_w = Pr + wave * 16 * P_STRIDE;
-
-  for (int64_t c0 = s_begin; c0 < s_end; c0 += KC) {
-    __syncthreads();
-    // ---- gather 64 entries: thread -> (key kk, quarter pp) ; 16 codes + 16 rope values each
-    {
-      const int kk = tid >> 2, pp = tid & 3;
-      const int64_t slot = c0 + kk;
-      bool valid = slot < s_end;
-      const uint8_t* codes = nullptr;
-      const uint16_t* rope = nullptr;
-      const float* scl = nullptr;
-      if (valid) {
-        if (slot < n_first) {
-          int64_t j = a.dense ? slot : (int64_t)a.topk[((size_t)b * a.Tq + tq) * a.k + slot];
-          valid = j >= 0 && j < N;
-          if (valid) {
-            codes = a.blk_codes + (blk_base + j) * kNope;
-            rope = a.blk_rope + (blk_base + j) * kRope;
-            scl = a.blk_scale + blk_base + j;
-          }
-        } else {
-          int64_t s = t - a.W + 1 + (slot - n_first);
-          valid = s >= 0;
-          if (valid) {
-            size_t e = win_base + (size_t)(s % a.ring);
-            codes = a.win_codes + e * kNope;
-            rope = a.win_rope + e * kRope;
-            scl = a.win_scale + e;
-          }
-        }
-      }
-      u32x4 cw = {0u, 0u, 0u, 0u}, r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u};
-      if (valid) {
-        cw = *reinterpret_cast<const u32x4*>(codes + pp * 16);
-        r0 = *reinterpret_cast<const u32x4*>(rope + pp * 16);
-        r1 = *reinterpret_cast<const u32x4*>(rope + pp * 16 + 8);
-      }
-      uint16_t cb[16];
+  // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3)
+  bf16x8 qb[4];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) cb[u] = e4m3_to_bf16((cw[u >> 2] >> (8 * (u & 3))) & 0xFFu);
-      u32x4 c_lo, c_hi;
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 v = qraw[ks];
+    if (ks >= 2) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        c_lo[u] = (uint32_t)cb[2 * u] | ((uint32_t)cb[2 * u + 1] << 16);
-        c_hi[u] = (uint32_t)cb[8 + 2 * u] | ((uint32_t)cb[8 + 2 * u + 1] << 16);
-      }
-      uint16_t* kd = Kd + kk * KD_STRIDE;
-      *reinterpret_cast<u32x4*>(kd + pp * 16) = c_lo;
-      *reinterpret_cast<u32x4*>(kd + pp * 16 + 8) = c_hi;
-      *reinterpret_cast<u32x4*>(kd + kNope + pp * 16) = r0;
-      *reinterpret_cast<u32x4*>(kd + kNope + pp * 16 + 8) = r1;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) Vt[(pp * 16 + u) * VT_STRIDE + kk] = cb[u];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        Vt[(kNope + pp * 16 + u) * VT_STRIDE + kk] = (uint16_t)((r0[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
-        Vt[(kNope + pp * 16 + 8 + u) * VT_STRIDE + kk] = (uint16_t)((r1[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
-      }
-      if (pp == 0) {
-        kscale[kk] = valid ? *scl : 0.0f;
-        kvalid[kk] = valid ? 1 : 0;
+        const int pi = 16 * (ks - 2) + 4 * g + u;
+        const float c = S.cos_t[pi], s = S.sin_t[pi];
+        const float x0 = bf16_to_f32((uint16_t)(v[u] & 0xFFFFu));
+        const float x1 = bf16_to_f32((uint16_t)(v[u] >> 16));
+        v[u] = (uint32_t)f32_to_bf16(x0 * c - x1 * s) | ((uint32_t)f32_to_bf16(x0 * s + x1 * c) << 16);
       }
     }
-    __syncthreads();
+    qb[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+  stage(F, pp, rr, S.kd[0], S.vt[0], S.scl[0]);
+  __syncthreads();
 
-    // ---- S = Q.K^T for this wave's 16 heads x 64 keys
-    float S[4][4];
+  constexpr float kC = kLog2eRsqrtD;
+  constexpr float kLazy = 8.0f;  // log2 units: O is rescaled only when a head's max rises by more
+  float m_run = -INFINITY, l_run = 0.0f;
+  v4f O[8];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-      const uint16_t* krow = Kd + (kt * 16 + col) * KD_STRIDE + 8 * kg;
-      an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], lds_bf16x8(krow), an, 0, 0, 0);
-      an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], lds_bf16x8(krow + 32), an, 0, 0, 0);
-      ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2], lds_bf16x8(krow + 64), ar, 0, 0, 0);
-      ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[3], lds_bf16x8(krow + 96), ar, 0, 0, 0);
-      const int key = kt * 16 + col;
-      const float sc = kscale[key];
-      const bool ok = kvalid[key] != 0;
+  for (int dt = 0; dt < 8; ++dt) O[dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  const bool active = wave * 16 < a.H;
+  const int n_chunks = (Q.total + kMChunk - 1) / kMChunk;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int cur = c & 1;
+    // the next chunk's gathers first (slots past the end read an in-bounds entry and are masked)
+    fetch(Q, S.list, (c + 1) * kMChunk, pp, rr, F);
+    if (active) {
+      const uint16_t* kd = S.kd[cur];
+      const uint16_t* vt = S.vt[cur];
+      const float* scl = S.scl[cur];
+      float Sv[2][4];
+      v4f sc4[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[kt][i] = ok ? (an[i] * sc + ar[i]) * inv_sqrt_d : -INFINITY;
-    }
-    // ---- online softmax per head row (rows 4kg+i live in the 16 lanes of group kg)
-    float alpha[4];
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint16_t* krow = kd + (tt * 16 + r) * kKdStride + 8 * g;
+        v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+        an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow)), qb[0], an, 0, 0, 0);
+        an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 32)), qb[1], an, 0, 0, 0);
+        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 64)), qb[2], ar, 0, 0, 0);
+        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 96)), qb[3], ar, 0, 0, 0);
+        sc4[tt] = *reinterpret_cast<const v4f*>(scl + tt * 16 + 4 * g);
+        // a slot without a key (scale -1, all-zero dims) is masked; an entry whose nope part is all
+        // zero has scale 0 and is a key like any other
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = fmaxf(fmaxf(S[0][i], S[1][i]), fmaxf(S[2][i], S[3][i]));
+        for (int v = 0; v < 4; ++v) Sv[tt][v] = sc4[tt][v] >= 0.0f ? an[v] * sc4[tt][v] + ar[v] : -INFINITY;
+      }
+      // online softmax of head r (its 32 keys are spread over the 4 lane groups)
+      float mx = fmaxf(fmaxf(fmaxf(Sv[0][0], Sv[0][1]), fmaxf(Sv[0][2], Sv[0][3])),
+                       fmaxf(fmaxf(Sv[1][0], Sv[1][1]), fmaxf(Sv[1][2], Sv[1][3])));
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const bool raise = mx * kC > m_run * kC + kLazy;  // also true for the first finite max (m_run = -inf)
+      if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_run - m_new) * kC) : 1.0f;  // 0 from -inf
+        l_run *= alpha;
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      const float m_new = fmaxf(m_run[i], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      alpha[i] = __expf(m_run[i] - m_use);
+        for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
       float rs = 0.0f;
+      u32x4 pr, pn;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float pv = __expf(S[kt][i] - m_use);
-        S[kt][i] = pv;
-        rs += pv;
+      for (int v = 0; v < 4; ++v) {
+        const float p0 = __builtin_amdgcn_exp2f((Sv[0][v] - m_use) * kC);
+        const float p1 = __builtin_amdgcn_exp2f((Sv[1][v] - m_use) * kC);
+        rs += p0 + p1;
+        pr[v] = pack_bf16(p0, p1);
+        pn[v] = pack_bf16(p0 * sc4[0][v], p1 * sc4[1][v]);
       }
+      rs += xor16(rs);
+      rs += xor32(rs);
+      l_run += rs;
+      // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P)
+      const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) rs += __shfl_xor(rs, o, 64);
-      l_run[i] = l_run[i] * alpha[i] + rs;
-      m_run[i] = m_new;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[nt][i] *= alpha[i];
-    // P (rope dims) and P*scale (nope dims) as bf16 A operands, via LDS
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = kt * 16 + col;
-      const float sc = kscale[key];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Pr_w[(4 * kg + i) * P_STRIDE + key] = f32_to_bf16(S[kt][i]);
-        Pn_w[(4 * kg + i) * P_STRIDE + key] = f32_to_bf16(S[kt][i] * sc);
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x4 va = *reinterpret_cast<const u32x4*>(vt + (dt * 16 + r) * kMVtStride + 8 * g);
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0, 0);
       }
     }
+    // the next chunk into the other buffer (last read in the previous step, before the barrier below)
+    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.vt[cur ^ 1], S.scl[cur ^ 1]);
     __syncthreads();
-    // ---- O += P.V : A rows = heads, K = keys; B columns = dims
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const uint16_t* prow = (nt < 4 ? Pn_w : Pr_w) + col * P_STRIDE + 8 * kg;
-      const uint16_t* vrow = Vt + (nt * 16 + col) * VT_STRIDE + 8 * kg;
-      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_bf16x8(prow), lds_bf16x8(vrow), O[nt], 0, 0, 0);
-      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_bf16x8(prow + 32), lds_bf16x8(vrow + 32), O[nt], 0, 0, 0);
-    }
   }
 
-  // ---- output: lane holds O[nt][i] = (head wave*16 + 4kg + i, dim nt*16 + col)
+  // ---- output: lane (r, g) holds head 16 * wave + r, dims dt * 16 + 4g .. +3
+  if (active && head_ok) {
+    const float inv = 1.0f / l_run;
+    const size_t row = ((size_t)b * a.Tq + tq) * a.H + head;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = wave * 16 + 4 * kg + i;
-    if (h >= a.H) continue;
-    const float inv = 1.0f / l_run[i];
-    uint16_t* o = a.out + (((size_t)b * a.Tq + tq) * a.H + h) * kHeadDim;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[nt * 16 + col] = f32_to_bf16(O[nt][i] * inv);
-    if (a.lse && col == 0) a.lse[((size_t)b * a.Tq + tq) * a.H + h] = m_run[i] + __logf(l_run[i]);
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(O[dt][0] * inv) | ((uint32_t)f32_to_bf16(O[dt][1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16(O[dt][2] * inv) | ((uint32_t)f32_to_bf16(O[dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(a.out + row * kHeadDim + dt * 16 + 4 * g) = pk;
+    }
+    if (a.lse && g == 0) a.lse[row] = m_run * 0.08838834764831845f + __logf(l_run);  // natural-log units
   }
 }
 
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s) {
   const unsigned nq = (unsigned)(B * a.Tq);
-  hipLaunchKernelGGL(attn_kernel, dim3(nq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_kernel, dim3(nq), dim3(kMThreads), 0, s, a);
   return hipGetLastError();
 }
 

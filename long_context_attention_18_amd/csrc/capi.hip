@@ -69,7 +69,7 @@ Layout layout(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
 bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring) {
   if (B < 1 || B > 65535) return false;
   if (max_ctx < pool_m(d) || max_ctx > ((int64_t)1 << 32)) return false;
-  if (n_blocks_max(d, max_ctx) > (int64_t)2048 * kScoreChunk) return false;  // score chunks per query fit the scan's LDS
+  if (n_blocks_max(d, max_ctx) > kMaxBlocks) return false;  // scan segments per query fit the selection's LDS
   if (ring < d->window || ring > (1 << 24)) return false;
   return true;
 }

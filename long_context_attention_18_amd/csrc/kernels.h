@@ -19,6 +19,8 @@ constexpr int kScoreThreads = kScoreWaves * 64;
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
+constexpr int64_t kMaxBlocks = 2048LL * kScoreChunk;  // compressed blocks per sequence the indexer serves
+constexpr int kMaxSegs = (int)(kMaxBlocks / kScanPerWG);  // candidate-scan segments per query (512)
 
 // ---- attention tiling ----------------------------------------------------
 constexpr int kAttnKeys = 64;                         // keys staged per iteration (many-query kernel)

@@ -23,7 +23,7 @@ constexpr int kRadixBins = 1 << kRadixBits;
 
 struct SelectLds {
   uint64_t cs[kCandCap];
-  uint32_t seg_off[2049];  // G2_q <= 2048 segments
+  uint32_t seg_off[kMaxSegs + 1];  // G2_q <= kMaxSegs segments
   uint32_t hist[kRadixBins];
   uint32_t wsum[8];
   uint32_t sel_digit, sel_above, sel_count, flat_needed;
@@ -202,6 +202,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
         // a small boundary bin: gather its elements and find the need-th largest by direct ranking
         // (keys are unique, so exactly one element has need-1 larger ones) instead of another pass
         if (tid == 0) S.small_n = 0u;
+        if (tid < 64) S.small[tid] = 0ull;  // unused slots rank below every element
         __syncthreads();
         for (int64_t i = tid; i < n; i += 512) {
           const uint64_t e = elem(i);
@@ -209,10 +210,12 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
         }
         __syncthreads();
         if (wave == 0) {
+          // all 64 slots, unrolled: the LDS reads go out together instead of one round trip per element
           const uint32_t c = S.sel_count;
-          const uint64_t mine = lane < (int)c ? S.small[lane] : 0ull;
+          const uint64_t mine = S.small[lane];
           uint32_t rank = 0;
-          for (uint32_t m = 0; m < c; ++m) rank += S.small[m] > mine ? 1u : 0u;
+#pragma unroll
+          for (int m = 0; m < 64; ++m) rank += S.small[m] > mine ? 1u : 0u;
           if (lane < (int)c && rank == need - 1) S.sel_thresh = mine;
         }
         __syncthreads();
