@@ -340,9 +340,19 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.m = cache->desc.m;
   a.G2 = W.G2;
   {
+    // score workgroups of the last query: one per chunk, or, with many queries, one per kMultiChunks
     const int64_t g1 = (a.len / a.m + kScoreChunk - 1) / kScoreChunk;  // score chunks of the last query
-    int64_t cm = 2 * (((int64_t)a.k + (g1 > 0 ? g1 : 1) - 1) / (g1 > 0 ? g1 : 1));
-    a.cmin = (int32_t)(cm < 16 ? 16 : (cm > kScoreChunk ? kScoreChunk : cm));
+    int64_t wgs = g1;
+    a.chunk_step = 0;
+    if ((int64_t)cache->batch * Tq >= kMultiMinQueries) {
+      wgs = (g1 + kMultiChunks - 1) / kMultiChunks;
+      wgs = wgs < 1 ? 1 : wgs;
+      a.chunk_step = (int32_t)wgs;
+    }
+    // each workgroup counts at least cmin keys (twice its share of k) into the query's histogram
+    const int64_t w = wgs > 0 ? wgs : 1;
+    const int64_t cm = 2 * (((int64_t)a.k + w - 1) / w);
+    a.cmin = (int32_t)(cm < 16 ? 16 : (cm > kCandCap ? kCandCap : cm));
   }
   *out = a;
   return LCA_OK;

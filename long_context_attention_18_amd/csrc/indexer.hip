@@ -150,36 +150,22 @@ struct ScoreLds {
   int lo;
 };
 
-// One score workgroup's chunk: kScoreChunk blocks from j_begin. FULL: the whole chunk is visible, so
-// every key load is one base address plus a constant offset and no block needs a bounds test.
-template <bool FULL>
-__device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
-
-  // ---- loads, smallest first (vector loads return in order): the query slice this lane quantises
-  // (lane -> head lane/8, dims 8*(lane%8)..+8), the head weights, then the keys.
-  const int qh = lane >> 3, qpart = lane & 7;
-  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
-  if (qh < a.HI) qraw = *reinterpret_cast<const uint4*>(a.qI + (((size_t)b * a.Tq + tq) * a.HI + qh) * kIdxDim + qpart * 8);
+// A workgroup's query: its MX-FP4 operands, head weights and exactness bounds (one per workgroup)
+struct ScoreQuery {
+  v8i A0, A1;
+  int sA, sB;
   float wlo[4], whi[4];  // head weights 0..3 and 4..7 (0 for heads >= H_I)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wlo[i] = i < a.HI ? wq[i] : 0.0f;
-    whi[i] = i + 4 < a.HI ? wq[i + 4] : 0.0f;
-  }
-  const size_t kbase = (size_t)b * a.max_blocks;
-  uint32_t* keys = q_keys(a, q);
-  const uint8_t* codes = a.idx_codes + kbase * 32;
-  const uint8_t* scl = a.idx_scale + kbase * 2;
-  const int wave_j0 = j_begin + wave * kScoreIters * 32;
-  const int n2 = 2 * (lane & 15) + ((lane >> 4) >> 1);  // block of this lane inside a 32-block tile
-  const int half = (lane >> 4) & 1;                      // which 16 bytes of its block's codes
-  // All of this wave's key loads (kScoreIters tiles x 16 B + 1 scale byte per lane), issued back to
-  // back: one base address plus constant offsets for a full chunk, else each address clamped to the
-  // last visible block (always in bounds).
-  uint4 bvs[kScoreIters];
-  int sbs[kScoreIters];
+  int dlo, dhi, k0lo, k0hi, k1lo, k1hi;
+  const float* wq;
+};
+
+// All of a wave's key loads for one chunk (kScoreIters tiles x 16 B + 1 scale byte per lane), issued
+// back to back in tile order (loads return in order, so the first tile pair can start as soon as its
+// own data is in). FULL: the whole chunk is visible, so each address is one base plus a constant
+// offset; otherwise each is clamped to the last visible block (always in bounds).
+template <bool FULL>
+__device__ __forceinline__ void load_keys(const uint8_t* codes, const uint8_t* scl, int wave_j0, int n2, int half,
+                                          int N, uint4 (&bvs)[kScoreIters], int (&sbs)[kScoreIters]) {
   if (FULL) {
     const uint8_t* cb = codes + (size_t)(wave_j0 + n2) * 32 + half * 16;
     const uint8_t* sb = scl + (size_t)(wave_j0 + n2) * 2 + half;
@@ -187,8 +173,6 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     for (int it = 0; it < kScoreIters; ++it) {
       bvs[it] = *reinterpret_cast<const uint4*>(cb + it * 32 * 32);
       sbs[it] = sb[it * 32 * 2];
-      // keep the tiles' loads in order: loads return in order, so the first tile pair can start as
-      // soon as its own data is in (a reordered issue would make it wait for most of the chunk)
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -201,76 +185,91 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
-  if (lane == 0) S.n_flag[wave] = 0;
+}
 
-  // ---- MX-FP4 query and the exactness bounds, once per workgroup by wave 0 (every wave quantising it
-  // for itself avoids the barrier but costs more: the 2 waves per SIMD compete for the VALU while the
-  // keys stream in)
-  if (wave == 0) {
-    uint32_t word = 0, sbyte = 0;
-    if (qh < a.HI) {
-      float x[8];
-      const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+// The MX-FP4 query and its exactness bounds, by wave 0 into LDS (the caller's barrier makes them
+// visible), from this lane's slice qraw (lane -> head lane/8, dims 8*(lane%8)..+8).
+__device__ __forceinline__ void quantise_query(const ScoreArgs& a, ScoreLds& S, uint4 qraw) {
+  const int lane = threadIdx.x & 63;
+  const int qh = lane >> 3, qpart = lane & 7;
+  uint32_t word = 0, sbyte = 0;
+  if (qh < a.HI) {
+    float x[8];
+    const uint32_t rw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[2 * u] = __uint_as_float(rw[u] << 16);
-        x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-      if (amax > 0.0f) {
-        int E = ilogbf(amax) - 2;
-        E = E < -127 ? -127 : (E > 127 ? 127 : E);
-        sbyte = (uint32_t)(E + 127);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
-      }
+    for (int u = 0; u < 4; ++u) {
+      x[2 * u] = __uint_as_float(rw[u] << 16);
+      x[2 * u + 1] = __uint_as_float(rw[u] & 0xFFFF0000u);
     }
-    S.qcode[qh * 8 + qpart] = word;
-    if ((qpart & 3) == 0) S.qscale[qh * 2 + (qpart >> 2)] = (int)sbyte;
-    // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
-    // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
-    const int q0 = __shfl((int)sbyte, (lane & 7) * 8, 64), q1 = __shfl((int)sbyte, (lane & 7) * 8 + 4, 64);
-    const bool live = (lane & 7) < a.HI;
-    int g0 = live ? -10 - (q0 - q1) : -100000, g1 = live ? 10 - (q0 - q1) : 100000;
-    int g2 = live ? 130 - q0 : -100000, g3 = live ? 370 - q0 : 100000;
-    int g4 = live ? 130 - q1 : -100000, g5 = live ? 370 - q1 : 100000;
+    float amax = 0.0f;
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      g0 = max(g0, __shfl_xor(g0, o, 64)); g1 = min(g1, __shfl_xor(g1, o, 64));
-      g2 = max(g2, __shfl_xor(g2, o, 64)); g3 = min(g3, __shfl_xor(g3, o, 64));
-      g4 = max(g4, __shfl_xor(g4, o, 64)); g5 = min(g5, __shfl_xor(g5, o, 64));
-    }
-    if (lane == 0) {
-      S.guard[0] = g0; S.guard[1] = g1; S.guard[2] = g2; S.guard[3] = g3; S.guard[4] = g4; S.guard[5] = g5;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the four lanes of one 32-element block
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    if (amax > 0.0f) {
+      int E = ilogbf(amax) - 2;
+      E = E < -127 ? -127 : (E > 127 ? 127 : E);
+      sbyte = (uint32_t)(E + 127);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
     }
   }
-  __syncthreads();  // quantised query and bounds visible
-  const int dlo = S.guard[0], dhi = S.guard[1], k0lo = S.guard[2], k0hi = S.guard[3], k1lo = S.guard[4],
-            k1hi = S.guard[5];
-  // ---- two A operands. Lane: row r = lane%16, K-group g = lane/16; row r holds (p, h) = (r/8, r%8)
-  // in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1, its codes in K-groups 2p, 2p+1 only.
+  S.qcode[qh * 8 + qpart] = word;
+  if ((qpart & 3) == 0) S.qscale[qh * 2 + (qpart >> 2)] = (int)sbyte;
+  // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
+  // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
+  const int q0 = __shfl((int)sbyte, (lane & 7) * 8, 64), q1 = __shfl((int)sbyte, (lane & 7) * 8 + 4, 64);
+  const bool live = (lane & 7) < a.HI;
+  int g0 = live ? -10 - (q0 - q1) : -100000, g1 = live ? 10 - (q0 - q1) : 100000;
+  int g2 = live ? 130 - q0 : -100000, g3 = live ? 370 - q0 : 100000;
+  int g4 = live ? 130 - q1 : -100000, g5 = live ? 370 - q1 : 100000;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    g0 = max(g0, __shfl_xor(g0, o, 64)); g1 = min(g1, __shfl_xor(g1, o, 64));
+    g2 = max(g2, __shfl_xor(g2, o, 64)); g3 = min(g3, __shfl_xor(g3, o, 64));
+    g4 = max(g4, __shfl_xor(g4, o, 64)); g5 = min(g5, __shfl_xor(g5, o, 64));
+  }
+  if (lane == 0) {
+    S.guard[0] = g0; S.guard[1] = g1; S.guard[2] = g2; S.guard[3] = g3; S.guard[4] = g4; S.guard[5] = g5;
+  }
+}
+
+// After the barrier that follows quantise_query: the two A operands. Lane: row r = lane%16, K-group
+// g = lane/16; row r holds (p, h) = (r/8, r%8) in operand A0 and (r/8, (r%8 + 4) % 8) in operand A1,
+// its codes in K-groups 2p, 2p+1 only.
+__device__ __forceinline__ void query_operands(const ScoreLds& S, ScoreQuery& Q) {
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4, p = r >> 3, odd = g & 1;
   const int hA = r & 7, hB = (hA + 4) & 7;
   uint32_t aA[4] = {0u, 0u, 0u, 0u}, aB[4] = {0u, 0u, 0u, 0u};
-  int sA = 127, sB = 127;
+  Q.sA = 127;
+  Q.sB = 127;
   if ((g >> 1) == p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       aA[u] = S.qcode[hA * 8 + odd * 4 + u];
       aB[u] = S.qcode[hB * 8 + odd * 4 + u];
     }
-    sA = S.qscale[hA * 2 + odd];
-    sB = S.qscale[hB * 2 + odd];
+    Q.sA = S.qscale[hA * 2 + odd];
+    Q.sB = S.qscale[hB * 2 + odd];
   }
-  const v8i A0 = {(int)aA[0], (int)aA[1], (int)aA[2], (int)aA[3], 0, 0, 0, 0};
-  const v8i A1 = {(int)aB[0], (int)aB[1], (int)aB[2], (int)aB[3], 0, 0, 0, 0};
+  Q.A0 = (v8i){(int)aA[0], (int)aA[1], (int)aA[2], (int)aA[3], 0, 0, 0, 0};
+  Q.A1 = (v8i){(int)aB[0], (int)aB[1], (int)aB[2], (int)aB[3], 0, 0, 0, 0};
+  Q.dlo = S.guard[0]; Q.dhi = S.guard[1]; Q.k0lo = S.guard[2]; Q.k0hi = S.guard[3]; Q.k1lo = S.guard[4];
+  Q.k1hi = S.guard[5];
+}
 
-  uint32_t lane_keys[kScoreIters / 2];  // this lane's final key per tile pair (0 = no block)
+// One chunk's scores from its loaded keys: the key of every visible block to `keys`, this lane's key
+// per tile pair to lane_keys (0 = no block); blocks outside the exactness bounds are rescored in fp64.
+// Contains workgroup barriers: every thread of the workgroup calls it.
+template <bool FULL>
+__device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, const ScoreQuery& Q, const uint4 (&bvs)[kScoreIters],
+                                            const int (&sbs)[kScoreIters], uint32_t* keys, const uint8_t* codes,
+                                            const uint8_t* scl, int N, int j_begin, int wave_j0, int n2,
+                                            uint32_t (&lane_keys)[kScoreIters / 2]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int odd = (lane >> 4) & 1;
+  if (lane == 0) S.n_flag[wave] = 0;  // this wave's own list: program order suffices
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) {
     const int tA = 2 * pr, tB = 2 * pr + 1;
@@ -281,16 +280,16 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     const v8i BA = {(int)bA.x, (int)bA.y, (int)bA.z, (int)bA.w, 0, 0, 0, 0};
     const v8i BB = {(int)bB.x, (int)bB.y, (int)bB.z, (int)bB.w, 0, 0, 0, 0};
     v4f accA = {0.0f, 0.0f, 0.0f, 0.0f}, accB = {0.0f, 0.0f, 0.0f, 0.0f};
-    accA = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, BA, accA, 4, 4, 0, sA, 0, sbA);
-    accB = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, BB, accB, 4, 4, 0, sB, 0, sbB);
+    accA = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.A0, BA, accA, 4, 4, 0, Q.sA, 0, sbA);
+    accB = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.A1, BB, accB, 4, 4, 0, Q.sB, 0, sbB);
     // rows 4g..4g+3 of this lane: tile A gives heads 0..3 on even g, 4..7 on odd g; tile B the reverse.
     // Heads 0..3 first (fmaf chain from +0), then the partner lane (g^1) continues with heads 4..7.
     float e = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e = fmaf(wlo[i], relu(odd ? accB[i] : accA[i]), e);
+    for (int i = 0; i < 4; ++i) e = fmaf(Q.wlo[i], relu(odd ? accB[i] : accA[i]), e);
     float sc = from_partner(e, odd);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc = fmaf(whi[i], relu(odd ? accA[i] : accB[i]), sc);
+    for (int i = 0; i < 4; ++i) sc = fmaf(Q.whi[i], relu(odd ? accA[i] : accB[i]), sc);
     // this lane now holds the final score of block jb: tile A if g is odd, tile B if even
     const int jb = wave_j0 + (odd ? tA : tB) * 32 + n2;
     const uint32_t other = from_partner_u((uint32_t)sbA | ((uint32_t)sbB << 8), odd);
@@ -298,7 +297,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     const int oth = odd ? (int)(other & 0xFFu) : (int)(other >> 8);
     const int ks0 = odd ? oth : own, ks1 = odd ? own : oth;
     const int dk = ks0 - ks1;
-    const bool bad = dk < dlo || dk > dhi || ks0 < k0lo || ks0 > k0hi || ks1 < k1lo || ks1 > k1hi;
+    const bool bad = dk < Q.dlo || dk > Q.dhi || ks0 < Q.k0lo || ks0 > Q.k0hi || ks1 < Q.k1lo || ks1 > Q.k1hi;
     uint32_t key = 0;
     if (FULL || jb < N) {
       if (sc == 0.0f) sc = 0.0f;
@@ -316,7 +315,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
     for (uint32_t f = tid; f < n; f += kScoreThreads) {
       const int jb = j_begin + (int)S.flag_blk[w][f];
       const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
-                                         S.qcode, S.qscale, wq, a.HI);
+                                         S.qcode, S.qscale, Q.wq, a.HI);
       keys[jb] = order_key(ex);
     }
     nf += n;
@@ -330,6 +329,93 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
       if (FULL || jb < N) lane_keys[pr] = keys[jb];
     }
   }
+}
+
+// The workgroup's maximum key (all threads get it); `m` is this lane's
+__device__ __forceinline__ uint32_t wg_max_key(ScoreLds& S, uint32_t m) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if (lane == 0) S.wmax[wave] = m;
+  __syncthreads();
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int w = 0; w < kScoreWaves; ++w) kmax = max(kmax, S.wmax[w]);
+  return kmax;
+}
+
+// lo = the highest bin at which the LDS histogram, counted from the top, reaches cmin (S.lo; every
+// thread calls it)
+__device__ __forceinline__ int hist_cmin_bin(ScoreLds& S, uint32_t cmin) {
+  const int tid = threadIdx.x;
+  constexpr int kPerT = kHistBins / kScoreThreads;  // bins per thread
+  if (tid == 0) S.lo = 0;
+  __syncthreads();
+  const int hi_b = kHistBins - kPerT * tid;  // this thread: bins [hi_b - kPerT, hi_b), threads in descending order
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 1; i <= kPerT; ++i) cnt += S.hist[hi_b - i];
+  uint32_t tot;
+  const uint32_t excl = block_excl_scan(cnt, S.wmax, &tot);
+  if (excl < cmin && excl + cnt >= cmin) {
+    uint32_t c = excl;
+    for (int i = 1; i <= kPerT; ++i) {
+      c += S.hist[hi_b - i];
+      if (c >= cmin) {
+        S.lo = hi_b - i;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  return S.lo;
+}
+
+// The LDS histogram's bins lo .. top_bin into the query's global histogram
+__device__ __forceinline__ void hist_publish(const ScoreArgs& a, ScoreLds& S, int q, int lo, int top_bin) {
+  for (int i = lo + (int)threadIdx.x; i <= top_bin; i += kScoreThreads) {
+    const uint32_t c = S.hist[i];
+    if (c) atomicAdd(&q_hist(a, q)[i], c);
+  }
+}
+
+// The query's loads (its MX-FP4 slice for quantise_query, the head weights) into Q / qraw
+__device__ __forceinline__ uint4 load_query(const ScoreArgs& a, int b, int tq, ScoreQuery& Q) {
+  const int lane = threadIdx.x & 63;
+  const int qh = lane >> 3, qpart = lane & 7;
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+  if (qh < a.HI) qraw = *reinterpret_cast<const uint4*>(a.qI + (((size_t)b * a.Tq + tq) * a.HI + qh) * kIdxDim + qpart * 8);
+  Q.wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Q.wlo[i] = i < a.HI ? Q.wq[i] : 0.0f;
+    Q.whi[i] = i + 4 < a.HI ? Q.wq[i + 4] : 0.0f;
+  }
+  return qraw;
+}
+
+// One score workgroup's chunk: kScoreChunk blocks from j_begin (few-query calls: every workgroup one
+// chunk). The keys' loads go out before the query is quantised.
+template <bool FULL>
+__device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  ScoreQuery Q;
+  const uint4 qraw = load_query(a, b, tq, Q);
+  const size_t kbase = (size_t)b * a.max_blocks;
+  uint32_t* keys = q_keys(a, q);
+  const uint8_t* codes = a.idx_codes + kbase * 32;
+  const uint8_t* scl = a.idx_scale + kbase * 2;
+  const int wave_j0 = j_begin + wave * kScoreIters * 32;
+  const int n2 = 2 * (lane & 15) + ((lane >> 4) >> 1);  // block of this lane inside a 32-block tile
+  uint4 bvs[kScoreIters];
+  int sbs[kScoreIters];
+  load_keys<FULL>(codes, scl, wave_j0, n2, (lane >> 4) & 1, N, bvs, sbs);
+  for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
+  if (wave == 0) quantise_query(a, S, qraw);
+  __syncthreads();  // quantised query and bounds visible
+  query_operands(S, Q);
+  uint32_t lane_keys[kScoreIters / 2];
+  score_pairs<FULL>(a, S, Q, bvs, sbs, keys, codes, scl, N, j_begin, wave_j0, n2, lane_keys);
   // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
   // and the 16 bins below it (down to a quarter of the max), or, when those hold fewer than cmin of the
   // chunk's keys, every bin down to where the chunk's count from the top reaches cmin. Counts in a bin
@@ -340,13 +426,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   uint32_t m = 0;
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) m = max(m, lane_keys[pr]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-  if (lane == 0) S.wmax[wave] = m;
-  __syncthreads();
-  uint32_t kmax = 0;
-#pragma unroll
-  for (int w = 0; w < kScoreWaves; ++w) kmax = max(kmax, S.wmax[w]);
+  const uint32_t kmax = wg_max_key(S, m);
   const int top_bin = (int)(kmax >> 20);
   const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
 #pragma unroll
@@ -370,42 +450,79 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
       const uint32_t key = lane_keys[pr];
       if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&S.hist[key >> 20], 1u);
     }
-    if (tid == 0) S.lo = 0;
-    __syncthreads();
-    constexpr int kPerT = kHistBins / kScoreThreads;  // bins per thread
-    const int hi_b = kHistBins - kPerT * tid;  // this thread: bins [hi_b - kPerT, hi_b), threads in descending order
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 1; i <= kPerT; ++i) cnt += S.hist[hi_b - i];
-    uint32_t tot;
-    const uint32_t excl = block_excl_scan(cnt, S.wmax, &tot);
-    const uint32_t cm = (uint32_t)a.cmin;
-    if (excl < cm && excl + cnt >= cm) {
-      uint32_t c = excl;
-      for (int i = 1; i <= kPerT; ++i) {
-        c += S.hist[hi_b - i];
-        if (c >= cm) {
-          S.lo = hi_b - i;
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    lo = S.lo;
+    lo = hist_cmin_bin(S, (uint32_t)a.cmin);
   }
-  for (int i = lo + tid; i <= top_bin; i += kScoreThreads) {
-    const uint32_t c = S.hist[i];
-    if (c) atomicAdd(&q_hist(a, q)[i], c);
-  }
+  hist_publish(a, S, q, lo, top_bin);
 }
 
+// A workgroup over chunks chunk0, chunk0 + step, ... of its query (many-query calls, where one
+// workgroup per chunk would repeat the query's set-up and histogram for every 2048 blocks): the query
+// is quantised once, every key of its chunks is counted in the LDS histogram, and the histogram is
+// published once, from the workgroup's maximum's bin down by 16 bins or to cmin keys.
+__device__ __forceinline__ void score_multi(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int chunk0,
+                                            int step) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  ScoreQuery Q;
+  const uint4 qraw = load_query(a, b, tq, Q);
+  const size_t kbase = (size_t)b * a.max_blocks;
+  uint32_t* keys = q_keys(a, q);
+  const uint8_t* codes = a.idx_codes + kbase * 32;
+  const uint8_t* scl = a.idx_scale + kbase * 2;
+  const int n2 = 2 * (lane & 15) + ((lane >> 4) >> 1);
+  const int half = (lane >> 4) & 1;
+  for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
+  if (wave == 0) quantise_query(a, S, qraw);
+  __syncthreads();
+  query_operands(S, Q);
+  uint32_t m = 0;
+  for (int c = chunk0; c * kScoreChunk < N; c += step) {
+    const int j_begin = c * kScoreChunk;
+    const int wave_j0 = j_begin + wave * kScoreIters * 32;
+    uint4 bvs[kScoreIters];
+    int sbs[kScoreIters];
+    uint32_t lane_keys[kScoreIters / 2];
+    if (j_begin + kScoreChunk <= N) {
+      load_keys<true>(codes, scl, wave_j0, n2, half, N, bvs, sbs);
+      score_pairs<true>(a, S, Q, bvs, sbs, keys, codes, scl, N, j_begin, wave_j0, n2, lane_keys);
+    } else {
+      load_keys<false>(codes, scl, wave_j0, n2, half, N, bvs, sbs);
+      score_pairs<false>(a, S, Q, bvs, sbs, keys, codes, scl, N, j_begin, wave_j0, n2, lane_keys);
+    }
+#pragma unroll
+    for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+      const uint32_t key = lane_keys[pr];
+      m = max(m, key);
+      if (key != 0) atomicAdd(&S.hist[key >> 20], 1u);
+    }
+    __syncthreads();  // every wave has read the flag lists: the next chunk may reuse them
+  }
+  const uint32_t kmax = wg_max_key(S, m);  // (its barrier also orders the histogram adds before the reads)
+  const int top_bin = (int)(kmax >> 20);
+  const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
+  if (wave == 0) {
+    uint32_t v = (lane <= top_bin - low_bin) ? S.hist[low_bin + lane] : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
+    if (lane == 0) S.range = v;
+  }
+  __syncthreads();
+  const int lo = (S.range < (uint32_t)a.cmin && low_bin > 0) ? hist_cmin_bin(S, (uint32_t)a.cmin) : low_bin;
+  hist_publish(a, S, q, lo, top_bin);
+}
+
+// blockIdx.x: a chunk of the query (a.chunk_step = 0) or the first of the chunks x, x + step, ...
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   __shared__ ScoreLds S;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
   const int N = (int)visible_blocks(a, b, tq);
-  const int j_begin = blockIdx.x * kScoreChunk;
-  if (j_begin >= N) return;
+  const int c0 = blockIdx.x;
+  if (c0 * kScoreChunk >= N) return;
+  if (a.chunk_step > 0) {
+    score_multi(a, S, q, b, tq, N, c0, a.chunk_step);
+    return;
+  }
+  const int j_begin = c0 * kScoreChunk;
   if (j_begin + kScoreChunk <= N) score_chunk<true>(a, S, q, b, tq, N, j_begin);
   else score_chunk<false>(a, S, q, b, tq, N, j_begin);
 }
@@ -538,7 +655,9 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
   const int64_t N_last = a.len / a.m;  // visible blocks of the last query (t = len-1)
   if (N_last <= a.k) return hipSuccess;  // every visible block is selected; no scores needed
   const unsigned nq = (unsigned)(B * a.Tq);
-  unsigned g1 = (unsigned)((N_last + kScoreChunk - 1) / kScoreChunk);
+  // a workgroup per chunk, or (many queries) chunk_step workgroups per query, each over every
+  // chunk_step-th chunk
+  unsigned g1 = a.chunk_step > 0 ? (unsigned)a.chunk_step : (unsigned)((N_last + kScoreChunk - 1) / kScoreChunk);
   hipLaunchKernelGGL(score_kernel, dim3(g1, nq), dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -16,6 +16,9 @@ constexpr int kScoreWaves = 8;                        // waves per score workgro
 constexpr int kScoreIters = 8;                        // 32-block tiles per wave
 constexpr int kScoreChunk = kScoreWaves * kScoreIters * 32;  // blocks per workgroup (2048)
 constexpr int kScoreThreads = kScoreWaves * 64;
+// Calls with at least kMultiMinQueries queries (chunked prefill) score kMultiChunks chunks per workgroup
+constexpr int kMultiMinQueries = 512;
+constexpr int kMultiChunks = 8;
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
@@ -78,7 +81,8 @@ struct ScoreArgs {
   int32_t k;
   int32_t m;
   int32_t G2;              // scan segments per query
-  int32_t cmin;            // keys each score chunk counts into the histogram at least (twice its share of k)
+  int32_t cmin;            // keys each score workgroup counts into the histogram at least (twice its share of k)
+  int32_t chunk_step;      // 0: a score workgroup per 2048-block chunk; else one per chunk_step chunks of a query
   // ragged batches (see IngestArgs): the queries of sequence b are its seq_T[b] new tokens, positions
   // seq_len[b] + i for rows i < seq_T[b]; null: positions len - Tq + i
   const int64_t* seq_len;

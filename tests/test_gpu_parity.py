@@ -97,6 +97,24 @@ def test_csa_chunked_prefill_queries():
     compare_cache(run, oc)
 
 
+def test_csa_prefill_many_queries_long_context():
+    """Many-query indexer calls over long contexts. Tq = 512 queries seeing up to 18,003 blocks (9 score
+    chunks of 2048, the last ragged): each query's chunks are scored by 2 workgroups (the even and the odd
+    chunks), each publishing one histogram. Then B = 2 x Tq = 256 over about 10,000 blocks: one workgroup
+    per query over all of its 5 chunks. Sampled queries: scores and top-k bit-exact, attention within the
+    bar."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=512)
+    for B, Tq, pre in ((1, 512, 71500), (2, 256, 40000)):
+        run = LayerRun(layer, B=B, max_ctx=pre + Tq, ring=Tq + 127, max_tq=Tq, sigma=1.0)
+        _ingest(run, [pre, Tq])
+        qin, topk, out, lse = run.run_queries(Tq)
+        oc = [run.oracle_caches(b, pre + Tq) for b in range(run.B)]
+        pos = list(range(run.len - Tq, run.len))
+        w = check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 37)) + [Tq - 1])
+        assert w["scores_checked"] > 0
+        print("prefill long-context", B, Tq, w)
+
+
 def test_ingest_chunking_invariance():
     """The same token stream ingested token by token, in 7s, or at once: identical cache bytes."""
     layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
