@@ -143,12 +143,14 @@ size_t lca_workspace_bytes(const lca_layer_desc* desc, int32_t batch, int32_t ma
 lca_status lca_workspace_init(void* ws_dev, size_t bytes, void* stream);
 
 /* Where the indexer leaves its scores (CSA): after lca_csa_index_score (or
- * lca_csa_indexer_topk) on a cache of this shape, the workspace holds at this
- * byte offset the row of max_ctx/m uint32 keys of query `query` (= b*Tq + i),
+ * lca_csa_indexer_topk / lca_csa_attend with B*Tq < 2048 or more than 65535
+ * visible blocks) on a cache of this shape, the workspace holds at this byte
+ * offset the row of max_ctx/m uint32 keys of query `query` (= b*Tq + i),
  * valid for its visible blocks j < (t+1)/m: key = bits(score) ^ (score < 0 ?
  * 0xFFFFFFFF : 0x80000000), so keys order like the scores. Written only when
- * some query of the call sees more than topk blocks. Returns 0 for HCA or
- * invalid arguments. */
+ * some query of the call sees more than topk blocks. (The combined calls with
+ * more queries score in query tiles and keep only the selection's
+ * candidates.) Returns 0 for HCA or invalid arguments. */
 size_t lca_workspace_scores_offset(const lca_layer_desc* desc, int32_t batch, int32_t query, int64_t max_ctx);
 
 /* CSA compressor (CSA paragraph and Figure 3: every m = 4 tokens pooled into
@@ -207,7 +209,9 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
  * lca_csa_topk_select leaves the workspace histograms counting it: the next
  * selection is then slower, still exact, and clears them):
  *  lca_csa_index_score: the lightning-indexer scores of every visible block
- *    of the Tq queries (an HBM stream over the FP4 keys);
+ *    of the Tq queries (an HBM stream over the FP4 keys; with B*Tq >= 2048
+ *    queries that each see at most 65535 blocks, query tiles of 8 that also
+ *    leave the selection's candidates);
  *  lca_csa_topk_select: the per-query top-k of those scores into topk_dev. */
 lca_status lca_csa_index_score(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, int32_t Tq,
                                void* ws_dev, size_t ws_bytes, void* stream);

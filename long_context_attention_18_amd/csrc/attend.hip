@@ -307,6 +307,11 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
     int32_t* o = args.s.topk + (size_t)q * a.k;
     for (int i = tid; i < a.k; i += 512) o[i] = S.list[i];
   }
+  if (MODE == kAttendSelect && !do_select && args.s.tiles && hg == 0 && split == 0 && args.s.topk) {
+    // query tiles leave no scan to write the list of a query that sees at most k blocks
+    int32_t* o = args.s.topk + (size_t)q * a.k;
+    for (int i = tid; i < a.k; i += 512) o[i] = (int64_t)i < N ? i : -1;
+  }
 
   // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3)
   bf16x8 qb[4];

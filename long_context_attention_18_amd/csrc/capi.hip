@@ -344,7 +344,10 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
     const int64_t g1 = (a.len / a.m + kScoreChunk - 1) / kScoreChunk;  // score chunks of the last query
     int64_t wgs = g1;
     a.chunk_step = 0;
-    if ((int64_t)cache->batch * Tq >= kMultiMinQueries) {
+    const int64_t nq = (int64_t)cache->batch * Tq;
+    // query tiles: many queries, each seeing at most kTileMaxBlocks blocks (the last query sees the most)
+    a.tiles = nq >= kTileMinQueries && a.len / a.m <= kTileMaxBlocks ? 1 : 0;
+    if (!a.tiles && nq >= kMultiMinQueries) {
       wgs = (g1 + kMultiChunks - 1) / kMultiChunks;
       wgs = wgs < 1 ? 1 : wgs;
       a.chunk_step = (int32_t)wgs;
@@ -367,6 +370,7 @@ lca_status lca_csa_index_score(lca_cache* cache, const uint16_t* qI_dev, const f
   ScoreArgs a;
   lca_status st = score_args(cache, qI_dev, w_dev, true, Tq, nullptr, false, ws_dev, ws_bytes, &a);
   if (st != LCA_OK) return st;
+  a.write_keys = 1;  // this call leaves every visible block's key in the workspace
   return launch_status(launch_index_score(a, cache->batch, (hipStream_t)stream));
 }
 

@@ -58,6 +58,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -187,9 +188,11 @@ __device__ __forceinline__ void load_keys(const uint8_t* codes, const uint8_t* s
   }
 }
 
-// The MX-FP4 query and its exactness bounds, by wave 0 into LDS (the caller's barrier makes them
-// visible), from this lane's slice qraw (lane -> head lane/8, dims 8*(lane%8)..+8).
-__device__ __forceinline__ void quantise_query(const ScoreArgs& a, ScoreLds& S, uint4 qraw) {
+// The MX-FP4 query and its exactness bounds, by one wave into LDS (the caller's barrier makes them
+// visible), from this lane's slice qraw (lane -> head lane/8, dims 8*(lane%8)..+8): codes to
+// qcode [head][8 words], E8M0 bytes to qscale [head][half], the six bounds to guard.
+__device__ __forceinline__ void quantise_query_into(const ScoreArgs& a, uint4 qraw, uint32_t* qcode, int* qscale,
+                                                    int* guard) {
   const int lane = threadIdx.x & 63;
   const int qh = lane >> 3, qpart = lane & 7;
   uint32_t word = 0, sbyte = 0;
@@ -214,8 +217,8 @@ __device__ __forceinline__ void quantise_query(const ScoreArgs& a, ScoreLds& S, 
       for (int i = 0; i < 8; ++i) word |= fp4_e2m1_code_cmp(ldexpf(x[i], -E)) << (4 * i);
     }
   }
-  S.qcode[qh * 8 + qpart] = word;
-  if ((qpart & 3) == 0) S.qscale[qh * 2 + (qpart >> 2)] = (int)sbyte;
+  qcode[qh * 8 + qpart] = word;
+  if ((qpart & 3) == 0) qscale[qh * 2 + (qpart >> 2)] = (int)sbyte;
   // bounds: |S0 - S1| <= 10 and 130 <= S_b <= 370 for every live head, S_b = qs_b + ks_b.
   // Lane 8h holds head h's half-0 byte, lane 8h+4 its half-1 byte.
   const int q0 = __shfl((int)sbyte, (lane & 7) * 8, 64), q1 = __shfl((int)sbyte, (lane & 7) * 8 + 4, 64);
@@ -230,8 +233,12 @@ __device__ __forceinline__ void quantise_query(const ScoreArgs& a, ScoreLds& S, 
     g4 = max(g4, __shfl_xor(g4, o, 64)); g5 = min(g5, __shfl_xor(g5, o, 64));
   }
   if (lane == 0) {
-    S.guard[0] = g0; S.guard[1] = g1; S.guard[2] = g2; S.guard[3] = g3; S.guard[4] = g4; S.guard[5] = g5;
+    guard[0] = g0; guard[1] = g1; guard[2] = g2; guard[3] = g3; guard[4] = g4; guard[5] = g5;
   }
+}
+
+__device__ __forceinline__ void quantise_query(const ScoreArgs& a, ScoreLds& S, uint4 qraw) {
+  quantise_query_into(a, qraw, S.qcode, S.qscale, S.guard);
 }
 
 // After the barrier that follows quantise_query: the two A operands. Lane: row r = lane%16, K-group
@@ -527,6 +534,329 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   else score_chunk<false>(a, S, q, b, tq, N, j_begin);
 }
 
+// ---- Many-query calls (chunked prefill): query tiles on the 32x32x64 scaled MFMA ------------------------
+//
+// A workgroup takes kTileQueries consecutive queries of one sequence and every block any of them sees, so
+// each key it loads serves all of them. Per 32-block tile a wave runs two
+// v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands (queries 0-3, then 4-7): K is the 64-dim key (lanes
+// 0-31 hold dims 0-31, lanes 32-63 dims 32-63, each with its own E8M0 byte), B column n is block n of the
+// tile, and A row r is one (query, head) pair, placed so that the output lands where the head sum wants
+// it: output register i of lane l holds row 8 (i/4) + 4 (l/32) + i%4, so row r is given query
+// (r/16) + 2 ((r/4) % 2) and head 4 ((r/8) % 2) + r%4, and lane l then holds in registers 0-7 all eight
+// heads of query 2 (l/32) and in registers 8-15 those of query 2 (l/32) + 1. The fmaf chain over heads
+// runs in one lane, in the definition's order, with no lane exchange. Every product term is useful, and
+// the exactness argument of the score kernel holds unchanged (each output is the same two scaled exact
+// terms; the same bounds flag the blocks that need the fp64 rescoring).
+// Pass 1 counts every score of the workgroup's queries in per-query LDS histograms (4096 bins of the top
+// 12 key bits, two 16-bit counts per word: a query sees at most kTileMaxBlocks blocks), which give each
+// query the exact bin L at which the count from the top reaches k, and the number of keys in bins >= L.
+// Pass 2 scores again (the same instructions, so the same keys) and writes every key >= L, in index
+// order, into the candidate segments the selection reads (wave ballots and one LDS count exchange per
+// round of kTileWaves tiles). No per-block score goes to memory, unless the call asks for them
+// (write_keys) or a query's candidates would not fit the selection's LDS (its keys then serve the
+// selection's path over every block).
+struct TileLds {
+  uint32_t hist[kTileQueries][kHistBins / 2];  // bin 2i in the low half of word i, bin 2i+1 in the high half
+  uint32_t qcode[kTileQueries][64];
+  int qscale[kTileQueries][16];
+  int guard[kTileQueries][6];
+  alignas(16) uint32_t cnt[2][kTileWaves][8];  // pass 2: candidates per (wave, lane slot j + 4 half) of a round
+  alignas(16) float wts[kTileQueries][8];      // head weights (0 beyond H_I), read per tile: registers are short
+  uint32_t Lkey[kTileQueries];
+  uint32_t ncand[kTileQueries];
+  int32_t Nq[kTileQueries];                    // blocks the query scores (0: none)
+};
+
+// query of the tile held by slot j (0-3) of a lane in half `half` (lanes 0-31: 0, 1, 4, 5; 32-63: 2, 3, 6, 7)
+__device__ __forceinline__ int tile_slot_query(int j, int half) { return (j & 1) + 2 * half + 4 * (j >> 1); }
+
+// This lane's MFMA query operands, the blocks its four queries see and the bounds all queries satisfy
+struct TileQuery {
+  v8i A0, A1;
+  int sA0, sA1;
+  int N[4];
+  int g[6];
+};
+
+// ReLU on the bit pattern: every negative float (and -0) has a negative int pattern, so max(int, 0) maps
+// it to +0 and keeps every positive float; one integer max instead of a NaN-quieting float max pair
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Keys of block jb (the lane's column) for this lane's four queries, from its loaded key slice; 0 where
+// the query does not see the block. Every lane of the wave calls it (MFMA and lane swap).
+__device__ __forceinline__ void tile_keys(const ScoreArgs& a, const TileLds& S, const TileQuery& Q, const uint8_t* codes,
+                                          uint4 kb, int ks, int jb, int jc, uint32_t (&key)[4]) {
+  const int half = (threadIdx.x >> 5) & 1;
+  const v8i B = {(int)kb.x, (int)kb.y, (int)kb.z, (int)kb.w, 0, 0, 0, 0};
+  v16f c[2];
+  c[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q.A0, B, (v16f){}, 4, 4, 0, Q.sA0, 0, ks);
+  c[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q.A1, B, (v16f){}, 4, 4, 0, Q.sA1, 0, ks);
+  auto rs = __builtin_amdgcn_permlane32_swap((uint32_t)ks, (uint32_t)ks, false, false);
+  const int ko = (int)(half ? rs[0] : rs[1]);  // the other half's scale byte of the same block
+  const int ks0 = half ? ko : ks, ks1 = half ? ks : ko;
+  const int dk = ks0 - ks1;
+  const bool ok_all = dk >= Q.g[0] && dk <= Q.g[1] && ks0 >= Q.g[2] && ks0 <= Q.g[3] && ks1 >= Q.g[4] &&
+                      ks1 <= Q.g[5];
+  float e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tile_slot_query(j, half);
+    const float4 wa = *reinterpret_cast<const float4*>(&S.wts[q][0]);
+    const float4 wb = *reinterpret_cast<const float4*>(&S.wts[q][4]);
+    const int base = 8 * (j & 1);
+    const v16f& cj = c[j >> 1];
+    float x = 0.0f;  // starts at +0, so it never becomes -0
+    x = fmaf(wa.x, relu_bits(cj[base + 0]), x);
+    x = fmaf(wa.y, relu_bits(cj[base + 1]), x);
+    x = fmaf(wa.z, relu_bits(cj[base + 2]), x);
+    x = fmaf(wa.w, relu_bits(cj[base + 3]), x);
+    x = fmaf(wb.x, relu_bits(cj[base + 4]), x);
+    x = fmaf(wb.y, relu_bits(cj[base + 5]), x);
+    x = fmaf(wb.z, relu_bits(cj[base + 6]), x);
+    x = fmaf(wb.w, relu_bits(cj[base + 7]), x);
+    e[j] = x;
+  }
+  if (!ok_all) {
+    // a block outside some query's exactness bounds: those queries' scores in fp64 (never with real data;
+    // one rolled loop keeps this path's registers out of the main path's)
+    const int tq0 = blockIdx.x * kTileQueries;
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+      const int q = tile_slot_query(j, half);
+      const int* g = S.guard[q];
+      if (dk < g[0] || dk > g[1] || ks0 < g[2] || ks0 > g[3] || ks1 < g[4] || ks1 > g[5]) {
+        const int tq = tq0 + q < a.Tq ? tq0 + q : a.Tq - 1;
+        const float x = exact_block_score(codes + (size_t)jc * 32, ks0, ks1, S.qcode[q], S.qscale[q],
+                                          a.w + ((size_t)blockIdx.y * a.Tq + tq) * a.HI, a.HI);
+        e[0] = j == 0 ? x : e[0];
+        e[1] = j == 1 ? x : e[1];
+        e[2] = j == 2 ? x : e[2];
+        e[3] = j == 3 ? x : e[3];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) key[j] = jb < Q.N[j] ? order_key(e[j]) : 0u;
+}
+
+// This lane's key slice of block jb (clamped to the last block any query sees: always in bounds)
+__device__ __forceinline__ void tile_load(const uint8_t* codes, const uint8_t* scl, int jb, int Nmax, uint4& kb, int& ks,
+                                          int& jc) {
+  const int half = (threadIdx.x >> 5) & 1;
+  jc = jb < Nmax ? jb : Nmax - 1;
+  kb = *reinterpret_cast<const uint4*>(codes + (size_t)jc * 32 + half * 16);
+  ks = scl[(size_t)jc * 2 + half];
+}
+
+__global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
+  __shared__ TileLds S;
+  constexpr int kThreads = kTileWaves * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int b = blockIdx.y;
+  const int tq0 = blockIdx.x * kTileQueries;
+  // the blocks each query scores: all it sees when it selects (N > k) or the call keeps every key, else
+  // none (the selection writes the list of a query with N <= k)
+  if (tid < kTileQueries) {
+    const int tq = tq0 + tid;
+    const int64_t N = tq < a.Tq ? visible_blocks(a, b, tq) : 0;
+    S.Nq[tid] = (N > a.k || a.write_keys) ? (int32_t)N : 0;
+  }
+  if (tid < kTileQueries * 8) {
+    const int q = tid >> 3, h = tid & 7;
+    const int tq = tq0 + q < a.Tq ? tq0 + q : a.Tq - 1;
+    S.wts[q][h] = h < a.HI ? a.w[((size_t)b * a.Tq + tq) * a.HI + h] : 0.0f;
+  }
+  for (int i = tid; i < kTileQueries * kHistBins / 2; i += kThreads) (&S.hist[0][0])[i] = 0u;
+  // wave w quantises query w (a query that scores nothing gets bounds nothing fails)
+  if (wave < kTileQueries) {
+    const int tq = tq0 + wave < a.Tq ? tq0 + wave : a.Tq - 1;
+    ScoreQuery Qs;
+    const uint4 qraw = load_query(a, b, tq, Qs);
+    quantise_query_into(a, qraw, S.qcode[wave], S.qscale[wave], S.guard[wave]);
+  }
+  __syncthreads();
+  if (tid < kTileQueries && S.Nq[tid] == 0) {
+    S.guard[tid][0] = -100000; S.guard[tid][1] = 100000; S.guard[tid][2] = -100000;
+    S.guard[tid][3] = 100000; S.guard[tid][4] = -100000; S.guard[tid][5] = 100000;
+  }
+  __syncthreads();
+  int Nmax = 0;
+#pragma unroll
+  for (int q = 0; q < kTileQueries; ++q) Nmax = max(Nmax, (int)S.Nq[q]);
+  if (Nmax == 0) return;  // no query of the tile scores anything
+
+  TileQuery Q;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    int v = S.guard[0][i];
+#pragma unroll
+    for (int q = 1; q < kTileQueries; ++q) v = (i & 1) ? min(v, S.guard[q][i]) : max(v, S.guard[q][i]);
+    Q.g[i] = v;
+  }
+  {
+    // A row lane%32 = r: query (r/16) + 2 ((r/4) % 2) (+4 in A1), head 4 ((r/8) % 2) + r%4; this lane's
+    // half of the 64 dims
+    const int r = lane & 31;
+    const int qi = (r >> 4) + 2 * ((r >> 2) & 1), h = 4 * ((r >> 3) & 1) + (r & 3);
+    uint32_t x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = S.qcode[qi][h * 8 + half * 4 + u];
+      y[u] = S.qcode[qi + 4][h * 8 + half * 4 + u];
+    }
+    Q.A0 = (v8i){(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+    Q.A1 = (v8i){(int)y[0], (int)y[1], (int)y[2], (int)y[3], 0, 0, 0, 0};
+    Q.sA0 = S.qscale[qi][h * 2 + half];
+    Q.sA1 = S.qscale[qi + 4][h * 2 + half];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) Q.N[j] = S.Nq[tile_slot_query(j, half)];
+  const size_t kbase = (size_t)b * a.max_blocks;
+  const uint8_t* codes = a.idx_codes + kbase * 32;
+  const uint8_t* scl = a.idx_scale + kbase * 2;
+  const int nt = (Nmax + 31) / 32;
+
+  // ---- pass 1: histograms (the next tile's key slice is loaded before this one is scored)
+  {
+    uint4 kb;
+    int ks, jc;
+    int t = wave;
+    if (t < nt) tile_load(codes, scl, t * 32 + (lane & 31), Nmax, kb, ks, jc);
+    for (; t < nt; t += kTileWaves) {
+      uint4 kb2 = kb;
+      int ks2 = ks, jc2 = jc;
+      if (t + kTileWaves < nt) tile_load(codes, scl, (t + kTileWaves) * 32 + (lane & 31), Nmax, kb2, ks2, jc2);
+      uint32_t key[4];
+      tile_keys(a, S, Q, codes, kb, ks, t * 32 + (lane & 31), jc, key);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (key[j] != 0u) {
+          const uint32_t bin = key[j] >> 20;
+          atomicAdd(&S.hist[tile_slot_query(j, half)][bin >> 1], 1u << ((bin & 1u) << 4));
+        }
+      }
+      kb = kb2;
+      ks = ks2;
+      jc = jc2;
+    }
+  }
+  __syncthreads();
+  // ---- per query (wave w: query w): the bin where the count from the top reaches k
+  if (wave < kTileQueries && S.Nq[wave] > a.k) {
+    const uint32_t* hq = S.hist[wave];
+    const uint32_t kk = (uint32_t)a.k;
+    const int top = kHistBins / 2 - 32 * lane;  // this lane: words top-32 .. top-1 (64 bins), from the top
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 1; i <= 32; ++i) {
+      const uint32_t v = hq[top - i];
+      c += (v & 0xFFFFu) + (v >> 16);
+    }
+    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t excl = incl - c;
+    if (excl < kk && incl >= kk) {
+      uint32_t run = excl;
+      for (int i = 1; i <= 32; ++i) {
+        const uint32_t v = hq[top - i];
+        run += v >> 16;
+        if (run >= kk) {
+          S.Lkey[wave] = (uint32_t)(2 * (top - i) + 1) << 20;
+          break;
+        }
+        run += v & 0xFFFFu;
+        if (run >= kk) {
+          S.Lkey[wave] = (uint32_t)(2 * (top - i)) << 20;
+          break;
+        }
+      }
+      S.ncand[wave] = run;
+    }
+  }
+  __syncthreads();
+
+  // ---- pass 2: candidates (key >= L) in index order, one segment of kScanPerWG blocks at a time
+  // this lane's queries' workspace rows (valid only where the query scores)
+  auto qrow = [&](int j) { return b * a.Tq + tq0 + tile_slot_query(j, half); };
+  uint32_t Lk[4];
+  bool sel[4], ovf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tile_slot_query(j, half);
+    sel[j] = Q.N[j] > a.k;  // only a query that selects has candidates
+    Lk[j] = sel[j] ? S.Lkey[q] : 0u;
+    ovf[j] = Q.N[j] > 0 && (a.write_keys || (sel[j] && S.ncand[q] > (uint32_t)kCandCap));
+  }
+  constexpr int kRoundBlocks = kTileWaves * 32;
+  static_assert(kScanPerWG % kRoundBlocks == 0, "a round of tiles lies in one candidate segment");
+  const int nrounds = (nt + kTileWaves - 1) / kTileWaves;
+  const uint32_t below = (1u << (lane & 31)) - 1u;
+  uint32_t run[4] = {0u, 0u, 0u, 0u};
+  int seg = 0;
+  uint4 kb;
+  int ks, jc;
+  if (wave < nt) tile_load(codes, scl, wave * 32 + (lane & 31), Nmax, kb, ks, jc);
+  for (int r = 0; r < nrounds; ++r) {
+    const int t = r * kTileWaves + wave;
+    const int jb = t * 32 + (lane & 31);
+    const int rseg = (r * kRoundBlocks) / kScanPerWG;
+    if (rseg != seg) {
+      if (wave == 0 && (lane & 31) == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (sel[j]) q_seg(a, qrow(j))[seg] = run[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) run[j] = 0u;
+      seg = rseg;
+    }
+    uint4 kb2 = kb;
+    int ks2 = ks, jc2 = jc;
+    if (t + kTileWaves < nt) tile_load(codes, scl, (t + kTileWaves) * 32 + (lane & 31), Nmax, kb2, ks2, jc2);
+    uint32_t key[4] = {0u, 0u, 0u, 0u};
+    if (t < nt) tile_keys(a, S, Q, codes, kb, ks, jb, jc, key);
+    kb = kb2;
+    ks = ks2;
+    jc = jc2;
+    uint32_t mine[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t m = __ballot(sel[j] && key[j] != 0u && key[j] >= Lk[j]);
+      mine[j] = half ? (uint32_t)(m >> 32) : (uint32_t)m;
+      if (lane == 0) {
+        S.cnt[r & 1][wave][j] = (uint32_t)__popc((uint32_t)m);
+        S.cnt[r & 1][wave][j + 4] = (uint32_t)__popc((uint32_t)(m >> 32));
+      }
+    }
+    __syncthreads();
+    uint32_t before[4] = {0u, 0u, 0u, 0u}, tot[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < kTileWaves; ++w) {
+      const uint4 c = *reinterpret_cast<const uint4*>(&S.cnt[r & 1][w][4 * half]);
+      const uint32_t cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        before[j] += w < wave ? cv[j] : 0u;
+        tot[j] += cv[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((mine[j] >> (lane & 31)) & 1u) {
+        const uint32_t pos = run[j] + before[j] + (uint32_t)__popc(mine[j] & below);
+        q_cand(a, qrow(j))[(size_t)seg * kScanPerWG + pos] =
+            ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)jb);
+      }
+      run[j] += tot[j];
+      if (ovf[j] && jb < Q.N[j]) q_keys(a, qrow(j))[jb] = key[j];
+    }
+  }
+  if (wave == 0 && (lane & 31) == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sel[j]) q_seg(a, qrow(j))[seg] = run[j];
+  }
+}
+
 // Candidate scan: every key >= L (the bound the query's global histogram gives) is written, in index
 // order, to this workgroup's segment of the candidate row; the segment's count goes to seg. A query with
 // at most k visible blocks gets its whole list (and its histogram cleared) here.
@@ -641,9 +971,18 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs args) {
 __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   __shared__ SelectLds S;
   const int q = blockIdx.x;
-  const int64_t N = visible_blocks(a, q / a.Tq, q % a.Tq);
-  if (N <= a.k) return;
-  for (int i = threadIdx.x; i < kHistBins; i += 512) q_hist(a, q)[i] = 0u;
+  const int b = q / a.Tq, tq = q % a.Tq;
+  const int64_t N = visible_blocks(a, b, tq);
+  if (N <= a.k) {
+    // query tiles leave no scan to write the list of a query that sees at most k blocks
+    if (a.tiles && query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq) >= 0) {
+      int32_t* out = a.topk + (size_t)q * a.k;
+      for (int i = threadIdx.x; i < a.k; i += 512) out[i] = (i < N) ? i : -1;
+    }
+    return;
+  }
+  if (!a.tiles)  // query tiles never count into the global histograms
+    for (int i = threadIdx.x; i < kHistBins; i += 512) q_hist(a, q)[i] = 0u;
   int32_t* out = a.topk + (size_t)q * a.k;
   const uint32_t n = select_query(a, q, N, S, out);
   for (int i = (int)n + (int)threadIdx.x; i < a.k; i += 512) out[i] = -1;  // only if fewer than k were found
@@ -657,6 +996,11 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
   const unsigned nq = (unsigned)(B * a.Tq);
   // a workgroup per chunk, or (many queries) chunk_step workgroups per query, each over every
   // chunk_step-th chunk
+  if (a.tiles) {
+    const unsigned gx = (unsigned)((a.Tq + kTileQueries - 1) / kTileQueries);
+    hipLaunchKernelGGL(tile_kernel, dim3(gx, (unsigned)B), dim3(kTileWaves * 64), 0, s, a);
+    return hipGetLastError();
+  }
   unsigned g1 = a.chunk_step > 0 ? (unsigned)a.chunk_step : (unsigned)((N_last + kScoreChunk - 1) / kScoreChunk);
   hipLaunchKernelGGL(score_kernel, dim3(g1, nq), dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
@@ -670,6 +1014,12 @@ hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool
   if (g2 < 1) g2 = 1;
   ScanArgs args{};
   args.a = a;
+  if (a.tiles) {
+    // the score launch wrote the candidates; a decode step's append never comes with query tiles
+    if (app && app_units > 0) return hipErrorInvalidValue;
+    if (with_select) hipLaunchKernelGGL(select_kernel, dim3(nq), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   if (app && app_units > 0) {
     args.app = *app;
     args.app_units = app_units;

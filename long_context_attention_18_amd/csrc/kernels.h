@@ -19,6 +19,12 @@ constexpr int kScoreThreads = kScoreWaves * 64;
 // Calls with at least kMultiMinQueries queries (chunked prefill) score kMultiChunks chunks per workgroup
 constexpr int kMultiMinQueries = 512;
 constexpr int kMultiChunks = 8;
+// Calls with at least kTileMinQueries queries, each seeing at most kTileMaxBlocks blocks, score in query
+// tiles: kTileQueries queries of one sequence per workgroup of kTileWaves waves (indexer.hip)
+constexpr int kTileMinQueries = 2048;
+constexpr int kTileQueries = 8;
+constexpr int kTileWaves = 8;
+constexpr int64_t kTileMaxBlocks = 65535;
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
@@ -28,6 +34,7 @@ constexpr int kMaxSegs = (int)(kMaxBlocks / kScanPerWG);  // candidate-scan segm
 // ---- attention tiling ----------------------------------------------------
 constexpr int kAttnKeys = 64;                         // keys staged per iteration (many-query kernel)
 constexpr int kAttendMaxQueries = 511;                // up to this many queries per call: attend.hip
+static_assert(kTileMinQueries > kAttendMaxQueries, "decode-step calls (with their append) never use query tiles");
 constexpr int64_t kMaxGridY = 65535;                  // launch limit of grid.y (indexer grids: one row per query)
 
 struct IngestArgs {
@@ -83,6 +90,8 @@ struct ScoreArgs {
   int32_t G2;              // scan segments per query
   int32_t cmin;            // keys each score workgroup counts into the histogram at least (twice its share of k)
   int32_t chunk_step;      // 0: a score workgroup per 2048-block chunk; else one per chunk_step chunks of a query
+  int32_t tiles;           // 1: query tiles (the score launch also writes the candidates; no scan)
+  int32_t write_keys;      // tiles: also write every visible block's key (the separate score call's contract)
   // ragged batches (see IngestArgs): the queries of sequence b are its seq_T[b] new tokens, positions
   // seq_len[b] + i for rows i < seq_T[b]; null: positions len - Tq + i
   const int64_t* seq_len;

@@ -18,6 +18,10 @@ REL_L2 = 1e-2
 MAX_ABS = 2e-2
 
 
+# queries per call from which the indexer's multi-chunk and query-tile paths apply
+MANY_QUERIES = 512
+
+
 def to_dev(a: np.ndarray):
     import torch
     if a.dtype == np.uint16:
@@ -118,6 +122,15 @@ class LayerRun:
                 self.dev.indexer_topk(to_dev(qin["qI"]), to_dev(qin["w"]), topk)
             torch.cuda.synchronize()
             if self.len // self.m > self.layer.topk:
+                if self.B * Tq >= MANY_QUERIES:
+                    # with many queries the combined calls keep no per-block scores: score again through
+                    # lca_csa_index_score (which keeps them) + lca_csa_topk_select, same lists required
+                    qI, w = to_dev(qin["qI"]), to_dev(qin["w"])
+                    tk2 = torch.full_like(topk, -7)
+                    self.dev.index_score(qI, w)
+                    self.dev.topk_select(Tq, tk2)
+                    torch.cuda.synchronize()
+                    assert torch.equal(tk2, topk), "separate score + select calls chose other lists"
                 self.last_scores = self.dev.index_scores(Tq)
             if not fused:
                 self.dev.sparse_attn(to_dev(qin["q"]), topk, out, lse)

@@ -115,6 +115,45 @@ def test_csa_prefill_many_queries_long_context():
         print("prefill long-context", B, Tq, w)
 
 
+def test_csa_prefill_query_tiles():
+    """Calls of 2048+ queries score in query tiles (8 queries of one sequence per workgroup, both passes).
+    B = 2 x Tq = 1030 (the last tile of each sequence partial) over about 7,800 blocks; then one sequence of
+    2056 queries from an empty cache, so tiles mix queries that see at most k blocks with queries that
+    select. Sampled queries: scores and top-k bit-exact, attention within the bar; the combined call and
+    the separate score + select calls give the same lists."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=256)
+    for B, Tq, pre in ((2, 1030, 30000), (1, 2056, 0)):
+        run = LayerRun(layer, B=B, max_ctx=pre + Tq, ring=Tq + 127, max_tq=Tq, sigma=1.0)
+        _ingest(run, ([pre] if pre else []) + [Tq])
+        qin, topk, out, lse = run.run_queries(Tq)
+        oc = [run.oracle_caches(b, pre + Tq) for b in range(run.B)]
+        pos = list(range(run.len - Tq, run.len))
+        w = check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 61)) + [Tq - 2, Tq - 1])
+        assert w["scores_checked"] > 0
+        print("query tiles", B, Tq, pre, w)
+
+
+def test_csa_query_tiles_all_weights_negative():
+    """Query tiles with every indexer weight negative: most scores are 0, so the bin that holds the k-th
+    key holds more candidates than the selection's LDS, and the tile kernel writes every key for the
+    selection's path over all blocks. Top-k and scores still bit-exact."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=256)
+
+    def qtransform(qin):
+        out = dict(qin)
+        out["w"] = -np.abs(qin["w"])
+        return out
+
+    Tq, pre = 2048, 40000
+    run = LayerRun(layer, B=1, max_ctx=pre + Tq, ring=Tq + 127, max_tq=Tq, sigma=1.0, qtransform=qtransform)
+    _ingest(run, [pre, Tq])
+    qin, topk, out, lse = run.run_queries(Tq)
+    oc = [run.oracle_caches(0, pre + Tq)]
+    pos = list(range(run.len - Tq, run.len))
+    w = check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 97)) + [Tq - 1])
+    assert w["scores_checked"] > 0
+
+
 def test_ingest_chunking_invariance():
     """The same token stream ingested token by token, in 7s, or at once: identical cache bytes."""
     layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
