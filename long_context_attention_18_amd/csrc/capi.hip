@@ -93,7 +93,10 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
     size_t q = align_up((size_t)kHistBins * 4);
-    W.off_seg = q; q = align_up(q + (size_t)W.G2 * 4);
+    // segment counts: kScanPerWG blocks per scan segment, kTileSeg per query-tile segment
+    const int64_t tile_blocks = max_blocks < kTileMaxBlocks ? max_blocks : kTileMaxBlocks;
+    const int64_t n_seg = std::max<int64_t>(W.G2, (tile_blocks + kTileSeg - 1) / kTileSeg);
+    W.off_seg = q; q = align_up(q + (size_t)n_seg * 4);
     W.off_keys = q; q = align_up(q + (size_t)max_blocks * 4);
     W.off_cand = q; q = align_up(q + (size_t)max_blocks * 8);
     W.qstride = q;

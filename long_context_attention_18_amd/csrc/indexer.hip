@@ -60,9 +60,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// bits(s) ^ 0xFFFFFFFF for a negative s, bits(s) | 0x80000000 otherwise: unsigned keys order like the floats
 __device__ __forceinline__ uint32_t order_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
@@ -584,6 +585,7 @@ __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(
 
 // Keys of block jb (the lane's column) for this lane's four queries, from its loaded key slice; 0 where
 // the query does not see the block. Every lane of the wave calls it (MFMA and lane swap).
+template <bool CHECK>
 __device__ __forceinline__ void tile_keys(const ScoreArgs& a, const TileLds& S, const TileQuery& Q, const uint8_t* codes,
                                           uint4 kb, int ks, int jb, int jc, uint32_t (&key)[4]) {
   const int half = (threadIdx.x >> 5) & 1;
@@ -636,7 +638,16 @@ __device__ __forceinline__ void tile_keys(const ScoreArgs& a, const TileLds& S, 
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) key[j] = jb < Q.N[j] ? order_key(e[j]) : 0u;
+  for (int j = 0; j < 4; ++j) key[j] = (!CHECK || jb < Q.N[j]) ? order_key(e[j]) : 0u;
+}
+
+// tile_keys, with the per-query visibility test only for a tile that reaches past the fewest blocks a
+// scoring query of the workgroup sees (Nmin); a query that scores nothing needs no zero keys
+__device__ __forceinline__ void tile_keys_at(const ScoreArgs& a, const TileLds& S, const TileQuery& Q, const uint8_t* codes,
+                                             uint4 kb, int ks, int t, int Nmin, int jc, uint32_t (&key)[4]) {
+  const int jb = t * 32 + (threadIdx.x & 31);
+  if (t * 32 + 32 <= Nmin) tile_keys<false>(a, S, Q, codes, kb, ks, jb, jc, key);
+  else tile_keys<true>(a, S, Q, codes, kb, ks, jb, jc, key);
 }
 
 // This lane's key slice of block jb (clamped to the last block any query sees: always in bounds)
@@ -680,9 +691,12 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
     S.guard[tid][3] = 100000; S.guard[tid][4] = -100000; S.guard[tid][5] = 100000;
   }
   __syncthreads();
-  int Nmax = 0;
+  int Nmax = 0, Nmin = 0x7FFFFFFF;
 #pragma unroll
-  for (int q = 0; q < kTileQueries; ++q) Nmax = max(Nmax, (int)S.Nq[q]);
+  for (int q = 0; q < kTileQueries; ++q) {
+    Nmax = max(Nmax, (int)S.Nq[q]);
+    if (S.Nq[q] > 0) Nmin = min(Nmin, (int)S.Nq[q]);
+  }
   if (Nmax == 0) return;  // no query of the tile scores anything
 
   TileQuery Q;
@@ -727,7 +741,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
       int ks2 = ks, jc2 = jc;
       if (t + kTileWaves < nt) tile_load(codes, scl, (t + kTileWaves) * 32 + (lane & 31), Nmax, kb2, ks2, jc2);
       uint32_t key[4];
-      tile_keys(a, S, Q, codes, kb, ks, t * 32 + (lane & 31), jc, key);
+      tile_keys_at(a, S, Q, codes, kb, ks, t, Nmin, jc, key);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (key[j] != 0u) {
@@ -774,7 +788,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
   }
   __syncthreads();
 
-  // ---- pass 2: candidates (key >= L) in index order, one segment of kScanPerWG blocks at a time
+  // ---- pass 2: candidates (key >= L) in index order. Wave w writes segments w, w + kTileWaves, ... of
+  // kTileSeg blocks each, in block order, so it needs no other wave's counts.
   // this lane's queries' workspace rows (valid only where the query scores)
   auto qrow = [&](int j) { return b * a.Tq + tq0 + tile_slot_query(j, half); };
   uint32_t Lk[4];
@@ -783,77 +798,50 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int q = tile_slot_query(j, half);
     sel[j] = Q.N[j] > a.k;  // only a query that selects has candidates
-    Lk[j] = sel[j] ? S.Lkey[q] : 0u;
+    // valid keys are never 0, so key >= max(L, 1) also leaves out the blocks a query does not see; no
+    // key of a finite score reaches 0xFFFFFFFF
+    Lk[j] = sel[j] ? max(S.Lkey[q], 1u) : 0xFFFFFFFFu;
     ovf[j] = Q.N[j] > 0 && (a.write_keys || (sel[j] && S.ncand[q] > (uint32_t)kCandCap));
   }
-  constexpr int kRoundBlocks = kTileWaves * 32;
-  static_assert(kScanPerWG % kRoundBlocks == 0, "a round of tiles lies in one candidate segment");
-  const int nrounds = (nt + kTileWaves - 1) / kTileWaves;
-  const uint32_t below = (1u << (lane & 31)) - 1u;
-  uint32_t run[4] = {0u, 0u, 0u, 0u};
-  int seg = 0;
-  uint4 kb;
-  int ks, jc;
-  if (wave < nt) tile_load(codes, scl, wave * 32 + (lane & 31), Nmax, kb, ks, jc);
-  for (int r = 0; r < nrounds; ++r) {
-    const int t = r * kTileWaves + wave;
-    const int jb = t * 32 + (lane & 31);
-    const int rseg = (r * kRoundBlocks) / kScanPerWG;
-    if (rseg != seg) {
-      if (wave == 0 && (lane & 31) == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (sel[j]) q_seg(a, qrow(j))[seg] = run[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) run[j] = 0u;
-      seg = rseg;
-    }
-    uint4 kb2 = kb;
-    int ks2 = ks, jc2 = jc;
-    if (t + kTileWaves < nt) tile_load(codes, scl, (t + kTileWaves) * 32 + (lane & 31), Nmax, kb2, ks2, jc2);
-    uint32_t key[4] = {0u, 0u, 0u, 0u};
-    if (t < nt) tile_keys(a, S, Q, codes, kb, ks, jb, jc, key);
-    kb = kb2;
-    ks = ks2;
-    jc = jc2;
-    uint32_t mine[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint64_t m = __ballot(sel[j] && key[j] != 0u && key[j] >= Lk[j]);
-      mine[j] = half ? (uint32_t)(m >> 32) : (uint32_t)m;
-      if (lane == 0) {
-        S.cnt[r & 1][wave][j] = (uint32_t)__popc((uint32_t)m);
-        S.cnt[r & 1][wave][j + 4] = (uint32_t)__popc((uint32_t)(m >> 32));
-      }
-    }
-    __syncthreads();
-    uint32_t before[4] = {0u, 0u, 0u, 0u}, tot[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int w = 0; w < kTileWaves; ++w) {
-      const uint4 c = *reinterpret_cast<const uint4*>(&S.cnt[r & 1][w][4 * half]);
-      const uint32_t cv[4] = {c.x, c.y, c.z, c.w};
+  constexpr int kSegTiles = kTileSeg / 32;
+  static_assert(kTileSeg % 32 == 0, "a candidate segment is whole tiles");
+  const int nseg = (Nmax + kTileSeg - 1) / kTileSeg;
+  for (int sg = wave; sg < nseg; sg += kTileWaves) {
+    const int t0 = sg * kSegTiles, t1 = min(t0 + kSegTiles, nt);
+    uint32_t run[4] = {0u, 0u, 0u, 0u};
+    uint4 kb;
+    int ks, jc;
+    tile_load(codes, scl, t0 * 32 + (lane & 31), Nmax, kb, ks, jc);
+    for (int t = t0; t < t1; ++t) {
+      const int jb = t * 32 + (lane & 31);
+      uint4 kb2 = kb;
+      int ks2 = ks, jc2 = jc;
+      if (t + 1 < t1) tile_load(codes, scl, jb + 32, Nmax, kb2, ks2, jc2);
+      uint32_t key[4];
+      tile_keys_at(a, S, Q, codes, kb, ks, t, Nmin, jc, key);
+      kb = kb2;
+      ks = ks2;
+      jc = jc2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        before[j] += w < wave ? cv[j] : 0u;
-        tot[j] += cv[j];
+        const bool c = key[j] >= Lk[j];
+        const uint64_t m = __ballot(c);
+        const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+        // candidates of this half before this lane, and in this half
+        const uint32_t nlo = (uint32_t)__popc(lo);
+        const uint32_t pre = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (half ? nlo : 0u);
+        if (c)
+          q_cand(a, qrow(j))[(size_t)sg * kTileSeg + run[j] + pre] =
+              ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)jb);
+        run[j] += half ? (uint32_t)__popc(hi) : nlo;
+        if (ovf[j] && jb < Q.N[j]) q_keys(a, qrow(j))[jb] = key[j];
       }
     }
+    if ((lane & 31) == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if ((mine[j] >> (lane & 31)) & 1u) {
-        const uint32_t pos = run[j] + before[j] + (uint32_t)__popc(mine[j] & below);
-        q_cand(a, qrow(j))[(size_t)seg * kScanPerWG + pos] =
-            ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)jb);
-      }
-      run[j] += tot[j];
-      if (ovf[j] && jb < Q.N[j]) q_keys(a, qrow(j))[jb] = key[j];
+      for (int j = 0; j < 4; ++j)
+        if (sel[j]) q_seg(a, qrow(j))[sg] = run[j];
     }
-  }
-  if (wave == 0 && (lane & 31) == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (sel[j]) q_seg(a, qrow(j))[seg] = run[j];
   }
 }
 

@@ -25,11 +25,13 @@ constexpr int kTileMinQueries = 2048;
 constexpr int kTileQueries = 8;
 constexpr int kTileWaves = 8;
 constexpr int64_t kTileMaxBlocks = 65535;
+constexpr int kTileSeg = 256;  // blocks per candidate segment of the query tiles (one wave writes a segment)
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
 constexpr int64_t kMaxBlocks = 2048LL * kScoreChunk;  // compressed blocks per sequence the indexer serves
 constexpr int kMaxSegs = (int)(kMaxBlocks / kScanPerWG);  // candidate-scan segments per query (512)
+static_assert((kTileMaxBlocks + kTileSeg - 1) / kTileSeg <= kMaxSegs, "query-tile segments fit the selection");
 
 // ---- attention tiling ----------------------------------------------------
 constexpr int kAttnKeys = 64;                         // keys staged per iteration (many-query kernel)
@@ -70,7 +72,7 @@ struct IngestArgs {
 };
 
 // The indexer's workspace is one block per query (so its place does not depend on how many queries
-// a call has): [histogram kHistBins u32][seg_cnt G2 u32][keys max_blocks u32]
+// a call has): [histogram kHistBins u32][seg_cnt u32 per candidate segment][keys max_blocks u32]
 // [candidates max_blocks u64], each part 256-byte aligned, qstride bytes per query.
 struct ScoreArgs {
   const uint16_t* qI;      // [B][Tq][HI][64]

@@ -55,8 +55,11 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   uint32_t* wsum = S.wsum;
 
   // One round of loads: every segment's count and, speculatively, its first kSpec slots (always in
-  // bounds: a segment has room for kScanPerWG candidates); only a fuller segment needs a second round.
-  const int G2_q = (int)((N + kScanPerWG - 1) / kScanPerWG);
+  // bounds: a segment has room for seg_sz candidates, and the workspace continues after the last
+  // query's); only a fuller segment needs a second round. Segments: kScanPerWG blocks (candidate scan)
+  // or kTileSeg (query tiles).
+  const int seg_sz = a.tiles ? kTileSeg : kScanPerWG;
+  const int G2_q = (int)((N + seg_sz - 1) / seg_sz);
   constexpr int kSpec = 256;
   const uint64_t* cand = q_cand(a, q);
   const int lanes_per_seg = G2_q <= 32 ? 16 : (G2_q <= 64 ? 8 : 0);  // speculation only for few segments
@@ -68,7 +71,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   if (lanes_per_seg && my_seg < G2_q) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (r < per_lane) spec[r] = cand[(size_t)my_seg * kScanPerWG + my_sub + r * lanes_per_seg];
+      if (r < per_lane) spec[r] = cand[(size_t)my_seg * seg_sz + my_sub + r * lanes_per_seg];
   }
   if (tid == 0) S.flat_needed = 0u;
   for (int g0 = 0; g0 < G2_q; g0 += 512) {
@@ -119,7 +122,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
         }
         const uint32_t off = i - seg_off[l];
         if (off >= covered) {
-          const uint64_t e = cand[(size_t)l * kScanPerWG + off];
+          const uint64_t e = cand[(size_t)l * seg_sz + off];
           cs[i] = e;
           lo = e < lo ? e : lo;
           hi = e > hi ? e : hi;
