@@ -6,6 +6,10 @@ hipcc cross-compiles here without a GPU. Flags:
                       fused multiply-adds are written explicitly.
   -Xclang -target-feature -Xclang -packed-fp32-ops
                       keep the compiler from forming packed fp32 VALU ops.
+  -mllvm --amdgpu-mfma-vgpr-form
+                      MFMA accumulators in VGPRs: an accumulator the VALU
+                      also touches (attention's output rescale) is otherwise
+                      copied between AGPRs and VGPRs on every loop trip.
 """
 import glob
 import os
@@ -32,7 +36,7 @@ def build(force: bool = True, verbose: bool = False) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "--amdgpu-mfma-vgpr-form",
                "-Wall", "-Wno-unused-function", "-c", src, "-o", obj]
         procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), src))
         objs.append(obj)

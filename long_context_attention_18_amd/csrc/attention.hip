@@ -36,6 +36,7 @@ struct ManyLds {
   uint16_t kd[2][kMChunk * kKdStride];    // key-major chunk (two buffers)
   uint16_t vt[2][kHeadDim * kMVtStride];  // dim-major chunk, keys in MFMA K order
   float scl[2][kMChunk];                  // the keys' FP8 scales (>= 0); -1 marks a slot without a key
+  uint32_t bad[2][kMWaves];               // per buffer and staging wave: some slot of the chunk holds no key
   int32_t list[kMaxTopk];                 // CSA: the query's top-k row
   float cos_t[32], sin_t[32];
 };
@@ -54,26 +55,26 @@ struct Query {
   const uint16_t *blk_rope, *win_rope;
   const float *blk_scale, *win_scale;
   size_t blk_row, win_row;  // b * max_blocks, b * ring
-  int64_t t, N;
-  int32_t n_first, total, W, ring;
+  int32_t N;                // visible blocks
+  int32_t n_first, total;   // slots [0, n_first): top-k row or dense blocks; then n_win window positions
+  int32_t win_base, ring;   // ring slot of the first window position (t - n_win + 1)
   bool dense;
 };
 
-// entry of key slot `slot`: slots [0, n_first) the top-k row or the dense blocks, then the window of
-// positions t-W+1 .. t; branch-free, with an in-bounds entry for slots that hold no key
+// entry of key slot `slot` (32-bit index arithmetic): slots [0, n_first) the top-k row or the dense
+// blocks, then the window positions t - n_win + 1 .. t; branch-free, with an in-bounds entry for slots
+// that hold no key
 __device__ __forceinline__ void slot_entry(const Query& Q, const int32_t* list, int slot, size_t* e, bool* win,
                                            bool* valid) {
   const bool in_first = slot < Q.n_first;
-  const int ls = in_first ? slot : 0;
-  const int64_t j = Q.dense ? (int64_t)ls : (int64_t)list[ls];
-  const int64_t s = Q.t - Q.W + 1 + (slot - Q.n_first);
+  const int j = Q.dense ? slot : list[in_first ? slot : 0];
   const bool ok_blk = j >= 0 && j < Q.N;
-  const bool ok_win = s >= 0;
-  *valid = slot < Q.total && (in_first ? ok_blk : ok_win);
+  const bool live = slot < Q.total;
+  int ws = Q.win_base + (slot - Q.n_first);  // < 2 ring for a live window slot: one conditional wrap
+  ws = ws >= Q.ring ? ws - Q.ring : ws;
+  *valid = live && (!in_first || ok_blk);
   *win = !in_first;
-  const int64_t jc = ok_blk ? j : 0;
-  const int64_t sc = ok_win ? s : 0;
-  *e = in_first ? Q.blk_row + (size_t)jc : Q.win_row + (size_t)(sc % Q.ring);
+  *e = in_first ? Q.blk_row + (uint32_t)(ok_blk ? j : 0) : Q.win_row + (uint32_t)(live ? ws : 0);
 }
 
 __device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int chunk0, int pp, int r, Fetch& F) {
@@ -92,8 +93,10 @@ __device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int c
   }
 }
 
-// the fetched dims into the chunk buffers: key-major rows and (tile 0, tile 1) pairs of dim-major rows
-__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, uint16_t* vt, float* scl) {
+// the fetched dims into the chunk buffers: key-major rows and (tile 0, tile 1) pairs of dim-major rows;
+// bad[wave]: whether some key of this wave's share is missing (the chunk then needs the masked path)
+__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, uint16_t* vt, float* scl,
+                                      uint32_t* bad) {
   u32x4 v[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -112,6 +115,8 @@ __device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* k
     scl[r] = F.valid[0] ? F.scale[0] : -1.0f;
     scl[16 + r] = F.valid[1] ? F.scale[1] : -1.0f;
   }
+  const uint64_t m = __ballot(!F.valid[0] || !F.valid[1]);
+  if ((threadIdx.x & 63) == 0) bad[threadIdx.x >> 6] = m != 0 ? 1u : 0u;
 }
 
 __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
@@ -132,13 +137,13 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
   Q.win_scale = a.win_scale;
   Q.blk_row = (size_t)b * a.max_blocks;
   Q.win_row = (size_t)b * a.ring;
-  Q.t = t;
-  Q.N = min((t + 1) / a.m, a.max_blocks);  // 0 for the window-only layer
+  Q.N = (int32_t)min((t + 1) / a.m, a.max_blocks);  // 0 for the window-only layer
   Q.dense = a.dense != 0;
-  Q.n_first = Q.dense ? (int32_t)Q.N : a.k;
-  Q.total = Q.n_first + a.W;
-  Q.W = a.W;
+  Q.n_first = Q.dense ? Q.N : a.k;
+  const int32_t n_win = (int32_t)min((int64_t)a.W, t + 1);
+  Q.total = Q.n_first + n_win;
   Q.ring = a.ring;
+  Q.win_base = (int32_t)((t - n_win + 1) % a.ring);
 
   // RoPE angles of position t, the top-k row (CSA), the query rows (head 16 * wave + r, dims 32 ks + 8 g)
   if (tid < 32) {
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     }
     qb[ks] = __builtin_bit_cast(bf16x8, v);
   }
-  stage(F, pp, rr, S.kd[0], S.vt[0], S.scl[0]);
+  stage(F, pp, rr, S.kd[0], S.vt[0], S.scl[0], S.bad[0]);
   __syncthreads();
 
   constexpr float kC = kLog2eRsqrtD;
@@ -216,10 +221,16 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
         ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 64)), qb[2], ar, 0, 0, 0);
         ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 96)), qb[3], ar, 0, 0, 0);
         sc4[tt] = *reinterpret_cast<const v4f*>(scl + tt * 16 + 4 * g);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Sv[tt][v] = fmaf(an[v], sc4[tt][v], ar[v]);
+      }
+      if (S.bad[cur][0] | S.bad[cur][1] | S.bad[cur][2] | S.bad[cur][3]) {
         // a slot without a key (scale -1, all-zero dims) is masked; an entry whose nope part is all
         // zero has scale 0 and is a key like any other
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Sv[tt][v] = sc4[tt][v] >= 0.0f ? an[v] * sc4[tt][v] + ar[v] : -INFINITY;
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Sv[tt][v] = sc4[tt][v] >= 0.0f ? Sv[tt][v] : -INFINITY;
       }
       // online softmax of head r (its 32 keys are spread over the 4 lane groups)
       float mx = fmaxf(fmaxf(fmaxf(Sv[0][0], Sv[0][1]), fmaxf(Sv[0][2], Sv[0][3])),
@@ -235,13 +246,13 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
         for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
         m_run = m_new;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      const float mk = (m_run == -INFINITY) ? 0.0f : m_run * kC;  // exp2 argument S kC - m kC, one fma
       float rs = 0.0f;
       u32x4 pr, pn;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p0 = __builtin_amdgcn_exp2f((Sv[0][v] - m_use) * kC);
-        const float p1 = __builtin_amdgcn_exp2f((Sv[1][v] - m_use) * kC);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(Sv[0][v], kC, -mk));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(Sv[1][v], kC, -mk));
         rs += p0 + p1;
         pr[v] = pack_bf16(p0, p1);
         pn[v] = pack_bf16(p0 * sc4[0][v], p1 * sc4[1][v]);
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       }
     }
     // the next chunk into the other buffer (last read in the previous step, before the barrier below)
-    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.vt[cur ^ 1], S.scl[cur ^ 1]);
+    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.vt[cur ^ 1], S.scl[cur ^ 1], S.bad[cur ^ 1]);
     __syncthreads();
   }
 
