@@ -10,14 +10,17 @@
 //   out   = softmax over ALL keys (one normalisation) . x
 //
 // All query heads share the one KV head. One workgroup per query, one wave per 16 heads. The keys go
-// 32 at a time through LDS, gathered, converted and transposed once for all heads: every thread
-// brings in 8 dims of two keys (key r of the two 16-key tiles), writes them key-major for S^T = K.Q^T
-// (keys as the MFMA's M dimension) and, as pairs (tile 0, tile 1) of one dim, dim-major for
-// O^T = V^T.P^T. The S^T accumulator is exactly the B operand of that product when MFMA K index
-// 8g + 2v + t is key 4g+v of tile t, so P never leaves registers. The FP8 codes and the BF16 RoPE dims
-// are exact in bf16; the per-entry fp32 scale multiplies the nope logits and is folded into P for the
-// nope output dims. The next chunk's gathers are issued before the current chunk is computed, into
-// the second of two LDS buffers, one barrier per chunk. Calls with up to 511 queries use attend.hip.
+// 32 at a time through LDS, gathered and converted once for all heads: every thread brings in 8 dims
+// of two keys (key r of the two 16-key tiles) and writes them key-major, the A operand of
+// S^T = K.Q^T (keys as the MFMA's M dimension). The S^T accumulator is exactly the B operand of
+// O^T = V^T.P^T when MFMA K index 8g + 2v + t is key 4g+v of tile t, so P never leaves registers, and
+// the V^T operand comes from the same key-major rows through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16: lane 4a + e of a 16-lane group gets element e of the 8-byte rows the group's
+// lanes a, a+4, a+8, a+12 address), each lane addressing the key its K index needs. The FP8 codes and
+// the BF16 RoPE dims are exact in bf16; the per-entry fp32 scale multiplies the nope logits and is
+// folded into P for the nope output dims. The next chunk's gathers are issued before the current chunk
+// is computed, into the second of two LDS buffers, one barrier per chunk. Calls with up to 511 queries
+// use attend.hip.
 #include "attn_common.h"
 #include "dev_formats.h"
 #include "kernels.h"
@@ -30,11 +33,11 @@ constexpr int kMWaves = 4;       // one wave per 16-head group
 constexpr int kMThreads = kMWaves * 64;
 constexpr int kMChunk = 32;      // keys per step: two 16-key tiles
 constexpr int kKdStride = 136;   // bf16 per key-major row (128 + 8 pad)
-constexpr int kMVtStride = 40;   // bf16 per dim-major row (32 keys + 8 pad; 80 B keeps 16-B reads aligned)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct ManyLds {
   uint16_t kd[2][kMChunk * kKdStride];    // key-major chunk (two buffers)
-  uint16_t vt[2][kHeadDim * kMVtStride];  // dim-major chunk, keys in MFMA K order
   float scl[2][kMChunk];                  // the keys' FP8 scales (>= 0); -1 marks a slot without a key
   uint32_t bad[2][kMWaves];               // per buffer and staging wave: some slot of the chunk holds no key
   int32_t list[kMaxTopk];                 // CSA: the query's top-k row
@@ -93,23 +96,15 @@ __device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int c
   }
 }
 
-// the fetched dims into the chunk buffers: key-major rows and (tile 0, tile 1) pairs of dim-major rows;
-// bad[wave]: whether some key of this wave's share is missing (the chunk then needs the masked path)
-__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, uint16_t* vt, float* scl,
-                                      uint32_t* bad) {
-  u32x4 v[2];
+// the fetched dims into the chunk buffer's key-major rows; bad[wave]: whether some key of this wave's
+// share is missing (the chunk then needs the masked path)
+__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, float* scl, uint32_t* bad) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    v[tt] = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
-    if (!F.valid[tt]) v[tt] = zero;
-    *reinterpret_cast<u32x4*>(kd + (tt * 16 + r) * kKdStride + 8 * pp) = v[tt];
-  }
-  const int kpos = 8 * (r >> 2) + 2 * (r & 3);  // MFMA K index of key r of tile 0 (tile 1: +1)
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const uint32_t pair = __builtin_amdgcn_perm(v[1][u >> 1], v[0][u >> 1], (u & 1) ? 0x07060302u : 0x05040100u);
-    *reinterpret_cast<uint32_t*>(vt + (8 * pp + u) * kMVtStride + kpos) = pair;
+    u32x4 v = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
+    if (!F.valid[tt]) v = zero;
+    *reinterpret_cast<u32x4*>(kd + (tt * 16 + r) * kKdStride + 8 * pp) = v;
   }
   if (pp == 0) {
     scl[r] = F.valid[0] ? F.scale[0] : -1.0f;
@@ -191,7 +186,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     }
     qb[ks] = __builtin_bit_cast(bf16x8, v);
   }
-  stage(F, pp, rr, S.kd[0], S.vt[0], S.scl[0], S.bad[0]);
+  stage(F, pp, rr, S.kd[0], S.scl[0], S.bad[0]);
   __syncthreads();
 
   constexpr float kC = kLog2eRsqrtD;
@@ -202,13 +197,21 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
   for (int dt = 0; dt < 8; ++dt) O[dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   const bool active = wave * 16 < a.H;
   const int n_chunks = (Q.total + kMChunk - 1) / kMChunk;
+  // V^T operand rows of this lane for the two transposing reads h: MFMA K index 8g + 4h + u (u = r / 4)
+  // is key 16 ((4h+u) % 2) + 4g + (4h+u) / 2; the lane addresses that key's dims 4 (r % 4) .. +3 of
+  // each 16-dim tile
+  int voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kk = 4 * h + (r >> 2);
+    voff[h] = (16 * (kk & 1) + 4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
+  }
   for (int c = 0; c < n_chunks; ++c) {
     const int cur = c & 1;
     // the next chunk's gathers first (slots past the end read an in-bounds entry and are masked)
     fetch(Q, S.list, (c + 1) * kMChunk, pp, rr, F);
     if (active) {
       const uint16_t* kd = S.kd[cur];
-      const uint16_t* vt = S.vt[cur];
       const float* scl = S.scl[cur];
       float Sv[2][4];
       v4f sc4[2];
@@ -264,12 +267,15 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vt + (dt * 16 + r) * kMVtStride + 8 * g);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kd + voff[0] + dt * 16));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kd + voff[1] + dt * 16));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+        const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0, 0);
       }
     }
     // the next chunk into the other buffer (last read in the previous step, before the barrier below)
-    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.vt[cur ^ 1], S.scl[cur ^ 1], S.bad[cur ^ 1]);
+    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.scl[cur ^ 1], S.bad[cur ^ 1]);
     __syncthreads();
   }
 
