@@ -29,8 +29,12 @@
 //   S^T = K . Q^T   A = 16 keys x 32 dims, straight from the gathered entry
 //                   (lane: key r, dims 8g..8g+7 of the K-step); B = Q^T
 //                   (lane: head r, same dims); out lane: head r, keys 4g+v.
-//   O^T = V^T . P^T A = V^T (lane: dim r of the tile, 8 keys) from a per-wave
-//                   LDS transpose; B = P^T (lane: head r, keys 8g..8g+7).
+//   O^T = V^T . P^T A = V^T (lane: dim r of the tile, 8 keys), read from the
+//                   wave's key-major LDS copy of the chunk by gfx950's
+//                   transposing LDS read (ds_read_b64_tr_b16: lane 4a + e of
+//                   a 16-lane group gets element e of the 8-byte rows lanes a,
+//                   a+4, a+8, a+12 address; each lane addresses the key its K
+//                   index needs); B = P^T (lane: head r, keys 8g..8g+7).
 // Within a 32-key chunk, MFMA K index 8g + 2v + tt is key 4g+v of 16-key tile
 // tt, so each lane's B operand for P^T is exactly the 8 logits it holds. The
 // FP8 codes and BF16 RoPE dims are exact in bf16; the fp32 scale multiplies
@@ -46,14 +50,16 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kChunk = 32;     // keys per wave step: two 16-key tiles
-constexpr int kVtStride = 40;  // bf16 per V^T row (32 keys + 8 pad; 80 B keeps 16-B reads aligned)
+constexpr int kKdStride = 136;  // bf16 per key-major LDS row (128 dims + 8 pad)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kRound = 4;      // chunks a wave gathers at once (VGPR budget)
 
 struct AttendLds {
   union {
     SelectLds sel;  // selection
     struct {
-      uint16_t vt[kWaves][kHeadDim * kVtStride];  // per-wave V^T of its current chunk
+      uint16_t kd[kWaves][kChunk * kKdStride];    // per-wave key-major copy of its current chunk
       float scl[kWaves][2][16];                   // per-wave key scales of the chunk's two tiles
     } b;
     struct {
@@ -119,14 +125,14 @@ struct Keys {
 };
 
 // One 32-key chunk of one wave: S^T = K . Q^T for the two 16-key tiles, the online softmax of head r,
-// V^T into the wave's LDS buffer, O^T += V^T . P^T. Lane (r, g): head r; keys 4g+v of each tile.
+// the keys into the wave's LDS buffer, O^T += V^T . P^T. Lane (r, g): head r; keys 4g+v of each tile.
 // Logits stay unscaled (S = q.x); the 1/sqrt(128) and log2(e) factors go into one multiply before
 // exp2. The running max m is raised only when a chunk's max exceeds it by more than kLazy (log2
 // units), and only then is O rescaled (once per wave, for the heads that moved): the softmax does
 // not depend on the reference point, and P stays below 2^kLazy. Slots at or beyond `end` are empty.
 __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int end, const bf16x8 (&qb)[4], float* scl,
-                                             uint16_t* vt, int kpos, int r, int g, float& m_run, float& l_run,
-                                             v4f (&O)[8]) {
+                                             uint16_t* kd, const int (&voff)[2], int r, int g, float& m_run,
+                                             float& l_run, v4f (&O)[8]) {
   constexpr float kC = kLog2eRsqrtD;
   constexpr float kLazy = 8.0f;
   u32x4 kn0[2], kn1[2];
@@ -176,26 +182,24 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
   rs += xor32(rs);
   l_run += rs;
 
-  // V^T of the chunk into this wave's LDS buffer: per dim, the pair (tile 0, tile 1) of key r
+  // the chunk's keys into this wave's LDS buffer, key-major: lane (r, g) holds dims 32G + 8g .. +7 of key r
+  // of both tiles (LDS operations of one wave complete in order, so the reads below see these writes)
   {
     const u32x4 grp[4][2] = {{kn0[0], kn0[1]}, {kn1[0], kn1[1]}, {cur.r0[0], cur.r0[1]}, {cur.r1[0], cur.r1[1]}};
 #pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      const int dim0 = 32 * G + 8 * g;
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // low (u even) or high (u odd) halves of the two tiles' words: v_perm_b32 byte select
-        const uint32_t pair = __builtin_amdgcn_perm(grp[G][1][u >> 1], grp[G][0][u >> 1],
-                                                    (u & 1) ? 0x07060302u : 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vt + (dim0 + u) * kVtStride + kpos) = pair;
-      }
-    }
+      for (int G = 0; G < 4; ++G)
+        *reinterpret_cast<u32x4*>(kd + (tt * 16 + r) * kKdStride + 32 * G + 8 * g) = grp[G][tt];
   }
   // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P)
   const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const u32x4 va = *reinterpret_cast<const u32x4*>(vt + (dt * 16 + r) * kVtStride + 8 * g);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kd + voff[0] + dt * 16));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kd + voff[1] + dt * 16));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+    const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
     O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0,
                                                      0);
   }
@@ -204,14 +208,14 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
 // NR chunks of one wave: every gather issued first, then the chunks in order (straight-line code).
 template <int NR>
 __device__ __forceinline__ void attend_round(const Keys K, int slot0, int end, const bf16x8 (&qb)[4], float* scl,
-                                             uint16_t* vt, int kpos, int r, int g, float& m_run, float& l_run,
-                                             v4f (&O)[8]) {
+                                             uint16_t* kd, const int (&voff)[2], int r, int g, float& m_run,
+                                             float& l_run, v4f (&O)[8]) {
   Raw buf[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) K.load(slot0 + u * kChunk, end, r, g, buf[u]);
 #pragma unroll
   for (int u = 0; u < NR; ++u)
-    attend_chunk(buf[u], slot0 + u * kChunk, end, qb, scl, vt, kpos, r, g, m_run, l_run, O);
+    attend_chunk(buf[u], slot0 + u * kChunk, end, qb, scl, kd, voff, r, g, m_run, l_run, O);
 }
 
 template <int MODE>
@@ -335,9 +339,17 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   v4f O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-  uint16_t* vt = S.u.b.vt[wave];
+  uint16_t* kd = S.u.b.kd[wave];
   float* scl = &S.u.b.scl[wave][0][0];
-  const int kpos = 8 * (r >> 2) + 2 * (r & 3);  // MFMA K index of key r of tile 0 (tile 1: +1)
+  // V^T operand rows of this lane for the two transposing reads h: MFMA K index 8g + 4h + u (u = r / 4)
+  // is key 16 ((4h+u) % 2) + 4g + (4h+u) / 2; the lane addresses that key's dims 4 (r % 4) .. +3 of
+  // each 16-dim tile
+  int voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kk = 4 * h + (r >> 2);
+    voff[h] = (16 * (kk & 1) + 4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
+  }
 
   // this workgroup: key slots [s_begin, s_end) of its split; wave w: [s_begin + w * per, + per), in rounds
   // of up to kRound chunks
@@ -353,10 +365,10 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   for (int c = 0; c < w_chunks; c += kRound) {
     const int slot0 = w_begin + c * kChunk;
     switch (min(kRound, w_chunks - c)) {
-      case 1: attend_round<1>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
-      case 2: attend_round<2>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
-      case 3: attend_round<3>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
-      default: attend_round<kRound>(K, slot0, w_end, qb, scl, vt, kpos, r, g, m_run, l_run, O); break;
+      case 1: attend_round<1>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
+      case 2: attend_round<2>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
+      case 3: attend_round<3>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
+      default: attend_round<kRound>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
     }
   }
 
