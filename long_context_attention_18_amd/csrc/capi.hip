@@ -390,6 +390,7 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
   ScoreArgs a;
   lca_status st = score_args(cache, qI_dev, w_dev, true, Tq, topk_dev, true, ws_dev, ws_bytes, &a);
   if (st != LCA_OK) return st;
+  a.tile_select = a.tiles;  // query tiles select in the score launch itself
   hipError_t e = launch_index_score(a, cache->batch, (hipStream_t)stream);
   if (e != hipSuccess) return LCA_ERR_LAUNCH;
   return launch_status(launch_topk_select(a, cache->batch, (hipStream_t)stream));

@@ -564,7 +564,9 @@ struct TileLds {
   alignas(16) uint32_t cnt[2][kTileWaves][8];  // pass 2: candidates per (wave, lane slot j + 4 half) of a round
   alignas(16) float wts[kTileQueries][8];      // head weights (0 beyond H_I), read per tile: registers are short
   uint32_t Lkey[kTileQueries];
-  uint32_t ncand[kTileQueries];
+  uint32_t ncand[kTileQueries];                // keys in bins >= L
+  uint32_t countL[kTileQueries];               // keys in bin L
+  uint32_t bcnt[kTileQueries];                 // pass 2: bin-L candidates gathered in LDS so far
   int32_t Nq[kTileQueries];                    // blocks the query scores (0: none)
 };
 
@@ -659,6 +661,138 @@ __device__ __forceinline__ void tile_load(const uint8_t* codes, const uint8_t* s
   ks = scl[(size_t)jc * 2 + half];
 }
 
+// Pass 3 of the combined call, one wave per query (row tq of sequence b, tile slot q): the query's top-k
+// list from its candidates. Every candidate in a bin above L is a winner; of the countL keys in bin L,
+// the `need` = k - (ncand - countL) largest (64-bit key, then lower index) are, found by a radix
+// select over the bin's keys (8-bit digits below the bin's 12 bits, from the LDS copy pass 2 gathered,
+// or, when the bin was too full for it, from the candidates in memory) until the digit's bin is taken
+// whole or holds at most 64 keys, which are ranked directly. The winners then go out in index order
+// (the candidates' order) with ballot prefix counts. The query's 8 KB of histogram words are the
+// wave's scratch: the bin-L copy (kTileBoundCap keys), the segment offsets, the digit bins.
+__device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int b, int tq, int q) {
+  const int lane = threadIdx.x & 63;
+  if (tq >= a.Tq) return;
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  if (t < 0) return;  // ragged: no query in this row
+  const int64_t N = (t + 1) / a.m;
+  const int qg = b * a.Tq + tq;
+  int32_t* out = a.topk + (size_t)qg * a.k;
+  if (N <= a.k) {  // every visible block, then -1
+    for (int i = lane; i < a.k; i += 64) out[i] = (i < N) ? i : -1;
+    return;
+  }
+  uint32_t* wl = &S.hist[q][0];
+  const uint64_t* blist = reinterpret_cast<const uint64_t*>(wl);  // words [0, 2 kTileBoundCap)
+  uint32_t* pref = wl + 2 * kTileBoundCap;                         // G + 1 segment offsets
+  uint32_t* rbin = pref + kTilePrefWords;                          // 256 digit bins (8-byte aligned)
+  uint64_t* small = reinterpret_cast<uint64_t*>(rbin);             // or 64 keys to rank (aliases rbin)
+  const uint64_t* cand = q_cand(a, qg);
+  const int G = (int)((N + kTileSeg - 1) / kTileSeg);
+  // segment offsets (exclusive prefix of the counts pass 2 wrote), in rounds of 64 segments
+  uint32_t total = 0;
+  for (int s0 = 0; s0 < G; s0 += 64) {
+    const uint32_t c = s0 + lane < G ? q_seg(a, qg)[s0 + lane] : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (s0 + lane < G) pref[s0 + lane] = total + incl - c;
+    total += (uint32_t)__shfl((int)incl, 63, 64);
+  }
+  if (lane == 0) pref[G] = total;
+  // candidate e of flat index i (index order): its segment by binary search over the offsets
+  auto flat = [&](uint32_t i) -> uint64_t {
+    int lo = 0, hi = G;  // pref[lo] <= i < pref[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pref[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    return cand[(size_t)lo * kTileSeg + (i - pref[lo])];
+  };
+  const uint32_t Lbin = S.Lkey[q] >> 20;
+  const uint32_t countL = S.countL[q];
+  uint32_t need = (uint32_t)a.k - (S.ncand[q] - countL);  // 1 <= need <= countL
+  const bool in_lds = countL <= (uint32_t)kTileBoundCap;
+  const uint32_t n_src = in_lds ? countL : total;
+  auto src = [&](uint32_t i) -> uint64_t { return in_lds ? blist[i] : flat(i); };
+  // radix select of the need-th largest key of bin L: (e & mask) == prefix selects the current bin
+  uint64_t prefix = (uint64_t)Lbin << 52, mask = 0xFFF0000000000000ull;
+  uint32_t cnt = countL;
+  for (int sh = 44; cnt != need; sh -= 8) {
+    const uint64_t dmask = sh >= 0 ? 0xFFull : (0xFFull >> -sh);  // the last digit: bits 3..0
+    const int shc = sh >= 0 ? sh : 0;
+    if (cnt <= 64) {
+      // at most 64 keys left: gather them and rank directly (keys are unique)
+      small[lane] = 0ull;  // unused slots rank below every key
+      uint32_t ns = 0;
+      for (uint32_t i0 = 0; i0 < n_src; i0 += 64) {
+        const uint32_t i = i0 + lane;
+        const uint64_t e = i < n_src ? src(i) : 0ull;
+        const bool m = i < n_src && (e & mask) == prefix;
+        const uint64_t bm = __ballot(m);
+        if (m) small[ns + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] = e;
+        ns += (uint32_t)__popcll(bm);
+      }
+      const uint64_t mine = small[lane];
+      uint32_t rank = 0;
+#pragma unroll
+      for (int m = 0; m < 64; ++m) rank += small[m] > mine ? 1u : 0u;
+      const uint64_t th = __ballot(lane < (int)cnt && rank == need - 1);
+      prefix = (uint64_t)__shfl((long long)mine, (int)__builtin_ctzll(th), 64);
+      mask = ~0ull;
+      break;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rbin[lane + 64 * u] = 0u;
+    for (uint32_t i = lane; i < n_src; i += 64) {
+      const uint64_t e = src(i);
+      if ((e & mask) == prefix) atomicAdd(&rbin[(uint32_t)((e >> shc) & dmask)], 1u);
+    }
+    // digit whose count from the top reaches need: lane l holds bins 255-4l .. 252-4l
+    uint32_t h4[4], c4 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      h4[u] = rbin[255 - 4 * lane - u];
+      c4 += h4[u];
+    }
+    const uint32_t incl = wave_incl_scan(c4);
+    const uint32_t excl = incl - c4;
+    uint32_t dsel = 0, above = 0, cd = 0;
+    if (excl < need && incl >= need) {
+      uint32_t run = excl;
+      for (int u = 0; u < 4; ++u) {
+        if (run + h4[u] >= need) {
+          dsel = 255u - 4u * lane - u;
+          above = run;
+          cd = h4[u];
+          break;
+        }
+        run += h4[u];
+      }
+    }
+    const uint64_t owner = __ballot(excl < need && incl >= need);
+    const int ol = (int)__builtin_ctzll(owner);
+    dsel = (uint32_t)__shfl((int)dsel, ol, 64);
+    above = (uint32_t)__shfl((int)above, ol, 64);
+    cd = (uint32_t)__shfl((int)cd, ol, 64);
+    need -= above;
+    prefix |= (uint64_t)dsel << shc;
+    mask |= dmask << shc;
+    cnt = cd;
+  }
+  // winners: (e & mask) >= prefix (every key of a higher bin or digit, and the bin's chosen ones), out in
+  // index order
+  uint32_t pos = 0;
+  for (uint32_t i0 = 0; i0 < total; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    const uint64_t e = i < total ? flat(i) : 0ull;
+    const bool w = i < total && (e & mask) >= prefix;
+    const uint64_t bm = __ballot(w);
+    const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+    if (w && p < (uint32_t)a.k) out[p] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
+    pos += (uint32_t)__popcll(bm);
+  }
+  for (uint32_t i = pos + lane; i < (uint32_t)a.k; i += 64) out[i] = -1;  // only if fewer than k were found
+}
+
 __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
   __shared__ TileLds S;
   constexpr int kThreads = kTileWaves * 64;
@@ -697,7 +831,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
     Nmax = max(Nmax, (int)S.Nq[q]);
     if (S.Nq[q] > 0) Nmin = min(Nmin, (int)S.Nq[q]);
   }
-  if (Nmax == 0) return;  // no query of the tile scores anything
+  if (Nmax == 0) {  // no query of the tile scores anything; the combined call still wants their lists
+    if (a.topk && a.tile_select) tile_select(a, S, b, tq0 + wave, wave);
+    return;
+  }
 
   TileQuery Q;
 #pragma unroll
@@ -775,15 +912,18 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
         run += v >> 16;
         if (run >= kk) {
           S.Lkey[wave] = (uint32_t)(2 * (top - i) + 1) << 20;
+          S.countL[wave] = v >> 16;
           break;
         }
         run += v & 0xFFFFu;
         if (run >= kk) {
           S.Lkey[wave] = (uint32_t)(2 * (top - i)) << 20;
+          S.countL[wave] = v & 0xFFFFu;
           break;
         }
       }
       S.ncand[wave] = run;
+      S.bcnt[wave] = 0u;
     }
   }
   __syncthreads();
@@ -802,6 +942,17 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
     // key of a finite score reaches 0xFFFFFFFF
     Lk[j] = sel[j] ? max(S.Lkey[q], 1u) : 0xFFFFFFFFu;
     ovf[j] = Q.N[j] > 0 && (a.write_keys || (sel[j] && S.ncand[q] > (uint32_t)kCandCap));
+  }
+  // the combined call selects here (pass 3): the keys of bin L, if they fit, are also gathered into
+  // the query's LDS scratch (its histogram's words, free once the thresholds are known)
+  const bool sel_here = a.topk != nullptr && a.tile_select != 0;
+  bool blst[4];
+  uint32_t Lb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tile_slot_query(j, half);
+    blst[j] = sel_here && sel[j] && S.countL[q] <= (uint32_t)kTileBoundCap;
+    Lb[j] = S.Lkey[q] >> 20;
   }
   constexpr int kSegTiles = kTileSeg / 32;
   static_assert(kTileSeg % 32 == 0, "a candidate segment is whole tiles");
@@ -830,9 +981,14 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
         // candidates of this half before this lane, and in this half
         const uint32_t nlo = (uint32_t)__popc(lo);
         const uint32_t pre = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (half ? nlo : 0u);
-        if (c)
-          q_cand(a, qrow(j))[(size_t)sg * kTileSeg + run[j] + pre] =
-              ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)jb);
+        if (c) {
+          const uint64_t e = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)jb);
+          q_cand(a, qrow(j))[(size_t)sg * kTileSeg + run[j] + pre] = e;
+          if (blst[j] && (key[j] >> 20) == Lb[j]) {
+            const int q = tile_slot_query(j, half);
+            reinterpret_cast<uint64_t*>(&S.hist[q][0])[atomicAdd(&S.bcnt[q], 1u)] = e;
+          }
+        }
         run[j] += half ? (uint32_t)__popc(hi) : nlo;
         if (ovf[j] && jb < Q.N[j]) q_keys(a, qrow(j))[jb] = key[j];
       }
@@ -842,6 +998,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
       for (int j = 0; j < 4; ++j)
         if (sel[j]) q_seg(a, qrow(j))[sg] = run[j];
     }
+  }
+  if (sel_here) {
+    __syncthreads();  // every wave's candidates, segment counts and bin-L lists are written
+    tile_select(a, S, b, tq0 + wave, wave);
   }
 }
 
@@ -1003,9 +1163,10 @@ hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool
   ScanArgs args{};
   args.a = a;
   if (a.tiles) {
-    // the score launch wrote the candidates; a decode step's append never comes with query tiles
+    // the score launch wrote the candidates (and, for the combined call, the lists); a decode step's
+    // append never comes with query tiles
     if (app && app_units > 0) return hipErrorInvalidValue;
-    if (with_select) hipLaunchKernelGGL(select_kernel, dim3(nq), dim3(512), 0, s, a);
+    if (with_select && !a.tile_select) hipLaunchKernelGGL(select_kernel, dim3(nq), dim3(512), 0, s, a);
     return hipGetLastError();
   }
   if (app && app_units > 0) {

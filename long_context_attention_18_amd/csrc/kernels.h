@@ -26,7 +26,13 @@ constexpr int kTileQueries = 8;
 constexpr int kTileWaves = 8;
 constexpr int64_t kTileMaxBlocks = 65535;
 constexpr int kTileSeg = 256;  // blocks per candidate segment of the query tiles (one wave writes a segment)
+constexpr int kTileBoundCap = 760;  // keys of a query's threshold bin the query tiles' selection holds in LDS
+constexpr int kTilePrefWords = 258;  // segment offsets (at most 257), even so the digit bins stay 8-byte aligned
+static_assert(kTileQueries == kTileWaves, "the tiles' selection runs one wave per query");
+static_assert((kTileMaxBlocks + kTileSeg - 1) / kTileSeg + 1 <= kTilePrefWords, "segment offsets fit");
 constexpr int kHistBins = 4096;                       // top 12 bits of the ordered score key
+static_assert(2 * kTileBoundCap + kTilePrefWords + 256 <= kHistBins / 2,
+              "a query's selection scratch fits its histogram words");
 constexpr int kScanPerWG = 8192;                      // keys per candidate-scan workgroup
 constexpr int kCandCap = 8192;                        // candidates the select kernel holds in LDS
 constexpr int64_t kMaxBlocks = 2048LL * kScoreChunk;  // compressed blocks per sequence the indexer serves
@@ -94,6 +100,7 @@ struct ScoreArgs {
   int32_t chunk_step;      // 0: a score workgroup per 2048-block chunk; else one per chunk_step chunks of a query
   int32_t tiles;           // 1: query tiles (the score launch also writes the candidates; no scan)
   int32_t write_keys;      // tiles: also write every visible block's key (the separate score call's contract)
+  int32_t tile_select;     // tiles: the score launch also selects the top-k lists into topk (combined call)
   // ragged batches (see IngestArgs): the queries of sequence b are its seq_T[b] new tokens, positions
   // seq_len[b] + i for rows i < seq_T[b]; null: positions len - Tq + i
   const int64_t* seq_len;
