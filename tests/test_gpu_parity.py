@@ -133,6 +133,23 @@ def test_csa_prefill_query_tiles():
         print("query tiles", B, Tq, pre, w)
 
 
+def test_csa_query_tiles_small_heads_and_fused_attention():
+    """Query tiles with H_I = 4 (heads 4-7 of the MFMA rows empty), k = 100 and a context whose block
+    count is not a multiple of 32, through the combined indexer call (selection in the tile kernel) and
+    through lca_csa_attend (tiles write candidates, the attention launch selects): both against the
+    oracle on sampled queries and against the separate score + select calls."""
+    layer = configs.Layer("csa", 4, n_heads=8, window=64, idx_heads=4, topk=100)
+    Tq, pre = 2050, 5003
+    for fused in (False, True):
+        run = LayerRun(layer, B=1, max_ctx=pre + Tq, ring=Tq + 63, max_tq=Tq, sigma=1.0, hidden=1024)
+        _ingest(run, [pre, Tq])
+        qin, topk, out, lse = run.run_queries(Tq, fused=fused)
+        oc = [run.oracle_caches(0, pre + Tq)]
+        pos = list(range(run.len - Tq, run.len))
+        w = check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 89)) + [Tq - 1])
+        assert w["scores_checked"] > 0
+
+
 def test_csa_query_tiles_all_weights_negative():
     """Query tiles with every indexer weight negative: most scores are 0, so the bin that holds the k-th
     key holds more candidates than the selection's LDS, and the tile kernel writes every key for the
