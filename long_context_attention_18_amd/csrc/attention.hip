@@ -39,7 +39,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 struct ManyLds {
   uint16_t kd[2][kMChunk * kKdStride];    // key-major chunk (two buffers)
   float scl[2][kMChunk];                  // the keys' FP8 scales (>= 0); -1 marks a slot without a key
-  uint32_t bad[2][kMWaves];               // per buffer and staging wave: some slot of the chunk holds no key
+  uint32_t kbad[2];                       // per chunk buffer: some slot of the chunk holds no key
+  uint32_t ent[2][kMChunk];               // entries of the slots of the chunk after next (~0: no key)
+  uint32_t ebad[2];                       // per entry buffer: some slot holds no key
   int32_t list[kMaxTopk];                 // CSA: the query's top-k row
   float cos_t[32], sin_t[32];
 };
@@ -51,6 +53,7 @@ struct Fetch {
   u32x4 rope[2];
   float scale[2];
   bool valid[2];
+  bool bad;  // some slot of the chunk holds no key (the same for every thread)
 };
 
 struct Query {
@@ -80,12 +83,31 @@ __device__ __forceinline__ void slot_entry(const Query& Q, const int32_t* list, 
   *e = in_first ? Q.blk_row + (uint32_t)(ok_blk ? j : 0) : Q.win_row + (uint32_t)(live ? ws : 0);
 }
 
-__device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int chunk0, int pp, int r, Fetch& F) {
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+// The entries of one chunk's 32 slots, once per chunk (lanes 0-31 of wave 0), for the threads that
+// gather them: ent[slot] = the entry index in its array (window or compressed: slot >= n_first), ~0
+// for a slot without a key; *ebad: whether any slot holds none.
+__device__ __forceinline__ void make_entries(const Query& Q, const int32_t* list, int chunk0, uint32_t* ent,
+                                             uint32_t* ebad) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < kMChunk) {
     size_t e;
     bool w, ok;
-    slot_entry(Q, list, chunk0 + tt * 16 + r, &e, &w, &ok);
+    slot_entry(Q, list, chunk0 + lane, &e, &w, &ok);
+    ent[lane] = ok ? (uint32_t)e : 0xFFFFFFFFu;  // entry indices stay below 2^32 (B x rows x 196 B of HBM)
+    const uint64_t m = __ballot(!ok);
+    if (lane == 0) *ebad = m != 0 ? 1u : 0u;
+  }
+}
+
+__device__ __forceinline__ void fetch(const Query& Q, const uint32_t* ent, const uint32_t* ebad, int chunk0, int pp,
+                                      int r, Fetch& F) {
+  F.bad = *ebad != 0u;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint32_t code = ent[tt * 16 + r];
+    const bool ok = code != 0xFFFFFFFFu;
+    const bool w = chunk0 + tt * 16 + r >= Q.n_first;
+    const size_t e = ok ? (size_t)code : (w ? Q.win_row : Q.blk_row);  // a slot without a key: an in-bounds entry
     F.valid[tt] = ok;
     if (pp < 8) {
       F.code[tt] = ldg<u32x2>((w ? Q.win_codes : Q.blk_codes) + e * kNope + 8 * pp);
@@ -96,22 +118,21 @@ __device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int c
   }
 }
 
-// the fetched dims into the chunk buffer's key-major rows; bad[wave]: whether some key of this wave's
-// share is missing (the chunk then needs the masked path)
-__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, float* scl, uint32_t* bad) {
+// the fetched dims into the chunk buffer's key-major rows (a slot without a key as zeros); *kbad: whether
+// the chunk needs the masked path
+__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, float* scl, uint32_t* kbad) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 v = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
-    if (!F.valid[tt]) v = zero;
+    if (F.bad && !F.valid[tt]) v = zero;
     *reinterpret_cast<u32x4*>(kd + (tt * 16 + r) * kKdStride + 8 * pp) = v;
   }
   if (pp == 0) {
     scl[r] = F.valid[0] ? F.scale[0] : -1.0f;
     scl[16 + r] = F.valid[1] ? F.scale[1] : -1.0f;
   }
-  const uint64_t m = __ballot(!F.valid[0] || !F.valid[1]);
-  if ((threadIdx.x & 63) == 0) bad[threadIdx.x >> 6] = m != 0 ? 1u : 0u;
+  if (threadIdx.x == 0) *kbad = F.bad ? 1u : 0u;
 }
 
 __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
@@ -163,11 +184,14 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     }
   }
   __syncthreads();  // angles and the top-k row in LDS
+  make_entries(Q, S.list, 0, S.ent[0], &S.ebad[0]);
+  make_entries(Q, S.list, kMChunk, S.ent[1], &S.ebad[1]);
+  __syncthreads();
 
-  // chunk 0 into buffer 0 (the gathers need the top-k row)
+  // chunk 0 into buffer 0
   const int pp = tid >> 4, rr = tid & 15;
   Fetch F;
-  fetch(Q, S.list, 0, pp, rr, F);
+  fetch(Q, S.ent[0], &S.ebad[0], 0, pp, rr, F);
 
   // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3)
   bf16x8 qb[4];
@@ -186,7 +210,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     }
     qb[ks] = __builtin_bit_cast(bf16x8, v);
   }
-  stage(F, pp, rr, S.kd[0], S.scl[0], S.bad[0]);
+  stage(F, pp, rr, S.kd[0], S.scl[0], &S.kbad[0]);
   __syncthreads();
 
   constexpr float kC = kLog2eRsqrtD;
@@ -208,8 +232,10 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
   }
   for (int c = 0; c < n_chunks; ++c) {
     const int cur = c & 1;
-    // the next chunk's gathers first (slots past the end read an in-bounds entry and are masked)
-    fetch(Q, S.list, (c + 1) * kMChunk, pp, rr, F);
+    // the next chunk's gathers first (slots past the end read an in-bounds entry and are masked), then
+    // the entries of the chunk after it into the entry buffer the fetch of this chunk read
+    fetch(Q, S.ent[(c + 1) & 1], &S.ebad[(c + 1) & 1], (c + 1) * kMChunk, pp, rr, F);
+    make_entries(Q, S.list, (c + 2) * kMChunk, S.ent[cur], &S.ebad[cur]);
     if (active) {
       const uint16_t* kd = S.kd[cur];
       const float* scl = S.scl[cur];
@@ -227,7 +253,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) Sv[tt][v] = fmaf(an[v], sc4[tt][v], ar[v]);
       }
-      if (S.bad[cur][0] | S.bad[cur][1] | S.bad[cur][2] | S.bad[cur][3]) {
+      if (S.kbad[cur]) {
         // a slot without a key (scale -1, all-zero dims) is masked; an entry whose nope part is all
         // zero has scale 0 and is a key like any other
 #pragma unroll
@@ -275,7 +301,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       }
     }
     // the next chunk into the other buffer (last read in the previous step, before the barrier below)
-    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.scl[cur ^ 1], S.bad[cur ^ 1]);
+    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.scl[cur ^ 1], &S.kbad[cur ^ 1]);
     __syncthreads();
   }
 
