@@ -32,12 +32,18 @@ namespace {
 constexpr int kMWaves = 4;       // one wave per 16-head group
 constexpr int kMThreads = kMWaves * 64;
 constexpr int kMChunk = 32;      // keys per step: two 16-key tiles
-constexpr int kKdStride = 136;   // bf16 per key-major row (128 + 8 pad)
+// Key-major chunk layout (bf16 offsets): row r of 16-key tile tt at tt * kKdTile + r * kKdStride. In
+// 4-byte LDS banks the row stride is 12 (mod 64) and tile 1 starts 32 banks after tile 0, so the 16 rows
+// a QK operand read touches (4 banks each) and the four 8-bank row pieces a transposing read gathers per
+// 16-lane group (keys 4g, 4g+1 of both tiles) all fall on distinct banks.
+constexpr int kKdStride = 152;                 // 76 banks per row: 128 bf16 + 24 pad
+constexpr int kKdTile = 16 * kKdStride + 64;   // tile 1 offset: 1248 banks, 32 (mod 64)
+constexpr int kKdBuf = kKdTile + 16 * kKdStride;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct ManyLds {
-  uint16_t kd[2][kMChunk * kKdStride];    // key-major chunk (two buffers)
+  uint16_t kd[2][kKdBuf];                 // key-major chunk (two buffers)
   float scl[2][kMChunk];                  // the keys' FP8 scales (>= 0); -1 marks a slot without a key
   uint32_t kbad[2];                       // per chunk buffer: some slot of the chunk holds no key
   uint32_t ent[2][kMChunk];               // entries of the slots of the chunk after next (~0: no key)
@@ -126,7 +132,7 @@ __device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* k
     const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 v = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
     if (F.bad && !F.valid[tt]) v = zero;
-    *reinterpret_cast<u32x4*>(kd + (tt * 16 + r) * kKdStride + 8 * pp) = v;
+    *reinterpret_cast<u32x4*>(kd + tt * kKdTile + r * kKdStride + 8 * pp) = v;
   }
   if (pp == 0) {
     scl[r] = F.valid[0] ? F.scale[0] : -1.0f;
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int kk = 4 * h + (r >> 2);
-    voff[h] = (16 * (kk & 1) + 4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
+    voff[h] = (kk & 1) * kKdTile + (4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
   }
   for (int c = 0; c < n_chunks; ++c) {
     const int cur = c & 1;
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       v4f sc4[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const uint16_t* krow = kd + (tt * 16 + r) * kKdStride + 8 * g;
+        const uint16_t* krow = kd + tt * kKdTile + r * kKdStride + 8 * g;
         v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
         an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow)), qb[0], an, 0, 0, 0);
         an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 32)), qb[1], an, 0, 0, 0);
