@@ -154,10 +154,9 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
     for (int v = 0; v < 4; ++v) Sv[tt][v] = (slot0 + v < end) ? an[v] * sc4[tt][v] + ar[v] : -INFINITY;
   }
   // online softmax of head r (its keys are spread over the 4 lane groups)
-  float mx = fmaxf(fmaxf(fmaxf(Sv[0][0], Sv[0][1]), fmaxf(Sv[0][2], Sv[0][3])),
-                   fmaxf(fmaxf(Sv[1][0], Sv[1][1]), fmaxf(Sv[1][2], Sv[1][3])));
-  mx = fmaxf(mx, xor16(mx));
-  mx = fmaxf(mx, xor32(mx));
+  float mx = max3_raw(max3_raw(Sv[0][0], Sv[0][1], Sv[0][2]), max3_raw(Sv[0][3], Sv[1][0], Sv[1][1]),
+                      max_raw(Sv[1][2], Sv[1][3]));
+  mx = pair_max32(pair_max16(mx));
   const bool raise = mx * kC > m_run * kC + kLazy;  // also true for the first finite max (m_run = -inf)
   if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
     const float m_new = raise ? mx : m_run;
@@ -174,12 +173,11 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
   for (int v = 0; v < 4; ++v) {
     const float p0 = __builtin_amdgcn_exp2f((Sv[0][v] - m_use) * kC);
     const float p1 = __builtin_amdgcn_exp2f((Sv[1][v] - m_use) * kC);
-    rs += p0 + p1;
+    rs = v == 0 ? p0 + p1 : rs + (p0 + p1);  // the first pair starts the sum (no add of +0)
     pr[v] = pack_bf16(p0, p1);
     pn[v] = pack_bf16(p0 * sc4[0][v], p1 * sc4[1][v]);
   }
-  rs += xor16(rs);
-  rs += xor32(rs);
+  rs = pair_sum32(pair_sum16(rs));
   l_run += rs;
 
   // the chunk's keys into this wave's LDS buffer, key-major: lane (r, g) holds dims 32G + 8g .. +7 of key r

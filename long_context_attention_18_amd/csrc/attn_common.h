@@ -31,6 +31,38 @@ __device__ __forceinline__ float xor32(float x) {
   return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
 }
 
+// Float max without the NaN-quieting max the compiler puts before a max of values it cannot prove
+// canonical (MFMA and lane-swap results): the logits here are never NaN.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// max / sum of x over lanes l and l ^ 16 (l ^ 32): a lane swap leaves the pair in its two outputs, so a
+// symmetric operation needs no lane select
+__device__ __forceinline__ float pair_max16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 8 E4M3FN codes (little-endian bytes) -> 8 bf16: v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts
 // two codes exactly (every E4M3FN value is a bf16 value; checked for all 256 codes on MI355X)
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 c) {
