@@ -31,14 +31,16 @@ namespace {
 
 constexpr int kMWaves = 4;       // one wave per 16-head group
 constexpr int kMThreads = kMWaves * 64;
-constexpr int kMChunk = 32;      // keys per step: two 16-key tiles
+constexpr int kMChunk = 32;      // keys per step: 16-key tiles, pairs of them one PV K-step
+constexpr int kMTiles = kMChunk / 16;
+static_assert(kMChunk % 32 == 0 && kMChunk <= 64, "whole PV K-steps; make_entries uses one wave");
 // Key-major chunk layout (bf16 offsets): row r of 16-key tile tt at tt * kKdTile + r * kKdStride. In
 // 4-byte LDS banks the row stride is 12 (mod 64) and tile 1 starts 32 banks after tile 0, so the 16 rows
 // a QK operand read touches (4 banks each) and the four 8-bank row pieces a transposing read gathers per
 // 16-lane group (keys 4g, 4g+1 of both tiles) all fall on distinct banks.
 constexpr int kKdStride = 152;                 // 76 banks per row: 128 bf16 + 24 pad
 constexpr int kKdTile = 16 * kKdStride + 64;   // tile 1 offset: 1248 banks, 32 (mod 64)
-constexpr int kKdBuf = kKdTile + 16 * kKdStride;
+constexpr int kKdBuf = (kMTiles - 1) * kKdTile + 16 * kKdStride;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -55,10 +57,10 @@ struct ManyLds {
 // The gather of one thread for one chunk: part pp = tid / 16 (dims 8pp .. 8pp+7; pp < 8 the FP8 nope
 // codes, pp >= 8 the BF16 RoPE dims), key r = tid % 16 of both tiles.
 struct Fetch {
-  u32x2 code[2];
-  u32x4 rope[2];
-  float scale[2];
-  bool valid[2];
+  u32x2 code[kMTiles];
+  u32x4 rope[kMTiles];
+  float scale[kMTiles];
+  bool valid[kMTiles];
   bool bad;  // some slot of the chunk holds no key (the same for every thread)
 };
 
@@ -89,7 +91,7 @@ __device__ __forceinline__ void slot_entry(const Query& Q, const int32_t* list, 
   *e = in_first ? Q.blk_row + (uint32_t)(ok_blk ? j : 0) : Q.win_row + (uint32_t)(live ? ws : 0);
 }
 
-// The entries of one chunk's 32 slots, once per chunk (lanes 0-31 of wave 0), for the threads that
+// The entries of one chunk's slots, once per chunk (the first kMChunk lanes of wave 0), for the threads that
 // gather them: ent[slot] = the entry index in its array (window or compressed: slot >= n_first), ~0
 // for a slot without a key; *ebad: whether any slot holds none.
 __device__ __forceinline__ void make_entries(const Query& Q, const int32_t* list, int chunk0, uint32_t* ent,
@@ -109,7 +111,7 @@ __device__ __forceinline__ void fetch(const Query& Q, const uint32_t* ent, const
                                       int r, Fetch& F) {
   F.bad = *ebad != 0u;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < kMTiles; ++tt) {
     const uint32_t code = ent[tt * 16 + r];
     const bool ok = code != 0xFFFFFFFFu;
     const bool w = chunk0 + tt * 16 + r >= Q.n_first;
@@ -128,15 +130,15 @@ __device__ __forceinline__ void fetch(const Query& Q, const uint32_t* ent, const
 // the chunk needs the masked path
 __device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, float* scl, uint32_t* kbad) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < kMTiles; ++tt) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 v = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
     if (F.bad && !F.valid[tt]) v = zero;
     *reinterpret_cast<u32x4*>(kd + tt * kKdTile + r * kKdStride + 8 * pp) = v;
   }
   if (pp == 0) {
-    scl[r] = F.valid[0] ? F.scale[0] : -1.0f;
-    scl[16 + r] = F.valid[1] ? F.scale[1] : -1.0f;
+#pragma unroll
+    for (int tt = 0; tt < kMTiles; ++tt) scl[16 * tt + r] = F.valid[tt] ? F.scale[tt] : -1.0f;
   }
   if (threadIdx.x == 0) *kbad = F.bad ? 1u : 0u;
 }
@@ -245,10 +247,10 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     if (active) {
       const uint16_t* kd = S.kd[cur];
       const float* scl = S.scl[cur];
-      float Sv[2][4];
-      v4f sc4[2];
+      float Sv[kMTiles][4];
+      v4f sc4[kMTiles];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < kMTiles; ++tt) {
         const uint16_t* krow = kd + tt * kKdTile + r * kKdStride + 8 * g;
         v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
         an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow)), qb[0], an, 0, 0, 0);
@@ -263,13 +265,17 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
         // a slot without a key (scale -1, all-zero dims) is masked; an entry whose nope part is all
         // zero has scale 0 and is a key like any other
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < kMTiles; ++tt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) Sv[tt][v] = sc4[tt][v] >= 0.0f ? Sv[tt][v] : -INFINITY;
       }
       // online softmax of head r (its 32 keys are spread over the 4 lane groups)
       float mx = max3_raw(max3_raw(Sv[0][0], Sv[0][1], Sv[0][2]), max3_raw(Sv[0][3], Sv[1][0], Sv[1][1]),
                           max_raw(Sv[1][2], Sv[1][3]));
+#pragma unroll
+      for (int tt = 2; tt < kMTiles; tt += 2)
+        mx = max3_raw(mx, max3_raw(Sv[tt][0], Sv[tt][1], Sv[tt][2]), max3_raw(Sv[tt][3], Sv[tt + 1][0],
+                      max3_raw(Sv[tt + 1][1], Sv[tt + 1][2], Sv[tt + 1][3])));
       mx = pair_max32(pair_max16(mx));
       const bool raise = mx * kC > m_run * kC + kLazy;  // also true for the first finite max (m_run = -inf)
       if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
@@ -282,27 +288,32 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       }
       const float mk = (m_run == -INFINITY) ? 0.0f : m_run * kC;  // exp2 argument S kC - m kC, one fma
       float rs = 0.0f;
-      u32x4 pr, pn;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(Sv[0][v], kC, -mk));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(Sv[1][v], kC, -mk));
-        rs = v == 0 ? p0 + p1 : rs + (p0 + p1);  // the first pair starts the sum (no add of +0)
-        pr[v] = pack_bf16(p0, p1);
-        pn[v] = pack_bf16(p0 * sc4[0][v], p1 * sc4[1][v]);
+      for (int ksp = 0; ksp < kMTiles / 2; ++ksp) {
+        // P of tiles 2 ksp, 2 ksp + 1: the B operand of one PV K-step
+        u32x4 pr, pn;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(Sv[2 * ksp][v], kC, -mk));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(Sv[2 * ksp + 1][v], kC, -mk));
+          rs = (ksp == 0 && v == 0) ? p0 + p1 : rs + (p0 + p1);  // the first pair starts the sum (no add of +0)
+          pr[v] = pack_bf16(p0, p1);
+          pn[v] = pack_bf16(p0 * sc4[2 * ksp][v], p1 * sc4[2 * ksp + 1][v]);
+        }
+        // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P)
+        const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
+        const uint16_t* kv = kd + 2 * ksp * kKdTile;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kv + voff[0] + dt * 16));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kv + voff[1] + dt * 16));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+          const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0, 0);
+        }
       }
       rs = pair_sum32(pair_sum16(rs));
       l_run += rs;
-      // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P)
-      const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kd + voff[0] + dt * 16));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kd + voff[1] + dt * 16));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-        const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0, 0);
-      }
     }
     // the next chunk into the other buffer (last read in the previous step, before the barrier below)
     if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.scl[cur ^ 1], &S.kbad[cur ^ 1]);
