@@ -47,6 +47,12 @@
 // too many), radix-selects the k-th largest 64-bit key (score_key << 32 |
 // ~j) and writes the winners by an order-preserving compaction, so the
 // output is ascending without a sort. Exact for any input.
+//
+// Calls with many queries (chunked prefill) take other shapes of kernel 1:
+// 512+ queries, a workgroup per 8 chunks of a query (one set-up, one
+// histogram); 2048+ queries that see at most kTileMaxBlocks blocks, query
+// tiles (tile_kernel: 8 queries per workgroup on the 32x32x64 MFMA), which
+// also do kernel 2's work, and kernel 3's for the combined call.
 #include "dev_formats.h"
 #include "ingest.h"
 #include "kernels.h"
