@@ -22,6 +22,72 @@ namespace lca {
 
 namespace {
 
+// Blocks of at most kPoolCache tokens (CSA: 4): every input of the block is loaded once, up front, and
+// each position's exp is computed once and kept for the weights -- the same operations in the same
+// order as the three passes below, so the same bits; the loads and the exps no longer sit in the
+// passes' dependency chains.
+constexpr int kPoolCache = 4;
+
+template <bool CSA>
+__device__ __forceinline__ void pool_cached(const IngestArgs& a, int b, int64_t len, int64_t j, int c, double& y_n,
+                                            double& y_r, double& y_i) {
+  const int m = a.m;
+  const int64_t p0 = j * m;
+  double xn[kPoolCache], xr[kPoolCache], xi[kPoolCache], vn[kPoolCache], vr[kPoolCache], vi[kPoolCache];
+#pragma unroll
+  for (int i = 0; i < kPoolCache; ++i) {
+    if (i < m) {
+      const int64_t p = p0 + i;
+      const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
+      const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
+      xn[i] = (double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c];
+      xr[i] = (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c];
+      vn[i] = (double)bf16_to_f32(kv[c]);
+      vr[i] = rope_channel(kv, c, p, a.inv_freq);
+      if (CSA) {
+        const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
+        const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
+        xi[i] = (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c];
+        vi[i] = (double)bf16_to_f32(ki[c]);
+      }
+    }
+  }
+  double mu_n = -INFINITY, mu_r = -INFINITY, mu_i = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPoolCache; ++i) {
+    if (i < m) {
+      mu_n = fmax(mu_n, xn[i]);
+      mu_r = fmax(mu_r, xr[i]);
+      if (CSA) mu_i = fmax(mu_i, xi[i]);
+    }
+  }
+  double S_n = 0.0, S_r = 0.0, S_i = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPoolCache; ++i) {
+    if (i < m) {
+      xn[i] = pool_exp(xn[i] - mu_n);  // from here on the position's exp
+      xr[i] = pool_exp(xr[i] - mu_r);
+      S_n = S_n + xn[i];
+      S_r = S_r + xr[i];
+      if (CSA) {
+        xi[i] = pool_exp(xi[i] - mu_i);
+        S_i = S_i + xi[i];
+      }
+    }
+  }
+  y_n = 0.0;
+  y_r = 0.0;
+  y_i = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPoolCache; ++i) {
+    if (i < m) {
+      y_n = fma(xn[i] / S_n, vn[i], y_n);
+      y_r = fma(xr[i] / S_r, vr[i], y_r);
+      if (CSA) y_i = fma(xi[i] / S_i, vi[i], y_i);
+    }
+  }
+}
+
 template <bool CSA>
 __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
   const int c = threadIdx.x;
@@ -32,6 +98,10 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
   // ragged batch: the blocks this sequence's own tokens complete (the grid covers the most of any)
   if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;
   const int64_t p0 = j * m;
+  double y_n = 0.0, y_r = 0.0, y_i = 0.0;
+  if (m <= kPoolCache) {
+    pool_cached<CSA>(a, b, len, j, c, y_n, y_r, y_i);
+  } else {
 
   // pass 1: per-channel max of gate + bias over the block's m positions
   double mu_n = -INFINITY, mu_r = -INFINITY, mu_i = -INFINITY;
@@ -58,7 +128,6 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
     }
   }
   // pass 3: weighted sum, one fma per position in ascending order
-  double y_n = 0.0, y_r = 0.0, y_i = 0.0;
   for (int i = 0; i < m; ++i) {
     const int64_t p = p0 + i;
     const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
@@ -73,6 +142,7 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
       double w_i = pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i) / S_i;
       y_i = fma(w_i, (double)bf16_to_f32(ki[c]), y_i);
     }
+  }
   }
 
   const size_t e = (size_t)b * a.max_blocks + (size_t)j;
