@@ -20,17 +20,38 @@ __device__ __forceinline__ const uint16_t* token_row(const IngestArgs& a, int b,
   return in + ((size_t)b * a.T + (size_t)(p - len)) * width;
 }
 
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
+// Max of v over lane groups, with VALU lane moves instead of LDS-crossbar shuffles: DPP quad permutes
+// (lane ^ 1, lane ^ 2) and row rotations (by 4, 8) give every lane its 16-lane row's max, and a
+// v_permlane16_swap (rows 0 <-> 1, 2 <-> 3) or v_permlane32_swap (lane halves) pairs the rows. A
+// double moves as its two 32-bit words; max is exact, so the grouping does not change the result.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double row_max(double v) {
+  v = fmax(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = fmax(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = fmax(v, dpp_move<0x124>(v));  // row_ror:4
+  return fmax(v, dpp_move<0x128>(v));  // row_ror:8
+}
+__device__ __forceinline__ double swap_max16(double v) {
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+  return fmax(__hiloint2double((int)hi[0], (int)lo[0]), __hiloint2double((int)hi[1], (int)lo[1]));
+}
+__device__ __forceinline__ double swap_max32(double v) {
+  auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+  auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+  return fmax(__hiloint2double((int)hi[0], (int)lo[0]), __hiloint2double((int)hi[1], (int)lo[1]));
 }
 
-__device__ __forceinline__ double half_wave_max(double v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
-}
+// max over the 64 lanes (every lane gets it)
+__device__ __forceinline__ double wave_max(double v) { return swap_max32(swap_max16(row_max(v))); }
+
+// max over lanes 0-31 and, separately, 32-63
+__device__ __forceinline__ double half_wave_max(double v) { return swap_max16(row_max(v)); }
 
 // RoPE-rotated value of channel 64+c of token p (pair (2i, 2i+1), i = c/2):
 //   even: x0 cos - x1 sin;  odd: x0 sin + x1 cos;  angle p * inv_freq[i]; fp64.

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
     double amax = half_wave_max(fabs(y_i));
     int E = (amax == 0.0) ? -127 : mx_block_exp(amax);
     uint32_t code = (amax == 0.0) ? 0u : fp4_e2m1_encode(ldexp(y_i, -E));
-    uint32_t hi = __shfl_down(code, 1, 64);
+    // the next lane's code (row_shl:1; the pairs (2i, 2i+1) never cross a 16-lane row)
+    uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code, 0x101, 0xf, 0xf, false);
     if ((c & 1) == 0) a.idx_codes[e * 32 + (c >> 1)] = (uint8_t)(code | (hi << 4));
     if ((c & 31) == 0) a.idx_scale[e * 2 + (c >> 5)] = (uint8_t)((amax == 0.0) ? 0 : E + 127);
   }
