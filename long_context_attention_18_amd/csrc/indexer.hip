@@ -722,7 +722,8 @@ __device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int 
   // radix select of the need-th largest key of bin L: (e & mask) == prefix selects the current bin
   uint64_t prefix = (uint64_t)Lbin << 52, mask = 0xFFF0000000000000ull;
   uint32_t cnt = countL;
-  for (int sh = 44; cnt != need; sh -= 8) {
+  // (keys are unique, so the 52 bits below the bin settle it by sh = -4; the bound only guards the loop)
+  for (int sh = 44; cnt != need && sh > -12; sh -= 8) {
     const uint64_t dmask = sh >= 0 ? 0xFFull : (0xFFull >> -sh);  // the last digit: bits 3..0
     const int shc = sh >= 0 ? sh : 0;
     if (cnt <= 64) {
@@ -734,7 +735,8 @@ __device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int 
         const uint64_t e = i < n_src ? src(i) : 0ull;
         const bool m = i < n_src && (e & mask) == prefix;
         const uint64_t bm = __ballot(m);
-        if (m) small[ns + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] = e;
+        const uint32_t at = ns + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+        if (m && at < 64u) small[at] = e;
         ns += (uint32_t)__popcll(bm);
       }
       const uint64_t mine = small[lane];
@@ -742,7 +744,7 @@ __device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int 
 #pragma unroll
       for (int m = 0; m < 64; ++m) rank += small[m] > mine ? 1u : 0u;
       const uint64_t th = __ballot(lane < (int)cnt && rank == need - 1);
-      prefix = (uint64_t)__shfl((long long)mine, (int)__builtin_ctzll(th), 64);
+      prefix = (uint64_t)__shfl((long long)mine, th ? (int)__builtin_ctzll(th) : 0, 64);
       mask = ~0ull;
       break;
     }
@@ -775,7 +777,7 @@ __device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int 
       }
     }
     const uint64_t owner = __ballot(excl < need && incl >= need);
-    const int ol = (int)__builtin_ctzll(owner);
+    const int ol = owner ? (int)__builtin_ctzll(owner) : 0;
     dsel = (uint32_t)__shfl((int)dsel, ol, 64);
     above = (uint32_t)__shfl((int)above, ol, 64);
     cd = (uint32_t)__shfl((int)cd, ol, 64);
@@ -992,7 +994,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 4) void tile_kernel(ScoreArgs a) {
           q_cand(a, qrow(j))[(size_t)sg * kTileSeg + run[j] + pre] = e;
           if (blst[j] && (key[j] >> 20) == Lb[j]) {
             const int q = tile_slot_query(j, half);
-            reinterpret_cast<uint64_t*>(&S.hist[q][0])[atomicAdd(&S.bcnt[q], 1u)] = e;
+            const uint32_t at = atomicAdd(&S.bcnt[q], 1u);  // < countL <= kTileBoundCap: pass 1 counted these keys
+            if (at < (uint32_t)kTileBoundCap) reinterpret_cast<uint64_t*>(&S.hist[q][0])[at] = e;
           }
         }
         run[j] += half ? (uint32_t)__popc(hi) : nlo;
