@@ -241,6 +241,27 @@ lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t T
 lca_status lca_swa_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev, float* lse_dev,
                         void* ws_dev, size_t ws_bytes, void* stream);
 
+/* One decode step of an HCA layer in one call: the T new tokens of every
+ * sequence go in (lca_hca_compress for the blocks they complete, then the
+ * window entries and tail copies of lca_swa_tail_append) and their T
+ * queries attend (lca_hca_dense_attn): the same cache bytes and outputs as
+ * those calls. One launch, two when a block completes: the append runs in
+ * the attention launch (each workgroup that reads the window writes the new
+ * entries itself before reading them back). For decode-sized calls:
+ * B * T <= 511 (else LCA_ERR_SHAPE); ring >= T + window - 1. Arguments as
+ * the three calls; lse_dev and ws_dev may be NULL. Checks everything before
+ * launching: a rejected call leaves the cache unchanged. */
+lca_status lca_hca_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const float* bias_dev,
+                        int32_t T, const uint16_t* q_dev, uint16_t* out_dev, float* lse_dev, void* ws_dev,
+                        size_t ws_bytes, void* stream);
+
+/* One decode step of a window-only layer (the final MTP block): the T new
+ * tokens' window entries (lca_swa_tail_append) and their queries' window
+ * attention (lca_swa_attn) in one launch; the same results as the two
+ * calls. Limits and checks as lca_hca_step. */
+lca_status lca_swa_step(lca_cache* cache, const uint16_t* kv_dev, int32_t T, const uint16_t* q_dev,
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* The CSA query path with the selection and the attention in one launch
  * (CSA paragraph: top-k compressed blocks per query; Figure 3: their
  * attention joined with the sliding-window branch under one softmax).

@@ -85,6 +85,8 @@ _SIGNATURES = {
     "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
                             _VP, _VP]),
+    "lca_hca_step": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_swa_step": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_snapshot_layout": (_I32, [_CP, _SP]),
     "lca_cache_snapshot": (_I32, [_CP, _I32, _VP, _SZ, _SP, _VP]),
     "lca_cache_restore": (_I32, [_CP, _I32, _VP, _SZ, _SP, _VP]),
@@ -228,6 +230,16 @@ def lca_csa_step(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out
                                                score_events[0], score_events[1]))
 
 
+def lca_hca_step(cache, kv, gate, bias, T, q, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_hca_step", lib().lca_hca_step(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(bias), T, _ptr(q),
+                                               _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_swa_step(cache, kv, T, q, out, lse, ws, ws_bytes, stream=None):
+    _check("lca_swa_step", lib().lca_swa_step(ctypes.byref(cache), _ptr(kv), T, _ptr(q), _ptr(out), _ptr(lse),
+                                               _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def lca_snapshot_layout(cache):
     info = lca_snapshot_info()
     _check("lca_snapshot_layout", lib().lca_snapshot_layout(ctypes.byref(cache), ctypes.byref(info)))
@@ -357,6 +369,14 @@ class DeviceLayer:
         """One decode step (CSA): T = kv.shape[1] tokens in, their queries attend."""
         lca_csa_step(self.cache, kv, gate, ik, ig, bias, idx_bias, kv.shape[1], qI, w, q, topk, out, lse, self.ws,
                      self.ws_bytes, stream, score_events)
+
+    def hca_step(self, kv, gate, bias, q, out, lse=None, stream=None):
+        """One decode step (HCA): T = kv.shape[1] tokens in (compress, append), their queries attend."""
+        lca_hca_step(self.cache, kv, gate, bias, kv.shape[1], q, out, lse, self.ws, self.ws_bytes, stream)
+
+    def swa_step(self, kv, q, out, lse=None, stream=None):
+        """One decode step (window-only): T = kv.shape[1] tokens' window entries, their queries attend."""
+        lca_swa_step(self.cache, kv, kv.shape[1], q, out, lse, self.ws, self.ws_bytes, stream)
 
     # ---- persistence: snapshots are device buffers; files hold their bytes as they are
     def snapshot(self, seq=0, stream=None):

@@ -41,6 +41,7 @@
 // the nope logits and is folded into P for the nope output dims.
 #include "attn_common.h"
 #include "dev_formats.h"
+#include "ingest.h"
 #include "kernels.h"
 #include "select.h"
 
@@ -303,6 +304,15 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
     if (hg == 0 && split == 0)  // every scan workgroup has read this query's histogram: clear it for the next call
       for (int i = tid; i < kHistBins; i += 512) q_hist(sa, q)[i] = 0u;
     K.n_list = (int)select_query(sa, q, N, S.u.sel, S.list);
+  }
+  if (MODE == kAttendDense && args.app_units > 0 && split == 0) {
+    // The step's append, in this launch: the window entries of the new tokens, which this workgroup's
+    // window slots read (every split-0 workgroup of the sequence writes them, the same bytes, then reads
+    // them back after the fence and barrier below), and the tail copies (head group 0 only; nothing here
+    // reads the tail). One wave per unit.
+    for (int unit = wave; unit < args.app_units; unit += kWaves)
+      if (unit < args.app.n_win || hg == 0) append_unit<false>(args.app, b, unit, lane);
+    __threadfence_block();
   }
   __syncthreads();
   if (do_select && hg == 0 && split == 0 && args.s.topk) {

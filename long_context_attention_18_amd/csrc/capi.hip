@@ -457,6 +457,53 @@ lca_status attention_impl(lca_cache* cache, int32_t kind, const uint16_t* q_dev,
   return launch_status(launch_attention(a, cache->batch, s));
 }
 
+// One decode step of a dense layer (HCA: compress when blocks complete, then attention with the append
+// in the same launch; window-only: the append in the attention launch). Every check before any launch.
+lca_status dense_step_impl(lca_cache* cache, int32_t kind, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                           const float* bias_dev, int32_t T, const uint16_t* q_dev, uint16_t* out_dev,
+                           float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  const bool hca = kind == LCA_KIND_HCA;
+  if (!cache_ok(cache) || !kv_dev || !q_dev || !out_dev || (hca && (!gate_dev || !bias_dev))) return LCA_ERR_NULL;
+  if (cache->desc.kind != kind) return LCA_ERR_UNSUPPORTED;
+  if (T < 1 || (int64_t)cache->batch * T > kAttendMaxQueries) return LCA_ERR_SHAPE;
+  if (cache->pending != 0 || cache->ragged) return LCA_ERR_ORDER;
+  if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
+  lca_cache after = *cache;  // the cache once the T tokens are in: what the queries see
+  after.len = cache->len + T;
+  AttendArgs args{};
+  lca_status st = attn_args(&after, kind, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
+  if (st != LCA_OK) return st;
+  attend_workspace(&args, &after, T, ws_dev, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t m = cache->desc.m;
+  const int64_t end = cache->len + T;
+  if (hca) {
+    const int64_t n_blocks = end / m - cache->len / m;
+    if (n_blocks > 0) {
+      IngestArgs ca = ingest_args(cache, kv_dev, gate_dev, nullptr, nullptr, T);
+      ca.bias = bias_dev;
+      ca.first = cache->len / m;
+      if (launch_compress(ca, false, n_blocks, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    }
+  }
+  IngestArgs app = ingest_args(cache, kv_dev, gate_dev, nullptr, nullptr, T);
+  const int64_t win_first = (end - cache->ring > cache->len) ? end - cache->ring : cache->len;
+  app.first = win_first;
+  app.n_win = (int32_t)(end - win_first);
+  int32_t n_tail = 0;
+  if (hca) {
+    int64_t tail_first = (end / m) * m;
+    if (tail_first < cache->len) tail_first = cache->len;
+    n_tail = (int32_t)(end - tail_first);
+  }
+  args.app = app;
+  args.app_units = app.n_win + n_tail;
+  if (launch_attend(args, cache->batch, kAttendDense, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  cache->len = end;
+  cache->pending = 0;
+  return LCA_OK;
+}
+
 lca_status topk_attn_impl(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, bool score,
                           const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
                           void* ws_dev, size_t ws_bytes, void* stream) {
@@ -493,6 +540,19 @@ lca_status lca_hca_dense_attn(lca_cache* cache, const uint16_t* q_dev, int32_t T
 lca_status lca_swa_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, uint16_t* out_dev, float* lse_dev,
                         void* ws_dev, size_t ws_bytes, void* stream) {
   return attention_impl(cache, LCA_KIND_SWA, q_dev, nullptr, Tq, out_dev, lse_dev, ws_dev, ws_bytes, stream);
+}
+
+lca_status lca_hca_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const float* bias_dev,
+                        int32_t T, const uint16_t* q_dev, uint16_t* out_dev, float* lse_dev, void* ws_dev,
+                        size_t ws_bytes, void* stream) {
+  return dense_step_impl(cache, LCA_KIND_HCA, kv_dev, gate_dev, bias_dev, T, q_dev, out_dev, lse_dev, ws_dev,
+                         ws_bytes, stream);
+}
+
+lca_status lca_swa_step(lca_cache* cache, const uint16_t* kv_dev, int32_t T, const uint16_t* q_dev,
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return dense_step_impl(cache, LCA_KIND_SWA, kv_dev, nullptr, nullptr, T, q_dev, out_dev, lse_dev, ws_dev,
+                         ws_bytes, stream);
 }
 
 lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq, int32_t* topk_dev,

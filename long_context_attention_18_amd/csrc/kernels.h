@@ -179,6 +179,10 @@ struct AttendArgs {
   AttendPartial* part;  // [B*Tq][groups][splits] (splits > 1)
   uint32_t* cnt;        // [B*Tq][groups], zero between calls (splits > 1)
   int32_t splits;
+  // kAttendDense with app_units > 0: the launch also appends the step's tokens (window entries by the
+  // split-0 workgroups that read the window, tail copies by head group 0 of split 0), before attending
+  IngestArgs app;
+  int32_t app_units;
 };
 
 // Contiguous runs copied between a cache and a snapshot buffer (persist.hip): run i moves `bytes`

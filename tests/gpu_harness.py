@@ -142,7 +142,8 @@ class LayerRun:
         return qin, (from_dev(topk) if topk is not None else None), from_dev(out, np.uint16), from_dev(lse)
 
     def step(self, T=1):
-        """T new tokens per sequence and their queries through lca_csa_step (one call)."""
+        """T new tokens per sequence and their queries through one step call (lca_csa_step, lca_hca_step or
+        lca_swa_step)."""
         import torch
         parts = [self.tokens(b, self.len, T) for b in range(self.B)]
         tok = {k: to_dev(np.stack([p[k] for p in parts])) for k in parts[0]}
@@ -151,6 +152,15 @@ class LayerRun:
         H = self.layer.n_heads
         out = torch.empty((self.B, T, H, 128), dtype=torch.int16, device="cuda")
         lse = torch.empty((self.B, T, H), dtype=torch.float32, device="cuda")
+        if not self.csa:
+            if self.swa:
+                self.dev.swa_step(tok["kv"], to_dev(qin["q"]), out, lse)
+            else:
+                self.dev.hca_step(tok["kv"], tok["gate"], self.bias_dev["bias"], to_dev(qin["q"]), out, lse)
+            torch.cuda.synchronize()
+            self.len += T
+            self.last_scores = None
+            return qin, None, from_dev(out, np.uint16), from_dev(lse)
         topk = torch.full((self.B, T, self.layer.topk), -7, dtype=torch.int32, device="cuda")
         self.dev.step(tok["kv"], tok["gate"], tok["ik"], tok["ig"], self.bias_dev["bias"], self.bias_dev["idx_bias"],
                       to_dev(qin["qI"]), to_dev(qin["w"]), to_dev(qin["q"]), out, lse, topk)

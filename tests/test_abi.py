@@ -103,6 +103,8 @@ def test_bad_arguments_are_rejected_before_any_launch():
     assert L.lca_csa_topk_attn(ctypes.byref(cache), 1, 1, None, 1, None, 1, 1, None) == -1
     assert L.lca_csa_step(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, 1, None, 1, 1, None, None,
                           None) == -1
+    assert L.lca_hca_step(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, None, None, 0, None) == -1
+    assert L.lca_swa_step(ctypes.byref(cache), 1, 1, 1, 1, None, None, 0, None) == -1
     assert L.lca_workspace_init(None, 256, None) == -1
 
 
@@ -161,6 +163,21 @@ def test_order_capacity_and_kind_checks():
     assert L.lca_csa_attend(ctypes.byref(h), P, P, P, 1, None, P, None, P, 1 << 30, None) == -3
     assert L.lca_csa_step(ctypes.byref(h), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, 1 << 30, None, None,
                           None) == -3
+    # the dense one-call steps: kind, null inputs, decode-sized T, capacity, order; a rejected call leaves
+    # the cache as it was
+    assert L.lca_hca_step(ctypes.byref(c), P, P, P, 1, P, P, None, None, 0, None) == -3   # CSA cache
+    assert L.lca_swa_step(ctypes.byref(h), P, 1, P, P, None, None, 0, None) == -3         # HCA cache
+    assert L.lca_hca_step(ctypes.byref(h), P, None, P, 1, P, P, None, None, 0, None) == -1  # HCA needs gate
+    assert L.lca_hca_step(ctypes.byref(h), P, P, P, 512, P, P, None, None, 0, None) == -2
+    assert L.lca_hca_step(ctypes.byref(h), P, P, P, 0, P, P, None, None, 0, None) == -2
+    h.len = 4090
+    assert L.lca_hca_step(ctypes.byref(h), P, P, P, 10, P, P, None, None, 0, None) == -4
+    assert h.len == 4090
+    h.len = 0
+    h.pending = 3
+    assert L.lca_hca_step(ctypes.byref(h), P, P, P, 1, P, P, None, None, 0, None) == -5
+    h.pending = 0
+    assert h.len == 0
 
 
 def test_workspace_bytes_grows_with_queries():

@@ -305,6 +305,30 @@ def test_csa_step_one_call_decode():
     compare_cache(a, oc)
 
 
+def test_dense_step_calls_match_separate_calls():
+    """lca_hca_step (compress + append in the attention launch) and lca_swa_step, across HCA block
+    boundaries and with T = 3 tokens per step: against the oracle, and bit for bit against compress + append
+    + dense / window attention on a twin cache (cache bytes, outputs, LSE)."""
+    for layer, ctx, steps in ((configs.Layer("hca", 128, n_heads=64, window=128), 2300, [1, 1, 3, 1, 1]),
+                              (configs.Layer("swa", 1, n_heads=64, window=128), 300, [1, 3, 1])):
+        a = LayerRun(layer, B=3, max_ctx=ctx + 40, ring=130, max_tq=3)
+        b = LayerRun(layer, B=3, max_ctx=ctx + 40, ring=130, max_tq=3)
+        for run in (a, b):
+            _ingest(run, [ctx])
+        oc = [a.oracle_caches(i, ctx + 40) for i in range(a.B)]
+        for T in steps * 4:
+            qa, _, oa, la = a.step(T)
+            b.ingest(T)
+            qb, _, ob, lb = b.run_queries(T)
+            check_queries(a, oc, qa, None, oa, la, list(range(a.len - T, a.len)))
+            assert np.array_equal(oa, ob)
+            assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+        va, vb = a.dev.views(), b.dev.views()
+        for k in va:
+            assert np.array_equal(va[k].cpu().numpy(), vb[k].cpu().numpy()), k
+        compare_cache(a, oc)
+
+
 def test_csa_step_short_context():
     """lca_csa_step from an empty cache: window-only queries, then N <= k, then selection (k = 16)."""
     layer = configs.Layer("csa", 4, n_heads=16, window=32, idx_heads=4, topk=16)
