@@ -54,23 +54,24 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   uint32_t* hist = S.hist;
   uint32_t* wsum = S.wsum;
 
-  // One round of loads: every segment's count and, speculatively, its first kSpec slots (always in
+  // One round of loads: every segment's count and, speculatively, its first `covered` slots (always in
   // bounds: a segment has room for seg_sz candidates, and the workspace continues after the last
   // query's); only a fuller segment needs a second round. Segments: kScanPerWG blocks (candidate scan)
   // or kTileSeg (query tiles).
   const int seg_sz = a.tiles ? kTileSeg : kScanPerWG;
   const int G2_q = (int)((N + seg_sz - 1) / seg_sz);
-  constexpr int kSpec = 256;
+  constexpr int kSpecPerLane = 16;  // speculative loads per thread
   const uint64_t* cand = q_cand(a, q);
   const int lanes_per_seg = G2_q <= 32 ? 16 : (G2_q <= 64 ? 8 : 0);  // speculation only for few segments
-  const uint32_t covered = lanes_per_seg ? kSpec : 0u;  // slots per segment the speculative loads place
-  uint64_t spec[16];
+  // slots per segment the speculative loads place: the first 256 (16 threads per segment) or 128 (8)
+  const uint32_t covered = (uint32_t)(lanes_per_seg * kSpecPerLane);
+  uint64_t spec[kSpecPerLane];
   const int my_seg = lanes_per_seg ? tid / lanes_per_seg : 0;
   const int my_sub = lanes_per_seg ? tid % lanes_per_seg : 0;
-  const int per_lane = lanes_per_seg ? kSpec / lanes_per_seg : 0;
+  const int per_lane = lanes_per_seg ? kSpecPerLane : 0;
   if (lanes_per_seg && my_seg < G2_q) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < kSpecPerLane; ++r)
       if (r < per_lane) spec[r] = cand[(size_t)my_seg * seg_sz + my_sub + r * lanes_per_seg];
   }
   if (tid == 0) S.flat_needed = 0u;
@@ -102,7 +103,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
     if (lanes_per_seg && my_seg < G2_q) {
       const uint32_t c = seg_off[my_seg + 1] - seg_off[my_seg];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < kSpecPerLane; ++r) {
         const uint32_t i = my_sub + r * lanes_per_seg;
         if (r < per_lane && i < c) {
           cs[seg_off[my_seg] + i] = spec[r];

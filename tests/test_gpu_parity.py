@@ -171,6 +171,43 @@ def test_csa_query_tiles_all_weights_negative():
     assert w["scores_checked"] > 0
 
 
+def test_selection_with_a_crowded_segment():
+    """Candidates bunched into one segment: the indexer keys of blocks 2560-2815 (one 256-block segment of
+    the query tiles) are scaled up 8x and every indexer weight is positive, so most of the top-256 of
+    nearly every query come from that segment. The
+    queries see about 10,500 blocks, 42 segments: the selection's first round of loads places the first
+    128 candidates of each segment and must fetch the rest of the crowded one. Combined call (selection
+    in the tile kernel), separate score + select calls and the fused attention launch all against the
+    oracle on sampled queries."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=256)
+
+    def transform(tok, pos0):
+        f = synth.bf16_to_f32(tok["ik"]).copy()
+        blk = (pos0 + np.arange(f.shape[0])) // 4
+        f[(blk >= 2560) & (blk < 2816)] *= np.float32(8.0)
+        out = dict(tok)
+        out["ik"] = synth.bf16_bits(f)
+        return out
+
+    def qtransform(qin):
+        out = dict(qin)
+        out["w"] = np.abs(qin["w"])
+        return out
+
+    Tq, pre = 2048, 40000
+    for fused in (False, True):
+        run = LayerRun(layer, B=1, max_ctx=pre + Tq, ring=Tq + 127, max_tq=Tq, sigma=1.0, transform=transform,
+                       qtransform=qtransform)
+        _ingest(run, [pre, Tq])
+        qin, topk, out, lse = run.run_queries(Tq, fused=fused)
+        crowded = ((topk[0] >= 2560) & (topk[0] < 2816)).sum(axis=1) > 128
+        assert crowded.mean() > 0.9, crowded.mean()
+        oc = [run.oracle_caches(0, pre + Tq)]
+        pos = list(range(run.len - Tq, run.len))
+        w = check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 97)) + [Tq - 1])
+        assert w["scores_checked"] > 0
+
+
 def test_ingest_chunking_invariance():
     """The same token stream ingested token by token, in 7s, or at once: identical cache bytes."""
     layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
