@@ -4,6 +4,7 @@
 // kernel launches. Every check happens before the first launch of a call, so
 // a rejected call enqueues nothing.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -311,6 +312,19 @@ lca_status lca_swa_tail_append(lca_cache* cache, const uint16_t* kv_dev, const u
 
 namespace {
 
+// compute units of the current device, read once per device
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, bool need_q, int32_t Tq,
                       int32_t* topk_dev, bool need_topk, void* ws_dev, size_t ws_bytes, ScoreArgs* out) {
   if (!cache_ok(cache)) return LCA_ERR_NULL;
@@ -354,6 +368,17 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
       wgs = (g1 + kMultiChunks - 1) / kMultiChunks;
       wgs = wgs < 1 ? 1 : wgs;
       a.chunk_step = (int32_t)wgs;
+    } else if (!a.tiles && g1 >= 2) {
+      // One workgroup per chunk runs as a single wave of workgroups when nq * g1 fits the compute units.
+      // When only the last, at most half-full chunk column pushes it past that, workgroup 0 of each
+      // query scores the last chunk after its own: a short second chunk instead of a second wave of
+      // whole workgroups after the first has drained.
+      const int64_t cap = (int64_t)kScoreWGsPerCU * device_cus();
+      const int64_t tail = a.len / a.m - (g1 - 1) * kScoreChunk;
+      if (nq * g1 > cap && nq * (g1 - 1) <= cap && tail <= kScoreChunk / 2) {
+        wgs = g1 - 1;
+        a.fold_tail = 1;
+      }
     }
     // each workgroup counts at least cmin keys (twice its share of k) into the query's histogram
     const int64_t w = wgs > 0 ? wgs : 1;

@@ -171,21 +171,21 @@ struct ScoreQuery {
 // back to back in tile order (loads return in order, so the first tile pair can start as soon as its
 // own data is in). FULL: the whole chunk is visible, so each address is one base plus a constant
 // offset; otherwise each is clamped to the last visible block (always in bounds).
-template <bool FULL>
+template <bool FULL, int ITERS = kScoreIters>
 __device__ __forceinline__ void load_keys(const uint8_t* codes, const uint8_t* scl, int wave_j0, int n2, int half,
-                                          int N, uint4 (&bvs)[kScoreIters], int (&sbs)[kScoreIters]) {
+                                          int N, uint4 (&bvs)[ITERS], int (&sbs)[ITERS]) {
   if (FULL) {
     const uint8_t* cb = codes + (size_t)(wave_j0 + n2) * 32 + half * 16;
     const uint8_t* sb = scl + (size_t)(wave_j0 + n2) * 2 + half;
 #pragma unroll
-    for (int it = 0; it < kScoreIters; ++it) {
+    for (int it = 0; it < ITERS; ++it) {
       bvs[it] = *reinterpret_cast<const uint4*>(cb + it * 32 * 32);
       sbs[it] = sb[it * 32 * 2];
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
-    for (int it = 0; it < kScoreIters; ++it) {
+    for (int it = 0; it < ITERS; ++it) {
       int jb = wave_j0 + it * 32 + n2;
       jb = jb < N ? jb : N - 1;
       bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + half * 16);
@@ -276,16 +276,16 @@ __device__ __forceinline__ void query_operands(const ScoreLds& S, ScoreQuery& Q)
 // One chunk's scores from its loaded keys: the key of every visible block to `keys`, this lane's key
 // per tile pair to lane_keys (0 = no block); blocks outside the exactness bounds are rescored in fp64.
 // Contains workgroup barriers: every thread of the workgroup calls it.
-template <bool FULL>
-__device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, const ScoreQuery& Q, const uint4 (&bvs)[kScoreIters],
-                                            const int (&sbs)[kScoreIters], uint32_t* keys, const uint8_t* codes,
+template <bool FULL, int ITERS = kScoreIters>
+__device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, const ScoreQuery& Q, const uint4 (&bvs)[ITERS],
+                                            const int (&sbs)[ITERS], uint32_t* keys, const uint8_t* codes,
                                             const uint8_t* scl, int N, int j_begin, int wave_j0, int n2,
-                                            uint32_t (&lane_keys)[kScoreIters / 2]) {
+                                            uint32_t (&lane_keys)[ITERS / 2]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int odd = (lane >> 4) & 1;
   if (lane == 0) S.n_flag[wave] = 0;  // this wave's own list: program order suffices
 #pragma unroll
-  for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+  for (int pr = 0; pr < ITERS / 2; ++pr) {
     const int tA = 2 * pr, tB = 2 * pr + 1;
     const bool liveA = FULL || wave_j0 + tA * 32 + n2 < N, liveB = FULL || wave_j0 + tB * 32 + n2 < N;
     const uint4 bA = liveA ? bvs[tA] : make_uint4(0u, 0u, 0u, 0u);
@@ -338,7 +338,7 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
     __syncthreads();
     __threadfence_block();
 #pragma unroll
-    for (int pr = 0; pr < kScoreIters / 2; ++pr) {
+    for (int pr = 0; pr < ITERS / 2; ++pr) {
       const int jb = wave_j0 + ((odd ? 2 * pr : 2 * pr + 1)) * 32 + n2;
       if (FULL || jb < N) lane_keys[pr] = keys[jb];
     }
@@ -394,24 +394,30 @@ __device__ __forceinline__ void hist_publish(const ScoreArgs& a, ScoreLds& S, in
 }
 
 // The query's loads (its MX-FP4 slice for quantise_query, the head weights) into Q / qraw
-__device__ __forceinline__ uint4 load_query(const ScoreArgs& a, int b, int tq, ScoreQuery& Q) {
-  const int lane = threadIdx.x & 63;
-  const int qh = lane >> 3, qpart = lane & 7;
-  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
-  if (qh < a.HI) qraw = *reinterpret_cast<const uint4*>(a.qI + (((size_t)b * a.Tq + tq) * a.HI + qh) * kIdxDim + qpart * 8);
+// the query's head weights (0 for heads >= H_I)
+__device__ __forceinline__ void load_weights(const ScoreArgs& a, int b, int tq, ScoreQuery& Q) {
   Q.wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     Q.wlo[i] = i < a.HI ? Q.wq[i] : 0.0f;
     Q.whi[i] = i + 4 < a.HI ? Q.wq[i + 4] : 0.0f;
   }
+}
+
+__device__ __forceinline__ uint4 load_query(const ScoreArgs& a, int b, int tq, ScoreQuery& Q) {
+  const int lane = threadIdx.x & 63;
+  const int qh = lane >> 3, qpart = lane & 7;
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+  if (qh < a.HI) qraw = *reinterpret_cast<const uint4*>(a.qI + (((size_t)b * a.Tq + tq) * a.HI + qh) * kIdxDim + qpart * 8);
+  load_weights(a, b, tq, Q);
   return qraw;
 }
 
 // One score workgroup's chunk: kScoreChunk blocks from j_begin (few-query calls: every workgroup one
 // chunk). The keys' loads go out before the query is quantised.
 template <bool FULL>
-__device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin) {
+__device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin,
+                                            int j_tail) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   ScoreQuery Q;
   const uint4 qraw = load_query(a, b, tq, Q);
@@ -424,12 +430,27 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   uint4 bvs[kScoreIters];
   int sbs[kScoreIters];
   load_keys<FULL>(codes, scl, wave_j0, n2, (lane >> 4) & 1, N, bvs, sbs);
+  // a folded last chunk (blocks j_tail..N-1, at most half a chunk: kTailIters tiles per wave), loaded
+  // with this one and scored after it into the same histogram
+  constexpr int kTailIters = kScoreIters / 2;
+  const bool has_tail = j_tail >= 0 && j_tail < N;
+  const int wave_t0 = j_tail + wave * kTailIters * 32;
+  uint4 tvs[kTailIters];
+  int tsb[kTailIters];
+  if (has_tail) load_keys<false, kTailIters>(codes, scl, wave_t0, n2, (lane >> 4) & 1, N, tvs, tsb);
   for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
   if (wave == 0) quantise_query(a, S, qraw);
   __syncthreads();  // quantised query and bounds visible
   query_operands(S, Q);
   uint32_t lane_keys[kScoreIters / 2];
   score_pairs<FULL>(a, S, Q, bvs, sbs, keys, codes, scl, N, j_begin, wave_j0, n2, lane_keys);
+  uint32_t tail_keys[kTailIters / 2];
+#pragma unroll
+  for (int pr = 0; pr < kTailIters / 2; ++pr) tail_keys[pr] = 0u;
+  if (has_tail) {
+    __syncthreads();  // every wave has read the first chunk's flag lists
+    score_pairs<false, kTailIters>(a, S, Q, tvs, tsb, keys, codes, scl, N, j_tail, wave_t0, n2, tail_keys);
+  }
   // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
   // and the 16 bins below it (down to a quarter of the max), or, when those hold fewer than cmin of the
   // chunk's keys, every bin down to where the chunk's count from the top reaches cmin. Counts in a bin
@@ -440,12 +461,14 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   uint32_t m = 0;
 #pragma unroll
   for (int pr = 0; pr < kScoreIters / 2; ++pr) m = max(m, lane_keys[pr]);
+#pragma unroll
+  for (int pr = 0; pr < kTailIters / 2; ++pr) m = max(m, tail_keys[pr]);
   const uint32_t kmax = wg_max_key(S, m);
   const int top_bin = (int)(kmax >> 20);
   const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
 #pragma unroll
-  for (int pr = 0; pr < kScoreIters / 2; ++pr) {
-    const uint32_t key = lane_keys[pr];
+  for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
+    const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
     if (key != 0 && (int)(key >> 20) >= low_bin) atomicAdd(&S.hist[key >> 20], 1u);
   }
   __syncthreads();
@@ -460,8 +483,8 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   if (S.range < (uint32_t)a.cmin && low_bin > 0) {
     // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
 #pragma unroll
-    for (int pr = 0; pr < kScoreIters / 2; ++pr) {
-      const uint32_t key = lane_keys[pr];
+    for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
+      const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
       if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&S.hist[key >> 20], 1u);
     }
     lo = hist_cmin_bin(S, (uint32_t)a.cmin);
@@ -525,7 +548,7 @@ __device__ __forceinline__ void score_multi(const ScoreArgs& a, ScoreLds& S, int
 }
 
 // blockIdx.x: a chunk of the query (a.chunk_step = 0) or the first of the chunks x, x + step, ...
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a) {  // <= 128 VGPRs: 2 per CU
   __shared__ ScoreLds S;
   const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
@@ -537,8 +560,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     return;
   }
   const int j_begin = c0 * kScoreChunk;
-  if (j_begin + kScoreChunk <= N) score_chunk<true>(a, S, q, b, tq, N, j_begin);
-  else score_chunk<false>(a, S, q, b, tq, N, j_begin);
+  const int j_tail = a.fold_tail && c0 == 0 ? (int)gridDim.x * kScoreChunk : -1;  // the chunk the grid leaves out
+  if (j_begin + kScoreChunk <= N) score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail);
+  else score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail);
 }
 
 // ---- Many-query calls (chunked prefill): query tiles on the 32x32x64 scaled MFMA ------------------------
@@ -1159,6 +1183,7 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
     return hipGetLastError();
   }
   unsigned g1 = a.chunk_step > 0 ? (unsigned)a.chunk_step : (unsigned)((N_last + kScoreChunk - 1) / kScoreChunk);
+  if (a.fold_tail && a.chunk_step == 0 && g1 >= 2) g1 -= 1;  // workgroup 0 scores the last chunk
   hipLaunchKernelGGL(score_kernel, dim3(g1, nq), dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
 }

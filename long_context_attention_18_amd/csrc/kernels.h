@@ -19,6 +19,8 @@ constexpr int kScoreThreads = kScoreWaves * 64;
 // Calls with at least kMultiMinQueries queries (chunked prefill) score kMultiChunks chunks per workgroup
 constexpr int kMultiMinQueries = 512;
 constexpr int kMultiChunks = 8;
+// score workgroups one compute unit holds at once (8 waves of at most 128 VGPRs, the kernel's launch bound)
+constexpr int kScoreWGsPerCU = 2;
 // Calls with at least kTileMinQueries queries, each seeing at most kTileMaxBlocks blocks, score in query
 // tiles: kTileQueries queries of one sequence per workgroup of kTileWaves waves (indexer.hip)
 constexpr int kTileMinQueries = 2048;
@@ -98,6 +100,8 @@ struct ScoreArgs {
   int32_t G2;              // scan segments per query
   int32_t cmin;            // keys each score workgroup counts into the histogram at least (twice its share of k)
   int32_t chunk_step;      // 0: a score workgroup per 2048-block chunk; else one per chunk_step chunks of a query
+  int32_t fold_tail;       // 1: the grid leaves out the last chunk of each query, which workgroup 0 scores
+                           //    after its own (decode grids that a short last chunk would push past the CUs)
   int32_t tiles;           // 1: query tiles (the score launch also writes the candidates; no scan)
   int32_t write_keys;      // tiles: also write every visible block's key (the separate score call's contract)
   int32_t tile_select;     // tiles: the score launch also selects the top-k lists into topk (combined call)

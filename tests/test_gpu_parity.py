@@ -115,6 +115,29 @@ def test_csa_prefill_many_queries_long_context():
         print("prefill long-context", B, Tq, w)
 
 
+def test_csa_score_tail_chunk_folded():
+    """257 queries over up to 2164 blocks: two score chunks each, the second holding 116 blocks. 257 x 2
+    score workgroups would not all fit on the compute units at once (two per unit), so each query's one
+    workgroup scores its first chunk and then the short last one (its keys loaded before the query's
+    quantisation, the tail's after the first chunk). Sampled queries: scores and top-k bit-exact,
+    attention within the bar."""
+    import torch
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=512)
+    pre, Tq = 8400, 257
+    n_last = (pre + Tq) // 4
+    if 2 * Tq <= 2 * torch.cuda.get_device_properties(0).multi_processor_count:
+        pytest.skip("the device holds every score workgroup at once: no folding")
+    assert n_last - 2048 <= 1024 and Tq * 1 <= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    run = LayerRun(layer, B=1, max_ctx=pre + Tq, ring=Tq + 127, max_tq=Tq, sigma=1.0)
+    _ingest(run, [pre, Tq])
+    qin, topk, out, lse = run.run_queries(Tq)
+    oc = [run.oracle_caches(0, pre + Tq)]
+    pos = list(range(run.len - Tq, run.len))
+    w = check_queries(run, oc, qin, topk, out, lse, pos, sample=list(range(0, Tq, 37)) + [Tq - 1])
+    assert w["scores_checked"] > 0
+    print("folded tail chunk", w)
+
+
 def test_csa_prefill_query_tiles():
     """Calls of 2048+ queries score in query tiles (8 queries of one sequence per workgroup, both passes).
     B = 2 x Tq = 1030 (the last tile of each sequence partial) over about 7,800 blocks; then one sequence of
