@@ -316,7 +316,9 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
     if (FULL || jb < N) {
       if (sc == 0.0f) sc = 0.0f;
       key = order_key(sc);
-      keys[jb] = key;
+      // written through to memory (agent scope): the next launch reads it from other XCDs, and the
+      // launch's end then has no dirty lines of it to write back
+      __hip_atomic_store(&keys[jb], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (bad) S.flag_blk[wave][atomicAdd(&S.n_flag[wave], 1u)] = (uint32_t)(jb - j_begin);
     }
     lane_keys[pr] = key;
@@ -330,7 +332,7 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
       const int jb = j_begin + (int)S.flag_blk[w][f];
       const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
                                          S.qcode, S.qscale, Q.wq, a.HI);
-      keys[jb] = order_key(ex);
+      __hip_atomic_store(&keys[jb], order_key(ex), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     nf += n;
   }
