@@ -22,75 +22,89 @@ namespace lca {
 
 namespace {
 
-// Blocks of at most kPoolCache tokens (CSA: 4): every input of the block is loaded once, up front, and
-// each position's exp is computed once and kept for the weights -- the same operations in the same
-// order as the three passes below, so the same bits; the loads and the exps no longer sit in the
-// passes' dependency chains.
+// Blocks of at most kPoolCache tokens (CSA: 4): one wave per position (wave i loads position i's inputs,
+// its RoPE rotation and, once the maxima are known, its exps), the position terms meet in LDS, and wave 0
+// sums them in ascending position order -- the same operations in the same order as the three passes
+// below, so the same bits, with the loads, the fp64 sincos and the exps of the positions side by side
+// instead of in one wave's dependency chain.
 constexpr int kPoolCache = 4;
 
+struct PoolLds {
+  double x[3][kPoolCache][64];  // gate + bias (nope, RoPE, indexer), then the position's exp
+  double v[3][kPoolCache][64];  // value: kv nope dim, RoPE'd kv dim, indexer key dim
+};
+
+// Wave w (< m) of the workgroup; every wave of the workgroup calls it (barriers). Wave 0 gets the pooled
+// values of its channel c.
 template <bool CSA>
-__device__ __forceinline__ void pool_cached(const IngestArgs& a, int b, int64_t len, int64_t j, int c, double& y_n,
-                                            double& y_r, double& y_i) {
+__device__ __forceinline__ void pool_waves(const IngestArgs& a, PoolLds& P, int b, int64_t len, int64_t j, int w,
+                                           int c, double& y_n, double& y_r, double& y_i) {
   const int m = a.m;
-  const int64_t p0 = j * m;
-  double xn[kPoolCache], xr[kPoolCache], xi[kPoolCache], vn[kPoolCache], vr[kPoolCache], vi[kPoolCache];
-#pragma unroll
-  for (int i = 0; i < kPoolCache; ++i) {
-    if (i < m) {
-      const int64_t p = p0 + i;
-      const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
-      const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
-      xn[i] = (double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c];
-      xr[i] = (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c];
-      vn[i] = (double)bf16_to_f32(kv[c]);
-      vr[i] = rope_channel(kv, c, p, a.inv_freq);
-      if (CSA) {
-        const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
-        const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
-        xi[i] = (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c];
-        vi[i] = (double)bf16_to_f32(ki[c]);
-      }
+  if (w < m) {
+    const int64_t p = j * m + w;
+    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
+    const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
+    P.x[0][w][c] = (double)bf16_to_f32(g[c]) + (double)a.bias[w * kHeadDim + c];
+    P.x[1][w][c] = (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[w * kHeadDim + kNope + c];
+    P.v[0][w][c] = (double)bf16_to_f32(kv[c]);
+    P.v[1][w][c] = rope_channel(kv, c, p, a.inv_freq);
+    if (CSA) {
+      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
+      const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
+      P.x[2][w][c] = (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[w * kIdxDim + c];
+      P.v[2][w][c] = (double)bf16_to_f32(ki[c]);
     }
   }
-  double mu_n = -INFINITY, mu_r = -INFINITY, mu_i = -INFINITY;
+  __syncthreads();
+  double e0 = 0.0, e1 = 0.0, e2 = 0.0;
+  if (w < m) {
+    // the per-channel maxima (order-free), then this position's exps
+    double mu[3] = {-INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-  for (int i = 0; i < kPoolCache; ++i) {
-    if (i < m) {
-      mu_n = fmax(mu_n, xn[i]);
-      mu_r = fmax(mu_r, xr[i]);
-      if (CSA) mu_i = fmax(mu_i, xi[i]);
-    }
+    for (int i = 0; i < kPoolCache; ++i)
+      if (i < m)
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+          if (s < 2 || CSA) mu[s] = fmax(mu[s], P.x[s][i][c]);
+    e0 = pool_exp(P.x[0][w][c] - mu[0]);
+    e1 = pool_exp(P.x[1][w][c] - mu[1]);
+    if (CSA) e2 = pool_exp(P.x[2][w][c] - mu[2]);
   }
+  __syncthreads();  // every wave has read the gate values the exps overwrite
+  if (w < m) {
+    P.x[0][w][c] = e0;
+    P.x[1][w][c] = e1;
+    if (CSA) P.x[2][w][c] = e2;
+  }
+  __syncthreads();
+  y_n = 0.0;
+  y_r = 0.0;
+  y_i = 0.0;
+  if (w != 0) return;
   double S_n = 0.0, S_r = 0.0, S_i = 0.0;
 #pragma unroll
   for (int i = 0; i < kPoolCache; ++i) {
     if (i < m) {
-      xn[i] = pool_exp(xn[i] - mu_n);  // from here on the position's exp
-      xr[i] = pool_exp(xr[i] - mu_r);
-      S_n = S_n + xn[i];
-      S_r = S_r + xr[i];
-      if (CSA) {
-        xi[i] = pool_exp(xi[i] - mu_i);
-        S_i = S_i + xi[i];
-      }
+      S_n = S_n + P.x[0][i][c];
+      S_r = S_r + P.x[1][i][c];
+      if (CSA) S_i = S_i + P.x[2][i][c];
     }
   }
-  y_n = 0.0;
-  y_r = 0.0;
-  y_i = 0.0;
 #pragma unroll
   for (int i = 0; i < kPoolCache; ++i) {
     if (i < m) {
-      y_n = fma(xn[i] / S_n, vn[i], y_n);
-      y_r = fma(xr[i] / S_r, vr[i], y_r);
-      if (CSA) y_i = fma(xi[i] / S_i, vi[i], y_i);
+      y_n = fma(P.x[0][i][c] / S_n, P.v[0][i][c], y_n);
+      y_r = fma(P.x[1][i][c] / S_r, P.v[1][i][c], y_r);
+      if (CSA) y_i = fma(P.x[2][i][c] / S_i, P.v[2][i][c], y_i);
     }
   }
 }
 
+// m <= kPoolCache: m waves per block (pool_waves); otherwise one wave over the block's m positions
 template <bool CSA>
-__global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
-  const int c = threadIdx.x;
+__global__ __launch_bounds__(64 * kPoolCache) void compress_kernel(IngestArgs a) {
+  __shared__ PoolLds P;
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int m = a.m;
   const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
@@ -100,7 +114,8 @@ __global__ __launch_bounds__(64) void compress_kernel(IngestArgs a) {
   const int64_t p0 = j * m;
   double y_n = 0.0, y_r = 0.0, y_i = 0.0;
   if (m <= kPoolCache) {
-    pool_cached<CSA>(a, b, len, j, c, y_n, y_r, y_i);
+    pool_waves<CSA>(a, P, b, len, j, w, c, y_n, y_r, y_i);
+    if (w != 0) return;
   } else {
 
   // pass 1: per-channel max of gate + bias over the block's m positions
@@ -176,8 +191,9 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16) {
 hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)n_blocks, (unsigned)a.B);
-  if (csa) hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(64), 0, s, a);
+  const unsigned threads = a.m <= kPoolCache ? 64u * (unsigned)a.m : 64u;  // a wave per position, or one
+  if (csa) hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(threads), 0, s, a);
+  else hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
