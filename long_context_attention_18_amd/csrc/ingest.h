@@ -55,13 +55,48 @@ __device__ __forceinline__ double half_wave_max(double v) { return swap_max16(ro
 
 // RoPE-rotated value of channel 64+c of token p (pair (2i, 2i+1), i = c/2):
 //   even: x0 cos - x1 sin;  odd: x0 sin + x1 cos;  angle p * inv_freq[i]; fp64.
+// sin and cos of a RoPE angle x (0 <= x < 2^30: a position times an inverse frequency <= 1). Cody and
+// Waite's reduction: k = the integer nearest x / (pi/2), r = x - k pi/2 with pi/2 split into three doubles
+// (one fma each, so every product is exact before its one rounding; |r| <= pi/4 to within 2^-53). Then
+// the Taylor series of sin through r^17 and of cos through r^18 (the first omitted terms stay below
+// 1e-19 on |r| <= pi/4) in Horner form, and the quadrant k mod 4. About 1.5 ulp; no branch, no table.
+__device__ __forceinline__ void rope_sincos(double x, double* sn, double* cs) {
+  const double k = rint(x * 0x1.45f306dc9c883p-1);  // 2/pi
+  double r = fma(-k, 0x1.921fb54442d18p+0, x);      // pi/2, first part
+  r = fma(-k, 0x1.1a62633145c07p-54, r);            // second part
+  r = fma(-k, -0x1.f1976b7ed8fbcp-110, r);          // third part
+  const double z = r * r;
+  double ps = 0x1.952c77030ad4ap-49;                // 1/17!
+  ps = fma(ps, z, -0x1.ae7f3e733b81fp-41);          // -1/15!
+  ps = fma(ps, z, 0x1.6124613a86d09p-33);           // 1/13!
+  ps = fma(ps, z, -0x1.ae64567f544e4p-26);          // -1/11!
+  ps = fma(ps, z, 0x1.71de3a556c734p-19);           // 1/9!
+  ps = fma(ps, z, -0x1.a01a01a01a01ap-13);          // -1/7!
+  ps = fma(ps, z, 0x1.1111111111111p-7);            // 1/5!
+  ps = fma(ps, z, -0x1.5555555555555p-3);           // -1/3!
+  const double s = fma(r * z, ps, r);
+  double pc = -0x1.6827863b97d97p-53;               // -1/18!
+  pc = fma(pc, z, 0x1.ae7f3e733b81fp-45);           // 1/16!
+  pc = fma(pc, z, -0x1.93974a8c07c9dp-37);          // -1/14!
+  pc = fma(pc, z, 0x1.1eed8eff8d898p-29);           // 1/12!
+  pc = fma(pc, z, -0x1.27e4fb7789f5cp-22);          // -1/10!
+  pc = fma(pc, z, 0x1.a01a01a01a01ap-16);           // 1/8!
+  pc = fma(pc, z, -0x1.6c16c16c16c17p-10);          // -1/6!
+  pc = fma(pc, z, 0x1.5555555555555p-5);            // 1/4!
+  pc = fma(pc, z, -0.5);                            // -1/2!
+  const double c = fma(z, pc, 1.0);
+  const int q = (int)((long long)k & 3);
+  *sn = q == 0 ? s : (q == 1 ? c : (q == 2 ? -s : -c));
+  *cs = q == 0 ? c : (q == 1 ? -s : (q == 2 ? -c : s));
+}
+
 __device__ __forceinline__ double rope_channel(const uint16_t* kv_row, int c, int64_t p, const double* inv_freq) {
   int i = c >> 1;
   double x0 = (double)bf16_to_f32(kv_row[kNope + 2 * i]);
   double x1 = (double)bf16_to_f32(kv_row[kNope + 2 * i + 1]);
   double phi = (double)p * inv_freq[i];
   double sn, cs;
-  sincos(phi, &sn, &cs);
+  rope_sincos(phi, &sn, &cs);
   return (c & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
 }
 
