@@ -101,68 +101,13 @@ __device__ __forceinline__ void pool_waves(const IngestArgs& a, PoolLds& P, int 
 }
 
 // m <= kPoolCache: m waves per block (pool_waves); otherwise one wave over the block's m positions
+// The block's entry from its pooled values (wave 0 of the workgroup: lane c holds nope dim c, RoPE dim
+// 64+c and, for CSA, indexer dim c)
 template <bool CSA>
-__global__ __launch_bounds__(64 * kPoolCache) void compress_kernel(IngestArgs a) {
-  __shared__ PoolLds P;
-  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = blockIdx.y;
-  const int m = a.m;
-  const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
-  const int64_t j = (a.seq_len ? len / m : a.first) + blockIdx.x;
-  // ragged batch: the blocks this sequence's own tokens complete (the grid covers the most of any)
-  if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;
-  const int64_t p0 = j * m;
-  double y_n = 0.0, y_r = 0.0, y_i = 0.0;
-  if (m <= kPoolCache) {
-    pool_waves<CSA>(a, P, b, len, j, w, c, y_n, y_r, y_i);
-    if (w != 0) return;
-  } else {
-
-  // pass 1: per-channel max of gate + bias over the block's m positions
-  double mu_n = -INFINITY, mu_r = -INFINITY, mu_i = -INFINITY;
-  for (int i = 0; i < m; ++i) {
-    const int64_t p = p0 + i;
-    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
-    mu_n = fmax(mu_n, (double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]);
-    mu_r = fmax(mu_r, (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]);
-    if (CSA) {
-      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
-      mu_i = fmax(mu_i, (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]);
-    }
-  }
-  // pass 2: softmax denominators, summed in ascending position order
-  double S_n = 0.0, S_r = 0.0, S_i = 0.0;
-  for (int i = 0; i < m; ++i) {
-    const int64_t p = p0 + i;
-    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
-    S_n = S_n + pool_exp(((double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]) - mu_n);
-    S_r = S_r + pool_exp(((double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]) - mu_r);
-    if (CSA) {
-      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
-      S_i = S_i + pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i);
-    }
-  }
-  // pass 3: weighted sum, one fma per position in ascending order
-  for (int i = 0; i < m; ++i) {
-    const int64_t p = p0 + i;
-    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
-    const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
-    double w_n = pool_exp(((double)bf16_to_f32(g[c]) + (double)a.bias[i * kHeadDim + c]) - mu_n) / S_n;
-    double w_r = pool_exp(((double)bf16_to_f32(g[kNope + c]) + (double)a.bias[i * kHeadDim + kNope + c]) - mu_r) / S_r;
-    y_n = fma(w_n, (double)bf16_to_f32(kv[c]), y_n);
-    y_r = fma(w_r, rope_channel(kv, c, p, a.inv_freq), y_r);
-    if (CSA) {
-      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
-      const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
-      double w_i = pool_exp(((double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c]) - mu_i) / S_i;
-      y_i = fma(w_i, (double)bf16_to_f32(ki[c]), y_i);
-    }
-  }
-  }
-
+__device__ __forceinline__ void finish_block(const IngestArgs& a, int b, int64_t j, int c, double y_n, double y_r,
+                                             double y_i) {
   const size_t e = (size_t)b * a.max_blocks + (size_t)j;
   write_entry(y_n, y_r, c, a.blk_codes + e * kNope, a.blk_scale + e, a.blk_rope + e * kRope);
-
   if (CSA) {
     // MX-FP4 indexer key: lanes 0..31 form scale block 0, lanes 32..63 block 1
     double amax = half_wave_max(fabs(y_i));
@@ -173,6 +118,116 @@ __global__ __launch_bounds__(64 * kPoolCache) void compress_kernel(IngestArgs a)
     if ((c & 1) == 0) a.idx_codes[e * 32 + (c >> 1)] = (uint8_t)(code | (hi << 4));
     if ((c & 31) == 0) a.idx_scale[e * 2 + (c >> 5)] = (uint8_t)((amax == 0.0) ? 0 : E + 127);
   }
+}
+
+// Blocks of at most kPoolCache tokens: a wave per position (pool_waves)
+template <bool CSA>
+__global__ __launch_bounds__(64 * kPoolCache) void compress_kernel(IngestArgs a) {
+  __shared__ PoolLds P;
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int m = a.m;
+  const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
+  const int64_t j = (a.seq_len ? len / m : a.first) + blockIdx.x;
+  // ragged batch: the blocks this sequence's own tokens complete (the grid covers the most of any)
+  if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;
+  double y_n, y_r, y_i;
+  pool_waves<CSA>(a, P, b, len, j, w, c, y_n, y_r, y_i);
+  if (w == 0) finish_block<CSA>(a, b, j, c, y_n, y_r, y_i);
+}
+
+// Longer blocks (HCA: 128 tokens): kLongWaves waves, wave w over positions w, w + kLongWaves, ..., one
+// stream (nope, RoPE, indexer) after the other. Per stream: the positions' gate + bias and their maximum
+// (the maximum is free of order); each position's exp into LDS; wave 0 sums the exps in ascending
+// position order; each position's weight (exp / sum) and value into LDS; wave 0 takes the weighted sum
+// with one fma per position in ascending order. The same operations in the same order as one wave
+// walking the positions, so the same bits; the loads, exps, divisions and sincos of the positions run
+// side by side instead of one position after the other.
+constexpr int kLongWaves = 8;
+constexpr int kLongMaxM = 128;
+constexpr int kLongPer = kLongMaxM / kLongWaves;  // positions per wave
+
+struct LongPoolLds {
+  double t[kLongMaxM][64];  // a stream's exps, then its weights
+  double v[kLongMaxM][64];  // a stream's values
+  double part[kLongWaves][64];
+  double sum[64];
+};
+
+template <bool CSA>
+__global__ __launch_bounds__(64 * kLongWaves) void compress_long_kernel(IngestArgs a) {
+  __shared__ LongPoolLds P;
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int m = a.m;
+  const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
+  const int64_t j = (a.seq_len ? len / m : a.first) + blockIdx.x;
+  if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;  // ragged batch, as above
+  const int64_t p0 = j * m;
+  double y[3] = {0.0, 0.0, 0.0};
+#pragma unroll 1
+  for (int st = 0; st < (CSA ? 3 : 2); ++st) {
+    // gate + bias of this wave's positions, and their maximum
+    double x[kLongPer];
+    double mu = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kLongPer; ++u) {
+      const int i = w + u * kLongWaves;
+      x[u] = 0.0;
+      if (i < m) {
+        const int64_t p = p0 + i;
+        if (st < 2) {
+          const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
+          const int col = st == 0 ? c : kNope + c;
+          x[u] = (double)bf16_to_f32(g[col]) + (double)a.bias[i * kHeadDim + col];
+        } else {
+          const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
+          x[u] = (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c];
+        }
+        mu = fmax(mu, x[u]);
+      }
+    }
+    P.part[w][c] = mu;
+    __syncthreads();
+#pragma unroll
+    for (int ww = 0; ww < kLongWaves; ++ww) mu = fmax(mu, P.part[ww][c]);
+#pragma unroll
+    for (int u = 0; u < kLongPer; ++u) {
+      const int i = w + u * kLongWaves;
+      if (i < m) P.t[i][c] = pool_exp(x[u] - mu);
+    }
+    __syncthreads();
+    if (w == 0) {
+      double S = 0.0;
+      for (int i = 0; i < m; ++i) S = S + P.t[i][c];
+      P.sum[c] = S;
+    }
+    __syncthreads();
+    const double S = P.sum[c];
+#pragma unroll 4
+    for (int u = 0; u < kLongPer; ++u) {
+      const int i = w + u * kLongWaves;
+      if (i < m) {
+        const int64_t p = p0 + i;
+        P.t[i][c] = P.t[i][c] / S;
+        if (st < 2) {
+          const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
+          P.v[i][c] = st == 0 ? (double)bf16_to_f32(kv[c]) : rope_channel(kv, c, p, a.inv_freq);
+        } else {
+          const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
+          P.v[i][c] = (double)bf16_to_f32(ki[c]);
+        }
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      double acc = 0.0;
+      for (int i = 0; i < m; ++i) acc = fma(P.t[i][c], P.v[i][c], acc);
+      y[st] = acc;
+    }
+    __syncthreads();  // wave 0 has read the arrays the next stream overwrites
+  }
+  if (w == 0) finish_block<CSA>(a, b, j, c, y[0], y[1], y[2]);
 }
 
 template <bool CSA>
@@ -191,9 +246,15 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16) {
 hipError_t launch_compress(const IngestArgs& a, bool csa, int64_t n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   dim3 grid((unsigned)n_blocks, (unsigned)a.B);
-  const unsigned threads = a.m <= kPoolCache ? 64u * (unsigned)a.m : 64u;  // a wave per position, or one
-  if (csa) hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(threads), 0, s, a);
-  else hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(threads), 0, s, a);
+  if (a.m > kLongMaxM) return hipErrorInvalidValue;
+  if (a.m <= kPoolCache) {
+    const dim3 threads(64u * (unsigned)a.m);  // a wave per position
+    if (csa) hipLaunchKernelGGL(compress_kernel<true>, grid, threads, 0, s, a);
+    else hipLaunchKernelGGL(compress_kernel<false>, grid, threads, 0, s, a);
+  } else {
+    if (csa) hipLaunchKernelGGL(compress_long_kernel<true>, grid, dim3(64 * kLongWaves), 0, s, a);
+    else hipLaunchKernelGGL(compress_long_kernel<false>, grid, dim3(64 * kLongWaves), 0, s, a);
+  }
   return hipGetLastError();
 }
 
