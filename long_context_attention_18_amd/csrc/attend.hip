@@ -217,6 +217,40 @@ __device__ __forceinline__ void attend_round(const Keys K, int slot0, int end, c
     attend_chunk(buf[u], slot0 + u * kChunk, end, qb, scl, kd, voff, r, g, m_run, l_run, O);
 }
 
+// The last split's merge of a (query, group): every split's (m, l, o slice) of this thread's head h and
+// dims d0..d0+3, loaded at once and unconditionally (a load behind a branch would make the compiler wait
+// for all outstanding loads there: one memory round trip per split), NS >= splits slots, the ones past
+// the last split duplicates of it that weigh 0. The partials were written with agent-scope stores by
+// workgroups on other XCDs, so they are read with agent-scope loads.
+template <int NS>
+__device__ __forceinline__ void merge_splits(const AttendPartial* all, int splits, int h, int d0, float& M, float& L,
+                                             float (&acc)[4]) {
+  constexpr float kC = kLog2eRsqrtD;
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  float mv[NS], lv[NS], ov[NS][4];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int sp = min(u, splits - 1);
+    mv[u] = ld(&all[sp].m[h]);
+    lv[u] = ld(&all[sp].l[h]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[u][i] = ld(&all[sp].o[h][d0 + i]);
+  }
+  M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) M = fmaxf(M, mv[u]);  // duplicates of the last split change nothing
+  L = 0.0f;
+  acc[0] = acc[1] = acc[2] = acc[3] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    // an empty split (m = -inf, l = 0, o = 0) weighs 0, and so does a duplicate
+    const float f = u < splits ? __builtin_amdgcn_exp2f((mv[u] - M) * kC) : 0.0f;
+    L += lv[u] * f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += ov[u][i] * f;
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   __shared__ AttendLds S;
@@ -224,7 +258,20 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int hgs = (a.H + 15) / 16;
-  const int hg = blockIdx.x % hgs, split = blockIdx.x / hgs, q = blockIdx.y;
+  // XCD-aware placement: the launch's workgroups go round-robin over the 8 XCDs in linear id order, and
+  // the head groups of one (query, split) gather the same key rows, so they take consecutive logical
+  // indices inside one XCD's share (its L2 then serves the rows once instead of once per group)
+  int hg, split, q;
+  {
+    const unsigned total = gridDim.x * gridDim.y;
+    const unsigned lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const unsigned xcd = lin % 8u, pos = lin / 8u;
+    const unsigned logical = xcd * (total / 8u) + min(xcd, total % 8u) + pos;
+    const unsigned per_q = gridDim.x;  // hgs x splits
+    q = (int)(logical / per_q);
+    hg = (int)(logical % per_q) % hgs;
+    split = (int)(logical % per_q) / hgs;
+  }
   const int b = q / a.Tq, tq = q % a.Tq;
   const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
   if (t < 0) return;  // ragged batch: no query in this row
@@ -430,31 +477,8 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
       if (!S.last) return;
       if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
       const AttendPartial* all = args.part + ((size_t)q * hgs + hg) * splits;
-      auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-      // every split's (m, l, o slice) loaded at once, unconditionally (a load behind a branch would make
-      // the compiler wait for all outstanding loads there: one memory round trip per split)
-      float mv[kAttendMaxSplits], lv[kAttendMaxSplits], ov[kAttendMaxSplits][4];
-#pragma unroll
-      for (int u = 0; u < kAttendMaxSplits; ++u) {
-        const int sp = min(u, splits - 1);
-        mv[u] = ld(&all[sp].m[h]);
-        lv[u] = ld(&all[sp].l[h]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ov[u][i] = ld(&all[sp].o[h][d0 + i]);
-      }
-      M = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kAttendMaxSplits; ++u) M = fmaxf(M, mv[u]);  // duplicates of the last split change nothing
-      L = 0.0f;
-      acc[0] = acc[1] = acc[2] = acc[3] = 0.0f;
-#pragma unroll
-      for (int u = 0; u < kAttendMaxSplits; ++u) {
-        // an empty split (m = -inf, l = 0, o = 0) weighs 0, and so does a duplicate
-        const float f = u < splits ? __builtin_amdgcn_exp2f((mv[u] - M) * kC) : 0.0f;
-        L += lv[u] * f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += ov[u][i] * f;
-      }
+      if (splits <= kAttendMaxSplits / 2) merge_splits<kAttendMaxSplits / 2>(all, splits, h, d0, M, L, acc);
+      else merge_splits<kAttendMaxSplits>(all, splits, h, d0, M, L, acc);
     }
     const int hh = hg * 16 + h;
     if (hh < a.H) {
