@@ -14,9 +14,13 @@ constexpr int kTailKv = 0, kTailGate = 128, kTailIk = 256, kTailIg = 320;
 
 // BF16 input row of token p (absolute position) of sequence b, which held len tokens before this call:
 // from the tail if an earlier call appended it, else from this call's input (row stride a.T).
+// `slot` is p mod m when the caller knows it (a block's own positions: the index in the block), else -1.
 __device__ __forceinline__ const uint16_t* token_row(const IngestArgs& a, int b, int64_t len, int64_t p,
-                                                     const uint16_t* in, int width, int tail_off) {
-  if (p < len) return a.tail + ((size_t)b * a.m + (size_t)(p % a.m)) * a.tail_width + tail_off;
+                                                     const uint16_t* in, int width, int tail_off, int slot = -1) {
+  if (p < len) {
+    const size_t sl = slot >= 0 ? (size_t)slot : (size_t)(p % a.m);  // (a 64-bit division otherwise)
+    return a.tail + ((size_t)b * a.m + sl) * a.tail_width + tail_off;
+  }
   return in + ((size_t)b * a.T + (size_t)(p - len)) * width;
 }
 

@@ -42,15 +42,15 @@ __device__ __forceinline__ void pool_waves(const IngestArgs& a, PoolLds& P, int 
   const int m = a.m;
   if (w < m) {
     const int64_t p = j * m + w;
-    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
-    const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
+    const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate, w);
+    const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv, w);
     P.x[0][w][c] = (double)bf16_to_f32(g[c]) + (double)a.bias[w * kHeadDim + c];
     P.x[1][w][c] = (double)bf16_to_f32(g[kNope + c]) + (double)a.bias[w * kHeadDim + kNope + c];
     P.v[0][w][c] = (double)bf16_to_f32(kv[c]);
     P.v[1][w][c] = rope_channel(kv, c, p, a.inv_freq);
     if (CSA) {
-      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
-      const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
+      const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg, w);
+      const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk, w);
       P.x[2][w][c] = (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[w * kIdxDim + c];
       P.v[2][w][c] = (double)bf16_to_f32(ki[c]);
     }
@@ -177,11 +177,11 @@ __global__ __launch_bounds__(64 * kLongWaves) void compress_long_kernel(IngestAr
       if (i < m) {
         const int64_t p = p0 + i;
         if (st < 2) {
-          const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate);
+          const uint16_t* g = token_row(a, b, len, p, a.gate, kHeadDim, kTailGate, i);
           const int col = st == 0 ? c : kNope + c;
           x[u] = (double)bf16_to_f32(g[col]) + (double)a.bias[i * kHeadDim + col];
         } else {
-          const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg);
+          const uint16_t* gi = token_row(a, b, len, p, a.ig, kIdxDim, kTailIg, i);
           x[u] = (double)bf16_to_f32(gi[c]) + (double)a.idx_bias[i * kIdxDim + c];
         }
         mu = fmax(mu, x[u]);
@@ -199,7 +199,8 @@ __global__ __launch_bounds__(64 * kLongWaves) void compress_long_kernel(IngestAr
     __syncthreads();
     if (w == 0) {
       double S = 0.0;
-      for (int i = 0; i < m; ++i) S = S + P.t[i][c];
+#pragma unroll 16
+      for (int i = 0; i < m; ++i) S = S + P.t[i][c];  // (unrolled: the LDS reads go out ahead of the adds)
       P.sum[c] = S;
     }
     __syncthreads();
@@ -211,10 +212,10 @@ __global__ __launch_bounds__(64 * kLongWaves) void compress_long_kernel(IngestAr
         const int64_t p = p0 + i;
         P.t[i][c] = P.t[i][c] / S;
         if (st < 2) {
-          const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv);
+          const uint16_t* kv = token_row(a, b, len, p, a.kv, kHeadDim, kTailKv, i);
           P.v[i][c] = st == 0 ? (double)bf16_to_f32(kv[c]) : rope_channel(kv, c, p, a.inv_freq);
         } else {
-          const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk);
+          const uint16_t* ki = token_row(a, b, len, p, a.ik, kIdxDim, kTailIk, i);
           P.v[i][c] = (double)bf16_to_f32(ki[c]);
         }
       }
@@ -222,6 +223,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void compress_long_kernel(IngestAr
     __syncthreads();
     if (w == 0) {
       double acc = 0.0;
+#pragma unroll 16
       for (int i = 0; i < m; ++i) acc = fma(P.t[i][c], P.v[i][c], acc);
       y[st] = acc;
     }
