@@ -313,9 +313,12 @@ def attn_bytes(layer, B, t):
     return B * ((n + w) * 196 + layer.n_heads * 128 * 2 * 2)
 
 
+SPIN_CYCLES = 1.2e6  # GPU cycles of pre-region spin per timed step and layer
+
+
 def total_spin_ms_estimate(K, n_layers):
-    """Lower estimate of the pre-region spin in ms (6e5 * max(20, K) * n_layers cycles at <= 2.4 GHz)."""
-    return 6.0e5 * max(20, K) * n_layers / 2.4e9 * 1e3
+    """Lower estimate of the pre-region spin in ms (SPIN_CYCLES * max(20, K) * n_layers cycles at <= 2.4 GHz)."""
+    return SPIN_CYCLES * max(20, K) * n_layers / 2.4e9 * 1e3
 
 
 def src_sha(path):
@@ -637,8 +640,9 @@ def main():
         # host as long as this stays below the GPU's time per step
         log(f"host enqueue per step in the warm-up: {warm_host_us:.1f} us")
         # keep the GPU busy while the host enqueues the whole timed region, so no step waits on the host
-        # (about 0.25 ms of spin per step and layer: several times the host's enqueue cost)
-        torch.cuda._sleep(int(6.0e5 * max(20, K) * len(layers)))
+        # (about 0.5 ms of spin per step and layer: several times the host's enqueue cost, also under a
+        # kernel-trace profiler, which slows each launch's enqueue)
+        torch.cuda._sleep(int(SPIN_CYCLES * max(20, K) * len(layers)))
         h0 = time.perf_counter()
         rec(ev_begin)
         run_steps(range(W, S), True)
