@@ -33,6 +33,29 @@ struct SelectLds {
   uint64_t sel_thresh;
 };
 
+// One step of an inclusive prefix min (lo) / max (hi) of 64-bit values over the wave, through DPP on the
+// two 32-bit halves; lanes the move does not reach keep the neutral value (all ones for min, 0 for max)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void minmax_step(uint64_t& lo, uint64_t& hi) {
+  const uint32_t l0 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)lo, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t l1 = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(lo >> 32), CTRL, ROW_MASK, 0xf, false);
+  const uint32_t h0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)hi, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t h1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(hi >> 32), CTRL, ROW_MASK, 0xf, false);
+  const uint64_t ol = ((uint64_t)l1 << 32) | l0, oh = ((uint64_t)h1 << 32) | h0;
+  lo = ol < lo ? ol : lo;
+  hi = oh > hi ? oh : hi;
+}
+
+// the wave's minimum and maximum end in lane 63 (the steps of wave_incl_scan)
+__device__ __forceinline__ void wave_minmax_u64(uint64_t& lo, uint64_t& hi) {
+  minmax_step<0x111, 0xf>(lo, hi);  // row_shr:1
+  minmax_step<0x112, 0xf>(lo, hi);  // row_shr:2
+  minmax_step<0x114, 0xf>(lo, hi);  // row_shr:4
+  minmax_step<0x118, 0xf>(lo, hi);  // row_shr:8
+  minmax_step<0x142, 0xa>(lo, hi);  // row_bcast:15 -> rows 1, 3
+  minmax_step<0x143, 0xc>(lo, hi);  // row_bcast:31 -> rows 2, 3
+}
+
 // exclusive prefix sum over the 512 threads of the workgroup (thread order); every thread calls it
 __device__ __forceinline__ uint32_t excl_scan_512(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -75,6 +98,10 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
       if (r < per_lane) spec[r] = cand[(size_t)my_seg * seg_sz + my_sub + r * lanes_per_seg];
   }
   if (tid == 0) S.flat_needed = 0u;
+  // the first radix pass's bins and the small-bin state, cleared now (the barriers below order them)
+  for (int i = tid; i < kRadixBins; i += 512) hist[i] = 0u;
+  if (tid == 0) S.small_n = 0u;
+  if (tid < 64) S.small[tid] = 0ull;  // unused slots rank below every element
   for (int g0 = 0; g0 < G2_q; g0 += 512) {
     const int gi = g0 + tid;
     const uint32_t c = gi < G2_q ? q_seg(a, q)[gi] : 0u;
@@ -137,13 +164,8 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
       hi = e > hi ? e : hi;
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
-    lo = l2 < lo ? l2 : lo;
-    hi = h2 > hi ? h2 : hi;
-  }
-  if (lane == 0) {
+  wave_minmax_u64(lo, hi);
+  if (lane == 63) {
     S.red_lo[wave] = lo;
     S.red_hi[wave] = hi;
   }
@@ -168,8 +190,6 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
     for (int shift = hb - (kRadixBits - 1); shift > -kRadixBits; shift -= kRadixBits) {
       const int sh = shift < 0 ? 0 : shift;  // the last digit may be narrower
       const uint64_t dmask = shift < 0 ? ((1ull << (shift + kRadixBits)) - 1ull) : (uint64_t)(kRadixBins - 1);
-      for (int i = tid; i < kRadixBins; i += 512) hist[i] = 0u;
-      __syncthreads();
       for (int64_t i = tid; i < n; i += 512) {
         const uint64_t e = elem(i);
         if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
@@ -180,6 +200,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         h4[j] = hist[kRadixBins - 1 - 4 * tid - j];
+        hist[kRadixBins - 1 - 4 * tid - j] = 0u;  // cleared for the next pass (its adds follow two barriers)
         c4 += h4[j];
       }
       const uint32_t excl = excl_scan_512(c4, wsum);
@@ -205,9 +226,6 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
       if (S.sel_count <= 64) {
         // a small boundary bin: gather its elements and find the need-th largest by direct ranking
         // (keys are unique, so exactly one element has need-1 larger ones) instead of another pass
-        if (tid == 0) S.small_n = 0u;
-        if (tid < 64) S.small[tid] = 0ull;  // unused slots rank below every element
-        __syncthreads();
         for (int64_t i = tid; i < n; i += 512) {
           const uint64_t e = elem(i);
           if ((e & mask) == prefix) S.small[atomicAdd(&S.small_n, 1u)] = e;
