@@ -231,6 +231,23 @@ def test_selection_with_a_crowded_segment():
         assert w["scores_checked"] > 0
 
 
+@pytest.mark.parametrize("kind,m", [("csa", 8), ("csa", 5), ("hca", 20)])
+def test_pooling_of_longer_and_odd_blocks(kind, m):
+    """Blocks of more than 4 tokens pool in eight waves (every eighth position each, the in-order sums
+    by wave 0 over LDS): CSA with m = 8 and 5 (the indexer stream too) and HCA with m = 20 (positions
+    not a multiple of the waves), ingested in ragged chunks, then decode steps that complete blocks.
+    Cache bytes and decode queries against the oracle."""
+    if kind == "csa":
+        layer = configs.Layer("csa", m, n_heads=16, window=64, idx_heads=4, topk=32)
+    else:
+        layer = configs.Layer("hca", m, n_heads=16, window=64)
+    run = LayerRun(layer, B=2, max_ctx=3000, ring=64)
+    _ingest(run, [1000, 13, 7, 977])
+    worst, oc = _decode(run, 2 * m + 1, run.len + 2 * m + 1)
+    compare_cache(run, oc)
+    print(kind, m, worst)
+
+
 def test_ingest_chunking_invariance():
     """The same token stream ingested token by token, in 7s, or at once: identical cache bytes."""
     layer = configs.Layer("csa", 4, n_heads=8, window=128, idx_heads=4, topk=64)
