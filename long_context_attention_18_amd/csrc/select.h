@@ -102,7 +102,18 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
   for (int i = tid; i < kRadixBins; i += 512) hist[i] = 0u;
   if (tid == 0) S.small_n = 0u;
   if (tid < 64) S.small[tid] = 0ull;  // unused slots rank below every element
-  for (int g0 = 0; g0 < G2_q; g0 += 512) {
+  if (G2_q <= 64) {
+    // one wave holds every segment count: its scan needs no workgroup barrier before the offsets
+    if (wave == 0) {
+      const uint32_t c = lane < G2_q ? q_seg(a, q)[lane] : 0u;
+      const uint32_t incl = wave_incl_scan(c);
+      if (lane < G2_q) seg_off[lane] = incl - c;
+      if (lane == 63) seg_off[G2_q] = incl;
+      if (c > covered) S.flat_needed = 1u;
+    }
+    __syncthreads();
+  }
+  for (int g0 = 0; G2_q > 64 && g0 < G2_q; g0 += 512) {
     const int gi = g0 + tid;
     const uint32_t c = gi < G2_q ? q_seg(a, q)[gi] : 0u;
     const uint32_t incl = wave_incl_scan(c);
