@@ -154,6 +154,7 @@ struct ScoreLds {
   uint32_t flag_blk[kScoreWaves][kScoreIters * 32];  // per wave: blocks to rescore exactly (offset in chunk)
   uint32_t n_flag[kScoreWaves];
   uint32_t wmax[kScoreWaves];
+  uint32_t wcnt[kScoreWaves];  // per wave: its keys in the chunk's top bins
   uint32_t range;
   int lo;
 };
@@ -350,9 +351,14 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
 // The workgroup's maximum key (all threads get it); `m` is this lane's
 __device__ __forceinline__ uint32_t wg_max_key(ScoreLds& S, uint32_t m) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-  if (lane == 0) S.wmax[wave] = m;
+  // inclusive prefix maximum through DPP (the steps of wave_incl_scan): lane 63 ends with the wave's
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xf, 0xf, false));  // row_shr:1
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xf, 0xf, false));  // row_shr:2
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xf, 0xf, false));  // row_shr:4
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xf, 0xf, false));  // row_shr:8
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  if (lane == 63) S.wmax[wave] = m;
   __syncthreads();
   uint32_t kmax = 0;
 #pragma unroll
@@ -395,7 +401,6 @@ __device__ __forceinline__ void hist_publish(const ScoreArgs& a, ScoreLds& S, in
   }
 }
 
-// The query's loads (its MX-FP4 slice for quantise_query, the head weights) into Q / qraw
 // the query's head weights (0 for heads >= H_I)
 __device__ __forceinline__ void load_weights(const ScoreArgs& a, int b, int tq, ScoreQuery& Q) {
   Q.wq = a.w + ((size_t)b * a.Tq + tq) * a.HI;
@@ -406,6 +411,7 @@ __device__ __forceinline__ void load_weights(const ScoreArgs& a, int b, int tq, 
   }
 }
 
+// The query's loads (its MX-FP4 slice for quantise_query, the head weights) into Q / qraw
 __device__ __forceinline__ uint4 load_query(const ScoreArgs& a, int b, int tq, ScoreQuery& Q) {
   const int lane = threadIdx.x & 63;
   const int qh = lane >> 3, qpart = lane & 7;
@@ -468,21 +474,23 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   const uint32_t kmax = wg_max_key(S, m);
   const int top_bin = (int)(kmax >> 20);
   const int low_bin = top_bin >= 16 ? top_bin - 16 : 0;
+  uint32_t in_range = 0;  // this lane's keys in bins low_bin..top_bin
 #pragma unroll
   for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
     const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
-    if (key != 0 && (int)(key >> 20) >= low_bin) atomicAdd(&S.hist[key >> 20], 1u);
+    if (key != 0 && (int)(key >> 20) >= low_bin) {
+      atomicAdd(&S.hist[key >> 20], 1u);
+      ++in_range;
+    }
   }
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t v = (lane <= top_bin - low_bin) ? S.hist[low_bin + lane] : 0u;
+  in_range = wave_incl_scan(in_range);  // lane 63: the wave's count
+  if (lane == 63) S.wcnt[wave] = in_range;
+  __syncthreads();  // the histogram adds and the counts are visible
+  uint32_t range = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-    if (lane == 0) S.range = v;
-  }
-  __syncthreads();
+  for (int w = 0; w < kScoreWaves; ++w) range += S.wcnt[w];
   int lo = low_bin;
-  if (S.range < (uint32_t)a.cmin && low_bin > 0) {
+  if (range < (uint32_t)a.cmin && low_bin > 0) {
     // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
 #pragma unroll
     for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
