@@ -73,6 +73,8 @@ def parse_args():
     p.add_argument("--workload", default="csa_decode_1m", choices=sorted(WORKLOAD_BY_NAME))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--oracle-queries", type=int, default=4, help="decode queries in the CPU-baseline sample")
+    p.add_argument("--no-parallel-oracle", action="store_true",
+                   help="time the oracle on one thread only (no all-threads timing)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 256 MiB device copy first (reference kernel for HBM counters)")
     p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
@@ -336,13 +338,17 @@ def load_traffic(kernel, workload, src):
     return d.get("bytes_per_launch")
 
 
-def oracle_sample(layers, wl, first_step, n_queries, threads):
-    """Oracle on sequence 0 of the first layer: cache build (not timed as decode), then n decode queries timed."""
+def oracle_sample(layers, wl, first_step, n_queries, threads, n_parallel=0):
+    """Oracle on sequence 0 of the first layer: cache build (not timed as decode), then n decode queries timed
+    on one thread; then, when n_parallel > 0, the first n_parallel decode queries again over `threads` host
+    threads (the C oracle releases the interpreter lock), timed as a whole."""
     import numpy as np
     import oracle as O
     L = layers[0]
     lay = L.layer
-    t_last = wl.context + first_step + n_queries - 1
+    n_steps = len(L.step_q_host["q"])
+    n_parallel = min(n_parallel, n_steps - first_step)
+    t_last = wl.context + first_step + max(n_queries, n_parallel) - 1
     upto = t_last + 1
     t0 = time.perf_counter()
     st = L.streams[0]
@@ -376,7 +382,18 @@ def oracle_sample(layers, wl, first_step, n_queries, threads):
                           d1 if lay.csa else None, win, win_pos0=lo)
         results.append((s, t, r))
     dec_s = time.perf_counter() - t0
-    return results, dec_s, build_s, nb
+    par = None
+    if n_parallel > 0:
+        def one(s):
+            t = wl.context + s
+            qh = {k: v[s, 0, 0] for k, v in L.step_q_host.items()}
+            return O.layer_query(lay.kind, lay.m, lay.topk, lay.window, t, qh["q"], qh.get("qI"), qh.get("w"), d1,
+                                 d1 if lay.csa else None, win, win_pos0=lo)
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(first_step, first_step + n_parallel)))
+        par = (n_parallel, time.perf_counter() - t0)
+    return results, dec_s, build_s, nb, par
 
 
 def prefill_bench(args, wl):
@@ -498,6 +515,7 @@ def prefill_bench(args, wl):
         parity["ok"] = parity["topk_exact"] and parity["max_rel_l2"] <= 1e-2 and parity["max_abs"] <= 2e-2
         result["cpu_baseline"] = {
             "value": round(parity["queries"] / t_or, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
             "sample": f"{parity['queries']} prefill queries (positions {C // 2}, {C - 1}, {last * C + C // 2}, "
                       f"{total - 1}) through the plain C oracle (scores, top-k, attention), single thread, "
                       f"{t_or:.2f} s; its cache build is not counted"}
@@ -506,6 +524,9 @@ def prefill_bench(args, wl):
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    if "parity_sample" in result and not result["parity_sample"]["ok"]:
+        log("parity sample FAILED: the GPU results differ from the oracle's beyond the bar")
+        return 3
     return 0
 
 
@@ -717,7 +738,8 @@ def main():
 
     if n_check:
         log("oracle sample (sequence 0) ...")
-        res, dec_s, build_s, nb = oracle_sample(layers, wl, W, n_check, args.threads)
+        n_par = 0 if args.no_parallel_oracle else max(n_check, args.threads)
+        res, dec_s, build_s, nb, par = oracle_sample(layers, wl, W, n_check, args.threads, n_par)
         L = layers[0]
         parity = {"queries": len(res), "topk_exact": True, "max_rel_l2": 0.0, "max_abs": 0.0}
         for s, t, r in res:
@@ -730,19 +752,34 @@ def main():
                 tk = L.kept[s]["topk"][0, 0].cpu().numpy()
                 parity["topk_exact"] &= bool(np.array_equal(tk, r["topk"]))
         parity["ok"] = parity["topk_exact"] and parity["max_rel_l2"] <= 1e-2 and parity["max_abs"] <= 2e-2
-        result["cpu_baseline"] = {
-            "value": round(len(res) / dec_s, 4), "unit": "query-tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(res)} decode queries of sequence 0 of layer 0 ({L.layer.kind.upper()}) at context "
-                      f"{wl.context}-{wl.context + len(res) - 1} ({nb} compressed blocks) through the plain C "
-                      f"oracle ({'scores, top-k, ' if L.csa else ''}attention), single thread, {dec_s:.2f} s; "
-                      f"its cache build for that "
-                      f"sequence ({build_s:.1f} s on {args.threads} threads) is not counted"}
+        what = (f"of sequence 0 of layer 0 ({L.layer.kind.upper()}) from context {wl.context} on ({nb} compressed "
+                f"blocks) through the plain C oracle ({'scores, top-k, ' if L.csa else ''}attention)")
+        single = {"value": round(len(res) / dec_s, 4), "queries": len(res), "seconds": round(dec_s, 3)}
+        if par:
+            n_p, par_s = par
+            result["cpu_baseline"] = {
+                "value": round(n_p / par_s, 4), "unit": "query-tok/s", "cores": args.threads, "kind": "oracle",
+                "host_cpus": os.cpu_count(), "single_thread": single,
+                "sample": f"{n_p} decode queries {what} on {args.threads} host threads, {par_s:.2f} s (and "
+                          f"{len(res)} of them on one thread, {dec_s:.2f} s: single_thread); the oracle's cache "
+                          f"build for that sequence ({build_s:.1f} s) is not counted"}
+        else:
+            result["cpu_baseline"] = {
+                "value": single["value"], "unit": "query-tok/s", "cores": 1, "kind": "oracle",
+                "host_cpus": os.cpu_count(),
+                "sample": f"{len(res)} decode queries {what}, single thread, {dec_s:.2f} s; the oracle's cache "
+                          f"build for that sequence ({build_s:.1f} s on {args.threads} threads) is not counted"}
         result["parity_sample"] = parity
-        log(f"oracle: {dec_s:.2f} s for {len(res)} queries; parity {parity}")
+        log(f"oracle: {dec_s:.2f} s for {len(res)} queries on one thread"
+            + (f", {par[1]:.2f} s for {par[0]} on {args.threads} threads" if par else "") + f"; parity {parity}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    if n_check and not result["parity_sample"]["ok"]:
+        log("parity sample FAILED: the GPU results differ from the oracle's beyond the bar")
+        return 3
+    return 0
 
 
 if __name__ == "__main__":
-    main()
+    sys.exit(main())

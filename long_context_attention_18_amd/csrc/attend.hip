@@ -352,13 +352,23 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
       for (int i = tid; i < kHistBins; i += 512) q_hist(sa, q)[i] = 0u;
     K.n_list = (int)select_query(sa, q, N, S.u.sel, S.list);
   }
-  if (MODE == kAttendDense && args.app_units > 0 && split == 0) {
-    // The step's append, in this launch: the window entries of the new tokens, which this workgroup's
-    // window slots read (every split-0 workgroup of the sequence writes them, the same bytes, then reads
-    // them back after the fence and barrier below), and the tail copies (head group 0 only; nothing here
-    // reads the tail). One wave per unit.
+  // this workgroup: key slots [s_begin, s_end) of its split (the window's slots first)
+  const int n_keys = K.n_win + K.n_list;
+  const int splits = args.splits;
+  const int per_split = ((n_keys + splits * 16 - 1) / (splits * 16)) * 16;
+  const int s_begin = split * per_split;
+  const int s_end = min(s_begin + per_split, n_keys);
+  if (MODE == kAttendDense && args.app_units > 0) {
+    // The step's append, in this launch: the window entries of the new tokens, which the newest window
+    // slots read. Every workgroup whose slot range reaches into the window writes all of its sequence's
+    // new entries (the same bytes from each; a ring slot holds nothing else any query of the call
+    // reads) and reads them back after the fence and barrier below, so no workgroup depends on
+    // another's writes. The tail copies go to head group 0 of split 0 (nothing here reads the tail).
+    // One wave per unit.
+    const bool reads_window = s_begin < K.n_win;
+    const bool writes_tail = hg == 0 && split == 0;
     for (int unit = wave; unit < args.app_units; unit += kWaves)
-      if (unit < args.app.n_win || hg == 0) append_unit<false>(args.app, b, unit, lane);
+      if (unit < args.app.n_win ? reads_window : writes_tail) append_unit<false>(args.app, b, unit, lane);
     __threadfence_block();
   }
   __syncthreads();
@@ -406,13 +416,7 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
     voff[h] = (16 * (kk & 1) + 4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
   }
 
-  // this workgroup: key slots [s_begin, s_end) of its split; wave w: [s_begin + w * per, + per), in rounds
-  // of up to kRound chunks
-  const int n_keys = K.n_win + K.n_list;
-  const int splits = args.splits;
-  const int per_split = ((n_keys + splits * 16 - 1) / (splits * 16)) * 16;
-  const int s_begin = split * per_split;
-  const int s_end = min(s_begin + per_split, n_keys);
+  // wave w: key slots [s_begin + w * per, + per) of the split, in rounds of up to kRound chunks
   const int per = ((per_split + kWaves * 16 - 1) / (kWaves * 16)) * 16;
   const int w_begin = s_begin + wave * per;
   const int w_end = min(w_begin + per, s_end);

@@ -205,7 +205,7 @@ void lcao_rope_rotate(double* x /* HEAD_DIM, in/out */, int64_t pos) {
 
 /* ------------------------------------------------------------------ */
 /* Softmax-gated pooling with a learned positional bias (CSA paragraph */
-/* of the molayo1419.me page; Figure 3 "every 4 tokens -> one entry";   */
+/* of the molayo1419.me page; Figure 3: m = 4 tokens per entry;        */
 /* HCA paragraph / Figure 4 for 128).  Reading: per-channel gates,      */
 /* bias[i][c] per position-in-block and channel, non-overlapping        */
 /* blocks.  For each channel c:                                          */

@@ -9,6 +9,9 @@ oracle's fp64 result.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 import oracle as O
@@ -20,6 +23,9 @@ MAX_ABS = 2e-2
 
 # queries per call from which the indexer's multi-chunk and query-tile paths apply
 MANY_QUERIES = 512
+
+# host threads for input generation and the oracle's long-context cache builds (the GPU machine's CPU share)
+THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def to_dev(a: np.ndarray):
@@ -169,14 +175,57 @@ class LayerRun:
         self.last_scores = self.dev.index_scores(T) if self.len // self.m > self.layer.topk else None
         return qin, from_dev(topk), from_dev(out, np.uint16), from_dev(lse)
 
+    def fill(self, total, chunk=16384):
+        """Ingest `total` more tokens per sequence through compress + append, in chunks, each chunk's
+        tokens generated by a thread pool (long contexts: millions of tokens)."""
+        import torch
+        end = self.len + total
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            while self.len < end:
+                T = min(chunk, end - self.len)
+                parts = list(ex.map(lambda b: self.tokens(b, self.len, T), range(self.B)))
+                d = {k: to_dev(np.stack([p[k] for p in parts])) for k in parts[0]}
+                if self.swa:
+                    self.dev.append(d["kv"], None)
+                elif self.csa:
+                    self.dev.compress(d["kv"], d["gate"], self.bias_dev["bias"], d["ik"], d["ig"],
+                                      self.bias_dev["idx_bias"])
+                    self.dev.append(d["kv"], d["gate"], d["ik"], d["ig"])
+                else:
+                    self.dev.compress(d["kv"], d["gate"], self.bias_dev["bias"])
+                    self.dev.append(d["kv"], d["gate"])
+                self.len += T
+                del d
+                torch.cuda.synchronize()
+
     # ---------------------------------------------------------------- oracle side
-    def oracle_caches(self, b, upto):
-        tok = self.tokens(b, 0, upto)
+    def oracle_caches(self, b, upto, win_from=0):
+        """The oracle's entries of sequence b for positions < upto: compressed blocks (and indexer keys)
+        and the per-token window entries of positions win_from.. (win["pos0"] = win_from). Long contexts
+        are generated and compressed by a thread pool over position / block ranges."""
+        sub = 65536
+        if upto <= sub:
+            tok = self.tokens(b, 0, upto)
+        else:
+            with cf.ThreadPoolExecutor(THREADS) as ex:
+                parts = list(ex.map(lambda p: self.tokens(b, p, min(sub, upto - p)), range(0, upto, sub)))
+            tok = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+        win = O.window_entries(tok["kv"][win_from:upto], win_from)
+        win["pos0"] = win_from
         if self.swa:
-            return None, O.window_entries(tok["kv"], 0)
-        d1 = O.compress(self.m, tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"), 0, self.bias["bias"],
-                        self.bias.get("idx_bias"), 0, upto // self.m)
-        win = O.window_entries(tok["kv"], 0)
+            return None, win
+        nb = upto // self.m
+        per = max(1024, (nb + THREADS - 1) // THREADS)
+
+        def comp(j0):
+            return O.compress(self.m, tok["kv"], tok["gate"], tok.get("ik"), tok.get("ig"), 0, self.bias["bias"],
+                              self.bias.get("idx_bias"), j0, min(nb, j0 + per))
+
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            cparts = list(ex.map(comp, range(0, nb, per)))
+        if not cparts:
+            cparts = [comp(0)]
+        d1 = {k: np.concatenate([p[k] for p in cparts]) for k in cparts[0]}
         return d1, win
 
 
@@ -198,12 +247,13 @@ def _compare_blocks(run, v, b, d1, nb, report):
         assert np.array_equal(isc, d1["idx_scales"][:nb]), f"seq {b}: E8M0 bytes differ"
 
 
-def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positions=None, lens=None):
+def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positions=None, lens=None, seqs=None):
     """Bit-exact block entries / indexer keys; window slots for the last R positions (or the last
-    window_positions of them). lens: each sequence's own length (ragged batches; default run.len)."""
+    window_positions of them). lens: each sequence's own length (ragged batches; default run.len).
+    seqs: the sequences to compare (default all; oracle_by_seq may then be a dict over them)."""
     v = run.dev.views()
     report = {"rope_ulp1": 0, "rope_total": 0}
-    for b in range(run.B):
+    for b in (range(run.B) if seqs is None else seqs):
         L = run.len if lens is None else int(lens[b])
         nb = 0 if run.swa else L // run.m
         d1, win = oracle_by_seq[b]
@@ -219,9 +269,11 @@ def compare_cache(run: LayerRun, oracle_by_seq, check_window=True, window_positi
             wc = from_dev(v["win_codes"][b])[slots]
             ws = from_dev(v["win_scale"][b])[slots]
             wr = from_dev(v["win_rope"][b], np.uint16)[slots]
-            assert np.array_equal(wc, win["nope"][lo:L]), f"seq {b}: window FP8 codes differ"
-            assert np.array_equal(ws.view(np.uint32), win["scale"][lo:L].view(np.uint32))
-            assert bf16_ulp_diff(wr, win["rope"][lo:L]).max(initial=0) <= 1
+            p0 = win.get("pos0", 0)
+            assert lo >= p0, "the oracle's window entries start after the positions compared"
+            assert np.array_equal(wc, win["nope"][lo - p0:L - p0]), f"seq {b}: window FP8 codes differ"
+            assert np.array_equal(ws.view(np.uint32), win["scale"][lo - p0:L - p0].view(np.uint32))
+            assert bf16_ulp_diff(wr, win["rope"][lo - p0:L - p0]).max(initial=0) <= 1
     return report
 
 
@@ -232,17 +284,19 @@ def attn_error(got_bf16: np.ndarray, ref_f64: np.ndarray):
     return rel, mab
 
 
-def check_queries(run: LayerRun, oracle_by_seq, qin, topk, out, lse, positions, sample=None):
-    """Oracle layer_query for each (seq, query) and the comparison bar."""
+def check_queries(run: LayerRun, oracle_by_seq, qin, topk, out, lse, positions, sample=None, seqs=None):
+    """Oracle layer_query for each (seq, query) and the comparison bar. oracle_by_seq: a list over all
+    sequences, or a dict {seq: caches} for the sampled sequences `seqs` (default: every sequence)."""
     worst = {"rel": 0.0, "abs": 0.0, "lse": 0.0, "scores_checked": 0}
     idx = range(len(positions)) if sample is None else sample
-    for b in range(run.B):
+    for b in (range(run.B) if seqs is None else seqs):
         d1, win = oracle_by_seq[b]
         for i in idx:
             t = positions[i]
             r = O.layer_query(run.layer.kind, run.m, run.layer.topk, run.layer.window, t, qin["q"][b, i],
                               qin.get("qI", [None] * run.B)[b][i] if run.csa else None,
-                              qin["w"][b, i] if run.csa else None, d1, d1 if run.csa else None, win)
+                              qin["w"][b, i] if run.csa else None, d1, d1 if run.csa else None, win,
+                              win_pos0=win.get("pos0", 0))
             if run.csa and run.last_scores is not None:
                 n = len(r["scores"])
                 gs = run.last_scores[b, i, :n]
