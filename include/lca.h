@@ -301,6 +301,27 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
                         uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
                         void* score_ev_begin, void* score_ev_end);
 
+/* lca_csa_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same launches and results as lca_csa_step (bit for bit), with the
+ * workspace taken from a 32 MiB device array inside the library instead of
+ * the caller's: one array per GPU the library runs on, held until the
+ * process ends. The call allocates nothing; the caller still passes every
+ * input and output. Its first call on a device (and any call whose
+ * workspace layout -- batch, T, max_ctx, layer -- differs from the previous
+ * call's on that device) first clears the bytes it uses with a fill kernel
+ * on `stream`. Limits: lca_workspace_bytes(desc, B, T, max_ctx) must not
+ * exceed 32 MiB (else LCA_ERR_WORKSPACE, nothing launched): a 1M-token
+ * context at B = 4 and T = 1 fits. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. qI_dev and w_dev are
+ * required; no timing events. */
+lca_status lca_csa_step_noalloc(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                                const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                                const float* idx_bias_dev, int32_t T, const uint16_t* qI_dev, const float* w_dev,
+                                const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                                void* stream);
+
 /* ---- persistence: snapshot and restore of one sequence's state ----------
  * The KV-cache section of velog.io "DeepSeek V4 논문 정리" keeps compressed KV
  * on disk for requests that share a prefix. A snapshot is a contiguous

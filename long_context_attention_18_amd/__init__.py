@@ -85,6 +85,7 @@ _SIGNATURES = {
     "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
                             _VP, _VP]),
+    "lca_csa_step_noalloc": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "lca_hca_step": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_swa_step": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_snapshot_layout": (_I32, [_CP, _SP]),
@@ -228,6 +229,12 @@ def lca_csa_step(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out
                                                _ptr(bias), _ptr(idx_bias), T, _ptr(qI), _ptr(w), _ptr(q), _ptr(topk),
                                                _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream),
                                                score_events[0], score_events[1]))
+
+
+def lca_csa_step_noalloc(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, stream=None):
+    _check("lca_csa_step_noalloc", lib().lca_csa_step_noalloc(
+        ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(ik), _ptr(ig), _ptr(bias), _ptr(idx_bias), T, _ptr(qI),
+        _ptr(w), _ptr(q), _ptr(topk), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def lca_hca_step(cache, kv, gate, bias, T, q, out, lse, ws, ws_bytes, stream=None):

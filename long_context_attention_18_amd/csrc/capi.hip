@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lca.h"
 #include "kernels.h"
@@ -586,22 +587,35 @@ lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq
                         stream);
 }
 
-lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
-                        const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
-                        const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
-                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
-                        void* score_ev_begin, void* score_ev_end) {
-  // every check first, so a rejected call leaves the cache as it was
+}  // extern "C"
+
+namespace {
+
+// The shape checks of a CSA decode step (every one before any launch).
+lca_status csa_step_check(const lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                          const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                          const float* idx_bias_dev, int32_t T) {
   if (!cache_ok(cache) || !kv_dev || !gate_dev || !ik_dev || !ig_dev || !bias_dev || !idx_bias_dev)
     return LCA_ERR_NULL;
   if (cache->desc.kind != LCA_KIND_CSA || !cache->idx_codes_dev) return LCA_ERR_UNSUPPORTED;
   if (T < 1 || (int64_t)cache->batch * T > kAttendMaxQueries) return LCA_ERR_SHAPE;
   if (cache->pending != 0 || cache->ragged) return LCA_ERR_ORDER;
   if (cache->len + T > cache->max_ctx) return LCA_ERR_CAPACITY;
+  return LCA_OK;
+}
+
+lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
+                         const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
+                         const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
+                         uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
+                         void* score_ev_begin, void* score_ev_end) {
+  // every check first, so a rejected call leaves the cache as it was
+  lca_status st = csa_step_check(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T);
+  if (st != LCA_OK) return st;
   lca_cache after = *cache;  // the cache once the T tokens are in: what the query kernels see
   after.len = cache->len + T;
   AttendArgs args{};
-  lca_status st = score_args(&after, qI_dev, w_dev, true, T, topk_dev, false, ws_dev, ws_bytes, &args.s);
+  st = score_args(&after, qI_dev, w_dev, true, T, topk_dev, false, ws_dev, ws_bytes, &args.s);
   if (st != LCA_OK) return st;
   st = attn_args(&after, LCA_KIND_CSA, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
   if (st != LCA_OK) return st;
@@ -634,6 +648,77 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
   cache->len = end;
   cache->pending = 0;
   return LCA_OK;
+}
+
+// ---- the CSA decode step without a caller workspace: for callers that cannot allocate (code under HIP
+// graph capture, tight serving loops). Its workspace is this file-scope device array, one per GPU the
+// library runs on, held until the process ends. Host code never uses the array's name as an address
+// (on the host it is only a stand-in for the symbol): the device address comes from hipGetSymbolAddress,
+// once per device, and every kernel gets that pointer.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+struct StaticScratch {
+  std::mutex mu;
+  void* ptr = nullptr;        // the device's address of `scratch`
+  uint64_t layout_key = 0;    // workspace layout of the last call on the device (0: none yet)
+};
+StaticScratch g_scratch[64];
+
+// The device address of `scratch` on the current device, zeroed at its first use; a call whose workspace
+// layout differs from the previous call's re-zeroes the bytes it uses (the histograms and counters it
+// needs zero sit where the last layout kept other data). Both fills are kernels on `stream`.
+lca_status static_scratch(const lca_cache* cache, int32_t T, hipStream_t stream, void** out) {
+  const WsLayout W = ws_layout(&cache->desc, cache->batch, T, cache->max_ctx);
+  if (W.total > kStaticScratchBytes) return LCA_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LCA_ERR_LAUNCH;
+  StaticScratch& S = g_scratch[dev];
+  std::lock_guard<std::mutex> lock(S.mu);
+  if (!S.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LCA_ERR_LAUNCH;
+    if (launch_fill_zero(p, kStaticScratchBytes, stream) != hipSuccess) return LCA_ERR_LAUNCH;
+    S.ptr = p;
+  }
+  const uint64_t key = ((uint64_t)W.qstride << 20) ^ ((uint64_t)W.total << 1) ^ 1u;
+  if (S.layout_key != key) {
+    if (launch_fill_zero(S.ptr, W.total, stream) != hipSuccess) return LCA_ERR_LAUNCH;
+    S.layout_key = key;
+  }
+  *out = S.ptr;
+  return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
+                        const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
+                        const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
+                        void* score_ev_begin, void* score_ev_end) {
+  return csa_step_impl(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, qI_dev, w_dev, q_dev,
+                       topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, stream, score_ev_begin, score_ev_end);
+}
+
+lca_status lca_csa_step_noalloc(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                                const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                                const float* idx_bias_dev, int32_t T, const uint16_t* qI_dev, const float* w_dev,
+                                const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                                void* stream) {
+  // the step's own checks first: a rejected call touches neither the cache nor the scratch
+  lca_status st = csa_step_check(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T);
+  if (st != LCA_OK) return st;
+  if (!qI_dev || !w_dev) return LCA_ERR_NULL;
+  void* ws = nullptr;
+  lca_cache after = *cache;
+  after.len = cache->len + T;
+  st = static_scratch(&after, T, (hipStream_t)stream, &ws);
+  if (st != LCA_OK) return st;
+  return csa_step_impl(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, qI_dev, w_dev, q_dev,
+                       topk_dev, out_dev, lse_dev, ws, kStaticScratchBytes, stream, nullptr, nullptr);
 }
 
 lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev,

@@ -363,3 +363,21 @@ def test_ragged_calls_checks():
     assert (info.len, info.n_blocks, info.n_win, info.n_tail) == (1001, 250, 128, 1)
     assert L.lca_ragged_snapshot(ctypes.byref(c), 0, 5000, None, 0, ctypes.byref(info), None) == -2
     assert L.lca_ragged_snapshot(ctypes.byref(c), 3, 10, P, big, ctypes.byref(info), None) == -2
+
+
+def test_noalloc_step_rejects_workspaces_beyond_its_scratch():
+    """lca_csa_step_noalloc takes its workspace from a fixed 32 MiB device array: a layout that needs more
+    (B = 64 sequences of 1M tokens) is refused with LCA_ERR_WORKSPACE before anything is launched, and its
+    shape checks are those of lca_csa_step."""
+    L = lca.lib()
+    args = (1, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, 1, None, None)
+    big = _fake_bound_cache("csa")
+    big.batch, big.max_ctx = 64, 1 << 20
+    big.max_blocks = big.max_ctx // 4
+    d = big.desc
+    assert lca.lca_workspace_bytes(d, 64, 1, 1 << 20) > 32 << 20
+    assert L.lca_csa_step_noalloc(ctypes.byref(big), *args) == -6
+    # the step's own checks come first: T = 0, a HCA cache, a missing qI
+    assert L.lca_csa_step_noalloc(ctypes.byref(big), 1, 1, 1, 1, 1, 1, 0, 1, 1, 1, None, 1, None, None) == -2
+    assert L.lca_csa_step_noalloc(ctypes.byref(_fake_bound_cache("hca")), *args) == -3
+    assert L.lca_csa_step_noalloc(ctypes.byref(big), 1, 1, 1, 1, 1, 1, 1, None, 1, 1, None, 1, None, None) == -1
