@@ -636,7 +636,7 @@ def main():
         f"{time.perf_counter() - t0:.1f} s")
 
     dom = next((L for L in layers if L.csa), layers[0])
-    dom_kernel = "score_kernel" if dom.csa else "attend_kernel"
+    dom_kernel = "index_select_kernel" if dom.csa else "attend_kernel"
     hev = HipEvents()
     mode = "prequeued"
     rec = lambda e: hev.record(e, False)

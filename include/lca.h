@@ -287,9 +287,14 @@ lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq
  * sequence go in (lca_csa_compress + lca_swa_tail_append: the blocks they
  * complete are pooled into D1/D3, their window entries and tail copies are
  * written) and their T queries attend (lca_csa_attend): same results, bit for
- * bit in the cache and the top-k lists. Three launches (four when a block
- * completes): compress, score, candidate scan with the append in the same
- * launch, selection + attention. For decode-sized calls: B * T <= 511
+ * bit in the cache and the top-k lists. Two launches (three when a block
+ * completes): compress, one launch that scores every visible block (a
+ * workgroup per 2048 blocks of each query, each keeping its best candidates)
+ * and has the last workgroup of each query to finish select its top-k (the
+ * append rides in the same launch), then the attention. (Queries seeing more
+ * than 1M blocks, or k too large for a query's chunks, take three: score,
+ * candidate scan with the append, selection + attention.) For decode-sized
+ * calls: B * T <= 511
  * (else LCA_ERR_SHAPE); ring >= T + window - 1. Inputs as for the compressor
  * and lca_csa_attend; topk_dev and lse_dev may be NULL. score_ev_begin /
  * score_ev_end, when not NULL, are hipEvent_t the call records on `stream`

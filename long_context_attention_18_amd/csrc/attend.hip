@@ -16,11 +16,11 @@
 // contiguous range of the key slots and issues the gathers of up to kRound
 // chunks at once (random reads: one memory latency per round).
 //
-// Modes: LIST (the caller's top-k list), DENSE (HCA: every visible block) and
-// SELECT (CSA: the workgroup first runs the exact top-k selection of its
-// query from the scan's candidates, select.h, into LDS -- the 4 head-group
-// workgroups of a query do it side by side, which costs no extra time in a
-// latency-bound step -- then attends over the result).
+// Modes: LIST (the caller's top-k list), LIST_WS (the list the indexer's
+// in-launch selection left in the workspace: the decode step's path), DENSE
+// (HCA: every visible block) and SELECT (CSA after a separate score call: the
+// workgroup first runs the exact top-k selection of its query from the scan's
+// candidates, select.h, into LDS, then attends over the result).
 //
 // Key slots: the window first, then the compressed entries (the softmax does
 // not depend on the order).
@@ -54,7 +54,7 @@ constexpr int kChunk = 32;     // keys per wave step: two 16-key tiles
 constexpr int kKdStride = 136;  // bf16 per key-major LDS row (128 dims + 8 pad)
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-constexpr int kRound = 4;      // chunks a wave gathers at once (VGPR budget)
+constexpr int kRound = 4;      // chunks a wave gathers at once (VGPR budget: five spill)
 
 struct AttendLds {
   union {
@@ -299,6 +299,10 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
   } else if (MODE == kAttendList) {
     K.n_list = a.k;
     K.use_list = true;
+  } else if (MODE == kAttendListWs) {
+    // the in-launch selection's list (k winners when N > k); a query that sees at most k blocks takes them all
+    K.use_list = N > a.k;
+    K.n_list = (int)(N > a.k ? (int64_t)a.k : N);
   } else {
     K.n_list = (int)(N < a.k ? N : (int64_t)a.k);
     K.use_list = do_select;
@@ -345,6 +349,10 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
       __syncthreads();
     }
     K.n_list = n;
+  }
+  if (MODE == kAttendListWs && K.use_list) {
+    const int32_t* lp = q_list(args.s, q);
+    for (int i = tid; i < a.k; i += 512) S.list[i] = lp[i];
   }
   if (do_select) {
     const ScoreArgs& sa = args.s;
@@ -427,6 +435,7 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
       case 1: attend_round<1>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
       case 2: attend_round<2>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
       case 3: attend_round<3>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
+      case 4: attend_round<4>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
       default: attend_round<kRound>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
     }
   }
@@ -503,6 +512,7 @@ hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_
   const unsigned nq = (unsigned)(B * args.t.Tq);
   const unsigned gx = (unsigned)((args.t.H + 15) / 16 * args.splits);
   if (mode == kAttendSelect) hipLaunchKernelGGL(attend_kernel<kAttendSelect>, dim3(gx, nq), dim3(512), 0, s, args);
+  else if (mode == kAttendListWs) hipLaunchKernelGGL(attend_kernel<kAttendListWs>, dim3(gx, nq), dim3(512), 0, s, args);
   else if (mode == kAttendDense) hipLaunchKernelGGL(attend_kernel<kAttendDense>, dim3(gx, nq), dim3(512), 0, s, args);
   else hipLaunchKernelGGL(attend_kernel<kAttendList>, dim3(gx, nq), dim3(512), 0, s, args);
   return hipGetLastError();

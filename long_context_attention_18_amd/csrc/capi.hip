@@ -81,7 +81,7 @@ bool sizes_ok(const lca_layer_desc* d, int32_t B, int64_t max_ctx, int32_t ring)
 // score keys, candidates), then the attention's split partials. The counters' and the per-query
 // blocks' places do not depend on a call's Tq, so what must be zero between calls stays put.
 struct WsLayout {
-  size_t cnt, qbase, qstride, off_seg, off_keys, off_cand, part, total;
+  size_t cnt, qbase, qstride, off_seg, off_keys, off_cand, off_sync, off_list, off_rec, part, total;
   int32_t G2;
 };
 
@@ -95,12 +95,17 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
     size_t q = align_up((size_t)kHistBins * 4);
-    // segment counts: kScanPerWG blocks per scan segment, kTileSeg per query-tile segment
+    // segment counts: kScanPerWG blocks per scan segment, kTileSeg per query-tile segment, kScoreChunk per
+    // in-launch-threshold segment
     const int64_t tile_blocks = max_blocks < kTileMaxBlocks ? max_blocks : kTileMaxBlocks;
-    const int64_t n_seg = std::max<int64_t>(W.G2, (tile_blocks + kTileSeg - 1) / kTileSeg);
+    const int64_t n_seg = std::max<int64_t>({(int64_t)W.G2, (tile_blocks + kTileSeg - 1) / kTileSeg,
+                                             (max_blocks + kScoreChunk - 1) / kScoreChunk});
     W.off_seg = q; q = align_up(q + (size_t)n_seg * 4);
     W.off_keys = q; q = align_up(q + (size_t)max_blocks * 4);
     W.off_cand = q; q = align_up(q + (size_t)max_blocks * 8);
+    W.off_sync = q; q = align_up(q + sizeof(uint64_t));      // the in-launch threshold's counter
+    W.off_list = q; q = align_up(q + (size_t)kMaxTopk * 4);   // its top-k list, read by the attention
+    W.off_rec = q; q = align_up(q + ((size_t)kRecHdrSlots + (size_t)n_seg * kRecMaxWords) * 8);  // its records
     W.qstride = q;
     off += nq * q;
   }
@@ -115,8 +120,9 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
 int32_t attend_splits(int32_t nq, int32_t H, int64_t n_keys) {
   const int64_t groups = (H + 15) / 16;
   const int64_t chunks = (n_keys + 31) / 32;
-  // up to 3 chunks per wave the partials, the fence and the merge cost more than the split saves
-  if (chunks <= 3 * 8) return 1;
+  // up to 3 chunks per wave the partials and the merge cost more than the split saves (and without splits
+  // a wave's chunks beyond kRound take a second round of gathers, which costs more than the merge)
+  if (chunks <= kAttendNoSplitChunks * 8) return 1;
   int64_t s = (chunks + 7) / 8;
   const int64_t cap = kAttendMaxWGs / (nq * groups);
   if (s > cap) s = cap;
@@ -349,6 +355,9 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   a.off_seg = W.off_seg;
   a.off_keys = W.off_keys;
   a.off_cand = W.off_cand;
+  a.off_sync = W.off_sync;
+  a.off_list = W.off_list;
+  a.off_rec = W.off_rec;
   a.topk = topk_dev;
   a.len = cache->len;
   a.max_blocks = cache->max_blocks;
@@ -390,6 +399,30 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
   return LCA_OK;
 }
 
+// The in-launch threshold and selection for a decode-sized call's score launch: one score workgroup per
+// chunk, every one of them counted in at its query's counter. Each workgroup's record carries its
+// candidates down to where cmin = twice its share of k plus 16 still fit, which covers the query's winners
+// unless a chunk holds far more than its share (then the last workgroup takes them from the key rows:
+// exact, slower). Records of 32 to 256 words, as cmin needs; the last workgroup reads all of them at once
+// (at most kPrefMaxLoads words per thread).
+bool use_coop(ScoreArgs* a, int64_t nq) {
+  if (a->tiles || a->chunk_step != 0) return false;
+  const int64_t nb = a->len / a->m;  // the most blocks a query of the call sees
+  const int64_t g1 = std::max<int64_t>(1, (nb + kScoreChunk - 1) / kScoreChunk);
+  const int64_t cols = a->fold_tail ? g1 - 1 : g1;
+  (void)nq;  // no workgroup waits for another: any number of them works
+  if (g1 > kMaxSegs) return false;
+  const int64_t cmin = 2 * ((a->k + cols - 1) / cols) + 16;
+  int64_t R = kRecMinWords;
+  while (R < cmin && R < kRecMaxWords) R *= 2;
+  if (R < cmin || g1 > kRecHdrSlots || g1 * R > (int64_t)kPrefMaxLoads * kScoreThreads) return false;
+  a->coop = 1;
+  a->n_cols = (int32_t)cols;
+  a->pref_slots = (int32_t)R;
+  a->cmin = (int32_t)cmin;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -416,6 +449,11 @@ lca_status lca_csa_indexer_topk(lca_cache* cache, const uint16_t* qI_dev, const 
   ScoreArgs a;
   lca_status st = score_args(cache, qI_dev, w_dev, true, Tq, topk_dev, true, ws_dev, ws_bytes, &a);
   if (st != LCA_OK) return st;
+  if (use_coop(&a, (int64_t)cache->batch * Tq)) {  // scores, bound, candidates and selection in one launch
+    ScanArgs sa{};
+    sa.a = a;
+    return launch_status(launch_index_select(sa, cache->batch, (hipStream_t)stream));
+  }
   a.tile_select = a.tiles;  // query tiles select in the score launch itself
   hipError_t e = launch_index_score(a, cache->batch, (hipStream_t)stream);
   if (e != hipSuccess) return LCA_ERR_LAUNCH;
@@ -540,6 +578,13 @@ lca_status topk_attn_impl(lca_cache* cache, const uint16_t* qI_dev, const float*
   if (st != LCA_OK) return st;
   attend_workspace(&args, cache, Tq, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
+  if (score && use_coop(&args.s, (int64_t)cache->batch * Tq)) {
+    // one launch for scores, bound, candidates and each query's selection; the attention reads the lists
+    ScanArgs sa{};
+    sa.a = args.s;
+    if (launch_index_select(sa, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    return launch_status(launch_attend(args, cache->batch, kAttendListWs, s));
+  }
   if (score) {
     hipError_t e = launch_index_score(args.s, cache->batch, s);
     if (e != hipSuccess) return LCA_ERR_LAUNCH;
@@ -631,10 +676,8 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
     ca.first = cache->len / m;
     if (launch_compress(ca, true, n_blocks, s) != hipSuccess) return LCA_ERR_LAUNCH;
   }
-  if (score_ev_begin && hipEventRecord((hipEvent_t)score_ev_begin, s) != hipSuccess) return LCA_ERR_LAUNCH;
-  if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
-  if (score_ev_end && hipEventRecord((hipEvent_t)score_ev_end, s) != hipSuccess) return LCA_ERR_LAUNCH;
-  // the append (window entries, tail) rides in the candidate-scan launch
+  // the append (window entries, tail): a row of the score launch (in-launch threshold) or of the
+  // candidate-scan launch; the attention after them reads the new window entries
   IngestArgs app = ingest_args(cache, kv_dev, gate_dev, ik_dev, ig_dev, T);
   const int64_t end = cache->len + T;
   const int64_t win_first = (end - cache->ring > cache->len) ? end - cache->ring : cache->len;
@@ -643,6 +686,23 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
   int64_t tail_first = (end / m) * m;
   if (tail_first < cache->len) tail_first = cache->len;
   const int32_t units = app.n_win + (int32_t)(end - tail_first);
+  if (use_coop(&args.s, (int64_t)cache->batch * T)) {
+    // two launches: scores + bound + candidates + selection (+ the append), then the attention
+    ScanArgs sa{};
+    sa.a = args.s;
+    sa.app = app;
+    sa.app_units = units;
+    if (score_ev_begin && hipEventRecord((hipEvent_t)score_ev_begin, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (launch_index_select(sa, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (score_ev_end && hipEventRecord((hipEvent_t)score_ev_end, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (launch_attend(args, cache->batch, kAttendListWs, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    cache->len = end;
+    cache->pending = 0;
+    return LCA_OK;
+  }
+  if (score_ev_begin && hipEventRecord((hipEvent_t)score_ev_begin, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (score_ev_end && hipEventRecord((hipEvent_t)score_ev_end, s) != hipSuccess) return LCA_ERR_LAUNCH;
   if (launch_topk_select(args.s, cache->batch, s, false, &app, units) != hipSuccess) return LCA_ERR_LAUNCH;
   if (launch_attend(args, cache->batch, kAttendSelect, s) != hipSuccess) return LCA_ERR_LAUNCH;
   cache->len = end;
@@ -1022,11 +1082,20 @@ lca_status lca_ragged_step(lca_cache* cache, int32_t T_max, const int64_t* len_h
   attend_workspace(&args, &after, T_max, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
   if (kind == LCA_KIND_CSA) {
-    // compress; score; candidate scan with the append in the same launch; selection + attention
+    // compress; then as lca_csa_step: scores + selection with the append in the same launch, then the
+    // attention -- or score, candidate scan with the append, selection + attention
     IngestArgs app;
     st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, false, &app, s);
     if (st != LCA_OK) return st;
     cache->ragged = 1;
+    if (use_coop(&args.s, (int64_t)cache->batch * T_max)) {
+      ScanArgs sa{};
+      sa.a = args.s;
+      sa.app = app;
+      sa.app_units = r.units;
+      if (launch_index_select(sa, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+      return launch_status(launch_attend(args, cache->batch, kAttendListWs, s));
+    }
     if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
     if (launch_topk_select(args.s, cache->batch, s, false, &app, r.units) != hipSuccess) return LCA_ERR_LAUNCH;
     return launch_status(launch_attend(args, cache->batch, kAttendSelect, s));

@@ -157,6 +157,12 @@ struct ScoreLds {
   uint32_t wcnt[kScoreWaves];  // per wave: its keys in the chunk's top bins
   uint32_t range;
   int lo;
+  int lo_reached;  // hist_cmin_bin found its bin
+  int coop_last;         // this workgroup is the last of its query to arrive
+  uint32_t coop_top;      // this workgroup's largest key; for the last to arrive, the query's
+  uint32_t coop_bound;    // the last to arrive: the highest record floor
+  uint32_t coop_lmin;     // the lowest record floor
+  uint32_t coop_total;    // candidates over all records
 };
 
 // A workgroup's query: its MX-FP4 operands, head weights and exactness bounds (one per workgroup)
@@ -277,11 +283,13 @@ __device__ __forceinline__ void query_operands(const ScoreLds& S, ScoreQuery& Q)
 // One chunk's scores from its loaded keys: the key of every visible block to `keys`, this lane's key
 // per tile pair to lane_keys (0 = no block); blocks outside the exactness bounds are rescored in fp64.
 // Contains workgroup barriers: every thread of the workgroup calls it.
+// keys: the query's global key row (written through); lkeys (or null): the workgroup's LDS key array,
+// indexed by the block's offset from j_begin, which gets the keys too (the in-launch threshold).
 template <bool FULL, int ITERS = kScoreIters>
 __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, const ScoreQuery& Q, const uint4 (&bvs)[ITERS],
                                             const int (&sbs)[ITERS], uint32_t* keys, const uint8_t* codes,
                                             const uint8_t* scl, int N, int j_begin, int wave_j0, int n2,
-                                            uint32_t (&lane_keys)[ITERS / 2]) {
+                                            uint32_t (&lane_keys)[ITERS / 2], uint32_t* lkeys = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int odd = (lane >> 4) & 1;
   if (lane == 0) S.n_flag[wave] = 0;  // this wave's own list: program order suffices
@@ -320,6 +328,7 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
       // written through to memory (agent scope): the next launch reads it from other XCDs, and the
       // launch's end then has no dirty lines of it to write back
       __hip_atomic_store(&keys[jb], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lkeys) lkeys[jb - j_begin] = key;
       if (bad) S.flag_blk[wave][atomicAdd(&S.n_flag[wave], 1u)] = (uint32_t)(jb - j_begin);
     }
     lane_keys[pr] = key;
@@ -334,6 +343,7 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
       const float ex = exact_block_score(codes + (size_t)jb * 32, scl[(size_t)jb * 2], scl[(size_t)jb * 2 + 1],
                                          S.qcode, S.qscale, Q.wq, a.HI);
       __hip_atomic_store(&keys[jb], order_key(ex), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lkeys) lkeys[jb - j_begin] = order_key(ex);
     }
     nf += n;
   }
@@ -343,7 +353,7 @@ __device__ __forceinline__ void score_pairs(const ScoreArgs& a, ScoreLds& S, con
 #pragma unroll
     for (int pr = 0; pr < ITERS / 2; ++pr) {
       const int jb = wave_j0 + ((odd ? 2 * pr : 2 * pr + 1)) * 32 + n2;
-      if (FULL || jb < N) lane_keys[pr] = keys[jb];
+      if (FULL || jb < N) lane_keys[pr] = lkeys ? lkeys[jb - j_begin] : keys[jb];
     }
   }
 }
@@ -371,7 +381,10 @@ __device__ __forceinline__ uint32_t wg_max_key(ScoreLds& S, uint32_t m) {
 __device__ __forceinline__ int hist_cmin_bin(ScoreLds& S, uint32_t cmin) {
   const int tid = threadIdx.x;
   constexpr int kPerT = kHistBins / kScoreThreads;  // bins per thread
-  if (tid == 0) S.lo = 0;
+  if (tid == 0) {
+    S.lo = 0;
+    S.lo_reached = 0;
+  }
   __syncthreads();
   const int hi_b = kHistBins - kPerT * tid;  // this thread: bins [hi_b - kPerT, hi_b), threads in descending order
   uint32_t cnt = 0;
@@ -385,6 +398,7 @@ __device__ __forceinline__ int hist_cmin_bin(ScoreLds& S, uint32_t cmin) {
       c += S.hist[hi_b - i];
       if (c >= cmin) {
         S.lo = hi_b - i;
+        S.lo_reached = 1;
         break;
       }
     }
@@ -423,9 +437,11 @@ __device__ __forceinline__ uint4 load_query(const ScoreArgs& a, int b, int tq, S
 
 // One score workgroup's chunk: kScoreChunk blocks from j_begin (few-query calls: every workgroup one
 // chunk). The keys' loads go out before the query is quantised.
+// lkeys (in-launch threshold): the workgroup's LDS key array -- the chunk's keys at offsets 0..2047,
+// the folded chunk's from kScoreChunk on -- which gets every key too. Returns the lowest bin published.
 template <bool FULL>
-__device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin,
-                                            int j_tail) {
+__device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin,
+                                           int j_tail, uint32_t* lkeys = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   ScoreQuery Q;
   const uint4 qraw = load_query(a, b, tq, Q);
@@ -451,13 +467,14 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
   __syncthreads();  // quantised query and bounds visible
   query_operands(S, Q);
   uint32_t lane_keys[kScoreIters / 2];
-  score_pairs<FULL>(a, S, Q, bvs, sbs, keys, codes, scl, N, j_begin, wave_j0, n2, lane_keys);
+  score_pairs<FULL>(a, S, Q, bvs, sbs, keys, codes, scl, N, j_begin, wave_j0, n2, lane_keys, lkeys);
   uint32_t tail_keys[kTailIters / 2];
 #pragma unroll
   for (int pr = 0; pr < kTailIters / 2; ++pr) tail_keys[pr] = 0u;
   if (has_tail) {
     __syncthreads();  // every wave has read the first chunk's flag lists
-    score_pairs<false, kTailIters>(a, S, Q, tvs, tsb, keys, codes, scl, N, j_tail, wave_t0, n2, tail_keys);
+    score_pairs<false, kTailIters>(a, S, Q, tvs, tsb, keys, codes, scl, N, j_tail, wave_t0, n2, tail_keys,
+                                   lkeys ? lkeys + kScoreChunk : nullptr);
   }
   // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
   // and the 16 bins below it (down to a quarter of the max), or, when those hold fewer than cmin of the
@@ -490,16 +507,38 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, ScoreLds& S, int
 #pragma unroll
   for (int w = 0; w < kScoreWaves; ++w) range += S.wcnt[w];
   int lo = low_bin;
-  if (range < (uint32_t)a.cmin && low_bin > 0) {
+  // in-launch threshold: the workgroup's candidates reach down as far as a.cmin of them fit (whole bins);
+  // the keys below the range are counted too when the range holds fewer than that
+  const uint32_t need = a.coop ? (uint32_t)a.cmin + 1u : (uint32_t)a.cmin;
+  const bool all_in = range < need && low_bin > 0;
+  if (all_in) {
     // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
 #pragma unroll
     for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
       const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
       if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&S.hist[key >> 20], 1u);
     }
-    lo = hist_cmin_bin(S, (uint32_t)a.cmin);
+    if (!a.coop) lo = hist_cmin_bin(S, (uint32_t)a.cmin);
+  }
+  if (a.coop) {
+    // the lowest bin at which the chunk's count from the top still fits cmin candidates: the bin just above
+    // the one where it first exceeds cmin (among the 17 counted bins, which hold more than cmin keys
+    // unless all_in; then over the whole histogram, or bin 0 when the chunk has no more than cmin keys)
+    if (all_in) {
+      lo = hist_cmin_bin(S, need);
+      lo = S.lo_reached ? lo + 1 : 0;
+    } else if (wave == 0) {
+      const bool in = lane <= top_bin - low_bin;
+      const uint32_t c = wave_incl_scan(in ? S.hist[top_bin - lane] : 0u);  // count of bins top_bin..top_bin-lane
+      const uint64_t over = __ballot(in && c >= need);
+      if (lane == 0) S.lo = over ? top_bin - (__ffsll((long long)over) - 1) + 1 : low_bin;
+    }
+    if (tid == 0) S.coop_top = kmax;
+    __syncthreads();
+    return all_in ? lo : S.lo;
   }
   hist_publish(a, S, q, lo, top_bin);
+  return lo;
 }
 
 // A workgroup over chunks chunk0, chunk0 + step, ... of its query (many-query calls, where one
@@ -573,6 +612,366 @@ __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a) { 
   const int j_tail = a.fold_tail && c0 == 0 ? (int)gridDim.x * kScoreChunk : -1;  // the chunk the grid leaves out
   if (j_begin + kScoreChunk <= N) score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail);
   else score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail);
+}
+
+// ---- In-launch threshold and selection (decode-sized calls) -----------------------------------------------
+//
+// No workgroup waits for another. Each score workgroup writes its keys to the query's key row and one
+// record per chunk: a header (the chunk's largest key, its floor bin lo, its candidate count) and its
+// candidates, the keys of bins >= lo in block order (zero-padded; a score's key is never 0), lo as low as
+// cmin candidates -- twice its share of k plus 16 -- still fit. Then it counts itself in at the query's
+// counter and ends. The last to arrive has every other workgroup's writes complete behind the counter: it
+// reads all records (one round of coalesced loads, kept in registers) and takes F = the highest floor.
+// Every record holds all of its keys >= F, so the candidates >= F are exactly the query's keys >= F; when
+// there are at least k of them they hold the top-k: a radix select on their 32-bit keys (LDS histograms
+// only), then the winners straight from the loaded records in block order, equal keys by lower block
+// first. Otherwise (a chunk with far more than its share of the winners), it takes the keys above a lower
+// bound from the key row in memory instead: the lowest floor, which every candidate clears, so that with k
+// candidates in all at least k keys do (else every key). Everything one workgroup writes for another goes
+// through memory at agent scope (the XCDs' L2s are not coherent), and a workgroup's writes complete before
+// it counts itself in.
+
+struct CoopLds {
+  union {
+    struct {
+      ScoreLds sc;
+      uint32_t keys[kScoreChunk + kScoreChunk / 2];  // every visible block's key: the chunk, then the folded one
+    } s;
+    SelectLds sel;  // the last workgroup selects
+  } u;
+};
+
+__device__ __forceinline__ void st_agent64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A record: the keys at LDS offsets 0..n-1 (blocks j0..j0+n-1) in bins >= lo, in block order, zero-padded
+// to R words (the caller's lo keeps them within R), and its header (top: the workgroup's largest key).
+// Every thread calls it.
+__device__ __forceinline__ void coop_record(const uint32_t* lk, int n, int64_t j0, int lo, uint32_t top,
+                                            uint64_t* hdr, uint64_t* cand, int R, uint32_t* wsum) {
+  constexpr int kPer = kScoreChunk / kScoreThreads;  // consecutive blocks per thread
+  const uint32_t L = (uint32_t)lo << 20;
+  const int i0 = (int)threadIdx.x * kPer;
+  uint32_t kv[kPer];
+  uint32_t c = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    kv[u] = i0 + u < n ? lk[i0 + u] : 0u;
+    c += (i0 + u < n && kv[u] >= L) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t pos = block_excl_scan(c, wsum, &total);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (i0 + u < n && kv[u] >= L) {
+      const uint32_t j = (uint32_t)(j0 + i0 + u);
+      st_agent64(&cand[pos], ((uint64_t)kv[u] << 32) | (uint64_t)(0xFFFFFFFFu - j));
+      ++pos;
+    }
+  }
+  for (int i = (int)total + (int)threadIdx.x; i < R; i += kScoreThreads) st_agent64(&cand[i], 0ull);
+  if (threadIdx.x == 0) st_agent64(hdr, ((uint64_t)top << 32) | ((uint64_t)(uint32_t)lo << 16) | total);
+  __syncthreads();  // wsum is reused by the next call
+}
+
+// The last to arrive, over every key of the query's row in memory: the keys >= the lower bound L in block
+// order into LDS (loads in batches of 16 keys per thread), then the selection in LDS; or, when more than
+// fit, the selection over every key straight from memory.
+__device__ __forceinline__ uint32_t coop_select_row(const ScoreArgs& a, SelectLds& S, int q, int N, uint32_t L,
+                                                    int32_t* out, int32_t* out2) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* keys = q_keys(a, q);
+  for (int i = tid; i < kRadixBins; i += kScoreThreads) S.hist[i] = 0u;
+  if (tid == 0) {
+    S.small_n = 0u;
+    S.sel_count = 0u;  // candidates so far
+  }
+  if (tid < 64) S.small[tid] = 0ull;
+  __syncthreads();
+  constexpr int kBatch = 16 * kScoreThreads;  // keys per batch: 16 consecutive per thread
+  uint64_t lo = ~0ull, hi = 0;
+  bool fits = true;
+  for (int j0 = 0; j0 < N && fits; j0 += kBatch) {
+    uint32_t kv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + tid * 16 + u;
+      kv[u] = j < N ? __hip_atomic_load(&keys[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c += (j0 + tid * 16 + u < N && kv[u] >= L) ? 1u : 0u;
+    const uint32_t base = S.sel_count;
+    uint32_t total;
+    uint32_t pos = block_excl_scan(c, S.wsum, &total);
+    if (base + total <= (uint32_t)kCandCap) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = j0 + tid * 16 + u;
+        if (j < N && kv[u] >= L) {
+          const uint64_t e = ((uint64_t)kv[u] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+          S.cs[base + pos++] = e;
+          lo = e < lo ? e : lo;
+          hi = e > hi ? e : hi;
+        }
+      }
+    }
+    __syncthreads();  // every thread has read sel_count and wsum
+    if (tid == 0) S.sel_count = base + total;
+    __syncthreads();
+    fits = S.sel_count <= (uint32_t)kCandCap;
+  }
+  const uint32_t n = S.sel_count;
+  if (fits && n >= (uint32_t)a.k) {
+    (void)lane;
+    (void)wave;
+    return select_core(a, S, (int64_t)n, lo, hi, [&](int64_t i) -> uint64_t { return S.cs[i]; }, out, out2);
+  }
+  // more candidates than the LDS holds: every key, straight from memory
+  auto elem = [&](int64_t i) -> uint64_t {
+    const uint32_t k = __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+  };
+  lo = ~0ull;
+  hi = 0;
+  for (int i = tid; i < N; i += kScoreThreads) {
+    const uint64_t e = elem(i);
+    lo = e < lo ? e : lo;
+    hi = e > hi ? e : hi;
+  }
+  __syncthreads();
+  return select_core(a, S, (int64_t)N, lo, hi, elem, out, out2);
+}
+
+// The last workgroup of a query to arrive: the selection into the workspace list (and topk), over NL
+// loaded record words per thread. Predicates are combined without short-circuit and LDS reads issued
+// together, so that no wave waits on one LDS round trip per loaded word.
+template <int NL>
+__device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int q, int N) {
+  ScoreLds& S = L.u.s.sc;
+  SelectLds& T = L.u.sel;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = (N + kScoreChunk - 1) / kScoreChunk;  // records (one per chunk)
+  const int R = a.pref_slots;
+  const int n_words = G * R;
+  const uint64_t* hdr = q_rec(a, q);
+  const uint64_t* cw = hdr + kRecHdrSlots;
+  // ---- one round of loads: the headers (thread t: record t) and every record's words (thread t, load u:
+  // word t + 512 u, so the words stay in block order along (u, wave, lane))
+  const uint64_t h = tid < G ? ld_agent64(&hdr[tid]) : 0ull;
+  uint64_t v[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int w = tid + u * kScoreThreads;
+    v[u] = w < n_words ? ld_agent64(&cw[w]) : 0ull;
+  }
+  // ---- headers: the highest and lowest floor, the largest key and the count over all records
+  if (wave * 64 < G) {
+    const bool hv = tid < G;
+    const uint32_t f = (uint32_t)(h >> 16) & 0xFFFFu;
+    uint64_t fmin = hv ? f : ~0ull, fmax = hv ? f : 0ull;
+    wave_minmax_u64(fmin, fmax);
+    uint64_t dummy = ~0ull, top = hv ? (h >> 32) : 0ull;
+    wave_minmax_u64(dummy, top);
+    const uint32_t cnt = wave_incl_scan(hv ? (uint32_t)h & 0xFFFFu : 0u);
+    if (lane == 63) {
+      atomicMax(&S.coop_bound, (uint32_t)fmax);
+      atomicMin(&S.coop_lmin, (uint32_t)fmin);
+      atomicMax(&S.coop_top, (uint32_t)top);
+      atomicAdd(&S.coop_total, cnt);
+    }
+  }
+  for (int i = tid; i < kRadixBins; i += kScoreThreads) T.hist[i] = 0u;  // (beyond the score LDS)
+  __syncthreads();
+  const uint32_t F = S.coop_bound;
+  int32_t* out = q_list(a, q);
+  int32_t* out2 = a.topk ? a.topk + (size_t)q * a.k : nullptr;
+  uint32_t n = 0;
+  bool fast = F < 4096u;  // (F = 4096: a record whose top bin alone holds more than cmin keys)
+  if (fast) {
+    // ---- radix select of the k-th largest key among the candidates (keys >= Fk, all <= the largest key
+    // Kt, so they share the bits above the highest bit in which Fk and Kt differ), kRadixBits at a time,
+    // until the digit bin that holds it is taken whole or the bits run out (equal keys). The first pass
+    // also counts the candidates.
+    const uint32_t Fk = F ? F << 20 : 1u, Kt = S.coop_top;
+    int hb = 31 - __clz(Fk ^ Kt);
+    hb = hb < 0 ? 0 : hb;
+    uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+    uint32_t prefix = Fk & mask;
+    uint32_t need = (uint32_t)a.k;
+    for (int shift = hb - (kRadixBits - 1); shift > -kRadixBits; shift -= kRadixBits) {
+      const int sh = shift < 0 ? 0 : shift;  // the last digit may be narrower
+      const uint32_t dmask = shift < 0 ? ((1u << (shift + kRadixBits)) - 1u) : (uint32_t)(kRadixBins - 1);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint32_t key = (uint32_t)(v[u] >> 32);
+        if ((key >= Fk) & ((key & mask) == prefix)) atomicAdd(&T.hist[(key >> sh) & dmask], 1u);
+      }
+      __syncthreads();
+      // counts from the top: thread t holds bins 2047-4t .. 2044-4t (cleared for the next pass)
+      uint32_t h4[4], c4 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h4[i] = T.hist[kRadixBins - 1 - 4 * tid - i];
+        c4 += h4[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T.hist[kRadixBins - 1 - 4 * tid - i] = 0u;
+      const uint32_t excl = excl_scan_512(c4, T.wsum);
+      if (shift == hb - (kRadixBits - 1)) {  // the first pass: every candidate counted
+        uint32_t C = 0;
+#pragma unroll
+        for (int w = 0; w < kScoreWaves; ++w) C += T.wsum[w];
+        if (C < (uint32_t)a.k) {
+          fast = false;
+          break;
+        }
+      }
+      if (excl < need && excl + c4 >= need) {
+        uint32_t c = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (c + h4[i] >= need) {
+            T.sel_digit = (uint32_t)(kRadixBins - 1 - 4 * tid - i);
+            T.sel_above = c;
+            T.sel_count = h4[i];
+            break;
+          }
+          c += h4[i];
+        }
+      }
+      __syncthreads();
+      need -= T.sel_above;
+      prefix |= T.sel_digit << sh;
+      mask |= dmask << sh;
+      if (T.sel_count == need) break;
+    }
+    if (fast) {
+      // ---- the winners in block order: the candidates above the boundary bin, and of those in it (equal
+      // keys once the bits ran out) the first `need`; per wave-load two ballot counts, one block scan
+      // over them (packed: above | in << 16)
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint32_t key = (uint32_t)(v[u] >> 32);
+        const bool in = key >= Fk;
+        const uint64_t mg = __ballot(in & ((key & mask) > prefix));
+        const uint64_t me = __ballot(in & ((key & mask) == prefix));
+        if (lane == 0 && tid + u * kScoreThreads < n_words)
+          S.flag_blk[1][u * kScoreWaves + wave] = (uint32_t)__popcll(mg) | ((uint32_t)__popcll(me) << 16);
+      }
+      __syncthreads();
+      const int n_wl = (n_words + 63) >> 6;
+      uint32_t total;
+      const uint32_t off = block_excl_scan(tid < n_wl ? S.flag_blk[1][tid] : 0u, S.wmax, &total);
+      if (tid < n_wl) S.flag_blk[2][tid] = off;
+      __syncthreads();
+      uint32_t base[NL];
+#pragma unroll
+      for (int u = 0; u < NL; ++u) base[u] = S.flag_blk[2][min(u * kScoreWaves + wave, kScoreIters * 32 - 1)];
+      const uint64_t lm = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint32_t key = (uint32_t)(v[u] >> 32);
+        const bool in = key >= Fk;
+        const bool gt = in & ((key & mask) > prefix), eq = in & ((key & mask) == prefix);
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        const uint32_t gb = (base[u] & 0xFFFFu) + (uint32_t)__popcll(mg & lm);
+        const uint32_t eb = (base[u] >> 16) + (uint32_t)__popcll(me & lm);
+        if (gt | (eq & (eb < need))) {
+          const uint32_t pos = gb + (eb < need ? eb : need);
+          const int32_t jb = (int32_t)(0xFFFFFFFFu - (uint32_t)v[u]);
+          if (pos < (uint32_t)a.k) {
+            out[pos] = jb;
+            if (out2) out2[pos] = jb;
+          }
+        }
+      }
+      const uint32_t ng = total & 0xFFFFu, ne = total >> 16;
+      n = ng + (ne < need ? ne : need);
+      n = n < (uint32_t)a.k ? n : (uint32_t)a.k;
+    }
+  }
+  if (!fast) {
+    // fewer than k keys >= F (a crowded chunk): a lower bound of the k-th key, then the key row
+    const uint32_t Lkey = S.coop_total >= (uint32_t)a.k ? S.coop_lmin << 20 : 0u;
+    __syncthreads();
+    n = coop_select_row(a, T, q, N, Lkey, out, out2);
+  }
+  for (int i = (int)n + tid; i < a.k; i += kScoreThreads) {  // only if fewer than k were found
+    out[i] = -1;
+    if (out2) out2[i] = -1;
+  }
+}
+
+// grid (max(n_cols, B), B*Tq [+ 1]): x = chunk of query y; the extra last row (app_units > 0) writes the
+// step's append, workgroup x for sequence x.
+template <int NL>
+__global__ __launch_bounds__(kScoreThreads, 4) void index_select_kernel(ScanArgs args) {  // <= 128 VGPRs
+  __shared__ CoopLds L;
+  const ScoreArgs& a = args.a;
+  if (args.app_units > 0 && (int)blockIdx.y == (int)gridDim.y - 1) {
+    const int b = blockIdx.x;
+    if (b < args.app.B)
+      for (int unit = (int)(threadIdx.x >> 6); unit < args.app_units; unit += kScoreWaves)
+        append_unit<true>(args.app, b, unit, threadIdx.x & 63);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int q = blockIdx.y;
+  const int b = q / a.Tq, tq = q % a.Tq;
+  const int c0 = blockIdx.x;
+  if (c0 >= a.n_cols) return;
+  if (query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq) < 0) return;  // ragged batch: no query in this row
+  const int N = (int)visible_blocks(a, b, tq);
+  if (N <= a.k) {
+    // every visible block is selected: no scores; the attention takes them all without a list
+    if (c0 == 0 && a.topk) {
+      int32_t* o = a.topk + (size_t)q * a.k;
+      for (int i = tid; i < a.k; i += kScoreThreads) o[i] = i < N ? i : -1;
+    }
+    return;
+  }
+  if (c0 * kScoreChunk >= N) return;
+  const int j_begin = c0 * kScoreChunk;
+  // the chunk the grid leaves out goes to a column that differs from query to query (two workgroups with
+  // the extra chunk on one compute unit would end last)
+  const int fold_col = (int)(((unsigned)q * 37u) % (unsigned)a.n_cols);
+  const int j_tail = a.fold_tail && c0 == fold_col ? a.n_cols * kScoreChunk : -1;
+  ScoreLds& S = L.u.s.sc;
+  const int lo = j_begin + kScoreChunk <= N ? score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys)
+                                            : score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys);
+  // this workgroup's record (the folded chunk's in its own record, after the others)
+  uint64_t* hdr = q_rec(a, q);
+  uint64_t* cw = hdr + kRecHdrSlots;
+  const int R = a.pref_slots;
+  const uint32_t top = S.coop_top;
+  coop_record(L.u.s.keys, min(kScoreChunk, N - j_begin), j_begin, lo, top, hdr + c0, cw + (size_t)c0 * R, R,
+              S.wmax);
+  if (j_tail >= 0 && j_tail < N)
+    coop_record(L.u.s.keys + kScoreChunk, N - j_tail, j_tail, lo, top, hdr + a.n_cols, cw + (size_t)a.n_cols * R,
+                R, S.wmax);
+  if (tid == 0) {  // the last to arrive: the selection's LDS counters
+    S.coop_top = 0u;
+    S.coop_bound = 0u;
+    S.coop_lmin = ~0u;
+    S.coop_total = 0u;
+  }
+  // count in (this thread's key and record writes complete first); the last to arrive goes on
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* sync = q_sync(a, q);
+  const int n_act = min(a.n_cols, (N + kScoreChunk - 1) / kScoreChunk);  // this query's score workgroups
+  if (tid == 0)
+    S.coop_last = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(n_act - 1);
+  __syncthreads();
+  if (!S.coop_last) return;
+  if (tid == 0) __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+  coop_select<NL>(a, L, q, N);
 }
 
 // ---- Many-query calls (chunked prefill): query tiles on the 32x32x64 scaled MFMA ------------------------
@@ -1195,6 +1594,23 @@ hipError_t launch_index_score(const ScoreArgs& a, int32_t B, hipStream_t s) {
   unsigned g1 = a.chunk_step > 0 ? (unsigned)a.chunk_step : (unsigned)((N_last + kScoreChunk - 1) / kScoreChunk);
   if (a.fold_tail && a.chunk_step == 0 && g1 >= 2) g1 -= 1;  // workgroup 0 scores the last chunk
   hipLaunchKernelGGL(score_kernel, dim3(g1, nq), dim3(kScoreThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_select(const ScanArgs& args, int32_t B, hipStream_t s) {
+  const unsigned nq = (unsigned)(B * args.a.Tq);
+  const unsigned cols = (unsigned)(args.a.n_cols > 0 ? args.a.n_cols : 1);
+  const bool app = args.app_units > 0;
+  const unsigned gx = app && (unsigned)B > cols ? (unsigned)B : cols;
+  // record words per thread of the last workgroup: the most any query of the call has
+  const int64_t words = (int64_t)(cols + (args.a.fold_tail ? 1 : 0)) * args.a.pref_slots;
+  if (words <= 9 * kScoreThreads)
+    hipLaunchKernelGGL(index_select_kernel<9>, dim3(gx, nq + (app ? 1u : 0u)), dim3(kScoreThreads), 0, s, args);
+  else if (words <= kPrefMaxLoads * kScoreThreads)
+    hipLaunchKernelGGL(index_select_kernel<kPrefMaxLoads>, dim3(gx, nq + (app ? 1u : 0u)), dim3(kScoreThreads), 0,
+                       s, args);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

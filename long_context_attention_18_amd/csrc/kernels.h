@@ -44,6 +44,7 @@ static_assert((kTileMaxBlocks + kTileSeg - 1) / kTileSeg <= kMaxSegs, "query-til
 // ---- attention tiling ----------------------------------------------------
 constexpr int kAttnKeys = 64;                         // keys staged per iteration (many-query kernel)
 constexpr int kAttendMaxQueries = 511;                // up to this many queries per call: attend.hip
+constexpr int kPrefMaxLoads = 17;  // segment slots one thread of the selecting score workgroup loads at once
 static_assert(kTileMinQueries > kAttendMaxQueries, "decode-step calls (with their append) never use query tiles");
 constexpr int64_t kMaxGridY = 65535;                  // launch limit of grid.y (indexer grids: one row per query)
 
@@ -105,6 +106,13 @@ struct ScoreArgs {
   int32_t tiles;           // 1: query tiles (the score launch also writes the candidates; no scan)
   int32_t write_keys;      // tiles: also write every visible block's key (the separate score call's contract)
   int32_t tile_select;     // tiles: the score launch also selects the top-k lists into topk (combined call)
+  // In-launch threshold and selection (decode-sized calls, indexer.hip): every score workgroup also writes
+  // a record (its bin counts and candidates) and counts itself in; the last of a query to arrive selects
+  // the query's top-k into its workspace list (and topk when not null)
+  int32_t coop;
+  int32_t n_cols;          // coop: score workgroup columns (chunks; the folded last chunk is not a column)
+  int32_t pref_slots;      // coop: 64-bit words per record (64, 128 or 256)
+  uint64_t off_sync, off_list, off_rec;
   // ragged batches (see IngestArgs): the queries of sequence b are its seq_T[b] new tokens, positions
   // seq_len[b] + i for rows i < seq_T[b]; null: positions len - Tq + i
   const int64_t* seq_len;
@@ -135,6 +143,17 @@ __device__ __forceinline__ uint32_t* q_hist(const ScoreArgs& a, int q) { return 
 __device__ __forceinline__ uint32_t* q_seg(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_seg); }
 __device__ __forceinline__ uint32_t* q_keys(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_keys); }
 __device__ __forceinline__ uint64_t* q_cand(const ScoreArgs& a, int q) { return (uint64_t*)(a.qbase + (size_t)q * a.qstride + a.off_cand); }
+// coop: the query's counter of score workgroups that arrived; zero between calls
+__device__ __forceinline__ uint32_t* q_sync(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_sync); }
+// coop: per query, kRecHdrSlots record headers (one 64-bit word per score chunk: the chunk's largest key
+// << 32 | its floor bin << 16 | its candidate count), then one record of pref_slots words per score chunk
+// (its candidates, key << 32 | ~block, in block order, zero-padded)
+constexpr int kRecHdrSlots = kMaxSegs;
+constexpr int kRecMinWords = 32;
+constexpr int kRecMaxWords = 256;
+__device__ __forceinline__ uint64_t* q_rec(const ScoreArgs& a, int q) { return (uint64_t*)(a.qbase + (size_t)q * a.qstride + a.off_rec); }
+// coop: the query's top-k list (k int32, ascending, -1 padded), read by the attention launch
+__device__ __forceinline__ int32_t* q_list(const ScoreArgs& a, int q) { return (int32_t*)(a.qbase + (size_t)q * a.qstride + a.off_list); }
 
 struct AttnArgs {
   const uint16_t* q;       // [B][Tq][H][128]
@@ -162,15 +181,17 @@ struct AttnArgs {
 };
 
 // One-launch attention for a few queries (attend.hip): the query's compressed entries come from the
-// caller's top-k list, from every visible block (HCA), or from the top-k selection run in the same
-// workgroup over the scan's candidates.
+// caller's top-k list (LIST), the list the in-launch selection left in the workspace (LIST_WS: always
+// valid; a query that sees at most k blocks attends to all of them without reading a list), every visible
+// block (DENSE), or the top-k selection run in the same workgroup over the scan's candidates (SELECT).
 constexpr int kMaxTopk = 2048;
-constexpr int kAttendList = 0, kAttendDense = 1, kAttendSelect = 2;
+constexpr int kAttendList = 0, kAttendDense = 1, kAttendSelect = 2, kAttendListWs = 3;
 // Key splits of the one-launch attention: a (query, 16-head group) may be spread over up to
 // kAttendMaxSplits workgroups (about one 32-key chunk per wave), each over its share of the keys; each writes a partial (running max,
 // sum and unnormalised O of its 16 heads) and the last to finish (a per-(query, group) counter,
 // release / acquire at agent scope) merges them.
 constexpr int kAttendMaxSplits = 8;
+constexpr int kAttendNoSplitChunks = 3;  // 32-key chunks per wave up to which a (query, head group) is not split
 constexpr int kAttendMaxWGs = 256;  // with splits, a call stays within one workgroup per CU (LDS allows one)
 struct AttendPartial {
   float m[16], l[16];
@@ -221,6 +242,9 @@ struct ScanArgs {
 };
 hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool with_select = true,
                               const IngestArgs* app = nullptr, int32_t app_units = 0);
+// The in-launch-threshold score launch (ScoreArgs.coop): scores, bound, candidates and the selection of
+// every query; with app_units > 0 one more row of workgroups writes the step's append.
+hipError_t launch_index_select(const ScanArgs& args, int32_t B, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s);
 

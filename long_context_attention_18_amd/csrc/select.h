@@ -67,10 +67,142 @@ __device__ __forceinline__ uint32_t excl_scan_512(uint32_t v, uint32_t* wsum) {
   return off + incl - v;
 }
 
+// The k-th largest of n elements (elem(i): the i-th; lo / hi: this thread's smallest and largest of the
+// ones it read) by radix select: on return the winners are exactly the elements e with (e & mask) >=
+// prefix. S.hist must be zero, S.small_n zero and S.small[] zero on entry (left zero again). Every thread
+// calls it.
+template <class Elem>
+__device__ inline void radix_bound(SelectLds& S, int64_t n, uint64_t lo, uint64_t hi, Elem elem, uint32_t k,
+                                   uint64_t* prefix_out, uint64_t* mask_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* hist = S.hist;
+  uint32_t* wsum = S.wsum;
+  wave_minmax_u64(lo, hi);
+  if (lane == 63) {
+    S.red_lo[wave] = lo;
+    S.red_hi[wave] = hi;
+  }
+  __syncthreads();
+
+  // every element a winner (n == k): no selection
+  uint64_t prefix = 0, mask = 0;
+  if (n > (int64_t)k) {
+    uint64_t glo = S.red_lo[0], ghi = S.red_hi[0];
+    for (int w = 1; w < 8; ++w) {
+      glo = S.red_lo[w] < glo ? S.red_lo[w] : glo;
+      ghi = S.red_hi[w] > ghi ? S.red_hi[w] : ghi;
+    }
+    // radix select of the k-th largest 64-bit key (score key, then lower index first), kRadixBits at a
+    // time from the highest bit in which the elements differ (keys are unique and n > k >= 1, so some
+    // bit differs), stopping as soon as the bin that holds it is taken whole
+    const int hb = 63 - __clzll((long long)(glo ^ ghi));
+    const uint64_t common = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+    prefix = glo & common;
+    mask = common;
+    uint32_t need = k;
+    for (int shift = hb - (kRadixBits - 1); shift > -kRadixBits; shift -= kRadixBits) {
+      const int sh = shift < 0 ? 0 : shift;  // the last digit may be narrower
+      const uint64_t dmask = shift < 0 ? ((1ull << (shift + kRadixBits)) - 1ull) : (uint64_t)(kRadixBins - 1);
+      for (int64_t i = tid; i < n; i += 512) {
+        const uint64_t e = elem(i);
+        if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
+      }
+      __syncthreads();
+      // counts from the top: thread t holds bins 2047-4t .. 2044-4t
+      uint32_t h4[4], c4 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h4[j] = hist[kRadixBins - 1 - 4 * tid - j];
+        hist[kRadixBins - 1 - 4 * tid - j] = 0u;  // cleared for the next pass (its adds follow two barriers)
+        c4 += h4[j];
+      }
+      const uint32_t excl = excl_scan_512(c4, wsum);
+      if (excl < need && excl + c4 >= need) {
+        uint32_t c = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (c + h4[j] >= need) {
+            S.sel_digit = (uint32_t)(kRadixBins - 1 - 4 * tid - j);
+            S.sel_above = c;
+            S.sel_count = h4[j];
+            break;
+          }
+          c += h4[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t d = S.sel_digit;
+      need -= S.sel_above;
+      prefix |= (uint64_t)d << sh;
+      mask |= dmask << sh;
+      if (S.sel_count == need) break;
+      if (S.sel_count <= 64) {
+        // a small boundary bin: gather its elements and find the need-th largest by direct ranking
+        // (keys are unique, so exactly one element has need-1 larger ones) instead of another pass
+        for (int64_t i = tid; i < n; i += 512) {
+          const uint64_t e = elem(i);
+          if ((e & mask) == prefix) S.small[atomicAdd(&S.small_n, 1u)] = e;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          // all 64 slots, unrolled: the LDS reads go out together instead of one round trip per element
+          const uint32_t c = S.sel_count;
+          const uint64_t mine = S.small[lane];
+          uint32_t rank = 0;
+#pragma unroll
+          for (int m = 0; m < 64; ++m) rank += S.small[m] > mine ? 1u : 0u;
+          if (lane < (int)c && rank == need - 1) S.sel_thresh = mine;
+        }
+        __syncthreads();
+        prefix = S.sel_thresh;  // the winners are exactly the elements >= the need-th largest of the bin
+        mask = ~0ull;
+        break;
+      }
+    }
+  }
+  *prefix_out = prefix;
+  *mask_out = mask;
+}
+
+// The selection proper, over n elements in index order (elem(i): the i-th; lo / hi: this thread's
+// smallest and largest of the ones it read): radix select of the k-th largest, then the winners in index
+// order to out (and out2). Returns the number of winners written (min(k, n)). Every thread calls it.
+template <class Elem>
+__device__ inline uint32_t select_core(const ScoreArgs& a, SelectLds& S, int64_t n, uint64_t lo, uint64_t hi,
+                                       Elem elem, int32_t* out, int32_t* out2) {
+  const int tid = threadIdx.x;
+  uint32_t* wsum = S.wsum;
+  uint64_t prefix, mask;
+  radix_bound(S, n, lo, hi, elem, (uint32_t)a.k, &prefix, &mask);
+  // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run
+  const int64_t per = (n + 511) / 512;
+  const int64_t i0 = (int64_t)tid * per;
+  const int64_t i1 = (i0 + per < n) ? i0 + per : n;
+  uint32_t mine = 0;
+  for (int64_t i = i0; i < i1; ++i) mine += ((elem(i) & mask) >= prefix) ? 1u : 0u;
+  uint32_t pos = excl_scan_512(mine, wsum);
+  uint32_t n_win = 0;
+  for (int w = 0; w < 8; ++w) n_win += wsum[w];
+  for (int64_t i = i0; i < i1; ++i) {
+    const uint64_t e = elem(i);
+    if ((e & mask) >= prefix) {
+      if (pos < (uint32_t)a.k) {
+        const int32_t j = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
+        out[pos] = j;
+        if (out2) out2[pos] = j;
+      }
+      ++pos;
+    }
+  }
+  return n_win < (uint32_t)a.k ? n_win : (uint32_t)a.k;
+}
+
 // Returns the number of winners written (min(k, N) whenever N > k). The candidate lower bound is only
 // a hint: with fewer than k candidates (a histogram left dirty by a score call without its selection)
 // or more than fit in LDS, the selection takes the path over every visible block and stays exact.
-__device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, SelectLds& S, int32_t* out) {
+// Winners go to out (and out2 when not null) in ascending block order.
+__device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, SelectLds& S, int32_t* out,
+                                        int32_t* out2 = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t* cs = S.cs;
   uint32_t* seg_off = S.seg_off;
@@ -175,106 +307,7 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
       hi = e > hi ? e : hi;
     }
   }
-  wave_minmax_u64(lo, hi);
-  if (lane == 63) {
-    S.red_lo[wave] = lo;
-    S.red_hi[wave] = hi;
-  }
-  __syncthreads();
-
-  // every element a winner (n == k): no selection
-  uint64_t prefix = 0, mask = 0;
-  if (n > (int64_t)a.k) {
-    uint64_t glo = S.red_lo[0], ghi = S.red_hi[0];
-    for (int w = 1; w < 8; ++w) {
-      glo = S.red_lo[w] < glo ? S.red_lo[w] : glo;
-      ghi = S.red_hi[w] > ghi ? S.red_hi[w] : ghi;
-    }
-    // radix select of the k-th largest 64-bit key (score key, then lower index first), kRadixBits at a
-    // time from the highest bit in which the elements differ (keys are unique and n > k >= 1, so some
-    // bit differs), stopping as soon as the bin that holds it is taken whole
-    const int hb = 63 - __clzll((long long)(glo ^ ghi));
-    const uint64_t common = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
-    prefix = glo & common;
-    mask = common;
-    uint32_t need = (uint32_t)a.k;
-    for (int shift = hb - (kRadixBits - 1); shift > -kRadixBits; shift -= kRadixBits) {
-      const int sh = shift < 0 ? 0 : shift;  // the last digit may be narrower
-      const uint64_t dmask = shift < 0 ? ((1ull << (shift + kRadixBits)) - 1ull) : (uint64_t)(kRadixBins - 1);
-      for (int64_t i = tid; i < n; i += 512) {
-        const uint64_t e = elem(i);
-        if ((e & mask) == prefix) atomicAdd(&hist[(uint32_t)((e >> sh) & dmask)], 1u);
-      }
-      __syncthreads();
-      // counts from the top: thread t holds bins 2047-4t .. 2044-4t
-      uint32_t h4[4], c4 = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h4[j] = hist[kRadixBins - 1 - 4 * tid - j];
-        hist[kRadixBins - 1 - 4 * tid - j] = 0u;  // cleared for the next pass (its adds follow two barriers)
-        c4 += h4[j];
-      }
-      const uint32_t excl = excl_scan_512(c4, wsum);
-      if (excl < need && excl + c4 >= need) {
-        uint32_t c = excl;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (c + h4[j] >= need) {
-            S.sel_digit = (uint32_t)(kRadixBins - 1 - 4 * tid - j);
-            S.sel_above = c;
-            S.sel_count = h4[j];
-            break;
-          }
-          c += h4[j];
-        }
-      }
-      __syncthreads();
-      const uint32_t d = S.sel_digit;
-      need -= S.sel_above;
-      prefix |= (uint64_t)d << sh;
-      mask |= dmask << sh;
-      if (S.sel_count == need) break;
-      if (S.sel_count <= 64) {
-        // a small boundary bin: gather its elements and find the need-th largest by direct ranking
-        // (keys are unique, so exactly one element has need-1 larger ones) instead of another pass
-        for (int64_t i = tid; i < n; i += 512) {
-          const uint64_t e = elem(i);
-          if ((e & mask) == prefix) S.small[atomicAdd(&S.small_n, 1u)] = e;
-        }
-        __syncthreads();
-        if (wave == 0) {
-          // all 64 slots, unrolled: the LDS reads go out together instead of one round trip per element
-          const uint32_t c = S.sel_count;
-          const uint64_t mine = S.small[lane];
-          uint32_t rank = 0;
-#pragma unroll
-          for (int m = 0; m < 64; ++m) rank += S.small[m] > mine ? 1u : 0u;
-          if (lane < (int)c && rank == need - 1) S.sel_thresh = mine;
-        }
-        __syncthreads();
-        prefix = S.sel_thresh;  // the winners are exactly the elements >= the need-th largest of the bin
-        mask = ~0ull;
-        break;
-      }
-    }
-  }
-  // winners (determined bits >= prefix), written in index order: each thread owns a contiguous run
-  const int64_t per = (n + 511) / 512;
-  const int64_t i0 = (int64_t)tid * per;
-  const int64_t i1 = (i0 + per < n) ? i0 + per : n;
-  uint32_t mine = 0;
-  for (int64_t i = i0; i < i1; ++i) mine += ((elem(i) & mask) >= prefix) ? 1u : 0u;
-  uint32_t pos = excl_scan_512(mine, wsum);
-  uint32_t n_win = 0;
-  for (int w = 0; w < 8; ++w) n_win += wsum[w];
-  for (int64_t i = i0; i < i1; ++i) {
-    const uint64_t e = elem(i);
-    if ((e & mask) >= prefix) {
-      if (pos < (uint32_t)a.k) out[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
-      ++pos;
-    }
-  }
-  return n_win < (uint32_t)a.k ? n_win : (uint32_t)a.k;
+  return select_core(a, S, n, lo, hi, elem, out, out2);
 }
 
 }  // namespace lca

@@ -128,16 +128,7 @@ class LayerRun:
                 self.dev.indexer_topk(to_dev(qin["qI"]), to_dev(qin["w"]), topk)
             torch.cuda.synchronize()
             if self.len // self.m > self.layer.topk:
-                if self.B * Tq >= MANY_QUERIES:
-                    # with many queries the combined calls keep no per-block scores: score again through
-                    # lca_csa_index_score (which keeps them) + lca_csa_topk_select, same lists required
-                    qI, w = to_dev(qin["qI"]), to_dev(qin["w"])
-                    tk2 = torch.full_like(topk, -7)
-                    self.dev.index_score(qI, w)
-                    self.dev.topk_select(Tq, tk2)
-                    torch.cuda.synchronize()
-                    assert torch.equal(tk2, topk), "separate score + select calls chose other lists"
-                self.last_scores = self.dev.index_scores(Tq)
+                self.last_scores = self.rescore(qin, topk)
             if not fused:
                 self.dev.sparse_attn(to_dev(qin["q"]), topk, out, lse)
         elif self.swa:
@@ -172,8 +163,21 @@ class LayerRun:
                       to_dev(qin["qI"]), to_dev(qin["w"]), to_dev(qin["q"]), out, lse, topk)
         torch.cuda.synchronize()
         self.len += T
-        self.last_scores = self.dev.index_scores(T) if self.len // self.m > self.layer.topk else None
+        self.last_scores = self.rescore(qin, topk) if self.len // self.m > self.layer.topk else None
         return qin, from_dev(topk), from_dev(out, np.uint16), from_dev(lse)
+
+    def rescore(self, qin, topk):
+        """The calls that selected in the indexer's own launch keep no per-block scores: score the same queries
+        again through lca_csa_index_score (which keeps them) + lca_csa_topk_select (which clears the
+        histograms it leaves), require the same lists, and return the scores [B][Tq][max_blocks]."""
+        import torch
+        Tq = topk.shape[1]
+        tk2 = torch.full_like(topk, -7)
+        self.dev.index_score(to_dev(qin["qI"]), to_dev(qin["w"]))
+        self.dev.topk_select(Tq, tk2)
+        torch.cuda.synchronize()
+        assert torch.equal(tk2, topk), "separate score + select calls chose other lists"
+        return self.dev.index_scores(Tq)
 
     def fill(self, total, chunk=16384):
         """Ingest `total` more tokens per sequence through compress + append, in chunks, each chunk's
