@@ -5,19 +5,26 @@ One step = one new token for each of the B sequences through every layer of
 the workload: compress the block the token completes (if any), append the
 token to the window state / tail, lightning-indexer scores and top-k (CSA
 layers), sparse (CSA) or dense (HCA) attention with the window under one
-softmax. All inputs of all steps are in HBM before the timed region. HIP
-events on the launch stream bracket the whole timed region and, in every
-step, the dominant kernel (the indexer's score stream over the FP4 keys), so
-its average duration is measured live on the stream it runs on. The steps are
-launched directly, behind a GPU spin that lasts until the host has enqueued
-the whole timed region ("prequeued"), so no step waits on the host.
+softmax. All inputs of all steps are in HBM before the timed region. The
+steps are launched directly, behind a GPU spin that lasts until the host has
+enqueued the whole timed region ("prequeued"), so no step waits on the host.
 
-Prints one JSON line. `value` is whole-job decode throughput in query
-tokens/s (B tokens per step / step time). `roofline` is the dominant
-kernel's algorithmic bytes per launch (34 B per visible indexer key, plus the
-queries) over its measured duration, against MI355X's 8 TB/s.
+Cold caches: a real model decodes through dozens of layers, each with its own
+cache, so no layer's cache is still in the 256 MB Infinity Cache when its
+next step comes. The bench therefore keeps R copies of the workload's layer
+caches (the same contents at other addresses) and runs step s on copy s mod R,
+with R chosen so that R steps read at least 512 MB (--replicas 1: every step
+on one copy, the warm case).
+
+Two timed regions of K steps: the first, with no events inside, gives `value`
+(whole-job decode throughput in query tokens/s: B tokens per step / step time)
+and `ms_per_step`; the second records HIP events between the step's launches
+on the launch stream (lca_csa_step_timed for CSA layers), which gives every
+kernel of the step its average duration (`kernels`). `roofline` is the
+time-dominant kernel's algorithmic bytes per launch over its measured
+duration, against MI355X's 8 TB/s.
 `cpu_baseline` times the plain C oracle on a bounded sample of the same
-workload (sequence 0, the first few timed decode queries) and doubles as a
+workload (sequence 0 of cache copy 0, its first decode queries) and doubles as a
 full-size parity check of those queries (top-k exact, attention within
 tolerance).
 
@@ -79,7 +86,9 @@ def parse_args():
                    help="run one plain 256 MiB device copy first (reference kernel for HBM counters)")
     p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     p.add_argument("--no-step-events", action="store_true",
-                   help="time the region without the per-step events around the dominant kernel (no roofline)")
+                   help="skip the second timed region (per-kernel events): no kernel durations, no roofline")
+    p.add_argument("--replicas", type=int, default=0,
+                   help="copies of the layer caches run round-robin (0: enough for 512 MB per round; 1: warm)")
     return p.parse_args()
 
 
@@ -145,6 +154,12 @@ class Layer:
         self.streams = [synth.TokenStream(wl.wid, self.stream_li, b, self.csa, wl.sigma) for b in range(self.B)]
         self.bias = {} if self.swa else synth.biases(wl.wid, li, layer.m, self.csa)
         self.bias_dev = {k: torch.from_numpy(v).cuda() for k, v in self.bias.items()}
+        self.reps = [self.dev]  # cache copies, step s on copy s mod len(reps)
+
+    def add_replicas(self, n):
+        """n - 1 more copies of the (filled) cache; every copy then takes its own local steps 0, 1, ..."""
+        self.reps = [self.dev] + [self.dev.replica() for _ in range(n - 1)]
+        self.rep_refs = [self.lca.ctypes.byref(d.cache) for d in self.reps]
 
     def _tokens_all(self, pos0, n):
         """[B][n][w] token arrays for all sequences, generated in parallel threads."""
@@ -215,50 +230,54 @@ class Layer:
         lca, torch = self.lca, self.torch
         self._lib = lca.lib()
         self._stream = torch.cuda.current_stream().cuda_stream
-        self._cache_ref = lca.ctypes.byref(self.dev.cache)
+        self.rep_refs = [lca.ctypes.byref(d.cache) for d in self.reps]
         self._bias = (None, None) if self.swa else \
             (self.bias_dev["bias"].data_ptr(), self.bias_dev["idx_bias"].data_ptr() if self.csa else None)
 
     def keep_outputs(self, steps):
-        """Give these steps their own output buffers (checked against the oracle afterwards)."""
+        """Give these local steps of copy 0 their own output buffers (checked against the oracle afterwards)."""
         torch = self.torch
         for s in steps:
             self.kept[s] = {"out": torch.empty_like(self.out)}
             if self.csa:
                 self.kept[s]["topk"] = torch.empty_like(self.topk)
 
-    def step(self, s, ev_score=None, rec=None):
+    def step(self, s, ev=None, rec=None):
+        """Global step s: local step s // R on copy s % R. ev: 4 events for lca_csa_step_timed (CSA), or a pair
+        recorded around the call (the other kinds)."""
+        R = len(self.reps)
+        r, j = s % R, s // R
+        c, dev = self.rep_refs[r], self.reps[r]
+        kept = self.kept.get(j) if r == 0 else None
+        out = (kept["out"] if kept else self.out).data_ptr()
         if self.csa:
-            # the whole CSA step in one library call; it records the events around its score launch
-            kv, gate, ik, ig, qI, w, q = self.step_ptrs[s]
-            kept = self.kept.get(s)
-            out = (kept["out"] if kept else self.out).data_ptr()
+            # the whole CSA step in one library call (the timed variant records events between its launches)
+            kv, gate, ik, ig, qI, w, q = self.step_ptrs[j]
             topk = (kept["topk"] if kept else self.topk).data_ptr()
-            ev0, ev1 = ev_score if ev_score is not None else (None, None)
-            rc = self._lib.lca_csa_step(self._cache_ref, kv, gate, ik, ig, self._bias[0], self._bias[1], 1, qI, w, q,
-                                        topk, out, None, self.dev.ws, self.dev.ws_bytes, self._stream, ev0, ev1)
+            args = (c, kv, gate, ik, ig, self._bias[0], self._bias[1], 1, qI, w, q, topk, out, None, dev.ws,
+                    dev.ws_bytes, self._stream)
+            if ev is None:
+                rc = self._lib.lca_csa_step(*args)
+            else:
+                rc = self._lib.lca_csa_step_timed(*args, (self.lca.ctypes.c_void_p * 4)(*ev))
             if rc != 0:
                 raise self.lca.LcaError("lca_csa_step", rc)
             return
-        kept = self.kept.get(s)
-        out = (kept["out"] if kept else self.out).data_ptr()
-        L, c, st = self._lib, self._cache_ref, self._stream
+        L, st = self._lib, self._stream
+        if ev is not None:
+            rec(ev[0])
         if self.swa:
             # window-only layer: the token's window entry and the window attention in one launch
-            kv, q = self.step_ptrs[s]
-            rc = L.lca_swa_step(c, kv, 1, q, out, None, self.dev.ws, self.dev.ws_bytes, st)
-            if rc != 0:
-                raise self.lca.LcaError("lca_swa_step", rc)
-            return
-        # HCA: one call -- compress when a block completes, then the append inside the attention launch
-        kv, gate, q = self.step_ptrs[s]
-        if ev_score is not None:
-            rec(ev_score[0])
-        rc = L.lca_hca_step(c, kv, gate, self._bias[0], 1, q, out, None, self.dev.ws, self.dev.ws_bytes, st)
-        if ev_score is not None:
-            rec(ev_score[1])
+            kv, q = self.step_ptrs[j]
+            rc = L.lca_swa_step(c, kv, 1, q, out, None, dev.ws, dev.ws_bytes, st)
+        else:
+            # HCA: one call -- compress when a block completes, then the append inside the attention launch
+            kv, gate, q = self.step_ptrs[j]
+            rc = L.lca_hca_step(c, kv, gate, self._bias[0], 1, q, out, None, dev.ws, dev.ws_bytes, st)
+        if ev is not None:
+            rec(ev[1])
         if rc != 0:
-            raise self.lca.LcaError("lca_hca_step", rc)
+            raise self.lca.LcaError("lca_swa_step" if self.swa else "lca_hca_step", rc)
 
 
 def fill_caches(layers, wl, chunk):
@@ -310,9 +329,19 @@ def score_bytes(layer, B, t):
 
 
 def attn_bytes(layer, B, t):
+    """Algorithmic bytes of one decode attention launch: 196 B per key entry (every visible block for HCA, the
+    min(k, N) selected ones and the list for CSA; the window), plus q and out."""
     n = (t + 1) // layer.m
     w = min(layer.window, t + 1)
+    if layer.csa:
+        return B * ((min(layer.topk, n) + w) * 196 + layer.topk * 4 + layer.n_heads * 128 * 2 * 2)
     return B * ((n + w) * 196 + layer.n_heads * 128 * 2 * 2)
+
+
+def compress_bytes(layer, B):
+    """Algorithmic bytes of one decode compress launch (one block per sequence): the block's m tokens in (kv,
+    gate, and for CSA ik, ig: 768 B per token), the entry out (196 B, + 34 B of indexer key for CSA)."""
+    return B * (layer.m * (768 if layer.csa else 512) + 196 + (34 if layer.csa else 0))
 
 
 SPIN_CYCLES = 1.2e6  # GPU cycles of pre-region spin per timed step and layer
@@ -622,94 +651,88 @@ def main():
         del a, b
 
     t0 = time.perf_counter()
-    layers = [Layer(wl, li, layer, S, args.threads) for li, layer in enumerate(wl.layers)]
+    # replicas: enough copies of the layer caches that one round of R steps reads >= 512 MB (a real model's
+    # other layers evict a layer's cache from the Infinity Cache before its next step), at most 16
+    step_bytes_1 = sum(configs.decode_step_bytes(l, wl.context + 1) * wl.batch for l in wl.layers)
+    R = args.replicas if args.replicas > 0 else max(1, min(16, -(-(512 << 20) // step_bytes_1)))
+    n_total = S + (0 if args.no_step_events else K)  # global steps: warm-up, timed, timed with events
+    n_local = -(-n_total // R) + 1                   # local steps of each copy
+    layers = [Layer(wl, li, layer, n_local, args.threads) for li, layer in enumerate(wl.layers)]
     chunk = max(4096, min(65536, (1 << 26) // (wl.batch * 768)))
     groups = fill_caches(layers, wl, chunk)
     for Ls in groups.values():
-        step_tok = Ls[0].step_tokens(S)
+        step_tok = Ls[0].step_tokens(n_local)
         for L in Ls:
-            L.make_step_inputs(S, step_tok)
-    n_check = 0 if args.no_cpu_baseline else max(1, args.oracle_queries)
-    layers[0].keep_outputs(range(W, W + n_check))
+            L.make_step_inputs(n_local, step_tok)
+    for L in layers:
+        L.add_replicas(R)
     torch.cuda.synchronize()
+    # the checked queries: copy 0's first local steps (global steps 0, R, 2R, ... of the warm-up and the first
+    # timed region)
+    j_check = 0
+    n_check = 0 if args.no_cpu_baseline else max(1, min(args.oracle_queries, (S - 1) // R + 1))
+    layers[0].keep_outputs(range(j_check, j_check + n_check))
+    cache_mb = sum(L.dev.cache_bytes for L in layers) * R / 2**20
     log(f"caches filled to {wl.context} tokens x {wl.batch} seqs x {len(layers)} layer(s) in "
-        f"{time.perf_counter() - t0:.1f} s")
+        f"{time.perf_counter() - t0:.1f} s; {R} cop{'y' if R == 1 else 'ies'} round-robin ({cache_mb:.0f} MB of "
+        f"caches, {step_bytes_1 * R / 2**20:.0f} MB read per round)")
 
     dom = next((L for L in layers if L.csa), layers[0])
-    dom_kernel = "index_select_kernel" if dom.csa else "attend_kernel"
     hev = HipEvents()
     mode = "prequeued"
     rec = lambda e: hev.record(e, False)
     ev_begin, ev_end = hev.create(), hev.create()
-    ev_dom = [(hev.create(), hev.create()) for _ in range(K)]
+    n_ev = 4 if dom.csa else 2
+    ev_dom = [tuple(hev.create() for _ in range(n_ev)) for _ in range(K)]
 
     def run_steps(steps, timed):
         for i, s in enumerate(steps):
             for L in layers:
-                L.step(s, ev_dom[i] if (timed and L is dom and not args.no_step_events) else None, rec)
+                L.step(s, ev_dom[i] if (timed and L is dom) else None, rec)
 
-    torch.cuda.synchronize()
-    if True:
-        # the first warm-up steps pay one-time costs (code objects loading); time the host on the rest
-        run_steps(range(W // 2), False)
-        torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        run_steps(range(W // 2, W), False)
-        warm_host_us = (time.perf_counter() - h0) * 1e6 / max(1, W - W // 2)
-        torch.cuda.synchronize()
-        # the host's own enqueue cost per step (warm-up, no spin ahead of it): the GPU never waits on the
-        # host as long as this stays below the GPU's time per step
-        log(f"host enqueue per step in the warm-up: {warm_host_us:.1f} us")
-        # keep the GPU busy while the host enqueues the whole timed region, so no step waits on the host
-        # (about 0.5 ms of spin per step and layer: several times the host's enqueue cost, also under a
+    def timed_region(steps, with_events):
+        # keep the GPU busy while the host enqueues the whole region, so no step waits on the host (about
+        # 0.5 ms of spin per step and layer: several times the host's enqueue cost, also under a
         # kernel-trace profiler, which slows each launch's enqueue)
         torch.cuda._sleep(int(SPIN_CYCLES * max(20, K) * len(layers)))
         h0 = time.perf_counter()
         rec(ev_begin)
-        run_steps(range(W, S), True)
+        run_steps(steps, with_events)
         rec(ev_end)
         enq_ms = (time.perf_counter() - h0) * 1e3
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - h0) * 1e3
-        log(f"host enqueue of the timed region: {enq_ms:.2f} ms")
-        # a long region fills the device queue: the host then blocks until the spin ends and enqueues
-        # the rest while the GPU runs, which costs nothing as long as it enqueues faster than the GPU runs
+        # a long region fills the device queue: the host then blocks until the spin ends and enqueues the
+        # rest while the GPU runs, which costs nothing as long as it enqueues faster than the GPU runs
         if enq_ms > total_spin_ms_estimate(K, len(layers)):
             log("the host enqueue outlasted the spin (device queue full); the GPU keeps the pace as long "
                 "as the warm-up's host time per step stays below the GPU's")
+        return hev.elapsed_ms(ev_begin, ev_end), enq_ms, host_ms
 
-    total_ms = hev.elapsed_ms(ev_begin, ev_end)
+    torch.cuda.synchronize()
+    # the first warm-up steps pay one-time costs (code objects loading); time the host on the rest
+    run_steps(range(W // 2), False)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    run_steps(range(W // 2, W), False)
+    warm_host_us = (time.perf_counter() - h0) * 1e6 / max(1, W - W // 2)
+    torch.cuda.synchronize()
+    # the host's own enqueue cost per step (warm-up, no spin ahead of it): the GPU never waits on the host as
+    # long as this stays below the GPU's time per step
+    log(f"host enqueue per step in the warm-up: {warm_host_us:.1f} us")
+    total_ms, enq_ms, host_ms = timed_region(range(W, S), False)
+    log(f"host enqueue of the timed region: {enq_ms:.2f} ms")
     ms_per_step = total_ms / K
     if warm_host_us > 0.9 * ms_per_step * 1e3:
         log(f"warning: host enqueue per step ({warm_host_us:.0f} us) is close to or above the GPU's "
             f"({ms_per_step * 1e3:.0f} us): the GPU may have waited on the host")
-    if args.no_step_events:
-        log(f"timed {K} steps without per-step events: {total_ms:.3f} ms; {ms_per_step * 1e3:.2f} us/step")
-        return 0
-    dom_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in ev_dom])
-    if not dom.csa:
-        # an HCA step's events bracket its one call; the steps whose token completes a block also compress
-        # (every m-th step), and stay out of the attention kernel's average
-        keep = np.array([(wl.context + s + 1) % dom.layer.m != 0 for s in range(W, S)])
-        dom_us = dom_us[keep] if keep.any() else dom_us
     value = wl.batch * K / (total_ms / 1e3)
     log(f"timed {K} steps: {total_ms:.3f} ms on the GPU clock ({host_ms:.3f} ms host incl. spin); "
-        f"{ms_per_step * 1e3:.2f} us/step; {dom_kernel} {dom_us.mean():.2f} us avg "
-        f"(min {dom_us.min():.2f}, max {dom_us.max():.2f})")
+        f"{ms_per_step * 1e3:.2f} us/step")
 
     # algorithmic bytes
-    t_steps = [wl.context + s for s in range(W, S)]
+    t_steps = [wl.context + s // R for s in range(W, S)]
     step_bytes = sum(configs.decode_step_bytes(L.layer, t + 1) * wl.batch for L in layers for t in t_steps) / K
-    if dom.csa:
-        dom_bytes = float(np.mean([score_bytes(dom.layer, wl.batch, t) for t in t_steps]))
-        src = src_sha(os.path.join(ROOT, "long_context_attention_18_amd", "csrc", "indexer.hip"))
-    else:
-        dom_bytes = float(np.mean([attn_bytes(dom.layer, wl.batch, t) for t in t_steps]))
-        src = src_sha(os.path.join(ROOT, "long_context_attention_18_amd", "csrc", "attention.hip"))
-    dom_avg_us = float(dom_us.mean())
-    achieved = dom_bytes / (dom_avg_us * 1e-6) / 1e9
-    traffic = load_traffic(dom_kernel, wl.name, src)
-
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -727,19 +750,61 @@ def main():
                    "layers": layers_label(wl.layers),
                    "n_heads": wl.layers[0].n_heads, "window": wl.layers[0].window,
                    "topk": max((l.topk for l in wl.layers), default=0),
-                   "idx_heads": max((l.idx_heads for l in wl.layers), default=0), "launch": mode},
-        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_avg_us, 3)},
+                   "idx_heads": max((l.idx_heads for l in wl.layers), default=0), "launch": mode,
+                   "cache_copies": R},
+        "roofline": None,
         "step_hbm": {"algorithmic_bytes": int(step_bytes),
                      "gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
     }
 
+    if not args.no_step_events:
+        # the second region: the same steps, with events between the dominant layer's launches
+        t2_ms, _, _ = timed_region(range(S, S + K), True)
+        t2 = [wl.context + s // R for s in range(S, S + K)]
+        ms = lambda a, b: np.array([hev.elapsed_ms(e[a], e[b]) * 1e3 for e in ev_dom])
+        kernels = []
+        if dom.csa:
+            comp_us, idx_us, att_us = ms(0, 1), ms(1, 2), ms(2, 3)
+            ran = np.array([(t + 1) % dom.layer.m == 0 for t in t2])  # steps whose token completes a block
+            idx_b = float(np.mean([score_bytes(dom.layer, wl.batch, t) for t in t2]))
+            att_b = float(np.mean([attn_bytes(dom.layer, wl.batch, t) for t in t2]))
+            kernels.append(("index_select_kernel", idx_us, idx_b, 1.0))
+            kernels.append(("attend_kernel<3>", att_us, att_b, 1.0))
+            if ran.any():
+                kernels.append(("compress_kernel", comp_us[ran], float(compress_bytes(dom.layer, wl.batch)),
+                                float(ran.mean())))
+        else:
+            d_us = ms(0, 1)
+            keep = np.array([(t + 1) % dom.layer.m != 0 for t in t2])  # no compress launch in the step
+            d_us = d_us[keep] if keep.any() else d_us
+            att_b = float(np.mean([attn_bytes(dom.layer, wl.batch, t) for t in t2]))
+            kernels.append(("attend_kernel<1>" if not dom.swa else "attend_kernel<1> (window)", d_us, att_b, 1.0))
+        per_step = sum(float(u.mean()) * f for _, u, _, f in kernels)
+        result["kernels"] = [
+            {"kernel": n, "avg_us": round(float(u.mean()), 3), "min_us": round(float(u.min()), 3),
+             "launches_per_step": round(f, 3), "bytes_per_launch": int(b),
+             "gbps": round(b / (float(u.mean()) * 1e-6) / 1e9, 1),
+             "frac": round(b / (float(u.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+             "share_of_step": round(float(u.mean()) * f / (t2_ms / K * 1e3), 4)}
+            for n, u, b, f in kernels]
+        dom_name, dom_us, dom_bytes, _ = max(kernels, key=lambda k: float(k[1].mean()) * k[3])
+        dom_avg_us = float(dom_us.mean())
+        achieved = dom_bytes / (dom_avg_us * 1e-6) / 1e9
+        src = src_sha(os.path.join(ROOT, "long_context_attention_18_amd", "csrc",
+                                   "indexer.hip" if dom_name.startswith("index") else "attend.hip"))
+        result["roofline"] = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                              "traffic": load_traffic(dom_name.split("<")[0], wl.name, src),
+                              "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_avg_us, 3)}
+        log(f"second region with per-launch events: {t2_ms / K * 1e3:.2f} us/step; " +
+            "; ".join(f"{n} {float(u.mean()):.2f} us x {f:.2f}/step" for n, u, _, f in kernels) +
+            f" (kernels {per_step:.1f} us of the step)")
+
     if n_check:
         log("oracle sample (sequence 0) ...")
         n_par = 0 if args.no_parallel_oracle else max(n_check, args.threads)
-        res, dec_s, build_s, nb, par = oracle_sample(layers, wl, W, n_check, args.threads, n_par)
+        res, dec_s, build_s, nb, par = oracle_sample(layers, wl, j_check, n_check, args.threads, n_par)
         L = layers[0]
         parity = {"queries": len(res), "topk_exact": True, "max_rel_l2": 0.0, "max_abs": 0.0}
         for s, t, r in res:

@@ -296,15 +296,27 @@ lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq
  * candidate scan with the append, selection + attention.) For decode-sized
  * calls: B * T <= 511
  * (else LCA_ERR_SHAPE); ring >= T + window - 1. Inputs as for the compressor
- * and lca_csa_attend; topk_dev and lse_dev may be NULL. score_ev_begin /
- * score_ev_end, when not NULL, are hipEvent_t the call records on `stream`
- * around the indexer score kernel (for timing it). Checks everything before
- * launching: a rejected call leaves the cache unchanged. */
+ * and lca_csa_attend; topk_dev and lse_dev may be NULL. Checks everything
+ * before launching: a rejected call leaves the cache unchanged. */
 lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
                         const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
                         const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
-                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
-                        void* score_ev_begin, void* score_ev_end);
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* lca_csa_step with timing marks, for measuring the step's kernels one by
+ * one: the same launches and results, plus hipEventRecord on `stream` of
+ * events[0] before the compress launch (when a block completes), events[1]
+ * before the indexer launch, events[2] after it (after the candidate scan
+ * on the three-launch path) and events[3] after the attention. events is a
+ * host array of 4 hipEvent_t (entries may be NULL: not recorded), owned by
+ * the caller; events == NULL is LCA_ERR_NULL. The marks sit between the
+ * launches, so they separate kernels that would otherwise follow each other
+ * directly. */
+lca_status lca_csa_step_timed(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                              const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                              const float* idx_bias_dev, int32_t T, const uint16_t* qI_dev, const float* w_dev,
+                              const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                              void* ws_dev, size_t ws_bytes, void* stream, void* const* events);
 
 /* lca_csa_step for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
@@ -320,7 +332,7 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
  * context at B = 4 and T = 1 fits. Every call on one GPU shares that GPU's
  * array: calls that overlap in time on one GPU (other streams, other host
  * threads) race and must be serialised by the caller. qI_dev and w_dev are
- * required; no timing events. */
+ * required. */
 lca_status lca_csa_step_noalloc(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
                                 const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
                                 const float* idx_bias_dev, int32_t T, const uint16_t* qI_dev, const float* w_dev,

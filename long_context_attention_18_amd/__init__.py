@@ -83,8 +83,9 @@ _SIGNATURES = {
     "lca_swa_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_attend": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_csa_topk_attn": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
-    "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP,
-                            _VP, _VP]),
+    "lca_csa_step": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "lca_csa_step_timed": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                  _VP, _VP]),
     "lca_csa_step_noalloc": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "lca_hca_step": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_swa_step": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -223,12 +224,20 @@ def lca_csa_topk_attn(cache, q, Tq, topk, out, lse, ws, ws_bytes, stream=None):
                                                          _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def lca_csa_step(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, ws, ws_bytes, stream=None,
-                 score_events=(None, None)):
+def lca_csa_step(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, ws, ws_bytes, stream=None):
     _check("lca_csa_step", lib().lca_csa_step(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(ik), _ptr(ig),
                                                _ptr(bias), _ptr(idx_bias), T, _ptr(qI), _ptr(w), _ptr(q), _ptr(topk),
-                                               _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream),
-                                               score_events[0], score_events[1]))
+                                               _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_csa_step_timed(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, ws, ws_bytes, stream,
+                       events):
+    """events: 4 hipEvent_t handles (or None), recorded between the step's launches."""
+    arr = (ctypes.c_void_p * 4)(*events)
+    _check("lca_csa_step_timed", lib().lca_csa_step_timed(ctypes.byref(cache), _ptr(kv), _ptr(gate), _ptr(ik),
+                                                           _ptr(ig), _ptr(bias), _ptr(idx_bias), T, _ptr(qI), _ptr(w),
+                                                           _ptr(q), _ptr(topk), _ptr(out), _ptr(lse), _ptr(ws),
+                                                           ws_bytes, _stream(stream), arr))
 
 
 def lca_csa_step_noalloc(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, stream=None):
@@ -317,6 +326,24 @@ class DeviceLayer:
         self.ws = (self.ws_mem.data_ptr() + 255) // 256 * 256
         lca_workspace_init(self.ws, self.ws_bytes, stream)
 
+    def replica(self, stream=None):
+        """A second cache with this one's contents in new device memory (bound, then a byte copy of the cache
+        memory, len and pending copied): the same state at other addresses. It shares this layer's
+        workspace, so calls on the two must not overlap in time."""
+        import copy
+        import torch
+        r = copy.copy(self)
+        r.mem = torch.empty_like(self.mem)
+        base = (r.mem.data_ptr() + 255) // 256 * 256
+        r.cache = lca_cache()
+        lca_cache_bind(self.desc, r.cache, base, self.cache_bytes, self.batch, self.max_ctx, self.ring, stream)
+        src = (self.mem.data_ptr() + 255) // 256 * 256
+        o_src, o_dst = src - self.mem.data_ptr(), base - r.mem.data_ptr()
+        with torch.cuda.stream(torch.cuda.ExternalStream(stream)) if stream else torch.cuda.stream(None):
+            r.mem[o_dst:o_dst + self.cache_bytes].copy_(self.mem[o_src:o_src + self.cache_bytes])
+        r.cache.len, r.cache.pending, r.cache.ragged = self.cache.len, self.cache.pending, self.cache.ragged
+        return r
+
     def reset(self, stream=None):
         """Empty the cache (rebind: zeroed, len = 0) and re-zero the workspace."""
         base = (self.mem.data_ptr() + 255) // 256 * 256
@@ -371,11 +398,10 @@ class DeviceLayer:
     def topk_attn(self, q, out, lse=None, topk=None, stream=None):
         lca_csa_topk_attn(self.cache, q, q.shape[1], topk, out, lse, self.ws, self.ws_bytes, stream)
 
-    def step(self, kv, gate, ik, ig, bias, idx_bias, qI, w, q, out, lse=None, topk=None, stream=None,
-             score_events=(None, None)):
+    def step(self, kv, gate, ik, ig, bias, idx_bias, qI, w, q, out, lse=None, topk=None, stream=None):
         """One decode step (CSA): T = kv.shape[1] tokens in, their queries attend."""
         lca_csa_step(self.cache, kv, gate, ik, ig, bias, idx_bias, kv.shape[1], qI, w, q, topk, out, lse, self.ws,
-                     self.ws_bytes, stream, score_events)
+                     self.ws_bytes, stream)
 
     def hca_step(self, kv, gate, bias, q, out, lse=None, stream=None):
         """One decode step (HCA): T = kv.shape[1] tokens in (compress, append), their queries attend."""

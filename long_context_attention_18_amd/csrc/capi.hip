@@ -653,7 +653,7 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
                          const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
                          const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
                          uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
-                         void* score_ev_begin, void* score_ev_end) {
+                         void* const* ev) {
   // every check first, so a rejected call leaves the cache as it was
   lca_status st = csa_step_check(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T);
   if (st != LCA_OK) return st;
@@ -666,7 +666,10 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
   if (st != LCA_OK) return st;
   attend_workspace(&args, &after, T, ws_dev, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
+  // the timed variant's events: step start, indexer start, indexer end, attention end
+  auto mark = [&](int i) { return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess; };
   const int64_t m = cache->desc.m;
+  if (!mark(0)) return LCA_ERR_LAUNCH;
   // compress the blocks the T tokens complete (their keys are scored below)
   const int64_t n_blocks = (cache->len + T) / m - cache->len / m;
   if (n_blocks > 0) {
@@ -692,19 +695,21 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
     sa.a = args.s;
     sa.app = app;
     sa.app_units = units;
-    if (score_ev_begin && hipEventRecord((hipEvent_t)score_ev_begin, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (!mark(1)) return LCA_ERR_LAUNCH;
     if (launch_index_select(sa, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
-    if (score_ev_end && hipEventRecord((hipEvent_t)score_ev_end, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (!mark(2)) return LCA_ERR_LAUNCH;
     if (launch_attend(args, cache->batch, kAttendListWs, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (!mark(3)) return LCA_ERR_LAUNCH;
     cache->len = end;
     cache->pending = 0;
     return LCA_OK;
   }
-  if (score_ev_begin && hipEventRecord((hipEvent_t)score_ev_begin, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (!mark(1)) return LCA_ERR_LAUNCH;
   if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
-  if (score_ev_end && hipEventRecord((hipEvent_t)score_ev_end, s) != hipSuccess) return LCA_ERR_LAUNCH;
   if (launch_topk_select(args.s, cache->batch, s, false, &app, units) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (!mark(2)) return LCA_ERR_LAUNCH;
   if (launch_attend(args, cache->batch, kAttendSelect, s) != hipSuccess) return LCA_ERR_LAUNCH;
+  if (!mark(3)) return LCA_ERR_LAUNCH;
   cache->len = end;
   cache->pending = 0;
   return LCA_OK;
@@ -757,10 +762,19 @@ extern "C" {
 lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev, const uint16_t* ik_dev,
                         const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
                         const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
-                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
-                        void* score_ev_begin, void* score_ev_end) {
+                        uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   return csa_step_impl(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, qI_dev, w_dev, q_dev,
-                       topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, stream, score_ev_begin, score_ev_end);
+                       topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, stream, nullptr);
+}
+
+lca_status lca_csa_step_timed(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                              const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                              const float* idx_bias_dev, int32_t T, const uint16_t* qI_dev, const float* w_dev,
+                              const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                              void* ws_dev, size_t ws_bytes, void* stream, void* const* events) {
+  if (!events) return LCA_ERR_NULL;
+  return csa_step_impl(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, qI_dev, w_dev, q_dev,
+                       topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, stream, events);
 }
 
 lca_status lca_csa_step_noalloc(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,
@@ -778,7 +792,7 @@ lca_status lca_csa_step_noalloc(lca_cache* cache, const uint16_t* kv_dev, const 
   st = static_scratch(&after, T, (hipStream_t)stream, &ws);
   if (st != LCA_OK) return st;
   return csa_step_impl(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, qI_dev, w_dev, q_dev,
-                       topk_dev, out_dev, lse_dev, ws, kStaticScratchBytes, stream, nullptr, nullptr);
+                       topk_dev, out_dev, lse_dev, ws, kStaticScratchBytes, stream, nullptr);
 }
 
 lca_status lca_csa_attend(lca_cache* cache, const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev,

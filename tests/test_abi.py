@@ -101,8 +101,7 @@ def test_bad_arguments_are_rejected_before_any_launch():
     assert L.lca_hca_dense_attn(ctypes.byref(cache), 1, 1, 1, None, 1, 1, None) == -1
     assert L.lca_csa_attend(ctypes.byref(cache), 1, 1, 1, 1, None, 1, None, 1, 1, None) == -1
     assert L.lca_csa_topk_attn(ctypes.byref(cache), 1, 1, None, 1, None, 1, 1, None) == -1
-    assert L.lca_csa_step(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, 1, None, 1, 1, None, None,
-                          None) == -1
+    assert L.lca_csa_step(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, 1, None, 1, 1, None) == -1
     assert L.lca_hca_step(ctypes.byref(cache), 1, 1, 1, 1, 1, 1, None, None, 0, None) == -1
     assert L.lca_swa_step(ctypes.byref(cache), 1, 1, 1, 1, None, None, 0, None) == -1
     assert L.lca_workspace_init(None, 256, None) == -1
@@ -141,10 +140,14 @@ def test_order_capacity_and_kind_checks():
     c.len = 100
     # one-call step: decode-sized only (B*T <= 511), rejected calls leave the cache as it was
     c.len = 0
-    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 512, P, P, P, None, P, None, P, 1 << 30, None, None,
-                          None) == -2
-    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, None, 0, None, None,
-                          None) == -6
+    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 512, P, P, P, None, P, None, P, 1 << 30, None) == -2
+    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, None, 0, None) == -6
+    # the timed variant: the same checks, and its event array is required
+    ev = (ctypes.c_void_p * 4)()
+    assert L.lca_csa_step_timed(ctypes.byref(c), P, P, P, P, P, P, 512, P, P, P, None, P, None, P, 1 << 30, None,
+                                ev) == -2
+    assert L.lca_csa_step_timed(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, 1 << 30, None,
+                                None) == -1
     assert c.len == 0 and c.pending == 0
     c.len = 100
     # workspace missing / too small
@@ -161,8 +164,7 @@ def test_order_capacity_and_kind_checks():
     h = _fake_bound_cache("hca")
     assert L.lca_csa_compress(ctypes.byref(h), P, P, P, P, P, P, 1, None) == -3
     assert L.lca_csa_attend(ctypes.byref(h), P, P, P, 1, None, P, None, P, 1 << 30, None) == -3
-    assert L.lca_csa_step(ctypes.byref(h), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, 1 << 30, None, None,
-                          None) == -3
+    assert L.lca_csa_step(ctypes.byref(h), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, 1 << 30, None) == -3
     # the dense one-call steps: kind, null inputs, decode-sized T, capacity, order; a rejected call leaves
     # the cache as it was
     assert L.lca_hca_step(ctypes.byref(c), P, P, P, 1, P, P, None, None, 0, None) == -3   # CSA cache
@@ -353,8 +355,7 @@ def test_ragged_calls_checks():
     c.ragged = 1                                                                   # as after a ragged call
     assert L.lca_csa_compress(ctypes.byref(c), P, P, P, P, P, P, 1, None) == -5
     assert L.lca_swa_tail_append(ctypes.byref(c), P, P, P, P, 1, None) == -5
-    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, big, None, None,
-                          None) == -5
+    assert L.lca_csa_step(ctypes.byref(c), P, P, P, P, P, P, 1, P, P, P, None, P, None, P, big, None) == -5
     info = lca.lca_snapshot_info()
     assert L.lca_snapshot_layout(ctypes.byref(c), ctypes.byref(info)) == -5
     assert L.lca_cache_snapshot(ctypes.byref(c), 0, P, big, ctypes.byref(info), None) == -5

@@ -534,3 +534,52 @@ def test_window_only_layer_many_queries_and_long_window():
     worst, oc = _decode(run, 3, 1503)
     compare_cache(run, oc)
     print("swa long-window worst", worst)
+
+
+def test_csa_step_timed_matches_the_step():
+    """lca_csa_step_timed (the same step with four events recorded between its launches) against lca_csa_step
+    on a twin cache: top-k lists, outputs, LSE and cache bytes bit for bit over steps across a block boundary;
+    the events completed in order (compress, indexer, attention)."""
+    import torch
+    import long_context_attention_18_amd as lca
+    import bench
+    try:
+        from gpu_harness import to_dev, from_dev
+    except ImportError:
+        from tests.gpu_harness import to_dev, from_dev
+    layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=256)
+    B, ctx = 2, 9001
+    a = LayerRun(layer, B=B, max_ctx=ctx + 12, ring=128)
+    b = LayerRun(layer, B=B, max_ctx=ctx + 12, ring=128)
+    for run in (a, b):
+        run.fill(ctx)
+    hev = bench.HipEvents()
+    ev = [hev.create() for _ in range(4)]
+    H, k = layer.n_heads, layer.topk
+    for _ in range(5):
+        parts = [a.tokens(i, a.len, 1) for i in range(B)]
+        tok = {key: to_dev(np.stack([p[key] for p in parts])) for key in parts[0]}
+        qd = {key: to_dev(v) for key, v in a.queries([a.len]).items()}
+        outs = []
+        for run, timed in ((a, True), (b, False)):
+            out = torch.empty((B, 1, H, 128), dtype=torch.int16, device="cuda")
+            lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+            topk = torch.full((B, 1, k), -7, dtype=torch.int32, device="cuda")
+            args = (run.dev.cache, tok["kv"], tok["gate"], tok["ik"], tok["ig"], run.bias_dev["bias"],
+                    run.bias_dev["idx_bias"], 1, qd["qI"], qd["w"], qd["q"], topk, out, lse, run.dev.ws,
+                    run.dev.ws_bytes, None)
+            if timed:
+                lca.lca_csa_step_timed(*args, ev)
+            else:
+                lca.lca_csa_step(*args)
+            run.len += 1
+            torch.cuda.synchronize()
+            outs.append((from_dev(topk), from_dev(out, np.uint16), from_dev(lse)))
+        (tka, oa, la), (tkb, ob, lb) = outs
+        assert np.array_equal(tka, tkb) and np.array_equal(oa, ob)
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+        assert all(hev.elapsed_ms(ev[i], ev[i + 1]) >= 0 for i in range(3))
+        assert hev.elapsed_ms(ev[1], ev[2]) > 0 and hev.elapsed_ms(ev[2], ev[3]) > 0
+    va, vb = a.dev.views(), b.dev.views()
+    for key in va:
+        assert np.array_equal(va[key].cpu().numpy(), vb[key].cpu().numpy()), key
