@@ -158,6 +158,9 @@ struct ScoreLds {
   uint32_t range;
   int lo;
   int lo_reached;  // hist_cmin_bin found its bin
+  uint32_t lo_above;  // hist_cmin_bin: the count in the bins above it
+  uint32_t lo_key;    // in-launch threshold: the record's floor key
+  uint32_t sub[256];  // in-launch threshold: keys of the floor's bin by their next 8 bits
   int coop_last;         // this workgroup is the last of its query to arrive
   uint32_t coop_top;      // this workgroup's largest key; for the last to arrive, the query's
   uint32_t coop_bound;    // the last to arrive: the highest record floor
@@ -395,9 +398,11 @@ __device__ __forceinline__ int hist_cmin_bin(ScoreLds& S, uint32_t cmin) {
   if (excl < cmin && excl + cnt >= cmin) {
     uint32_t c = excl;
     for (int i = 1; i <= kPerT; ++i) {
+      const uint32_t above = c;
       c += S.hist[hi_b - i];
       if (c >= cmin) {
         S.lo = hi_b - i;
+        S.lo_above = above;
         S.lo_reached = 1;
         break;
       }
@@ -463,6 +468,7 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
   int tsb[kTailIters];
   if (has_tail) load_keys<false, kTailIters>(codes, scl, wave_t0, n2, (lane >> 4) & 1, N, tvs, tsb);
   for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
+  if (a.coop && tid < 256) S.sub[tid] = 0;
   if (wave == 0) quantise_query(a, S, qraw);
   __syncthreads();  // quantised query and bounds visible
   query_operands(S, Q);
@@ -507,9 +513,9 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
 #pragma unroll
   for (int w = 0; w < kScoreWaves; ++w) range += S.wcnt[w];
   int lo = low_bin;
-  // in-launch threshold: the workgroup's candidates reach down as far as a.cmin of them fit (whole bins);
+  // in-launch threshold: the workgroup's candidates reach down as far as its record holds them (pref_slots);
   // the keys below the range are counted too when the range holds fewer than that
-  const uint32_t need = a.coop ? (uint32_t)a.cmin + 1u : (uint32_t)a.cmin;
+  const uint32_t need = a.coop ? (uint32_t)a.pref_slots + 1u : (uint32_t)a.cmin;
   const bool all_in = range < need && low_bin > 0;
   if (all_in) {
     // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
@@ -521,21 +527,71 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
     if (!a.coop) lo = hist_cmin_bin(S, (uint32_t)a.cmin);
   }
   if (a.coop) {
-    // the lowest bin at which the chunk's count from the top still fits cmin candidates: the bin just above
-    // the one where it first exceeds cmin (among the 17 counted bins, which hold more than cmin keys
-    // unless all_in; then over the whole histogram, or bin 0 when the chunk has no more than cmin keys)
+    // The floor: the lowest key at which the chunk's count from the top still fits its record (need - 1
+    // keys). First the bin B where the count from the top reaches need, with the count in the bins above
+    // it (among the 17 counted bins, which hold need keys unless all_in; then over the whole histogram;
+    // no such bin: every counted key fits, floor at low_bin, or 0 with all_in). Then a histogram of B's
+    // keys by their next 8 bits: the floor is the lowest boundary of those sub-bins at which the count
+    // still fits. (A floor on whole bins sits above the query's k-th key whenever one chunk holds more
+    // than its record's worth of keys in a crowded bin that also holds the k-th.)
     if (all_in) {
-      lo = hist_cmin_bin(S, need);
-      lo = S.lo_reached ? lo + 1 : 0;
-    } else if (wave == 0) {
-      const bool in = lane <= top_bin - low_bin;
-      const uint32_t c = wave_incl_scan(in ? S.hist[top_bin - lane] : 0u);  // count of bins top_bin..top_bin-lane
-      const uint64_t over = __ballot(in && c >= need);
-      if (lane == 0) S.lo = over ? top_bin - (__ffsll((long long)over) - 1) + 1 : low_bin;
+      hist_cmin_bin(S, need);  // S.lo, S.lo_above, S.lo_reached
+    } else {
+      if (tid == 0) S.lo_reached = 0;
+      __syncthreads();
+      if (wave == 0) {
+        const bool in = lane <= top_bin - low_bin;
+        const uint32_t h = in ? S.hist[top_bin - lane] : 0u;
+        const uint32_t c = wave_incl_scan(h);  // count of bins top_bin..top_bin-lane
+        const uint64_t over = __ballot(in && c >= need);
+        if (over && lane == __ffsll((long long)over) - 1) {
+          S.lo = top_bin - lane;
+          S.lo_above = c - h;
+          S.lo_reached = 1;
+        }
+      }
+      __syncthreads();
+    }
+    uint32_t floor_key;
+    if (!S.lo_reached) {
+      floor_key = all_in ? 0u : (uint32_t)low_bin << 20;
+    } else {
+      const uint32_t B = (uint32_t)S.lo, room = need - 1u - S.lo_above;  // keys of B the record can take
+#pragma unroll
+      for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
+        const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
+        if (key != 0 && (key >> 20) == B) atomicAdd(&S.sub[(key >> 12) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l: sub-bins 255-4l .. 252-4l; the first whose count from the top exceeds room
+        uint32_t h4[4], c4 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h4[i] = S.sub[255 - 4 * lane - i];
+          c4 += h4[i];
+        }
+        const uint32_t incl = wave_incl_scan(c4);
+        if (incl - c4 <= room && incl > room) {
+          uint32_t c = incl - c4, sb = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (c + h4[i] > room) {
+              sb = (uint32_t)(255 - 4 * lane - i);
+              break;
+            }
+            c += h4[i];
+          }
+          const uint64_t f = ((uint64_t)B << 20) + ((uint64_t)(sb + 1u) << 12);  // (B + 1) << 20 when sb = 255
+          S.lo_key = f > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)f;  // all-ones: no candidates
+        }
+      }
+      __syncthreads();
+      floor_key = S.lo_key;
     }
     if (tid == 0) S.coop_top = kmax;
     __syncthreads();
-    return all_in ? lo : S.lo;
+    return (int)floor_key;
   }
   hist_publish(a, S, q, lo, top_bin);
   return lo;
@@ -648,13 +704,12 @@ __device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A record: the keys at LDS offsets 0..n-1 (blocks j0..j0+n-1) in bins >= lo, in block order, zero-padded
-// to R words (the caller's lo keeps them within R), and its header (top: the workgroup's largest key).
-// Every thread calls it.
-__device__ __forceinline__ void coop_record(const uint32_t* lk, int n, int64_t j0, int lo, uint32_t top,
+// A record: the keys at LDS offsets 0..n-1 (blocks j0..j0+n-1) >= the floor key L, in block order,
+// zero-padded to R words (the caller's floor keeps them within R), and its header (the floor key, the bin
+// of the workgroup's largest key, the count). Every thread calls it.
+__device__ __forceinline__ void coop_record(const uint32_t* lk, int n, int64_t j0, uint32_t L, uint32_t top,
                                             uint64_t* hdr, uint64_t* cand, int R, uint32_t* wsum) {
   constexpr int kPer = kScoreChunk / kScoreThreads;  // consecutive blocks per thread
-  const uint32_t L = (uint32_t)lo << 20;
   const int i0 = (int)threadIdx.x * kPer;
   uint32_t kv[kPer];
   uint32_t c = 0;
@@ -674,7 +729,7 @@ __device__ __forceinline__ void coop_record(const uint32_t* lk, int n, int64_t j
     }
   }
   for (int i = (int)total + (int)threadIdx.x; i < R; i += kScoreThreads) st_agent64(&cand[i], 0ull);
-  if (threadIdx.x == 0) st_agent64(hdr, ((uint64_t)top << 32) | ((uint64_t)(uint32_t)lo << 16) | total);
+  if (threadIdx.x == 0) st_agent64(hdr, ((uint64_t)L << 32) | ((uint64_t)(top >> 20) << 16) | total);
   __syncthreads();  // wsum is reused by the next call
 }
 
@@ -772,10 +827,11 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
   // ---- headers: the highest and lowest floor, the largest key and the count over all records
   if (wave * 64 < G) {
     const bool hv = tid < G;
-    const uint32_t f = (uint32_t)(h >> 16) & 0xFFFFu;
+    const uint64_t f = h >> 32;  // the record's floor key
     uint64_t fmin = hv ? f : ~0ull, fmax = hv ? f : 0ull;
     wave_minmax_u64(fmin, fmax);
-    uint64_t dummy = ~0ull, top = hv ? (h >> 32) : 0ull;
+    // an upper bound of the record's keys: the end of its largest key's bin
+    uint64_t dummy = ~0ull, top = hv ? ((((h >> 16) & 0xFFFull) << 20) | 0xFFFFFull) : 0ull;
     wave_minmax_u64(dummy, top);
     const uint32_t cnt = wave_incl_scan(hv ? (uint32_t)h & 0xFFFFu : 0u);
     if (lane == 63) {
@@ -787,17 +843,17 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
   }
   for (int i = tid; i < kRadixBins; i += kScoreThreads) T.hist[i] = 0u;  // (beyond the score LDS)
   __syncthreads();
-  const uint32_t F = S.coop_bound;
+  const uint32_t F = S.coop_bound;  // the highest floor key
   int32_t* out = q_list(a, q);
   int32_t* out2 = a.topk ? a.topk + (size_t)q * a.k : nullptr;
   uint32_t n = 0;
-  bool fast = F < 4096u;  // (F = 4096: a record whose top bin alone holds more than cmin keys)
+  bool fast = F != 0xFFFFFFFFu;  // (all ones: a record holds no key, its top bin alone overflowing it)
   if (fast) {
     // ---- radix select of the k-th largest key among the candidates (keys >= Fk, all <= the largest key
     // Kt, so they share the bits above the highest bit in which Fk and Kt differ), kRadixBits at a time,
     // until the digit bin that holds it is taken whole or the bits run out (equal keys). The first pass
     // also counts the candidates.
-    const uint32_t Fk = F ? F << 20 : 1u, Kt = S.coop_top;
+    const uint32_t Fk = F ? F : 1u, Kt = S.coop_top;
     int hb = 31 - __clz(Fk ^ Kt);
     hb = hb < 0 ? 0 : hb;
     uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
@@ -897,7 +953,7 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
   }
   if (!fast) {
     // fewer than k keys >= F (a crowded chunk): a lower bound of the k-th key, then the key row
-    const uint32_t Lkey = S.coop_total >= (uint32_t)a.k ? S.coop_lmin << 20 : 0u;
+    const uint32_t Lkey = S.coop_total >= (uint32_t)a.k ? S.coop_lmin : 0u;
     __syncthreads();
     n = coop_select_row(a, T, q, N, Lkey, out, out2);
   }
@@ -942,8 +998,9 @@ __global__ __launch_bounds__(kScoreThreads, 4) void index_select_kernel(ScanArgs
   const int fold_col = (int)(((unsigned)q * 37u) % (unsigned)a.n_cols);
   const int j_tail = a.fold_tail && c0 == fold_col ? a.n_cols * kScoreChunk : -1;
   ScoreLds& S = L.u.s.sc;
-  const int lo = j_begin + kScoreChunk <= N ? score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys)
-                                            : score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys);
+  const uint32_t lo = (uint32_t)(j_begin + kScoreChunk <= N
+                                     ? score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys)
+                                     : score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys));
   // this workgroup's record (the folded chunk's in its own record, after the others)
   uint64_t* hdr = q_rec(a, q);
   uint64_t* cw = hdr + kRecHdrSlots;
