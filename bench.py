@@ -89,6 +89,8 @@ def parse_args():
                    help="skip the second timed region (per-kernel events): no kernel durations, no roofline")
     p.add_argument("--replicas", type=int, default=0,
                    help="copies of the layer caches run round-robin (0: enough for 512 MB per round; 1: warm)")
+    p.add_argument("--graph", action="store_true",
+                   help="time the decode step as HIP graph replays (lca_ragged_step_graph: lengths on the device)")
     return p.parse_args()
 
 
@@ -188,6 +190,15 @@ class Layer:
 
     def ingest(self, tok):
         """T tokens of every sequence ([B][T][...] device tensors) into the cache."""
+        if getattr(self, "ragged_lens", None) is not None:
+            # graph mode: the cache is driven through the ragged calls (lengths on the device later)
+            np = self.np
+            T = tok["kv"].shape[1]
+            b = self.bias_dev
+            self.dev.ragged_ingest(self.ragged_lens, np.full(self.B, T, np.int32), tok["kv"], tok.get("gate"),
+                                   b.get("bias"), tok.get("ik"), tok.get("ig"), b.get("idx_bias"))
+            self.ragged_lens += T
+            return
         if self.swa:
             self.dev.append(tok["kv"], None)
             return
@@ -613,6 +624,135 @@ def persist_bench(args, wl):
     return 0
 
 
+def graph_bench(args, wl):
+    """The decode step as HIP graph replays: every layer's step of one cache copy captured once
+    (lca_ragged_step_graph, whose kernels take the lengths from the device and whose attention launch
+    advances them), then K replays timed, copy s mod R at step s. The step inputs stay those of the first
+    decode step (the kernels' work does not depend on their values beyond the data-dependent top-k); the
+    first replay of copy 0 is checked against the oracle when the CPU baseline runs."""
+    import numpy as np
+    import torch
+    import long_context_attention_18_amd as lca
+    from long_context_attention_18_amd import configs
+    K, W = args.steps, args.warmup
+    step_bytes_1 = sum(configs.decode_step_bytes(l, wl.context + 1) * wl.batch for l in wl.layers)
+    R = args.replicas if args.replicas > 0 else max(1, min(16, -(-(512 << 20) // step_bytes_1)))
+    n_local = -(-(W + K) // R) + 2
+    t0 = time.perf_counter()
+    layers = [Layer(wl, li, layer, n_local, args.threads) for li, layer in enumerate(wl.layers)]
+    for L in layers:
+        L.ragged_lens = np.zeros(wl.batch, np.int64)
+    groups = fill_caches(layers, wl, max(4096, min(65536, (1 << 26) // (wl.batch * 768))))
+    for Ls in groups.values():
+        st = Ls[0].step_tokens(2)
+        for L in Ls:
+            L.make_step_inputs(2, st)
+            L.add_replicas(R)
+    cap = wl.context + n_local
+    # every cache has its own device lengths: each layer's attention launch advances its own
+    lens = {(L.li, r): torch.full((wl.batch,), wl.context, dtype=torch.int64, device="cuda")
+            for L in layers for r in range(R)}
+    T_dev = torch.ones((wl.batch,), dtype=torch.int32, device="cuda")
+    # the checked layers: the first, and the first CSA layer when it is another
+    chk_layers = [] if args.no_cpu_baseline else [layers[0]] + [L for L in layers[1:] if L.csa][:1]
+    for L in chk_layers:
+        L.kept[0] = {"out": torch.empty_like(L.out)}
+        if L.csa:
+            L.kept[0]["topk"] = torch.empty_like(L.topk)
+    check = chk_layers or None
+    torch.cuda.synchronize()
+    log(f"caches filled through the ragged calls in {time.perf_counter() - t0:.1f} s; {R} cop{'y' if R == 1 else 'ies'}")
+    graphs = []
+    side = torch.cuda.Stream()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            st = torch.cuda.current_stream().cuda_stream
+            for L in layers:
+                dev = L.reps[r]
+                ptrs = L.step_ptrs[0]
+                kept = L.kept.get(0) if r == 0 else None
+                out = (kept["out"] if kept else L.out).data_ptr()
+                if L.csa:
+                    kv, gate, ik, ig, qI, w, q = ptrs
+                    topk = (kept["topk"] if kept else L.topk).data_ptr()
+                    bias = (L.bias_dev["bias"].data_ptr(), L.bias_dev["idx_bias"].data_ptr())
+                elif L.swa:
+                    (kv, q), gate, ik, ig, qI, w, topk, bias = ptrs, None, None, None, None, None, None, (None, None)
+                else:
+                    (kv, gate, q), ik, ig, qI, w, topk = ptrs, None, None, None, None, None
+                    bias = (L.bias_dev["bias"].data_ptr(), None)
+                rc = L._lib.lca_ragged_step_graph(L.rep_refs[r], 1, cap, lens[(L.li, r)].data_ptr(), T_dev.data_ptr(),
+                                                  kv, gate,
+                                                  ik, ig, bias[0], bias[1], qI, w, q, topk, out, None, dev.ws,
+                                                  dev.ws_bytes, st)
+                if rc != 0:
+                    raise lca.LcaError("lca_ragged_step_graph", rc)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # replay 0 (copy 0, position context): its outputs are kept for the oracle before later replays of the
+    # same graph overwrite them
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    first = {L.li: {k: v.clone() for k, v in L.kept[0].items()} for L in chk_layers}
+    for s in range(1, max(W, 1)):
+        graphs[s % R].replay()
+    torch.cuda.synchronize()
+    W = max(W, 1)
+    hev = HipEvents()
+    e0, e1 = hev.create(), hev.create()
+    torch.cuda._sleep(int(SPIN_CYCLES * 20))
+    h0 = time.perf_counter()
+    hev.record(e0, False)
+    for s in range(W, W + K):
+        graphs[s % R].replay()
+    hev.record(e1, False)
+    host_us = (time.perf_counter() - h0) * 1e6 / K
+    torch.cuda.synchronize()
+    total_ms = hev.elapsed_ms(e0, e1)
+    for (li, r), ln in lens.items():  # every replay took its step (none ran into the capacity)
+        n_r = len(range(r, W + K, R))
+        assert (ln.cpu().numpy() == wl.context + n_r).all(), (li, r, ln.cpu().numpy(), n_r)
+    ms_per_step = total_ms / K
+    value = wl.batch * K / (total_ms / 1e3)
+    log(f"timed {K} graph replays: {total_ms:.3f} ms on the GPU clock; {ms_per_step * 1e3:.2f} us/step; host "
+        f"{host_us:.1f} us per replay")
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4+bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "layers": layers_label(wl.layers),
+                   "launch": "graph", "cache_copies": R},
+        "host_us_per_step": round(host_us, 2), "roofline": None, "cpu_baseline": None,
+    }
+    if check is not None:
+        # the first replay of copy 0 was the step at position context with the first step's inputs: its
+        # outputs (sequence 0 of each checked layer) against the oracle
+        ok = True
+        for L in chk_layers:
+            res, dec_s, _, _, _ = oracle_sample([L], wl, 0, 1, args.threads, 0)
+            s, t, rr = res[0]
+            g_out = synth_bf16(first[L.li]["out"][0, 0].cpu().numpy())
+            rel = float(np.linalg.norm(g_out - rr["out_f64"]) / np.linalg.norm(rr["out_f64"]))
+            lok = rel <= 1e-2
+            if L.csa:
+                lok = lok and np.array_equal(first[L.li]["topk"][0, 0].cpu().numpy(), rr["topk"])
+            log(f"first replay of layer {L.li} ({L.layer.kind.upper()}) against the oracle: rel-L2 {rel:.2e}, "
+                f"{'ok' if lok else 'FAILED'}")
+            ok = ok and lok
+        result["parity_sample"] = {"queries": len(chk_layers), "ok": bool(ok)}
+    print(json.dumps(result), flush=True)
+    if "parity_sample" in result and not result["parity_sample"]["ok"]:
+        return 3
+    return 0
+
+
+def synth_bf16(u16):
+    import numpy as np
+    from long_context_attention_18_amd import synth
+    return synth.bf16_to_f32(u16.view(np.uint16)).astype(np.float64)
+
+
 def ctypes_ref(x):
     import ctypes
     return ctypes.byref(x)
@@ -639,6 +779,9 @@ def main():
     if wl.prefill_chunk:
         log(f"workload {wl.name}: {wl.note}")
         return prefill_bench(args, wl)
+    if args.graph:
+        log(f"workload {wl.name}: {wl.note}; HIP graph replays")
+        return graph_bench(args, wl)
     K, W = args.steps, args.warmup
     S = W + K
     log(f"workload {wl.name}: {wl.note}; warmup {W}, steps {K}")

@@ -442,6 +442,35 @@ lca_status lca_ragged_step(lca_cache* cache, int32_t T_max, const int64_t* len_h
                            const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev,
                            float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
+/* lca_ragged_step with the lengths on the device only, for a step captured
+ * once in a HIP graph and replayed: the call reads no length on the host.
+ * Its launches are sized for any step of T[b] <= T_max tokens that ends at
+ * or below cap_len tokens (T_max <= cap_len <= max_ctx): grids for cap_len,
+ * the compress launch every time (at most ceil(T_max / m) blocks per
+ * sequence), the largest append; each kernel takes sequence b's length and
+ * token count from len_dev[b] and T_dev[b] when it runs. At the end of the
+ * step the attention launch adds T[b] to len_dev[b] on the device, so every
+ * replay takes the next tokens (T_dev may change between replays). A
+ * sequence whose len + T[b] would exceed cap_len takes no step: its len
+ * stays, its rows are neither read nor written. len_dev (int64 [B], device,
+ * read and written) and T_dev (int32 [B], device) are the caller's, as are
+ * every input and output (fixed addresses: a replay reads and writes the
+ * same buffers, refilled by the caller between replays). The workspace
+ * (lca_workspace_bytes for max_tq >= T_max) is required for every kind: the
+ * launch's length-advance counter lives in it. The results are those of
+ * lca_ragged_step at the same lengths; bit for bit where the attention's
+ * key splits, which follow the launch sizes (here cap_len), are the same
+ * (tested against lca_csa_step and lca_hca_step on an equal cache, replay
+ * after replay), else within rounding. Checks as there, with cap_len <
+ * T_max or > max_ctx: LCA_ERR_CAPACITY; the cache must be ragged or empty.
+ * Enqueues no memset and no host synchronisation: capturable. */
+lca_status lca_ragged_step_graph(lca_cache* cache, int32_t T_max, int64_t cap_len, int64_t* len_dev,
+                                 const int32_t* T_dev, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                                 const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                                 const float* idx_bias_dev, const uint16_t* qI_dev, const float* w_dev,
+                                 const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                                 void* ws_dev, size_t ws_bytes, void* stream);
+
 /* lca_cache_snapshot for a sequence of a ragged cache that holds `len`
  * tokens (the caller's len[seq]). With dst_dev = NULL it only fills *info
  * (the layout, for sizing the buffer). */

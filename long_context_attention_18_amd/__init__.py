@@ -95,6 +95,8 @@ _SIGNATURES = {
     "lca_ragged_ingest": (_I32, [_CP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "lca_ragged_step": (_I32, [_CP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                _VP, _VP, _VP, _SZ, _VP]),
+    "lca_ragged_step_graph": (_I32, [_CP, _I32, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                     _VP, _VP, _VP, _SZ, _VP]),
     "lca_ragged_snapshot": (_I32, [_CP, _I32, _I64, _VP, _SZ, _SP, _VP]),
     "lca_status_str": (ctypes.c_char_p, [_I32]),
 }
@@ -288,6 +290,14 @@ def lca_ragged_step(cache, T_max, len_host, T_host, len_dev, T_dev, kv, gate, ik
         ctypes.byref(cache), T_max, len_host.ctypes.data, T_host.ctypes.data, _ptr(len_dev), _ptr(T_dev), _ptr(kv),
         _ptr(gate), _ptr(ik), _ptr(ig), _ptr(bias), _ptr(idx_bias), _ptr(qI), _ptr(w), _ptr(q), _ptr(topk),
         _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lca_ragged_step_graph(cache, T_max, cap_len, len_dev, T_dev, kv, gate, ik, ig, bias, idx_bias, qI, w, q, topk, out,
+                          lse, ws, ws_bytes, stream=None):
+    _check("lca_ragged_step_graph", lib().lca_ragged_step_graph(
+        ctypes.byref(cache), T_max, cap_len, _ptr(len_dev), _ptr(T_dev), _ptr(kv), _ptr(gate), _ptr(ik), _ptr(ig),
+        _ptr(bias), _ptr(idx_bias), _ptr(qI), _ptr(w), _ptr(q), _ptr(topk), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+        _stream(stream)))
 
 
 def lca_ragged_snapshot(cache, seq, length, dst, nbytes, stream=None):

@@ -273,7 +273,25 @@ __global__ __launch_bounds__(512) void attend_kernel(AttendArgs args) {
     split = (int)(logical % per_q) / hgs;
   }
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq);
+  if (args.adv_len) {
+    // lengths on the device: every workgroup counts itself in once each of its waves holds its length (the
+    // load complete), and the last one advances every sequence's length for the next step
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(args.adv_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+      if (old == gridDim.x * gridDim.y - 1u) {
+        if (lane == 0) __hip_atomic_store(args.adv_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int nb = (int)(gridDim.y / (unsigned)a.Tq);
+        for (int bb = lane; bb < nb; bb += 64)
+          args.adv_len[bb] = a.seq_len[bb] + ragged_T(a.seq_len, a.seq_T, a.seq_cap, bb);
+      }
+    }
+  }
   if (t < 0) return;  // ragged batch: no query in this row
   // visible blocks; max_blocks bounds them (0 for the window-only layer, which has no compressed stream)
   const int64_t N = min((t + 1) / a.m, a.max_blocks);

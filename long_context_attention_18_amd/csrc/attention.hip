@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int q = blockIdx.x;
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq);
   if (t < 0) return;  // ragged batch: no query in this row
 
   Query Q;

@@ -1001,6 +1001,7 @@ struct Ragged {
   int64_t max_end;
   int64_t blocks;  // most blocks one sequence completes
   int32_t units;   // most append units (window entries + tail rows) of one sequence
+  int64_t cap;     // > 0: the kernels' capacity guard (lengths on the device, see ragged_T)
 };
 
 lca_status ragged_check(lca_cache* c, int32_t T_max, const int64_t* len_h, const int32_t* T_h,
@@ -1010,7 +1011,7 @@ lca_status ragged_check(lca_cache* c, int32_t T_max, const int64_t* len_h, const
   if (c->pending != 0) return LCA_ERR_ORDER;
   if (!c->ragged && c->len != 0) return LCA_ERR_ORDER;  // a cache turns ragged while empty
   const int64_t m = c->desc.m;
-  *r = Ragged{len_d, T_d, T_max, 0, 0, 0};
+  *r = Ragged{len_d, T_d, T_max, 0, 0, 0, 0};
   for (int32_t b = 0; b < c->batch; ++b) {
     const int64_t len = len_h[b];
     const int32_t T = T_h[b];
@@ -1038,6 +1039,7 @@ lca_status ragged_ingest_impl(lca_cache* c, const Ragged& r, const uint16_t* kv,
   a.len = 0;
   a.seq_len = r.len_dev;
   a.seq_T = r.T_dev;
+  a.seq_cap = r.cap;
   a.bias = bias;
   a.idx_bias = csa ? idx_bias : nullptr;
   if (r.blocks > 0 && launch_compress(a, csa, r.blocks, s) != hipSuccess) return LCA_ERR_LAUNCH;
@@ -1046,6 +1048,66 @@ lca_status ragged_ingest_impl(lca_cache* c, const Ragged& r, const uint16_t* kv,
   if (app_out) *app_out = a;
   if (with_append && launch_append(a, csa, r.units, s) != hipSuccess) return LCA_ERR_LAUNCH;
   return LCA_OK;
+}
+
+// A ragged step's launches (lca_ragged_step; lca_ragged_step_graph when adv_len is set: the attention
+// launch then advances the lengths on the device).
+lca_status ragged_step_impl(lca_cache* cache, const Ragged& r, int64_t* adv_len, const uint16_t* kv_dev,
+                            const uint16_t* gate_dev, const uint16_t* ik_dev, const uint16_t* ig_dev,
+                            const float* bias_dev, const float* idx_bias_dev, const uint16_t* qI_dev,
+                            const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev,
+                            float* lse_dev, void* ws_dev, size_t ws_bytes, hipStream_t s) {
+  const int32_t T_max = r.T_max;
+  if ((int64_t)cache->batch * T_max > kAttendMaxQueries) return LCA_ERR_SHAPE;
+  if (!kv_dev || !q_dev || !out_dev) return LCA_ERR_NULL;
+  const int32_t kind = cache->desc.kind;
+  // the queries' view: the cache after the call, sized by the longest sequence (the argument builders
+  // check shapes against it; the kernels take each sequence's own length from len_dev / T_dev)
+  lca_cache after = *cache;
+  after.ragged = 0;
+  after.len = std::max<int64_t>(r.max_end, T_max);
+  AttendArgs args{};
+  lca_status st;
+  if (kind == LCA_KIND_CSA) {
+    st = score_args(&after, qI_dev, w_dev, true, T_max, topk_dev, false, ws_dev, ws_bytes, &args.s);
+    if (st != LCA_OK) return st;
+    args.s.seq_len = r.len_dev;
+    args.s.seq_T = r.T_dev;
+    args.s.seq_cap = r.cap;
+  }
+  st = attn_args(&after, kind, q_dev, nullptr, T_max, out_dev, lse_dev, &args.t);
+  if (st != LCA_OK) return st;
+  args.t.seq_len = r.len_dev;
+  args.t.seq_T = r.T_dev;
+  args.t.seq_cap = r.cap;
+  attend_workspace(&args, &after, T_max, ws_dev, ws_bytes);
+  if (adv_len) {
+    args.adv_len = adv_len;
+    args.adv_cnt = (uint32_t*)ws_dev + kAdvCounter;
+  }
+  if (kind == LCA_KIND_CSA) {
+    // compress; then as lca_csa_step: scores + selection with the append in the same launch, then the
+    // attention -- or score, candidate scan with the append, selection + attention
+    IngestArgs app;
+    st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, false, &app, s);
+    if (st != LCA_OK) return st;
+    cache->ragged = 1;
+    if (use_coop(&args.s, (int64_t)cache->batch * T_max)) {
+      ScanArgs sa{};
+      sa.a = args.s;
+      sa.app = app;
+      sa.app_units = r.units;
+      if (launch_index_select(sa, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+      return launch_status(launch_attend(args, cache->batch, kAttendListWs, s));
+    }
+    if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
+    if (launch_topk_select(args.s, cache->batch, s, false, &app, r.units) != hipSuccess) return LCA_ERR_LAUNCH;
+    return launch_status(launch_attend(args, cache->batch, kAttendSelect, s));
+  }
+  st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, nullptr, nullptr, bias_dev, nullptr, true, nullptr, s);
+  if (st != LCA_OK) return st;
+  cache->ragged = 1;
+  return launch_status(launch_attend(args, cache->batch, kAttendDense, s));
 }
 
 }  // namespace
@@ -1074,50 +1136,33 @@ lca_status lca_ragged_step(lca_cache* cache, int32_t T_max, const int64_t* len_h
   Ragged r;
   lca_status st = ragged_check(cache, T_max, len_host, T_host, len_dev, T_dev, &r);
   if (st != LCA_OK) return st;
-  if ((int64_t)cache->batch * T_max > kAttendMaxQueries) return LCA_ERR_SHAPE;
-  if (!kv_dev || !q_dev || !out_dev) return LCA_ERR_NULL;
-  const int32_t kind = cache->desc.kind;
-  // the queries' view: the cache after the call, sized by the longest sequence (the argument builders
-  // check shapes against it; the kernels take each sequence's own length from len_dev / T_dev)
-  lca_cache after = *cache;
-  after.ragged = 0;
-  after.len = std::max<int64_t>(r.max_end, T_max);
-  AttendArgs args{};
-  if (kind == LCA_KIND_CSA) {
-    st = score_args(&after, qI_dev, w_dev, true, T_max, topk_dev, false, ws_dev, ws_bytes, &args.s);
-    if (st != LCA_OK) return st;
-    args.s.seq_len = len_dev;
-    args.s.seq_T = T_dev;
-  }
-  st = attn_args(&after, kind, q_dev, nullptr, T_max, out_dev, lse_dev, &args.t);
-  if (st != LCA_OK) return st;
-  args.t.seq_len = len_dev;
-  args.t.seq_T = T_dev;
-  attend_workspace(&args, &after, T_max, ws_dev, ws_bytes);
-  hipStream_t s = (hipStream_t)stream;
-  if (kind == LCA_KIND_CSA) {
-    // compress; then as lca_csa_step: scores + selection with the append in the same launch, then the
-    // attention -- or score, candidate scan with the append, selection + attention
-    IngestArgs app;
-    st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, false, &app, s);
-    if (st != LCA_OK) return st;
-    cache->ragged = 1;
-    if (use_coop(&args.s, (int64_t)cache->batch * T_max)) {
-      ScanArgs sa{};
-      sa.a = args.s;
-      sa.app = app;
-      sa.app_units = r.units;
-      if (launch_index_select(sa, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
-      return launch_status(launch_attend(args, cache->batch, kAttendListWs, s));
-    }
-    if (launch_index_score(args.s, cache->batch, s) != hipSuccess) return LCA_ERR_LAUNCH;
-    if (launch_topk_select(args.s, cache->batch, s, false, &app, r.units) != hipSuccess) return LCA_ERR_LAUNCH;
-    return launch_status(launch_attend(args, cache->batch, kAttendSelect, s));
-  }
-  st = ragged_ingest_impl(cache, r, kv_dev, gate_dev, nullptr, nullptr, bias_dev, nullptr, true, nullptr, s);
-  if (st != LCA_OK) return st;
-  cache->ragged = 1;
-  return launch_status(launch_attend(args, cache->batch, kAttendDense, s));
+  return ragged_step_impl(cache, r, nullptr, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, qI_dev, w_dev,
+                          q_dev, topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, (hipStream_t)stream);
+}
+
+lca_status lca_ragged_step_graph(lca_cache* cache, int32_t T_max, int64_t cap_len, int64_t* len_dev,
+                                 const int32_t* T_dev, const uint16_t* kv_dev, const uint16_t* gate_dev,
+                                 const uint16_t* ik_dev, const uint16_t* ig_dev, const float* bias_dev,
+                                 const float* idx_bias_dev, const uint16_t* qI_dev, const float* w_dev,
+                                 const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
+                                 void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!cache_ok(cache) || !len_dev || !T_dev) return LCA_ERR_NULL;
+  if (T_max < 1 || T_max > (1 << 24)) return LCA_ERR_SHAPE;
+  if (cap_len < T_max || cap_len > cache->max_ctx) return LCA_ERR_CAPACITY;
+  if (cache->pending != 0) return LCA_ERR_ORDER;
+  if (!cache->ragged && cache->len != 0) return LCA_ERR_ORDER;  // a cache turns ragged while empty
+  if (!ws_dev) return LCA_ERR_WORKSPACE;  // the advance counter lives there
+  if (ws_bytes < lca_workspace_bytes(&cache->desc, cache->batch, T_max, cache->max_ctx)) return LCA_ERR_WORKSPACE;
+  // the launches of any step of T_max tokens per sequence that ends at or below cap_len: grids for cap_len,
+  // the compress launch always (at most ceil(T_max / m) blocks per sequence), the largest append
+  const int64_t m = cache->desc.m;
+  Ragged r{len_dev, T_dev, T_max, cap_len, 0, 0, cap_len};
+  if (cache->desc.kind != LCA_KIND_SWA) r.blocks = (T_max + m - 1) / m;
+  const int64_t win = std::min<int64_t>(T_max, cache->ring);
+  const int64_t tail = cache->desc.kind == LCA_KIND_SWA ? 0 : std::min<int64_t>(T_max, m - 1);
+  r.units = (int32_t)(win + tail);
+  return ragged_step_impl(cache, r, len_dev, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, qI_dev, w_dev,
+                          q_dev, topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -105,7 +105,7 @@ __device__ __forceinline__ float exact_block_score(const uint8_t* kc, int ks0, i
 
 // blocks visible to query row tq of sequence b (0 for a row without a query)
 __device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int b, int tq) {
-  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq);
   return t < 0 ? 0 : (t + 1) / a.m;
 }
 
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(kScoreThreads, 4) void index_select_kernel(ScanArgs
   const int b = q / a.Tq, tq = q % a.Tq;
   const int c0 = blockIdx.x;
   if (c0 >= a.n_cols) return;
-  if (query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq) < 0) return;  // ragged batch: no query in this row
+  if (query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq) < 0) return;  // ragged batch: no query in this row
   const int N = (int)visible_blocks(a, b, tq);
   if (N <= a.k) {
     // every visible block is selected: no scores; the attention takes them all without a list
@@ -1168,7 +1168,7 @@ __device__ __forceinline__ void tile_load(const uint8_t* codes, const uint8_t* s
 __device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int b, int tq, int q) {
   const int lane = threadIdx.x & 63;
   if (tq >= a.Tq) return;
-  const int64_t t = query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq);
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq);
   if (t < 0) return;  // ragged: no query in this row
   const int64_t N = (t + 1) / a.m;
   const int qg = b * a.Tq + tq;
@@ -1529,7 +1529,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs args) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = blockIdx.y;
   const int tq = q % a.Tq;
-  if (query_t(a.seq_len, a.seq_T, a.len, a.Tq, q / a.Tq, tq) < 0) return;  // ragged: no query in this row
+  if (query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, q / a.Tq, tq) < 0) return;  // ragged: no query in this row
   const int64_t N = visible_blocks(a, q / a.Tq, tq);
   if (N <= a.k) {
     // every visible block is selected; one workgroup writes the list and clears the histogram
@@ -1622,7 +1622,7 @@ __global__ __launch_bounds__(512) void select_kernel(ScoreArgs a) {
   const int64_t N = visible_blocks(a, b, tq);
   if (N <= a.k) {
     // query tiles leave no scan to write the list of a query that sees at most k blocks
-    if (a.tiles && query_t(a.seq_len, a.seq_T, a.len, a.Tq, b, tq) >= 0) {
+    if (a.tiles && query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq) >= 0) {
       int32_t* out = a.topk + (size_t)q * a.k;
       for (int i = threadIdx.x; i < a.k; i += 512) out[i] = (i < N) ? i : -1;
     }

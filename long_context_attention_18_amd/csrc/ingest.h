@@ -127,7 +127,7 @@ __device__ __forceinline__ void append_unit(const IngestArgs& a, int b, int unit
   int32_t n_win = a.n_win;
   if (a.seq_len) {  // ragged batch: this sequence's own window tokens and tail rows; units beyond them idle
     len = a.seq_len[b];
-    end = len + a.seq_T[b];
+    end = len + ragged_T(a.seq_len, a.seq_T, a.seq_cap, b);
     first = end - a.ring > len ? end - a.ring : len;
     n_win = (int32_t)(end - first);
     int64_t tail_first = (end / a.m) * a.m;

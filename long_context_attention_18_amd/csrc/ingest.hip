@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * kPoolCache) void compress_kernel(IngestArgs a)
   const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
   const int64_t j = (a.seq_len ? len / m : a.first) + blockIdx.x;
   // ragged batch: the blocks this sequence's own tokens complete (the grid covers the most of any)
-  if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;
+  if (a.seq_len && j >= (len + ragged_T(a.seq_len, a.seq_T, a.seq_cap, b)) / m) return;
   double y_n, y_r, y_i;
   pool_waves<CSA>(a, P, b, len, j, w, c, y_n, y_r, y_i);
   if (w == 0) finish_block<CSA>(a, b, j, c, y_n, y_r, y_i);
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void compress_long_kernel(IngestAr
   const int m = a.m;
   const int64_t len = a.seq_len ? a.seq_len[b] : a.len;
   const int64_t j = (a.seq_len ? len / m : a.first) + blockIdx.x;
-  if (a.seq_len && j >= (len + a.seq_T[b]) / m) return;  // ragged batch, as above
+  if (a.seq_len && j >= (len + ragged_T(a.seq_len, a.seq_T, a.seq_cap, b)) / m) return;  // ragged batch, as above
   const int64_t p0 = j * m;
   double y[3] = {0.0, 0.0, 0.0};
 #pragma unroll 1

@@ -75,9 +75,11 @@ struct IngestArgs {
   int32_t B;
   const double* inv_freq;  // [32], device copy of the cache's RoPE frequencies
   // ragged batches: sequence b holds seq_len[b] tokens before the call and adds seq_T[b] <= T of them
-  // (rows 0..seq_T[b]-1 of its inputs); null: every sequence holds len and adds T
+  // (rows 0..seq_T[b]-1 of its inputs); null: every sequence holds len and adds T. seq_cap > 0: a
+  // sequence that would hold more than seq_cap tokens adds none (ragged_T)
   const int64_t* seq_len;
   const int32_t* seq_T;
+  int64_t seq_cap;
 };
 
 // The indexer's workspace is one block per query (so its place does not depend on how many queries
@@ -117,6 +119,7 @@ struct ScoreArgs {
   // seq_len[b] + i for rows i < seq_T[b]; null: positions len - Tq + i
   const int64_t* seq_len;
   const int32_t* seq_T;
+  int64_t seq_cap;
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row broadcasts (GFX9
@@ -132,10 +135,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// Tokens sequence b adds in a ragged call: seq_T[b], or none when that would take it beyond seq_cap
+// (cap > 0: the capacity a call sized its launches for without reading the lengths on the host)
+__device__ __forceinline__ int32_t ragged_T(const int64_t* seq_len, const int32_t* seq_T, int64_t cap, int b) {
+  const int32_t T = seq_T[b];
+  return (cap > 0 && seq_len[b] + T > cap) ? 0 : T;
+}
+
 // Position of query row tq of sequence b, or -1 when the row holds no query (ragged batches)
-__device__ __forceinline__ int64_t query_t(const int64_t* seq_len, const int32_t* seq_T, int64_t len, int32_t Tq,
-                                           int b, int tq) {
-  if (seq_len) return tq < seq_T[b] ? seq_len[b] + tq : -1;
+__device__ __forceinline__ int64_t query_t(const int64_t* seq_len, const int32_t* seq_T, int64_t cap, int64_t len,
+                                           int32_t Tq, int b, int tq) {
+  if (seq_len) return tq < ragged_T(seq_len, seq_T, cap, b) ? seq_len[b] + tq : -1;
   return len - Tq + tq;
 }
 
@@ -178,6 +188,7 @@ struct AttnArgs {
   const double* inv_freq;  // [32], device copy of the cache's RoPE frequencies
   const int64_t* seq_len;  // ragged batches, as in ScoreArgs
   const int32_t* seq_T;
+  int64_t seq_cap;
 };
 
 // One-launch attention for a few queries (attend.hip): the query's compressed entries come from the
@@ -198,6 +209,8 @@ struct AttendPartial {
   float o[16][kHeadDim];
 };
 constexpr size_t kAttendCounterBytes = 8192;  // (query, group) counters: 511 queries x 4 groups x 4 B, padded
+constexpr int kAdvCounter = (int)(kAttendCounterBytes / 4) - 1;  // the length-advance counter: the last slot
+static_assert(511 * 4 <= kAdvCounter, "advance counter overlaps the (query, group) counters");
 struct AttendArgs {
   ScoreArgs s;  // selection inputs (kAttendSelect)
   AttnArgs t;
@@ -208,6 +221,10 @@ struct AttendArgs {
   // split-0 workgroups that read the window, tail copies by head group 0 of split 0), before attending
   IngestArgs app;
   int32_t app_units;
+  // a step whose lengths live on the device (capture-friendly ragged step): the last workgroup of the
+  // launch to have read its length (adv_cnt, zero between calls) adds ragged_T to every seq_len
+  int64_t* adv_len;
+  uint32_t* adv_cnt;
 };
 
 // Contiguous runs copied between a cache and a snapshot buffer (persist.hip): run i moves `bytes`

@@ -201,6 +201,26 @@ void ragged_paths() {
   // uniform calls refuse a ragged cache
   EXPECT(lca_csa_step(c, U16, U16, U16, U16, F32, F32, 1, U16, F32, U16, TOPK, O16, OF32, b.wsp(), b.ws_bytes,
                       nullptr) == LCA_ERR_ORDER);
+  // the capture-friendly step: lengths on the device only; a second ragged cache, empty
+  Bound g;
+  EXPECT(bind(g, d, 3, 20000, 131, 1));
+  int64_t* LDG = reinterpret_cast<int64_t*>(0x80000);
+  for (int i = 0; i < 3; ++i) {
+    stub_reset();
+    EXPECT(lca_ragged_step_graph(&g.c, 1, 12000, LDG, TD, U16, U16, U16, U16, F32, F32, U16, F32, U16, TOPK, O16,
+                                 OF32, g.wsp(), g.ws_bytes, nullptr) == LCA_OK);
+    EXPECT(stub_launches("compress") == 1 && stub_launches("attend") == 1);
+    EXPECT(stub_launches("index_select") + stub_launches("index_score") == 1);
+  }
+  EXPECT(g.c.ragged == 1);
+  EXPECT(lca_ragged_step_graph(&g.c, 1, 30000, LDG, TD, U16, U16, U16, U16, F32, F32, U16, F32, U16, TOPK, O16, OF32,
+                               g.wsp(), g.ws_bytes, nullptr) == LCA_ERR_CAPACITY);
+  EXPECT(lca_ragged_step_graph(&g.c, 1, 12000, LDG, TD, U16, U16, U16, U16, F32, F32, U16, F32, U16, TOPK, O16, OF32,
+                               nullptr, 0, nullptr) == LCA_ERR_WORKSPACE);
+  EXPECT(lca_ragged_step_graph(&g.c, 1, 12000, nullptr, TD, U16, U16, U16, U16, F32, F32, U16, F32, U16, TOPK, O16,
+                               OF32, g.wsp(), g.ws_bytes, nullptr) == LCA_ERR_NULL);
+  EXPECT(lca_ragged_step_graph(&b.c, 512, 12000, LDG, TD, U16, U16, U16, U16, F32, F32, U16, F32, U16, TOPK, O16,
+                               OF32, b.wsp(), b.ws_bytes, nullptr) != LCA_OK);  // B * T beyond 511
   lca_snapshot_info info;
   std::vector<uint8_t> snap(1 << 22);
   void* sp = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(snap.data()) + 255) & ~uintptr_t(255));
