@@ -81,3 +81,41 @@ def test_threshold_after_a_score_call_without_selection(ctx):
     for _ in range(2):
         qa, tk, out, lse = run.step(1)
         check_queries(run, oc, qa, tk, out, lse, [run.len - 1])
+
+
+# one indexer key input for every token: a quarter of FP4 grid values (exact in bf16; the pooled key is
+# the same vector up to the last bits of fp64, which the FP4 codes and their power-of-two scale ignore:
+# the largest magnitude 1.5 is no power of two and every element sits on the grid)
+_GRID = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 1.0], np.float32)
+_IK = (0.25 * _GRID[np.arange(64) % 8] * np.where(np.arange(64) % 3 == 0, -1.0, 1.0)).astype(np.float32)
+
+
+def _same_key(tok, pos0):
+    """Every token's indexer key input is _IK: every pooled indexer key, hence every score, is equal."""
+    out = dict(tok)
+    out["ik"] = synth.bf16_bits(np.broadcast_to(_IK, tok["ik"].shape).copy())
+    return out
+
+
+@pytest.mark.parametrize("ctx", [20001, 41001])
+def test_all_scores_equal_select_the_first_blocks(ctx):
+    """Every block gets the same indexer key, so every score ties: the top-k are the k lowest blocks. No
+    record can hold any key (each chunk's 2048 equal keys overflow it in one sub-bin), so the selecting
+    workgroup takes the key row: 5000 visible blocks (they fit its LDS) or 10250 (more than fit: straight
+    from memory). Lists, scores and outputs against the oracle, through lca_csa_step and lca_csa_attend."""
+    layer = configs.Layer("csa", 4, n_heads=16, window=128, idx_heads=8, topk=256)
+    run = LayerRun(layer, B=2, max_ctx=ctx + 8, ring=128, transform=_same_key)
+    run.fill(ctx)
+    oc = [run.oracle_caches(i, ctx + 4) for i in range(run.B)]
+    for i in range(3):
+        if i % 2 == 0:
+            qin, tk, out, lse = run.step(1)
+        else:
+            run.ingest(1)
+            qin, tk, out, lse = run.run_queries(1, fused=True)
+        scores = run.last_scores
+        if scores is not None:
+            s = scores[:, 0, : run.len // 4]
+            assert (s == s[:, :1]).all(), "the transform should make every score equal"
+        assert (tk == np.arange(layer.topk)).all(), tk[:, 0, :8]
+        check_queries(run, oc, qin, tk, out, lse, [run.len - 1])
