@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -405,6 +406,27 @@ lca_status score_args(lca_cache* cache, const uint16_t* qI_dev, const float* w_d
 // unless a chunk holds far more than its share (then the last workgroup takes them from the key rows:
 // exact, slower). Records of 32 to 256 words, as cmin needs; the last workgroup reads all of them at once
 // (at most kPrefMaxLoads words per thread).
+// The one-launch step (csa_step_kernel) takes a call whose attention splits hold at most kStepListMax
+// slots each; LCA_STEP_UNFUSED in the environment keeps the two-launch path (the same results).
+bool step_fusable(const lca_cache* before, const lca_cache* after, const AttendArgs& args) {
+  if (std::getenv("LCA_STEP_UNFUSED")) return false;
+  if (args.splits > 1 && (!args.part || !args.cnt)) return false;
+  const int64_t N_last = after->len / after->desc.m;
+  const int64_t n_list = N_last < after->desc.topk ? N_last : after->desc.topk;
+  const int64_t n_win = after->len < after->desc.window ? after->len : after->desc.window;
+  const int64_t per_split = (n_list + n_win + args.splits * 16 - 1) / (args.splits * 16) * 16;
+  (void)before;
+  return per_split <= kStepListMax;
+}
+
+// A new nonzero token for every step launch (its lists' ready words compare against it)
+uint32_t next_step_token() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t t = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  if (t == 0u) t = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return t;
+}
+
 bool use_coop(ScoreArgs* a, int64_t nq) {
   if (a->tiles || a->chunk_step != 0) return false;
   const int64_t nb = a->len / a->m;  // the most blocks a query of the call sees
@@ -690,6 +712,25 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
   if (tail_first < cache->len) tail_first = cache->len;
   const int32_t units = app.n_win + (int32_t)(end - tail_first);
   if (use_coop(&args.s, (int64_t)cache->batch * T)) {
+    if (step_fusable(cache, &after, args)) {
+      // one launch: the score workgroups (scores, records, the selection by the last of each query), then
+      // the attention workgroups over the lists (and the append)
+      StepArgs sa{};
+      sa.idx.a = args.s;
+      sa.att = args;
+      sa.att.app = app;
+      sa.att.app_units = units;
+      sa.token = next_step_token();
+      sa.n_queries = cache->batch * T;
+      sa.n_idx = (sa.n_queries * args.s.n_cols + 7) / 8 * 8;
+      sa.n_att = sa.n_queries * ((after.desc.n_heads + 15) / 16) * args.splits;
+      if (!mark(1)) return LCA_ERR_LAUNCH;
+      if (launch_csa_step(sa, s) != hipSuccess) return LCA_ERR_LAUNCH;
+      if (!mark(2) || !mark(3)) return LCA_ERR_LAUNCH;
+      cache->len = end;
+      cache->pending = 0;
+      return LCA_OK;
+    }
     // two launches: scores + bound + candidates + selection (+ the append), then the attention
     ScanArgs sa{};
     sa.a = args.s;

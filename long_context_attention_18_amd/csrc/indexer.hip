@@ -57,6 +57,7 @@
 #include "ingest.h"
 #include "kernels.h"
 #include "select.h"
+#include "attend_core.h"
 
 namespace lca {
 
@@ -784,7 +785,8 @@ __device__ __forceinline__ uint32_t coop_select_row(const ScoreArgs& a, SelectLd
   if (fits && n >= (uint32_t)a.k) {
     (void)lane;
     (void)wave;
-    return select_core(a, S, (int64_t)n, lo, hi, [&](int64_t i) -> uint64_t { return S.cs[i]; }, out, out2);
+    return select_core<true>(a, S, (int64_t)n, lo, hi, [&](int64_t i) -> uint64_t { return S.cs[i]; }, out,
+                             out2);
   }
   // more candidates than the LDS holds: every key, straight from memory
   auto elem = [&](int64_t i) -> uint64_t {
@@ -799,7 +801,7 @@ __device__ __forceinline__ uint32_t coop_select_row(const ScoreArgs& a, SelectLd
     hi = e > hi ? e : hi;
   }
   __syncthreads();
-  return select_core(a, S, (int64_t)N, lo, hi, elem, out, out2);
+  return select_core<true>(a, S, (int64_t)N, lo, hi, elem, out, out2);
 }
 
 // The last workgroup of a query to arrive: the selection into the workspace list (and topk), over NL
@@ -941,7 +943,7 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
           const uint32_t pos = gb + (eb < need ? eb : need);
           const int32_t jb = (int32_t)(0xFFFFFFFFu - (uint32_t)v[u]);
           if (pos < (uint32_t)a.k) {
-            out[pos] = jb;
+            __hip_atomic_store(&out[pos], jb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (out2) out2[pos] = jb;
           }
         }
@@ -958,29 +960,20 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
     n = coop_select_row(a, T, q, N, Lkey, out, out2);
   }
   for (int i = (int)n + tid; i < a.k; i += kScoreThreads) {  // only if fewer than k were found
-    out[i] = -1;
+    __hip_atomic_store(&out[i], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (out2) out2[i] = -1;
   }
 }
 
 // grid (max(n_cols, B), B*Tq [+ 1]): x = chunk of query y; the extra last row (app_units > 0) writes the
 // step's append, workgroup x for sequence x.
+// Score workgroup (query q, chunk column c0) of the one-launch indexer. token != 0 (the step launch): the
+// last to arrive also publishes the list, once every thread's list stores have completed, by storing token
+// into the query's ready word, which the attention workgroups of the same launch wait for.
 template <int NL>
-__global__ __launch_bounds__(kScoreThreads, 4) void index_select_kernel(ScanArgs args) {  // <= 128 VGPRs
-  __shared__ CoopLds L;
-  const ScoreArgs& a = args.a;
-  if (args.app_units > 0 && (int)blockIdx.y == (int)gridDim.y - 1) {
-    const int b = blockIdx.x;
-    if (b < args.app.B)
-      for (int unit = (int)(threadIdx.x >> 6); unit < args.app_units; unit += kScoreWaves)
-        append_unit<true>(args.app, b, unit, threadIdx.x & 63);
-    return;
-  }
+__device__ __forceinline__ void index_select_wg(const ScoreArgs& a, CoopLds& L, int q, int c0, uint32_t token) {
   const int tid = threadIdx.x;
-  const int q = blockIdx.y;
   const int b = q / a.Tq, tq = q % a.Tq;
-  const int c0 = blockIdx.x;
-  if (c0 >= a.n_cols) return;
   if (query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq) < 0) return;  // ragged batch: no query in this row
   const int N = (int)visible_blocks(a, b, tq);
   if (N <= a.k) {
@@ -1029,6 +1022,163 @@ __global__ __launch_bounds__(kScoreThreads, 4) void index_select_kernel(ScanArgs
   if (!S.coop_last) return;
   if (tid == 0) __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
   coop_select<NL>(a, L, q, N);
+  if (token != 0u) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's list stores have completed
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(sync + 1, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// grid (max(n_cols, B), B*Tq [+ 1]): x = chunk of query y; the extra last row (app_units > 0) writes the
+// step's append, workgroup x for sequence x.
+template <int NL>
+__global__ __launch_bounds__(kScoreThreads, 4) void index_select_kernel(ScanArgs args) {  // <= 128 VGPRs
+  __shared__ CoopLds L;
+  if (args.app_units > 0 && (int)blockIdx.y == (int)gridDim.y - 1) {
+    const int b = blockIdx.x;
+    if (b < args.app.B)
+      for (int unit = (int)(threadIdx.x >> 6); unit < args.app_units; unit += kScoreWaves)
+        append_unit<true>(args.app, b, unit, threadIdx.x & 63);
+    return;
+  }
+  if ((int)blockIdx.x >= args.a.n_cols) return;
+  index_select_wg<NL>(args.a, L, (int)blockIdx.y, (int)blockIdx.x, 0u);
+}
+
+// ---- The CSA decode step in one launch: the indexer above and the attention over its lists ---------------
+//
+// Workgroups [0, n_idx) are the score workgroups of index_select_kernel (query-major, n_cols a query, the
+// count rounded up to a multiple of 8 so that the attention's ids keep their XCD); the rest are attention
+// workgroups (query, 16-head group, key split), placed as attend_kernel places them. An attention workgroup
+// that needs its query's list (the query sees more than k blocks) waits for the token its query's last score
+// workgroup stores once the list is complete, then loads its split's slice of the list with agent-scope
+// loads. The wait cannot deadlock: score workgroups never wait, and the attention workgroups come last in
+// the grid (they are dispatched after every score workgroup, and while they wait they hold fewer compute
+// units than the grid's score workgroups can run on). It is bounded all the same (kStepWaitTicks of the
+// 100 MHz clock): a workgroup that gives up attends no keys and poisons its partial, so the query's output
+// rows are NaN rather than silently wrong. The step's append (window entries, tail) is written by the
+// attention workgroups that read the window, as in the dense attention launch.
+struct StepAttnLds {
+  AttnWaveLds w;
+  int32_t list[kStepListMax];  // this split's slice of the list
+  int last;                    // this workgroup merges the splits
+  uint32_t timed_out;
+  float cos_t[32], sin_t[32];
+};
+
+__device__ __forceinline__ bool wait_token(const uint32_t* word, uint32_t token) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != token) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kStepWaitTicks) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Attention workgroup (query q, head group hg, key split) of the step launch.
+__device__ __forceinline__ void step_attend(const StepArgs& sa, StepAttnLds& S, int q, int hg, int split) {
+  const AttendArgs& args = sa.att;
+  const AttnArgs& a = args.t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int b = q / a.Tq, tq = q % a.Tq;
+  const int64_t t = query_t(a.seq_len, a.seq_T, a.seq_cap, a.len, a.Tq, b, tq);
+  if (t < 0) return;  // ragged batch: no query in this row
+  const int64_t N = min((t + 1) / a.m, a.max_blocks);
+  Keys K;
+  K.win_codes = a.win_codes;
+  K.blk_codes = a.blk_codes;
+  K.win_rope = a.win_rope;
+  K.blk_rope = a.blk_rope;
+  K.win_scale = a.win_scale;
+  K.blk_scale = a.blk_scale;
+  K.ring = (uint32_t)a.ring;
+  K.list = S.list;
+  K.win_row = (size_t)b * a.ring;
+  K.blk_row = (size_t)b * a.max_blocks;
+  K.n_win = (int)((int64_t)a.W < t + 1 ? (int64_t)a.W : t + 1);
+  K.win_base = (uint32_t)((t - K.n_win + 1) % a.ring);
+  K.j_max = N > 0 ? N - 1 : 0;
+  // the selection's list (k winners when N > k); a query that sees at most k blocks takes them all
+  K.use_list = N > a.k;
+  K.n_list = (int)(N > a.k ? (int64_t)a.k : N);
+  if (tid < 32) {
+    float sn, cs;
+    rope_angle(t, a.inv_freq[tid], &sn, &cs);
+    S.cos_t[tid] = cs;
+    S.sin_t[tid] = sn;
+  }
+  const int head = hg * 16 + r;
+  const bool head_ok = head < a.H;
+  u32x4 qraw[4];
+  {
+    const uint16_t* qp = a.q + (((size_t)b * a.Tq + tq) * a.H + (head_ok ? head : 0)) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qraw[ks] = head_ok ? *reinterpret_cast<const u32x4*>(qp + ks * 32 + 8 * g) : (u32x4){0u, 0u, 0u, 0u};
+  }
+  const int n_keys = K.n_win + K.n_list;
+  const int splits = args.splits;
+  const int per_split = ((n_keys + splits * 16 - 1) / (splits * 16)) * 16;
+  const int s_begin = split * per_split;
+  int s_end = min(s_begin + per_split, n_keys);
+  if (args.app_units > 0) {
+    // the step's append: every workgroup whose slots reach into the window writes all of its sequence's
+    // new window entries (the same bytes from each) and reads them back after the fence and barrier below;
+    // the tail copies (with the indexer's inputs) go to head group 0 of split 0. One wave per unit.
+    const bool reads_window = s_begin < K.n_win;
+    const bool writes_tail = hg == 0 && split == 0;
+    for (int unit = wave; unit < args.app_units; unit += kWaves)
+      if (unit < args.app.n_win ? reads_window : writes_tail) append_unit<true>(args.app, b, unit, lane);
+    __threadfence_block();
+  }
+  K.list0 = 0;
+  if (K.use_list) {
+    if (tid == 0) S.timed_out = wait_token(q_sync(args.s, q) + 1, sa.token) ? 0u : 1u;
+    __syncthreads();
+    const int l0 = min(max(s_begin - K.n_win, 0), K.n_list), l1 = min(max(s_end - K.n_win, 0), K.n_list);
+    const int32_t* lp = q_list(args.s, q);
+    for (int i = l0 + tid; i < l1; i += kScoreThreads)
+      S.list[i - l0] = __hip_atomic_load(&lp[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    K.list0 = l0;
+  } else if (tid == 0) {
+    S.timed_out = 0u;
+  }
+  __syncthreads();
+  const bool poison = S.timed_out != 0u;
+  if (poison) s_end = s_begin;
+  bf16x8 qb[4];
+  rotate_query(qraw, S.cos_t, S.sin_t, g, qb);
+  float m_run, l_run;
+  v4f O[8];
+  attend_slots<1>(K, s_begin, s_end, per_split, qb, S.w, wave, r, g, m_run, l_run, O);
+  attend_finish(args, S.w, &S.last, q, hg, split, m_run, l_run, O, poison);
+}
+
+template <int NL>
+__global__ __launch_bounds__(kScoreThreads, 4) void csa_step_kernel(StepArgs sa) {  // <= 128 VGPRs
+  __shared__ union {
+    CoopLds idx;
+    StepAttnLds att;
+  } U;
+  const int lin = (int)blockIdx.x;
+  if (lin < sa.n_idx) {
+    const int cols = sa.idx.a.n_cols;
+    const int q = lin / cols, c0 = lin - q * cols;
+    if (q < sa.n_queries) index_select_wg<NL>(sa.idx.a, U.idx, q, c0, sa.token);
+    return;
+  }
+  // the attention workgroups: consecutive logical ids (the head groups of a (query, split)) inside one XCD's
+  // share, as in attend_kernel; n_idx is a multiple of 8, so la % 8 is the XCD
+  const unsigned total = (unsigned)sa.n_att, la = (unsigned)(lin - sa.n_idx);
+  const unsigned xcd = la % 8u, pos = la / 8u;
+  const unsigned logical = xcd * (total / 8u) + min(xcd, total % 8u) + pos;
+  const int hgs = (sa.att.t.H + 15) / 16;
+  const unsigned per_q = (unsigned)(hgs * sa.att.splits);
+  const int q = (int)(logical / per_q);
+  const int hg = (int)(logical % per_q) % hgs;
+  const int split = (int)(logical % per_q) / hgs;
+  step_attend(sa, U.att, q, hg, split);
 }
 
 // ---- Many-query calls (chunked prefill): query tiles on the 32x32x64 scaled MFMA ------------------------
@@ -1666,6 +1816,18 @@ hipError_t launch_index_select(const ScanArgs& args, int32_t B, hipStream_t s) {
   else if (words <= kPrefMaxLoads * kScoreThreads)
     hipLaunchKernelGGL(index_select_kernel<kPrefMaxLoads>, dim3(gx, nq + (app ? 1u : 0u)), dim3(kScoreThreads), 0,
                        s, args);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_csa_step(const StepArgs& sa, hipStream_t s) {
+  const unsigned grid = (unsigned)(sa.n_idx + sa.n_att);
+  const int64_t words = (int64_t)(sa.idx.a.n_cols + (sa.idx.a.fold_tail ? 1 : 0)) * sa.idx.a.pref_slots;
+  if (words <= 9 * kScoreThreads)
+    hipLaunchKernelGGL(csa_step_kernel<9>, dim3(grid), dim3(kScoreThreads), 0, s, sa);
+  else if (words <= kPrefMaxLoads * kScoreThreads)
+    hipLaunchKernelGGL(csa_step_kernel<kPrefMaxLoads>, dim3(grid), dim3(kScoreThreads), 0, s, sa);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -227,6 +227,7 @@ struct AttendArgs {
   uint32_t* adv_cnt;
 };
 
+
 // Contiguous runs copied between a cache and a snapshot buffer (persist.hip): run i moves `bytes`
 // from src + y * src_stride to dst + y * dst_stride for every grid row y < n_dst (src = null: writes
 // zeros); the launcher sets `unit` (16, 4 or 1 bytes) from the addresses' alignment. Workgroup (0, 0)
@@ -262,6 +263,22 @@ hipError_t launch_topk_select(const ScoreArgs& a, int32_t B, hipStream_t s, bool
 // The in-launch-threshold score launch (ScoreArgs.coop): scores, bound, candidates and the selection of
 // every query; with app_units > 0 one more row of workgroups writes the step's append.
 hipError_t launch_index_select(const ScanArgs& args, int32_t B, hipStream_t s);
+// The CSA decode step in one launch (csa_step_kernel, indexer.hip): the one-launch indexer's score
+// workgroups, then the attention workgroups over the lists they leave (list mode, the step's append
+// written by the attention). Each query's last score workgroup stores `token` into the second word of
+// the query's sync slot once its list is complete; a new token every launch, so the word needs no reset.
+constexpr int kStepListMax = 512;                 // list slots one attention split holds in LDS
+constexpr uint64_t kStepWaitTicks = 50000000ull;  // 0.5 s of the 100 MHz clock: the list wait's bound
+struct StepArgs {
+  ScanArgs idx;       // idx.a: the scores and selection (coop); no append row
+  AttendArgs att;     // the attention (list mode) and the append
+  uint32_t token;     // nonzero
+  int32_t n_queries;  // B * Tq
+  int32_t n_idx;      // n_queries * n_cols, rounded up to a multiple of 8
+  int32_t n_att;      // n_queries * head groups * splits
+};
+static_assert(sizeof(StepArgs) <= 4096, "kernel arguments beyond 4 KiB");
+hipError_t launch_csa_step(const StepArgs& sa, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int32_t B, hipStream_t s);
 

@@ -167,7 +167,9 @@ __device__ inline void radix_bound(SelectLds& S, int64_t n, uint64_t lo, uint64_
 // The selection proper, over n elements in index order (elem(i): the i-th; lo / hi: this thread's
 // smallest and largest of the ones it read): radix select of the k-th largest, then the winners in index
 // order to out (and out2). Returns the number of winners written (min(k, n)). Every thread calls it.
-template <class Elem>
+// kAgentOut: out is written with agent-scope stores (a list that workgroups on other XCDs read in the same
+// launch).
+template <bool kAgentOut = false, class Elem>
 __device__ inline uint32_t select_core(const ScoreArgs& a, SelectLds& S, int64_t n, uint64_t lo, uint64_t hi,
                                        Elem elem, int32_t* out, int32_t* out2) {
   const int tid = threadIdx.x;
@@ -188,7 +190,8 @@ __device__ inline uint32_t select_core(const ScoreArgs& a, SelectLds& S, int64_t
     if ((e & mask) >= prefix) {
       if (pos < (uint32_t)a.k) {
         const int32_t j = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
-        out[pos] = j;
+        if constexpr (kAgentOut) __hip_atomic_store(&out[pos], j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else out[pos] = j;
         if (out2) out2[pos] = j;
       }
       ++pos;

@@ -7,6 +7,7 @@
 // the other device pointers are never dereferenced.
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -105,9 +106,22 @@ void csa_paths(int k) {
     EXPECT(lca_csa_step(c, U16, U16, U16, U16, F32, F32, 1, U16, F32, U16, TOPK, O16, nullptr, b.wsp(), b.ws_bytes,
                         nullptr) == LCA_OK);
     EXPECT(stub_launches("compress") == (completes ? 1 : 0));
-    EXPECT(stub_launches("index_select") == (one_launch ? 1 : 0) && stub_launches("attend") == 1);
+    // one launch for the indexer and the attention, or the indexer's launch(es) and the attention's
+    EXPECT(one_launch ? stub_launches("csa_step") == 1 && stub_launches("index_select") == 0 &&
+                            stub_launches("attend") == 0
+                      : stub_launches("csa_step") == 0 && stub_launches("attend") == 1);
     EXPECT(stub_launches("topk_select") == (one_launch ? 0 : 1));
   }
+  // the two-launch path on request
+  setenv("LCA_STEP_UNFUSED", "1", 1);
+  for (int i = 0; i < 2; ++i) {
+    stub_reset();
+    EXPECT(lca_csa_step(c, U16, U16, U16, U16, F32, F32, 1, U16, F32, U16, TOPK, O16, nullptr, b.wsp(), b.ws_bytes,
+                        nullptr) == LCA_OK);
+    EXPECT(stub_launches("csa_step") == 0 && stub_launches("attend") == 1);
+    EXPECT(stub_launches("index_select") == (one_launch ? 1 : 0));
+  }
+  unsetenv("LCA_STEP_UNFUSED");
   void* ev[4] = {reinterpret_cast<void*>(1), nullptr, reinterpret_cast<void*>(2), reinterpret_cast<void*>(3)};
   const int64_t len0 = c->len;
   EXPECT(lca_csa_step_timed(c, U16, U16, U16, U16, F32, F32, 1, U16, F32, U16, TOPK, O16, nullptr, b.wsp(),

@@ -10,7 +10,7 @@
 namespace {
 int g_count[16];
 const char* g_names[16] = {"copy_runs", "compress", "append", "fill_zero", "index_score", "topk_select",
-                           "index_select", "attend", "attention"};
+                           "index_select", "attend", "attention", "csa_step"};
 
 void need(bool ok, const char* what) {
   if (!ok) {
@@ -21,7 +21,7 @@ void need(bool ok, const char* what) {
 }  // namespace
 
 extern "C" int stub_launches(const char* name) {
-  for (int i = 0; i < 9; ++i)
+  for (int i = 0; i < 10; ++i)
     if (!std::strcmp(name, g_names[i])) return g_count[i];
   return -1;
 }
@@ -68,6 +68,20 @@ hipError_t launch_index_select(const ScanArgs& args, int32_t B, hipStream_t) {
        "records per query");
   need(a.cmin <= a.pref_slots, "candidates per record");
   ++g_count[6];
+  return hipSuccess;
+}
+hipError_t launch_csa_step(const StepArgs& sa, hipStream_t) {
+  const ScoreArgs& a = sa.idx.a;
+  need(sa.token != 0u && sa.n_queries >= 1 && a.coop == 1 && a.n_cols >= 1 && sa.idx.app_units == 0, "step");
+  need(sa.n_idx % 8 == 0 && sa.n_idx >= sa.n_queries * a.n_cols && sa.n_idx < sa.n_queries * a.n_cols + 8,
+       "step score workgroups");
+  const int hgs = (sa.att.t.H + 15) / 16;
+  need(sa.att.splits >= 1 && sa.n_att == sa.n_queries * hgs * sa.att.splits, "step attention workgroups");
+  need(sa.att.splits == 1 || (sa.att.part && sa.att.cnt && sa.n_att <= kAttendMaxWGs), "step partials");
+  need((int64_t)(a.n_cols + (a.fold_tail ? 1 : 0)) * a.pref_slots <= (int64_t)kPrefMaxLoads * kScoreThreads,
+       "step records per query");
+  need(sa.att.app_units >= 0 && sa.att.t.Tq == a.Tq, "step append");
+  ++g_count[9];
   return hipSuccess;
 }
 hipError_t launch_attend(const AttendArgs& args, int32_t B, int mode, hipStream_t) {
