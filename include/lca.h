@@ -287,14 +287,17 @@ lca_status lca_csa_topk_attn(lca_cache* cache, const uint16_t* q_dev, int32_t Tq
  * sequence go in (lca_csa_compress + lca_swa_tail_append: the blocks they
  * complete are pooled into D1/D3, their window entries and tail copies are
  * written) and their T queries attend (lca_csa_attend): same results, bit for
- * bit in the cache and the top-k lists. Two launches (three when a block
- * completes): compress, one launch that scores every visible block (a
- * workgroup per 2048 blocks of each query, each keeping its best candidates)
- * and has the last workgroup of each query to finish select its top-k (the
- * append rides in the same launch), then the attention. (Queries seeing more
- * than 1M blocks, or k too large for a query's chunks, take three: score,
- * candidate scan with the append, selection + attention.) For decode-sized
- * calls: B * T <= 511
+ * bit in the cache and the top-k lists. One launch (two when a block
+ * completes: compress first): workgroups that score every visible block (a
+ * workgroup per 2048 blocks of each query, each keeping its best candidates),
+ * the last of each query to finish selecting its top-k, and after them in the
+ * same grid the attention workgroups, each of which waits for its query's
+ * list (the append rides with them). With the environment variable
+ * LCA_STEP_UNFUSED set, or when a query's key split would exceed 512 keys,
+ * the indexer and the attention take a launch each (the same results, bit for
+ * bit). (Queries seeing more than 1M blocks, or k too large for a query's
+ * chunks, take three: score, candidate scan with the append, selection +
+ * attention.) For decode-sized calls: B * T <= 511
  * (else LCA_ERR_SHAPE); ring >= T + window - 1. Inputs as for the compressor
  * and lca_csa_attend; topk_dev and lse_dev may be NULL. Checks everything
  * before launching: a rejected call leaves the cache unchanged. */
@@ -307,7 +310,8 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
  * one: the same launches and results, plus hipEventRecord on `stream` of
  * events[0] before the compress launch (when a block completes), events[1]
  * before the indexer launch, events[2] after it (after the candidate scan
- * on the three-launch path) and events[3] after the attention. events is a
+ * on the three-launch path) and events[3] after the attention (on the
+ * one-launch path events[2] and events[3] both follow the step's launch). events is a
  * host array of 4 hipEvent_t (entries may be NULL: not recorded), owned by
  * the caller; events == NULL is LCA_ERR_NULL. The marks sit between the
  * launches, so they separate kernels that would otherwise follow each other
