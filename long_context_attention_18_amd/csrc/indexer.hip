@@ -157,13 +157,13 @@ struct ScoreLds {
   uint32_t wmax[kScoreWaves];
   uint32_t wcnt[kScoreWaves];  // per wave: its keys in the chunk's top bins
   uint32_t range;
-  int lo;
-  int lo_reached;  // hist_cmin_bin found its bin
-  uint32_t lo_above;  // hist_cmin_bin: the count in the bins above it
+  int lo;             // hist_cmin_bin's bin; the record floor's bin (-1: none)
+  int lo_reached;     // hist_cmin_bin found its bin
+  uint32_t lo_above;  // the count in the bins above it
   uint32_t lo_key;    // in-launch threshold: the record's floor key
   uint32_t sub[256];  // in-launch threshold: keys of the floor's bin by their next 8 bits
   int coop_last;         // this workgroup is the last of its query to arrive
-  uint32_t coop_top;      // this workgroup's largest key; for the last to arrive, the query's
+  uint32_t coop_top;      // the last to arrive: the query's largest key
   uint32_t coop_bound;    // the last to arrive: the highest record floor
   uint32_t coop_lmin;     // the lowest record floor
   uint32_t coop_total;    // candidates over all records
@@ -441,13 +441,90 @@ __device__ __forceinline__ uint4 load_query(const ScoreArgs& a, int b, int tq, S
   return qraw;
 }
 
+// In-launch threshold: the chunk's record floor and largest key (*top), from the keys in registers; every
+// thread calls it. The floor is the lowest key at which the chunk's count from the top still fits its record
+// (pref_slots words): every nonzero key goes into the LDS histogram of the top 12 key bits, wave 0 finds the
+// bin B where the count from the top first exceeds pref_slots (64 bins a round, from the largest key's bin
+// down), and a histogram of B's keys by their next 8 bits gives the lowest boundary of those sub-bins at
+// which the count still fits. No such bin: every key fits, floor 0. (A floor on whole bins sits above the
+// query's k-th key whenever one chunk holds more than its record's worth of keys in a crowded bin that also
+// holds the k-th.) Four barriers.
+template <int NA, int NB>
+__device__ __forceinline__ uint32_t coop_floor(const ScoreArgs& a, ScoreLds& S, const uint32_t (&ka)[NA],
+                                               const uint32_t (&kb)[NB], uint32_t* top) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  (void)tid;
+  const uint32_t need = (uint32_t)a.pref_slots + 1u;
+  uint32_t m = 0;
+#pragma unroll
+  for (int pr = 0; pr < NA + NB; ++pr) {
+    const uint32_t key = pr < NA ? ka[pr] : kb[pr - NA];
+    m = max(m, key);
+    if (key != 0) atomicAdd(&S.hist[key >> 20], 1u);
+  }
+  const uint32_t kmax = wg_max_key(S, m);  // (its barrier also completes the histogram)
+  if (top) *top = kmax;
+  if (wave == 0) {
+    uint32_t above = 0;  // keys in the bins above this round's
+    for (int hi = (int)(kmax >> 20); hi >= 0; hi -= 64) {
+      const int bin = hi - lane;
+      const uint32_t h = bin >= 0 ? S.hist[bin] : 0u;
+      const uint32_t c = wave_incl_scan(h) + above;  // count of bins hi..bin
+      const uint64_t over = __ballot(c >= need);
+      if (over) {
+        if (lane == __ffsll((long long)over) - 1) {
+          S.lo = bin;
+          S.lo_above = c - h;
+        }
+        break;
+      }
+      above = (uint32_t)__builtin_amdgcn_readlane((int)c, 63);
+    }
+  }
+  __syncthreads();
+  const int B = S.lo;
+  if (B < 0) return 0u;
+  const uint32_t room = need - 1u - S.lo_above;  // keys of B the record can take
+#pragma unroll
+  for (int pr = 0; pr < NA + NB; ++pr) {
+    const uint32_t key = pr < NA ? ka[pr] : kb[pr - NA];
+    if (key != 0 && (int)(key >> 20) == B) atomicAdd(&S.sub[(key >> 12) & 255u], 1u);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane l: sub-bins 255-4l .. 252-4l; the first whose count from the top exceeds room
+    uint32_t h4[4], c4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h4[i] = S.sub[255 - 4 * lane - i];
+      c4 += h4[i];
+    }
+    const uint32_t incl = wave_incl_scan(c4);
+    if (incl - c4 <= room && incl > room) {
+      uint32_t c = incl - c4, sb = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (c + h4[i] > room) {
+          sb = (uint32_t)(255 - 4 * lane - i);
+          break;
+        }
+        c += h4[i];
+      }
+      const uint64_t f = ((uint64_t)(uint32_t)B << 20) + ((uint64_t)(sb + 1u) << 12);  // (B + 1) << 20 when sb = 255
+      S.lo_key = f > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)f;  // all-ones: no candidates
+    }
+  }
+  __syncthreads();
+  return S.lo_key;
+}
+
 // One score workgroup's chunk: kScoreChunk blocks from j_begin (few-query calls: every workgroup one
 // chunk). The keys' loads go out before the query is quantised.
 // lkeys (in-launch threshold): the workgroup's LDS key array -- the chunk's keys at offsets 0..2047,
 // the folded chunk's from kScoreChunk on -- which gets every key too. Returns the lowest bin published.
 template <bool FULL>
 __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int q, int b, int tq, int N, int j_begin,
-                                           int j_tail, uint32_t* lkeys = nullptr) {
+                                           int j_tail, uint32_t* lkeys = nullptr, uint32_t* top = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   ScoreQuery Q;
   const uint4 qraw = load_query(a, b, tq, Q);
@@ -470,6 +547,7 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
   if (has_tail) load_keys<false, kTailIters>(codes, scl, wave_t0, n2, (lane >> 4) & 1, N, tvs, tsb);
   for (int i = tid; i < kHistBins; i += kScoreThreads) S.hist[i] = 0;
   if (a.coop && tid < 256) S.sub[tid] = 0;
+  if (a.coop && tid == 0) S.lo = -1;
   if (wave == 0) quantise_query(a, S, qraw);
   __syncthreads();  // quantised query and bounds visible
   query_operands(S, Q);
@@ -483,6 +561,7 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
     score_pairs<false, kTailIters>(a, S, Q, tvs, tsb, keys, codes, scl, N, j_tail, wave_t0, n2, tail_keys,
                                    lkeys ? lkeys + kScoreChunk : nullptr);
   }
+  if (a.coop) return (int)coop_floor(a, S, lane_keys, tail_keys, top);
   // ---- top of this chunk into the query's global histogram (top 12 key bits): the chunk max's bin
   // and the 16 bins below it (down to a quarter of the max), or, when those hold fewer than cmin of the
   // chunk's keys, every bin down to where the chunk's count from the top reaches cmin. Counts in a bin
@@ -514,9 +593,7 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
 #pragma unroll
   for (int w = 0; w < kScoreWaves; ++w) range += S.wcnt[w];
   int lo = low_bin;
-  // in-launch threshold: the workgroup's candidates reach down as far as its record holds them (pref_slots);
-  // the keys below the range are counted too when the range holds fewer than that
-  const uint32_t need = a.coop ? (uint32_t)a.pref_slots + 1u : (uint32_t)a.cmin;
+  const uint32_t need = (uint32_t)a.cmin;
   const bool all_in = range < need && low_bin > 0;
   if (all_in) {
     // the rest of the chunk's keys, then the highest bin at which the count from the top reaches cmin
@@ -525,74 +602,7 @@ __device__ __forceinline__ int score_chunk(const ScoreArgs& a, ScoreLds& S, int 
       const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
       if (key != 0 && (int)(key >> 20) < low_bin) atomicAdd(&S.hist[key >> 20], 1u);
     }
-    if (!a.coop) lo = hist_cmin_bin(S, (uint32_t)a.cmin);
-  }
-  if (a.coop) {
-    // The floor: the lowest key at which the chunk's count from the top still fits its record (need - 1
-    // keys). First the bin B where the count from the top reaches need, with the count in the bins above
-    // it (among the 17 counted bins, which hold need keys unless all_in; then over the whole histogram;
-    // no such bin: every counted key fits, floor at low_bin, or 0 with all_in). Then a histogram of B's
-    // keys by their next 8 bits: the floor is the lowest boundary of those sub-bins at which the count
-    // still fits. (A floor on whole bins sits above the query's k-th key whenever one chunk holds more
-    // than its record's worth of keys in a crowded bin that also holds the k-th.)
-    if (all_in) {
-      hist_cmin_bin(S, need);  // S.lo, S.lo_above, S.lo_reached
-    } else {
-      if (tid == 0) S.lo_reached = 0;
-      __syncthreads();
-      if (wave == 0) {
-        const bool in = lane <= top_bin - low_bin;
-        const uint32_t h = in ? S.hist[top_bin - lane] : 0u;
-        const uint32_t c = wave_incl_scan(h);  // count of bins top_bin..top_bin-lane
-        const uint64_t over = __ballot(in && c >= need);
-        if (over && lane == __ffsll((long long)over) - 1) {
-          S.lo = top_bin - lane;
-          S.lo_above = c - h;
-          S.lo_reached = 1;
-        }
-      }
-      __syncthreads();
-    }
-    uint32_t floor_key;
-    if (!S.lo_reached) {
-      floor_key = all_in ? 0u : (uint32_t)low_bin << 20;
-    } else {
-      const uint32_t B = (uint32_t)S.lo, room = need - 1u - S.lo_above;  // keys of B the record can take
-#pragma unroll
-      for (int pr = 0; pr < (kScoreIters + kTailIters) / 2; ++pr) {
-        const uint32_t key = pr < kScoreIters / 2 ? lane_keys[pr] : tail_keys[pr - kScoreIters / 2];
-        if (key != 0 && (key >> 20) == B) atomicAdd(&S.sub[(key >> 12) & 255u], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l: sub-bins 255-4l .. 252-4l; the first whose count from the top exceeds room
-        uint32_t h4[4], c4 = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h4[i] = S.sub[255 - 4 * lane - i];
-          c4 += h4[i];
-        }
-        const uint32_t incl = wave_incl_scan(c4);
-        if (incl - c4 <= room && incl > room) {
-          uint32_t c = incl - c4, sb = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (c + h4[i] > room) {
-              sb = (uint32_t)(255 - 4 * lane - i);
-              break;
-            }
-            c += h4[i];
-          }
-          const uint64_t f = ((uint64_t)B << 20) + ((uint64_t)(sb + 1u) << 12);  // (B + 1) << 20 when sb = 255
-          S.lo_key = f > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)f;  // all-ones: no candidates
-        }
-      }
-      __syncthreads();
-      floor_key = S.lo_key;
-    }
-    if (tid == 0) S.coop_top = kmax;
-    __syncthreads();
-    return (int)floor_key;
+    lo = hist_cmin_bin(S, (uint32_t)a.cmin);
   }
   hist_publish(a, S, q, lo, top_bin);
   return lo;
@@ -817,13 +827,14 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
   const int n_words = G * R;
   const uint64_t* hdr = q_rec(a, q);
   const uint64_t* cw = hdr + kRecHdrSlots;
-  // ---- one round of loads: the headers (thread t: record t) and every record's words (thread t, load u:
-  // word t + 512 u, so the words stay in block order along (u, wave, lane))
+  // ---- one round of loads: the headers (thread t: record t) and every record's words (wave w, load u,
+  // lane l: word 64 (NL w + u) + l, so each wave holds a contiguous run of the words, in block order along
+  // (u, lane))
   const uint64_t h = tid < G ? ld_agent64(&hdr[tid]) : 0ull;
   uint64_t v[NL];
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
-    const int w = tid + u * kScoreThreads;
+    const int w = 64 * (NL * wave + u) + lane;
     v[u] = w < n_words ? ld_agent64(&cw[w]) : 0ull;
   }
   // ---- headers: the highest and lowest floor, the largest key and the count over all records
@@ -910,35 +921,39 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
     }
     if (fast) {
       // ---- the winners in block order: the candidates above the boundary bin, and of those in it (equal
-      // keys once the bits ran out) the first `need`; per wave-load two ballot counts, one block scan
-      // over them (packed: above | in << 16)
+      // keys once the bits ran out) the first `need`. Each wave counts both kinds over its run of words
+      // (ballots), the waves exchange their counts once, and each lane's position is its wave's offset
+      // plus the count of winners before it in the wave's run.
+      uint64_t mg[NL], me[NL];
+      uint32_t cg = 0, ce = 0;
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const uint32_t key = (uint32_t)(v[u] >> 32);
         const bool in = key >= Fk;
-        const uint64_t mg = __ballot(in & ((key & mask) > prefix));
-        const uint64_t me = __ballot(in & ((key & mask) == prefix));
-        if (lane == 0 && tid + u * kScoreThreads < n_words)
-          S.flag_blk[1][u * kScoreWaves + wave] = (uint32_t)__popcll(mg) | ((uint32_t)__popcll(me) << 16);
+        mg[u] = __ballot(in & ((key & mask) > prefix));
+        me[u] = __ballot(in & ((key & mask) == prefix));
+        cg += (uint32_t)__popcll(mg[u]);
+        ce += (uint32_t)__popcll(me[u]);
       }
+      if (lane == 0) S.flag_blk[1][wave] = cg | (ce << 16);  // at most 64 NL < 2^16 each
       __syncthreads();
-      const int n_wl = (n_words + 63) >> 6;
-      uint32_t total;
-      const uint32_t off = block_excl_scan(tid < n_wl ? S.flag_blk[1][tid] : 0u, S.wmax, &total);
-      if (tid < n_wl) S.flag_blk[2][tid] = off;
-      __syncthreads();
-      uint32_t base[NL];
+      uint32_t bg = 0, be = 0, ng = 0, ne = 0;
 #pragma unroll
-      for (int u = 0; u < NL; ++u) base[u] = S.flag_blk[2][min(u * kScoreWaves + wave, kScoreIters * 32 - 1)];
+      for (int w = 0; w < kScoreWaves; ++w) {
+        const uint32_t x = S.flag_blk[1][w];
+        if (w < wave) {
+          bg += x & 0xFFFFu;
+          be += x >> 16;
+        }
+        ng += x & 0xFFFFu;
+        ne += x >> 16;
+      }
       const uint64_t lm = (1ull << lane) - 1ull;
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const uint32_t key = (uint32_t)(v[u] >> 32);
-        const bool in = key >= Fk;
-        const bool gt = in & ((key & mask) > prefix), eq = in & ((key & mask) == prefix);
-        const uint64_t mg = __ballot(gt), me = __ballot(eq);
-        const uint32_t gb = (base[u] & 0xFFFFu) + (uint32_t)__popcll(mg & lm);
-        const uint32_t eb = (base[u] >> 16) + (uint32_t)__popcll(me & lm);
+        const bool gt = (mg[u] >> lane) & 1ull, eq = (me[u] >> lane) & 1ull;
+        const uint32_t gb = bg + (uint32_t)__popcll(mg[u] & lm);
+        const uint32_t eb = be + (uint32_t)__popcll(me[u] & lm);
         if (gt | (eq & (eb < need))) {
           const uint32_t pos = gb + (eb < need ? eb : need);
           const int32_t jb = (int32_t)(0xFFFFFFFFu - (uint32_t)v[u]);
@@ -947,8 +962,9 @@ __device__ __forceinline__ void coop_select(const ScoreArgs& a, CoopLds& L, int 
             if (out2) out2[pos] = jb;
           }
         }
+        bg += (uint32_t)__popcll(mg[u]);
+        be += (uint32_t)__popcll(me[u]);
       }
-      const uint32_t ng = total & 0xFFFFu, ne = total >> 16;
       n = ng + (ne < need ? ne : need);
       n = n < (uint32_t)a.k ? n : (uint32_t)a.k;
     }
@@ -991,14 +1007,14 @@ __device__ __forceinline__ void index_select_wg(const ScoreArgs& a, CoopLds& L, 
   const int fold_col = (int)(((unsigned)q * 37u) % (unsigned)a.n_cols);
   const int j_tail = a.fold_tail && c0 == fold_col ? a.n_cols * kScoreChunk : -1;
   ScoreLds& S = L.u.s.sc;
+  uint32_t top;  // the chunk's largest key
   const uint32_t lo = (uint32_t)(j_begin + kScoreChunk <= N
-                                     ? score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys)
-                                     : score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys));
+                                     ? score_chunk<true>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys, &top)
+                                     : score_chunk<false>(a, S, q, b, tq, N, j_begin, j_tail, L.u.s.keys, &top));
   // this workgroup's record (the folded chunk's in its own record, after the others)
   uint64_t* hdr = q_rec(a, q);
   uint64_t* cw = hdr + kRecHdrSlots;
   const int R = a.pref_slots;
-  const uint32_t top = S.coop_top;
   coop_record(L.u.s.keys, min(kScoreChunk, N - j_begin), j_begin, lo, top, hdr + c0, cw + (size_t)c0 * R, R,
               S.wmax);
   if (j_tail >= 0 && j_tail < N)
