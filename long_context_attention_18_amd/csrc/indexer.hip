@@ -178,10 +178,17 @@ struct ScoreQuery {
   const float* wq;
 };
 
+// A 16-byte non-temporal load (the key stream is read once per call: its lines need not stay cached).
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // All of a wave's key loads for one chunk (kScoreIters tiles x 16 B + 1 scale byte per lane), issued
 // back to back in tile order (loads return in order, so the first tile pair can start as soon as its
-// own data is in). FULL: the whole chunk is visible, so each address is one base plus a constant
-// offset; otherwise each is clamped to the last visible block (always in bounds).
+// own data is in), non-temporal. FULL: the whole chunk is visible, so each address is one base plus a
+// constant offset; otherwise each is clamped to the last visible block (always in bounds).
 template <bool FULL, int ITERS = kScoreIters>
 __device__ __forceinline__ void load_keys(const uint8_t* codes, const uint8_t* scl, int wave_j0, int n2, int half,
                                           int N, uint4 (&bvs)[ITERS], int (&sbs)[ITERS]) {
@@ -190,8 +197,8 @@ __device__ __forceinline__ void load_keys(const uint8_t* codes, const uint8_t* s
     const uint8_t* sb = scl + (size_t)(wave_j0 + n2) * 2 + half;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      bvs[it] = *reinterpret_cast<const uint4*>(cb + it * 32 * 32);
-      sbs[it] = sb[it * 32 * 2];
+      bvs[it] = ld_stream16(cb + it * 32 * 32);
+      sbs[it] = __builtin_nontemporal_load(sb + it * 32 * 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -199,8 +206,8 @@ __device__ __forceinline__ void load_keys(const uint8_t* codes, const uint8_t* s
     for (int it = 0; it < ITERS; ++it) {
       int jb = wave_j0 + it * 32 + n2;
       jb = jb < N ? jb : N - 1;
-      bvs[it] = *reinterpret_cast<const uint4*>(codes + (size_t)jb * 32 + half * 16);
-      sbs[it] = scl[(size_t)jb * 2 + half];
+      bvs[it] = ld_stream16(codes + (size_t)jb * 32 + half * 16);
+      sbs[it] = __builtin_nontemporal_load(scl + (size_t)jb * 2 + half);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
