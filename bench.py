@@ -915,8 +915,8 @@ def main():
             ran = np.array([(t + 1) % dom.layer.m == 0 for t in t2])  # steps whose token completes a block
             idx_b = float(np.mean([score_bytes(dom.layer, wl.batch, t) for t in t2]))
             att_b = float(np.mean([attn_bytes(dom.layer, wl.batch, t) for t in t2]))
-            if float(att_us.mean()) < 1.0:
-                # the one-launch step (no attention launch after the indexer's): scores, selection, attention
+            if lca.lca_csa_step_launches(dom.dev.cache, 1, dom.dev.ws, dom.dev.ws_bytes) == 1:
+                # the one-launch step (events 2 and 3 both follow it): scores, selection, attention
                 kernels.append(("csa_step_kernel", idx_us, idx_b + att_b, 1.0))
             else:
                 kernels.append(("index_select_kernel", idx_us, idx_b, 1.0))

@@ -322,6 +322,17 @@ lca_status lca_csa_step_timed(lca_cache* cache, const uint16_t* kv_dev, const ui
                               const uint16_t* q_dev, int32_t* topk_dev, uint16_t* out_dev, float* lse_dev,
                               void* ws_dev, size_t ws_bytes, void* stream, void* const* events);
 
+/* The kernel launches lca_csa_step would make for T tokens per sequence on
+ * this cache and workspace, after the compress launch of a step whose
+ * tokens complete a block: 1 (the indexer and the attention in one launch),
+ * 2 (the indexer's launch, then the attention's) or 3 (score, candidate scan
+ * with the append, selection + attention), in *launches. Launches nothing
+ * and changes nothing; the same checks as lca_csa_step on the cache, T and
+ * the workspace (its status when they fail). For tools that time or
+ * profile the step's kernels. */
+lca_status lca_csa_step_launches(const lca_cache* cache, int32_t T, void* ws_dev, size_t ws_bytes,
+                                 int32_t* launches);
+
 /* lca_csa_step for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
  * same launches and results as lca_csa_step (bit for bit), with the

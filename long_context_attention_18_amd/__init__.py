@@ -87,6 +87,7 @@ _SIGNATURES = {
     "lca_csa_step_timed": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                   _VP, _VP]),
     "lca_csa_step_noalloc": (_I32, [_CP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "lca_csa_step_launches": (_I32, [_CP, _I32, _VP, _SZ, ctypes.POINTER(ctypes.c_int32)]),
     "lca_hca_step": (_I32, [_CP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_swa_step": (_I32, [_CP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lca_snapshot_layout": (_I32, [_CP, _SP]),
@@ -240,6 +241,14 @@ def lca_csa_step_timed(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, top
                                                            _ptr(ig), _ptr(bias), _ptr(idx_bias), T, _ptr(qI), _ptr(w),
                                                            _ptr(q), _ptr(topk), _ptr(out), _ptr(lse), _ptr(ws),
                                                            ws_bytes, _stream(stream), arr))
+
+
+def lca_csa_step_launches(cache, T, ws, ws_bytes):
+    """Kernel launches lca_csa_step makes after the compress launch: 1, 2 or 3."""
+    n = ctypes.c_int32(0)
+    _check("lca_csa_step_launches", lib().lca_csa_step_launches(ctypes.byref(cache), T, _ptr(ws), ws_bytes,
+                                                                 ctypes.byref(n)))
+    return n.value
 
 
 def lca_csa_step_noalloc(cache, kv, gate, ik, ig, bias, idx_bias, T, qI, w, q, topk, out, lse, stream=None):

@@ -675,7 +675,7 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
                          const uint16_t* ig_dev, const float* bias_dev, const float* idx_bias_dev, int32_t T,
                          const uint16_t* qI_dev, const float* w_dev, const uint16_t* q_dev, int32_t* topk_dev,
                          uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream,
-                         void* const* ev) {
+                         void* const* ev, int32_t* plan = nullptr) {
   // every check first, so a rejected call leaves the cache as it was
   lca_status st = csa_step_check(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T);
   if (st != LCA_OK) return st;
@@ -687,6 +687,12 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
   st = attn_args(&after, LCA_KIND_CSA, q_dev, nullptr, T, out_dev, lse_dev, &args.t);
   if (st != LCA_OK) return st;
   attend_workspace(&args, &after, T, ws_dev, ws_bytes);
+  const bool coop = use_coop(&args.s, (int64_t)cache->batch * T);
+  const bool one_launch = coop && step_fusable(cache, &after, args);
+  if (plan) {  // the launches the step takes after the compress, nothing launched
+    *plan = one_launch ? 1 : coop ? 2 : 3;
+    return LCA_OK;
+  }
   hipStream_t s = (hipStream_t)stream;
   // the timed variant's events: step start, indexer start, indexer end, attention end
   auto mark = [&](int i) { return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess; };
@@ -711,8 +717,8 @@ lca_status csa_step_impl(lca_cache* cache, const uint16_t* kv_dev, const uint16_
   int64_t tail_first = (end / m) * m;
   if (tail_first < cache->len) tail_first = cache->len;
   const int32_t units = app.n_win + (int32_t)(end - tail_first);
-  if (use_coop(&args.s, (int64_t)cache->batch * T)) {
-    if (step_fusable(cache, &after, args)) {
+  if (coop) {
+    if (one_launch) {
       // one launch: the score workgroups (scores, records, the selection by the last of each query), then
       // the attention workgroups over the lists (and the append)
       StepArgs sa{};
@@ -806,6 +812,18 @@ lca_status lca_csa_step(lca_cache* cache, const uint16_t* kv_dev, const uint16_t
                         uint16_t* out_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   return csa_step_impl(cache, kv_dev, gate_dev, ik_dev, ig_dev, bias_dev, idx_bias_dev, T, qI_dev, w_dev, q_dev,
                        topk_dev, out_dev, lse_dev, ws_dev, ws_bytes, stream, nullptr);
+}
+
+lca_status lca_csa_step_launches(const lca_cache* cache, int32_t T, void* ws_dev, size_t ws_bytes,
+                                 int32_t* launches) {
+  if (!cache || !launches) return LCA_ERR_NULL;
+  // the step's own checks and plan, on a copy of the cache, with stand-in inputs that nothing reads
+  static uint16_t in16[1];
+  static float in32[1];
+  static int32_t topk[1];
+  lca_cache c = *cache;
+  return csa_step_impl(&c, in16, in16, in16, in16, in32, in32, T, in16, in32, in16, topk, in16, nullptr, ws_dev,
+                       ws_bytes, nullptr, nullptr, launches);
 }
 
 lca_status lca_csa_step_timed(lca_cache* cache, const uint16_t* kv_dev, const uint16_t* gate_dev,

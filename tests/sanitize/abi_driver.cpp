@@ -112,8 +112,13 @@ void csa_paths(int k) {
                       : stub_launches("csa_step") == 0 && stub_launches("attend") == 1);
     EXPECT(stub_launches("topk_select") == (one_launch ? 0 : 1));
   }
+  // the launch plan agrees with the launches
+  int32_t plan = 0;
+  EXPECT(lca_csa_step_launches(c, 1, b.wsp(), b.ws_bytes, &plan) == LCA_OK && plan == (one_launch ? 1 : 3));
+  EXPECT(lca_csa_step_launches(c, 1, nullptr, 0, &plan) == LCA_ERR_WORKSPACE);
   // the two-launch path on request
   setenv("LCA_STEP_UNFUSED", "1", 1);
+  EXPECT(lca_csa_step_launches(c, 1, b.wsp(), b.ws_bytes, &plan) == LCA_OK && plan == (one_launch ? 2 : 3));
   for (int i = 0; i < 2; ++i) {
     stub_reset();
     EXPECT(lca_csa_step(c, U16, U16, U16, U16, F32, F32, 1, U16, F32, U16, TOPK, O16, nullptr, b.wsp(), b.ws_bytes,

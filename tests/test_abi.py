@@ -150,6 +150,13 @@ def test_order_capacity_and_kind_checks():
                                 None) == -1
     assert c.len == 0 and c.pending == 0
     c.len = 100
+    # the step's launch plan: the step's checks, nothing launched, the cache untouched
+    n = ctypes.c_int32(-1)
+    assert L.lca_csa_step_launches(ctypes.byref(c), 1, P, 1 << 30, ctypes.byref(n)) == 0 and n.value in (1, 2, 3)
+    assert L.lca_csa_step_launches(ctypes.byref(c), 512, P, 1 << 30, ctypes.byref(n)) == -2
+    assert L.lca_csa_step_launches(ctypes.byref(c), 1, None, 0, ctypes.byref(n)) == -6
+    assert L.lca_csa_step_launches(ctypes.byref(c), 1, P, 1 << 30, None) == -1
+    assert c.len == 100 and c.pending == 0
     # workspace missing / too small
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, None, 0, None) == -6
     assert L.lca_csa_indexer_topk(ctypes.byref(c), P, P, 1, P, P, 16, None) == -6

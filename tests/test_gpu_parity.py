@@ -599,6 +599,13 @@ def test_csa_step_one_launch_matches_two_launches(B, steps):
     b = LayerRun(layer, B=B, max_ctx=ctx + 16, ring=131, max_tq=3)
     for run in (a, b):
         run.fill(ctx)
+    import long_context_attention_18_amd as lca
+    assert lca.lca_csa_step_launches(a.dev.cache, 1, a.dev.ws, a.dev.ws_bytes) == 1
+    os.environ["LCA_STEP_UNFUSED"] = "1"
+    try:
+        assert lca.lca_csa_step_launches(b.dev.cache, 1, b.dev.ws, b.dev.ws_bytes) == 2
+    finally:
+        del os.environ["LCA_STEP_UNFUSED"]
     for T in steps:
         qa, tka, oa, la = a.step(T)
         os.environ["LCA_STEP_UNFUSED"] = "1"
