@@ -591,10 +591,11 @@ def test_csa_step_one_launch_matches_two_launches(B, steps):
     """The CSA step in one launch (score workgroups, then attention workgroups that wait for their query's
     list) against the two-launch path (LCA_STEP_UNFUSED) on a twin cache, k = 1024 with five key splits and
     T = 1-3 tokens per step: top-k lists, outputs, LSE and cache bytes bit for bit; the oracle on the last
-    step's queries."""
+    step's queries. 70K tokens: 9 score chunks a query, the fewest whose records hold k = 1024 (the
+    indexer's one-launch form, which the step fuses with the attention)."""
     import os
     layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=1024)
-    ctx = 9001
+    ctx = 70001
     a = LayerRun(layer, B=B, max_ctx=ctx + 16, ring=131, max_tq=3)
     b = LayerRun(layer, B=B, max_ctx=ctx + 16, ring=131, max_tq=3)
     for run in (a, b):
