@@ -90,8 +90,12 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
   WsLayout W{};
   const int64_t max_blocks = n_blocks_max(d, max_ctx);
   const size_t nq = (size_t)B * (size_t)max_tq;
+  // the attention's (query, group) counters, then its key splits' partials, then the per-query blocks: no
+  // offset depends on the call's Tq, so calls with different query counts share one workspace (the
+  // per-query state a call leaves zero stays where the next call looks for it)
   W.cnt = 0;
-  size_t off = kAttendCounterBytes;
+  W.part = align_up(kAttendCounterBytes);
+  size_t off = align_up(W.part + (size_t)kAttendMaxWGs * sizeof(AttendPartial));
   W.qbase = off;
   W.G2 = (int32_t)((max_blocks + kScanPerWG - 1) / kScanPerWG);
   if (d->kind == LCA_KIND_CSA) {
@@ -104,15 +108,14 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
     W.off_seg = q; q = align_up(q + (size_t)n_seg * 4);
     W.off_keys = q; q = align_up(q + (size_t)max_blocks * 4);
     W.off_cand = q; q = align_up(q + (size_t)max_blocks * 8);
-    W.off_sync = q; q = align_up(q + sizeof(uint64_t));      // the in-launch threshold's counter
+    W.off_sync = q; q = align_up(q + sizeof(uint64_t));      // the in-launch threshold's counter, ready word
     W.off_list = q; q = align_up(q + (size_t)kMaxTopk * 4);   // its top-k list, read by the attention
     W.off_rec = q; q = align_up(q + ((size_t)kRecHdrSlots + (size_t)n_seg * kRecMaxWords) * 8);  // its records
     W.qstride = q;
     off += nq * q;
   }
-  W.part = align_up(off);
-  // partials exist only with splits, and then (query, group, split) triples number <= kAttendMaxWGs
-  W.total = align_up(W.part + (size_t)kAttendMaxWGs * sizeof(AttendPartial));
+  // (partials exist only with splits, and then (query, group, split) triples number <= kAttendMaxWGs)
+  W.total = align_up(off);
   return W;
 }
 

@@ -586,13 +586,15 @@ def test_csa_step_timed_matches_the_step():
         assert np.array_equal(va[key].cpu().numpy(), vb[key].cpu().numpy()), key
 
 
-@pytest.mark.parametrize("B,steps", [(3, [1, 2, 1, 3, 1, 1]), (1, [1, 1, 1, 2])])
+@pytest.mark.parametrize("B,steps", [(3, [1, 2, 1, 3, 1, 3]), (1, [1, 1, 1, 2])])
 def test_csa_step_one_launch_matches_two_launches(B, steps):
     """The CSA step in one launch (score workgroups, then attention workgroups that wait for their query's
     list) against the two-launch path (LCA_STEP_UNFUSED) on a twin cache, k = 1024 with five key splits and
     T = 1-3 tokens per step: top-k lists, outputs, LSE and cache bytes bit for bit; the oracle on the last
     step's queries. 70K tokens: 9 score chunks a query, the fewest whose records hold k = 1024 (the
-    indexer's one-launch form, which the step fuses with the attention)."""
+    indexer's one-launch form, which the step fuses with the attention). The changing T also checks that
+    calls with different query counts share a workspace (the key splits' partials once lay where a call
+    with more queries keeps its per-query counters)."""
     import os
     layer = configs.Layer("csa", 4, n_heads=64, window=128, idx_heads=8, topk=1024)
     ctx = 70001
@@ -620,5 +622,5 @@ def test_csa_step_one_launch_matches_two_launches(B, steps):
     va, vb = a.dev.views(), b.dev.views()
     for k in va:
         assert np.array_equal(va[k].cpu().numpy(), vb[k].cpu().numpy()), k
-    oc = [a.oracle_caches(0, a.len)]
-    check_queries(a, oc, qa, tka, oa, la, list(range(a.len - steps[-1], a.len)), seqs=[0])
+    oc = {i: a.oracle_caches(i, a.len) for i in range(B)}
+    check_queries(a, oc, qa, tka, oa, la, list(range(a.len - steps[-1], a.len)), seqs=list(range(B)))
