@@ -169,17 +169,18 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
   }
 }
 
-// NR chunks of one wave: every gather issued first, then the chunks in order (straight-line code).
+// NR chunks of one wave (chunk u at slot0 + u stride): every gather issued first, then the chunks in order
+// (straight-line code).
 template <int NR>
-__device__ __forceinline__ void attend_round(const Keys K, int slot0, int end, const bf16x8 (&qb)[4], float* scl,
-                                             uint16_t* kd, const int (&voff)[2], int r, int g, float& m_run,
-                                             float& l_run, v4f (&O)[8]) {
+__device__ __forceinline__ void attend_round(const Keys K, int slot0, int stride, int end, const bf16x8 (&qb)[4],
+                                             float* scl, uint16_t* kd, const int (&voff)[2], int r, int g,
+                                             float& m_run, float& l_run, v4f (&O)[8]) {
   Raw buf[NR];
 #pragma unroll
-  for (int u = 0; u < NR; ++u) K.load(slot0 + u * kChunk, end, r, g, buf[u]);
+  for (int u = 0; u < NR; ++u) K.load(slot0 + u * stride, end, r, g, buf[u]);
 #pragma unroll
   for (int u = 0; u < NR; ++u)
-    attend_chunk(buf[u], slot0 + u * kChunk, end, qb, scl, kd, voff, r, g, m_run, l_run, O);
+    attend_chunk(buf[u], slot0 + u * stride, end, qb, scl, kd, voff, r, g, m_run, l_run, O);
 }
 
 // The last split's merge of a (query, group): every split's (m, l, o slice) of this thread's head h and
@@ -237,9 +238,9 @@ __device__ __forceinline__ void rotate_query(const u32x4 (&qraw)[4], const float
   }
 }
 
-// Wave `wave`'s share of a split's key slots [s_begin, s_end) (per_split slots a split): slots
-// [s_begin + wave * per, + per), in rounds of up to KR chunks whose gathers are issued together. Starts
-// the running state (m_run, l_run, O) of the wave's 16 heads.
+// Wave `wave`'s share of a split's key slots [s_begin, s_end): every 8th 32-slot chunk from the wave's
+// own, in rounds of up to KR chunks whose gathers are issued together. Starts the running state (m_run,
+// l_run, O) of the wave's 16 heads.
 template <int KR>
 __device__ __forceinline__ void attend_slots(const Keys& K, int s_begin, int s_end, int per_split,
                                              const bf16x8 (&qb)[4], AttnWaveLds& W, int wave, int r, int g,
@@ -259,22 +260,28 @@ __device__ __forceinline__ void attend_slots(const Keys& K, int s_begin, int s_e
     const int kk = 4 * h + (r >> 2);
     voff[h] = (16 * (kk & 1) + 4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
   }
-  const int per = ((per_split + kWaves * 16 - 1) / (kWaves * 16)) * 16;
-  const int w_begin = s_begin + wave * per;
-  const int w_end = min(w_begin + per, s_end);
-  const int w_chunks = (per + kChunk - 1) / kChunk;  // the same for every wave
-  for (int c = 0; c < w_chunks; c += KR) {
-    const int slot0 = w_begin + c * kChunk;
-    switch (min(KR, w_chunks - c)) {
-      case 1: attend_round<1>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
+  // the split's 32-slot chunks (the last one partial) dealt to the waves in turn: wave w takes chunks w,
+  // w + 8, ..., so no wave holds more than one chunk beyond another's and only the split's last chunk is
+  // partial (per-wave ranges rounded each wave's share up to whole chunks)
+  (void)per_split;
+  constexpr int kStride = kWaves * kChunk;
+  const int n_ch = (s_end - s_begin + kChunk - 1) / kChunk;
+  const int mine = n_ch > wave ? (n_ch - wave + kWaves - 1) / kWaves : 0;
+  for (int c = 0; c < mine; c += KR) {
+    const int slot0 = s_begin + (wave + c * kWaves) * kChunk;
+    switch (min(KR, mine - c)) {
+      case 1: attend_round<1>(K, slot0, kStride, s_end, qb, scl, kd, voff, r, g, m_run, l_run, O); break;
       case 2:
-        if constexpr (KR >= 2) attend_round<2>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O);
+        if constexpr (KR >= 2)
+          attend_round<2>(K, slot0, kStride, s_end, qb, scl, kd, voff, r, g, m_run, l_run, O);
         break;
       case 3:
-        if constexpr (KR >= 3) attend_round<3>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O);
+        if constexpr (KR >= 3)
+          attend_round<3>(K, slot0, kStride, s_end, qb, scl, kd, voff, r, g, m_run, l_run, O);
         break;
       default:
-        if constexpr (KR >= 4) attend_round<KR>(K, slot0, w_end, qb, scl, kd, voff, r, g, m_run, l_run, O);
+        if constexpr (KR >= 4)
+          attend_round<KR>(K, slot0, kStride, s_end, qb, scl, kd, voff, r, g, m_run, l_run, O);
         break;
     }
   }
