@@ -115,9 +115,15 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
     ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.r1[tt]), qb[3], ar, 0, 0, 0);
     if (g == 0) scl[tt * 16 + r] = cur.sc[tt];
     sc4[tt] = *reinterpret_cast<const v4f*>(scl + tt * 16 + 4 * g);
-    const int slot0 = chunk_slot + tt * 16 + 4 * g;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) Sv[tt][v] = (slot0 + v < end) ? an[v] * sc4[tt][v] + ar[v] : -INFINITY;
+    for (int v = 0; v < 4; ++v) Sv[tt][v] = fmaf(an[v], sc4[tt][v], ar[v]);
+  }
+  if (chunk_slot + kChunk > end) {  // the split's last chunk: slots at or beyond end are empty
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (chunk_slot + tt * 16 + 4 * g + v >= end) Sv[tt][v] = -INFINITY;
   }
   // online softmax of head r (its keys are spread over the 4 lane groups)
   float mx = max3_raw(max3_raw(Sv[0][0], Sv[0][1], Sv[0][2]), max3_raw(Sv[0][3], Sv[1][0], Sv[1][1]),
@@ -133,12 +139,13 @@ __device__ __forceinline__ void attend_chunk(const Raw& cur, int chunk_slot, int
     m_run = m_new;
   }
   const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+  const float mC = m_use * kC;
   float rs = 0.0f;
   u32x4 pr, pn;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const float p0 = __builtin_amdgcn_exp2f((Sv[0][v] - m_use) * kC);
-    const float p1 = __builtin_amdgcn_exp2f((Sv[1][v] - m_use) * kC);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(Sv[0][v], kC, -mC));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(Sv[1][v], kC, -mC));
     rs = v == 0 ? p0 + p1 : rs + (p0 + p1);  // the first pair starts the sum (no add of +0)
     pr[v] = pack_bf16(p0, p1);
     pn[v] = pack_bf16(p0 * sc4[0][v], p1 * sc4[1][v]);
