@@ -19,8 +19,11 @@
 // lanes a, a+4, a+8, a+12 address), each lane addressing the key its K index needs. The FP8 codes and
 // the BF16 RoPE dims are exact in bf16; the per-entry fp32 scale multiplies the nope logits and is
 // folded into P for the nope output dims. The next chunk's gathers are issued before the current chunk
-// is computed, into the second of two LDS buffers, one barrier per chunk. Calls with up to 511 queries
-// use attend.hip.
+// is computed, into the second of two LDS buffers, one barrier per chunk. The window's slots start at the
+// first whole 16-key tile after the compressed ones, so a tile reads one array, whose base (the sequence's
+// rows) is the same for every lane and takes 32-bit byte offsets; each gathering thread resolves its key's
+// entry itself (the top-k row is in LDS). Waves 0-1 gather FP8 codes and scales, waves 2-3 RoPE dims, each
+// kind in its own copy of the chunk loop. Calls with up to 511 queries use attend.hip.
 #include "attn_common.h"
 #include "dev_formats.h"
 #include "kernels.h"
@@ -33,7 +36,7 @@ constexpr int kMWaves = 4;       // one wave per 16-head group
 constexpr int kMThreads = kMWaves * 64;
 constexpr int kMChunk = 32;      // keys per step: 16-key tiles, pairs of them one PV K-step
 constexpr int kMTiles = kMChunk / 16;
-static_assert(kMChunk % 32 == 0 && kMChunk <= 64, "whole PV K-steps; make_entries uses one wave");
+static_assert(kMChunk % 32 == 0 && kMChunk <= 64, "whole PV K-steps");
 // Key-major chunk layout (bf16 offsets): row r of 16-key tile tt at tt * kKdTile + r * kKdStride. In
 // 4-byte LDS banks the row stride is 12 (mod 64) and tile 1 starts 32 banks after tile 0, so the 16 rows
 // a QK operand read touches (4 banks each) and the four 8-bank row pieces a transposing read gathers per
@@ -45,102 +48,92 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct ManyLds {
-  uint16_t kd[2][kKdBuf];                 // key-major chunk (two buffers)
-  float scl[2][kMChunk];                  // the keys' FP8 scales (>= 0); -1 marks a slot without a key
-  uint32_t kbad[2];                       // per chunk buffer: some slot of the chunk holds no key
-  uint32_t ent[2][kMChunk];               // entries of the slots of the chunk after next (~0: no key)
-  uint32_t ebad[2];                       // per entry buffer: some slot holds no key
-  int32_t list[kMaxTopk];                 // CSA: the query's top-k row
+  uint16_t kd[2][kKdBuf];  // key-major chunk (two buffers)
+  float scl[2][kMChunk];   // the keys' FP8 scales (>= 0); -1 marks a slot without a key
+  uint32_t kbad[2];        // per chunk buffer: some slot of the chunk holds no key
+  int32_t list[kMaxTopk];  // CSA: the query's top-k row
   float cos_t[32], sin_t[32];
 };
 
 // The gather of one thread for one chunk: part pp = tid / 16 (dims 8pp .. 8pp+7; pp < 8 the FP8 nope
 // codes, pp >= 8 the BF16 RoPE dims), key r = tid % 16 of both tiles.
-struct Fetch {
-  u32x2 code[kMTiles];
-  u32x4 rope[kMTiles];
-  float scale[kMTiles];
-  bool valid[kMTiles];
-  bool bad;  // some slot of the chunk holds no key (the same for every thread)
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
 };
 
+struct Fetch {
+  u32x4 d[kMTiles];  // the part's dims: FP8 codes in the first two words (pp < 8), else BF16 RoPE dims
+  float scale[kMTiles];
+  bool valid[kMTiles];
+};
+
+// One query's key slots: [0, n_first) the top-k row (CSA) or the visible blocks (HCA), then, from the
+// first whole 16-key tile on (win0), the window positions t - n_win + 1 .. t; slots in between hold no
+// key. A tile is thus all compressed or all window, and the choice of array is the same for every lane.
 struct Query {
-  const uint8_t *blk_codes, *win_codes;
+  const uint8_t *blk_codes, *win_codes;  // this sequence's rows (offsets below stay under 2^32 bytes)
   const uint16_t *blk_rope, *win_rope;
   const float *blk_scale, *win_scale;
-  size_t blk_row, win_row;  // b * max_blocks, b * ring
   int32_t N;                // visible blocks
-  int32_t n_first, total;   // slots [0, n_first): top-k row or dense blocks; then n_win window positions
+  int32_t n_first;          // top-k slots or visible blocks
+  int32_t win0, total;      // first window slot (n_first rounded up to 16), win0 + n_win
   int32_t win_base, ring;   // ring slot of the first window position (t - n_win + 1)
   bool dense;
 };
 
-// entry of key slot `slot` (32-bit index arithmetic): slots [0, n_first) the top-k row or the dense
-// blocks, then the window positions t - n_win + 1 .. t; branch-free, with an in-bounds entry for slots
-// that hold no key
-__device__ __forceinline__ void slot_entry(const Query& Q, const int32_t* list, int slot, size_t* e, bool* win,
-                                           bool* valid) {
-  const bool in_first = slot < Q.n_first;
-  const int j = Q.dense ? slot : list[in_first ? slot : 0];
-  const bool ok_blk = j >= 0 && j < Q.N;
-  const bool live = slot < Q.total;
-  int ws = Q.win_base + (slot - Q.n_first);  // < 2 ring for a live window slot: one conditional wrap
-  ws = ws >= Q.ring ? ws - Q.ring : ws;
-  *valid = live && (!in_first || ok_blk);
-  *win = !in_first;
-  *e = in_first ? Q.blk_row + (uint32_t)(ok_blk ? j : 0) : Q.win_row + (uint32_t)(live ? ws : 0);
-}
-
-// The entries of one chunk's slots, once per chunk (the first kMChunk lanes of wave 0), for the threads that
-// gather them: ent[slot] = the entry index in its array (window or compressed: slot >= n_first), ~0
-// for a slot without a key; *ebad: whether any slot holds none.
-__device__ __forceinline__ void make_entries(const Query& Q, const int32_t* list, int chunk0, uint32_t* ent,
-                                             uint32_t* ebad) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < kMChunk) {
-    size_t e;
-    bool w, ok;
-    slot_entry(Q, list, chunk0 + lane, &e, &w, &ok);
-    ent[lane] = ok ? (uint32_t)e : 0xFFFFFFFFu;  // entry indices stay below 2^32 (B x rows x 196 B of HBM)
-    const uint64_t m = __ballot(!ok);
-    if (lane == 0) *ebad = m != 0 ? 1u : 0u;
-  }
-}
-
-__device__ __forceinline__ void fetch(const Query& Q, const uint32_t* ent, const uint32_t* ebad, int chunk0, int pp,
-                                      int r, Fetch& F) {
-  F.bad = *ebad != 0u;
+// The gathers of key r of the chunk's two tiles (this thread's part). A slot without a key reads row 0
+// of its array (in bounds) and is flagged; its row is zeroed when staged. Branch-free (the array choice is
+// uniform), so that the compiler can keep two chunks' loads in flight and wait for the older ones only.
+template <bool NOPE>
+__device__ __forceinline__ void fetch(const Query& Q, const int32_t* list, int chunk0, int pp, int r, Fetch& F) {
 #pragma unroll
   for (int tt = 0; tt < kMTiles; ++tt) {
-    const uint32_t code = ent[tt * 16 + r];
-    const bool ok = code != 0xFFFFFFFFu;
-    const bool w = chunk0 + tt * 16 + r >= Q.n_first;
-    const size_t e = ok ? (size_t)code : (w ? Q.win_row : Q.blk_row);  // a slot without a key: an in-bounds entry
+    const int tile0 = chunk0 + tt * 16;
+    const int slot = tile0 + r;
+    const bool win = tile0 >= Q.win0;
+    int ws = Q.win_base + (slot - Q.win0);  // < 2 ring for a live window slot: one conditional wrap
+    ws = ws >= Q.ring ? ws - Q.ring : ws;
+    const int jl = list[min(slot, kMaxTopk - 1)];  // (CSA: slot < win0 <= kMaxTopk; unused otherwise)
+    const int j = Q.dense ? slot : jl;
+    const bool ok = win ? slot < Q.total : (slot < Q.n_first && j >= 0 && j < Q.N);
+    const uint32_t e = ok ? (uint32_t)(win ? ws : j) : 0u;
     F.valid[tt] = ok;
-    if (pp < 8) {
-      F.code[tt] = ldg<u32x2>((w ? Q.win_codes : Q.blk_codes) + e * kNope + 8 * pp);
-      F.scale[tt] = ldg<float>((w ? Q.win_scale : Q.blk_scale) + e);
+    // byte offsets in 32 bits from the sequence's (uniform) row base
+    if (NOPE) {
+      const u32x2 c = ldg<u32x2>((win ? Q.win_codes : Q.blk_codes) + (e * (uint32_t)kNope + 8u * (uint32_t)pp));
+      F.d[tt][0] = c[0];
+      F.d[tt][1] = c[1];
+      F.scale[tt] = ldg<float>((const uint8_t*)(win ? Q.win_scale : Q.blk_scale) + e * 4u);
     } else {
-      F.rope[tt] = ldg<u32x4>((w ? Q.win_rope : Q.blk_rope) + e * kRope + 8 * (pp - 8));
+      F.d[tt] = ldg<u32x4>((const uint8_t*)(win ? Q.win_rope : Q.blk_rope) +
+                           (e * (uint32_t)(2 * kRope) + 16u * (uint32_t)(pp - 8)));
     }
   }
 }
 
 // the fetched dims into the chunk buffer's key-major rows (a slot without a key as zeros); *kbad: whether
-// the chunk needs the masked path
-__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, uint16_t* kd, float* scl, uint32_t* kbad) {
+// the chunk needs the masked path (wave 0's part-0 lanes cover all of the chunk's slots)
+template <bool NOPE>
+__device__ __forceinline__ void stage(const Fetch& F, int pp, int r, int koff, uint16_t* kd, float* scl, uint32_t* kbad) {
+  bool bad = false;
+#pragma unroll
+  for (int tt = 0; tt < kMTiles; ++tt) bad |= !F.valid[tt];
 #pragma unroll
   for (int tt = 0; tt < kMTiles; ++tt) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 v = pp < 8 ? fp8x8_to_bf16(F.code[tt]) : F.rope[tt];
-    if (F.bad && !F.valid[tt]) v = zero;
-    *reinterpret_cast<u32x4*>(kd + tt * kKdTile + r * kKdStride + 8 * pp) = v;
+    u32x4 v = NOPE ? fp8x8_to_bf16((u32x2){F.d[tt][0], F.d[tt][1]}) : F.d[tt];
+    if (bad && !F.valid[tt]) v = zero;
+    *reinterpret_cast<u32x4*>(kd + tt * kKdTile + koff) = v;
   }
-  if (pp == 0) {
+  if (NOPE && pp == 0) {
 #pragma unroll
     for (int tt = 0; tt < kMTiles; ++tt) scl[16 * tt + r] = F.valid[tt] ? F.scale[tt] : -1.0f;
   }
-  if (threadIdx.x == 0) *kbad = F.bad ? 1u : 0u;
+  if (NOPE && threadIdx.x < 64) {
+    const uint64_t m = __ballot(pp == 0 && bad);
+    if (threadIdx.x == 0) *kbad = m != 0 ? 1u : 0u;
+  }
 }
 
 __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
@@ -153,19 +146,19 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
   if (t < 0) return;  // ragged batch: no query in this row
 
   Query Q;
-  Q.blk_codes = a.blk_codes;
-  Q.win_codes = a.win_codes;
-  Q.blk_rope = a.blk_rope;
-  Q.win_rope = a.win_rope;
-  Q.blk_scale = a.blk_scale;
-  Q.win_scale = a.win_scale;
-  Q.blk_row = (size_t)b * a.max_blocks;
-  Q.win_row = (size_t)b * a.ring;
+  const size_t brow = (size_t)b * a.max_blocks, wrow = (size_t)b * a.ring;
+  Q.blk_codes = a.blk_codes + brow * kNope;
+  Q.win_codes = a.win_codes + wrow * kNope;
+  Q.blk_rope = a.blk_rope + brow * kRope;
+  Q.win_rope = a.win_rope + wrow * kRope;
+  Q.blk_scale = a.blk_scale + brow;
+  Q.win_scale = a.win_scale + wrow;
   Q.N = (int32_t)min((t + 1) / a.m, a.max_blocks);  // 0 for the window-only layer
   Q.dense = a.dense != 0;
   Q.n_first = Q.dense ? Q.N : a.k;
+  Q.win0 = (Q.n_first + 15) & ~15;
   const int32_t n_win = (int32_t)min((int64_t)a.W, t + 1);
-  Q.total = Q.n_first + n_win;
+  Q.total = Q.win0 + n_win;
   Q.ring = a.ring;
   Q.win_base = (int32_t)((t - n_win + 1) % a.ring);
 
@@ -192,14 +185,6 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     }
   }
   __syncthreads();  // angles and the top-k row in LDS
-  make_entries(Q, S.list, 0, S.ent[0], &S.ebad[0]);
-  make_entries(Q, S.list, kMChunk, S.ent[1], &S.ebad[1]);
-  __syncthreads();
-
-  // chunk 0 into buffer 0
-  const int pp = tid >> 4, rr = tid & 15;
-  Fetch F;
-  fetch(Q, S.ent[0], &S.ebad[0], 0, pp, rr, F);
 
   // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3)
   bf16x8 qb[4];
@@ -218,8 +203,6 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     }
     qb[ks] = __builtin_bit_cast(bf16x8, v);
   }
-  stage(F, pp, rr, S.kd[0], S.scl[0], &S.kbad[0]);
-  __syncthreads();
 
   constexpr float kC = kLog2eRsqrtD;
   constexpr float kLazy = 8.0f;  // log2 units: O is rescaled only when a head's max rises by more
@@ -238,12 +221,20 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
     const int kk = 4 * h + (r >> 2);
     voff[h] = (kk & 1) * kKdTile + (4 * g + (kk >> 1)) * kKdStride + 4 * (r & 3);
   }
-  for (int c = 0; c < n_chunks; ++c) {
-    const int cur = c & 1;
-    // the next chunk's gathers first (slots past the end read an in-bounds entry and are masked), then
-    // the entries of the chunk after it into the entry buffer the fetch of this chunk read
-    fetch(Q, S.ent[(c + 1) & 1], &S.ebad[(c + 1) & 1], (c + 1) * kMChunk, pp, rr, F);
-    make_entries(Q, S.list, (c + 2) * kMChunk, S.ent[cur], &S.ebad[cur]);
+  // This thread gathers part pp of key rr of both tiles of a chunk (parts 0-7, the FP8 codes, in waves 0-1;
+  // the choice is per wave, so each kind of wave runs its own copy of the loop).
+  const int pp = tid >> 4, rr = tid & 15;
+  const int koff = rr * kKdStride + 8 * pp;
+  auto run = [&](auto nope_tag) {
+    constexpr bool NOPE = decltype(nope_tag)::value;
+    Fetch F;
+    fetch<NOPE>(Q, S.list, 0, pp, rr, F);
+    stage<NOPE>(F, pp, rr, koff, S.kd[0], S.scl[0], &S.kbad[0]);
+    __syncthreads();
+  // Step c (chunk c in buffer cur): the next chunk's gathers first (slots past the end read an in-bounds
+  // entry and are masked), then chunk c, then the next chunk into the other buffer.
+  auto step = [&](int c, int cur) {
+    fetch<NOPE>(Q, S.list, (c + 1) * kMChunk, pp, rr, F);
     if (active) {
       const uint16_t* kd = S.kd[cur];
       const float* scl = S.scl[cur];
@@ -316,9 +307,16 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       l_run += rs;
     }
     // the next chunk into the other buffer (last read in the previous step, before the barrier below)
-    if (c + 1 < n_chunks) stage(F, pp, rr, S.kd[cur ^ 1], S.scl[cur ^ 1], &S.kbad[cur ^ 1]);
+    if (c + 1 < n_chunks) stage<NOPE>(F, pp, rr, koff, S.kd[cur ^ 1], S.scl[cur ^ 1], &S.kbad[cur ^ 1]);
     __syncthreads();
+  };
+  for (int c = 0; c < n_chunks; c += 2) {
+    step(c, 0);
+    if (c + 1 < n_chunks) step(c + 1, 1);
   }
+  };
+  if (__builtin_amdgcn_readfirstlane(pp) < 8) run(BoolTag<true>{});
+  else run(BoolTag<false>{});
 
   // ---- output: lane (r, g) holds head 16 * wave + r, dims dt * 16 + 4g .. +3
   if (active && head_ok) {
