@@ -200,14 +200,19 @@ __device__ __forceinline__ void merge_splits(const AttendPartial* all, int split
                                              float (&acc)[4]) {
   constexpr float kC = kLog2eRsqrtD;
   auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto ld2 = [](const float* p, float* v) {  // two adjacent floats in one 8-byte load
+    const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v[0] = __uint_as_float((uint32_t)w);
+    v[1] = __uint_as_float((uint32_t)(w >> 32));
+  };
   float mv[NS], lv[NS], ov[NS][4];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     const int sp = min(u, splits - 1);
     mv[u] = ld(&all[sp].m[h]);
     lv[u] = ld(&all[sp].l[h]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ov[u][i] = ld(&all[sp].o[h][d0 + i]);
+    ld2(&all[sp].o[h][d0], &ov[u][0]);
+    ld2(&all[sp].o[h][d0 + 2], &ov[u][2]);
   }
   M = -INFINITY;
 #pragma unroll
@@ -319,15 +324,19 @@ __device__ __forceinline__ void attend_finish(const AttendArgs& args, AttnWaveLd
   const int h = tid >> 5, d0 = (tid & 31) * 4;
   // wave states in raw logit units (q . x): weight 2^((m_w - M) log2(e) / sqrt(128))
   constexpr float kC = kLog2eRsqrtD;
+  // branch-free, so that the LDS reads of all 8 wave states are issued together; a wave without keys
+  // (m = -inf, l = 0, o = 0) weighs 0
+  float mw[kWaves];
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, W.c.m[w][h]);
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = W.c.m[w][h];
+    M = fmaxf(M, mw[w]);
+  }
   float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const float mw = W.c.m[w][h];
-    if (mw == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f((mw - M) * kC);
+    const float f = mw[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mw[w] - M) * kC);
     L += W.c.l[w][h] * f;
     const v4f ov = *reinterpret_cast<const v4f*>(&W.c.o[w][h][d0]);
 #pragma unroll
@@ -342,8 +351,11 @@ __device__ __forceinline__ void attend_finish(const AttendArgs& args, AttnWaveLd
     // dirty line of the L2, at several microseconds). Each thread waits for its own stores to
     // complete before the workgroup counts itself in.
     AttendPartial* mine = args.part + ((size_t)q * hgs + hg) * splits + split;
+    uint64_t* op = reinterpret_cast<uint64_t*>(&mine->o[h][d0]);  // (16-byte aligned: d0 % 4 == 0)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __hip_atomic_store(&mine->o[h][d0 + i], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 2; ++i)
+      __hip_atomic_store(op + i, (uint64_t)__float_as_uint(acc[2 * i]) | ((uint64_t)__float_as_uint(acc[2 * i + 1]) << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d0 == 0) {
       __hip_atomic_store(&mine->m[h], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&mine->l[h], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
