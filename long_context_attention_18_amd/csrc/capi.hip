@@ -108,7 +108,7 @@ WsLayout ws_layout(const lca_layer_desc* d, int32_t B, int32_t max_tq, int64_t m
     W.off_seg = q; q = align_up(q + (size_t)n_seg * 4);
     W.off_keys = q; q = align_up(q + (size_t)max_blocks * 4);
     W.off_cand = q; q = align_up(q + (size_t)max_blocks * 8);
-    W.off_sync = q; q = align_up(q + sizeof(uint64_t));      // the in-launch threshold's counter, ready word
+    W.off_sync = q; q = align_up(q + kSyncBytes);             // the in-launch threshold's counter, ready word
     W.off_list = q; q = align_up(q + (size_t)kMaxTopk * 4);   // its top-k list, read by the attention
     W.off_rec = q; q = align_up(q + ((size_t)kRecHdrSlots + (size_t)n_seg * kRecMaxWords) * 8);  // its records
     W.qstride = q;

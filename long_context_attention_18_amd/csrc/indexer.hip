@@ -1048,7 +1048,7 @@ __device__ __forceinline__ void index_select_wg(const ScoreArgs& a, CoopLds& L, 
   if (token != 0u) {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's list stores have completed
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(sync + 1, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(sync + kSyncReady, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1157,7 +1157,7 @@ __device__ __forceinline__ void step_attend(const StepArgs& sa, StepAttnLds& S, 
   }
   K.list0 = 0;
   if (K.use_list) {
-    if (tid == 0) S.timed_out = wait_token(q_sync(args.s, q) + 1, sa.token) ? 0u : 1u;
+    if (tid == 0) S.timed_out = wait_token(q_sync(args.s, q) + kSyncReady, sa.token) ? 0u : 1u;
     __syncthreads();
     const int l0 = min(max(s_begin - K.n_win, 0), K.n_list), l1 = min(max(s_end - K.n_win, 0), K.n_list);
     const int32_t* lp = q_list(args.s, q);

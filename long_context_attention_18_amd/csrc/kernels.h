@@ -153,8 +153,13 @@ __device__ __forceinline__ uint32_t* q_hist(const ScoreArgs& a, int q) { return 
 __device__ __forceinline__ uint32_t* q_seg(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_seg); }
 __device__ __forceinline__ uint32_t* q_keys(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_keys); }
 __device__ __forceinline__ uint64_t* q_cand(const ScoreArgs& a, int q) { return (uint64_t*)(a.qbase + (size_t)q * a.qstride + a.off_cand); }
-// coop: the query's counter of score workgroups that arrived; zero between calls
+// coop: the query's counter of score workgroups that arrived (word 0; zero between calls) and, for the
+// one-launch step, its list-ready word (word kSyncReady: the launch's token once the list is out). The two
+// sit in different 128-byte lines: the attention workgroups poll the ready word while the score
+// workgroups count themselves in, and polls of the counter's line slow those atomics down.
 __device__ __forceinline__ uint32_t* q_sync(const ScoreArgs& a, int q) { return (uint32_t*)(a.qbase + (size_t)q * a.qstride + a.off_sync); }
+constexpr int kSyncReady = 32;
+constexpr int kSyncBytes = 256;
 // coop: per query, kRecHdrSlots record headers (one 64-bit word per score chunk: the chunk's largest key
 // << 32 | its floor bin << 16 | its candidate count), then one record of pref_slots words per score chunk
 // (its candidates, key << 32 | ~block, in block order, zero-padded)
