@@ -110,16 +110,19 @@ __device__ __forceinline__ int64_t visible_blocks(const ScoreArgs& a, int b, int
   return t < 0 ? 0 : (t + 1) / a.m;
 }
 
-// exclusive prefix sum of `v` over the threads of a workgroup; *total gets the sum
+// exclusive prefix sum of `v` over the threads of a workgroup of kScoreWaves waves (every caller's);
+// *total gets the sum. The waves' sums are read all at once, branch-free.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint32_t off = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) off += wsum[w];
-    tot += wsum[w];
+#pragma unroll
+  for (int w = 0; w < kScoreWaves; ++w) {
+    const uint32_t x = wsum[w];
+    off += w < wave ? x : 0u;
+    tot += x;
   }
   *total = tot;
   return off + incl - v;

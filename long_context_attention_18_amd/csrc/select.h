@@ -63,7 +63,11 @@ __device__ __forceinline__ uint32_t excl_scan_512(uint32_t v, uint32_t* wsum) {
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += wsum[w];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {  // all 8 read at once (a loop to `wave` would wait for each read in turn)
+    const uint32_t x = wsum[w];
+    off += w < wave ? x : 0u;
+  }
   return off + incl - v;
 }
 
@@ -255,7 +259,11 @@ __device__ inline uint32_t select_query(const ScoreArgs& a, int q, int64_t N, Se
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     uint32_t base = g0 == 0 ? 0u : seg_off[g0];
-    for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t x = wsum[w];
+      base += w < wave ? x : 0u;
+    }
     if (gi < G2_q) seg_off[gi] = base + incl - c;
     if (tid == 511) seg_off[g0 + 512 < G2_q ? g0 + 512 : G2_q] = base + incl;
     if (c > covered) S.flat_needed = 1u;
