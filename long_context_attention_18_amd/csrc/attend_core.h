@@ -369,7 +369,8 @@ __device__ __forceinline__ void attend_finish(const AttendArgs& args, AttnWaveLd
     if (!*last) return;
     if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     const AttendPartial* all = args.part + ((size_t)q * hgs + hg) * splits;
-    if (splits <= kAttendMaxSplits / 2) merge_splits<kAttendMaxSplits / 2>(all, splits, h, d0, M, L, acc);
+    if (splits <= 4) merge_splits<4>(all, splits, h, d0, M, L, acc);
+    else if (splits <= 8) merge_splits<8>(all, splits, h, d0, M, L, acc);
     else merge_splits<kAttendMaxSplits>(all, splits, h, d0, M, L, acc);
   }
   const int hh = hg * 16 + h;

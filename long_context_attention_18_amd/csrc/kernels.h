@@ -204,9 +204,9 @@ constexpr int kMaxTopk = 2048;
 constexpr int kAttendList = 0, kAttendDense = 1, kAttendSelect = 2, kAttendListWs = 3;
 // Key splits of the one-launch attention: a (query, 16-head group) may be spread over up to
 // kAttendMaxSplits workgroups (about one 32-key chunk per wave), each over its share of the keys; each writes a partial (running max,
-// sum and unnormalised O of its 16 heads) and the last to finish (a per-(query, group) counter,
-// release / acquire at agent scope) merges them.
-constexpr int kAttendMaxSplits = 8;
+// sum and unnormalised O of its 16 heads) with agent-scope stores that complete before it counts itself
+// in on a per-(query, group) counter, and the last to count in merges them.
+constexpr int kAttendMaxSplits = 16;
 constexpr int kAttendNoSplitChunks = 3;  // 32-key chunks per wave up to which a (query, head group) is not split
 constexpr int kAttendMaxWGs = 256;  // with splits, a call stays within one workgroup per CU (LDS allows one)
 struct AttendPartial {
