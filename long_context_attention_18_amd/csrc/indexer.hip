@@ -1455,14 +1455,22 @@ __device__ __forceinline__ void tile_select(const ScoreArgs& a, TileLds& S, int 
   // winners: (e & mask) >= prefix (every key of a higher bin or digit, and the bin's chosen ones), out in
   // index order
   uint32_t pos = 0;
-  for (uint32_t i0 = 0; i0 < total; i0 += 64) {
-    const uint32_t i = i0 + lane;
-    const uint64_t e = i < total ? flat(i) : 0ull;
-    const bool w = i < total && (e & mask) >= prefix;
-    const uint64_t bm = __ballot(w);
-    const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-    if (w && p < (uint32_t)a.k) out[p] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
-    pos += (uint32_t)__popcll(bm);
+  for (uint32_t i0 = 0; i0 < total; i0 += 256) {  // 256 candidates per round, their loads issued together
+    uint64_t e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + 64u * u + (uint32_t)lane;
+      e[u] = i < total ? flat(i) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + 64u * u + (uint32_t)lane;
+      const bool w = i < total && (e[u] & mask) >= prefix;
+      const uint64_t bm = __ballot(w);
+      const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+      if (w && p < (uint32_t)a.k) out[p] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[u] & 0xFFFFFFFFu));
+      pos += (uint32_t)__popcll(bm);
+    }
   }
   for (uint32_t i = pos + lane; i < (uint32_t)a.k; i += 64) out[i] = -1;  // only if fewer than k were found
 }
