@@ -70,6 +70,7 @@ WORKLOAD_BY_NAME = {"csa_decode_small": 0, "hca_decode_64k": 1, "csa_decode_1m":
 PERSIST_METRIC = "snapshot + restore GB/s of one 1M-token CSA sequence's compressed state, 1 GPU"
 PREFILL_METRIC = "chunked-prefill tok/s (CSA layer, 131072 tokens, chunk 8192), 1 GPU"
 MXFP4_PEAK_TFLOPS = 10100.0
+BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse_args():
@@ -478,7 +479,7 @@ def prefill_bench(args, wl):
     log(f"inputs of {total} tokens on the device in {time.perf_counter() - t0:.1f} s")
     hev = HipEvents()
     rec = lambda e: hev.record(e, False)
-    ev = [(hev.create(), hev.create()) for _ in range(n_chunks)]
+    ev = [(hev.create(), hev.create(), hev.create()) for _ in range(n_chunks)]
     ev_begin, ev_end = hev.create(), hev.create()
     last = n_chunks - 1
 
@@ -495,6 +496,8 @@ def prefill_bench(args, wl):
         if timed:
             rec(ev[c][1])
         dev.sparse_attn(qin["q"], tk, o)
+        if timed:
+            rec(ev[c][2])
 
     for c in range(2):
         chunk(c, False)
@@ -508,7 +511,14 @@ def prefill_bench(args, wl):
     rec(ev_end)
     torch.cuda.synchronize()
     total_ms = hev.elapsed_ms(ev_begin, ev_end)
-    sc_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b in ev])
+    sc_us = np.array([hev.elapsed_ms(a, b) * 1e3 for a, b, _ in ev])
+    at_us = np.array([hev.elapsed_ms(b, e) * 1e3 for _, b, e in ev])
+    # BF16 MFMA flops of the attention: per query and head, QK^T and PV^T over its keys (the top-k
+    # entries, or every visible block while there are at most k, plus the window), 128 dims each
+    t_all = np.arange(total)
+    keys = np.minimum((t_all + 1) // layer.m, k) + np.minimum(layer.window, t_all + 1)
+    at_flops = float(keys.sum()) * H * 128 * 2 * 2
+    at_rate = at_flops / (at_us.sum() * 1e-6) / 1e12
     # MXFP4 MACs of the indexer: every visible block of every query, H_I heads x 64 dims (counted once,
     # although the query tiles score each block twice)
     flops = []
@@ -519,7 +529,8 @@ def prefill_bench(args, wl):
     sel = [c for c in range(n_chunks) if flops[c] > 0]
     achieved = float(np.sum([flops[c] for c in sel]) / np.sum([sc_us[c] * 1e-6 for c in sel]) / 1e12)
     log(f"timed prefill of {total} tokens: {total_ms:.2f} ms; indexer (score + select) {sc_us[sel].mean():.1f} us "
-        f"avg per chunk ({achieved:.1f} TFLOP/s MXFP4)")
+        f"avg per chunk ({achieved:.1f} TFLOP/s MXFP4); attention {at_us.mean():.1f} us avg per chunk "
+        f"({at_rate:.1f} TFLOP/s BF16)")
     result = {
         "metric": PREFILL_METRIC, "value": round(total / (total_ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1,
         "steps": n_chunks, "warmup": 2, "ms_per_step": round(total_ms / n_chunks, 4), "higher_is_better": True,
@@ -529,6 +540,9 @@ def prefill_bench(args, wl):
         "roofline": {"bound": "mfma", "kernel": "tile_kernel + select_kernel", "achieved": round(achieved, 2),
                      "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP4_PEAK_TFLOPS, 5),
                      "traffic": None, "avg_launch_us": round(float(sc_us[sel].mean()), 2)},
+        "attention": {"kernel": "attn_kernel", "avg_launch_us": round(float(at_us.mean()), 2),
+                      "achieved": round(at_rate, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(at_rate / BF16_PEAK_TFLOPS, 5)},
     }
     if not args.no_cpu_baseline:
         import oracle as O
