@@ -18,7 +18,10 @@
 // (ds_read_b64_tr_b16: lane 4a + e of a 16-lane group gets element e of the 8-byte rows the group's
 // lanes a, a+4, a+8, a+12 address), each lane addressing the key its K index needs. The FP8 codes and
 // the BF16 RoPE dims are exact in bf16; the per-entry fp32 scale multiplies the nope logits and is
-// folded into P for the nope output dims. The next chunk's gathers are issued before the current chunk
+// folded into P for the nope output dims. The query is taken times log2(e)/sqrt(128) before its bf16
+// rounding and the RoPE half of each logit's MFMA chain starts at minus the head's running maximum, so
+// the chunk's values are the exp2 arguments as they come out; each head's softmax denominator is a
+// ninth PV MFMA over an all-ones V tile (the same bf16 P as the output's). The next chunk's gathers are issued before the current chunk
 // is computed, into the second of two LDS buffers, one barrier per chunk. The window's slots start at the
 // first whole 16-key tile after the compressed ones, so a tile reads one array, whose base (the sequence's
 // rows) is the same for every lane and takes 32-bit byte offsets; each gathering thread resolves its key's
@@ -186,30 +189,41 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();  // angles and the top-k row in LDS
 
-  // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3)
+  // rotated query as the B operand of S^T = K . Q^T (RoPE dims 64..127: ks = 2, 3), times log2(e)/sqrt(128)
+  // before its bf16 rounding: the logits come out of the MFMA in exp2 units
+  constexpr float kC = kLog2eRsqrtD;
   bf16x8 qb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     u32x4 v = qraw[ks];
-    if (ks >= 2) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u) {
+      const float x0 = bf16_to_f32((uint16_t)(v[u] & 0xFFFFu));
+      const float x1 = bf16_to_f32((uint16_t)(v[u] >> 16));
+      float y0 = x0, y1 = x1;
+      if (ks >= 2) {
         const int pi = 16 * (ks - 2) + 4 * g + u;
         const float c = S.cos_t[pi], s = S.sin_t[pi];
-        const float x0 = bf16_to_f32((uint16_t)(v[u] & 0xFFFFu));
-        const float x1 = bf16_to_f32((uint16_t)(v[u] >> 16));
-        v[u] = (uint32_t)f32_to_bf16(x0 * c - x1 * s) | ((uint32_t)f32_to_bf16(x0 * s + x1 * c) << 16);
+        y0 = x0 * c - x1 * s;
+        y1 = x0 * s + x1 * c;
       }
+      v[u] = (uint32_t)f32_to_bf16(y0 * kC) | ((uint32_t)f32_to_bf16(y1 * kC) << 16);
     }
     qb[ks] = __builtin_bit_cast(bf16x8, v);
   }
 
-  constexpr float kC = kLog2eRsqrtD;
-  constexpr float kLazy = 8.0f;  // log2 units: O is rescaled only when a head's max rises by more
-  float m_run = -INFINITY, l_run = 0.0f;
-  v4f O[8];
+  // Running state of head r (log2 units): m_run, the softmax's reference point (-inf until the head has a
+  // key); the RoPE half of every logit starts its MFMA chain at -ref (ref = m_run, 0 before the first
+  // key), so the chunk's values are already logit - ref, the exp2 argument. O is rescaled only when a
+  // chunk's maximum rises above ref by more than kLazy (lim); the row sum l accumulates in a ninth PV
+  // MFMA whose V tile is all ones (every lane of head r holds it), from the same bf16 P as O.
+  constexpr float kLazy = 8.0f;
+  float m_run = -INFINITY, ref = 0.0f, lim = -INFINITY;
+  v4f nref = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f O[8], Lsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const bool active = wave * 16 < a.H;
   const int n_chunks = (Q.total + kMChunk - 1) / kMChunk;
   // V^T operand rows of this lane for the two transposing reads h: MFMA K index 8g + 4h + u (u = r / 4)
@@ -243,14 +257,14 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int tt = 0; tt < kMTiles; ++tt) {
         const uint16_t* krow = kd + tt * kKdTile + r * kKdStride + 8 * g;
-        v4f an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f an = {0.0f, 0.0f, 0.0f, 0.0f};
         an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow)), qb[0], an, 0, 0, 0);
         an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 32)), qb[1], an, 0, 0, 0);
-        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 64)), qb[2], ar, 0, 0, 0);
+        v4f ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 64)), qb[2], nref, 0, 0, 0);
         ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 96)), qb[3], ar, 0, 0, 0);
         sc4[tt] = *reinterpret_cast<const v4f*>(scl + tt * 16 + 4 * g);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Sv[tt][v] = fmaf(an[v], sc4[tt][v], ar[v]);
+        for (int v = 0; v < 4; ++v) Sv[tt][v] = fmaf(an[v], sc4[tt][v], ar[v]);  // logit - ref
       }
       if (S.kbad[cur]) {
         // a slot without a key (scale -1, all-zero dims) is masked; an entry whose nope part is all
@@ -267,31 +281,36 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       for (int tt = 2; tt < kMTiles; tt += 2)
         mx = max3_raw(mx, max3_raw(Sv[tt][0], Sv[tt][1], Sv[tt][2]), max3_raw(Sv[tt][3], Sv[tt + 1][0],
                       max3_raw(Sv[tt + 1][1], Sv[tt + 1][2], Sv[tt + 1][3])));
-      mx = pair_max32(pair_max16(mx));
-      const bool raise = mx * kC > m_run * kC + kLazy;  // also true for the first finite max (m_run = -inf)
+      mx = pair_max32(pair_max16(mx));  // the chunk's largest logit - ref
+      const bool raise = mx > lim;      // the first finite maximum, or a rise of more than kLazy
       if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
-        const float m_new = raise ? mx : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f((m_run - m_new) * kC) : 1.0f;  // 0 from -inf
-        l_run *= alpha;
+        const float m_new = raise ? mx + ref : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 from -inf
+        const float sh = raise ? mx : 0.0f;                                          // m_new - ref
+#pragma unroll
+        for (int tt = 0; tt < kMTiles; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Sv[tt][v] -= sh;
+        Lsum *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
         m_run = m_new;
+        ref = m_run == -INFINITY ? 0.0f : m_run;
+        lim = m_run == -INFINITY ? -INFINITY : kLazy;
+        nref = (v4f){-ref, -ref, -ref, -ref};
       }
-      const float mk = (m_run == -INFINITY) ? 0.0f : m_run * kC;  // exp2 argument S kC - m kC, one fma
-      float rs = 0.0f;
 #pragma unroll
       for (int ksp = 0; ksp < kMTiles / 2; ++ksp) {
         // P of tiles 2 ksp, 2 ksp + 1: the B operand of one PV K-step
         u32x4 pr, pn;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(Sv[2 * ksp][v], kC, -mk));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(Sv[2 * ksp + 1][v], kC, -mk));
-          rs = (ksp == 0 && v == 0) ? p0 + p1 : rs + (p0 + p1);  // the first pair starts the sum (no add of +0)
+          const float p0 = __builtin_amdgcn_exp2f(Sv[2 * ksp][v]);
+          const float p1 = __builtin_amdgcn_exp2f(Sv[2 * ksp + 1][v]);
           pr[v] = pack_bf16(p0, p1);
           pn[v] = pack_bf16(p0 * sc4[2 * ksp][v], p1 * sc4[2 * ksp + 1][v]);
         }
-        // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P)
+        // O^T += V^T . P^T : dim tiles 0..3 (nope, P * scale), 4..7 (RoPE, P); the row sums from the ones tile
         const bf16x8 bn = __builtin_bit_cast(bf16x8, pn), br = __builtin_bit_cast(bf16x8, pr);
         const uint16_t* kv = kd + 2 * ksp * kKdTile;
 #pragma unroll
@@ -302,9 +321,8 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
           const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
           O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), dt < 4 ? bn : br, O[dt], 0, 0, 0);
         }
+        Lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, br, Lsum, 0, 0, 0);
       }
-      rs = pair_sum32(pair_sum16(rs));
-      l_run += rs;
     }
     // the next chunk into the other buffer (last read in the previous step, before the barrier below)
     if (c + 1 < n_chunks) stage<NOPE>(F, pp, rr, koff, S.kd[cur ^ 1], S.scl[cur ^ 1], &S.kbad[cur ^ 1]);
@@ -320,6 +338,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
 
   // ---- output: lane (r, g) holds head 16 * wave + r, dims dt * 16 + 4g .. +3
   if (active && head_ok) {
+    const float l_run = Lsum[0];
     const float inv = 1.0f / l_run;
     const size_t row = ((size_t)b * a.Tq + tq) * a.H + head;
 #pragma unroll
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(kMThreads) void attn_kernel(AttnArgs a) {
       pk.y = (uint32_t)f32_to_bf16(O[dt][2] * inv) | ((uint32_t)f32_to_bf16(O[dt][3] * inv) << 16);
       *reinterpret_cast<uint2*>(a.out + row * kHeadDim + dt * 16 + 4 * g) = pk;
     }
-    if (a.lse && g == 0) a.lse[row] = m_run * 0.08838834764831845f + __logf(l_run);  // natural-log units
+    if (a.lse && g == 0) a.lse[row] = m_run * 0.6931471805599453f + __logf(l_run);  // natural-log units
   }
 }
 
